@@ -1,0 +1,252 @@
+// api.hip -- the extern "C" entry points of liblca.so: host-side validation, workspace layout, dispatch.
+// Every check runs before anything is enqueued, so an error return leaves the stream untouched.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lca_internal.h"
+
+
+using namespace lca;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Validates one tensor descriptor: format, dim, pointers and their alignment.
+int check_tensor(const lca_tensor& t, bool allow_fp4, bool allow_mixed) {
+  if (t.dim <= 0 || t.cap <= 0 || !t.data) return LCA_ERR_INVALID_ARG;
+  switch (t.format) {
+    case LCA_F32:
+    case LCA_BF16:
+      break;
+    case LCA_MIXED_FP8:
+      if (!allow_mixed) return LCA_ERR_UNSUPPORTED;
+      if (t.rope_dims <= 0 || t.rope_dims >= t.dim || !t.rope || !t.scale) return LCA_ERR_INVALID_ARG;
+      if (!aligned16(t.rope) || ((uintptr_t)t.scale & 3u)) return LCA_ERR_ALIGNMENT;
+      break;
+    case LCA_FP4:
+      if (!allow_fp4) return LCA_ERR_UNSUPPORTED;
+      if (t.dim % 16 != 0 || !t.scale) return LCA_ERR_INVALID_ARG;
+      if ((uintptr_t)t.scale & 3u) return LCA_ERR_ALIGNMENT;
+      break;
+    default:
+      return LCA_ERR_INVALID_ARG;
+  }
+  if (!aligned16(t.data)) return LCA_ERR_ALIGNMENT;
+  return LCA_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? LCA_OK : LCA_ERR_HIP; }
+
+// Split plan of the attention: rows = B * Sq query rows, each with up to max_entries list positions.
+void attn_plan(int B, int Sq, int H, int max_entries, int& n_splits, int& split_len) {
+  const long long rows = (long long)B * Sq;
+  n_splits = 1;
+  split_len = max_entries > 0 ? max_entries : 1;
+  if (rows >= 256 || max_entries <= 64) return;
+  const long long want = (256 + rows - 1) / rows;
+  long long len = (max_entries + want - 1) / want;
+  len = (len + 31) / 32 * 32;
+  if (len < 64) len = 64;
+  long long ns = (max_entries + len - 1) / len;
+  const long long max_splits = 16000 / (H > 0 ? H : 1) - 1;  // merge keeps H * (splits + 1) floats in LDS
+  if (ns > max_splits) {
+    ns = max_splits;
+    len = (max_entries + ns - 1) / ns;
+    len = (len + 31) / 32 * 32;
+    ns = (max_entries + len - 1) / len;
+  }
+  n_splits = (int)ns;
+  split_len = (int)len;
+}
+
+size_t attn_ws_size(int B, int Sq, int H, int D, int max_entries) {
+  int ns, len;
+  attn_plan(B, Sq, H, max_entries, ns, len);
+  if (ns <= 1) return 0;
+  const size_t items = (size_t)B * Sq * ns;
+  return align_up(items * H * D * sizeof(float)) + align_up(items * H * 2 * sizeof(float));
+}
+
+int run_attn(const void* q, int q_format, const lca_tensor& comp, int N, int hca_m, const lca_tensor& raw,
+             long long raw_start, int S_raw, const int32_t* idx, int k, const float* sink, int B, int Sq, int H, int D,
+             int window, float scale, long long q_start, void* out, int out_format, float* lse, void* ws,
+             size_t ws_bytes, void* stream) {
+  if (!q || !sink || !out) return LCA_ERR_INVALID_ARG;
+  if (B <= 0 || Sq <= 0 || H <= 0 || D <= 0 || window < 0 || N < 0 || q_start < 0) return LCA_ERR_INVALID_ARG;
+  if (hca_m == 0 && (k < 0 || (k > 0 && !idx))) return LCA_ERR_INVALID_ARG;
+  if (q_format != LCA_F32 && q_format != LCA_BF16) return LCA_ERR_INVALID_ARG;
+  if (out_format != LCA_F32 && out_format != LCA_BF16) return LCA_ERR_INVALID_ARG;
+  int rc = check_tensor(comp, false, true);
+  if (rc) return rc;
+  if (window > 0) {
+    rc = check_tensor(raw, false, true);
+    if (rc) return rc;
+    if (raw.format != comp.format || raw.dim != D || (raw.format == LCA_MIXED_FP8 && raw.rope_dims != comp.rope_dims))
+      return LCA_ERR_INVALID_ARG;
+    // every window position of every query must be inside the raw span
+    long long first_w0 = q_start - window + 1;
+    if (first_w0 < 0) first_w0 = 0;
+    const long long last_t = q_start + Sq - 1;
+    if (S_raw <= 0 || S_raw > raw.cap || first_w0 < raw_start || last_t >= raw_start + S_raw) return LCA_ERR_INVALID_ARG;
+  }
+  if (comp.dim != D || (long long)N > comp.cap) return LCA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(out) || (idx && ((uintptr_t)idx & 3u)) || ((uintptr_t)sink & 3u))
+    return LCA_ERR_ALIGNMENT;
+  const bool mfma = attn_uses_mfma(H, D, q_format, comp.format);
+  if (!mfma) {
+    if (H > 64 || D > 512 || (long long)H * D > 8192) return LCA_ERR_UNSUPPORTED;
+    if (comp.format == LCA_MIXED_FP8 && (D - comp.rope_dims) <= 0) return LCA_ERR_INVALID_ARG;
+  } else if (comp.format == LCA_MIXED_FP8 && comp.rope_dims != 64) {
+    return LCA_ERR_UNSUPPORTED;
+  }
+  const int max_entries = window + (hca_m > 0 ? N : k);
+  int ns, len;
+  attn_plan(B, Sq, H, max_entries, ns, len);
+  const size_t need = attn_ws_size(B, Sq, H, D, max_entries);
+  if (need > 0 && (!ws || ws_bytes < need)) return LCA_ERR_WORKSPACE;
+
+  AttnArgs a{};
+  a.q = q;
+  a.q_format = q_format;
+  a.comp = comp;
+  a.raw = raw;
+  a.N = N;
+  a.raw_start = raw_start;
+  a.S_raw = S_raw;
+  a.idx = idx;
+  a.k = k;
+  a.hca_m = hca_m;
+  a.sink = sink;
+  a.B = B;
+  a.Sq = Sq;
+  a.H = H;
+  a.D = D;
+  a.window = window;
+  a.scale = scale;
+  a.q_start = q_start;
+  a.out = out;
+  a.out_format = out_format;
+  a.lse = lse;
+  a.n_splits = ns;
+  a.split_len = len;
+  if (ns > 1) {
+    const size_t items = (size_t)B * Sq * ns;
+    a.part_o = (float*)ws;
+    a.part_ml = (float*)((char*)ws + align_up(items * H * D * sizeof(float)));
+  }
+  return hip_status(launch_attn(a, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lca_status_string(int status) {
+  switch (status) {
+    case LCA_OK:
+      return "LCA_OK";
+    case LCA_ERR_INVALID_ARG:
+      return "LCA_ERR_INVALID_ARG: null pointer, bad size or inconsistent arguments";
+    case LCA_ERR_UNSUPPORTED:
+      return "LCA_ERR_UNSUPPORTED: no kernel for this shape/format combination";
+    case LCA_ERR_WORKSPACE:
+      return "LCA_ERR_WORKSPACE: workspace missing or too small";
+    case LCA_ERR_ALIGNMENT:
+      return "LCA_ERR_ALIGNMENT: pointer not 16-byte aligned";
+    case LCA_ERR_HIP:
+      return "LCA_ERR_HIP: the HIP runtime rejected a launch";
+    default:
+      return "unknown lca status";
+  }
+}
+
+int lca_encode(const float* src, int B, long long rows, long long row0, lca_tensor dst, void* stream) {
+  if (!src || B <= 0 || rows < 0 || row0 < 0) return LCA_ERR_INVALID_ARG;
+  int rc = check_tensor(dst, true, true);
+  if (rc) return rc;
+  if (row0 + rows > dst.cap) return LCA_ERR_INVALID_ARG;
+  if (dst.dim > 1024) return LCA_ERR_UNSUPPORTED;
+  if (rows == 0) return LCA_OK;
+  return hip_status(launch_encode(src, B, rows, row0, dst, (hipStream_t)stream));
+}
+
+int kv_compress(const float* Ca, const float* Cb, const float* Za, const float* Zb, const float* Ba, const float* Bb,
+                const float* tail_Cb, const float* tail_Zb, int B, long long n, int c, int m, int overlap,
+                long long start_pos, lca_tensor out, void* stream) {
+  if (!Ca || !Za || !Ba || B <= 0 || n <= 0 || c <= 0 || m <= 0 || start_pos < 0) return LCA_ERR_INVALID_ARG;
+  if (overlap && (!Cb || !Zb || !Bb)) return LCA_ERR_INVALID_ARG;
+  if (start_pos % m != 0) return LCA_ERR_INVALID_ARG;
+  if (overlap && start_pos > 0 && (!tail_Cb || !tail_Zb)) return LCA_ERR_INVALID_ARG;
+  int rc = check_tensor(out, true, true);
+  if (rc) return rc;
+  if (out.dim != c) return LCA_ERR_INVALID_ARG;
+  if (c > 1024) return LCA_ERR_UNSUPPORTED;
+  const long long nb = (n + m - 1) / m;
+  if (start_pos / m + nb > out.cap) return LCA_ERR_INVALID_ARG;
+  return hip_status(launch_compress(Ca, overlap ? Cb : nullptr, Za, overlap ? Zb : nullptr, Ba, overlap ? Bb : nullptr,
+                                    (overlap && start_pos > 0) ? tail_Cb : nullptr,
+                                    (overlap && start_pos > 0) ? tail_Zb : nullptr, B, n, c, m, overlap ? 1 : 0,
+                                    start_pos, out, (hipStream_t)stream));
+}
+
+size_t indexer_score_topk_workspace_size(int B, int Sq, int N, int k) {
+  (void)k;
+  if (B <= 0 || Sq <= 0 || N <= 0) return kAlign;
+  return align_up((size_t)B * Sq * N * sizeof(uint32_t));
+}
+
+int indexer_score_topk(lca_tensor qI, const float* w, lca_tensor kI, int B, int Sq, int HI, int DI, int N, int m, int k,
+                       long long q_start_pos, int32_t* idx_out, float* score_out, void* ws, size_t ws_bytes,
+                       void* stream) {
+  if (!w || !idx_out || B <= 0 || Sq <= 0 || HI <= 0 || DI <= 0 || N < 0 || m <= 0 || k <= 0 || q_start_pos < 0)
+    return LCA_ERR_INVALID_ARG;
+  int rc = check_tensor(qI, true, false);
+  if (rc) return rc;
+  rc = check_tensor(kI, true, false);
+  if (rc) return rc;
+  if (qI.dim != DI || kI.dim != DI || qI.cap < (long long)Sq * HI || kI.cap < N) return LCA_ERR_INVALID_ARG;
+  if ((qI.format == LCA_FP4) != (kI.format == LCA_FP4)) return LCA_ERR_UNSUPPORTED;
+  if (HI > 64 || DI > 128) return LCA_ERR_UNSUPPORTED;
+  if (((uintptr_t)w & 3u) || ((uintptr_t)idx_out & 3u) || (score_out && ((uintptr_t)score_out & 3u)))
+    return LCA_ERR_ALIGNMENT;
+  if (N > 0 && (!ws || ws_bytes < indexer_score_topk_workspace_size(B, Sq, N, k))) return LCA_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  IdxArgs a{qI, kI, w, (uint32_t*)ws, B, Sq, HI, DI, N, m, q_start_pos};
+  if (N > 0) {
+    rc = hip_status(launch_indexer_scores(a, st));
+    if (rc) return rc;
+  }
+  SelArgs s{(const uint32_t*)ws, idx_out, score_out, B * Sq, Sq, N, m, k, q_start_pos};
+  return hip_status(launch_topk(s, st));
+}
+
+size_t sparse_mqa_attn_workspace_size(int B, int Sq, int H, int D, int max_entries) {
+  return attn_ws_size(B, Sq, H, D, max_entries);
+}
+
+int sparse_mqa_attn(const void* q, int q_format, lca_tensor kv_comp, int N, lca_tensor kv_raw, long long raw_start_pos,
+                    int S_raw, const int32_t* idx, int k, const float* sink, int B, int Sq, int H, int D, int window,
+                    float scale, long long q_start_pos, void* out, int out_format, float* lse_out, void* ws,
+                    size_t ws_bytes, void* stream) {
+  return run_attn(q, q_format, kv_comp, N, 0, kv_raw, raw_start_pos, S_raw, idx, k, sink, B, Sq, H, D, window, scale,
+                  q_start_pos, out, out_format, lse_out, ws, ws_bytes, stream);
+}
+
+size_t hca_attn_workspace_size(int B, int Sq, int H, int D, int max_entries) {
+  return attn_ws_size(B, Sq, H, D, max_entries);
+}
+
+int hca_attn(const void* q, int q_format, lca_tensor kv_comp, int N, int m, lca_tensor kv_raw, long long raw_start_pos,
+             int S_raw, const float* sink, int B, int Sq, int H, int D, int window, float scale,
+             long long q_start_pos, void* out, int out_format, float* lse_out, void* ws, size_t ws_bytes,
+             void* stream) {
+  if (m <= 0) return LCA_ERR_INVALID_ARG;
+  return run_attn(q, q_format, kv_comp, N, m, kv_raw, raw_start_pos, S_raw, nullptr, 0, sink, B, Sq, H, D, window,
+                  scale, q_start_pos, out, out_format, lse_out, ws, ws_bytes, stream);
+}
+
+}  // extern "C"

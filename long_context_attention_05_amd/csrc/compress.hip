@@ -1,0 +1,229 @@
+// compress.hip -- stage 1 (KV compression) and the cache codec's quantise-on-write.
+//
+// KV compression follows the paper notes ("DeepSeek-V4: Towards Highly Efficient Million-Token Context
+// Intelligence"), section 2.3 Eq. 11-12 and the Compressor excerpt, and section 2.4 Eq. 22-23: per channel,
+// a softmax over the candidates' logits (gate + learned position bias) weights the candidates' values;
+// with overlap (CSA) the candidates are the block's own tokens from stream a plus the previous block's tokens
+// from stream b.  The work is a pure HBM stream (each input value is read once, 1/m as much is written), so it
+// runs on the vector ALU: one workgroup per (entry, sequence), one thread per channel slice, loads coalesced
+// along channels, an online softmax in fp32.
+//
+// The codec (mixed-precision cache: cosmocat page section 3; Mind Observatory page) is applied in the same
+// pass: fp32 entries are encoded to bf16 / fp8 e4m3 with a per-entry scale plus bf16 RoPE dims / fp4 e2m1 with
+// per-16 power-of-two scales while the row is still in registers.
+#include "lca_device.h"
+#include "lca_internal.h"
+
+namespace lca {
+
+constexpr int kRowThreads = 256;
+
+struct RowOut {
+  int format, dim, rope;
+  long long cap;
+  void* data;
+  void* rope_data;
+  void* scale;
+};
+
+__device__ __forceinline__ float block_max_256(float v, float* red) {
+  v = wave_max(v);
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __syncthreads();
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  float r = red[0];
+  for (int i = 1; i < (int)(blockDim.x >> 6); ++i) r = fmaxf(r, red[i]);
+  return r;
+}
+
+// Encode one row held as v[u] = channel (threadIdx.x + blockDim.x * u), u < CPT, and store it at `row`.
+// All threads of the block must call this (block-wide reduction for the fp8 scale).
+template <int CPT>
+__device__ void store_row(const RowOut& o, long long row, const float (&v)[CPT], float* red) {
+  const int c = o.dim;
+  const int nt = blockDim.x;
+  if (o.format == LCA_F32) {
+    float* d = (float*)o.data + row * c;
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      int j = threadIdx.x + nt * u;
+      if (j < c) d[j] = v[u];
+    }
+  } else if (o.format == LCA_BF16) {
+    uint16_t* d = (uint16_t*)o.data + row * c;
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      int j = threadIdx.x + nt * u;
+      if (j < c) d[j] = f32_to_bf16(v[u]);
+    }
+  } else if (o.format == LCA_MIXED_FP8) {
+    const int dm = c - o.rope;
+    float am = 0.0f;
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      int j = threadIdx.x + nt * u;
+      if (j < dm) am = fmaxf(am, fabsf(v[u]));
+    }
+    am = block_max_256(am, red);
+    const float s = (am == 0.0f) ? 1.0f : am / 448.0f;  // IEEE fp32 divide
+    uint8_t* d = (uint8_t*)o.data + row * dm;
+    uint16_t* rd = (uint16_t*)o.rope_data + row * o.rope;
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      int j = threadIdx.x + nt * u;
+      if (j < dm) {
+        float y = fminf(fmaxf(v[u] / s, -448.0f), 448.0f);
+        d[j] = fp8_encode(y);
+      } else if (j < c) {
+        rd[j - dm] = f32_to_bf16(v[u]);
+      }
+    }
+    if (threadIdx.x == 0) ((float*)o.scale)[row] = s;
+  } else {  // LCA_FP4: groups of 16 consecutive channels live in 16 consecutive lanes
+    uint8_t* d = (uint8_t*)o.data + row * (c / 2);
+    uint8_t* sc = (uint8_t*)o.scale + row * (c / 16);
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      int j = threadIdx.x + nt * u;
+      float a = (j < c) ? fabsf(v[u]) : 0.0f;
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
+      int e = fp4_group_exp(a);
+      float y = ldexpf(v[u], -e);
+      uint32_t code = fp4_encode(y);
+      uint32_t other = __shfl_xor(code, 1, 64);
+      if (j < c) {
+        if ((j & 1) == 0) d[j >> 1] = (uint8_t)(code | (other << 4));
+        if ((j & 15) == 0) sc[j >> 4] = (uint8_t)(e + 127);
+      }
+    }
+  }
+}
+
+template <int CPT>
+__global__ __launch_bounds__(kRowThreads) void encode_rows_kernel(const float* __restrict__ src, long long rows,
+                                                                   long long row0, RowOut o) {
+  __shared__ float red[kRowThreads / 64];
+  const long long r = blockIdx.x;
+  const int b = blockIdx.y;
+  const float* s = src + ((long long)b * rows + r) * o.dim;
+  float v[CPT];
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) {
+    int j = threadIdx.x + blockDim.x * u;
+    v[u] = (j < o.dim) ? s[j] : 0.0f;
+  }
+  store_row<CPT>(o, (long long)b * o.cap + row0 + r, v, red);
+}
+
+struct CompressArgs {
+  const float *Ca, *Cb, *Za, *Zb, *Ba, *Bb, *tCb, *tZb;
+  long long n, start_pos;
+  int c, m, overlap;
+};
+
+__device__ __forceinline__ void softmax_acc(float l, float x, float& mx, float& den, float& num) {
+  float nm = fmaxf(mx, l);
+  float sc = __expf(mx - nm);
+  float e = __expf(l - nm);
+  den = den * sc + e;
+  num = num * sc + e * x;
+  mx = nm;
+}
+
+template <int CPT>
+__global__ __launch_bounds__(kRowThreads) void compress_kernel(CompressArgs a, RowOut o) {
+  __shared__ float red[kRowThreads / 64];
+  const long long i = blockIdx.x;  // local entry index
+  const int b = blockIdx.y;
+  const int c = a.c, m = a.m;
+  const long long gblock = a.start_pos / m + i;
+  float mx[CPT], den[CPT], num[CPT];
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) {
+    mx[u] = -INFINITY;
+    den[u] = 0.0f;
+    num[u] = 0.0f;
+  }
+  const long long base = (long long)b * a.n;
+  // stream a: block i's own tokens
+  for (int r = 0; r < m; ++r) {
+    long long p = (long long)m * i + r;
+    if (p >= a.n) break;
+    const float* zr = a.Za + (base + p) * c;
+    const float* cr = a.Ca + (base + p) * c;
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      int j = threadIdx.x + blockDim.x * u;
+      if (j < c) softmax_acc(zr[j] + a.Ba[r * c + j], cr[j], mx[u], den[u], num[u]);
+    }
+  }
+  // stream b: block i-1's tokens (absent for the first block of the sequence)
+  if (a.overlap && gblock >= 1) {
+    for (int r = 0; r < m; ++r) {
+      const float *zr, *cr;
+      if (i >= 1) {
+        long long p = (long long)m * (i - 1) + r;
+        zr = a.Zb + (base + p) * c;
+        cr = a.Cb + (base + p) * c;
+      } else {
+        zr = a.tZb + ((long long)b * m + r) * c;
+        cr = a.tCb + ((long long)b * m + r) * c;
+      }
+#pragma unroll
+      for (int u = 0; u < CPT; ++u) {
+        int j = threadIdx.x + blockDim.x * u;
+        if (j < c) softmax_acc(zr[j] + a.Bb[r * c + j], cr[j], mx[u], den[u], num[u]);
+      }
+    }
+  }
+  float v[CPT];
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) v[u] = num[u] / den[u];
+  store_row<CPT>(o, (long long)b * o.cap + gblock, v, red);
+}
+
+static RowOut row_out(const lca_tensor& t) {
+  return RowOut{t.format, t.dim, t.rope_dims, t.cap, t.data, t.rope, t.scale};
+}
+
+static int threads_for(int c) {
+  int nt = ((c + 63) / 64) * 64;
+  return nt > kRowThreads ? kRowThreads : nt;
+}
+
+hipError_t launch_encode(const float* src, int B, long long rows, long long row0, const lca_tensor& dst,
+                         hipStream_t st) {
+  RowOut o = row_out(dst);
+  int nt = threads_for(dst.dim);
+  int cpt = (dst.dim + nt - 1) / nt;
+  dim3 grid((unsigned)rows, (unsigned)B);
+  if (cpt <= 1)
+    hipLaunchKernelGGL(encode_rows_kernel<1>, grid, dim3(nt), 0, st, src, rows, row0, o);
+  else if (cpt <= 2)
+    hipLaunchKernelGGL(encode_rows_kernel<2>, grid, dim3(nt), 0, st, src, rows, row0, o);
+  else
+    hipLaunchKernelGGL(encode_rows_kernel<4>, grid, dim3(nt), 0, st, src, rows, row0, o);
+  return hipGetLastError();
+}
+
+hipError_t launch_compress(const float* Ca, const float* Cb, const float* Za, const float* Zb, const float* Ba,
+                           const float* Bb, const float* tCb, const float* tZb, int B, long long n, int c, int m,
+                           int overlap, long long start_pos, const lca_tensor& out, hipStream_t st) {
+  CompressArgs a{Ca, Cb, Za, Zb, Ba, Bb, tCb, tZb, n, start_pos, c, m, overlap};
+  RowOut o = row_out(out);
+  int nt = threads_for(c);
+  int cpt = (c + nt - 1) / nt;
+  long long nb = (n + m - 1) / m;
+  dim3 grid((unsigned)nb, (unsigned)B);
+  if (cpt <= 1)
+    hipLaunchKernelGGL(compress_kernel<1>, grid, dim3(nt), 0, st, a, o);
+  else if (cpt <= 2)
+    hipLaunchKernelGGL(compress_kernel<2>, grid, dim3(nt), 0, st, a, o);
+  else
+    hipLaunchKernelGGL(compress_kernel<4>, grid, dim3(nt), 0, st, a, o);
+  return hipGetLastError();
+}
+
+}  // namespace lca

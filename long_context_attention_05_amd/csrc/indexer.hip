@@ -1,0 +1,250 @@
+// indexer.hip -- stage 2a, Lightning Indexer scores (paper notes "DeepSeek-V4: Towards Highly Efficient
+// Million-Token Context Intelligence", section 2.3 Eq. 16 and the Indexer excerpt; cosmocat page section 3;
+// 67808.cn explainer section 2: 64 indexer heads of dim 128, low-rank queries, FP4).
+//
+//   s[t][i] = sum_h w[t][h] * max(0, qI[t][h] . kI[i])      for visible i < min(floor(t/m), N)
+//
+// The per-head dots are a dense contraction [heads x DI] x [DI x entries], so the 64x128 case runs on MFMA
+// (v_mfma_f32_32x32x16_bf16): each wave holds 64 keys in registers as the B operand and takes the queries
+// (A operand, heads as rows) from LDS, so one key load serves every query of the block (prefill) and the K
+// stream is read once (decode).  fp4 keys/queries are widened to bf16 in registers, which is exact (a 2-bit
+// significand times a power of two).  Other shapes and fp32 inputs use a vector-ALU kernel.
+//
+// Both kernels reduce the heads the same way so that exact dots give bit-identical scores:
+//   p[h] = fl32(w[h] * max(0, d[h])), then a halving tree a[j] += a[j + L/2] over L = 64, 32, ..., 2
+// (zero padded to a power of two).  Scores are written to the workspace as order-preserving uint32 keys.
+#include "lca_device.h"
+#include "lca_internal.h"
+
+namespace lca {
+
+
+__host__ __device__ __forceinline__ int nvis_of(long long t, int m, int N) {
+  long long v = t / m;
+  return (int)(v < N ? v : N);
+}
+
+// ------------------------------------------------------------------------------------------------
+// vector-ALU kernel: any HI <= 64, DI <= 128, formats F32 / BF16 / FP4
+// ------------------------------------------------------------------------------------------------
+constexpr int kSimtTile = 32;
+
+__device__ __forceinline__ float load_elem(const lca_tensor& t, long long row, int j) {
+  if (t.format == LCA_F32) return ((const float*)t.data)[row * t.dim + j];
+  if (t.format == LCA_BF16) return bf16_to_f32(((const uint16_t*)t.data)[row * t.dim + j]);
+  // FP4
+  uint32_t byte = ((const uint8_t*)t.data)[row * (t.dim / 2) + (j >> 1)];
+  uint32_t code = (j & 1) ? (byte >> 4) : (byte & 15u);
+  int e = (int)((const uint8_t*)t.scale)[row * (t.dim / 16) + (j >> 4)] - 127;
+  return fp4_value(code) * exp2i(e);
+}
+
+__global__ __launch_bounds__(256) void idx_score_simt(IdxArgs a) {
+#pragma clang fp contract(off)
+  __shared__ float q_s[64 * 128];
+  __shared__ float k_s[kSimtTile * 129];
+  __shared__ float p_s[kSimtTile * 65];
+  const int b = blockIdx.z, r = blockIdx.y;
+  const long long t = a.q_start + r;
+  const int nvis = nvis_of(t, a.m, a.N);
+  const int e0 = blockIdx.x * kSimtTile;
+  if (e0 >= nvis) return;
+  const int HI = a.HI, DI = a.DI;
+  const long long qrow0 = ((long long)b * a.Sq + r) * HI;
+  for (int x = threadIdx.x; x < HI * DI; x += blockDim.x) q_s[x] = load_elem(a.q, qrow0 + x / DI, x % DI);
+  for (int x = threadIdx.x; x < kSimtTile * DI; x += blockDim.x) {
+    int e = x / DI, j = x % DI;
+    k_s[e * 129 + j] = (e0 + e < nvis) ? load_elem(a.k, (long long)b * a.k.cap + e0 + e, j) : 0.0f;
+  }
+  __syncthreads();
+  const float* wr = a.w + ((long long)b * a.Sq + r) * HI;
+  const int e = threadIdx.x % kSimtTile;
+  for (int h = threadIdx.x / kSimtTile; h < HI; h += blockDim.x / kSimtTile) {
+    float d = 0.0f;
+    for (int j = 0; j < DI; ++j) d = fmaf(q_s[h * DI + j], k_s[e * 129 + j], d);
+    p_s[e * 65 + h] = wr[h] * fmaxf(d, 0.0f);
+  }
+  __syncthreads();
+  if (threadIdx.x < kSimtTile && e0 + threadIdx.x < nvis) {
+    int P = 1;
+    while (P < HI) P <<= 1;
+    float v[64];
+    for (int h = 0; h < P; ++h) v[h] = (h < HI) ? p_s[threadIdx.x * 65 + h] : 0.0f;
+    for (int L = P; L > 1; L >>= 1)
+      for (int j = 0; j < L / 2; ++j) v[j] = v[j] + v[j + L / 2];
+    a.keys[((long long)b * a.Sq + r) * a.N + e0 + threadIdx.x] = score_key(v[0]);
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
+// MFMA kernel: HI = 64, DI = 128, BF16 or FP4 operands
+// ------------------------------------------------------------------------------------------------
+// Lane layouts of v_mfma_f32_32x32x16_bf16 (wave64):
+//   A (32 x 16): lane l holds A[l % 32][8 * (l / 32) + v], v = 0..7
+//   B (16 x 32): lane l holds B[8 * (l / 32) + v][l % 32]
+//   D (32 x 32): lane l, register r holds D[8 * (r / 4) + 4 * (l / 32) + (r % 4)][l % 32]
+// The contraction index of K-step s (0..7) is mapped to channel 64 * (l / 32) + 8 * s + v, the same for A and
+// B, so each lane reads 128 contiguous bytes of one key row.
+constexpr int kMfmaEntriesPerWave = 64;
+constexpr int kMfmaEntriesPerBlock = 4 * kMfmaEntriesPerWave;
+constexpr int kQStride = 136;  // bf16 elements per query head row in LDS (128 + 8 padding: no bank conflicts)
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// Eight consecutive fp4 codes (one little-endian uint32) with their scale, widened to eight bf16 (exact).
+__device__ __forceinline__ uint4 fp4x8_to_bf16x8(uint32_t codes, int e) {
+  const float s = exp2i(e);
+  uint4 r;
+  r.x = pack_bf16x2(fp4_value(codes & 15u) * s, fp4_value((codes >> 4) & 15u) * s);
+  r.y = pack_bf16x2(fp4_value((codes >> 8) & 15u) * s, fp4_value((codes >> 12) & 15u) * s);
+  r.z = pack_bf16x2(fp4_value((codes >> 16) & 15u) * s, fp4_value((codes >> 20) & 15u) * s);
+  r.w = pack_bf16x2(fp4_value((codes >> 24) & 15u) * s, fp4_value((codes >> 28) & 15u) * s);
+  return r;
+}
+
+// 64 consecutive channels [64g, 64g + 64) of one row as eight 8-channel chunks.
+template <int FMT>
+__device__ __forceinline__ void load_row64(const lca_tensor& t, long long row, int g, uint4 (&out)[8]) {
+  if (FMT == LCA_BF16) {
+    const uint4* p = (const uint4*)((const uint16_t*)t.data + row * 128 + 64 * g);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) out[s] = p[s];
+  } else {
+    const uint4* p = (const uint4*)((const uint8_t*)t.data + row * 64 + 32 * g);
+    uint4 c0 = p[0], c1 = p[1];
+    uint32_t sc = *(const uint32_t*)((const uint8_t*)t.scale + row * 8 + 4 * g);
+    uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) out[s] = fp4x8_to_bf16x8(cw[s], (int)((sc >> (8 * (s >> 1))) & 255u) - 127);
+  }
+}
+
+template <int FMT>
+__global__ __launch_bounds__(256) void idx_score_mfma(IdxArgs a, int qpb) {
+#pragma clang fp contract(off)
+  __shared__ uint16_t q_s[64 * kQStride];
+  __shared__ float w_s[64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = lane >> 5, col = lane & 31;
+  const int b = blockIdx.z;
+  const int e0 = blockIdx.x * kMfmaEntriesPerBlock + wave * kMfmaEntriesPerWave;
+  const int r_begin = blockIdx.y * qpb;
+  const int r_end = min(r_begin + qpb, a.Sq);
+  const int nvis_last = nvis_of(a.q_start + r_end - 1, a.m, a.N);
+  if (blockIdx.x * kMfmaEntriesPerBlock >= nvis_last) return;  // whole block invisible to every query
+
+  // keys of this wave: two 32-entry column tiles, B operand for 8 K-steps each
+  bf16x8_t kb[2][8];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int e = e0 + 32 * u + col;
+    uint4 raw[8];
+    if (e < nvis_last) {
+      load_row64<FMT>(a.k, (long long)b * a.k.cap + e, g, raw);
+    } else {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) raw[s] = make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) kb[u][s] = __builtin_bit_cast(bf16x8_t, raw[s]);
+  }
+
+  for (int r = r_begin; r < r_end; ++r) {
+    const long long t = a.q_start + r;
+    const int nvis = nvis_of(t, a.m, a.N);
+    if (blockIdx.x * kMfmaEntriesPerBlock >= nvis) continue;  // block-uniform
+    __syncthreads();
+    {  // stage the 64 x 128 query block (bf16) in LDS: 256 threads x 4 chunks of 8 channels
+      const long long qrow0 = ((long long)b * a.Sq + r) * 64;
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int chunk = threadIdx.x + 256 * it;  // 1024 chunks of 8 channels
+        const int h = chunk >> 4, c8 = chunk & 15;
+        uint4 v;
+        if (FMT == LCA_BF16) {
+          v = *(const uint4*)((const uint16_t*)a.q.data + (qrow0 + h) * 128 + 8 * c8);
+        } else {
+          uint32_t codes = *(const uint32_t*)((const uint8_t*)a.q.data + (qrow0 + h) * 64 + 4 * c8);
+          int e = (int)((const uint8_t*)a.q.scale)[(qrow0 + h) * 8 + (c8 >> 1)] - 127;
+          v = fp4x8_to_bf16x8(codes, e);
+        }
+        *(uint4*)&q_s[h * kQStride + 8 * c8] = v;
+      }
+      if (threadIdx.x < 64) w_s[threadIdx.x] = a.w[((long long)b * a.Sq + r) * 64 + threadIdx.x];
+    }
+    __syncthreads();
+    if (e0 >= nvis) continue;  // wave-uniform
+
+    f32x16_t acc[2][2];
+#pragma unroll
+    for (int T = 0; T < 2; ++T)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int x = 0; x < 16; ++x) acc[T][u][x] = 0.0f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+#pragma unroll
+      for (int T = 0; T < 2; ++T) {
+        const uint4 qv = *(const uint4*)&q_s[(32 * T + col) * kQStride + 64 * g + 8 * s];
+        const bf16x8_t qa = __builtin_bit_cast(bf16x8_t, qv);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) acc[T][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kb[u][s], acc[T][u], 0, 0, 0);
+      }
+    }
+    // epilogue: head h = 32T + 8(x/4) + 4g + (x%4) for register x; fixed halving tree over h
+    float wv[2][16];
+#pragma unroll
+    for (int T = 0; T < 2; ++T)
+#pragma unroll
+      for (int x = 0; x < 16; ++x) wv[T][x] = w_s[32 * T + 8 * (x >> 2) + 4 * g + (x & 3)];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      float l1[16];
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {  // level 1: h + 32
+        float p0 = wv[0][x] * fmaxf(acc[0][u][x], 0.0f);
+        float p1 = wv[1][x] * fmaxf(acc[1][u][x], 0.0f);
+        l1[x] = p0 + p1;
+      }
+      float l2[8], l3[4], l4[4];
+#pragma unroll
+      for (int x = 0; x < 8; ++x) l2[x] = l1[x] + l1[x + 8];  // h + 16
+#pragma unroll
+      for (int x = 0; x < 4; ++x) l3[x] = l2[x] + l2[x + 4];  // h + 8
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {  // h + 4: the partner lane holds the other 4g half
+        float o = __shfl_xor(l3[x], 32, 64);
+        l4[x] = (g == 0) ? (l3[x] + o) : (o + l3[x]);
+      }
+      float l5_0 = l4[0] + l4[2], l5_1 = l4[1] + l4[3];  // h + 2
+      float s = l5_0 + l5_1;                             // h + 1
+      const int e = e0 + 32 * u + col;
+      if (g == 0 && e < nvis) a.keys[((long long)b * a.Sq + r) * a.N + e] = score_key(s);
+    }
+  }
+}
+
+hipError_t launch_indexer_scores(const IdxArgs& a, hipStream_t st) {
+  const int nvis_max = nvis_of(a.q_start + a.Sq - 1, a.m, a.N);
+  if (nvis_max <= 0) return hipSuccess;
+  const bool mfma = a.HI == 64 && a.DI == 128 && a.q.format == a.k.format &&
+                    (a.q.format == LCA_BF16 || a.q.format == LCA_FP4);
+  if (mfma) {
+    const int qpb = a.Sq >= 16 ? 16 : a.Sq;
+    dim3 grid((unsigned)((nvis_max + kMfmaEntriesPerBlock - 1) / kMfmaEntriesPerBlock),
+              (unsigned)((a.Sq + qpb - 1) / qpb), (unsigned)a.B);
+    if (a.q.format == LCA_BF16)
+      hipLaunchKernelGGL(idx_score_mfma<LCA_BF16>, grid, dim3(256), 0, st, a, qpb);
+    else
+      hipLaunchKernelGGL(idx_score_mfma<LCA_FP4>, grid, dim3(256), 0, st, a, qpb);
+  } else {
+    dim3 grid((unsigned)((nvis_max + kSimtTile - 1) / kSimtTile), (unsigned)a.Sq, (unsigned)a.B);
+    hipLaunchKernelGGL(idx_score_simt, grid, dim3(256), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace lca

@@ -1,0 +1,63 @@
+// lca_internal.h -- argument blocks and launchers shared between the entry points (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/lca.h"
+
+namespace lca {
+
+// stage 1 + codec (compress.hip)
+hipError_t launch_encode(const float* src, int B, long long rows, long long row0, const lca_tensor& dst,
+                         hipStream_t st);
+hipError_t launch_compress(const float* Ca, const float* Cb, const float* Za, const float* Zb, const float* Ba,
+                           const float* Bb, const float* tCb, const float* tZb, int B, long long n, int c, int m,
+                           int overlap, long long start_pos, const lca_tensor& out, hipStream_t st);
+
+// stage 2a, indexer scores (indexer.hip)
+struct IdxArgs {
+  lca_tensor q, k;
+  const float* w;
+  uint32_t* keys;  // [B][Sq][N] order-preserving score keys (workspace)
+  int B, Sq, HI, DI, N, m;
+  long long q_start;
+};
+hipError_t launch_indexer_scores(const IdxArgs& a, hipStream_t st);
+
+// stage 2b, exact top-k (topk.hip)
+struct SelArgs {
+  const uint32_t* keys;  // [rows][N]
+  int32_t* idx_out;      // [rows][k]
+  float* score_out;      // nullable [rows][k]
+  int rows, Sq, N, m, k;
+  long long q_start;
+};
+hipError_t launch_topk(const SelArgs& a, hipStream_t st);
+
+// stages 3/4, attention (attn.hip)
+struct AttnArgs {
+  const void* q;
+  int q_format;
+  lca_tensor comp, raw;
+  int N;
+  long long raw_start;
+  int S_raw;
+  const int32_t* idx;  // sparse mode: [B][Sq][k]
+  int k;
+  int hca_m;  // > 0: dense over the visible entries
+  const float* sink;
+  int B, Sq, H, D, window;
+  float scale;
+  long long q_start;
+  void* out;
+  int out_format;
+  float* lse;
+  int n_splits, split_len;
+  float* part_o;   // [B][Sq][n_splits][H][D]
+  float* part_ml;  // [B][Sq][n_splits][H][2]
+};
+bool attn_uses_mfma(int H, int D, int q_format, int kv_format);
+hipError_t launch_attn(AttnArgs a, hipStream_t st);
+
+}  // namespace lca

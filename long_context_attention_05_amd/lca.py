@@ -1,0 +1,177 @@
+"""ctypes binding of liblca.so (include/lca.h).
+
+Argument marshalling only: every step runs in the HIP kernels of liblca.so.  Torch tensors supply device memory
+and the current stream.  If the library is not built, importing this module raises -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liblca.so")
+
+LCA_F32, LCA_BF16, LCA_MIXED_FP8, LCA_FP4 = 0, 1, 2, 3
+FORMATS = {"f32": LCA_F32, "bf16": LCA_BF16, "mixed": LCA_MIXED_FP8, "fp4": LCA_FP4}
+STATUS = {0: "LCA_OK", -1: "LCA_ERR_INVALID_ARG", -2: "LCA_ERR_UNSUPPORTED", -3: "LCA_ERR_WORKSPACE",
+          -4: "LCA_ERR_ALIGNMENT", -5: "LCA_ERR_HIP"}
+
+
+class LcaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__("%s failed: %s" % (fn, STATUS.get(status, status)))
+        self.status = status
+
+
+class lca_tensor(ctypes.Structure):
+    _fields_ = [("format", ctypes.c_int), ("dim", ctypes.c_int), ("rope_dims", ctypes.c_int),
+                ("cap", ctypes.c_longlong), ("data", ctypes.c_void_p), ("rope", ctypes.c_void_p),
+                ("scale", ctypes.c_void_p)]
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError("liblca.so is not built (run long_context_attention_05_amd/build.py); no fallback exists")
+_lib = ctypes.CDLL(LIB_PATH)
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_L = ctypes.c_longlong
+_F = ctypes.c_float
+_S = ctypes.c_size_t
+
+_lib.lca_status_string.argtypes = [_I]
+_lib.lca_status_string.restype = ctypes.c_char_p
+_lib.lca_encode.argtypes = [_P, _I, _L, _L, lca_tensor, _P]
+_lib.kv_compress.argtypes = [_P] * 8 + [_I, _L, _I, _I, _I, _L, lca_tensor, _P]
+_lib.indexer_score_topk_workspace_size.argtypes = [_I, _I, _I, _I]
+_lib.indexer_score_topk_workspace_size.restype = _S
+_lib.indexer_score_topk.argtypes = [lca_tensor, _P, lca_tensor] + [_I] * 7 + [_L, _P, _P, _P, _S, _P]
+_lib.sparse_mqa_attn_workspace_size.argtypes = [_I] * 5
+_lib.sparse_mqa_attn_workspace_size.restype = _S
+_lib.sparse_mqa_attn.argtypes = [_P, _I, lca_tensor, _I, lca_tensor, _L, _I, _P, _I, _P] + [_I] * 5 + [
+    _F, _L, _P, _I, _P, _P, _S, _P]
+_lib.hca_attn_workspace_size.argtypes = [_I] * 5
+_lib.hca_attn_workspace_size.restype = _S
+_lib.hca_attn.argtypes = [_P, _I, lca_tensor, _I, _I, lca_tensor, _L, _I, _P] + [_I] * 5 + [
+    _F, _L, _P, _I, _P, _P, _S, _P]
+
+
+def library():
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return _lib.lca_status_string(int(status)).decode()
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(fn: str, rc: int):
+    if rc != 0:
+        raise LcaError(fn, rc)
+
+
+class CacheTensor:
+    """Device storage of one lca_tensor (owns its torch tensors): `cap` rows per sequence for B sequences."""
+
+    def __init__(self, fmt: str, B: int, cap: int, dim: int, rope: int = 0, device="cuda"):
+        import torch
+        self.fmt, self.B, self.cap, self.dim, self.rope = fmt, B, cap, dim, rope
+        rows = B * cap
+        self.rope_t = self.scale_t = None
+        if fmt == "f32":
+            self.data = torch.empty((rows, dim), dtype=torch.float32, device=device)
+        elif fmt == "bf16":
+            self.data = torch.empty((rows, dim), dtype=torch.int16, device=device)
+        elif fmt == "mixed":
+            self.data = torch.empty((rows, dim - rope), dtype=torch.uint8, device=device)
+            self.rope_t = torch.empty((rows, rope), dtype=torch.int16, device=device)
+            self.scale_t = torch.empty((rows,), dtype=torch.float32, device=device)
+        elif fmt == "fp4":
+            self.data = torch.empty((rows, dim // 2), dtype=torch.uint8, device=device)
+            self.scale_t = torch.empty((rows, dim // 16), dtype=torch.uint8, device=device)
+        else:
+            raise ValueError(fmt)
+
+    def desc(self) -> lca_tensor:
+        return lca_tensor(FORMATS[self.fmt], self.dim, self.rope, self.cap, _ptr(self.data), _ptr(self.rope_t),
+                          _ptr(self.scale_t))
+
+    def host(self) -> dict:
+        """Copy to host numpy arrays (for comparisons), as a dict of raw storage arrays."""
+        import numpy as np
+        d = dict(fmt=self.fmt, dim=self.dim, rope=self.rope, cap=self.cap)
+        d["data"] = self.data.cpu().numpy()
+        if self.fmt == "bf16":
+            d["data"] = d["data"].view(np.uint16)
+        d["rope_data"] = None if self.rope_t is None else self.rope_t.cpu().numpy().view(np.uint16)
+        d["scale"] = None if self.scale_t is None else self.scale_t.cpu().numpy()
+        return d
+
+
+def plain_desc(t, fmt: str, dim: int, cap: int) -> lca_tensor:
+    """Descriptor over an existing dense f32/bf16 tensor (rows = B * cap)."""
+    return lca_tensor(FORMATS[fmt], dim, 0, cap, _ptr(t), None, None)
+
+
+# ----------------------------------------------------------------------------------------------------
+# entry points (names as in include/lca.h)
+# ----------------------------------------------------------------------------------------------------
+def lca_encode(src, B: int, rows: int, row0: int, dst: lca_tensor, stream=None):
+    _check("lca_encode", _lib.lca_encode(_ptr(src), B, rows, row0, dst, _stream(stream)))
+
+
+def kv_compress(Ca, Cb, Za, Zb, Ba, Bb, tail_Cb, tail_Zb, B: int, n: int, c: int, m: int, overlap: bool,
+                start_pos: int, out: lca_tensor, stream=None):
+    _check("kv_compress", _lib.kv_compress(_ptr(Ca), _ptr(Cb), _ptr(Za), _ptr(Zb), _ptr(Ba), _ptr(Bb), _ptr(tail_Cb),
+                                           _ptr(tail_Zb), B, n, c, m, int(bool(overlap)), start_pos, out,
+                                           _stream(stream)))
+
+
+def indexer_score_topk_workspace_size(B: int, Sq: int, N: int, k: int) -> int:
+    return int(_lib.indexer_score_topk_workspace_size(B, Sq, N, k))
+
+
+def indexer_score_topk(qI: lca_tensor, w, kI: lca_tensor, B: int, Sq: int, HI: int, DI: int, N: int, m: int, k: int,
+                       q_start_pos: int, idx_out, score_out, ws, ws_bytes: int, stream=None):
+    _check("indexer_score_topk", _lib.indexer_score_topk(qI, _ptr(w), kI, B, Sq, HI, DI, N, m, k, q_start_pos,
+                                                         _ptr(idx_out), _ptr(score_out), _ptr(ws), ws_bytes,
+                                                         _stream(stream)))
+
+
+def sparse_mqa_attn_workspace_size(B: int, Sq: int, H: int, D: int, max_entries: int) -> int:
+    return int(_lib.sparse_mqa_attn_workspace_size(B, Sq, H, D, max_entries))
+
+
+def sparse_mqa_attn(q, q_format: int, kv_comp: lca_tensor, N: int, kv_raw: lca_tensor, raw_start_pos: int, S_raw: int,
+                    idx, k: int, sink, B: int, Sq: int, H: int, D: int, window: int, scale: float, q_start_pos: int,
+                    out, out_format: int, lse_out, ws, ws_bytes: int, stream=None):
+    _check("sparse_mqa_attn", _lib.sparse_mqa_attn(_ptr(q), q_format, kv_comp, N, kv_raw, raw_start_pos, S_raw,
+                                                   _ptr(idx), k, _ptr(sink), B, Sq, H, D, window, scale, q_start_pos,
+                                                   _ptr(out), out_format, _ptr(lse_out), _ptr(ws), ws_bytes,
+                                                   _stream(stream)))
+
+
+def hca_attn_workspace_size(B: int, Sq: int, H: int, D: int, max_entries: int) -> int:
+    return int(_lib.hca_attn_workspace_size(B, Sq, H, D, max_entries))
+
+
+def hca_attn(q, q_format: int, kv_comp: lca_tensor, N: int, m: int, kv_raw: lca_tensor, raw_start_pos: int, S_raw: int,
+             sink, B: int, Sq: int, H: int, D: int, window: int, scale: float, q_start_pos: int, out, out_format: int,
+             lse_out, ws, ws_bytes: int, stream=None):
+    _check("hca_attn", _lib.hca_attn(_ptr(q), q_format, kv_comp, N, m, kv_raw, raw_start_pos, S_raw, _ptr(sink), B, Sq,
+                                     H, D, window, scale, q_start_pos, _ptr(out), out_format, _ptr(lse_out), _ptr(ws),
+                                     ws_bytes, _stream(stream)))
