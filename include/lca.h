@@ -70,6 +70,9 @@ typedef struct {
 /* Human-readable name of a status code (static string). */
 const char* lca_status_string(int status);
 
+/* The HIP runtime's message for the last LCA_ERR_HIP returned on the calling host thread (static string). */
+const char* lca_last_hip_error(void);
+
 /*
  * lca_encode -- quantise-on-write: encode fp32 rows into a cache tensor's format (the codec of the
  * mixed-precision cache).  src: float [B][rows][dst.dim].  Writes rows [row0, row0 + rows) of every
@@ -122,6 +125,15 @@ int kv_compress(const float* Ca, const float* Cb, const float* Za, const float* 
  *         DI > 256, q/k formats not both float-like or both FP4), WORKSPACE, ALIGNMENT.
  */
 size_t indexer_score_topk_workspace_size(int B, int Sq, int N, int k);
+
+/*
+ * lca_set_score_events -- profiling hook for the dominant kernel.  While both are non-NULL, every
+ * indexer_score_topk call made from the calling host thread records ev_begin (a hipEvent_t) on its stream just
+ * before its scoring kernel and ev_end just after it, so the caller can time that kernel with
+ * hipEventElapsedTime.  Pass NULL, NULL to stop.  The events are owned by the caller.
+ */
+void lca_set_score_events(void* ev_begin, void* ev_end);
+
 int indexer_score_topk(lca_tensor qI, const float* w, lca_tensor kI, int B, int Sq, int HI, int DI, int N, int m, int k,
                        long long q_start_pos, int32_t* idx_out, float* score_out, void* ws, size_t ws_bytes,
                        void* stream);

@@ -39,7 +39,15 @@ int check_tensor(const lca_tensor& t, bool allow_fp4, bool allow_mixed) {
   return LCA_OK;
 }
 
-int hip_status(hipError_t e) { return e == hipSuccess ? LCA_OK : LCA_ERR_HIP; }
+thread_local hipError_t t_last_hip = hipSuccess;
+
+int hip_status(hipError_t e) {
+  if (e != hipSuccess) t_last_hip = e;
+  return e == hipSuccess ? LCA_OK : LCA_ERR_HIP;
+}
+
+// profiling hook (per host thread): events recorded around the indexer scoring kernel
+thread_local hipEvent_t t_ev_begin = nullptr, t_ev_end = nullptr;
 
 // Split plan of the attention: rows = B * Sq query rows, each with up to max_entries list positions.
 void attn_plan(int B, int Sq, int H, int max_entries, int& n_splits, int& split_len) {
@@ -52,7 +60,8 @@ void attn_plan(int B, int Sq, int H, int max_entries, int& n_splits, int& split_
   len = (len + 31) / 32 * 32;
   if (len < 64) len = 64;
   long long ns = (max_entries + len - 1) / len;
-  const long long max_splits = 16000 / (H > 0 ? H : 1) - 1;  // merge keeps H * (splits + 1) floats in LDS
+  (void)H;
+  const long long max_splits = 4096;  // the merge keeps one weight per split in LDS
   if (ns > max_splits) {
     ns = max_splits;
     len = (max_entries + ns - 1) / ns;
@@ -193,6 +202,13 @@ int kv_compress(const float* Ca, const float* Cb, const float* Za, const float* 
                                     start_pos, out, (hipStream_t)stream));
 }
 
+const char* lca_last_hip_error(void) { return hipGetErrorString(t_last_hip); }
+
+void lca_set_score_events(void* ev_begin, void* ev_end) {
+  t_ev_begin = (hipEvent_t)ev_begin;
+  t_ev_end = (hipEvent_t)ev_end;
+}
+
 size_t indexer_score_topk_workspace_size(int B, int Sq, int N, int k) {
   (void)k;
   if (B <= 0 || Sq <= 0 || N <= 0) return kAlign;
@@ -217,8 +233,11 @@ int indexer_score_topk(lca_tensor qI, const float* w, lca_tensor kI, int B, int 
   hipStream_t st = (hipStream_t)stream;
   IdxArgs a{qI, kI, w, (uint32_t*)ws, B, Sq, HI, DI, N, m, q_start_pos};
   if (N > 0) {
+    const bool timed = t_ev_begin && t_ev_end;
+    if (timed && hipEventRecord(t_ev_begin, st) != hipSuccess) return LCA_ERR_HIP;
     rc = hip_status(launch_indexer_scores(a, st));
     if (rc) return rc;
+    if (timed && hipEventRecord(t_ev_end, st) != hipSuccess) return LCA_ERR_HIP;
   }
   SelArgs s{(const uint32_t*)ws, idx_out, score_out, B * Sq, Sq, N, m, k, q_start_pos};
   return hip_status(launch_topk(s, st));

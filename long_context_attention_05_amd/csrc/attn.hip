@@ -378,45 +378,56 @@ __global__ __launch_bounds__(256) void attn_simt_kernel(AttnArgs a) {
 // ------------------------------------------------------------------------------------------------
 // merge of splits + sink
 // ------------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
-  extern __shared__ float coef[];  // [H][n_splits] weights, then [H] 1/den
-  const int r = blockIdx.x, b = blockIdx.y;
+// One workgroup per (head, query row, sequence): combine the splits' (max, sum, o) with the sink.
+constexpr int kMergeThreads = 128;
+__global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
+  extern __shared__ float wsplit[];  // [n_splits] weights e^(m_s - M)
+  __shared__ float red[kMergeThreads / 64];
+  __shared__ float stat[2];
+  const int h = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
   const int H = a.H, D = a.D, S = a.n_splits;
   const long long item0 = ((long long)b * a.Sq + r) * S;
-  float* inv = coef + H * S;
-  for (int h = threadIdx.x; h < H; h += blockDim.x) {
-    const float z = a.sink[h];
-    float M = z;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, a.part_ml[((item0 + s) * H + h) * 2 + 0]);
-    float den = 0.0f;
-    if (M != -INFINITY) {
-      den = (z == -INFINITY) ? 0.0f : __expf(z - M);
-      for (int s = 0; s < S; ++s) {
-        const float ms = a.part_ml[((item0 + s) * H + h) * 2 + 0];
-        const float w = (ms == -INFINITY) ? 0.0f : __expf(ms - M);
-        coef[h * S + s] = w;
-        den += w * a.part_ml[((item0 + s) * H + h) * 2 + 1];
-      }
-    } else {
-      for (int s = 0; s < S; ++s) coef[h * S + s] = 0.0f;
-    }
-    inv[h] = den > 0.0f ? 1.0f / den : 0.0f;
+  const float z = a.sink[h];
+  // M = max(z, m_s)
+  float mloc = -INFINITY;
+  for (int s = threadIdx.x; s < S; s += blockDim.x) mloc = fmaxf(mloc, a.part_ml[((item0 + s) * H + h) * 2 + 0]);
+  mloc = wave_max(mloc);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mloc;
+  __syncthreads();
+  float M = z;
+  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) M = fmaxf(M, red[i]);
+  __syncthreads();
+  // den = e^(z - M) + sum_s e^(m_s - M) l_s
+  float dloc = 0.0f;
+  for (int s = threadIdx.x; s < S; s += blockDim.x) {
+    const float ms = a.part_ml[((item0 + s) * H + h) * 2 + 0];
+    const float wgt = (M == -INFINITY || ms == -INFINITY) ? 0.0f : __expf(ms - M);
+    wsplit[s] = wgt;
+    dloc += wgt * a.part_ml[((item0 + s) * H + h) * 2 + 1];
+  }
+  dloc = wave_sum(dloc);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = dloc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float den = (M == -INFINITY || z == -INFINITY) ? 0.0f : __expf(z - M);
+    for (int i = 0; i < (int)(blockDim.x >> 6); ++i) den += red[i];
+    stat[0] = den > 0.0f ? 1.0f / den : 0.0f;
     if (a.lse) a.lse[((long long)b * a.Sq + r) * H + h] = (M == -INFINITY) ? -INFINITY : M + __logf(den);
   }
   __syncthreads();
-  for (int x = threadIdx.x; x < H * D; x += blockDim.x) {
-    const int h = x / D;
+  const float inv = stat[0];
+  const long long ob = (((long long)b * a.Sq + r) * H + h) * D;
+  for (int x = threadIdx.x; x < D; x += blockDim.x) {
     float acc = 0.0f;
     for (int s = 0; s < S; ++s) {
-      const float w = coef[h * S + s];
-      if (w != 0.0f) acc = fmaf(w, a.part_o[(item0 + s) * H * D + x], acc);
+      const float wgt = wsplit[s];
+      if (wgt != 0.0f) acc = fmaf(wgt, a.part_o[((item0 + s) * H + h) * D + x], acc);
     }
-    const float v = acc * inv[h];
-    const long long oi = ((long long)b * a.Sq + r) * H * D + x;
+    const float v = acc * inv;
     if (a.out_format == LCA_F32)
-      ((float*)a.out)[oi] = v;
+      ((float*)a.out)[ob + x] = v;
     else
-      ((uint16_t*)a.out)[oi] = f32_to_bf16(v);
+      ((uint16_t*)a.out)[ob + x] = f32_to_bf16(v);
   }
 }
 
@@ -430,6 +441,7 @@ bool attn_uses_mfma(int H, int D, int q_format, int kv_format) {
 hipError_t launch_attn(AttnArgs a, hipStream_t st) {
   const bool mfma = attn_uses_mfma(a.H, a.D, a.q_format, a.comp.format);
   dim3 grid((unsigned)a.n_splits, (unsigned)a.Sq, (unsigned)a.B);
+  clear_stale_error();
   if (mfma) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) dev = 0;
@@ -451,8 +463,9 @@ hipError_t launch_attn(AttnArgs a, hipStream_t st) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_splits == 1) return e;
-  const size_t lds = sizeof(float) * ((size_t)a.H * a.n_splits + a.H);
-  hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)a.Sq, (unsigned)a.B), dim3(256), lds, st, a);
+  const size_t lds = sizeof(float) * (size_t)a.n_splits;
+  hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)a.H, (unsigned)a.Sq, (unsigned)a.B), dim3(kMergeThreads), lds,
+                     st, a);
   return hipGetLastError();
 }
 

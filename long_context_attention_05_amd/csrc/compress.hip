@@ -199,6 +199,7 @@ hipError_t launch_encode(const float* src, int B, long long rows, long long row0
   int nt = threads_for(dst.dim);
   int cpt = (dst.dim + nt - 1) / nt;
   dim3 grid((unsigned)rows, (unsigned)B);
+  clear_stale_error();
   if (cpt <= 1)
     hipLaunchKernelGGL(encode_rows_kernel<1>, grid, dim3(nt), 0, st, src, rows, row0, o);
   else if (cpt <= 2)
@@ -217,6 +218,7 @@ hipError_t launch_compress(const float* Ca, const float* Cb, const float* Za, co
   int cpt = (c + nt - 1) / nt;
   long long nb = (n + m - 1) / m;
   dim3 grid((unsigned)nb, (unsigned)B);
+  clear_stale_error();
   if (cpt <= 1)
     hipLaunchKernelGGL(compress_kernel<1>, grid, dim3(nt), 0, st, a, o);
   else if (cpt <= 2)

@@ -227,12 +227,184 @@ __global__ __launch_bounds__(256) void idx_score_mfma(IdxArgs a, int qpb) {
   }
 }
 
+// ------------------------------------------------------------------------------------------------
+// decode MFMA kernel (one query row per sequence): the key stream is the whole cost, so keys move in
+// fully coalesced 16-byte loads (16 lanes per 256-byte key row) into a double-buffered LDS tile while the
+// previous tile is scored; the query block stays in registers for the whole entry range of the workgroup.
+// ------------------------------------------------------------------------------------------------
+constexpr int kDecTile = 128;      // entries per tile, 32 per wave
+constexpr int kKRowB = 272;        // LDS bytes per bf16 key row (256 + 16 padding)
+constexpr int kKRowF4 = 80;        // LDS bytes per fp4 key row (64 codes + 8 scales + 8 padding)
+
+template <int FMT>
+constexpr int dec_row_bytes() { return FMT == LCA_BF16 ? kKRowB : kKRowF4; }
+
+template <int FMT>
+__device__ __forceinline__ void dec_load_tile(const IdxArgs& a, int b, int e0, int nvis, uint4 (&v)[8]) {
+  const int tid = threadIdx.x;
+  if (FMT == LCA_BF16) {
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      const int c = tid + 256 * x, e = c >> 4, piece = c & 15;
+      v[x] = (e0 + e < nvis)
+                 ? *(const uint4*)((const uint8_t*)a.k.data + ((long long)b * a.k.cap + e0 + e) * 256 + 16 * piece)
+                 : make_uint4(0, 0, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int c = tid + 256 * x, e = c >> 2, piece = c & 3;
+      v[x] = (e0 + e < nvis)
+                 ? *(const uint4*)((const uint8_t*)a.k.data + ((long long)b * a.k.cap + e0 + e) * 64 + 16 * piece)
+                 : make_uint4(0, 0, 0, 0);
+    }
+    const int e = tid >> 1, half = tid & 1;
+    v[2].x = (e0 + e < nvis) ? *(const uint32_t*)((const uint8_t*)a.k.scale + ((long long)b * a.k.cap + e0 + e) * 8 +
+                                                  4 * half)
+                             : 0u;
+  }
+}
+
+template <int FMT>
+__device__ __forceinline__ void dec_store_tile(uint8_t* buf, const uint4 (&v)[8]) {
+  const int tid = threadIdx.x;
+  if (FMT == LCA_BF16) {
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      const int c = tid + 256 * x, e = c >> 4, piece = c & 15;
+      *(uint4*)(buf + e * kKRowB + 16 * piece) = v[x];
+    }
+  } else {
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int c = tid + 256 * x, e = c >> 2, piece = c & 3;
+      *(uint4*)(buf + e * kKRowF4 + 16 * piece) = v[x];
+    }
+    const int e = tid >> 1, half = tid & 1;
+    *(uint32_t*)(buf + e * kKRowF4 + 64 + 4 * half) = v[2].x;
+  }
+}
+
+template <int FMT>
+__global__ __launch_bounds__(256, 2) void idx_score_decode(IdxArgs a, int tiles_per_block) {
+#pragma clang fp contract(off)
+  extern __shared__ __attribute__((aligned(16))) uint8_t dec_lds[];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = lane >> 5, col = lane & 31;
+  const int b = blockIdx.y;
+  const int nvis = nvis_of(a.q_start, a.m, a.N);
+  const int ntiles = (nvis + kDecTile - 1) / kDecTile;
+  const int t_begin = blockIdx.x * tiles_per_block;
+  const int t_end = min(t_begin + tiles_per_block, ntiles);
+  if (t_begin >= t_end) return;
+  constexpr int RB = dec_row_bytes<FMT>();
+
+  uint4 pre[8];
+  dec_load_tile<FMT>(a, b, t_begin * kDecTile, nvis, pre);
+
+  // query block (64 heads x 128) as the A operand: lane holds head 32T + col, channels 64g + 8s .. + 7
+  bf16x8_t qa[2][8];
+  float wv[2][16];
+  {
+    const long long qrow0 = (long long)b * 64;
+#pragma unroll
+    for (int T = 0; T < 2; ++T) {
+      const long long row = qrow0 + 32 * T + col;
+      uint4 raw[8];
+      load_row64<FMT>(a.q, row, g, raw);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) qa[T][s] = __builtin_bit_cast(bf16x8_t, raw[s]);
+#pragma unroll
+      for (int x = 0; x < 16; ++x) wv[T][x] = a.w[(long long)b * 64 + 32 * T + 8 * (x >> 2) + 4 * g + (x & 3)];
+    }
+  }
+  dec_store_tile<FMT>(dec_lds, pre);
+  __syncthreads();
+
+  for (int tt = t_begin; tt < t_end; ++tt) {
+    const int cur = (tt - t_begin) & 1;
+    if (tt + 1 < t_end) dec_load_tile<FMT>(a, b, (tt + 1) * kDecTile, nvis, pre);
+
+    // B operand: the wave's 32 keys, channels 64g + 8s .. + 7
+    bf16x8_t kb[8];
+    const uint8_t* rowp = dec_lds + cur * (kDecTile * RB) + (32 * wave + col) * RB;
+    if (FMT == LCA_BF16) {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) kb[s] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(rowp + 128 * g + 16 * s));
+    } else {
+      const uint4 c0 = *(const uint4*)(rowp + 32 * g), c1 = *(const uint4*)(rowp + 32 * g + 16);
+      const uint32_t sc = *(const uint32_t*)(rowp + 64 + 4 * g);
+      const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        kb[s] = __builtin_bit_cast(bf16x8_t, fp4x8_to_bf16x8(cw[s], (int)((sc >> (8 * (s >> 1))) & 255u) - 127));
+    }
+    f32x16_t acc[2];
+#pragma unroll
+    for (int T = 0; T < 2; ++T)
+#pragma unroll
+      for (int x = 0; x < 16; ++x) acc[T][x] = 0.0f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int T = 0; T < 2; ++T) acc[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[T][s], kb[s], acc[T], 0, 0, 0);
+
+    // fixed halving tree over the 64 heads (see the header comment)
+    float l1[16];
+#pragma unroll
+    for (int x = 0; x < 16; ++x) {
+      const float p0 = wv[0][x] * fmaxf(acc[0][x], 0.0f);
+      const float p1 = wv[1][x] * fmaxf(acc[1][x], 0.0f);
+      l1[x] = p0 + p1;
+    }
+    float l2[8], l3[4], l4[4];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) l2[x] = l1[x] + l1[x + 8];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) l3[x] = l2[x] + l2[x + 4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const float o = __shfl_xor(l3[x], 32, 64);
+      l4[x] = (g == 0) ? (l3[x] + o) : (o + l3[x]);
+    }
+    const float s = (l4[0] + l4[2]) + (l4[1] + l4[3]);
+    const int e = tt * kDecTile + 32 * wave + col;
+    if (g == 0 && e < nvis) a.keys[(long long)b * a.N + e] = score_key(s);
+
+    if (tt + 1 < t_end) dec_store_tile<FMT>(dec_lds + (cur ^ 1) * (kDecTile * RB), pre);
+    __syncthreads();
+  }
+}
+
+static bool g_dec_attr[64];
+
 hipError_t launch_indexer_scores(const IdxArgs& a, hipStream_t st) {
   const int nvis_max = nvis_of(a.q_start + a.Sq - 1, a.m, a.N);
   if (nvis_max <= 0) return hipSuccess;
+  clear_stale_error();
   const bool mfma = a.HI == 64 && a.DI == 128 && a.q.format == a.k.format &&
                     (a.q.format == LCA_BF16 || a.q.format == LCA_FP4);
-  if (mfma) {
+  if (mfma && a.Sq == 1) {
+    const int ntiles = (nvis_max + kDecTile - 1) / kDecTile;
+    int bps = (512 + a.B - 1) / a.B;  // about two workgroups per CU over the whole batch
+    if (bps > ntiles) bps = ntiles;
+    const int tpb = (ntiles + bps - 1) / bps;
+    bps = (ntiles + tpb - 1) / tpb;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    if (dev >= 0 && dev < 64 && !g_dec_attr[dev]) {
+      hipError_t e = hipFuncSetAttribute((const void*)idx_score_decode<LCA_BF16>,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kDecTile * kKRowB);
+      if (e != hipSuccess) return e;
+      g_dec_attr[dev] = true;
+    }
+    if (a.q.format == LCA_BF16)
+      hipLaunchKernelGGL(idx_score_decode<LCA_BF16>, dim3((unsigned)bps, (unsigned)a.B), dim3(256),
+                         2 * kDecTile * kKRowB, st, a, tpb);
+    else
+      hipLaunchKernelGGL(idx_score_decode<LCA_FP4>, dim3((unsigned)bps, (unsigned)a.B), dim3(256),
+                         2 * kDecTile * kKRowF4, st, a, tpb);
+  } else if (mfma) {
     const int qpb = a.Sq >= 16 ? 16 : a.Sq;
     dim3 grid((unsigned)((nvis_max + kMfmaEntriesPerBlock - 1) / kMfmaEntriesPerBlock),
               (unsigned)((a.Sq + qpb - 1) / qpb), (unsigned)a.B);

@@ -8,6 +8,13 @@
 
 namespace lca {
 
+// Drops an error left in the runtime by an earlier, unrelated call, so that the status read after a launch
+// belongs to that launch.
+inline void clear_stale_error() {
+  hipError_t e = hipGetLastError();
+  (void)e;
+}
+
 // stage 1 + codec (compress.hip)
 hipError_t launch_encode(const float* src, int B, long long rows, long long row0, const lca_tensor& dst,
                          hipStream_t st);

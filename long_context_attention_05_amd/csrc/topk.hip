@@ -20,15 +20,19 @@ constexpr int kLdsKeys = 32768;  // 128 KB of keys in LDS
 constexpr size_t kSelDynLds = (size_t)kLdsKeys * 4;
 
 
-// Inclusive scan over the block (1024 threads, one value each); `tot` receives the block total.
-__device__ __forceinline__ int block_incl_scan(int v, int* wsum, int& tot) {
+constexpr int kBorderCap = 2048;  // keys of the border bin kept in LDS for passes 2 and 3
+constexpr int kPerThread = 8;     // entries per thread in the ordered compaction
+
+// Exclusive scan over the block (1024 threads, one value each); `tot` receives the block total.
+__device__ __forceinline__ int block_excl_scan(int v, int* wsum, int& tot) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int incl = v;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    int n = __shfl_up(v, o, 64);
-    if (lane >= o) v += n;
+    int n = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += n;
   }
-  if (lane == 63) wsum[w] = v;
+  if (lane == 63) wsum[w] = incl;
   __syncthreads();
   int before = 0;
   tot = 0;
@@ -39,21 +43,41 @@ __device__ __forceinline__ int block_incl_scan(int v, int* wsum, int& tot) {
     tot += x;
   }
   __syncthreads();
-  return v + before;
+  return before + incl - v;
+}
+
+// Finds, among 2048 histogram bins read in descending order, the bin holding the need-th largest key.
+// Returns the bin; *above receives the number of keys in higher bins.
+__device__ __forceinline__ int find_bin(const int* hist, int need, int* wsum, int* shared_pair) {
+  const int tid = threadIdx.x;
+  const int bhi = 2047 - 2 * tid, blo = bhi - 1;
+  const int hh = hist[bhi], hl = hist[blo];
+  int tot;
+  const int before = block_excl_scan(hh + hl, wsum, tot);
+  if (before < need && before + hh >= need) {
+    shared_pair[0] = bhi;
+    shared_pair[1] = before;
+  } else if (before + hh < need && before + hh + hl >= need) {
+    shared_pair[0] = blo;
+    shared_pair[1] = before + hh;
+  }
+  __syncthreads();
+  return shared_pair[0];
 }
 
 template <bool kLds>
 __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(SelArgs a) {
   extern __shared__ uint32_t keys_s[];
   __shared__ int hist[2048];
+  __shared__ uint32_t border[kBorderCap];
   __shared__ int wsum[kSelWaves];
-  __shared__ int cnt[2][2][kSelWaves];
-  __shared__ int found_bin, found_above;
+  __shared__ int pair[2];
+  __shared__ int border_n;
 
   const int row = blockIdx.x;
   const int r = row % a.Sq;
   const long long t = a.q_start + r;
-  long long nv = t / a.m;
+  const long long nv = t / a.m;
   const int nvis = (int)(nv < a.N ? nv : a.N);
   const int k = a.k;
   int32_t* out = a.idx_out + (long long)row * k;
@@ -68,84 +92,98 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(SelArgs a) {
     }
     return;
   }
-  if (kLds) {
-    for (int i = tid; i < nvis; i += kSelThreads) keys_s[i] = kg[i];
-  }
   const uint32_t* K = kLds ? keys_s : kg;
 
-  uint32_t prefix = 0, mask = 0;
-  int need = k;
-  const int shifts[3] = {21, 10, 0};
-  const int nbits[3] = {11, 11, 10};
-  for (int pass = 0; pass < 3; ++pass) {
-    const int sh = shifts[pass], nb = 1 << nbits[pass];
-    for (int i = tid; i < 2048; i += kSelThreads) hist[i] = 0;
-    __syncthreads();
-    for (int i = tid; i < nvis; i += kSelThreads) {
-      uint32_t key = K[i];
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> sh) & (nb - 1)], 1);
-    }
-    __syncthreads();
-    // bins in descending order: thread tid owns bins hi = 2047 - 2 tid and lo = hi - 1 (only nb bins exist)
-    const int bhi = 2047 - 2 * tid, blo = bhi - 1;
-    const int hh = bhi < nb ? hist[bhi] : 0;
-    const int hl = blo < nb ? hist[blo] : 0;
-    int tot;
-    const int incl = block_incl_scan(hh + hl, wsum, tot);
-    const int before = incl - hh - hl;
-    if (before < need && before + hh >= need) {
-      found_bin = bhi;
-      found_above = before;
-    } else if (before + hh < need && before + hh + hl >= need) {
-      found_bin = blo;
-      found_above = before + hh;
-    }
-    __syncthreads();
-    prefix |= (uint32_t)found_bin << sh;
-    mask |= (uint32_t)(nb - 1) << sh;
-    need -= found_above;
-    __syncthreads();
+  // pass 1 (key bits [31:21]) fused with staging the row in LDS
+  for (int i = tid; i < 2048; i += kSelThreads) hist[i] = 0;
+  if (tid == 0) border_n = 0;
+  __syncthreads();
+  for (int i = tid; i < nvis; i += kSelThreads) {
+    const uint32_t key = kg[i];
+    if (kLds) keys_s[i] = key;
+    atomicAdd(&hist[key >> 21], 1);
   }
-  const uint32_t kappa = prefix;
+  __syncthreads();
+  int need = k;
+  const int b1 = find_bin(hist, need, wsum, pair);
+  need -= pair[1];
+  __syncthreads();
 
-  // entry-ordered compaction: keys > kappa, then the first `need` keys == kappa
-  const int lane = tid & 63, w = tid >> 6;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  int sel_run = 0, eq_run = 0, parity = 0;
-  for (int base = 0; base < nvis && sel_run < k; base += kSelThreads) {
-    const int i = base + tid;
-    const uint32_t key = i < nvis ? K[i] : 0u;
-    const bool gt = i < nvis && key > kappa;
-    const bool eq = i < nvis && key == kappa;
-    const uint64_t bgt = __ballot(gt), beq = __ballot(eq);
-    if (lane == 0) {
-      cnt[parity][0][w] = __popcll(bgt);
-      cnt[parity][1][w] = __popcll(beq);
+  // border bin: the keys sharing the 11-bit prefix b1
+  for (int i = tid; i < nvis; i += kSelThreads) {
+    const uint32_t key = K[i];
+    if ((int)(key >> 21) == b1) {
+      const int pos = atomicAdd(&border_n, 1);
+      if (pos < kBorderCap) border[pos] = key;
+    }
+    if (i < 2048) hist[i] = 0;
+  }
+  for (int i = nvis + tid; i < 2048; i += kSelThreads) hist[i] = 0;
+  __syncthreads();
+  const int nb = border_n;
+  const bool in_lds = nb <= kBorderCap;
+  const uint32_t* src = in_lds ? border : K;
+  const int n_src = in_lds ? nb : nvis;
+
+  // passes 2 (bits [20:10]) and 3 (bits [9:0]) over the border keys only
+  uint32_t prefix = (uint32_t)b1 << 21, mask = 0xFFE00000u;
+  for (int pass = 0; pass < 2; ++pass) {
+    const int sh = pass == 0 ? 10 : 0;
+    const uint32_t digit = pass == 0 ? 0x7FFu : 0x3FFu;
+    for (int i = tid; i < n_src; i += kSelThreads) {
+      const uint32_t key = src[i];
+      if ((key & mask) == prefix) atomicAdd(&hist[(key >> sh) & digit], 1);
     }
     __syncthreads();
-    int eq_before = eq_run, sel_before = sel_run, eq_acc = eq_run, sel_acc = sel_run;
-    for (int x = 0; x < kSelWaves; ++x) {
-      const int cg = cnt[parity][0][x], ce = cnt[parity][1][x];
-      int take = need - eq_acc;
-      take = take < 0 ? 0 : (take > ce ? ce : take);
-      if (x == w) {
-        eq_before = eq_acc;
-        sel_before = sel_acc;
+    const int bn = find_bin(hist, need, wsum, pair);
+    need -= pair[1];
+    prefix |= (uint32_t)bn << sh;
+    mask |= digit << sh;
+    __syncthreads();
+    if (pass == 0) {
+      for (int i = tid; i < 2048; i += kSelThreads) hist[i] = 0;
+      __syncthreads();
+    }
+  }
+  const uint32_t kappa = prefix;  // the k-th largest key; `need` of the keys equal to it are selected
+
+  // entry-ordered compaction: every key > kappa, then the first `need` keys == kappa
+  int sel_run = 0, eq_run = 0;
+  for (int base = 0; base < nvis && sel_run < k; base += kSelThreads * kPerThread) {
+    const int i0 = base + tid * kPerThread;
+    uint32_t kk[kPerThread];
+    int gt = 0, eq = 0;
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      kk[j] = (i0 + j < nvis) ? K[i0 + j] : 0u;
+      const bool valid = i0 + j < nvis;
+      gt += (valid && kk[j] > kappa) ? 1 : 0;
+      eq += (valid && kk[j] == kappa) ? 1 : 0;
+    }
+    int tot;
+    const int packed_before = block_excl_scan(gt | (eq << 16), wsum, tot);
+    const int gt_before = packed_before & 0xFFFF, eq_before = packed_before >> 16;
+    const int rem = need - eq_run > 0 ? need - eq_run : 0;
+    int pos = sel_run + gt_before + (eq_before < rem ? eq_before : rem);
+    int eq_seen = eq_run + eq_before;
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      const int i = i0 + j;
+      if (i >= nvis) break;
+      bool sel = kk[j] > kappa;
+      if (kk[j] == kappa) {
+        sel = eq_seen < need;
+        ++eq_seen;
       }
-      eq_acc += ce;
-      sel_acc += cg + take;
+      if (sel) {
+        out[pos] = i;
+        if (sout) sout[pos] = key_score(kk[j]);
+        ++pos;
+      }
     }
-    const int eqrank = eq_before + __popcll(beq & lt_mask);
-    const bool sel = gt || (eq && eqrank < need);
-    const uint64_t bsel = __ballot(sel);
-    if (sel) {
-      const int pos = sel_before + __popcll(bsel & lt_mask);
-      out[pos] = i;
-      if (sout) sout[pos] = key_score(key);
-    }
-    eq_run = eq_acc;
-    sel_run = sel_acc;
-    parity ^= 1;
+    const int tot_gt = tot & 0xFFFF, tot_eq = tot >> 16;
+    sel_run += tot_gt + (tot_eq < rem ? tot_eq : rem);
+    eq_run += tot_eq;
   }
 }
 
@@ -156,6 +194,7 @@ hipError_t launch_topk(const SelArgs& a, hipStream_t st) {
   // the longest visible row decides the variant (rows of one call differ only by their causal limit)
   long long nv = (a.q_start + a.Sq - 1) / a.m;
   const int nvis_max = (int)(nv < a.N ? nv : a.N);
+  clear_stale_error();
   if (nvis_max <= kLdsKeys) {
     if (!g_lds_attr_set) {
       hipError_t e = hipFuncSetAttribute((const void*)topk_select_kernel<true>,

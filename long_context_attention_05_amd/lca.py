@@ -19,7 +19,10 @@ STATUS = {0: "LCA_OK", -1: "LCA_ERR_INVALID_ARG", -2: "LCA_ERR_UNSUPPORTED", -3:
 
 class LcaError(RuntimeError):
     def __init__(self, fn: str, status: int):
-        super().__init__("%s failed: %s" % (fn, STATUS.get(status, status)))
+        msg = "%s failed: %s" % (fn, STATUS.get(status, status))
+        if status == -5:
+            msg += " (%s)" % _lib.lca_last_hip_error().decode()
+        super().__init__(msg)
         self.status = status
 
 
@@ -41,11 +44,15 @@ _S = ctypes.c_size_t
 
 _lib.lca_status_string.argtypes = [_I]
 _lib.lca_status_string.restype = ctypes.c_char_p
+_lib.lca_last_hip_error.argtypes = []
+_lib.lca_last_hip_error.restype = ctypes.c_char_p
 _lib.lca_encode.argtypes = [_P, _I, _L, _L, lca_tensor, _P]
 _lib.kv_compress.argtypes = [_P] * 8 + [_I, _L, _I, _I, _I, _L, lca_tensor, _P]
 _lib.indexer_score_topk_workspace_size.argtypes = [_I, _I, _I, _I]
 _lib.indexer_score_topk_workspace_size.restype = _S
 _lib.indexer_score_topk.argtypes = [lca_tensor, _P, lca_tensor] + [_I] * 7 + [_L, _P, _P, _P, _S, _P]
+_lib.lca_set_score_events.argtypes = [_P, _P]
+_lib.lca_set_score_events.restype = None
 _lib.sparse_mqa_attn_workspace_size.argtypes = [_I] * 5
 _lib.sparse_mqa_attn_workspace_size.restype = _S
 _lib.sparse_mqa_attn.argtypes = [_P, _I, lca_tensor, _I, lca_tensor, _L, _I, _P, _I, _P] + [_I] * 5 + [
@@ -143,6 +150,11 @@ def kv_compress(Ca, Cb, Za, Zb, Ba, Bb, tail_Cb, tail_Zb, B: int, n: int, c: int
 
 def indexer_score_topk_workspace_size(B: int, Sq: int, N: int, k: int) -> int:
     return int(_lib.indexer_score_topk_workspace_size(B, Sq, N, k))
+
+
+def lca_set_score_events(ev_begin, ev_end):
+    """hipEvent_t handles (ints) recorded around the indexer scoring kernel; None, None to stop."""
+    _lib.lca_set_score_events(ev_begin, ev_end)
 
 
 def indexer_score_topk(qI: lca_tensor, w, kI: lca_tensor, B: int, Sq: int, HI: int, DI: int, N: int, m: int, k: int,

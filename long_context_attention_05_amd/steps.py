@@ -1,0 +1,239 @@
+"""One layer step as a fixed sequence of C-ABI calls over preallocated device buffers.
+
+A CSA decode step is: kv_compress (append the new token to the latent cache and to the indexer-key cache) ->
+indexer_score_topk -> sparse_mqa_attn.  An HCA decode step is kv_compress -> hca_attn.  A CSA prefill chunk is
+kv_compress of the chunk (both caches) -> indexer_score_topk -> sparse_mqa_attn over every row of the chunk.
+This module only allocates buffers, uploads the caller's host arrays and sequences the calls; all arithmetic runs
+in liblca.so.  `copies` > 1 keeps independent copies of the large caches so that consecutive steps read distinct
+addresses (the 256 MB last-level cache then cannot serve a repeated step).
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import lca
+
+DEV = "cuda"
+
+
+def _up(x: np.ndarray) -> torch.Tensor:
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint16:
+        x = x.view(np.int16)
+    return torch.from_numpy(x).to(DEV)
+
+
+def _bf16_bits(x: np.ndarray) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def _entry_bytes(fmt: str, dim: int, rope: int) -> int:
+    return {"f32": 4 * dim, "bf16": 2 * dim, "mixed": (dim - rope) + 2 * rope + 4, "fp4": dim // 2 + dim // 16}[fmt]
+
+
+def make_cache(fmt: str, B: int, cap: int, dim: int, rope: int, x: np.ndarray | None) -> lca.CacheTensor:
+    """Cache of `cap` rows per sequence; rows [0, x.shape[1]) hold x (bf16 by cast of the given values, mixed/fp4
+    encoded on the GPU by lca_encode)."""
+    c = lca.CacheTensor(fmt, B, cap, dim, rope)
+    if x is None:
+        return c
+    rows = x.shape[1]
+    if fmt == "bf16":
+        c.data.view(B, cap, dim)[:, :rows] = _up(_bf16_bits(x))
+    elif fmt == "f32":
+        c.data.view(B, cap, dim)[:, :rows] = _up(x.astype(np.float32))
+    else:
+        for b in range(B):  # one sequence at a time keeps the fp32 staging buffer small
+            src = _up(x[b:b + 1].astype(np.float32))
+            d = c.desc()
+            d.data = c.data[b * cap:].data_ptr()
+            d.rope = None if c.rope_t is None else c.rope_t[b * cap:].data_ptr()
+            d.scale = c.scale_t[b * cap:].data_ptr()
+            d.cap = cap
+            lca.lca_encode(src, 1, rows, 0, d)
+            del src
+    return c
+
+
+def clone_cache(c: lca.CacheTensor) -> lca.CacheTensor:
+    n = lca.CacheTensor.__new__(lca.CacheTensor)
+    n.__dict__.update(c.__dict__)
+    n.data = c.data.clone()
+    n.rope_t = None if c.rope_t is None else c.rope_t.clone()
+    n.scale_t = None if c.scale_t is None else c.scale_t.clone()
+    return n
+
+
+class _Streams:
+    """Device copies of one set of compression streams."""
+
+    def __init__(self, inp: dict, tag: str, overlap: bool, with_tail: bool):
+        self.Ca, self.Za = _up(inp["Ca" + tag]), _up(inp["Za" + tag])
+        self.Ba = _up(inp["Ba" + tag])
+        self.Cb = self.Zb = self.Bb = self.tCb = self.tZb = None
+        if overlap:
+            self.Cb, self.Zb, self.Bb = _up(inp["Cb" + tag]), _up(inp["Zb" + tag]), _up(inp["Bb" + tag])
+            if with_tail:
+                self.tCb, self.tZb = _up(inp["tail_Cb" + tag]), _up(inp["tail_Zb" + tag])
+        self.B, self.n, self.c = inp["Ca" + tag].shape
+        self.nbytes = sum(t.numel() * 4 for t in (self.Ca, self.Za, self.Cb, self.Zb, self.tCb, self.tZb)
+                          if t is not None)
+
+    def compress(self, m: int, overlap: bool, start_pos: int, out: lca.CacheTensor, stream=None):
+        lca.kv_compress(self.Ca, self.Cb, self.Za, self.Zb, self.Ba, self.Bb, self.tCb, self.tZb, self.B, self.n,
+                        self.c, m, overlap, start_pos, out.desc(), stream)
+
+
+class CsaDecode:
+    """CSA decode step of a batch of B sequences holding n_ctx tokens (N = n_ctx / 4 committed entries)."""
+
+    def __init__(self, w, inp: dict, copies: int = 1):
+        self.w = w
+        B, N, D, DI, HI, H, k = w.B, w.N, w.D, w.DI, w.HI, w.H, w.k
+        self.copies = copies
+        cap = N + 1  # room for the provisional entry of the block the new token starts
+        base_comp = make_cache(w.main_fmt, B, cap, D, w.rope, inp["comp"])
+        base_keys = make_cache(w.key_fmt, B, cap, DI, 0, inp["keys"])
+        base_raw = make_cache(w.main_fmt, B, w.window, D, w.rope, inp["window_kv"])
+        self.comp = [base_comp] + [clone_cache(base_comp) for _ in range(copies - 1)]
+        self.keys = [base_keys] + [clone_cache(base_keys) for _ in range(copies - 1)]
+        self.raw = [base_raw] + [clone_cache(base_raw) for _ in range(copies - 1)]
+        self.q = _up(_bf16_bits(inp["q"]))
+        if w.qi_fmt == "fp4":
+            self.qI = make_cache("fp4", B, HI, DI, 0, inp["qI"].reshape(B, HI, DI))
+            self.qI_desc = self.qI.desc()
+        else:
+            self.qI = _up(_bf16_bits(inp["qI"]))
+            self.qI_desc = lca.plain_desc(self.qI, "bf16", DI, HI)
+        self.wgt = _up(inp["w"])
+        self.sink = _up(inp["sink"])
+        self.main = _Streams(inp, "", True, True)
+        self.ind = _Streams(inp, "_I", True, True)
+        self.idx = torch.empty((B, 1, k), dtype=torch.int32, device=DEV)
+        self.scores = torch.empty((B, 1, k), dtype=torch.float32, device=DEV)
+        self.out = torch.empty((B, 1, H, D), dtype=torch.int16, device=DEV)
+        self.lse = torch.empty((B, 1, H), dtype=torch.float32, device=DEV)
+        self.ws_i_bytes = lca.indexer_score_topk_workspace_size(B, 1, N, k)
+        self.ws_a_bytes = lca.sparse_mqa_attn_workspace_size(B, 1, H, D, w.window + k)
+        self.ws_i = torch.empty(max(self.ws_i_bytes, 256), dtype=torch.uint8, device=DEV)
+        self.ws_a = torch.empty(max(self.ws_a_bytes, 256), dtype=torch.uint8, device=DEV)
+        self.raw_start = w.n_ctx - w.window + 1
+
+    def run(self, c: int = 0, stream=None):
+        w = self.w
+        self.main.compress(4, True, w.n_ctx, self.comp[c], stream)
+        self.ind.compress(4, True, w.n_ctx, self.keys[c], stream)
+        lca.indexer_score_topk(self.qI_desc, self.wgt, self.keys[c].desc(), w.B, 1, w.HI, w.DI, w.N, 4, w.k, w.n_ctx,
+                               self.idx, self.scores, self.ws_i, self.ws_i_bytes, stream)
+        lca.sparse_mqa_attn(self.q, lca.LCA_BF16, self.comp[c].desc(), w.N, self.raw[c].desc(), self.raw_start,
+                            w.window, self.idx, w.k, self.sink, w.B, 1, w.H, w.D, w.window, w.scale, w.n_ctx, self.out,
+                            lca.LCA_BF16, self.lse, self.ws_a, self.ws_a_bytes, stream)
+
+    # algorithmic traffic and work of one step (what the method must move / compute)
+    def score_kernel_bytes(self) -> int:
+        w = self.w
+        key_b = _entry_bytes(w.key_fmt, w.DI, 0) * w.B * w.N
+        qi_b = _entry_bytes(w.qi_fmt, w.DI, 0) * w.B * w.HI
+        return key_b + qi_b + 4 * w.B * w.HI
+
+    def step_bytes(self) -> int:
+        w = self.w
+        eb = _entry_bytes(w.main_fmt, w.D, w.rope)
+        gather = eb * w.B * (w.k + w.window)
+        q_out = 2 * 2 * w.B * w.H * w.D
+        idx = 2 * 4 * w.B * w.k
+        return self.score_kernel_bytes() + gather + q_out + idx + self.main.nbytes + self.ind.nbytes
+
+    def step_flops(self) -> int:
+        w = self.w
+        return 2 * w.B * w.HI * w.DI * w.N + 4 * w.B * w.H * w.D * (w.k + w.window)
+
+
+class HcaDecode:
+    """HCA decode step: B sequences of n_ctx tokens, N = n_ctx / 128 entries, dense attention."""
+
+    def __init__(self, w, inp: dict, copies: int = 1):
+        self.w = w
+        B, N, D, H = w.B, w.N, w.D, w.H
+        base_comp = make_cache(w.main_fmt, B, N + 1, D, w.rope, inp["comp"])
+        base_raw = make_cache(w.main_fmt, B, w.window, D, w.rope, inp["window_kv"])
+        self.comp = [base_comp] + [clone_cache(base_comp) for _ in range(copies - 1)]
+        self.raw = [base_raw] + [clone_cache(base_raw) for _ in range(copies - 1)]
+        self.q = _up(_bf16_bits(inp["q"]))
+        self.sink = _up(inp["sink"])
+        self.main = _Streams(inp, "", False, False)
+        self.out = torch.empty((B, 1, H, D), dtype=torch.int16, device=DEV)
+        self.lse = torch.empty((B, 1, H), dtype=torch.float32, device=DEV)
+        self.ws_bytes = lca.hca_attn_workspace_size(B, 1, H, D, w.window + N)
+        self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=DEV)
+        self.raw_start = w.n_ctx - w.window + 1
+
+    def run(self, c: int = 0, stream=None):
+        w = self.w
+        self.main.compress(w.m, False, w.n_ctx, self.comp[c], stream)
+        lca.hca_attn(self.q, lca.LCA_BF16, self.comp[c].desc(), w.N, w.m, self.raw[c].desc(), self.raw_start, w.window,
+                     self.sink, w.B, 1, w.H, w.D, w.window, w.scale, w.n_ctx, self.out, lca.LCA_BF16, self.lse, self.ws,
+                     self.ws_bytes, stream)
+
+    def step_bytes(self) -> int:
+        w = self.w
+        eb = _entry_bytes(w.main_fmt, w.D, w.rope)
+        return eb * w.B * (w.N + w.window) + 2 * 2 * w.B * w.H * w.D + self.main.nbytes
+
+    def step_flops(self) -> int:
+        w = self.w
+        return 4 * w.B * w.H * w.D * (w.N + w.window)
+
+
+class CsaPrefill:
+    """CSA prefill chunk: Sq new tokens after n_ctx cached ones (N0 = n_ctx / 4 given entries)."""
+
+    def __init__(self, w, inp: dict):
+        self.w = w
+        B, D, DI, HI, H, k, Sq = w.B, w.D, w.DI, w.HI, w.H, w.k, w.Sq
+        self.N0 = w.n_ctx // w.m
+        self.N = (w.n_ctx + Sq) // w.m
+        self.comp = make_cache(w.main_fmt, B, self.N, D, w.rope, inp.get("comp"))
+        self.keys = make_cache(w.key_fmt, B, self.N, DI, 0, inp.get("keys"))
+        self.raw_start = inp["raw_start"]
+        self.S_raw = inp["raw_kv"].shape[1]
+        self.raw = make_cache(w.main_fmt, B, self.S_raw, D, w.rope, inp["raw_kv"])
+        self.q = _up(_bf16_bits(inp["q"]))
+        self.qI = _up(_bf16_bits(inp["qI"]))
+        self.qI_desc = lca.plain_desc(self.qI, "bf16", DI, Sq * HI)
+        self.wgt = _up(inp["w"])
+        self.sink = _up(inp["sink"])
+        self.main = _Streams(inp, "", True, w.n_ctx > 0)
+        self.ind = _Streams(inp, "_I", True, w.n_ctx > 0)
+        self.idx = torch.empty((B, Sq, k), dtype=torch.int32, device=DEV)
+        self.scores = torch.empty((B, Sq, k), dtype=torch.float32, device=DEV)
+        self.out = torch.empty((B, Sq, H, D), dtype=torch.int16, device=DEV)
+        self.lse = torch.empty((B, Sq, H), dtype=torch.float32, device=DEV)
+        self.ws_i_bytes = lca.indexer_score_topk_workspace_size(B, Sq, self.N, k)
+        self.ws_a_bytes = lca.sparse_mqa_attn_workspace_size(B, Sq, H, D, w.window + k)
+        self.ws_i = torch.empty(max(self.ws_i_bytes, 256), dtype=torch.uint8, device=DEV)
+        self.ws_a = torch.empty(max(self.ws_a_bytes, 256), dtype=torch.uint8, device=DEV)
+
+    def run(self, c: int = 0, stream=None):
+        w = self.w
+        self.main.compress(4, True, w.n_ctx, self.comp, stream)
+        self.ind.compress(4, True, w.n_ctx, self.keys, stream)
+        lca.indexer_score_topk(self.qI_desc, self.wgt, self.keys.desc(), w.B, w.Sq, w.HI, w.DI, self.N, 4, w.k,
+                               w.n_ctx, self.idx, self.scores, self.ws_i, self.ws_i_bytes, stream)
+        lca.sparse_mqa_attn(self.q, lca.LCA_BF16, self.comp.desc(), self.N, self.raw.desc(), self.raw_start, self.S_raw,
+                            self.idx, w.k, self.sink, w.B, w.Sq, w.H, w.D, w.window, w.scale, w.n_ctx, self.out,
+                            lca.LCA_BF16, self.lse, self.ws_a, self.ws_a_bytes, stream)
+
+    def visible_pairs(self) -> int:
+        w = self.w
+        t = w.n_ctx + np.arange(w.Sq, dtype=np.int64)
+        return int(np.minimum(t // w.m, self.N).sum()) * w.B
+
+    def score_kernel_flops(self) -> int:
+        return 2 * self.w.HI * self.w.DI * self.visible_pairs()
+
+    def step_flops(self) -> int:
+        w = self.w
+        return self.score_kernel_flops() + 4 * w.B * w.Sq * w.H * w.D * (w.k + w.window)
