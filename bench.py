@@ -36,6 +36,9 @@ def parse():
     p.add_argument("--workload", default="csa_decode_128k_bf16")
     p.add_argument("--copies", type=int, default=4)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--calibrate-copy-mib", type=int, default=0,
+                   help="before the steps, run one device copy of this many MiB (a known-size reference for HBM "
+                        "byte counters collected around the run)")
     return p.parse_args()
 
 
@@ -83,14 +86,26 @@ def traffic_record(kernel: str, workload: str, src_files, per_launch_units: floa
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline_csa_decode(w, inp, sample_seqs: int):
-    """The oracle, as it stands, on `sample_seqs` sequences of the decode step (append, score, top-k, attend)."""
+def cpu_baseline_csa_decode(w, inp, sample_seqs: int, min_wall_s: float = 1.0):
+    """The oracle, as it stands, on `sample_seqs` sequences of the decode step (append, score, top-k, attend),
+    repeated until at least `min_wall_s` of wall time (about 10-30 s of CPU time on the machine's cores) has passed."""
+    from oracle import oracle as orc
+    S = sample_seqs
+    sl = slice(0, S)
+    reps, t0 = 0, time.perf_counter()
+    while reps == 0 or time.perf_counter() - t0 < min_wall_s:
+        _oracle_csa_decode_once(w, inp, S, sl)
+        reps += 1
+    dt = time.perf_counter() - t0
+    return dict(value=reps * S / dt, unit="tokens/s", cores=orc.num_threads(), kind="oracle",
+                sample="%d repetition(s) of %d of %d sequences of one decode step (compress append, fp64 indexer "
+                       "scores over all %d entries, top-%d, attention); %.2f s wall" % (reps, S, w.B, w.N, w.k, dt))
+
+
+def _oracle_csa_decode_once(w, inp, S, sl):
     import numpy as np
     import lca_inputs as gen
     from oracle import oracle as orc
-    S = sample_seqs
-    t0 = time.perf_counter()
-    sl = slice(0, S)
     for tag in ("", "_I"):
         orc.kv_compress(inp["Ca" + tag][sl], inp["Cb" + tag][sl], inp["Za" + tag][sl], inp["Zb" + tag][sl],
                         inp["Ba" + tag], inp["Bb" + tag], inp["tail_Cb" + tag][sl], inp["tail_Zb" + tag][sl], m=4,
@@ -116,18 +131,26 @@ def cpu_baseline_csa_decode(w, inp, sample_seqs: int):
     qa = orc.plain_cache(gen.bf16_bits(inp["q"][sl]), "bf16")
     orc.attn(qa, cc, w.N, rc, w.n_ctx - w.window + 1, w.window, idx.reshape(S, 1, w.k), w.k, 0, inp["sink"], S, 1, w.H,
              w.D, w.window, w.scale, w.n_ctx)
-    dt = time.perf_counter() - t0
-    return dict(value=S / dt, unit="tokens/s", cores=orc.num_threads(), kind="oracle",
-                sample="%d of %d sequences of one decode step (compress append, fp64 indexer scores over all %d "
-                       "entries, top-%d, attention); %.2f s wall" % (S, w.B, w.N, w.k, dt))
 
 
-def cpu_baseline_hca_decode(w, inp, sample_seqs: int):
+def cpu_baseline_hca_decode(w, inp, sample_seqs: int, min_wall_s: float = 1.0):
     import lca_inputs as gen
     from oracle import oracle as orc
     S = sample_seqs
     sl = slice(0, S)
-    t0 = time.perf_counter()
+    reps, t0 = 0, time.perf_counter()
+    while reps == 0 or time.perf_counter() - t0 < min_wall_s:
+        _oracle_hca_decode_once(w, inp, S, sl)
+        reps += 1
+    dt = time.perf_counter() - t0
+    return dict(value=reps * S / dt, unit="tokens/s", cores=orc.num_threads(), kind="oracle",
+                sample="%d repetition(s) of %d of %d sequences of one HCA decode step (append + dense attention over "
+                       "%d entries); %.2f s wall" % (reps, S, w.B, w.N, dt))
+
+
+def _oracle_hca_decode_once(w, inp, S, sl):
+    import lca_inputs as gen
+    from oracle import oracle as orc
     orc.kv_compress(inp["Ca"][sl], None, inp["Za"][sl], None, inp["Ba"], None, m=w.m, overlap=False,
                     start_pos=w.n_ctx)
     cc = orc.plain_cache(gen.bf16_bits(inp["comp"][sl]), "bf16")
@@ -136,10 +159,6 @@ def cpu_baseline_hca_decode(w, inp, sample_seqs: int):
     qa = orc.plain_cache(gen.bf16_bits(inp["q"][sl]), "bf16")
     orc.attn(qa, cc, w.N, rc, w.n_ctx - w.window + 1, w.window, None, 0, w.m, inp["sink"], S, 1, w.H, w.D, w.window,
              w.scale, w.n_ctx)
-    dt = time.perf_counter() - t0
-    return dict(value=S / dt, unit="tokens/s", cores=orc.num_threads(), kind="oracle",
-                sample="%d of %d sequences of one HCA decode step (append + dense attention over %d entries); "
-                       "%.2f s wall" % (S, w.B, w.N, dt))
 
 
 def main():
@@ -166,6 +185,15 @@ def main():
         copies = 1
     torch.cuda.synchronize()
     print("inputs ready in %.1f s" % (time.perf_counter() - t_gen), file=sys.stderr, flush=True)
+
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib * (1 << 20) // 4
+        src_t = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst_t = torch.empty_like(src_t)
+        torch.cuda.synchronize()
+        dst_t.copy_(src_t)
+        torch.cuda.synchronize()
+        del src_t, dst_t
 
     ev = HipEvents()
     has_scores = w.HI > 0
@@ -213,9 +241,9 @@ def main():
         if w.Sq == 1:
             per_launch = step.score_kernel_bytes()
             achieved = per_launch / (avg_ms / 1e3) / 1e9
-            res["roofline"] = {"kernel": "idx_score_mfma", "bound": "hbm", "achieved": achieved,
+            res["roofline"] = {"kernel": "idx_score_decode", "bound": "hbm", "achieved": achieved,
                                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                               "traffic": traffic_record("idx_score_mfma", w.name, src, per_launch),
+                               "traffic": traffic_record("idx_score_decode", w.name, src, per_launch),
                                "avg_launch_us": avg_ms * 1e3, "algorithmic_bytes_per_launch": per_launch}
         else:
             per_launch = step.score_kernel_flops()
@@ -226,9 +254,9 @@ def main():
                                "avg_launch_us": avg_ms * 1e3, "algorithmic_flops_per_launch": per_launch}
     if not args.no_cpu_baseline:
         if w.Sq == 1 and w.HI > 0:
-            res["cpu_baseline"] = cpu_baseline_csa_decode(w, inp, sample_seqs=max(1, min(w.B, 2)))
+            res["cpu_baseline"] = cpu_baseline_csa_decode(w, inp, sample_seqs=w.B)
         elif w.Sq == 1:
-            res["cpu_baseline"] = cpu_baseline_hca_decode(w, inp, sample_seqs=1)
+            res["cpu_baseline"] = cpu_baseline_hca_decode(w, inp, sample_seqs=w.B)
     print(json.dumps(res), flush=True)
 
 

@@ -147,34 +147,46 @@ __global__ __launch_bounds__(kRowThreads) void compress_kernel(CompressArgs a, R
     num[u] = 0.0f;
   }
   const long long base = (long long)b * a.n;
-  // stream a: block i's own tokens
-  for (int r = 0; r < m; ++r) {
-    long long p = (long long)m * i + r;
-    if (p >= a.n) break;
-    const float* zr = a.Za + (base + p) * c;
-    const float* cr = a.Ca + (base + p) * c;
+  // stream a: block i's own tokens; stream b: block i-1's tokens (absent for the first block of the sequence).
+  // Candidates are taken four at a time with all their loads issued before the softmax updates.
+  const long long pa0 = (long long)m * i;
+  const int na = (int)((a.n - pa0) < m ? (a.n - pa0) : m);
+  const int nbk = (a.overlap && gblock >= 1) ? m : 0;
+  for (int r0 = 0; r0 < na + nbk; r0 += 4) {
+    float zl[4][CPT], cv[4][CPT];
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      int j = threadIdx.x + blockDim.x * u;
-      if (j < c) softmax_acc(zr[j] + a.Ba[r * c + j], cr[j], mx[u], den[u], num[u]);
-    }
-  }
-  // stream b: block i-1's tokens (absent for the first block of the sequence)
-  if (a.overlap && gblock >= 1) {
-    for (int r = 0; r < m; ++r) {
-      const float *zr, *cr;
-      if (i >= 1) {
-        long long p = (long long)m * (i - 1) + r;
-        zr = a.Zb + (base + p) * c;
-        cr = a.Cb + (base + p) * c;
+    for (int q = 0; q < 4; ++q) {
+      const int rr = r0 + q;
+      const bool from_a = rr < na;
+      const int r = from_a ? rr : rr - na;
+      const float *zr, *cr, *br;
+      if (from_a) {
+        zr = a.Za + (base + pa0 + r) * c;
+        cr = a.Ca + (base + pa0 + r) * c;
+        br = a.Ba + (long long)r * c;
+      } else if (i >= 1) {
+        zr = a.Zb + (base + pa0 - m + r) * c;
+        cr = a.Cb + (base + pa0 - m + r) * c;
+        br = a.Bb + (long long)r * c;
       } else {
         zr = a.tZb + ((long long)b * m + r) * c;
         cr = a.tCb + ((long long)b * m + r) * c;
+        br = a.Bb + (long long)r * c;
       }
+      const bool ok = rr < na + nbk;
 #pragma unroll
       for (int u = 0; u < CPT; ++u) {
-        int j = threadIdx.x + blockDim.x * u;
-        if (j < c) softmax_acc(zr[j] + a.Bb[r * c + j], cr[j], mx[u], den[u], num[u]);
+        const int j = threadIdx.x + blockDim.x * u;
+        const bool v = ok && j < c;
+        zl[q][u] = v ? zr[j] + br[j] : 0.0f;
+        cv[q][u] = v ? cr[j] : 0.0f;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (r0 + q < na + nbk) {
+#pragma unroll
+        for (int u = 0; u < CPT; ++u) softmax_acc(zl[q][u], cv[q][u], mx[u], den[u], num[u]);
       }
     }
   }

@@ -98,10 +98,21 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(SelArgs a) {
   for (int i = tid; i < 2048; i += kSelThreads) hist[i] = 0;
   if (tid == 0) border_n = 0;
   __syncthreads();
-  for (int i = tid; i < nvis; i += kSelThreads) {
-    const uint32_t key = kg[i];
-    if (kLds) keys_s[i] = key;
-    atomicAdd(&hist[key >> 21], 1);
+  for (int base = 0; base < nvis; base += kSelThreads * kPerThread) {
+    uint32_t kv[kPerThread];  // eight independent loads in flight per thread
+#pragma unroll
+    for (int u = 0; u < kPerThread; ++u) {
+      const int i = base + tid + kSelThreads * u;
+      kv[u] = i < nvis ? kg[i] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kPerThread; ++u) {
+      const int i = base + tid + kSelThreads * u;
+      if (i < nvis) {
+        if (kLds) keys_s[i] = kv[u];
+        atomicAdd(&hist[kv[u] >> 21], 1);
+      }
+    }
   }
   __syncthreads();
   int need = k;
@@ -110,15 +121,23 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(SelArgs a) {
   __syncthreads();
 
   // border bin: the keys sharing the 11-bit prefix b1
-  for (int i = tid; i < nvis; i += kSelThreads) {
-    const uint32_t key = K[i];
-    if ((int)(key >> 21) == b1) {
-      const int pos = atomicAdd(&border_n, 1);
-      if (pos < kBorderCap) border[pos] = key;
+  for (int i = tid; i < 2048; i += kSelThreads) hist[i] = 0;
+  for (int base = 0; base < nvis; base += kSelThreads * kPerThread) {
+    uint32_t kv[kPerThread];
+#pragma unroll
+    for (int u = 0; u < kPerThread; ++u) {
+      const int i = base + tid + kSelThreads * u;
+      kv[u] = i < nvis ? K[i] : 0u;
     }
-    if (i < 2048) hist[i] = 0;
+#pragma unroll
+    for (int u = 0; u < kPerThread; ++u) {
+      const int i = base + tid + kSelThreads * u;
+      if (i < nvis && (int)(kv[u] >> 21) == b1) {
+        const int pos = atomicAdd(&border_n, 1);
+        if (pos < kBorderCap) border[pos] = kv[u];
+      }
+    }
   }
-  for (int i = nvis + tid; i < 2048; i += kSelThreads) hist[i] = 0;
   __syncthreads();
   const int nb = border_n;
   const bool in_lds = nb <= kBorderCap;
