@@ -50,34 +50,47 @@ int hip_status(hipError_t e) {
 thread_local hipEvent_t t_ev_begin = nullptr, t_ev_end = nullptr;
 
 // Split plan of the attention: rows = B * Sq query rows, each with up to max_entries list positions.
-void attn_plan(int B, int Sq, int H, int max_entries, int& n_splits, int& split_len) {
+// hg: the head-group kernel (few rows), which runs 4 workgroups per (row, split).
+void attn_plan(int B, int Sq, int H, int max_entries, bool hg, int& n_splits, int& split_len) {
   const long long rows = (long long)B * Sq;
   n_splits = 1;
   split_len = max_entries > 0 ? max_entries : 1;
   if (rows >= 256 || max_entries <= 64) return;
-  const long long want = (256 + rows - 1) / rows;
+  const long long unit = hg ? 64 : 32;
+  const long long per_row = hg ? rows * (H / 16) : rows;
+  const long long want = (256 + per_row - 1) / per_row;
   long long len = (max_entries + want - 1) / want;
-  len = (len + 31) / 32 * 32;
+  len = (len + unit - 1) / unit * unit;
   if (len < 64) len = 64;
   long long ns = (max_entries + len - 1) / len;
-  (void)H;
   const long long max_splits = 4096;  // the merge keeps one weight per split in LDS
   if (ns > max_splits) {
     ns = max_splits;
     len = (max_entries + ns - 1) / ns;
-    len = (len + 31) / 32 * 32;
+    len = (len + unit - 1) / unit * unit;
     ns = (max_entries + len - 1) / len;
   }
   n_splits = (int)ns;
   split_len = (int)len;
 }
 
-size_t attn_ws_size(int B, int Sq, int H, int D, int max_entries) {
+bool attn_hg(int B, int Sq, int H, int D, int q_format, int kv_format) {
+  return attn_uses_mfma(H, D, q_format, kv_format) && (long long)B * Sq < 256;
+}
+
+size_t attn_ws_plan_size(int B, int Sq, int H, int D, int max_entries, bool hg) {
   int ns, len;
-  attn_plan(B, Sq, H, max_entries, ns, len);
+  attn_plan(B, Sq, H, max_entries, hg, ns, len);
   if (ns <= 1) return 0;
   const size_t items = (size_t)B * Sq * ns;
   return align_up(items * H * D * sizeof(float)) + align_up(items * H * 2 * sizeof(float));
+}
+
+// Enough for whichever kernel the call will take (the size query does not know the formats).
+size_t attn_ws_size(int B, int Sq, int H, int D, int max_entries) {
+  const size_t a = attn_ws_plan_size(B, Sq, H, D, max_entries, false);
+  const size_t b = (H == 64 && D == 512) ? attn_ws_plan_size(B, Sq, H, D, max_entries, true) : 0;
+  return a > b ? a : b;
 }
 
 int run_attn(const void* q, int q_format, const lca_tensor& comp, int N, int hca_m, const lca_tensor& raw,
@@ -113,9 +126,10 @@ int run_attn(const void* q, int q_format, const lca_tensor& comp, int N, int hca
     return LCA_ERR_UNSUPPORTED;
   }
   const int max_entries = window + (hca_m > 0 ? N : k);
+  const bool hg = attn_hg(B, Sq, H, D, q_format, comp.format);
   int ns, len;
-  attn_plan(B, Sq, H, max_entries, ns, len);
-  const size_t need = attn_ws_size(B, Sq, H, D, max_entries);
+  attn_plan(B, Sq, H, max_entries, hg, ns, len);
+  const size_t need = attn_ws_plan_size(B, Sq, H, D, max_entries, hg);
   if (need > 0 && (!ws || ws_bytes < need)) return LCA_ERR_WORKSPACE;
 
   AttnArgs a{};
@@ -142,6 +156,7 @@ int run_attn(const void* q, int q_format, const lca_tensor& comp, int N, int hca
   a.lse = lse;
   a.n_splits = ns;
   a.split_len = len;
+  a.hg_mode = hg ? 1 : 0;
   if (ns > 1) {
     const size_t items = (size_t)B * Sq * ns;
     a.part_o = (float*)ws;
@@ -209,10 +224,35 @@ void lca_set_score_events(void* ev_begin, void* ev_end) {
   t_ev_end = (hipEvent_t)ev_end;
 }
 
+// Workspace of indexer_score_topk: the score keys [B * Sq][N]; for one query row per sequence (decode) also the
+// multi-workgroup select buffers: per-row state, per-slice counts and candidate segments.
+struct IdxWs {
+  size_t keys, state, counts, cand, total;
+};
+constexpr long long kMaxMultiN = 256LL * kSliceKeys;  // slices per row <= 256
+
+IdxWs idx_ws_layout(int B, int Sq, int N) {
+  IdxWs l{};
+  const size_t rows = (size_t)B * Sq;
+  l.keys = 0;
+  size_t off = align_up(rows * N * sizeof(uint32_t));
+  if (Sq == 1 && N <= kMaxMultiN) {
+    const size_t slots = ((size_t)N + kSliceKeys - 1) / kSliceKeys;
+    l.state = off;
+    off += align_up(rows * kSelStateInts * sizeof(int));
+    l.counts = off;
+    off += align_up(rows * slots * sizeof(int));
+    l.cand = off;
+    off += align_up(rows * N * sizeof(uint2));
+  }
+  l.total = off > kAlign ? off : kAlign;
+  return l;
+}
+
 size_t indexer_score_topk_workspace_size(int B, int Sq, int N, int k) {
   (void)k;
   if (B <= 0 || Sq <= 0 || N <= 0) return kAlign;
-  return align_up((size_t)B * Sq * N * sizeof(uint32_t));
+  return idx_ws_layout(B, Sq, N).total;
 }
 
 int indexer_score_topk(lca_tensor qI, const float* w, lca_tensor kI, int B, int Sq, int HI, int DI, int N, int m, int k,
@@ -231,7 +271,12 @@ int indexer_score_topk(lca_tensor qI, const float* w, lca_tensor kI, int B, int 
     return LCA_ERR_ALIGNMENT;
   if (N > 0 && (!ws || ws_bytes < indexer_score_topk_workspace_size(B, Sq, N, k))) return LCA_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
-  IdxArgs a{qI, kI, w, (uint32_t*)ws, B, Sq, HI, DI, N, m, q_start_pos};
+  const IdxWs L = idx_ws_layout(B, Sq, N > 0 ? N : 1);
+  const bool multi = N > 0 && Sq == 1 && N <= kMaxMultiN &&
+                     indexer_uses_decode_kernel(B, Sq, HI, DI, qI.format, kI.format);
+  char* wsb = (char*)ws;
+  int* state = multi ? (int*)(wsb + L.state) : nullptr;
+  IdxArgs a{qI, kI, w, (uint32_t*)(wsb + L.keys), B, Sq, HI, DI, N, m, q_start_pos, state};
   if (N > 0) {
     const bool timed = t_ev_begin && t_ev_end;
     if (timed && hipEventRecord(t_ev_begin, st) != hipSuccess) return LCA_ERR_HIP;
@@ -239,7 +284,8 @@ int indexer_score_topk(lca_tensor qI, const float* w, lca_tensor kI, int B, int 
     if (rc) return rc;
     if (timed && hipEventRecord(t_ev_end, st) != hipSuccess) return LCA_ERR_HIP;
   }
-  SelArgs s{(const uint32_t*)ws, idx_out, score_out, B * Sq, Sq, N, m, k, q_start_pos};
+  SelArgs s{(const uint32_t*)(wsb + L.keys), idx_out, score_out, B * Sq, Sq, N, m, k, q_start_pos, state,
+            multi ? (int*)(wsb + L.counts) : nullptr, multi ? (uint2*)(wsb + L.cand) : nullptr};
   return hip_status(launch_topk(s, st));
 }
 

@@ -255,6 +255,335 @@ __global__ __launch_bounds__(kAttnThreads) void attn_mfma_kernel(AttnArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------------
+// head-group MFMA kernel (few query rows: decode): H = 64, D = 512, bf16 or mixed fp8/bf16 entries
+// ------------------------------------------------------------------------------------------------
+// A workgroup owns 16 heads (one head group) of one query row and one slice of the row's entry list; each of its
+// four waves takes every fourth 16-entry tile of the slice:
+//   S^T = K Q^T     v_mfma_f32_16x16x32_bf16, A = the tile's 16 rows from LDS, B = the 16 heads' queries (LDS)
+//   O^T += V^T P^T  v_mfma_f32_16x16x16_bf16, A = V^T read by ds_read_b64_tr_b16 straight from the row-major tile,
+//                   B = P^T, which is exactly the S^T accumulator layout (lane: head l % 16, entries 4 (l / 16) + v)
+// ds_read_b64_tr_b16: in each 16-lane group, output lane 4a + e takes element e of the 8-byte chunks addressed by
+// group lanes a, a + 4, a + 8, a + 12.  Group lane a + 4v addresses entry 4G + v, channels 16 dt + 4a .. + 3, so
+// lane 4a + e receives V[4G + v][16 dt + 4a + e] for v = 0..3, the A layout of the 16x16x16 instruction.
+// fp8 entries are widened to bf16 exactly when the tile is written to LDS; their per-entry scale multiplies the
+// fp8-channel part of the logit and is folded into P for the fp8 channels.
+// The four waves' (max, sum, o) are merged in LDS at the end; the four head groups of a (row, slice) pair get
+// workgroup ids congruent mod 8 so that they run on one XCD and share its L2 copy of the gathered entries.
+constexpr int kHgRow = 520;                                   // bf16 per LDS row (1040 bytes)
+constexpr int kHgOStride = 516;                               // floats per head row in the merge buffer
+
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+// Each wave owns its own 16-entry LDS tile.  The next tile's 16 rows are loaded into registers (one wave-wide
+// 16-byte load per row, fully coalesced) while the current tile is scored, then written over the consumed tile, so
+// gathers overlap compute and no workgroup barrier is needed until the final merge.
+constexpr int kWTile = 16;
+constexpr float kRescaleSlack = 8.0f;
+constexpr int kWBufBytes = kWTile * kHgRow * 2;  // 16640
+// four wave tiles, then the per-wave (max, sum) of the merge; the merge's 2 x 16 x kHgOStride floats reuse the tiles
+// + the 16 heads' queries (shared), the waves' (max, sum) and entry scales
+constexpr size_t kHgwLds = (size_t)5 * kWBufBytes + 4 * 16 * 2 * 4 + 4 * 16 * 4;
+static_assert((size_t)2 * 16 * kHgOStride * 4 <= (size_t)4 * kWBufBytes, "merge buffer fits the tiles");
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const u32x4_t gbl_u32x4_t;
+
+struct WaveTile {
+  uint4 v[kWTile];  // lane i: bytes 16 i .. 16 i + 15 of each of the tile's 16 rows
+  uint64_t valid;   // bit j: entry j of the tile is real (padding loads a mapped dummy row, masked in the logits)
+};
+
+// Loads the 16 rows of list positions [p0, p0 + 16) into registers; each wave-wide 16-byte load reads one whole
+// 1 KB row.  Loads go through the global address space (not flat) so that waits on LDS traffic do not also wait
+// for these loads.
+__device__ __forceinline__ WaveTile wave_load_tile(const AttnArgs& a, const RowList& L, int b, int r, int p0,
+                                                   int p_end, int lane) {
+  WaveTile T;
+  const int p = p0 + (lane & 15);
+  long long row = -1;
+  if (lane < 16 && p < p_end) row = list_row(a, L, b, r, p);
+  const bool valid = row >= 0;
+  const unsigned long long base =
+      valid ? (unsigned long long)((const uint8_t*)(p < L.nw ? a.raw.data : a.comp.data) + row * 1024)
+            : (unsigned long long)((const uint8_t*)a.comp.data + (long long)b * a.comp.cap * 1024);
+  T.valid = __ballot(valid) & 0xFFFFull;
+#pragma unroll
+  for (int j = 0; j < kWTile; ++j) {
+    const unsigned long long rb = __shfl(base, j, 64);
+    const u32x4_t x = *(gbl_u32x4_t*)(rb + 16 * (unsigned long long)lane);
+    T.v[j] = make_uint4(x.x, x.y, x.z, x.w);
+  }
+  return T;
+}
+
+__device__ __forceinline__ void wave_store_tile(uint8_t* buf, int lane, const WaveTile& T) {
+#pragma unroll
+  for (int j = 0; j < kWTile; ++j) *(uint4*)(buf + j * (kHgRow * 2) + 16 * lane) = T.v[j];
+}
+
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2_t;
+
+// Four OCP e4m3 codes -> four bf16 (exact: every e4m3 value is a bf16 value), via the hardware fp8 -> f32 conversion.
+__device__ __forceinline__ uint2 fp8x4_to_bf16x4(uint32_t w) {
+  const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  uint2 r;
+  r.x = (__float_as_uint(lo[0]) >> 16) | (__float_as_uint(lo[1]) & 0xFFFF0000u);
+  r.y = (__float_as_uint(hi[0]) >> 16) | (__float_as_uint(hi[1]) & 0xFFFF0000u);
+  return r;
+}
+
+struct WaveTileMixed {
+  uint4 v[kWTile];  // lane c < 28: fp8 chunk c (channels 16c .. 16c + 15); 28 <= c < 36: RoPE chunk c - 28
+  float scale;      // lane j < 16: the per-entry fp8 scale of row j
+  uint64_t valid;
+};
+
+__device__ __forceinline__ WaveTileMixed wave_load_tile_mixed(const AttnArgs& a, const RowList& L, int b, int r,
+                                                              int p0, int p_end, int lane) {
+  WaveTileMixed T;
+  const int p = p0 + (lane & 15);
+  long long row = -1;
+  if (lane < 16 && p < p_end) row = list_row(a, L, b, r, p);
+  const bool valid = row >= 0;
+  const bool raw = valid && p < L.nw;
+  const long long rr = valid ? row : (long long)b * a.comp.cap;
+  const lca_tensor& src = raw ? a.raw : a.comp;
+  const unsigned long long fbase = (unsigned long long)((const uint8_t*)src.data + rr * 448);
+  const unsigned long long rbase = (unsigned long long)((const uint8_t*)src.rope + rr * 128);
+  T.scale = valid ? ((const float*)src.scale)[rr] : 1.0f;
+  T.valid = __ballot(valid) & 0xFFFFull;
+  const unsigned long long off = lane < 28 ? 16ull * lane : 16ull * (lane - 28);
+#pragma unroll
+  for (int j = 0; j < kWTile; ++j) {
+    const unsigned long long fb = __shfl(fbase, j, 64), rb = __shfl(rbase, j, 64);
+    if (lane < 36) {
+      const u32x4_t x = *(gbl_u32x4_t*)((lane < 28 ? fb : rb) + off);
+      T.v[j] = make_uint4(x.x, x.y, x.z, x.w);
+    } else {
+      T.v[j] = make_uint4(0, 0, 0, 0);
+    }
+  }
+  return T;
+}
+
+__device__ __forceinline__ void wave_store_tile_mixed(uint8_t* buf, float* scale_w, int lane, const WaveTileMixed& T) {
+#pragma unroll
+  for (int j = 0; j < kWTile; ++j) {
+    uint8_t* row = buf + j * (kHgRow * 2);
+    if (lane < 28) {
+      const uint2 a0 = fp8x4_to_bf16x4(T.v[j].x), a1 = fp8x4_to_bf16x4(T.v[j].y);
+      const uint2 a2 = fp8x4_to_bf16x4(T.v[j].z), a3 = fp8x4_to_bf16x4(T.v[j].w);
+      *(uint4*)(row + 32 * lane) = make_uint4(a0.x, a0.y, a1.x, a1.y);
+      *(uint4*)(row + 32 * lane + 16) = make_uint4(a2.x, a2.y, a3.x, a3.y);
+    } else if (lane < 36) {
+      *(uint4*)(row + 896 + 16 * (lane - 28)) = T.v[j];
+    }
+  }
+  if (lane < 16) scale_w[lane] = T.scale;
+}
+
+template <int FMT>
+__global__ __launch_bounds__(256) void attn_hgw_kernel(AttnArgs a, int pairs) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t hgw_lds[];
+  const int id = blockIdx.x;
+  const int hg = (id & 31) >> 3;
+  const int pair = (id >> 5) * 8 + (id & 7);
+  if (pair >= pairs) return;
+  const int S = a.n_splits;
+  const int qrow = pair / S, split = pair % S;
+  const int b = qrow / a.Sq, r = qrow % a.Sq;
+  const long long t = a.q_start + r;
+  const RowList L = row_list(a, t);
+  const int total = L.nw + L.nc;
+  const int p_begin = split * a.split_len;
+  const int p_end = min(p_begin + a.split_len, total);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int hl = lane & 15, grp = lane >> 4;
+  const int head = 16 * hg + hl;
+  uint8_t* wbuf = hgw_lds + wave * kWBufBytes;
+  uint16_t* q_s = (uint16_t*)(hgw_lds + 4 * kWBufBytes);  // [16 heads][kHgRow]
+  float* ml_s = (float*)(hgw_lds + 5 * kWBufBytes);         // [4 waves][16 heads][2]
+  float* esc_w = ml_s + 4 * 16 * 2 + 16 * wave;             // [4 waves][16] entry scales (fp8 cache)
+
+  const int ntiles = p_end > p_begin ? (p_end - p_begin + kWTile - 1) / kWTile : 0;
+  int tt = wave;
+  uint64_t cur = 0;
+  if (tt < ntiles) {
+    if (FMT == LCA_BF16) {
+      const WaveTile T0 = wave_load_tile(a, L, b, r, p_begin + kWTile * tt, p_end, lane);
+      wave_store_tile(wbuf, lane, T0);
+      cur = T0.valid;
+    } else {
+      const WaveTileMixed T0 = wave_load_tile_mixed(a, L, b, r, p_begin + kWTile * tt, p_end, lane);
+      wave_store_tile_mixed(wbuf, esc_w, lane, T0);
+      cur = T0.valid;
+    }
+  }
+
+  {  // the 16 heads' queries (16 KB), once per workgroup: thread -> 4 chunks of 16 bytes
+    const uint8_t* qg = (const uint8_t*)a.q + ((long long)qrow * 64 + 16 * hg) * 1024;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int c = threadIdx.x + 256 * x, h = c >> 6, piece = c & 63;
+      *(uint4*)((uint8_t*)q_s + h * (kHgRow * 2) + 16 * piece) = *(const uint4*)(qg + h * 1024 + 16 * piece);
+    }
+  }
+  __syncthreads();
+  f32x4_t acc_o[32];
+#pragma unroll
+  for (int dt = 0; dt < 32; ++dt) acc_o[dt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  float m_run = -INFINITY, l_run = 0.0f;
+  const uint16_t* qsp = q_s + hl * kHgRow + 8 * grp;
+
+  for (; tt < ntiles; tt += 4) {
+    // the next tile's rows are in flight while this one is scored (past the slice end: masked dummy rows)
+    WaveTile nxt;
+    WaveTileMixed nxm;
+    if (FMT == LCA_BF16)
+      nxt = wave_load_tile(a, L, b, r, p_begin + kWTile * (tt + 4), p_end, lane);
+    else
+      nxm = wave_load_tile_mixed(a, L, b, r, p_begin + kWTile * (tt + 4), p_end, lane);
+    const uint16_t* kt = (const uint16_t*)wbuf;
+
+    f32x4_t am = {0.0f, 0.0f, 0.0f, 0.0f}, ar = {0.0f, 0.0f, 0.0f, 0.0f};
+    const uint16_t* kp = kt + hl * kHgRow + 8 * grp;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      const bf16x8_t kv = __builtin_bit_cast(bf16x8_t, *(const uint4*)(kp + 32 * s));
+      const bf16x8_t qv = __builtin_bit_cast(bf16x8_t, *(const uint4*)(qsp + 32 * s));
+      if (FMT == LCA_MIXED_FP8 && s >= 14)  // RoPE channels: bf16, not scaled
+        ar = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qv, ar, 0, 0, 0);
+      else
+        am = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qv, am, 0, 0, 0);
+    }
+    float lg[4], esc[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      esc[x] = (FMT == LCA_MIXED_FP8) ? esc_w[4 * grp + x] : 1.0f;
+      const float l = (FMT == LCA_MIXED_FP8) ? a.scale * (esc[x] * am[x] + ar[x]) : a.scale * am[x];
+      lg[x] = ((cur >> (4 * grp + x)) & 1ull) ? l : -INFINITY;
+    }
+    float mt = fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3]));
+    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    // The reference max only moves when a logit exceeds it by more than kRescaleSlack (e^8 keeps every weight and
+    // sum far inside fp32, and bf16 keeps 8 significant bits at any scale), so the accumulators are rescaled a few
+    // times per row instead of on every tile.
+    const float m_new = (mt > m_run + kRescaleSlack) ? mt : m_run;
+    const float alpha = (m_new == m_run) ? 1.0f : __expf(m_run - m_new);
+    float pv[4], psum = 0.0f;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      pv[x] = (lg[x] == -INFINITY) ? 0.0f : __expf(lg[x] - m_new);
+      psum += pv[x];
+    }
+    psum += __shfl_xor(psum, 16, 64);
+    psum += __shfl_xor(psum, 32, 64);
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    s16x4_t pb, pbs;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      pb[x] = (short)f32_to_bf16(pv[x]);
+      pbs[x] = (FMT == LCA_MIXED_FP8) ? (short)f32_to_bf16(pv[x] * esc[x]) : pb[x];  // fp8 channels carry the scale
+    }
+    const uint16_t* vp = kt + (4 * grp + (hl >> 2)) * kHgRow + 4 * (hl & 3);
+    if (__ballot(alpha != 1.0f)) {  // wave-uniform: some head's reference max moved
+#pragma unroll
+      for (int dt = 0; dt < 32; ++dt) acc_o[dt] *= alpha;
+    }
+#pragma unroll
+    for (int dt = 0; dt < 32; ++dt) {
+      const s16x4_t av = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vp + 16 * dt));
+      acc_o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, (FMT == LCA_MIXED_FP8 && dt < 28) ? pbs : pb, acc_o[dt],
+                                                            0, 0, 0);
+    }
+    if (FMT == LCA_BF16) {  // the tile's LDS reads are complete: refill in place
+      wave_store_tile(wbuf, lane, nxt);
+      cur = nxt.valid;
+    } else {
+      wave_store_tile_mixed(wbuf, esc_w, lane, nxm);
+      cur = nxm.valid;
+    }
+  }
+
+  // merge the four waves (same heads, different entries)
+  __syncthreads();
+  if (grp == 0) {
+    ml_s[(wave * 16 + hl) * 2 + 0] = m_run;
+    ml_s[(wave * 16 + hl) * 2 + 1] = l_run;
+  }
+  __syncthreads();
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) M = fmaxf(M, ml_s[(w * 16 + hl) * 2 + 0]);
+  float Lsum = 0.0f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float mw = ml_s[(w * 16 + hl) * 2 + 0];
+    Lsum += (mw == -INFINITY) ? 0.0f : ml_s[(w * 16 + hl) * 2 + 1] * __expf(mw - M);
+  }
+  const float own = (m_run == -INFINITY) ? 0.0f : __expf(m_run - M);
+#pragma unroll
+  for (int dt = 0; dt < 32; ++dt) acc_o[dt] *= own;
+  float* ob = (float*)hgw_lds;  // [2][16][kHgOStride]
+  if (wave >= 2) {
+#pragma unroll
+    for (int dt = 0; dt < 32; ++dt)
+      *(f32x4_t*)(ob + ((wave - 2) * 16 + hl) * kHgOStride + 16 * dt + 4 * grp) = acc_o[dt];
+  }
+  __syncthreads();
+  if (wave < 2) {
+#pragma unroll
+    for (int dt = 0; dt < 32; ++dt) acc_o[dt] += *(const f32x4_t*)(ob + (wave * 16 + hl) * kHgOStride + 16 * dt + 4 * grp);
+  }
+  __syncthreads();
+  if (wave == 1) {
+#pragma unroll
+    for (int dt = 0; dt < 32; ++dt) *(f32x4_t*)(ob + hl * kHgOStride + 16 * dt + 4 * grp) = acc_o[dt];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int dt = 0; dt < 32; ++dt) acc_o[dt] += *(const f32x4_t*)(ob + hl * kHgOStride + 16 * dt + 4 * grp);
+
+  if (S == 1) {
+    const float z = a.sink[head];
+    const float Mz = fmaxf(M, z);
+    float den = 0.0f, f = 0.0f;
+    if (Mz != -INFINITY) {
+      den = ((z == -INFINITY) ? 0.0f : __expf(z - Mz)) + ((M == -INFINITY) ? 0.0f : Lsum * __expf(M - Mz));
+      f = (M == -INFINITY) ? 0.0f : __expf(M - Mz) / den;
+    }
+    const long long obase = ((long long)qrow * 64 + head) * 512;
+#pragma unroll
+    for (int dt = 0; dt < 32; ++dt) {
+      const int c0 = 16 * dt + 4 * grp;
+      if (a.out_format == LCA_F32) {
+        *(float4*)((float*)a.out + obase + c0) =
+            make_float4(acc_o[dt][0] * f, acc_o[dt][1] * f, acc_o[dt][2] * f, acc_o[dt][3] * f);
+      } else {
+        uint2 w2;
+        w2.x = (uint32_t)f32_to_bf16(acc_o[dt][0] * f) | ((uint32_t)f32_to_bf16(acc_o[dt][1] * f) << 16);
+        w2.y = (uint32_t)f32_to_bf16(acc_o[dt][2] * f) | ((uint32_t)f32_to_bf16(acc_o[dt][3] * f) << 16);
+        *(uint2*)((uint16_t*)a.out + obase + c0) = w2;
+      }
+    }
+    if (a.lse && grp == 0) a.lse[(long long)qrow * 64 + head] = (Mz == -INFINITY) ? -INFINITY : Mz + __logf(den);
+  } else {
+    const long long item = (long long)qrow * S + split;
+    float* po = a.part_o + (item * 64 + head) * 512;
+#pragma unroll
+    for (int dt = 0; dt < 32; ++dt) *(f32x4_t*)(po + 16 * dt + 4 * grp) = acc_o[dt];
+    if (grp == 0) {
+      a.part_ml[(item * 64 + head) * 2 + 0] = M;
+      a.part_ml[(item * 64 + head) * 2 + 1] = Lsum;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
 // vector-ALU kernel: H * D <= 8192, any supported format (fp32 accumulation)
 // ------------------------------------------------------------------------------------------------
 constexpr int kSimtTE = 8;
@@ -419,10 +748,7 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
   const long long ob = (((long long)b * a.Sq + r) * H + h) * D;
   for (int x = threadIdx.x; x < D; x += blockDim.x) {
     float acc = 0.0f;
-    for (int s = 0; s < S; ++s) {
-      const float wgt = wsplit[s];
-      if (wgt != 0.0f) acc = fmaf(wgt, a.part_o[((item0 + s) * H + h) * D + x], acc);
-    }
+    for (int s = 0; s < S; ++s) acc = fmaf(wsplit[s], a.part_o[((item0 + s) * H + h) * D + x], acc);
     const float v = acc * inv;
     if (a.out_format == LCA_F32)
       ((float*)a.out)[ob + x] = v;
@@ -433,6 +759,7 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
 
 constexpr size_t kMfmaLds = (size_t)kTE * kRowStride * 2 + (size_t)512 * kTStride * 2 + kTE * 4 * 2;
 static bool g_attn_attr[64];
+static bool g_hg_attr[64];
 
 bool attn_uses_mfma(int H, int D, int q_format, int kv_format) {
   return H == 64 && D == 512 && q_format == LCA_BF16 && (kv_format == LCA_BF16 || kv_format == LCA_MIXED_FP8);
@@ -442,7 +769,25 @@ hipError_t launch_attn(AttnArgs a, hipStream_t st) {
   const bool mfma = attn_uses_mfma(a.H, a.D, a.q_format, a.comp.format);
   dim3 grid((unsigned)a.n_splits, (unsigned)a.Sq, (unsigned)a.B);
   clear_stale_error();
-  if (mfma) {
+  if (mfma && a.hg_mode) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    if (dev >= 0 && dev < 64 && !g_hg_attr[dev]) {
+      hipError_t e = hipFuncSetAttribute((const void*)attn_hgw_kernel<LCA_BF16>,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)kHgwLds);
+      if (e == hipSuccess)
+        e = hipFuncSetAttribute((const void*)attn_hgw_kernel<LCA_MIXED_FP8>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kHgwLds);
+      if (e != hipSuccess) return e;
+      g_hg_attr[dev] = true;
+    }
+    const int pairs = a.B * a.Sq * a.n_splits;
+    const dim3 hgrid((unsigned)(((pairs + 7) / 8) * 32));
+    if (a.comp.format == LCA_BF16)
+      hipLaunchKernelGGL(attn_hgw_kernel<LCA_BF16>, hgrid, dim3(256), kHgwLds, st, a, pairs);
+    else
+      hipLaunchKernelGGL(attn_hgw_kernel<LCA_MIXED_FP8>, hgrid, dim3(256), kHgwLds, st, a, pairs);
+  } else if (mfma) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) dev = 0;
     if (dev >= 0 && dev < 64 && !g_attn_attr[dev]) {

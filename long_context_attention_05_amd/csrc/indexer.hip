@@ -292,6 +292,8 @@ __global__ __launch_bounds__(256, 2) void idx_score_decode(IdxArgs a, int tiles_
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 5, col = lane & 31;
   const int b = blockIdx.y;
+  if (a.sel_state && blockIdx.x == 0)  // the select that follows accumulates into this row's state
+    for (int i = threadIdx.x; i < kSelStateInts; i += blockDim.x) a.sel_state[(long long)b * kSelStateInts + i] = 0;
   const int nvis = nvis_of(a.q_start, a.m, a.N);
   const int ntiles = (nvis + kDecTile - 1) / kDecTile;
   const int t_begin = blockIdx.x * tiles_per_block;
@@ -376,7 +378,119 @@ __global__ __launch_bounds__(256, 2) void idx_score_decode(IdxArgs a, int tiles_
   }
 }
 
+// ------------------------------------------------------------------------------------------------
+// decode kernel for fp4 keys and queries: block-scaled MFMA on the stored codes
+// ------------------------------------------------------------------------------------------------
+// v_mfma_scale_f32_16x16x128_f8f6f4 with both operands in fp4 e2m1 applies one E8M0 scale per lane to the lane's
+// 32 contraction slots (A: lane l holds row l % 16, slots 32 (l / 16) .. + 31; B: column l % 16, same slots).  The
+// cache scales each 16 elements, so each lane fills the first 16 slots of its block with one 16-element group and
+// the other 16 with zeros; two instructions (h = 0, 1) cover the 8 groups of a 128-dim row: block b of
+// instruction h holds group 2b + h.  Products of fp4 values and their block sums are exact, scaled by powers of
+// two, so the per-head dots equal the exact ones whenever they fit fp32 -- the fixed head-reduction order then
+// makes the scores bit-reproducible.  The 16x16 accumulator holds heads 16T + 4(l/16) + r for key l % 16.
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8_t;
+
+__device__ __forceinline__ i32x8_t fp4_operand(uint32_t lo, uint32_t hi) {
+  i32x8_t v = {(int)lo, (int)hi, 0, 0, 0, 0, 0, 0};
+  return v;
+}
+
+__global__ __launch_bounds__(256, 2) void idx_score_decode_fp4(IdxArgs a, int tiles_per_block) {
+#pragma clang fp contract(off)
+  extern __shared__ __attribute__((aligned(16))) uint8_t dec_lds[];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = lane >> 4, col = lane & 15;
+  const int b = blockIdx.y;
+  if (a.sel_state && blockIdx.x == 0)  // the select that follows accumulates into this row's state
+    for (int i = threadIdx.x; i < kSelStateInts; i += blockDim.x) a.sel_state[(long long)b * kSelStateInts + i] = 0;
+  const int nvis = nvis_of(a.q_start, a.m, a.N);
+  const int ntiles = (nvis + kDecTile - 1) / kDecTile;
+  const int t_begin = blockIdx.x * tiles_per_block;
+  const int t_end = min(t_begin + tiles_per_block, ntiles);
+  if (t_begin >= t_end) return;
+  constexpr int RB = kKRowF4;
+
+  uint4 pre[8];
+  dec_load_tile<LCA_FP4>(a, b, t_begin * kDecTile, nvis, pre);
+
+  // query operands: M-tile T = heads 16T .. 16T + 15; lane holds head 16T + col, groups 2g and 2g + 1
+  uint32_t qc[4][4];  // [T][0..1] = group 2g codes, [2..3] = group 2g + 1 codes
+  int qs[4][2];
+  float wv[4][4];
+#pragma unroll
+  for (int T = 0; T < 4; ++T) {
+    const long long row = (long long)b * 64 + 16 * T + col;
+    const uint4 c = *(const uint4*)((const uint8_t*)a.q.data + row * 64 + 16 * g);
+    qc[T][0] = c.x;
+    qc[T][1] = c.y;
+    qc[T][2] = c.z;
+    qc[T][3] = c.w;
+    const uint32_t s2 = *(const uint16_t*)((const uint8_t*)a.q.scale + row * 8 + 2 * g);
+    qs[T][0] = (int)(s2 & 255u);
+    qs[T][1] = (int)(s2 >> 8);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) wv[T][r] = a.w[(long long)b * 64 + 16 * T + 4 * g + r];
+  }
+  dec_store_tile<LCA_FP4>(dec_lds, pre);
+  __syncthreads();
+
+  for (int tt = t_begin; tt < t_end; ++tt) {
+    const int cur = (tt - t_begin) & 1;
+    if (tt + 1 < t_end) dec_load_tile<LCA_FP4>(a, b, (tt + 1) * kDecTile, nvis, pre);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const uint8_t* rowp = dec_lds + cur * (kDecTile * RB) + (32 * wave + 16 * u + col) * RB;
+      const uint4 kc = *(const uint4*)(rowp + 16 * g);
+      const uint32_t ks2 = *(const uint16_t*)(rowp + 64 + 2 * g);
+      const i32x8_t kop0 = fp4_operand(kc.x, kc.y), kop1 = fp4_operand(kc.z, kc.w);
+      const int ks0 = (int)(ks2 & 255u), ks1 = (int)(ks2 >> 8);
+      f32x4_t acc[4];
+#pragma unroll
+      for (int T = 0; T < 4; ++T) {
+        acc[T] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        acc[T] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fp4_operand(qc[T][0], qc[T][1]), kop0, acc[T], 4, 4,
+                                                                  0, qs[T][0], 0, ks0);
+        acc[T] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fp4_operand(qc[T][2], qc[T][3]), kop1, acc[T], 4, 4,
+                                                                  0, qs[T][1], 0, ks1);
+      }
+      // halving tree: h+32 (T, T+2), h+16 (T, T+1) in-lane; h+8 (g, g+2) and h+4 (g, g+1) across lanes;
+      // h+2, h+1 in-lane
+      float l1[2][4], l2[4], l3[4], l4[4];
+#pragma unroll
+      for (int T = 0; T < 2; ++T)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p0 = wv[T][r] * fmaxf(acc[T][r], 0.0f);
+          const float p1 = wv[T + 2][r] * fmaxf(acc[T + 2][r], 0.0f);
+          l1[T][r] = p0 + p1;
+        }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) l2[r] = l1[0][r] + l1[1][r];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float o = __shfl_xor(l2[r], 32, 64);
+        l3[r] = (g < 2) ? (l2[r] + o) : (o + l2[r]);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float o = __shfl_xor(l3[r], 16, 64);
+        l4[r] = ((g & 1) == 0) ? (l3[r] + o) : (o + l3[r]);
+      }
+      const float s = (l4[0] + l4[2]) + (l4[1] + l4[3]);
+      const int e = tt * kDecTile + 32 * wave + 16 * u + col;
+      if (g == 0 && e < nvis) a.keys[(long long)b * a.N + e] = score_key(s);
+    }
+    if (tt + 1 < t_end) dec_store_tile<LCA_FP4>(dec_lds + (cur ^ 1) * (kDecTile * RB), pre);
+    __syncthreads();
+  }
+}
+
 static bool g_dec_attr[64];
+
+bool indexer_uses_decode_kernel(int B, int Sq, int HI, int DI, int q_format, int k_format) {
+  (void)B;
+  return Sq == 1 && HI == 64 && DI == 128 && q_format == k_format && (q_format == LCA_BF16 || q_format == LCA_FP4);
+}
 
 hipError_t launch_indexer_scores(const IdxArgs& a, hipStream_t st) {
   const int nvis_max = nvis_of(a.q_start + a.Sq - 1, a.m, a.N);
@@ -384,7 +498,7 @@ hipError_t launch_indexer_scores(const IdxArgs& a, hipStream_t st) {
   clear_stale_error();
   const bool mfma = a.HI == 64 && a.DI == 128 && a.q.format == a.k.format &&
                     (a.q.format == LCA_BF16 || a.q.format == LCA_FP4);
-  if (mfma && a.Sq == 1) {
+  if (indexer_uses_decode_kernel(a.B, a.Sq, a.HI, a.DI, a.q.format, a.k.format)) {
     const int ntiles = (nvis_max + kDecTile - 1) / kDecTile;
     int bps = (512 + a.B - 1) / a.B;  // about two workgroups per CU over the whole batch
     if (bps > ntiles) bps = ntiles;
@@ -402,8 +516,8 @@ hipError_t launch_indexer_scores(const IdxArgs& a, hipStream_t st) {
       hipLaunchKernelGGL(idx_score_decode<LCA_BF16>, dim3((unsigned)bps, (unsigned)a.B), dim3(256),
                          2 * kDecTile * kKRowB, st, a, tpb);
     else
-      hipLaunchKernelGGL(idx_score_decode<LCA_FP4>, dim3((unsigned)bps, (unsigned)a.B), dim3(256),
-                         2 * kDecTile * kKRowF4, st, a, tpb);
+      hipLaunchKernelGGL(idx_score_decode_fp4, dim3((unsigned)bps, (unsigned)a.B), dim3(256), 2 * kDecTile * kKRowF4,
+                         st, a, tpb);
   } else if (mfma) {
     const int qpb = a.Sq >= 16 ? 16 : a.Sq;
     dim3 grid((unsigned)((nvis_max + kMfmaEntriesPerBlock - 1) / kMfmaEntriesPerBlock),

@@ -29,7 +29,10 @@ struct IdxArgs {
   uint32_t* keys;  // [B][Sq][N] order-preserving score keys (workspace)
   int B, Sq, HI, DI, N, m;
   long long q_start;
+  int* sel_state;  // nullable: [B * Sq][kSelStateInts] per-row select state the decode kernels zero
 };
+// Whether launch_indexer_scores takes the one-row-per-sequence decode kernels (which zero sel_state).
+bool indexer_uses_decode_kernel(int B, int Sq, int HI, int DI, int q_format, int k_format);
 hipError_t launch_indexer_scores(const IdxArgs& a, hipStream_t st);
 
 // stage 2b, exact top-k (topk.hip)
@@ -39,7 +42,13 @@ struct SelArgs {
   float* score_out;      // nullable [rows][k]
   int rows, Sq, N, m, k;
   long long q_start;
+  // multi-workgroup select (decode rows); all null for the one-workgroup-per-row select
+  int* sel_state;  // [rows][kSelStateInts]: 2048-bin histogram, arrival counter (zeroed before the call)
+  int* counts;     // [rows][slices]
+  uint2* cand;     // [rows][N] (key, entry) candidates, slice s at [s * kSliceKeys]
 };
+constexpr int kSelStateInts = 2048 + 64;  // histogram + arrival counter (padded)
+constexpr int kSliceKeys = 4096;          // keys per workgroup in the multi-workgroup select
 hipError_t launch_topk(const SelArgs& a, hipStream_t st);
 
 // stages 3/4, attention (attn.hip)
@@ -63,6 +72,7 @@ struct AttnArgs {
   int n_splits, split_len;
   float* part_o;   // [B][Sq][n_splits][H][D]
   float* part_ml;  // [B][Sq][n_splits][H][2]
+  int hg_mode;     // 1: one workgroup per (16-head group, row, split) -- few rows (decode)
 };
 bool attn_uses_mfma(int H, int D, int q_format, int kv_format);
 hipError_t launch_attn(AttnArgs a, hipStream_t st);

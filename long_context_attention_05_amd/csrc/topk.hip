@@ -206,6 +206,262 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(SelArgs a) {
   }
 }
 
+// ------------------------------------------------------------------------------------------------
+// multi-workgroup select for decode rows (few rows, up to ~1M entries each)
+// ------------------------------------------------------------------------------------------------
+// Each row is cut into slices of kSliceKeys entries, one 256-thread workgroup per slice.
+//   topk_hist_kernel:    slice histogram of key bits [31:21] in LDS, added into the row's histogram.
+//   topk_collect_kernel: every slice finds the border bin b1 from the row histogram, writes its keys with
+//                        bin >= b1 (a superset of the selection of about k + |border| keys) in entry order to its
+//                        candidate segment, then counts itself in with an atomic; the last slice of the row to
+//                        arrive runs passes 2-3 and the ordered output over the row's candidates.
+// The row histogram and arrival counter are zeroed by the scoring kernel that precedes these launches.
+constexpr int kMbThreads = 256;
+constexpr int kMbPerThread = kSliceKeys / kMbThreads;  // 16
+constexpr int kCandCap = 6144;                         // candidates staged in LDS by the finishing slice
+
+__device__ __forceinline__ int sel_row_nvis(const SelArgs& a, int row) {
+  const long long t = a.q_start + row % a.Sq;
+  const long long nv = t / a.m;
+  return (int)(nv < a.N ? nv : a.N);
+}
+
+// Exclusive scan over a 256-thread block.
+__device__ __forceinline__ int block256_excl_scan(int v, int* wsum, int& tot) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int n = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += n;
+  }
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  int before = 0;
+  tot = 0;
+#pragma unroll
+  for (int i = 0; i < kMbThreads / 64; ++i) {
+    const int x = wsum[i];
+    if (i < w) before += x;
+    tot += x;
+  }
+  __syncthreads();
+  return before + incl - v;
+}
+
+// Bin (of 2048, descending order) holding the need-th largest key; *above = keys in higher bins.  256 threads,
+// thread t owning bins 2047 - 8t - j, j = 0..7.
+__device__ __forceinline__ int find_bin256(const int* hist, int need, int* wsum, int* sh, int* above) {
+  const int t = threadIdx.x;
+  int loc[8], sum = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    loc[j] = hist[2047 - 8 * t - j];
+    sum += loc[j];
+  }
+  int tot;
+  int cum = block256_excl_scan(sum, wsum, tot);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (cum < need && cum + loc[j] >= need) {
+      sh[0] = 2047 - 8 * t - j;
+      sh[1] = cum;
+    }
+    cum += loc[j];
+  }
+  __syncthreads();
+  *above = sh[1];
+  return sh[0];
+}
+
+__global__ __launch_bounds__(kMbThreads) void topk_hist_kernel(SelArgs a) {
+  __shared__ int hist[2048];
+  const int p = blockIdx.x, row = blockIdx.y;
+  const int nvis = sel_row_nvis(a, row);
+  const int s0 = p * kSliceKeys;
+  if (nvis <= a.k || s0 >= nvis) return;
+  const int s1 = min(s0 + kSliceKeys, nvis);
+  for (int i = threadIdx.x; i < 2048; i += kMbThreads) hist[i] = 0;
+  __syncthreads();
+  const uint32_t* kg = a.keys + (long long)row * a.N;
+  uint32_t kv[kMbPerThread];
+#pragma unroll
+  for (int u = 0; u < kMbPerThread; ++u) {
+    const int i = s0 + threadIdx.x + kMbThreads * u;
+    kv[u] = i < s1 ? kg[i] : 0u;
+  }
+#pragma unroll
+  for (int u = 0; u < kMbPerThread; ++u)
+    if (s0 + (int)threadIdx.x + kMbThreads * u < s1) atomicAdd(&hist[kv[u] >> 21], 1);
+  __syncthreads();
+  int* gh = a.sel_state + (long long)row * kSelStateInts;
+  for (int i = threadIdx.x; i < 2048; i += kMbThreads) {
+    const int c = hist[i];
+    if (c) atomicAdd(&gh[i], c);
+  }
+}
+
+// Candidate j of the row (entry order): segment of j found by binary search over the segment offsets.
+__device__ __forceinline__ uint2 cand_global(const SelArgs& a, int row, const int* seg_off, int nseg, int j) {
+  int lo = 0, hi = nseg - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (seg_off[mid] <= j) lo = mid; else hi = mid - 1;
+  }
+  return a.cand[(long long)row * a.N + (long long)lo * kSliceKeys + (j - seg_off[lo])];
+}
+
+__global__ __launch_bounds__(kMbThreads) void topk_collect_kernel(SelArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t mb_lds[];  // the slice's keys
+  __shared__ int hist[2048];
+  __shared__ int wsum[kMbThreads / 64];
+  __shared__ int sh[4];
+  const int p = blockIdx.x, row = blockIdx.y, tid = threadIdx.x;
+  const int nvis = sel_row_nvis(a, row);
+  const int k = a.k;
+  int32_t* out = a.idx_out + (long long)row * k;
+  float* sout = a.score_out ? a.score_out + (long long)row * k : nullptr;
+  const uint32_t* kg = a.keys + (long long)row * a.N;
+  if (nvis <= k) {
+    if (p == 0)
+      for (int j = tid; j < k; j += kMbThreads) {
+        out[j] = j < nvis ? j : -1;
+        if (sout) sout[j] = j < nvis ? key_score(kg[j]) : -INFINITY;
+      }
+    return;
+  }
+  const int P = (nvis + kSliceKeys - 1) / kSliceKeys;
+  if (p >= P) return;
+  int* gh = a.sel_state + (long long)row * kSelStateInts;
+  const int slots = (a.N + kSliceKeys - 1) / kSliceKeys;
+
+  // border bin b1 from the row histogram
+  for (int i = tid; i < 2048; i += kMbThreads) hist[i] = gh[i];
+  __syncthreads();
+  int above1;
+  const int b1 = find_bin256(hist, k, wsum, sh, &above1);
+
+  // this slice's keys with bin >= b1, in entry order
+  const int s0 = p * kSliceKeys, s1 = min(s0 + kSliceKeys, nvis);
+#pragma unroll
+  for (int u = 0; u < kMbPerThread; ++u) {
+    const int i = s0 + tid + kMbThreads * u;
+    mb_lds[tid + kMbThreads * u] = i < s1 ? kg[i] : 0u;
+  }
+  __syncthreads();
+  int cnt = 0;
+#pragma unroll
+  for (int j = 0; j < kMbPerThread; ++j) {
+    const int jj = kMbPerThread * tid + j;
+    cnt += (s0 + jj < s1 && (int)(mb_lds[jj] >> 21) >= b1) ? 1 : 0;
+  }
+  int tot;
+  int pos = block256_excl_scan(cnt, wsum, tot);
+  uint2* seg = a.cand + (long long)row * a.N + s0;
+#pragma unroll
+  for (int j = 0; j < kMbPerThread; ++j) {
+    const int jj = kMbPerThread * tid + j;
+    const uint32_t key = mb_lds[jj];
+    if (s0 + jj < s1 && (int)(key >> 21) >= b1) seg[pos++] = make_uint2(key, (uint32_t)(s0 + jj));
+  }
+  if (tid == 0) a.counts[(long long)row * slots + p] = tot;
+}
+
+// One workgroup per row: passes 2-3 and the ordered output over the row's candidates (a separate launch, so the
+// candidates written by every slice are visible without cross-workgroup fences).
+__global__ __launch_bounds__(kMbThreads) void topk_finish_kernel(SelArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t mb_lds[];  // the row's candidates
+  __shared__ int hist[2048];
+  __shared__ int seg_off[257];
+  __shared__ int wsum[kMbThreads / 64];
+  __shared__ int sh[4];
+  const int row = blockIdx.x, tid = threadIdx.x;
+  const int nvis = sel_row_nvis(a, row);
+  const int k = a.k;
+  if (nvis <= k) return;  // written by the collect kernel
+  int32_t* out = a.idx_out + (long long)row * k;
+  float* sout = a.score_out ? a.score_out + (long long)row * k : nullptr;
+  const int P = (nvis + kSliceKeys - 1) / kSliceKeys;
+  const int slots = (a.N + kSliceKeys - 1) / kSliceKeys;
+  const int* gh = a.sel_state + (long long)row * kSelStateInts;
+  for (int i = tid; i < 2048; i += kMbThreads) hist[i] = gh[i];
+  __syncthreads();
+  int above1;
+  const int b1 = find_bin256(hist, k, wsum, sh, &above1);
+  const int c = tid < P ? a.counts[(long long)row * slots + tid] : 0;
+  int total;
+  const int off = block256_excl_scan(c, wsum, total);
+  if (tid < P) seg_off[tid] = off;
+  __syncthreads();
+  const bool in_lds = total <= kCandCap;
+  uint2* cl = (uint2*)mb_lds;
+  if (in_lds) {
+    for (int j = tid; j < total; j += kMbThreads) cl[j] = cand_global(a, row, seg_off, P, j);
+  }
+  __syncthreads();
+  auto cand = [&](int j) -> uint2 { return in_lds ? cl[j] : cand_global(a, row, seg_off, P, j); };
+
+  // passes 2 and 3 over the border candidates
+  int need = k - above1;
+  uint32_t prefix = (uint32_t)b1 << 21, mask = 0xFFE00000u;
+  for (int pass = 0; pass < 2; ++pass) {
+    const int shf = pass == 0 ? 10 : 0;
+    const uint32_t digit = pass == 0 ? 0x7FFu : 0x3FFu;
+    for (int i = tid; i < 2048; i += kMbThreads) hist[i] = 0;
+    __syncthreads();
+    for (int j = tid; j < total; j += kMbThreads) {
+      const uint32_t key = cand(j).x;
+      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shf) & digit], 1);
+    }
+    __syncthreads();
+    int above;
+    const int bn = find_bin256(hist, need, wsum, sh, &above);
+    need -= above;
+    prefix |= (uint32_t)bn << shf;
+    mask |= digit << shf;
+    __syncthreads();
+  }
+  const uint32_t kappa = prefix;
+
+  // ordered output: candidates > kappa, then the first `need` equal to kappa
+  int sel_run = 0, eq_run = 0;
+  for (int base = 0; base < total && sel_run < k; base += kMbThreads * 8) {
+    const int j0 = base + 8 * tid;
+    uint2 cv[8];
+    int gt = 0, eq = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bool v = j0 + j < total;
+      cv[j] = v ? cand(j0 + j) : make_uint2(0u, 0u);
+      gt += (v && cv[j].x > kappa) ? 1 : 0;
+      eq += (v && cv[j].x == kappa) ? 1 : 0;
+    }
+    int ptot;
+    const int packed = block256_excl_scan(gt | (eq << 16), wsum, ptot);
+    const int gt_before = packed & 0xFFFF, eq_before = packed >> 16;
+    const int rem = need - eq_run > 0 ? need - eq_run : 0;
+    int o = sel_run + gt_before + (eq_before < rem ? eq_before : rem);
+    int eq_seen = eq_run + eq_before;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j0 + j >= total) break;
+      bool sel = cv[j].x > kappa;
+      if (cv[j].x == kappa) {
+        sel = eq_seen < need;
+        ++eq_seen;
+      }
+      if (sel) {
+        out[o] = (int32_t)cv[j].y;
+        if (sout) sout[o] = key_score(cv[j].x);
+        ++o;
+      }
+    }
+    const int tg = ptot & 0xFFFF, te = ptot >> 16;
+    sel_run += tg + (te < rem ? te : rem);
+    eq_run += te;
+  }
+}
+
 static bool g_lds_attr_set = false;
 
 hipError_t launch_topk(const SelArgs& a, hipStream_t st) {
@@ -214,7 +470,14 @@ hipError_t launch_topk(const SelArgs& a, hipStream_t st) {
   long long nv = (a.q_start + a.Sq - 1) / a.m;
   const int nvis_max = (int)(nv < a.N ? nv : a.N);
   clear_stale_error();
-  if (nvis_max <= kLdsKeys) {
+  if (a.sel_state) {
+    const int P = nvis_max > 0 ? (nvis_max + kSliceKeys - 1) / kSliceKeys : 1;
+    dim3 grid((unsigned)P, (unsigned)a.rows);
+    if (nvis_max > a.k) hipLaunchKernelGGL(topk_hist_kernel, grid, dim3(kMbThreads), 0, st, a);
+    hipLaunchKernelGGL(topk_collect_kernel, grid, dim3(kMbThreads), (size_t)kSliceKeys * 4, st, a);
+    if (nvis_max > a.k)
+      hipLaunchKernelGGL(topk_finish_kernel, dim3((unsigned)a.rows), dim3(kMbThreads), (size_t)kCandCap * 8, st, a);
+  } else if (nvis_max <= kLdsKeys) {
     if (!g_lds_attr_set) {
       hipError_t e = hipFuncSetAttribute((const void*)topk_select_kernel<true>,
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSelDynLds);
