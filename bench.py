@@ -239,11 +239,12 @@ def main():
         durs = [ev.elapsed_ms(a, b) for a, b in pairs]
         avg_ms = sum(durs) / len(durs)
         if w.Sq == 1:
+            kname = "idx_score_decode_fp4" if w.key_fmt == "fp4" else "idx_score_decode_bf16"
             per_launch = step.score_kernel_bytes()
             achieved = per_launch / (avg_ms / 1e3) / 1e9
-            res["roofline"] = {"kernel": "idx_score_decode", "bound": "hbm", "achieved": achieved,
+            res["roofline"] = {"kernel": kname, "bound": "hbm", "achieved": achieved,
                                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                               "traffic": traffic_record("idx_score_decode", w.name, src, per_launch),
+                               "traffic": traffic_record(kname, w.name, src, per_launch),
                                "avg_launch_us": avg_ms * 1e3, "algorithmic_bytes_per_launch": per_launch}
         else:
             per_launch = step.score_kernel_flops()

@@ -225,7 +225,7 @@ void lca_set_score_events(void* ev_begin, void* ev_end) {
 }
 
 // Workspace of indexer_score_topk: the score keys [B * Sq][N]; for one query row per sequence (decode) also the
-// multi-workgroup select buffers: per-row state, per-slice counts and candidate segments.
+// select buffers of the decode path: per-row histograms, per-slice counts and candidate segments.
 struct IdxWs {
   size_t keys, state, counts, cand, total;
 };
@@ -278,6 +278,10 @@ int indexer_score_topk(lca_tensor qI, const float* w, lca_tensor kI, int B, int 
   int* state = multi ? (int*)(wsb + L.state) : nullptr;
   IdxArgs a{qI, kI, w, (uint32_t*)(wsb + L.keys), B, Sq, HI, DI, N, m, q_start_pos, state};
   if (N > 0) {
+    if (state) {  // the decode scoring kernels add into the row histograms
+      rc = hip_status(launch_sel_zero(state, B * Sq, st));
+      if (rc) return rc;
+    }
     const bool timed = t_ev_begin && t_ev_end;
     if (timed && hipEventRecord(t_ev_begin, st) != hipSuccess) return LCA_ERR_HIP;
     rc = hip_status(launch_indexer_scores(a, st));

@@ -228,166 +228,166 @@ __global__ __launch_bounds__(256) void idx_score_mfma(IdxArgs a, int qpb) {
 }
 
 // ------------------------------------------------------------------------------------------------
-// decode MFMA kernel (one query row per sequence): the key stream is the whole cost, so keys move in
-// fully coalesced 16-byte loads (16 lanes per 256-byte key row) into a double-buffered LDS tile while the
-// previous tile is scored; the query block stays in registers for the whole entry range of the workgroup.
+// decode kernels (one query row per sequence): the key stream is the whole cost
 // ------------------------------------------------------------------------------------------------
-constexpr int kDecTile = 128;      // entries per tile, 32 per wave
-constexpr int kKRowB = 272;        // LDS bytes per bf16 key row (256 + 16 padding)
-constexpr int kKRowF4 = 80;        // LDS bytes per fp4 key row (64 codes + 8 scales + 8 padding)
+// Both formats use 16-key MFMA column blocks whose B operand is a run of whole cache rows, so each lane loads its
+// operand bytes straight from HBM into registers (no LDS staging, no barriers in the loop).  A wave streams its own
+// slab of keys in stages; the next stage's loads are issued, unconditionally, before the current stage is scored,
+// so the wait for a stage's data never drains the loads behind it.  Past the end of the workgroup's range the
+// addresses clamp to its last key (loaded, scored, never written).
+//
+// Accumulator layout of both 16x16 MFMAs: lane l, register r holds head 16 T + 4 (l / 16) + r (M-tile T) for key
+// l % 16.  The fixed halving tree over the 64 heads is then: h+32 (T, T+2) and h+16 (T, T+1) in-lane, h+8 (lanes
+// l, l ^ 32) and h+4 (l, l ^ 16) across lanes, h+2 and h+1 in-lane.
+//
+// With a row histogram to fill (decode select), each workgroup counts its keys' bits [31:21] in LDS and adds the
+// counts into the row's histogram, zeroed before the launch.  The select that follows reads it instead of making
+// its own first pass over the keys.
 
-template <int FMT>
-constexpr int dec_row_bytes() { return FMT == LCA_BF16 ? kKRowB : kKRowF4; }
-
-template <int FMT>
-__device__ __forceinline__ void dec_load_tile(const IdxArgs& a, int b, int e0, int nvis, uint4 (&v)[8]) {
-  const int tid = threadIdx.x;
-  if (FMT == LCA_BF16) {
+__device__ __forceinline__ float head_tree(const f32x4_t (&acc)[4], const float (&wv)[4][4], int g) {
+  float l1[2][4], l2[4], l3[4], l4[4];
 #pragma unroll
-    for (int x = 0; x < 8; ++x) {
-      const int c = tid + 256 * x, e = c >> 4, piece = c & 15;
-      v[x] = (e0 + e < nvis)
-                 ? *(const uint4*)((const uint8_t*)a.k.data + ((long long)b * a.k.cap + e0 + e) * 256 + 16 * piece)
-                 : make_uint4(0, 0, 0, 0);
-    }
-  } else {
+  for (int T = 0; T < 2; ++T)
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const int c = tid + 256 * x, e = c >> 2, piece = c & 3;
-      v[x] = (e0 + e < nvis)
-                 ? *(const uint4*)((const uint8_t*)a.k.data + ((long long)b * a.k.cap + e0 + e) * 64 + 16 * piece)
-                 : make_uint4(0, 0, 0, 0);
+    for (int r = 0; r < 4; ++r) {
+      const float p0 = wv[T][r] * fmaxf(acc[T][r], 0.0f);
+      const float p1 = wv[T + 2][r] * fmaxf(acc[T + 2][r], 0.0f);
+      l1[T][r] = p0 + p1;
     }
-    const int e = tid >> 1, half = tid & 1;
-    v[2].x = (e0 + e < nvis) ? *(const uint32_t*)((const uint8_t*)a.k.scale + ((long long)b * a.k.cap + e0 + e) * 8 +
-                                                  4 * half)
-                             : 0u;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) l2[r] = l1[0][r] + l1[1][r];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float o = __shfl_xor(l2[r], 32, 64);
+    l3[r] = (g < 2) ? (l2[r] + o) : (o + l2[r]);
   }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float o = __shfl_xor(l3[r], 16, 64);
+    l4[r] = ((g & 1) == 0) ? (l3[r] + o) : (o + l3[r]);
+  }
+  return (l4[0] + l4[2]) + (l4[1] + l4[3]);
 }
 
-template <int FMT>
-__device__ __forceinline__ void dec_store_tile(uint8_t* buf, const uint4 (&v)[8]) {
-  const int tid = threadIdx.x;
-  if (FMT == LCA_BF16) {
-#pragma unroll
-    for (int x = 0; x < 8; ++x) {
-      const int c = tid + 256 * x, e = c >> 4, piece = c & 15;
-      *(uint4*)(buf + e * kKRowB + 16 * piece) = v[x];
-    }
-  } else {
-#pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const int c = tid + 256 * x, e = c >> 2, piece = c & 3;
-      *(uint4*)(buf + e * kKRowF4 + 16 * piece) = v[x];
-    }
-    const int e = tid >> 1, half = tid & 1;
-    *(uint32_t*)(buf + e * kKRowF4 + 64 + 4 * half) = v[2].x;
-  }
-}
-
-template <int FMT>
-__global__ __launch_bounds__(256, 2) void idx_score_decode(IdxArgs a, int tiles_per_block) {
-#pragma clang fp contract(off)
-  extern __shared__ __attribute__((aligned(16))) uint8_t dec_lds[];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int g = lane >> 5, col = lane & 31;
-  const int b = blockIdx.y;
-  if (a.sel_state && blockIdx.x == 0)  // the select that follows accumulates into this row's state
-    for (int i = threadIdx.x; i < kSelStateInts; i += blockDim.x) a.sel_state[(long long)b * kSelStateInts + i] = 0;
-  const int nvis = nvis_of(a.q_start, a.m, a.N);
-  const int ntiles = (nvis + kDecTile - 1) / kDecTile;
-  const int t_begin = blockIdx.x * tiles_per_block;
-  const int t_end = min(t_begin + tiles_per_block, ntiles);
-  if (t_begin >= t_end) return;
-  constexpr int RB = dec_row_bytes<FMT>();
-
-  uint4 pre[8];
-  dec_load_tile<FMT>(a, b, t_begin * kDecTile, nvis, pre);
-
-  // query block (64 heads x 128) as the A operand: lane holds head 32T + col, channels 64g + 8s .. + 7
-  bf16x8_t qa[2][8];
-  float wv[2][16];
-  {
-    const long long qrow0 = (long long)b * 64;
-#pragma unroll
-    for (int T = 0; T < 2; ++T) {
-      const long long row = qrow0 + 32 * T + col;
-      uint4 raw[8];
-      load_row64<FMT>(a.q, row, g, raw);
-#pragma unroll
-      for (int s = 0; s < 8; ++s) qa[T][s] = __builtin_bit_cast(bf16x8_t, raw[s]);
-#pragma unroll
-      for (int x = 0; x < 16; ++x) wv[T][x] = a.w[(long long)b * 64 + 32 * T + 8 * (x >> 2) + 4 * g + (x & 3)];
-    }
-  }
-  dec_store_tile<FMT>(dec_lds, pre);
+__device__ __forceinline__ void flush_hist(const int* hist_s, int* gh) {
   __syncthreads();
-
-  for (int tt = t_begin; tt < t_end; ++tt) {
-    const int cur = (tt - t_begin) & 1;
-    if (tt + 1 < t_end) dec_load_tile<FMT>(a, b, (tt + 1) * kDecTile, nvis, pre);
-
-    // B operand: the wave's 32 keys, channels 64g + 8s .. + 7
-    bf16x8_t kb[8];
-    const uint8_t* rowp = dec_lds + cur * (kDecTile * RB) + (32 * wave + col) * RB;
-    if (FMT == LCA_BF16) {
-#pragma unroll
-      for (int s = 0; s < 8; ++s) kb[s] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(rowp + 128 * g + 16 * s));
-    } else {
-      const uint4 c0 = *(const uint4*)(rowp + 32 * g), c1 = *(const uint4*)(rowp + 32 * g + 16);
-      const uint32_t sc = *(const uint32_t*)(rowp + 64 + 4 * g);
-      const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-#pragma unroll
-      for (int s = 0; s < 8; ++s)
-        kb[s] = __builtin_bit_cast(bf16x8_t, fp4x8_to_bf16x8(cw[s], (int)((sc >> (8 * (s >> 1))) & 255u) - 127));
-    }
-    f32x16_t acc[2];
-#pragma unroll
-    for (int T = 0; T < 2; ++T)
-#pragma unroll
-      for (int x = 0; x < 16; ++x) acc[T][x] = 0.0f;
-#pragma unroll
-    for (int s = 0; s < 8; ++s)
-#pragma unroll
-      for (int T = 0; T < 2; ++T) acc[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[T][s], kb[s], acc[T], 0, 0, 0);
-
-    // fixed halving tree over the 64 heads (see the header comment)
-    float l1[16];
-#pragma unroll
-    for (int x = 0; x < 16; ++x) {
-      const float p0 = wv[0][x] * fmaxf(acc[0][x], 0.0f);
-      const float p1 = wv[1][x] * fmaxf(acc[1][x], 0.0f);
-      l1[x] = p0 + p1;
-    }
-    float l2[8], l3[4], l4[4];
-#pragma unroll
-    for (int x = 0; x < 8; ++x) l2[x] = l1[x] + l1[x + 8];
-#pragma unroll
-    for (int x = 0; x < 4; ++x) l3[x] = l2[x] + l2[x + 4];
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      const float o = __shfl_xor(l3[x], 32, 64);
-      l4[x] = (g == 0) ? (l3[x] + o) : (o + l3[x]);
-    }
-    const float s = (l4[0] + l4[2]) + (l4[1] + l4[3]);
-    const int e = tt * kDecTile + 32 * wave + col;
-    if (g == 0 && e < nvis) a.keys[(long long)b * a.N + e] = score_key(s);
-
-    if (tt + 1 < t_end) dec_store_tile<FMT>(dec_lds + (cur ^ 1) * (kDecTile * RB), pre);
-    __syncthreads();
+  for (int i = threadIdx.x; i < kSelBins; i += blockDim.x) {
+    const int c = hist_s[i];
+    if (c) atomicAdd(&gh[i], c);
   }
 }
 
-// ------------------------------------------------------------------------------------------------
-// decode kernel for fp4 keys and queries: block-scaled MFMA on the stored codes
-// ------------------------------------------------------------------------------------------------
-// v_mfma_scale_f32_16x16x128_f8f6f4 with both operands in fp4 e2m1 applies one E8M0 scale per lane to the lane's
-// 32 contraction slots (A: lane l holds row l % 16, slots 32 (l / 16) .. + 31; B: column l % 16, same slots).  The
-// cache scales each 16 elements, so each lane fills the first 16 slots of its block with one 16-element group and
-// the other 16 with zeros; two instructions (h = 0, 1) cover the 8 groups of a 128-dim row: block b of
-// instruction h holds group 2b + h.  Products of fp4 values and their block sums are exact, scaled by powers of
-// two, so the per-head dots equal the exact ones whenever they fit fp32 -- the fixed head-reduction order then
-// makes the scores bit-reproducible.  The 16x16 accumulator holds heads 16T + 4(l/16) + r for key l % 16.
+// Scores of four 16-key groups (every lane of a key holds its score after the head tree): lane (g, col) takes
+// group q0 + g, so that one store writes 64 keys.  The store is unconditional -- a lane past the range holds the
+// score of the clamped key k1 - 1 and writes that same value there -- and is issued after the next stage's loads,
+// so no branch or register reuse separates the loads in flight from their waits.
+struct KeyOut {
+  uint32_t key;
+  int e;
+};
+
+__device__ __forceinline__ KeyOut pick_key4(int gbase, int g, const float (&sc)[4]) {
+  const float s = g == 0 ? sc[0] : g == 1 ? sc[1] : g == 2 ? sc[2] : sc[3];
+  return KeyOut{score_key(s), gbase + 16 * g + (int)(threadIdx.x & 15)};
+}
+
+__device__ __forceinline__ void store_key(const IdxArgs& a, int b, int k1, const KeyOut& o, int* hist_s, bool hist) {
+  a.keys[(long long)b * a.N + min(o.e, k1 - 1)] = o.key;
+  if (hist && o.e < k1) atomicAdd(&hist_s[o.key >> 21], 1);
+}
+
+// Keys [k0, k1) of sequence b for the workgroup; the slab of wave w in stage st starts at k0 + st * 4 * KPW + w * KPW,
+// KPW = 16 * groups keys.
+
+// ---- bf16: v_mfma_f32_16x16x32_bf16, A = queries (lane: head 16T + l % 16, channels 8 (l / 16) + 32 s + v),
+//      B = keys (lane: key l % 16, the same channels), i.e. 16 bytes at 16 (l / 16) + 64 s of the 256-byte row.
+constexpr int kBfGroups = 4;  // 16-key groups per wave per stage (16 KB per wave in flight)
+
+struct BfStage {
+  uint4 c[kBfGroups][4];
+};
+
+__device__ __forceinline__ void bf_load_stage(BfStage& S, const uint8_t* kb, int kbase, int klast, int lane) {
+  const int g = lane >> 4, col = lane & 15;
+#pragma unroll
+  for (int j = 0; j < kBfGroups; ++j) {
+    const int e = min(kbase + 16 * j + col, klast);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) S.c[j][s] = *(const uint4*)(kb + (long long)e * 256 + 16 * g + 64 * s);
+  }
+}
+
+template <int NST>
+__global__ __launch_bounds__(256, 2) void idx_score_decode_bf16(IdxArgs a) {
+#pragma clang fp contract(off)
+  __shared__ int hist_s[kSelBins];
+  constexpr int KPW = 16 * kBfGroups;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = lane >> 4, col = lane & 15;
+  const int b = blockIdx.y;
+  const int nvis = nvis_of(a.q_start, a.m, a.N);
+  const int k0 = blockIdx.x * (NST * 4 * KPW);
+  const int k1 = min(k0 + NST * 4 * KPW, nvis);
+  if (k0 >= k1) return;
+  const bool hist = a.sel_state != nullptr;
+  if (hist)
+    for (int i = threadIdx.x; i < kSelBins; i += blockDim.x) hist_s[i] = 0;
+  const uint8_t* kb = (const uint8_t*)a.k.data + (long long)b * a.k.cap * 256;
+
+  BfStage S[2];
+  bf_load_stage(S[0], kb, k0 + wave * KPW, k1 - 1, lane);
+  bf16x8_t qa[4][4];
+  float wv[4][4];
+#pragma unroll
+  for (int T = 0; T < 4; ++T) {
+    const uint8_t* qrow = (const uint8_t*)a.q.data + ((long long)b * 64 + 16 * T + col) * 256;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qa[T][s] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(qrow + 16 * g + 64 * s));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) wv[T][r] = a.w[(long long)b * 64 + 16 * T + 4 * g + r];
+  }
+  if (hist) __syncthreads();  // histogram zeroed before any update
+
+  // straight-line stages (fully unrolled): the next stage's loads are in flight while this one is scored, and each
+  // stage's keys are stored after the following stage's loads are issued
+  KeyOut pend{0u, k1};
+#pragma unroll
+  for (int st = 0; st < NST; ++st) {
+    const int kbase = k0 + st * 4 * KPW + wave * KPW;
+    if (st + 1 < NST) {
+      bf_load_stage(S[(st + 1) & 1], kb, kbase + 4 * KPW, k1 - 1, lane);
+      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the scoring
+    }
+    if (st > 0) store_key(a, b, k1, pend, hist_s, hist);
+    const BfStage& C = S[st & 1];
+    float sc[kBfGroups];
+#pragma unroll
+    for (int j = 0; j < kBfGroups; ++j) {
+      f32x4_t acc[4];
+#pragma unroll
+      for (int T = 0; T < 4; ++T) acc[T] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const bf16x8_t kv = __builtin_bit_cast(bf16x8_t, C.c[j][s]);
+#pragma unroll
+        for (int T = 0; T < 4; ++T) acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[T][s], kv, acc[T], 0, 0, 0);
+      }
+      sc[j] = head_tree(acc, wv, g);
+    }
+    pend = pick_key4(kbase, g, sc);
+  }
+  store_key(a, b, k1, pend, hist_s, hist);
+  if (hist) flush_hist(hist_s, a.sel_state + (long long)b * kSelStateInts);
+}
+
+// ---- fp4: v_mfma_scale_f32_16x16x128_f8f6f4 with both operands in fp4 e2m1 applies one E8M0 scale per lane to
+// the lane's 32 contraction slots (A: lane l holds row l % 16, slots 32 (l / 16) .. + 31; B: column l % 16, same
+// slots).  The cache scales each 16 elements, so each lane fills the first 16 slots of its block with one
+// 16-element group and the other 16 with zeros; two instructions (h = 0, 1) cover the 8 groups of a 128-dim row:
+// block b of instruction h holds group 2b + h.  A lane's operand bytes are 16 bytes at 16 (l / 16) of the key's
+// 64-byte code row (groups 2g, 2g + 1) and the two scale bytes at 2 (l / 16) of its 8-byte scale row.  Products of
+// fp4 values and their block sums are exact, scaled by powers of two, so the per-head dots equal the exact ones
+// whenever they fit fp32 -- the fixed head-reduction order then makes the scores bit-reproducible.
 typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8_t;
 
 __device__ __forceinline__ i32x8_t fp4_operand(uint32_t lo, uint32_t hi) {
@@ -395,24 +395,44 @@ __device__ __forceinline__ i32x8_t fp4_operand(uint32_t lo, uint32_t hi) {
   return v;
 }
 
-__global__ __launch_bounds__(256, 2) void idx_score_decode_fp4(IdxArgs a, int tiles_per_block) {
+constexpr int kF4Groups = 8;  // 16-key groups per wave per stage (9 KB per wave in flight)
+
+struct F4Stage {
+  uint4 c[kF4Groups];
+  uint32_t s[kF4Groups];
+};
+
+__device__ __forceinline__ void f4_load_stage(F4Stage& S, const uint8_t* codes, const uint8_t* scales, int kbase,
+                                              int klast, int lane) {
+  const int g = lane >> 4, col = lane & 15;
+#pragma unroll
+  for (int j = 0; j < kF4Groups; ++j) {
+    const int e = min(kbase + 16 * j + col, klast);
+    S.c[j] = *(const uint4*)(codes + (long long)e * 64 + 16 * g);
+    S.s[j] = *(const uint16_t*)(scales + (long long)e * 8 + 2 * g);
+  }
+}
+
+template <int NST>
+__global__ __launch_bounds__(256, 2) void idx_score_decode_fp4(IdxArgs a) {
 #pragma clang fp contract(off)
-  extern __shared__ __attribute__((aligned(16))) uint8_t dec_lds[];
+  __shared__ int hist_s[kSelBins];
+  constexpr int KPW = 16 * kF4Groups;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 4, col = lane & 15;
   const int b = blockIdx.y;
-  if (a.sel_state && blockIdx.x == 0)  // the select that follows accumulates into this row's state
-    for (int i = threadIdx.x; i < kSelStateInts; i += blockDim.x) a.sel_state[(long long)b * kSelStateInts + i] = 0;
   const int nvis = nvis_of(a.q_start, a.m, a.N);
-  const int ntiles = (nvis + kDecTile - 1) / kDecTile;
-  const int t_begin = blockIdx.x * tiles_per_block;
-  const int t_end = min(t_begin + tiles_per_block, ntiles);
-  if (t_begin >= t_end) return;
-  constexpr int RB = kKRowF4;
+  const int k0 = blockIdx.x * (NST * 4 * KPW);
+  const int k1 = min(k0 + NST * 4 * KPW, nvis);
+  if (k0 >= k1) return;
+  const bool hist = a.sel_state != nullptr;
+  if (hist)
+    for (int i = threadIdx.x; i < kSelBins; i += blockDim.x) hist_s[i] = 0;
+  const uint8_t* codes = (const uint8_t*)a.k.data + (long long)b * a.k.cap * 64;
+  const uint8_t* scales = (const uint8_t*)a.k.scale + (long long)b * a.k.cap * 8;
 
-  uint4 pre[8];
-  dec_load_tile<LCA_FP4>(a, b, t_begin * kDecTile, nvis, pre);
-
+  F4Stage S[2];
+  f4_load_stage(S[0], codes, scales, k0 + wave * KPW, k1 - 1, lane);
   // query operands: M-tile T = heads 16T .. 16T + 15; lane holds head 16T + col, groups 2g and 2g + 1
   uint32_t qc[4][4];  // [T][0..1] = group 2g codes, [2..3] = group 2g + 1 codes
   int qs[4][2];
@@ -431,61 +451,46 @@ __global__ __launch_bounds__(256, 2) void idx_score_decode_fp4(IdxArgs a, int ti
 #pragma unroll
     for (int r = 0; r < 4; ++r) wv[T][r] = a.w[(long long)b * 64 + 16 * T + 4 * g + r];
   }
-  dec_store_tile<LCA_FP4>(dec_lds, pre);
-  __syncthreads();
+  if (hist) __syncthreads();  // histogram zeroed before any update
 
-  for (int tt = t_begin; tt < t_end; ++tt) {
-    const int cur = (tt - t_begin) & 1;
-    if (tt + 1 < t_end) dec_load_tile<LCA_FP4>(a, b, (tt + 1) * kDecTile, nvis, pre);
+  // straight-line stages as in the bf16 kernel; a stage is two batches of four groups, and each batch's keys are
+  // stored once the next batch (or the next stage's loads) is under way
+  KeyOut pend{0u, k1};
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const uint8_t* rowp = dec_lds + cur * (kDecTile * RB) + (32 * wave + 16 * u + col) * RB;
-      const uint4 kc = *(const uint4*)(rowp + 16 * g);
-      const uint32_t ks2 = *(const uint16_t*)(rowp + 64 + 2 * g);
-      const i32x8_t kop0 = fp4_operand(kc.x, kc.y), kop1 = fp4_operand(kc.z, kc.w);
-      const int ks0 = (int)(ks2 & 255u), ks1 = (int)(ks2 >> 8);
-      f32x4_t acc[4];
-#pragma unroll
-      for (int T = 0; T < 4; ++T) {
-        acc[T] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        acc[T] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fp4_operand(qc[T][0], qc[T][1]), kop0, acc[T], 4, 4,
-                                                                  0, qs[T][0], 0, ks0);
-        acc[T] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fp4_operand(qc[T][2], qc[T][3]), kop1, acc[T], 4, 4,
-                                                                  0, qs[T][1], 0, ks1);
-      }
-      // halving tree: h+32 (T, T+2), h+16 (T, T+1) in-lane; h+8 (g, g+2) and h+4 (g, g+1) across lanes;
-      // h+2, h+1 in-lane
-      float l1[2][4], l2[4], l3[4], l4[4];
-#pragma unroll
-      for (int T = 0; T < 2; ++T)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p0 = wv[T][r] * fmaxf(acc[T][r], 0.0f);
-          const float p1 = wv[T + 2][r] * fmaxf(acc[T + 2][r], 0.0f);
-          l1[T][r] = p0 + p1;
-        }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) l2[r] = l1[0][r] + l1[1][r];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float o = __shfl_xor(l2[r], 32, 64);
-        l3[r] = (g < 2) ? (l2[r] + o) : (o + l2[r]);
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float o = __shfl_xor(l3[r], 16, 64);
-        l4[r] = ((g & 1) == 0) ? (l3[r] + o) : (o + l3[r]);
-      }
-      const float s = (l4[0] + l4[2]) + (l4[1] + l4[3]);
-      const int e = tt * kDecTile + 32 * wave + 16 * u + col;
-      if (g == 0 && e < nvis) a.keys[(long long)b * a.N + e] = score_key(s);
+  for (int st = 0; st < NST; ++st) {
+    const int kbase = k0 + st * 4 * KPW + wave * KPW;
+    if (st + 1 < NST) {
+      f4_load_stage(S[(st + 1) & 1], codes, scales, kbase + 4 * KPW, k1 - 1, lane);
+      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the scoring
     }
-    if (tt + 1 < t_end) dec_store_tile<LCA_FP4>(dec_lds + (cur ^ 1) * (kDecTile * RB), pre);
-    __syncthreads();
+    const F4Stage& C = S[st & 1];
+#pragma unroll
+    for (int q = 0; q < kF4Groups / 4; ++q) {
+      if (st > 0 || q > 0) store_key(a, b, k1, pend, hist_s, hist);
+      float sc[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int j = 4 * q + jj;
+        const uint4 kc = C.c[j];
+        const i32x8_t kop0 = fp4_operand(kc.x, kc.y), kop1 = fp4_operand(kc.z, kc.w);
+        const int ks0 = (int)(C.s[j] & 255u), ks1 = (int)(C.s[j] >> 8);
+        f32x4_t acc[4];
+#pragma unroll
+        for (int T = 0; T < 4; ++T) {
+          acc[T] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+          acc[T] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fp4_operand(qc[T][0], qc[T][1]), kop0, acc[T], 4,
+                                                                    4, 0, qs[T][0], 0, ks0);
+          acc[T] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fp4_operand(qc[T][2], qc[T][3]), kop1, acc[T], 4,
+                                                                    4, 0, qs[T][1], 0, ks1);
+        }
+        sc[jj] = head_tree(acc, wv, g);
+      }
+      pend = pick_key4(kbase + 64 * q, g, sc);
+    }
   }
+  store_key(a, b, k1, pend, hist_s, hist);
+  if (hist) flush_hist(hist_s, a.sel_state + (long long)b * kSelStateInts);
 }
-
-static bool g_dec_attr[64];
 
 bool indexer_uses_decode_kernel(int B, int Sq, int HI, int DI, int q_format, int k_format) {
   (void)B;
@@ -499,25 +504,22 @@ hipError_t launch_indexer_scores(const IdxArgs& a, hipStream_t st) {
   const bool mfma = a.HI == 64 && a.DI == 128 && a.q.format == a.k.format &&
                     (a.q.format == LCA_BF16 || a.q.format == LCA_FP4);
   if (indexer_uses_decode_kernel(a.B, a.Sq, a.HI, a.DI, a.q.format, a.k.format)) {
-    const int ntiles = (nvis_max + kDecTile - 1) / kDecTile;
-    int bps = (512 + a.B - 1) / a.B;  // about two workgroups per CU over the whole batch
-    if (bps > ntiles) bps = ntiles;
-    const int tpb = (ntiles + bps - 1) / bps;
-    bps = (ntiles + tpb - 1) / tpb;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-    if (dev >= 0 && dev < 64 && !g_dec_attr[dev]) {
-      hipError_t e = hipFuncSetAttribute((const void*)idx_score_decode<LCA_BF16>,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kDecTile * kKRowB);
-      if (e != hipSuccess) return e;
-      g_dec_attr[dev] = true;
+    // a fixed key range per workgroup (NST stages of 4 waves x KPW keys), the grid grows with the context; fewer
+    // stages when that leaves fewer than about two workgroups per CU
+    const bool fp4 = a.q.format == LCA_FP4;
+    const int kpw = fp4 ? 16 * kF4Groups : 16 * kBfGroups;
+    int nst = 4;
+    while (nst > 1 && (long long)a.B * ((nvis_max + nst * 4 * kpw - 1) / (nst * 4 * kpw)) < 512) nst >>= 1;
+    const dim3 grid((unsigned)((nvis_max + nst * 4 * kpw - 1) / (nst * 4 * kpw)), (unsigned)a.B);
+    if (fp4) {
+      if (nst == 4) hipLaunchKernelGGL(idx_score_decode_fp4<4>, grid, dim3(256), 0, st, a);
+      else if (nst == 2) hipLaunchKernelGGL(idx_score_decode_fp4<2>, grid, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL(idx_score_decode_fp4<1>, grid, dim3(256), 0, st, a);
+    } else {
+      if (nst == 4) hipLaunchKernelGGL(idx_score_decode_bf16<4>, grid, dim3(256), 0, st, a);
+      else if (nst == 2) hipLaunchKernelGGL(idx_score_decode_bf16<2>, grid, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL(idx_score_decode_bf16<1>, grid, dim3(256), 0, st, a);
     }
-    if (a.q.format == LCA_BF16)
-      hipLaunchKernelGGL(idx_score_decode<LCA_BF16>, dim3((unsigned)bps, (unsigned)a.B), dim3(256),
-                         2 * kDecTile * kKRowB, st, a, tpb);
-    else
-      hipLaunchKernelGGL(idx_score_decode_fp4, dim3((unsigned)bps, (unsigned)a.B), dim3(256), 2 * kDecTile * kKRowF4,
-                         st, a, tpb);
   } else if (mfma) {
     const int qpb = a.Sq >= 16 ? 16 : a.Sq;
     dim3 grid((unsigned)((nvis_max + kMfmaEntriesPerBlock - 1) / kMfmaEntriesPerBlock),

@@ -29,9 +29,9 @@ struct IdxArgs {
   uint32_t* keys;  // [B][Sq][N] order-preserving score keys (workspace)
   int B, Sq, HI, DI, N, m;
   long long q_start;
-  int* sel_state;  // nullable: [B * Sq][kSelStateInts] per-row select state the decode kernels zero
+  int* sel_state;  // nullable: [B * Sq][kSelStateInts] row histograms the decode kernels add into (zeroed first)
 };
-// Whether launch_indexer_scores takes the one-row-per-sequence decode kernels (which zero sel_state).
+// Whether launch_indexer_scores takes the one-row-per-sequence decode kernels (which fill sel_state).
 bool indexer_uses_decode_kernel(int B, int Sq, int HI, int DI, int q_format, int k_format);
 hipError_t launch_indexer_scores(const IdxArgs& a, hipStream_t st);
 
@@ -42,13 +42,18 @@ struct SelArgs {
   float* score_out;      // nullable [rows][k]
   int rows, Sq, N, m, k;
   long long q_start;
-  // multi-workgroup select (decode rows); all null for the one-workgroup-per-row select
-  int* sel_state;  // [rows][kSelStateInts]: 2048-bin histogram, arrival counter (zeroed before the call)
+  // decode rows: the row histograms written by the scoring kernel, and the multi-workgroup select buffers; all null
+  // for the select that makes its own histogram passes
+  int* sel_state;  // [rows][kSelStateInts]: histograms of key bits [31:21] (all keys, from the scoring kernel) and
+                   // of bits [20:10] (keys of the border bin, from the candidate collection)
   int* counts;     // [rows][slices]
   uint2* cand;     // [rows][N] (key, entry) candidates, slice s at [s * kSliceKeys]
 };
-constexpr int kSelStateInts = 2048 + 64;  // histogram + arrival counter (padded)
-constexpr int kSliceKeys = 4096;          // keys per workgroup in the multi-workgroup select
+constexpr int kSelBins = 2048;
+constexpr int kSelStateInts = 2 * kSelBins;
+constexpr int kSliceKeys = 4096;  // keys per workgroup in the multi-workgroup select
+// Zeroes the row histograms [rows][kSelStateInts] (a fill kernel, so that it may be captured in a graph).
+hipError_t launch_sel_zero(int* state, int rows, hipStream_t st);
 hipError_t launch_topk(const SelArgs& a, hipStream_t st);
 
 // stages 3/4, attention (attn.hip)

@@ -207,24 +207,39 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(SelArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------------
-// multi-workgroup select for decode rows (few rows, up to ~1M entries each)
+// decode rows (one query per sequence): the scoring kernel has already built each row's histogram of key bits
+// [31:21], so pass 1 is a read of 2048 counts instead of a pass over the keys.  Every pass over all the keys runs
+// spread over many workgroups; one workgroup per row then works on a few thousand candidates only.
 // ------------------------------------------------------------------------------------------------
-// Each row is cut into slices of kSliceKeys entries, one 256-thread workgroup per slice.
-//   topk_hist_kernel:    slice histogram of key bits [31:21] in LDS, added into the row's histogram.
-//   topk_collect_kernel: every slice finds the border bin b1 from the row histogram, writes its keys with
-//                        bin >= b1 (a superset of the selection of about k + |border| keys) in entry order to its
-//                        candidate segment, then counts itself in with an atomic; the last slice of the row to
-//                        arrive runs passes 2-3 and the ordered output over the row's candidates.
-// The row histogram and arrival counter are zeroed by the scoring kernel that precedes these launches.
-constexpr int kMbThreads = 256;
-constexpr int kMbPerThread = kSliceKeys / kMbThreads;  // 16
-constexpr int kCandCap = 6144;                         // candidates staged in LDS by the finishing slice
+__global__ __launch_bounds__(256) void sel_zero_kernel(int* state) {
+  int4* p = (int4*)(state + (long long)blockIdx.x * kSelStateInts);
+  for (int i = threadIdx.x; i < kSelStateInts / 4; i += blockDim.x) p[i] = make_int4(0, 0, 0, 0);
+}
+
+hipError_t launch_sel_zero(int* state, int rows, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  clear_stale_error();
+  hipLaunchKernelGGL(sel_zero_kernel, dim3((unsigned)rows), dim3(256), 0, st, state);
+  return hipGetLastError();
+}
 
 __device__ __forceinline__ int sel_row_nvis(const SelArgs& a, int row) {
   const long long t = a.q_start + row % a.Sq;
   const long long nv = t / a.m;
   return (int)(nv < a.N ? nv : a.N);
 }
+
+// Each row is cut into slices of kSliceKeys entries, one 256-thread workgroup per slice.
+//   topk_collect_kernel: every slice finds the border bin b1 from the row histogram, writes its keys with bin >= b1
+//                        (a superset of the selection: about k + |border| keys per row) in entry order to its
+//                        candidate segment with the segment's length, and adds bits [20:10] of its border-bin keys
+//                        into the row's second histogram (pass 2).
+//   topk_finish_kernel:  one workgroup per row (a separate launch, so that every slice's writes are visible without
+//                        cross-workgroup fences) reads both histograms, gathers the segments, resolves bits [9:0]
+//                        over the candidates (pass 3) and writes the output.
+constexpr int kMbThreads = 256;
+constexpr int kMbPerThread = kSliceKeys / kMbThreads;  // 16
+constexpr int kCandCap = 6144;                         // candidates staged in LDS by the finishing workgroup
 
 // Exclusive scan over a 256-thread block.
 __device__ __forceinline__ int block256_excl_scan(int v, int* wsum, int& tot) {
@@ -274,154 +289,175 @@ __device__ __forceinline__ int find_bin256(const int* hist, int need, int* wsum,
   return sh[0];
 }
 
-__global__ __launch_bounds__(kMbThreads) void topk_hist_kernel(SelArgs a) {
-  __shared__ int hist[2048];
-  const int p = blockIdx.x, row = blockIdx.y;
-  const int nvis = sel_row_nvis(a, row);
-  const int s0 = p * kSliceKeys;
-  if (nvis <= a.k || s0 >= nvis) return;
-  const int s1 = min(s0 + kSliceKeys, nvis);
-  for (int i = threadIdx.x; i < 2048; i += kMbThreads) hist[i] = 0;
-  __syncthreads();
-  const uint32_t* kg = a.keys + (long long)row * a.N;
-  uint32_t kv[kMbPerThread];
-#pragma unroll
-  for (int u = 0; u < kMbPerThread; ++u) {
-    const int i = s0 + threadIdx.x + kMbThreads * u;
-    kv[u] = i < s1 ? kg[i] : 0u;
-  }
-#pragma unroll
-  for (int u = 0; u < kMbPerThread; ++u)
-    if (s0 + (int)threadIdx.x + kMbThreads * u < s1) atomicAdd(&hist[kv[u] >> 21], 1);
-  __syncthreads();
-  int* gh = a.sel_state + (long long)row * kSelStateInts;
-  for (int i = threadIdx.x; i < 2048; i += kMbThreads) {
-    const int c = hist[i];
-    if (c) atomicAdd(&gh[i], c);
-  }
-}
-
-// Candidate j of the row (entry order): segment of j found by binary search over the segment offsets.
-__device__ __forceinline__ uint2 cand_global(const SelArgs& a, int row, const int* seg_off, int nseg, int j) {
-  int lo = 0, hi = nseg - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (seg_off[mid] <= j) lo = mid; else hi = mid - 1;
-  }
-  return a.cand[(long long)row * a.N + (long long)lo * kSliceKeys + (j - seg_off[lo])];
-}
-
 __global__ __launch_bounds__(kMbThreads) void topk_collect_kernel(SelArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint32_t mb_lds[];  // the slice's keys
-  __shared__ int hist[2048];
+  __shared__ int hist[kSelBins];
   __shared__ int wsum[kMbThreads / 64];
   __shared__ int sh[4];
   const int p = blockIdx.x, row = blockIdx.y, tid = threadIdx.x;
   const int nvis = sel_row_nvis(a, row);
   const int k = a.k;
-  int32_t* out = a.idx_out + (long long)row * k;
-  float* sout = a.score_out ? a.score_out + (long long)row * k : nullptr;
   const uint32_t* kg = a.keys + (long long)row * a.N;
-  if (nvis <= k) {
-    if (p == 0)
-      for (int j = tid; j < k; j += kMbThreads) {
-        out[j] = j < nvis ? j : -1;
-        if (sout) sout[j] = j < nvis ? key_score(kg[j]) : -INFINITY;
-      }
-    return;
-  }
+  if (nvis <= k) return;  // the finishing kernel writes the whole row
   const int P = (nvis + kSliceKeys - 1) / kSliceKeys;
   if (p >= P) return;
-  int* gh = a.sel_state + (long long)row * kSelStateInts;
   const int slots = (a.N + kSliceKeys - 1) / kSliceKeys;
+  const int s0 = p * kSliceKeys, s1 = min(s0 + kSliceKeys, nvis);
 
-  // border bin b1 from the row histogram
-  for (int i = tid; i < 2048; i += kMbThreads) hist[i] = gh[i];
+  // the slice's keys and the row histogram, all loads in flight together
+  uint32_t kv[kMbPerThread];
+#pragma unroll
+  for (int u = 0; u < kMbPerThread; ++u) {
+    const int i = s0 + tid + kMbThreads * u;
+    kv[u] = i < s1 ? kg[i] : 0u;
+  }
+  const int* gh = a.sel_state + (long long)row * kSelStateInts;
+  int hv[kSelBins / kMbThreads];
+#pragma unroll
+  for (int u = 0; u < kSelBins / kMbThreads; ++u) hv[u] = gh[tid + kMbThreads * u];
+#pragma unroll
+  for (int u = 0; u < kMbPerThread; ++u) mb_lds[tid + kMbThreads * u] = kv[u];
+#pragma unroll
+  for (int u = 0; u < kSelBins / kMbThreads; ++u) hist[tid + kMbThreads * u] = hv[u];
   __syncthreads();
   int above1;
   const int b1 = find_bin256(hist, k, wsum, sh, &above1);
 
   // this slice's keys with bin >= b1, in entry order
-  const int s0 = p * kSliceKeys, s1 = min(s0 + kSliceKeys, nvis);
-#pragma unroll
-  for (int u = 0; u < kMbPerThread; ++u) {
-    const int i = s0 + tid + kMbThreads * u;
-    mb_lds[tid + kMbThreads * u] = i < s1 ? kg[i] : 0u;
-  }
-  __syncthreads();
   int cnt = 0;
 #pragma unroll
   for (int j = 0; j < kMbPerThread; ++j) {
     const int jj = kMbPerThread * tid + j;
     cnt += (s0 + jj < s1 && (int)(mb_lds[jj] >> 21) >= b1) ? 1 : 0;
   }
+#pragma unroll
+  for (int u = 0; u < kSelBins / kMbThreads; ++u) hist[tid + kMbThreads * u] = 0;  // reused for pass 2
   int tot;
-  int pos = block256_excl_scan(cnt, wsum, tot);
+  int pos = block256_excl_scan(cnt, wsum, tot);  // (its barriers also publish the zeroed histogram)
   uint2* seg = a.cand + (long long)row * a.N + s0;
 #pragma unroll
   for (int j = 0; j < kMbPerThread; ++j) {
     const int jj = kMbPerThread * tid + j;
     const uint32_t key = mb_lds[jj];
-    if (s0 + jj < s1 && (int)(key >> 21) >= b1) seg[pos++] = make_uint2(key, (uint32_t)(s0 + jj));
+    if (s0 + jj < s1 && (int)(key >> 21) >= b1) {
+      seg[pos++] = make_uint2(key, (uint32_t)(s0 + jj));
+      if ((int)(key >> 21) == b1) atomicAdd(&hist[(key >> 10) & 0x7FFu], 1);
+    }
   }
   if (tid == 0) a.counts[(long long)row * slots + p] = tot;
+  __syncthreads();
+  int* gh2 = a.sel_state + (long long)row * kSelStateInts + kSelBins;
+#pragma unroll
+  for (int u = 0; u < kSelBins / kMbThreads; ++u) {
+    const int c = hist[tid + kMbThreads * u];
+    if (c) atomicAdd(&gh2[tid + kMbThreads * u], c);
+  }
 }
 
-// One workgroup per row: passes 2-3 and the ordered output over the row's candidates (a separate launch, so the
-// candidates written by every slice are visible without cross-workgroup fences).
+// Segment of candidate j (row order): the last segment whose start offset is <= j.
+__device__ __forceinline__ int cand_segment(const int* seg_off, int nseg, int j) {
+  int lo = 0, hi = nseg - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (seg_off[mid] <= j) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+constexpr size_t kFinishLds = (size_t)kCandCap * 8 + (size_t)kCandCap * 2;  // candidates + segment map
+
 __global__ __launch_bounds__(kMbThreads) void topk_finish_kernel(SelArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint32_t mb_lds[];  // the row's candidates
-  __shared__ int hist[2048];
+  extern __shared__ __attribute__((aligned(16))) uint32_t mb_lds[];  // the row's candidates, then the segment map
+  __shared__ int hist[kSelBins];
+  __shared__ int hist2[kSelBins];
   __shared__ int seg_off[257];
   __shared__ int wsum[kMbThreads / 64];
   __shared__ int sh[4];
   const int row = blockIdx.x, tid = threadIdx.x;
   const int nvis = sel_row_nvis(a, row);
   const int k = a.k;
-  if (nvis <= k) return;  // written by the collect kernel
   int32_t* out = a.idx_out + (long long)row * k;
   float* sout = a.score_out ? a.score_out + (long long)row * k : nullptr;
+  if (nvis <= k) {  // every visible entry is selected
+    const uint32_t* kg = a.keys + (long long)row * a.N;
+    for (int j = tid; j < k; j += kMbThreads) {
+      out[j] = j < nvis ? j : -1;
+      if (sout) sout[j] = j < nvis ? key_score(kg[j]) : -INFINITY;
+    }
+    return;
+  }
   const int P = (nvis + kSliceKeys - 1) / kSliceKeys;
   const int slots = (a.N + kSliceKeys - 1) / kSliceKeys;
   const int* gh = a.sel_state + (long long)row * kSelStateInts;
-  for (int i = tid; i < 2048; i += kMbThreads) hist[i] = gh[i];
-  __syncthreads();
-  int above1;
-  const int b1 = find_bin256(hist, k, wsum, sh, &above1);
+  // segment lengths and both histograms, all loads in flight together
   const int c = tid < P ? a.counts[(long long)row * slots + tid] : 0;
+  int hv[kSelBins / kMbThreads], hv2[kSelBins / kMbThreads];
+#pragma unroll
+  for (int u = 0; u < kSelBins / kMbThreads; ++u) {
+    hv[u] = gh[tid + kMbThreads * u];
+    hv2[u] = gh[kSelBins + tid + kMbThreads * u];
+  }
+#pragma unroll
+  for (int u = 0; u < kSelBins / kMbThreads; ++u) {
+    hist[tid + kMbThreads * u] = hv[u];
+    hist2[tid + kMbThreads * u] = hv2[u];
+  }
   int total;
-  const int off = block256_excl_scan(c, wsum, total);
+  const int off = block256_excl_scan(c, wsum, total);  // (its barriers also publish both histograms)
   if (tid < P) seg_off[tid] = off;
-  __syncthreads();
+  // passes 1 and 2 from the histograms
+  int above;
+  const int b1 = find_bin256(hist, k, wsum, sh, &above);
+  int need = k - above;
+  const int b2 = find_bin256(hist2, need, wsum, sh, &above);
+  need -= above;
+  const uint32_t prefix12 = ((uint32_t)b1 << 21) | ((uint32_t)b2 << 10);
+
+  const uint2* cseg = a.cand + (long long)row * a.N;
   const bool in_lds = total <= kCandCap;
   uint2* cl = (uint2*)mb_lds;
+  uint16_t* seg_of = (uint16_t*)(mb_lds + 2 * kCandCap);  // candidate -> its segment
   if (in_lds) {
-    for (int j = tid; j < total; j += kMbThreads) cl[j] = cand_global(a, row, seg_off, P, j);
+    if (tid < P)
+      for (int i = 0; i < c; ++i) seg_of[off + i] = (uint16_t)tid;
+    __syncthreads();
+    // straight-line gather, eight candidates per thread at a time: indices clamp to the last candidate (loaded
+    // again, not stored), so the map reads, then the loads, all go out together
+    for (int base = 0; base < total; base += 8 * kMbThreads) {
+      int jc[8], sg[8];
+      uint2 cv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        jc[i] = min(base + tid + kMbThreads * i, total - 1);
+        sg[i] = seg_of[jc[i]];
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) cv[i] = cseg[(long long)sg[i] * kSliceKeys + (jc[i] - seg_off[sg[i]])];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (base + tid + kMbThreads * i < total) cl[base + tid + kMbThreads * i] = cv[i];
+    }
   }
   __syncthreads();
-  auto cand = [&](int j) -> uint2 { return in_lds ? cl[j] : cand_global(a, row, seg_off, P, j); };
+  // more candidates than fit in LDS (many keys in the border bin): read them from the segments, locating each by a
+  // search over the segment offsets
+  auto cand = [&](int j) -> uint2 {
+    if (in_lds) return cl[j];
+    const int sgm = cand_segment(seg_off, P, j);
+    return cseg[(long long)sgm * kSliceKeys + (j - seg_off[sgm])];
+  };
 
-  // passes 2 and 3 over the border candidates
-  int need = k - above1;
-  uint32_t prefix = (uint32_t)b1 << 21, mask = 0xFFE00000u;
-  for (int pass = 0; pass < 2; ++pass) {
-    const int shf = pass == 0 ? 10 : 0;
-    const uint32_t digit = pass == 0 ? 0x7FFu : 0x3FFu;
-    for (int i = tid; i < 2048; i += kMbThreads) hist[i] = 0;
-    __syncthreads();
-    for (int j = tid; j < total; j += kMbThreads) {
-      const uint32_t key = cand(j).x;
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shf) & digit], 1);
-    }
-    __syncthreads();
-    int above;
-    const int bn = find_bin256(hist, need, wsum, sh, &above);
-    need -= above;
-    prefix |= (uint32_t)bn << shf;
-    mask |= digit << shf;
-    __syncthreads();
+  // pass 3 (bits [9:0]) over the candidates sharing the 21-bit prefix
+  for (int i = tid; i < kSelBins; i += kMbThreads) hist[i] = 0;
+  __syncthreads();
+  for (int j = tid; j < total; j += kMbThreads) {
+    const uint32_t key = cand(j).x;
+    if ((key & 0xFFFFFC00u) == prefix12) atomicAdd(&hist[key & 0x3FFu], 1);
   }
-  const uint32_t kappa = prefix;
+  __syncthreads();
+  const int b3 = find_bin256(hist, need, wsum, sh, &above);
+  need -= above;
+  const uint32_t kappa = prefix12 | (uint32_t)b3;  // the k-th largest key; `need` of the keys equal to it are taken
 
   // ordered output: candidates > kappa, then the first `need` equal to kappa
   int sel_run = 0, eq_run = 0;
@@ -451,8 +487,10 @@ __global__ __launch_bounds__(kMbThreads) void topk_finish_kernel(SelArgs a) {
         ++eq_seen;
       }
       if (sel) {
-        out[o] = (int32_t)cv[j].y;
-        if (sout) sout[o] = key_score(cv[j].x);
+        if (o < k) {  // always true for histograms consistent with the keys
+          out[o] = (int32_t)cv[j].y;
+          if (sout) sout[o] = key_score(cv[j].x);
+        }
         ++o;
       }
     }
@@ -471,12 +509,11 @@ hipError_t launch_topk(const SelArgs& a, hipStream_t st) {
   const int nvis_max = (int)(nv < a.N ? nv : a.N);
   clear_stale_error();
   if (a.sel_state) {
-    const int P = nvis_max > 0 ? (nvis_max + kSliceKeys - 1) / kSliceKeys : 1;
-    dim3 grid((unsigned)P, (unsigned)a.rows);
-    if (nvis_max > a.k) hipLaunchKernelGGL(topk_hist_kernel, grid, dim3(kMbThreads), 0, st, a);
-    hipLaunchKernelGGL(topk_collect_kernel, grid, dim3(kMbThreads), (size_t)kSliceKeys * 4, st, a);
+    const int P = (nvis_max + kSliceKeys - 1) / kSliceKeys;
     if (nvis_max > a.k)
-      hipLaunchKernelGGL(topk_finish_kernel, dim3((unsigned)a.rows), dim3(kMbThreads), (size_t)kCandCap * 8, st, a);
+      hipLaunchKernelGGL(topk_collect_kernel, dim3((unsigned)P, (unsigned)a.rows), dim3(kMbThreads),
+                         (size_t)kSliceKeys * 4, st, a);
+    hipLaunchKernelGGL(topk_finish_kernel, dim3((unsigned)a.rows), dim3(kMbThreads), kFinishLds, st, a);
   } else if (nvis_max <= kLdsKeys) {
     if (!g_lds_attr_set) {
       hipError_t e = hipFuncSetAttribute((const void*)topk_select_kernel<true>,

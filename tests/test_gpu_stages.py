@@ -167,7 +167,7 @@ def test_indexer_simt_f32_prefill():
     assert st["exact_rows"] >= st["rows"] * 0.98
 
 
-@pytest.mark.parametrize("B,N,k", [(3, 2037, 512), (2, 700, 1024), (1, 40000, 1024), (2, 100, 512)])
+@pytest.mark.parametrize("B,N,k", [(3, 2037, 512), (2, 700, 1024), (1, 40000, 1024), (2, 100, 512), (16, 16411, 512)])
 def test_indexer_mfma_bf16_decode(B, N, k):
     st = _indexer_case(B, 1, 64, 128, N, 4, k, 4 * N + 3, "bf16", 11)
     assert st["exact_rows"] >= st["rows"] - 1
@@ -181,7 +181,7 @@ def test_indexer_mfma_bf16_prefill_causal():
 
 
 @pytest.mark.parametrize("B,Sq,N,k,HI,DI", [(2, 1, 3000, 1024, 64, 128), (1, 3, 40000, 1024, 64, 128),
-                                             (2, 2, 500, 64, 16, 64)])
+                                             (2, 2, 500, 64, 16, 64), (8, 1, 65613, 1024, 64, 128)])
 def test_indexer_fp4_bit_exact(B, Sq, N, k, HI, DI):
     _indexer_case(B, Sq, HI, DI, N, 4, k, 4 * N, "fp4", 14)
 
