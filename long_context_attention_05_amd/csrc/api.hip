@@ -50,18 +50,20 @@ int hip_status(hipError_t e) {
 thread_local hipEvent_t t_ev_begin = nullptr, t_ev_end = nullptr;
 
 // Split plan of the attention: rows = B * Sq query rows, each with up to max_entries list positions.
-// hg: the head-group kernel (few rows), which runs 4 workgroups per (row, split).
-void attn_plan(int B, int Sq, int H, int max_entries, bool hg, int& n_splits, int& split_len) {
+// mode 0: one workgroup per (row, split), all heads; 1 (head-group kernel): four workgroups of 16 heads per (row,
+// split); 2 (wide kernel): one workgroup per (row, split) with the channels split over its waves.
+void attn_plan(int B, int Sq, int H, int max_entries, int mode, int& n_splits, int& split_len) {
   const long long rows = (long long)B * Sq;
   n_splits = 1;
   split_len = max_entries > 0 ? max_entries : 1;
   if (rows >= 256 || max_entries <= 64) return;
-  const long long unit = hg ? 64 : 32;
-  const long long per_row = hg ? rows * (H / 16) : rows;
+  const long long unit = mode == 1 ? 64 : 32;
+  const long long per_row = mode == 1 ? rows * (H / 16) : rows;
   const long long want = (256 + per_row - 1) / per_row;
   long long len = (max_entries + want - 1) / want;
   len = (len + unit - 1) / unit * unit;
   if (len < 64) len = 64;
+  if (mode != 0 && len > kHgSplitMax) len = kHgSplitMax;  // these kernels resolve a slice's rows into LDS
   long long ns = (max_entries + len - 1) / len;
   const long long max_splits = 4096;  // the merge keeps one weight per split in LDS
   if (ns > max_splits) {
@@ -74,13 +76,16 @@ void attn_plan(int B, int Sq, int H, int max_entries, bool hg, int& n_splits, in
   split_len = (int)len;
 }
 
-bool attn_hg(int B, int Sq, int H, int D, int q_format, int kv_format) {
-  return attn_uses_mfma(H, D, q_format, kv_format) && (long long)B * Sq < 256;
+// The kernel a call takes: few query rows on the MFMA path go to the head-group kernel (sparse lists) or the
+// wide kernel (dense HCA lists, many entries per row).
+int attn_mode(int B, int Sq, int H, int D, int q_format, int kv_format, int hca_m) {
+  if (!attn_uses_mfma(H, D, q_format, kv_format) || (long long)B * Sq >= 256) return 0;
+  return hca_m > 0 ? 2 : 1;
 }
 
-size_t attn_ws_plan_size(int B, int Sq, int H, int D, int max_entries, bool hg) {
+size_t attn_ws_plan_size(int B, int Sq, int H, int D, int max_entries, int mode) {
   int ns, len;
-  attn_plan(B, Sq, H, max_entries, hg, ns, len);
+  attn_plan(B, Sq, H, max_entries, mode, ns, len);
   if (ns <= 1) return 0;
   const size_t items = (size_t)B * Sq * ns;
   return align_up(items * H * D * sizeof(float)) + align_up(items * H * 2 * sizeof(float));
@@ -88,9 +93,13 @@ size_t attn_ws_plan_size(int B, int Sq, int H, int D, int max_entries, bool hg) 
 
 // Enough for whichever kernel the call will take (the size query does not know the formats).
 size_t attn_ws_size(int B, int Sq, int H, int D, int max_entries) {
-  const size_t a = attn_ws_plan_size(B, Sq, H, D, max_entries, false);
-  const size_t b = (H == 64 && D == 512) ? attn_ws_plan_size(B, Sq, H, D, max_entries, true) : 0;
-  return a > b ? a : b;
+  size_t need = attn_ws_plan_size(B, Sq, H, D, max_entries, 0);
+  if (H == 64 && D == 512)
+    for (int mode = 1; mode <= 2; ++mode) {
+      const size_t m = attn_ws_plan_size(B, Sq, H, D, max_entries, mode);
+      if (m > need) need = m;
+    }
+  return need;
 }
 
 int run_attn(const void* q, int q_format, const lca_tensor& comp, int N, int hca_m, const lca_tensor& raw,
@@ -126,10 +135,11 @@ int run_attn(const void* q, int q_format, const lca_tensor& comp, int N, int hca
     return LCA_ERR_UNSUPPORTED;
   }
   const int max_entries = window + (hca_m > 0 ? N : k);
-  const bool hg = attn_hg(B, Sq, H, D, q_format, comp.format);
+  const int mode = attn_mode(B, Sq, H, D, q_format, comp.format, hca_m);
   int ns, len;
-  attn_plan(B, Sq, H, max_entries, hg, ns, len);
-  const size_t need = attn_ws_plan_size(B, Sq, H, D, max_entries, hg);
+  attn_plan(B, Sq, H, max_entries, mode, ns, len);
+  if (mode != 0 && len > kHgSplitMax) return LCA_ERR_UNSUPPORTED;  // more than 4096 x 2048 list positions per row
+  const size_t need = attn_ws_plan_size(B, Sq, H, D, max_entries, mode);
   if (need > 0 && (!ws || ws_bytes < need)) return LCA_ERR_WORKSPACE;
 
   AttnArgs a{};
@@ -156,7 +166,7 @@ int run_attn(const void* q, int q_format, const lca_tensor& comp, int N, int hca
   a.lse = lse;
   a.n_splits = ns;
   a.split_len = len;
-  a.hg_mode = hg ? 1 : 0;
+  a.hg_mode = mode;
   if (ns > 1) {
     const size_t items = (size_t)B * Sq * ns;
     a.part_o = (float*)ws;

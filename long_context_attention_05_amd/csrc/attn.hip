@@ -176,8 +176,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_mfma_kernel(AttnArgs a) {
     // online softmax for head `head` (lanes hl, hl+16, hl+32, hl+48 hold its 32 logits)
     float mt = fmaxf(fmaxf(fmaxf(lg[0][0], lg[0][1]), fmaxf(lg[0][2], lg[0][3])),
                      fmaxf(fmaxf(lg[1][0], lg[1][1]), fmaxf(lg[1][2], lg[1][3])));
-    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    mt = xor32_max(xor16_max(mt));
     const float m_new = fmaxf(m_run, mt);
     const float alpha = (m_new == -INFINITY) ? 1.0f : __expf(m_run - m_new);
     float pv[2][4], psum = 0.0f;
@@ -188,8 +187,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_mfma_kernel(AttnArgs a) {
         pv[et][x] = (lg[et][x] == -INFINITY) ? 0.0f : __expf(lg[et][x] - m_new);
         psum += pv[et][x];
       }
-    psum += __shfl_xor(psum, 16, 64);
-    psum += __shfl_xor(psum, 32, 64);
+    psum = xor32_sum(xor16_sum(psum));
     l_run = l_run * alpha + psum;
     m_run = m_new;
 #pragma unroll
@@ -257,73 +255,43 @@ __global__ __launch_bounds__(kAttnThreads) void attn_mfma_kernel(AttnArgs a) {
 // ------------------------------------------------------------------------------------------------
 // head-group MFMA kernel (few query rows: decode): H = 64, D = 512, bf16 or mixed fp8/bf16 entries
 // ------------------------------------------------------------------------------------------------
-// A workgroup owns 16 heads (one head group) of one query row and one slice of the row's entry list; each of its
-// four waves takes every fourth 16-entry tile of the slice:
-//   S^T = K Q^T     v_mfma_f32_16x16x32_bf16, A = the tile's 16 rows from LDS, B = the 16 heads' queries (LDS)
-//   O^T += V^T P^T  v_mfma_f32_16x16x16_bf16, A = V^T read by ds_read_b64_tr_b16 straight from the row-major tile,
-//                   B = P^T, which is exactly the S^T accumulator layout (lane: head l % 16, entries 4 (l / 16) + v)
+// One workgroup per (16-head group, query row, slice of the row's list); each of its four waves streams its own
+// 16-entry tiles of the slice and keeps an online softmax for the 16 heads.
+//   S^T = K Q^T     v_mfma_f32_16x16x32_bf16, A = the tile (lane: entry l % 16, channels 32 s + 8 (l / 16) + v),
+//                   B = the 16 heads' queries (lane: head l % 16, the same channels); both stay in registers.
+//   O^T += V^T P^T  v_mfma_f32_16x16x16_bf16, A = V^T read by ds_read_b64_tr_b16 from the tile written row-major
+//                   to LDS, B = P^T, which is exactly the S^T accumulator layout (lane: head l % 16, entries
+//                   4 (l / 16) + v).
 // ds_read_b64_tr_b16: in each 16-lane group, output lane 4a + e takes element e of the 8-byte chunks addressed by
 // group lanes a, a + 4, a + 8, a + 12.  Group lane a + 4v addresses entry 4G + v, channels 16 dt + 4a .. + 3, so
 // lane 4a + e receives V[4G + v][16 dt + 4a + e] for v = 0..3, the A layout of the 16x16x16 instruction.
-// fp8 entries are widened to bf16 exactly when the tile is written to LDS; their per-entry scale multiplies the
-// fp8-channel part of the logit and is folded into P for the fp8 channels.
-// The four waves' (max, sum, o) are merged in LDS at the end; the four head groups of a (row, slice) pair get
-// workgroup ids congruent mod 8 so that they run on one XCD and share its L2 copy of the gathered entries.
-constexpr int kHgRow = 520;                                   // bf16 per LDS row (1040 bytes)
-constexpr int kHgOStride = 516;                               // floats per head row in the merge buffer
-
-typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
-
-// Each wave owns its own 16-entry LDS tile.  The next tile's 16 rows are loaded into registers (one wave-wide
-// 16-byte load per row, fully coalesced) while the current tile is scored, then written over the consumed tile, so
-// gathers overlap compute and no workgroup barrier is needed until the final merge.
-constexpr int kWTile = 16;
+// The tile is loaded straight into the S^T operand layout, the next one in flight while a tile is scored; the rows
+// of the slice's list
+// positions are resolved once into LDS so that a tile's loads never wait on an index load.  fp8 entries are widened
+// to bf16 in registers (exact: every e4m3 value is a bf16 value); their per-entry scale multiplies the fp8-channel
+// part of the logit and is folded into P for the fp8 channels.  The four waves' (max, sum, o) are merged in LDS at
+// the end; the four head groups of a (row, slice) pair get workgroup ids congruent mod 8 so that they run on one
+// XCD and share its L2 copy of the gathered entries.
+constexpr int kHgRow = 520;                // bf16 per LDS tile row (1040 bytes)
+constexpr int kHgOStride = 516;            // floats per head row in the merge buffer
+constexpr int kWTile = 16;                 // entries per wave tile
 constexpr float kRescaleSlack = 8.0f;
 constexpr int kWBufBytes = kWTile * kHgRow * 2;  // 16640
-// four wave tiles, then the per-wave (max, sum) of the merge; the merge's 2 x 16 x kHgOStride floats reuse the tiles
-// + the 16 heads' queries (shared), the waves' (max, sum) and entry scales
-constexpr size_t kHgwLds = (size_t)5 * kWBufBytes + 4 * 16 * 2 * 4 + 4 * 16 * 4;
+// four wave tiles (the merge's 2 x 16 x kHgOStride floats reuse them), the row table, the waves' (max, sum) and
+// the entry scales
+constexpr size_t kHgTableOff = (size_t)4 * kWBufBytes;
+constexpr size_t kHgMlOff = kHgTableOff + (size_t)kHgSplitMax * 4;
+constexpr size_t kHgwLds = kHgMlOff + 4 * 16 * 2 * 4 + 4 * 16 * 4;
 static_assert((size_t)2 * 16 * kHgOStride * 4 <= (size_t)4 * kWBufBytes, "merge buffer fits the tiles");
 
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(1))) const u32x4_t gbl_u32x4_t;
-
-struct WaveTile {
-  uint4 v[kWTile];  // lane i: bytes 16 i .. 16 i + 15 of each of the tile's 16 rows
-  uint64_t valid;   // bit j: entry j of the tile is real (padding loads a mapped dummy row, masked in the logits)
-};
-
-// Loads the 16 rows of list positions [p0, p0 + 16) into registers; each wave-wide 16-byte load reads one whole
-// 1 KB row.  Loads go through the global address space (not flat) so that waits on LDS traffic do not also wait
-// for these loads.
-__device__ __forceinline__ WaveTile wave_load_tile(const AttnArgs& a, const RowList& L, int b, int r, int p0,
-                                                   int p_end, int lane) {
-  WaveTile T;
-  const int p = p0 + (lane & 15);
-  long long row = -1;
-  if (lane < 16 && p < p_end) row = list_row(a, L, b, r, p);
-  const bool valid = row >= 0;
-  const unsigned long long base =
-      valid ? (unsigned long long)((const uint8_t*)(p < L.nw ? a.raw.data : a.comp.data) + row * 1024)
-            : (unsigned long long)((const uint8_t*)a.comp.data + (long long)b * a.comp.cap * 1024);
-  T.valid = __ballot(valid) & 0xFFFFull;
-#pragma unroll
-  for (int j = 0; j < kWTile; ++j) {
-    const unsigned long long rb = __shfl(base, j, 64);
-    const u32x4_t x = *(gbl_u32x4_t*)(rb + 16 * (unsigned long long)lane);
-    T.v[j] = make_uint4(x.x, x.y, x.z, x.w);
-  }
-  return T;
-}
-
-__device__ __forceinline__ void wave_store_tile(uint8_t* buf, int lane, const WaveTile& T) {
-#pragma unroll
-  for (int j = 0; j < kWTile; ++j) *(uint4*)(buf + j * (kHgRow * 2) + 16 * lane) = T.v[j];
-}
-
+typedef __attribute__((address_space(1))) const u32x2_t gbl_u32x2_t;
 typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2_t;
 
-// Four OCP e4m3 codes -> four bf16 (exact: every e4m3 value is a bf16 value), via the hardware fp8 -> f32 conversion.
+// Four OCP e4m3 codes -> four bf16 (exact), via the hardware fp8 -> f32 conversion.
 __device__ __forceinline__ uint2 fp8x4_to_bf16x4(uint32_t w) {
   const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
   const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
@@ -333,54 +301,72 @@ __device__ __forceinline__ uint2 fp8x4_to_bf16x4(uint32_t w) {
   return r;
 }
 
-struct WaveTileMixed {
-  uint4 v[kWTile];  // lane c < 28: fp8 chunk c (channels 16c .. 16c + 15); 28 <= c < 36: RoPE chunk c - 28
-  float scale;      // lane j < 16: the per-entry fp8 scale of row j
+// A wave's tile in the S^T operand layout.  bf16: v[s] = bytes 64 s + 16 (l / 16) .. + 15 of entry l % 16's row.
+// mixed: f[s] = fp8 bytes 32 s + 8 (l / 16) .. + 7 (s < 14), r[s] = RoPE bf16 bytes 64 s + 16 (l / 16) .. (s < 2).
+template <int FMT>
+struct HgTile;
+template <>
+struct HgTile<LCA_BF16> {
+  uint4 v[16];
+  uint64_t valid;  // bit j: entry j of the tile is real (the others load a clamped row and are masked)
+};
+template <>
+struct HgTile<LCA_MIXED_FP8> {
+  uint2 f[14];
+  uint4 r[2];
+  float scale;     // entry l % 16's fp8 scale
   uint64_t valid;
 };
 
-__device__ __forceinline__ WaveTileMixed wave_load_tile_mixed(const AttnArgs& a, const RowList& L, int b, int r,
-                                                              int p0, int p_end, int lane) {
-  WaveTileMixed T;
-  const int p = p0 + (lane & 15);
-  long long row = -1;
-  if (lane < 16 && p < p_end) row = list_row(a, L, b, r, p);
-  const bool valid = row >= 0;
-  const bool raw = valid && p < L.nw;
-  const long long rr = valid ? row : (long long)b * a.comp.cap;
+struct HgSlice {
+  int b, p_begin, npos, nw;  // list positions [p_begin, p_begin + npos); the first nw of the list are the window
+};
+
+template <int FMT>
+__device__ __forceinline__ void hg_load(HgTile<FMT>& T, const AttnArgs& a, const HgSlice& sl, const int* rows_s,
+                                        int i0, int lane) {
+  const int hl = lane & 15, grp = lane >> 4;
+  const int i = min(i0 + hl, sl.npos - 1);
+  const int row = rows_s[i];
+  const bool raw = sl.p_begin + i < sl.nw;
   const lca_tensor& src = raw ? a.raw : a.comp;
-  const unsigned long long fbase = (unsigned long long)((const uint8_t*)src.data + rr * 448);
-  const unsigned long long rbase = (unsigned long long)((const uint8_t*)src.rope + rr * 128);
-  T.scale = valid ? ((const float*)src.scale)[rr] : 1.0f;
-  T.valid = __ballot(valid) & 0xFFFFull;
-  const unsigned long long off = lane < 28 ? 16ull * lane : 16ull * (lane - 28);
+  const long long rr = (long long)sl.b * src.cap + (row >= 0 ? row : 0);
+  T.valid = __ballot(lane < 16 && i0 + hl < sl.npos && row >= 0) & 0xFFFFull;
+  if constexpr (FMT == LCA_BF16) {
+    const unsigned long long base = (unsigned long long)((const uint8_t*)src.data + rr * 1024) + 16 * grp;
 #pragma unroll
-  for (int j = 0; j < kWTile; ++j) {
-    const unsigned long long fb = __shfl(fbase, j, 64), rb = __shfl(rbase, j, 64);
-    if (lane < 36) {
-      const u32x4_t x = *(gbl_u32x4_t*)((lane < 28 ? fb : rb) + off);
-      T.v[j] = make_uint4(x.x, x.y, x.z, x.w);
-    } else {
-      T.v[j] = make_uint4(0, 0, 0, 0);
+    for (int s = 0; s < 16; ++s) {
+      const u32x4_t x = *(gbl_u32x4_t*)(base + 64 * s);
+      T.v[s] = make_uint4(x.x, x.y, x.z, x.w);
     }
+  } else {
+    HgTile<LCA_MIXED_FP8>& M = T;
+    const unsigned long long fb = (unsigned long long)((const uint8_t*)src.data + rr * 448) + 8 * grp;
+    const unsigned long long rb = (unsigned long long)((const uint8_t*)src.rope + rr * 128) + 16 * grp;
+#pragma unroll
+    for (int s = 0; s < 14; ++s) {
+      const u32x2_t x = *(gbl_u32x2_t*)(fb + 32 * s);
+      M.f[s] = make_uint2(x.x, x.y);
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const u32x4_t x = *(gbl_u32x4_t*)(rb + 64 * s);
+      M.r[s] = make_uint4(x.x, x.y, x.z, x.w);
+    }
+    M.scale = ((const float*)src.scale)[rr];
   }
-  return T;
 }
 
-__device__ __forceinline__ void wave_store_tile_mixed(uint8_t* buf, float* scale_w, int lane, const WaveTileMixed& T) {
-#pragma unroll
-  for (int j = 0; j < kWTile; ++j) {
-    uint8_t* row = buf + j * (kHgRow * 2);
-    if (lane < 28) {
-      const uint2 a0 = fp8x4_to_bf16x4(T.v[j].x), a1 = fp8x4_to_bf16x4(T.v[j].y);
-      const uint2 a2 = fp8x4_to_bf16x4(T.v[j].z), a3 = fp8x4_to_bf16x4(T.v[j].w);
-      *(uint4*)(row + 32 * lane) = make_uint4(a0.x, a0.y, a1.x, a1.y);
-      *(uint4*)(row + 32 * lane + 16) = make_uint4(a2.x, a2.y, a3.x, a3.y);
-    } else if (lane < 36) {
-      *(uint4*)(row + 896 + 16 * (lane - 28)) = T.v[j];
-    }
+// The tile's 8 channels of K-step s as bf16 (the A operand), widened from fp8 for the mixed format.
+template <int FMT>
+__device__ __forceinline__ uint4 hg_chunk(const HgTile<FMT>& T, int s) {
+  if constexpr (FMT == LCA_BF16) {
+    return T.v[s];
+  } else {
+    if (s >= 14) return T.r[s - 14];
+    const uint2 lo = fp8x4_to_bf16x4(T.f[s].x), hi = fp8x4_to_bf16x4(T.f[s].y);
+    return make_uint4(lo.x, lo.y, hi.x, hi.y);
   }
-  if (lane < 16) scale_w[lane] = T.scale;
 }
 
 template <int FMT>
@@ -396,77 +382,80 @@ __global__ __launch_bounds__(256) void attn_hgw_kernel(AttnArgs a, int pairs) {
   const long long t = a.q_start + r;
   const RowList L = row_list(a, t);
   const int total = L.nw + L.nc;
-  const int p_begin = split * a.split_len;
-  const int p_end = min(p_begin + a.split_len, total);
+  HgSlice sl;
+  sl.b = b;
+  sl.p_begin = split * a.split_len;
+  sl.npos = max(min(a.split_len, total - sl.p_begin), 0);
+  sl.nw = L.nw;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int hl = lane & 15, grp = lane >> 4;
   const int head = 16 * hg + hl;
   uint8_t* wbuf = hgw_lds + wave * kWBufBytes;
-  uint16_t* q_s = (uint16_t*)(hgw_lds + 4 * kWBufBytes);  // [16 heads][kHgRow]
-  float* ml_s = (float*)(hgw_lds + 5 * kWBufBytes);         // [4 waves][16 heads][2]
-  float* esc_w = ml_s + 4 * 16 * 2 + 16 * wave;             // [4 waves][16] entry scales (fp8 cache)
+  int* rows_s = (int*)(hgw_lds + kHgTableOff);
+  float* ml_s = (float*)(hgw_lds + kHgMlOff);  // [4 waves][16 heads][2]
+  float* esc_w = ml_s + 4 * 16 * 2 + 16 * wave;  // [4 waves][16] entry scales (fp8 cache)
 
-  const int ntiles = p_end > p_begin ? (p_end - p_begin + kWTile - 1) / kWTile : 0;
-  int tt = wave;
-  uint64_t cur = 0;
-  if (tt < ntiles) {
-    if (FMT == LCA_BF16) {
-      const WaveTile T0 = wave_load_tile(a, L, b, r, p_begin + kWTile * tt, p_end, lane);
-      wave_store_tile(wbuf, lane, T0);
-      cur = T0.valid;
+  // rows of the slice's list positions (window positions index the raw tensor, the rest the compressed one; -1:
+  // padding)
+  for (int i = threadIdx.x; i < sl.npos; i += blockDim.x) {
+    const int p = sl.p_begin + i;
+    int row;
+    if (p < L.nw) {
+      row = (int)(L.w0 + p - a.raw_start);
+    } else if (a.hca_m > 0) {
+      row = p - L.nw;
     } else {
-      const WaveTileMixed T0 = wave_load_tile_mixed(a, L, b, r, p_begin + kWTile * tt, p_end, lane);
-      wave_store_tile_mixed(wbuf, esc_w, lane, T0);
-      cur = T0.valid;
+      const int e = a.idx[((long long)b * a.Sq + r) * a.k + (p - L.nw)];
+      row = (e >= 0 && e < a.N) ? e : -1;
     }
+    rows_s[i] = row;
   }
-
-  {  // the 16 heads' queries (16 KB), once per workgroup: thread -> 4 chunks of 16 bytes
-    const uint8_t* qg = (const uint8_t*)a.q + ((long long)qrow * 64 + 16 * hg) * 1024;
+  // the 16 heads' queries as the B operand: lane holds head 16 hg + hl, channels 32 s + 8 grp .. + 7
+  bf16x8_t qv[16];
+  {
+    const uint8_t* qp = (const uint8_t*)a.q + ((long long)qrow * 64 + head) * 1024 + 16 * grp;
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      const int c = threadIdx.x + 256 * x, h = c >> 6, piece = c & 63;
-      *(uint4*)((uint8_t*)q_s + h * (kHgRow * 2) + 16 * piece) = *(const uint4*)(qg + h * 1024 + 16 * piece);
-    }
+    for (int s = 0; s < 16; ++s) qv[s] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(qp + 64 * s));
   }
   __syncthreads();
+
   f32x4_t acc_o[32];
 #pragma unroll
   for (int dt = 0; dt < 32; ++dt) acc_o[dt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   float m_run = -INFINITY, l_run = 0.0f;
-  const uint16_t* qsp = q_s + hl * kHgRow + 8 * grp;
+  const uint16_t* kt = (const uint16_t*)wbuf;
+  const uint16_t* vp = kt + (4 * grp + (hl >> 2)) * kHgRow + 4 * (hl & 3);
 
-  for (; tt < ntiles; tt += 4) {
-    // the next tile's rows are in flight while this one is scored (past the slice end: masked dummy rows)
-    WaveTile nxt;
-    WaveTileMixed nxm;
-    if (FMT == LCA_BF16)
-      nxt = wave_load_tile(a, L, b, r, p_begin + kWTile * (tt + 4), p_end, lane);
-    else
-      nxm = wave_load_tile_mixed(a, L, b, r, p_begin + kWTile * (tt + 4), p_end, lane);
-    const uint16_t* kt = (const uint16_t*)wbuf;
-
+  // Scores tile T, then reuses its registers for the loads of the tile at list offset next_i0.
+  auto process = [&](HgTile<FMT>& T, int next_i0) {
+    // S^T for the tile's 16 entries x 16 heads; the tile goes to LDS (bf16) for the V^T reads
     f32x4_t am = {0.0f, 0.0f, 0.0f, 0.0f}, ar = {0.0f, 0.0f, 0.0f, 0.0f};
-    const uint16_t* kp = kt + hl * kHgRow + 8 * grp;
 #pragma unroll
     for (int s = 0; s < 16; ++s) {
-      const bf16x8_t kv = __builtin_bit_cast(bf16x8_t, *(const uint4*)(kp + 32 * s));
-      const bf16x8_t qv = __builtin_bit_cast(bf16x8_t, *(const uint4*)(qsp + 32 * s));
+      const uint4 c = hg_chunk<FMT>(T, s);
+      *(uint4*)(wbuf + hl * (kHgRow * 2) + 64 * s + 16 * grp) = c;
+      const bf16x8_t kv = __builtin_bit_cast(bf16x8_t, c);
       if (FMT == LCA_MIXED_FP8 && s >= 14)  // RoPE channels: bf16, not scaled
-        ar = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qv, ar, 0, 0, 0);
+        ar = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qv[s], ar, 0, 0, 0);
       else
-        am = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qv, am, 0, 0, 0);
+        am = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qv[s], am, 0, 0, 0);
     }
-    float lg[4], esc[4];
+    float esc[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+    if constexpr (FMT == LCA_MIXED_FP8) {
+      if (lane < 16) esc_w[lane] = T.scale;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) esc[x] = esc_w[4 * grp + x];
+    }
+    const uint64_t valid = T.valid;
+    hg_load<FMT>(T, a, sl, rows_s, next_i0, lane);  // the tile's registers are free: the next tile is in flight
+    float lg[4];
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
-      esc[x] = (FMT == LCA_MIXED_FP8) ? esc_w[4 * grp + x] : 1.0f;
       const float l = (FMT == LCA_MIXED_FP8) ? a.scale * (esc[x] * am[x] + ar[x]) : a.scale * am[x];
-      lg[x] = ((cur >> (4 * grp + x)) & 1ull) ? l : -INFINITY;
+      lg[x] = ((valid >> (4 * grp + x)) & 1ull) ? l : -INFINITY;
     }
     float mt = fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3]));
-    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    mt = xor32_max(xor16_max(mt));
     // The reference max only moves when a logit exceeds it by more than kRescaleSlack (e^8 keeps every weight and
     // sum far inside fp32, and bf16 keeps 8 significant bits at any scale), so the accumulators are rescaled a few
     // times per row instead of on every tile.
@@ -478,8 +467,7 @@ __global__ __launch_bounds__(256) void attn_hgw_kernel(AttnArgs a, int pairs) {
       pv[x] = (lg[x] == -INFINITY) ? 0.0f : __expf(lg[x] - m_new);
       psum += pv[x];
     }
-    psum += __shfl_xor(psum, 16, 64);
-    psum += __shfl_xor(psum, 32, 64);
+    psum = xor32_sum(xor16_sum(psum));
     l_run = l_run * alpha + psum;
     m_run = m_new;
     s16x4_t pb, pbs;
@@ -488,24 +476,30 @@ __global__ __launch_bounds__(256) void attn_hgw_kernel(AttnArgs a, int pairs) {
       pb[x] = (short)f32_to_bf16(pv[x]);
       pbs[x] = (FMT == LCA_MIXED_FP8) ? (short)f32_to_bf16(pv[x] * esc[x]) : pb[x];  // fp8 channels carry the scale
     }
-    const uint16_t* vp = kt + (4 * grp + (hl >> 2)) * kHgRow + 4 * (hl & 3);
     if (__ballot(alpha != 1.0f)) {  // wave-uniform: some head's reference max moved
 #pragma unroll
       for (int dt = 0; dt < 32; ++dt) acc_o[dt] *= alpha;
     }
+    // V^T reads eight channel tiles ahead of the products
 #pragma unroll
-    for (int dt = 0; dt < 32; ++dt) {
-      const s16x4_t av = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vp + 16 * dt));
-      acc_o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, (FMT == LCA_MIXED_FP8 && dt < 28) ? pbs : pb, acc_o[dt],
-                                                            0, 0, 0);
+    for (int d0 = 0; d0 < 32; d0 += 8) {
+      s16x4_t av[8];
+#pragma unroll
+      for (int d = 0; d < 8; ++d) av[d] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vp + 16 * (d0 + d)));
+#pragma unroll
+      for (int d = 0; d < 8; ++d)
+        acc_o[d0 + d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+            av[d], (FMT == LCA_MIXED_FP8 && d0 + d < 28) ? pbs : pb, acc_o[d0 + d], 0, 0, 0);
     }
-    if (FMT == LCA_BF16) {  // the tile's LDS reads are complete: refill in place
-      wave_store_tile(wbuf, lane, nxt);
-      cur = nxt.valid;
-    } else {
-      wave_store_tile_mixed(wbuf, esc_w, lane, nxm);
-      cur = nxm.valid;
-    }
+  };
+
+  // the wave's tiles tt = wave, wave + 4, ...: each tile's registers take the next tile's loads as soon as its
+  // S^T products are issued, so the loads overlap the softmax and the V^T products
+  const int ntiles = (sl.npos + kWTile - 1) / kWTile;
+  if (wave < ntiles) {
+    HgTile<FMT> T;
+    hg_load<FMT>(T, a, sl, rows_s, kWTile * wave, lane);
+    for (int tt = wave; tt < ntiles; tt += 4) process(T, kWTile * (tt + 4));
   }
 
   // merge the four waves (same heads, different entries)
@@ -579,6 +573,347 @@ __global__ __launch_bounds__(256) void attn_hgw_kernel(AttnArgs a, int pairs) {
     if (grp == 0) {
       a.part_ml[(item * 64 + head) * 2 + 0] = M;
       a.part_ml[(item * 64 + head) * 2 + 1] = Lsum;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
+// wide MFMA kernel (few query rows over many entries: dense HCA decode): H = 64, D = 512, bf16 or mixed entries
+// ------------------------------------------------------------------------------------------------
+// One workgroup per (query row, slice of its list) with all 64 heads; wave w owns channels [128 w, 128 w + 128) of
+// every entry, so each entry is read from memory once per workgroup and each wave streams only its quarter of it.
+// Per 32-entry tile:
+//   partial S^T (v_mfma_f32_16x16x32_bf16: A = the wave's channels of the tile, B = those channels of the 64
+//     heads' queries, both in registers) -> LDS; barrier;
+//   wave w sums the four partials for heads [16 w, 16 w + 16), runs their online softmax (lazy rescale as in the
+//     head-group kernel) and writes P (bf16, and P times the entry's fp8 scale) and the rescale factors to LDS;
+//     barrier;
+//   O^T += V^T P^T for the wave's channels and all heads (v_mfma_f32_16x16x32_bf16, K = the tile's 32 entries:
+//     A = V^T from two ds_read_b64_tr_b16 of the wave's own row-major tile in LDS, B = P^T from LDS).
+// The output of a wave's channels needs no cross-wave merge; the heads' (max, sum) come from their owners.
+constexpr int kWdTile = 32;                                 // entries per tile
+constexpr int kWdRowB = 272;                                // LDS bytes per tile row (a wave's 128 channels + pad)
+constexpr int kWdTileBytes = kWdTile * kWdRowB;             // 8704 per wave
+constexpr int kWdSpStride = 36;                             // floats per head row of a wave's partial logits
+constexpr int kWdPStride = 40;                              // bf16 per head row of P (32 entries + pad)
+constexpr size_t kWdSpOff = (size_t)4 * kWdTileBytes;
+constexpr size_t kWdPOff = kWdSpOff + (size_t)4 * 64 * kWdSpStride * 4;
+constexpr size_t kWdAlphaOff = kWdPOff + (size_t)2 * 64 * kWdPStride * 2;
+constexpr size_t kWdTableOff = kWdAlphaOff + 64 * 4;
+constexpr size_t kWdMlOff = kWdTableOff + (size_t)kHgSplitMax * 4;
+constexpr size_t kWdQOff = kWdMlOff + 64 * 2 * 4;              // queries in operand layout, 16 KB per wave
+constexpr size_t kWdLds = kWdQOff + (size_t)4 * 16 * 64 * 16;
+static_assert(kWdLds <= 160 * 1024, "wide kernel LDS");
+
+// A wave's tile: for entry 16 eb + l % 16 and K-step s, channels 128 w + 32 s + 8 (l / 16) .. + 7.
+template <int FMT>
+struct WdTile;
+template <>
+struct WdTile<LCA_BF16> {
+  uint4 v[2][4];
+  uint32_t valid;  // bit j: entry j of the tile is real
+};
+template <>
+struct WdTile<LCA_MIXED_FP8> {
+  uint2 f[2][4];   // fp8 codes of the step (channels < 448)
+  uint4 r[2][2];   // wave 3, steps 2..3: RoPE channels 448.. in bf16
+  float scale[2];  // the fp8 scale of entry 16 eb + l % 16
+  uint32_t valid;
+};
+
+template <int FMT>
+__device__ __forceinline__ void wd_load(WdTile<FMT>& T, const AttnArgs& a, const HgSlice& sl, const int* rows_s,
+                                        int i0, int wave, int lane) {
+  const int hl = lane & 15, grp = lane >> 4;
+  uint32_t valid = 0;
+#pragma unroll
+  for (int eb = 0; eb < 2; ++eb) {
+    const int i = min(i0 + 16 * eb + hl, sl.npos - 1);
+    const int row = rows_s[i];
+    const bool raw = sl.p_begin + i < sl.nw;
+    const lca_tensor& src = raw ? a.raw : a.comp;
+    const long long rr = (long long)sl.b * src.cap + (row >= 0 ? row : 0);
+    valid |= (uint32_t)(__ballot(lane < 16 && i0 + 16 * eb + hl < sl.npos && row >= 0) & 0xFFFFull) << (16 * eb);
+    if constexpr (FMT == LCA_BF16) {
+      const unsigned long long base = (unsigned long long)((const uint8_t*)src.data + rr * 1024) + 256 * wave + 16 * grp;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const u32x4_t x = *(gbl_u32x4_t*)(base + 64 * s);
+        T.v[eb][s] = make_uint4(x.x, x.y, x.z, x.w);
+      }
+    } else {
+      const unsigned long long fb = (unsigned long long)((const uint8_t*)src.data + rr * 448) + 128 * wave + 8 * grp;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        if (wave == 3 && s >= 2) {
+          const u32x4_t x = *(gbl_u32x4_t*)((unsigned long long)((const uint8_t*)src.rope + rr * 128) + 16 * grp +
+                                            64 * (s - 2));
+          T.r[eb][s - 2] = make_uint4(x.x, x.y, x.z, x.w);
+        } else {
+          const u32x2_t x = *(gbl_u32x2_t*)(fb + 32 * s);
+          T.f[eb][s] = make_uint2(x.x, x.y);
+        }
+      }
+      T.scale[eb] = ((const float*)src.scale)[rr];
+    }
+  }
+  T.valid = valid;
+}
+
+template <int FMT>
+__device__ __forceinline__ uint4 wd_chunk(const WdTile<FMT>& T, int eb, int s, int wave) {
+  if constexpr (FMT == LCA_BF16) {
+    return T.v[eb][s];
+  } else {
+    if (wave == 3 && s >= 2) return T.r[eb][s - 2];
+    const uint2 lo = fp8x4_to_bf16x4(T.f[eb][s].x), hi = fp8x4_to_bf16x4(T.f[eb][s].y);
+    return make_uint4(lo.x, lo.y, hi.x, hi.y);
+  }
+}
+
+template <int FMT>
+__global__ __launch_bounds__(256) void attn_wide_kernel(AttnArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t wd_lds[];
+  const int item = blockIdx.x;
+  const int S = a.n_splits;
+  const int qrow = item / S, split = item % S;
+  const int b = qrow / a.Sq, r = qrow % a.Sq;
+  const long long t = a.q_start + r;
+  const RowList L = row_list(a, t);
+  const int total = L.nw + L.nc;
+  HgSlice sl;
+  sl.b = b;
+  sl.p_begin = split * a.split_len;
+  sl.npos = max(min(a.split_len, total - sl.p_begin), 0);
+  sl.nw = L.nw;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int hl = lane & 15, grp = lane >> 4;
+  uint8_t* tbuf = wd_lds + wave * kWdTileBytes;
+  float* sp = (float*)(wd_lds + kWdSpOff);             // [4 waves][64 heads][kWdSpStride]
+  uint16_t* P_s = (uint16_t*)(wd_lds + kWdPOff);       // [64 heads][kWdPStride]
+  uint16_t* Pe_s = P_s + 64 * kWdPStride;              // P times the entry scale (fp8 channels)
+  float* alpha_s = (float*)(wd_lds + kWdAlphaOff);     // [64]
+  int* rows_s = (int*)(wd_lds + kWdTableOff);
+  float* ml_s = (float*)(wd_lds + kWdMlOff);           // [64][2]
+  uint4* q_s = (uint4*)(wd_lds + kWdQOff) + wave * 16 * 64;  // [s][hb][lane] B operands of this wave's channels
+  constexpr bool kMixed = FMT == LCA_MIXED_FP8;
+
+  for (int i = threadIdx.x; i < sl.npos; i += blockDim.x) {
+    const int p = sl.p_begin + i;
+    int row;
+    if (p < L.nw) {
+      row = (int)(L.w0 + p - a.raw_start);
+    } else if (a.hca_m > 0) {
+      row = p - L.nw;
+    } else {
+      const int e = a.idx[((long long)b * a.Sq + r) * a.k + (p - L.nw)];
+      row = (e >= 0 && e < a.N) ? e : -1;
+    }
+    rows_s[i] = row;
+  }
+  // queries (B operand of the partial S^T: lane holds head 16 hb + hl, channels 128 wave + 32 s + 8 grp .. + 7),
+  // kept in LDS in operand order so that the registers go to tiles in flight
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb) {
+    const uint8_t* qp = (const uint8_t*)a.q + ((long long)qrow * 64 + 16 * hb + hl) * 1024 + 256 * wave + 16 * grp;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) q_s[(4 * s + hb) * 64 + lane] = *(const uint4*)(qp + 64 * s);
+  }
+  __syncthreads();
+
+  f32x4_t acc_o[8][4];  // [channel tile mb][head block hb]: channel 128 wave + 16 mb + 4 grp + x, head 16 hb + hl
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) acc_o[mb][hb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  float m_run = -INFINITY, l_run = 0.0f;  // of head 16 wave + hl (this wave owns its softmax)
+  // fp8 channels of this wave's tile rows mb: all for waves 0..2, mb < 4 for wave 3 (channels 384..447)
+  const int scaled_mb = (kMixed && wave == 3) ? 4 : 8;
+
+  auto step = [&](WdTile<FMT>& T, int next_i0) {
+    // partial S^T of the tile over this wave's channels; the tile goes to LDS (bf16) for the V^T reads.  fp8
+    // channels are scaled by the entry's scale before the RoPE channels (wave 3, steps 2..3) add in.
+    float esc[2][4];  // the scales of the accumulator's entries 16 eb + 4 grp + x (lane 4 grp + x loaded them)
+#pragma unroll
+    for (int eb = 0; eb < 2; ++eb)
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        if constexpr (kMixed) esc[eb][x] = __shfl(T.scale[eb], 4 * grp + x, 64);
+        else esc[eb][x] = 1.0f;
+      }
+    auto scale_partial = [&](f32x4_t (&acc)[2][4]) {
+#pragma unroll
+      for (int eb = 0; eb < 2; ++eb)
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+          for (int x = 0; x < 4; ++x) acc[eb][hb][x] = esc[eb][x] * acc[eb][hb][x];
+    };
+    f32x4_t sacc[2][4];
+#pragma unroll
+    for (int eb = 0; eb < 2; ++eb)
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb) sacc[eb][hb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (kMixed && wave == 3 && s == 2) scale_partial(sacc);
+      bf16x8_t qv[4];
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb) qv[hb] = __builtin_bit_cast(bf16x8_t, q_s[(4 * s + hb) * 64 + lane]);
+#pragma unroll
+      for (int eb = 0; eb < 2; ++eb) {
+        const uint4 c = wd_chunk<FMT>(T, eb, s, wave);
+        *(uint4*)(tbuf + (16 * eb + hl) * kWdRowB + 64 * s + 16 * grp) = c;
+        const bf16x8_t kv = __builtin_bit_cast(bf16x8_t, c);
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb)
+          sacc[eb][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qv[hb], sacc[eb][hb], 0, 0, 0);
+      }
+    }
+    if (kMixed && wave != 3) scale_partial(sacc);
+    const uint32_t valid = T.valid;
+#pragma unroll
+    for (int eb = 0; eb < 2; ++eb)
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb)
+        *(f32x4_t*)(sp + (wave * 64 + 16 * hb + hl) * kWdSpStride + 16 * eb + 4 * grp) = sacc[eb][hb];
+    wd_load<FMT>(T, a, sl, rows_s, next_i0, wave, lane);  // the tile's registers are free: the next tile is in flight
+    __syncthreads();
+
+    // softmax of heads 16 wave + hl over the tile's entries 16 eb + 4 grp + x
+    float lg[2][4];
+#pragma unroll
+    for (int eb = 0; eb < 2; ++eb) {
+      f32x4_t s4 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) s4 += *(const f32x4_t*)(sp + (w * 64 + 16 * wave + hl) * kWdSpStride + 16 * eb + 4 * grp);
+#pragma unroll
+      for (int x = 0; x < 4; ++x) lg[eb][x] = ((valid >> (16 * eb + 4 * grp + x)) & 1u) ? a.scale * s4[x] : -INFINITY;
+    }
+    float mt = -INFINITY;
+#pragma unroll
+    for (int eb = 0; eb < 2; ++eb)
+#pragma unroll
+      for (int x = 0; x < 4; ++x) mt = fmaxf(mt, lg[eb][x]);
+    mt = xor32_max(xor16_max(mt));
+    const float m_new = (mt > m_run + kRescaleSlack) ? mt : m_run;
+    const float alpha = (m_new == m_run) ? 1.0f : __expf(m_run - m_new);
+    float psum = 0.0f;
+#pragma unroll
+    for (int eb = 0; eb < 2; ++eb) {
+      float p[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        p[x] = (lg[eb][x] == -INFINITY) ? 0.0f : __expf(lg[eb][x] - m_new);
+        psum += p[x];
+      }
+      uint2 pw;
+      pw.x = (uint32_t)f32_to_bf16(p[0]) | ((uint32_t)f32_to_bf16(p[1]) << 16);
+      pw.y = (uint32_t)f32_to_bf16(p[2]) | ((uint32_t)f32_to_bf16(p[3]) << 16);
+      *(uint2*)(P_s + (16 * wave + hl) * kWdPStride + 16 * eb + 4 * grp) = pw;
+      if constexpr (kMixed) {
+        uint2 pe;
+        pe.x = (uint32_t)f32_to_bf16(p[0] * esc[eb][0]) | ((uint32_t)f32_to_bf16(p[1] * esc[eb][1]) << 16);
+        pe.y = (uint32_t)f32_to_bf16(p[2] * esc[eb][2]) | ((uint32_t)f32_to_bf16(p[3] * esc[eb][3]) << 16);
+        *(uint2*)(Pe_s + (16 * wave + hl) * kWdPStride + 16 * eb + 4 * grp) = pe;
+      }
+    }
+    psum = xor32_sum(xor16_sum(psum));
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    if (grp == 0) alpha_s[16 * wave + hl] = alpha;
+    __syncthreads();
+
+    // O^T += V^T P^T over this wave's channels, all 64 heads
+    float al[4];
+    bool any = false;
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) {
+      al[hb] = alpha_s[16 * hb + hl];
+      any |= al[hb] != 1.0f;
+    }
+    if (__ballot(any)) {
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) acc_o[mb][hb] *= al[hb];
+    }
+    // P^T operands: P times the entry scale for the fp8 channel tiles, plain P for the RoPE ones (wave 3, mb >= 4)
+    bf16x8_t bp[4];
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb)
+      bp[hb] = __builtin_bit_cast(bf16x8_t, *(const uint4*)((kMixed ? Pe_s : P_s) + (16 * hb + hl) * kWdPStride + 8 * grp));
+    const uint8_t* vrow = tbuf + (8 * grp + (hl >> 2)) * kWdRowB + 8 * (hl & 3);
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+      if (kMixed && mb == scaled_mb) {
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb)
+          bp[hb] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(P_s + (16 * hb + hl) * kWdPStride + 8 * grp));
+      }
+      const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vrow + 32 * mb));
+      const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vrow + 4 * kWdRowB + 32 * mb));
+      const bf16x8_t av = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb)
+        acc_o[mb][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bp[hb], acc_o[mb][hb], 0, 0, 0);
+    }
+  };
+
+  const int ntiles = (sl.npos + kWdTile - 1) / kWdTile;
+  if (ntiles > 0) {  // uniform over the workgroup: every wave takes every tile (its own channels)
+    // two tiles in turn: one is in flight while the other is scored
+    WdTile<FMT> TA, TB;
+    wd_load<FMT>(TA, a, sl, rows_s, 0, wave, lane);
+    wd_load<FMT>(TB, a, sl, rows_s, kWdTile, wave, lane);
+    for (int tt = 0; tt < ntiles; tt += 2) {
+      step(TA, kWdTile * (tt + 2));
+      if (tt + 1 >= ntiles) break;
+      step(TB, kWdTile * (tt + 3));
+    }
+  }
+
+  // every head's (max, sum) from its owner
+  if (grp == 0) {
+    ml_s[(16 * wave + hl) * 2 + 0] = m_run;
+    ml_s[(16 * wave + hl) * 2 + 1] = l_run;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb) {
+    const int head = 16 * hb + hl;
+    const float M = ml_s[head * 2 + 0], Ls = ml_s[head * 2 + 1];
+    if (S == 1) {
+      const float z = a.sink[head];
+      const float Mz = fmaxf(M, z);
+      float den = 0.0f, f = 0.0f;
+      if (Mz != -INFINITY) {
+        den = ((z == -INFINITY) ? 0.0f : __expf(z - Mz)) + ((M == -INFINITY) ? 0.0f : Ls * __expf(M - Mz));
+        f = (M == -INFINITY) ? 0.0f : __expf(M - Mz) / den;
+      }
+      const long long obase = ((long long)qrow * 64 + head) * 512 + 128 * wave + 4 * grp;
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) {
+        const f32x4_t o = acc_o[mb][hb];
+        if (a.out_format == LCA_F32) {
+          *(float4*)((float*)a.out + obase + 16 * mb) = make_float4(o[0] * f, o[1] * f, o[2] * f, o[3] * f);
+        } else {
+          uint2 w2;
+          w2.x = (uint32_t)f32_to_bf16(o[0] * f) | ((uint32_t)f32_to_bf16(o[1] * f) << 16);
+          w2.y = (uint32_t)f32_to_bf16(o[2] * f) | ((uint32_t)f32_to_bf16(o[3] * f) << 16);
+          *(uint2*)((uint16_t*)a.out + obase + 16 * mb) = w2;
+        }
+      }
+      if (a.lse && wave == hb && grp == 0)
+        a.lse[(long long)qrow * 64 + head] = (Mz == -INFINITY) ? -INFINITY : Mz + __logf(den);
+    } else {
+      float* po = a.part_o + ((long long)item * 64 + head) * 512 + 128 * wave + 4 * grp;
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) *(f32x4_t*)(po + 16 * mb) = acc_o[mb][hb];
+      if (wave == hb && grp == 0) {
+        a.part_ml[((long long)item * 64 + head) * 2 + 0] = M;
+        a.part_ml[((long long)item * 64 + head) * 2 + 1] = Ls;
+      }
     }
   }
 }
@@ -760,6 +1095,7 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
 constexpr size_t kMfmaLds = (size_t)kTE * kRowStride * 2 + (size_t)512 * kTStride * 2 + kTE * 4 * 2;
 static bool g_attn_attr[64];
 static bool g_hg_attr[64];
+static bool g_wd_attr[64];
 
 bool attn_uses_mfma(int H, int D, int q_format, int kv_format) {
   return H == 64 && D == 512 && q_format == LCA_BF16 && (kv_format == LCA_BF16 || kv_format == LCA_MIXED_FP8);
@@ -769,7 +1105,24 @@ hipError_t launch_attn(AttnArgs a, hipStream_t st) {
   const bool mfma = attn_uses_mfma(a.H, a.D, a.q_format, a.comp.format);
   dim3 grid((unsigned)a.n_splits, (unsigned)a.Sq, (unsigned)a.B);
   clear_stale_error();
-  if (mfma && a.hg_mode) {
+  if (mfma && a.hg_mode == 2) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    if (dev >= 0 && dev < 64 && !g_wd_attr[dev]) {
+      hipError_t e = hipFuncSetAttribute((const void*)attn_wide_kernel<LCA_BF16>,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)kWdLds);
+      if (e == hipSuccess)
+        e = hipFuncSetAttribute((const void*)attn_wide_kernel<LCA_MIXED_FP8>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kWdLds);
+      if (e != hipSuccess) return e;
+      g_wd_attr[dev] = true;
+    }
+    const dim3 wgrid((unsigned)(a.B * a.Sq * a.n_splits));
+    if (a.comp.format == LCA_BF16)
+      hipLaunchKernelGGL(attn_wide_kernel<LCA_BF16>, wgrid, dim3(256), kWdLds, st, a);
+    else
+      hipLaunchKernelGGL(attn_wide_kernel<LCA_MIXED_FP8>, wgrid, dim3(256), kWdLds, st, a);
+  } else if (mfma && a.hg_mode == 1) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) dev = 0;
     if (dev >= 0 && dev < 64 && !g_hg_attr[dev]) {

@@ -215,10 +215,7 @@ __global__ __launch_bounds__(256) void idx_score_mfma(IdxArgs a, int qpb) {
 #pragma unroll
       for (int x = 0; x < 4; ++x) l3[x] = l2[x] + l2[x + 4];  // h + 8
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {  // h + 4: the partner lane holds the other 4g half
-        float o = __shfl_xor(l3[x], 32, 64);
-        l4[x] = (g == 0) ? (l3[x] + o) : (o + l3[x]);
-      }
+      for (int x = 0; x < 4; ++x) l4[x] = xor32_sum(l3[x]);  // h + 4: the partner lane holds the other 4g half
       float l5_0 = l4[0] + l4[2], l5_1 = l4[1] + l4[3];  // h + 2
       float s = l5_0 + l5_1;                             // h + 1
       const int e = e0 + 32 * u + col;
@@ -244,7 +241,7 @@ __global__ __launch_bounds__(256) void idx_score_mfma(IdxArgs a, int qpb) {
 // counts into the row's histogram, zeroed before the launch.  The select that follows reads it instead of making
 // its own first pass over the keys.
 
-__device__ __forceinline__ float head_tree(const f32x4_t (&acc)[4], const float (&wv)[4][4], int g) {
+__device__ __forceinline__ float head_tree(const f32x4_t (&acc)[4], const float (&wv)[4][4]) {
   float l1[2][4], l2[4], l3[4], l4[4];
 #pragma unroll
   for (int T = 0; T < 2; ++T)
@@ -257,15 +254,9 @@ __device__ __forceinline__ float head_tree(const f32x4_t (&acc)[4], const float 
 #pragma unroll
   for (int r = 0; r < 4; ++r) l2[r] = l1[0][r] + l1[1][r];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const float o = __shfl_xor(l2[r], 32, 64);
-    l3[r] = (g < 2) ? (l2[r] + o) : (o + l2[r]);
-  }
+  for (int r = 0; r < 4; ++r) l3[r] = xor32_sum(l2[r]);
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const float o = __shfl_xor(l3[r], 16, 64);
-    l4[r] = ((g & 1) == 0) ? (l3[r] + o) : (o + l3[r]);
-  }
+  for (int r = 0; r < 4; ++r) l4[r] = xor16_sum(l3[r]);
   return (l4[0] + l4[2]) + (l4[1] + l4[3]);
 }
 
@@ -372,7 +363,7 @@ __global__ __launch_bounds__(256, 2) void idx_score_decode_bf16(IdxArgs a) {
 #pragma unroll
         for (int T = 0; T < 4; ++T) acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[T][s], kv, acc[T], 0, 0, 0);
       }
-      sc[j] = head_tree(acc, wv, g);
+      sc[j] = head_tree(acc, wv);
     }
     pend = pick_key4(kbase, g, sc);
   }
@@ -483,7 +474,7 @@ __global__ __launch_bounds__(256, 2) void idx_score_decode_fp4(IdxArgs a) {
           acc[T] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fp4_operand(qc[T][2], qc[T][3]), kop1, acc[T], 4,
                                                                     4, 0, qs[T][1], 0, ks1);
         }
-        sc[jj] = head_tree(acc, wv, g);
+        sc[jj] = head_tree(acc, wv);
       }
       pend = pick_key4(kbase + 64 * q, g, sc);
     }

@@ -100,6 +100,40 @@ __device__ __forceinline__ float key_score(uint32_t k) {
 // ------------------------------------------------------------------------------------------------
 // Wave / block reductions
 // ------------------------------------------------------------------------------------------------
+// Cross-lane combines by lane swaps on the VALU (v_permlane32_swap / v_permlane16_swap, no LDS round trip).  With
+// both operands equal to x, permlane32_swap returns (x[l & 31], x[(l & 31) + 32]) and permlane16_swap returns the
+// even-row and odd-row values of each pair of 16-lane rows, so every lane gets its own and its partner's value;
+// fp32 addition is commutative, so the sum equals own + partner in either lane of the pair.
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Inclusive prefix sum over the 64 lanes with DPP: Hillis-Steele shifts 1, 2, 4, 8 inside each 16-lane row (lanes
+// shifted in from outside the row read 0), then row 1 and row 3 add the last lane of the row before them
+// (row_bcast:15) and rows 2-3 add lane 31 (row_bcast:31).  Masked-off rows add the 0 passed as the old value.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
+  return v;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));

@@ -77,8 +77,10 @@ struct AttnArgs {
   int n_splits, split_len;
   float* part_o;   // [B][Sq][n_splits][H][D]
   float* part_ml;  // [B][Sq][n_splits][H][2]
-  int hg_mode;     // 1: one workgroup per (16-head group, row, split) -- few rows (decode)
+  int hg_mode;     // 1: one workgroup per (16-head group, row, split); 2: one per (row, split) with the channels
+                   // split over the waves -- few rows (decode)
 };
+constexpr int kHgSplitMax = 2048;  // list positions per workgroup slice in the head-group kernel
 bool attn_uses_mfma(int H, int D, int q_format, int kv_format);
 hipError_t launch_attn(AttnArgs a, hipStream_t st);
 

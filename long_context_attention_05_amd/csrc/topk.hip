@@ -26,12 +26,7 @@ constexpr int kPerThread = 8;     // entries per thread in the ordered compactio
 // Exclusive scan over the block (1024 threads, one value each); `tot` receives the block total.
 __device__ __forceinline__ int block_excl_scan(int v, int* wsum, int& tot) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int n = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += n;
-  }
+  const int incl = wave_incl_scan(v);
   if (lane == 63) wsum[w] = incl;
   __syncthreads();
   int before = 0;
@@ -244,12 +239,7 @@ constexpr int kCandCap = 6144;                         // candidates staged in L
 // Exclusive scan over a 256-thread block.
 __device__ __forceinline__ int block256_excl_scan(int v, int* wsum, int& tot) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int n = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += n;
-  }
+  const int incl = wave_incl_scan(v);
   if (lane == 63) wsum[w] = incl;
   __syncthreads();
   int before = 0;

@@ -279,6 +279,14 @@ def test_attn_mfma(B, Sq, N, k, window, fmt):
     np.testing.assert_allclose(l, lr, rtol=1e-3, atol=1e-3)
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "mixed"])
+def test_hca_short_list_single_split(fmt):
+    # window 16 + 40 entries: one slice per row, the output finalized in the attention kernel itself
+    o, ref, l, lr = _attn_case(3, 1, 64, 512, 40, 0, 16, 128 * 40 + 7, fmt, 31, hca_m=128)
+    assert row_rel_err(o, ref) <= 1e-2
+    np.testing.assert_allclose(l, lr, rtol=1e-3, atol=1e-3)
+
+
 @pytest.mark.parametrize("fmt,H,D", [("bf16", 64, 512), ("mixed", 64, 512), ("f32", 4, 64)])
 def test_hca_dense(fmt, H, D):
     m, N = 128, 300
@@ -304,7 +312,10 @@ def test_attn_degenerate_sets(fmt, H, D):
 
 
 def test_attn_hca_equals_sparse_with_all_visible():
-    """Two GPU entry points, same arithmetic: hca_attn == sparse_mqa_attn with idx = all visible entries."""
+    """Two GPU entry points over the same list: hca_attn == sparse_mqa_attn with idx = all visible entries.
+
+    They take different kernels (all-heads wide kernel vs. 16-head groups) with different split plans, so the
+    probabilities are rounded to bf16 against different running maxima: agreement is to the bf16-path bound."""
     g = _rng(28)
     B, Sq, H, D, N, m, W = 2, 1, 64, 512, 200, 128, 128
     q_start = m * N + 5
@@ -324,7 +335,8 @@ def test_attn_hca_equals_sparse_with_all_visible():
     lca.sparse_mqa_attn(qd, lca.LCA_BF16, cg.desc(), N, rg.desc(), raw_start, W, idx, N, sink, B, Sq, H, D, W, 0.05,
                         q_start, o2, lca.LCA_F32, None, ws(n2), n2)
     torch.cuda.synchronize()
-    assert torch.equal(o1, o2)
+    a1, a2 = o1.cpu().numpy().astype(np.float64), o2.cpu().numpy().astype(np.float64)
+    assert row_rel_err(a1, a2) <= 1e-2
 
 
 def test_repeat_calls_bit_identical():
