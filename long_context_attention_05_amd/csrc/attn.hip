@@ -580,43 +580,44 @@ __global__ __launch_bounds__(256) void attn_hgw_kernel(AttnArgs a, int pairs) {
 // ------------------------------------------------------------------------------------------------
 // wide MFMA kernel (few query rows over many entries: dense HCA decode): H = 64, D = 512, bf16 or mixed entries
 // ------------------------------------------------------------------------------------------------
-// One workgroup per (query row, slice of its list) with all 64 heads; wave w owns channels [128 w, 128 w + 128) of
-// every entry, so each entry is read from memory once per workgroup and each wave streams only its quarter of it.
-// Per 32-entry tile:
-//   partial S^T (v_mfma_f32_16x16x32_bf16: A = the wave's channels of the tile, B = those channels of the 64
-//     heads' queries, both in registers) -> LDS; barrier;
-//   wave w sums the four partials for heads [16 w, 16 w + 16), runs their online softmax (lazy rescale as in the
+// One 512-thread workgroup per (query row, slice of its list) with all 64 heads; wave w owns channels
+// [64 w, 64 w + 64) of every entry (for the mixed cache, waves 0..6 hold the 448 fp8 channels and wave 7 the 64 RoPE
+// channels), so each entry is read from memory once per workgroup and each wave streams only its 128 bytes of it.
+// Two waves share each SIMD, so one wave's LDS and barrier latencies overlap the other's products.  Per 32-entry tile:
+//   partial S^T (v_mfma_f32_16x16x32_bf16: A = the wave's channels of the tile, B = those channels of the 64 heads'
+//     queries, both in registers; fp8 waves scale it by the entry's scale) -> LDS; barrier;
+//   wave w sums the eight partials of heads [8 w, 8 w + 8), runs their online softmax (lazy rescale as in the
 //     head-group kernel) and writes P (bf16, and P times the entry's fp8 scale) and the rescale factors to LDS;
 //     barrier;
 //   O^T += V^T P^T for the wave's channels and all heads (v_mfma_f32_16x16x32_bf16, K = the tile's 32 entries:
 //     A = V^T from two ds_read_b64_tr_b16 of the wave's own row-major tile in LDS, B = P^T from LDS).
 // The output of a wave's channels needs no cross-wave merge; the heads' (max, sum) come from their owners.
+constexpr int kWdWaves = 8;
+constexpr int kWdThreads = 64 * kWdWaves;
 constexpr int kWdTile = 32;                                 // entries per tile
-constexpr int kWdRowB = 272;                                // LDS bytes per tile row (a wave's 128 channels + pad)
-constexpr int kWdTileBytes = kWdTile * kWdRowB;             // 8704 per wave
+constexpr int kWdRowB = 144;                                // LDS bytes per tile row (a wave's 64 channels + pad)
+constexpr int kWdTileBytes = kWdTile * kWdRowB;             // 4608 per wave
 constexpr int kWdSpStride = 36;                             // floats per head row of a wave's partial logits
 constexpr int kWdPStride = 40;                              // bf16 per head row of P (32 entries + pad)
-constexpr size_t kWdSpOff = (size_t)4 * kWdTileBytes;
-constexpr size_t kWdPOff = kWdSpOff + (size_t)4 * 64 * kWdSpStride * 4;
+constexpr size_t kWdSpOff = (size_t)kWdWaves * kWdTileBytes;
+constexpr size_t kWdPOff = kWdSpOff + (size_t)kWdWaves * 64 * kWdSpStride * 4;
 constexpr size_t kWdAlphaOff = kWdPOff + (size_t)2 * 64 * kWdPStride * 2;
 constexpr size_t kWdTableOff = kWdAlphaOff + 64 * 4;
 constexpr size_t kWdMlOff = kWdTableOff + (size_t)kHgSplitMax * 4;
-constexpr size_t kWdQOff = kWdMlOff + 64 * 2 * 4;              // queries in operand layout, 16 KB per wave
-constexpr size_t kWdLds = kWdQOff + (size_t)4 * 16 * 64 * 16;
+constexpr size_t kWdLds = kWdMlOff + 64 * 2 * 4;
 static_assert(kWdLds <= 160 * 1024, "wide kernel LDS");
 
-// A wave's tile: for entry 16 eb + l % 16 and K-step s, channels 128 w + 32 s + 8 (l / 16) .. + 7.
+// A wave's tile: for entry 16 eb + l % 16 and K-step s, channels 64 w + 32 s + 8 (l / 16) .. + 7.
 template <int FMT>
 struct WdTile;
 template <>
 struct WdTile<LCA_BF16> {
-  uint4 v[2][4];
+  uint4 v[2][2];
   uint32_t valid;  // bit j: entry j of the tile is real
 };
 template <>
 struct WdTile<LCA_MIXED_FP8> {
-  uint2 f[2][4];   // fp8 codes of the step (channels < 448)
-  uint4 r[2][2];   // wave 3, steps 2..3: RoPE channels 448.. in bf16
+  uint4 c[2][2];   // waves 0..6: the 8 fp8 codes in .x, .y; wave 7: the 8 RoPE channels in bf16
   float scale[2];  // the fp8 scale of entry 16 eb + l % 16
   uint32_t valid;
 };
@@ -635,23 +636,26 @@ __device__ __forceinline__ void wd_load(WdTile<FMT>& T, const AttnArgs& a, const
     const long long rr = (long long)sl.b * src.cap + (row >= 0 ? row : 0);
     valid |= (uint32_t)(__ballot(lane < 16 && i0 + 16 * eb + hl < sl.npos && row >= 0) & 0xFFFFull) << (16 * eb);
     if constexpr (FMT == LCA_BF16) {
-      const unsigned long long base = (unsigned long long)((const uint8_t*)src.data + rr * 1024) + 256 * wave + 16 * grp;
+      const unsigned long long base = (unsigned long long)((const uint8_t*)src.data + rr * 1024) + 128 * wave + 16 * grp;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
+      for (int s = 0; s < 2; ++s) {
         const u32x4_t x = *(gbl_u32x4_t*)(base + 64 * s);
         T.v[eb][s] = make_uint4(x.x, x.y, x.z, x.w);
       }
     } else {
-      const unsigned long long fb = (unsigned long long)((const uint8_t*)src.data + rr * 448) + 128 * wave + 8 * grp;
+      if (wave == 7) {
+        const unsigned long long rb = (unsigned long long)((const uint8_t*)src.rope + rr * 128) + 16 * grp;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        if (wave == 3 && s >= 2) {
-          const u32x4_t x = *(gbl_u32x4_t*)((unsigned long long)((const uint8_t*)src.rope + rr * 128) + 16 * grp +
-                                            64 * (s - 2));
-          T.r[eb][s - 2] = make_uint4(x.x, x.y, x.z, x.w);
-        } else {
+        for (int s = 0; s < 2; ++s) {
+          const u32x4_t x = *(gbl_u32x4_t*)(rb + 64 * s);
+          T.c[eb][s] = make_uint4(x.x, x.y, x.z, x.w);
+        }
+      } else {
+        const unsigned long long fb = (unsigned long long)((const uint8_t*)src.data + rr * 448) + 64 * wave + 8 * grp;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
           const u32x2_t x = *(gbl_u32x2_t*)(fb + 32 * s);
-          T.f[eb][s] = make_uint2(x.x, x.y);
+          T.c[eb][s] = make_uint4(x.x, x.y, 0u, 0u);
         }
       }
       T.scale[eb] = ((const float*)src.scale)[rr];
@@ -665,14 +669,19 @@ __device__ __forceinline__ uint4 wd_chunk(const WdTile<FMT>& T, int eb, int s, i
   if constexpr (FMT == LCA_BF16) {
     return T.v[eb][s];
   } else {
-    if (wave == 3 && s >= 2) return T.r[eb][s - 2];
-    const uint2 lo = fp8x4_to_bf16x4(T.f[eb][s].x), hi = fp8x4_to_bf16x4(T.f[eb][s].y);
+    if (wave == 7) return T.c[eb][s];
+    const uint2 lo = fp8x4_to_bf16x4(T.c[eb][s].x), hi = fp8x4_to_bf16x4(T.c[eb][s].y);
     return make_uint4(lo.x, lo.y, hi.x, hi.y);
   }
 }
 
+// Exchange with the lane 8 apart inside each 16-lane row (row_ror:8).
+__device__ __forceinline__ float xor8_get(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false));
+}
+
 template <int FMT>
-__global__ __launch_bounds__(256) void attn_wide_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kWdThreads) void attn_wide_kernel(AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t wd_lds[];
   const int item = blockIdx.x;
   const int S = a.n_splits;
@@ -688,15 +697,16 @@ __global__ __launch_bounds__(256) void attn_wide_kernel(AttnArgs a) {
   sl.nw = L.nw;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int hl = lane & 15, grp = lane >> 4;
+  const int oh = 8 * wave + (lane & 7), oq = lane >> 3;  // softmax owner lane: head oh, entries 4 oq .. 4 oq + 3
   uint8_t* tbuf = wd_lds + wave * kWdTileBytes;
-  float* sp = (float*)(wd_lds + kWdSpOff);             // [4 waves][64 heads][kWdSpStride]
+  float* sp = (float*)(wd_lds + kWdSpOff);             // [8 waves][64 heads][kWdSpStride]
   uint16_t* P_s = (uint16_t*)(wd_lds + kWdPOff);       // [64 heads][kWdPStride]
   uint16_t* Pe_s = P_s + 64 * kWdPStride;              // P times the entry scale (fp8 channels)
   float* alpha_s = (float*)(wd_lds + kWdAlphaOff);     // [64]
   int* rows_s = (int*)(wd_lds + kWdTableOff);
   float* ml_s = (float*)(wd_lds + kWdMlOff);           // [64][2]
-  uint4* q_s = (uint4*)(wd_lds + kWdQOff) + wave * 16 * 64;  // [s][hb][lane] B operands of this wave's channels
   constexpr bool kMixed = FMT == LCA_MIXED_FP8;
+  const bool fp8_wave = kMixed && wave < 7;
 
   for (int i = threadIdx.x; i < sl.npos; i += blockDim.x) {
     const int p = sl.p_begin + i;
@@ -711,55 +721,32 @@ __global__ __launch_bounds__(256) void attn_wide_kernel(AttnArgs a) {
     }
     rows_s[i] = row;
   }
-  // queries (B operand of the partial S^T: lane holds head 16 hb + hl, channels 128 wave + 32 s + 8 grp .. + 7),
-  // kept in LDS in operand order so that the registers go to tiles in flight
+  // queries (B operand of the partial S^T): lane holds head 16 hb + hl, channels 64 wave + 32 s + 8 grp .. + 7
+  bf16x8_t qv[2][4];
 #pragma unroll
   for (int hb = 0; hb < 4; ++hb) {
-    const uint8_t* qp = (const uint8_t*)a.q + ((long long)qrow * 64 + 16 * hb + hl) * 1024 + 256 * wave + 16 * grp;
+    const uint8_t* qp = (const uint8_t*)a.q + ((long long)qrow * 64 + 16 * hb + hl) * 1024 + 128 * wave + 16 * grp;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) q_s[(4 * s + hb) * 64 + lane] = *(const uint4*)(qp + 64 * s);
+    for (int s = 0; s < 2; ++s) qv[s][hb] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(qp + 64 * s));
   }
   __syncthreads();
 
-  f32x4_t acc_o[8][4];  // [channel tile mb][head block hb]: channel 128 wave + 16 mb + 4 grp + x, head 16 hb + hl
+  f32x4_t acc_o[4][4];  // [channel tile mb][head block hb]: channel 64 wave + 16 mb + 4 grp + x, head 16 hb + hl
 #pragma unroll
-  for (int mb = 0; mb < 8; ++mb)
+  for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb) acc_o[mb][hb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  float m_run = -INFINITY, l_run = 0.0f;  // of head 16 wave + hl (this wave owns its softmax)
-  // fp8 channels of this wave's tile rows mb: all for waves 0..2, mb < 4 for wave 3 (channels 384..447)
-  const int scaled_mb = (kMixed && wave == 3) ? 4 : 8;
+  float m_run = -INFINITY, l_run = 0.0f;  // of head oh (owned by this wave)
 
   auto step = [&](WdTile<FMT>& T, int next_i0) {
-    // partial S^T of the tile over this wave's channels; the tile goes to LDS (bf16) for the V^T reads.  fp8
-    // channels are scaled by the entry's scale before the RoPE channels (wave 3, steps 2..3) add in.
-    float esc[2][4];  // the scales of the accumulator's entries 16 eb + 4 grp + x (lane 4 grp + x loaded them)
-#pragma unroll
-    for (int eb = 0; eb < 2; ++eb)
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        if constexpr (kMixed) esc[eb][x] = __shfl(T.scale[eb], 4 * grp + x, 64);
-        else esc[eb][x] = 1.0f;
-      }
-    auto scale_partial = [&](f32x4_t (&acc)[2][4]) {
-#pragma unroll
-      for (int eb = 0; eb < 2; ++eb)
-#pragma unroll
-        for (int hb = 0; hb < 4; ++hb)
-#pragma unroll
-          for (int x = 0; x < 4; ++x) acc[eb][hb][x] = esc[eb][x] * acc[eb][hb][x];
-    };
+    // partial S^T of the tile over this wave's channels; the tile goes to LDS (bf16) for the V^T reads
     f32x4_t sacc[2][4];
 #pragma unroll
     for (int eb = 0; eb < 2; ++eb)
 #pragma unroll
       for (int hb = 0; hb < 4; ++hb) sacc[eb][hb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      if (kMixed && wave == 3 && s == 2) scale_partial(sacc);
-      bf16x8_t qv[4];
-#pragma unroll
-      for (int hb = 0; hb < 4; ++hb) qv[hb] = __builtin_bit_cast(bf16x8_t, q_s[(4 * s + hb) * 64 + lane]);
+    for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int eb = 0; eb < 2; ++eb) {
         const uint4 c = wd_chunk<FMT>(T, eb, s, wave);
@@ -767,61 +754,71 @@ __global__ __launch_bounds__(256) void attn_wide_kernel(AttnArgs a) {
         const bf16x8_t kv = __builtin_bit_cast(bf16x8_t, c);
 #pragma unroll
         for (int hb = 0; hb < 4; ++hb)
-          sacc[eb][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qv[hb], sacc[eb][hb], 0, 0, 0);
+          sacc[eb][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qv[s][hb], sacc[eb][hb], 0, 0, 0);
       }
+    if (fp8_wave) {  // the entry scales of the accumulator's entries 16 eb + 4 grp + x (lane 4 grp + x loaded them)
+#pragma unroll
+      for (int eb = 0; eb < 2; ++eb)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          float sc = 1.0f;
+          if constexpr (kMixed) sc = __shfl(T.scale[eb], 4 * grp + x, 64);
+#pragma unroll
+          for (int hb = 0; hb < 4; ++hb) sacc[eb][hb][x] = sc * sacc[eb][hb][x];
+        }
     }
-    if (kMixed && wave != 3) scale_partial(sacc);
-    const uint32_t valid = T.valid;
 #pragma unroll
     for (int eb = 0; eb < 2; ++eb)
 #pragma unroll
       for (int hb = 0; hb < 4; ++hb)
         *(f32x4_t*)(sp + (wave * 64 + 16 * hb + hl) * kWdSpStride + 16 * eb + 4 * grp) = sacc[eb][hb];
+    // the owner lanes' entry scales (entries 4 oq + x: lane (4 oq + x) % 16 of block (4 oq + x) / 16 loaded them)
+    float esc[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+    if constexpr (kMixed) {
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int e = 4 * oq + x;
+        const float s0 = __shfl(T.scale[0], e & 15, 64), s1 = __shfl(T.scale[1], e & 15, 64);
+        esc[x] = e < 16 ? s0 : s1;
+      }
+    }
+    const uint32_t valid = T.valid;
     wd_load<FMT>(T, a, sl, rows_s, next_i0, wave, lane);  // the tile's registers are free: the next tile is in flight
     __syncthreads();
 
-    // softmax of heads 16 wave + hl over the tile's entries 16 eb + 4 grp + x
-    float lg[2][4];
+    // softmax of head oh over the tile's entries 4 oq + x
+    f32x4_t s4 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int eb = 0; eb < 2; ++eb) {
-      f32x4_t s4 = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int w = 0; w < kWdWaves; ++w) s4 += *(const f32x4_t*)(sp + (w * 64 + oh) * kWdSpStride + 4 * oq);
+    float lg[4];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) s4 += *(const f32x4_t*)(sp + (w * 64 + 16 * wave + hl) * kWdSpStride + 16 * eb + 4 * grp);
-#pragma unroll
-      for (int x = 0; x < 4; ++x) lg[eb][x] = ((valid >> (16 * eb + 4 * grp + x)) & 1u) ? a.scale * s4[x] : -INFINITY;
-    }
-    float mt = -INFINITY;
-#pragma unroll
-    for (int eb = 0; eb < 2; ++eb)
-#pragma unroll
-      for (int x = 0; x < 4; ++x) mt = fmaxf(mt, lg[eb][x]);
+    for (int x = 0; x < 4; ++x) lg[x] = ((valid >> (4 * oq + x)) & 1u) ? a.scale * s4[x] : -INFINITY;
+    float mt = fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3]));
+    mt = fmaxf(mt, xor8_get(mt));
     mt = xor32_max(xor16_max(mt));
     const float m_new = (mt > m_run + kRescaleSlack) ? mt : m_run;
     const float alpha = (m_new == m_run) ? 1.0f : __expf(m_run - m_new);
-    float psum = 0.0f;
+    float p[4], psum = 0.0f;
 #pragma unroll
-    for (int eb = 0; eb < 2; ++eb) {
-      float p[4];
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        p[x] = (lg[eb][x] == -INFINITY) ? 0.0f : __expf(lg[eb][x] - m_new);
-        psum += p[x];
-      }
-      uint2 pw;
-      pw.x = (uint32_t)f32_to_bf16(p[0]) | ((uint32_t)f32_to_bf16(p[1]) << 16);
-      pw.y = (uint32_t)f32_to_bf16(p[2]) | ((uint32_t)f32_to_bf16(p[3]) << 16);
-      *(uint2*)(P_s + (16 * wave + hl) * kWdPStride + 16 * eb + 4 * grp) = pw;
-      if constexpr (kMixed) {
-        uint2 pe;
-        pe.x = (uint32_t)f32_to_bf16(p[0] * esc[eb][0]) | ((uint32_t)f32_to_bf16(p[1] * esc[eb][1]) << 16);
-        pe.y = (uint32_t)f32_to_bf16(p[2] * esc[eb][2]) | ((uint32_t)f32_to_bf16(p[3] * esc[eb][3]) << 16);
-        *(uint2*)(Pe_s + (16 * wave + hl) * kWdPStride + 16 * eb + 4 * grp) = pe;
-      }
+    for (int x = 0; x < 4; ++x) {
+      p[x] = (lg[x] == -INFINITY) ? 0.0f : __expf(lg[x] - m_new);
+      psum += p[x];
     }
+    uint2 pw;
+    pw.x = (uint32_t)f32_to_bf16(p[0]) | ((uint32_t)f32_to_bf16(p[1]) << 16);
+    pw.y = (uint32_t)f32_to_bf16(p[2]) | ((uint32_t)f32_to_bf16(p[3]) << 16);
+    *(uint2*)(P_s + oh * kWdPStride + 4 * oq) = pw;
+    if constexpr (kMixed) {
+      uint2 pe;
+      pe.x = (uint32_t)f32_to_bf16(p[0] * esc[0]) | ((uint32_t)f32_to_bf16(p[1] * esc[1]) << 16);
+      pe.y = (uint32_t)f32_to_bf16(p[2] * esc[2]) | ((uint32_t)f32_to_bf16(p[3] * esc[3]) << 16);
+      *(uint2*)(Pe_s + oh * kWdPStride + 4 * oq) = pe;
+    }
+    psum += xor8_get(psum);
     psum = xor32_sum(xor16_sum(psum));
     l_run = l_run * alpha + psum;
     m_run = m_new;
-    if (grp == 0) alpha_s[16 * wave + hl] = alpha;
+    if (lane < 8) alpha_s[oh] = alpha;
     __syncthreads();
 
     // O^T += V^T P^T over this wave's channels, all 64 heads
@@ -834,23 +831,18 @@ __global__ __launch_bounds__(256) void attn_wide_kernel(AttnArgs a) {
     }
     if (__ballot(any)) {
 #pragma unroll
-      for (int mb = 0; mb < 8; ++mb)
+      for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
         for (int hb = 0; hb < 4; ++hb) acc_o[mb][hb] *= al[hb];
     }
-    // P^T operands: P times the entry scale for the fp8 channel tiles, plain P for the RoPE ones (wave 3, mb >= 4)
+    const uint16_t* Pw = fp8_wave ? Pe_s : P_s;  // the fp8 channels carry the entry scale
     bf16x8_t bp[4];
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb)
-      bp[hb] = __builtin_bit_cast(bf16x8_t, *(const uint4*)((kMixed ? Pe_s : P_s) + (16 * hb + hl) * kWdPStride + 8 * grp));
+      bp[hb] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(Pw + (16 * hb + hl) * kWdPStride + 8 * grp));
     const uint8_t* vrow = tbuf + (8 * grp + (hl >> 2)) * kWdRowB + 8 * (hl & 3);
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb) {
-      if (kMixed && mb == scaled_mb) {
-#pragma unroll
-        for (int hb = 0; hb < 4; ++hb)
-          bp[hb] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(P_s + (16 * hb + hl) * kWdPStride + 8 * grp));
-      }
+    for (int mb = 0; mb < 4; ++mb) {
       const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vrow + 32 * mb));
       const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vrow + 4 * kWdRowB + 32 * mb));
       const bf16x8_t av = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -862,21 +854,17 @@ __global__ __launch_bounds__(256) void attn_wide_kernel(AttnArgs a) {
 
   const int ntiles = (sl.npos + kWdTile - 1) / kWdTile;
   if (ntiles > 0) {  // uniform over the workgroup: every wave takes every tile (its own channels)
-    // two tiles in turn: one is in flight while the other is scored
-    WdTile<FMT> TA, TB;
-    wd_load<FMT>(TA, a, sl, rows_s, 0, wave, lane);
-    wd_load<FMT>(TB, a, sl, rows_s, kWdTile, wave, lane);
-    for (int tt = 0; tt < ntiles; tt += 2) {
-      step(TA, kWdTile * (tt + 2));
-      if (tt + 1 >= ntiles) break;
-      step(TB, kWdTile * (tt + 3));
-    }
+    // one tile buffer: the next tile loads as soon as a tile's S^T products are issued (a second buffer costs
+    // more registers than two waves per SIMD leave, and a spill reload would drain the loads in flight)
+    WdTile<FMT> T;
+    wd_load<FMT>(T, a, sl, rows_s, 0, wave, lane);
+    for (int tt = 0; tt < ntiles; ++tt) step(T, kWdTile * (tt + 1));
   }
 
   // every head's (max, sum) from its owner
-  if (grp == 0) {
-    ml_s[(16 * wave + hl) * 2 + 0] = m_run;
-    ml_s[(16 * wave + hl) * 2 + 1] = l_run;
+  if (lane < 8) {
+    ml_s[oh * 2 + 0] = m_run;
+    ml_s[oh * 2 + 1] = l_run;
   }
   __syncthreads();
 #pragma unroll
@@ -891,9 +879,9 @@ __global__ __launch_bounds__(256) void attn_wide_kernel(AttnArgs a) {
         den = ((z == -INFINITY) ? 0.0f : __expf(z - Mz)) + ((M == -INFINITY) ? 0.0f : Ls * __expf(M - Mz));
         f = (M == -INFINITY) ? 0.0f : __expf(M - Mz) / den;
       }
-      const long long obase = ((long long)qrow * 64 + head) * 512 + 128 * wave + 4 * grp;
+      const long long obase = ((long long)qrow * 64 + head) * 512 + 64 * wave + 4 * grp;
 #pragma unroll
-      for (int mb = 0; mb < 8; ++mb) {
+      for (int mb = 0; mb < 4; ++mb) {
         const f32x4_t o = acc_o[mb][hb];
         if (a.out_format == LCA_F32) {
           *(float4*)((float*)a.out + obase + 16 * mb) = make_float4(o[0] * f, o[1] * f, o[2] * f, o[3] * f);
@@ -904,13 +892,13 @@ __global__ __launch_bounds__(256) void attn_wide_kernel(AttnArgs a) {
           *(uint2*)((uint16_t*)a.out + obase + 16 * mb) = w2;
         }
       }
-      if (a.lse && wave == hb && grp == 0)
+      if (a.lse && wave == 2 * hb + (hl >> 3) && grp == 0)
         a.lse[(long long)qrow * 64 + head] = (Mz == -INFINITY) ? -INFINITY : Mz + __logf(den);
     } else {
-      float* po = a.part_o + ((long long)item * 64 + head) * 512 + 128 * wave + 4 * grp;
+      float* po = a.part_o + ((long long)item * 64 + head) * 512 + 64 * wave + 4 * grp;
 #pragma unroll
-      for (int mb = 0; mb < 8; ++mb) *(f32x4_t*)(po + 16 * mb) = acc_o[mb][hb];
-      if (wave == hb && grp == 0) {
+      for (int mb = 0; mb < 4; ++mb) *(f32x4_t*)(po + 16 * mb) = acc_o[mb][hb];
+      if (wave == 2 * hb + (hl >> 3) && grp == 0) {
         a.part_ml[((long long)item * 64 + head) * 2 + 0] = M;
         a.part_ml[((long long)item * 64 + head) * 2 + 1] = Ls;
       }
@@ -1081,6 +1069,33 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
   __syncthreads();
   const float inv = stat[0];
   const long long ob = (((long long)b * a.Sq + r) * H + h) * D;
+  if ((D & 3) == 0) {
+    // four channels per thread, eight splits' loads in flight at a time
+    const float* po = a.part_o + (item0 * H + h) * D;
+    const long long sstride = (long long)H * D;
+    for (int c = 4 * threadIdx.x; c < D; c += 4 * blockDim.x) {
+      f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      int s0 = 0;
+      for (; s0 + 8 <= S; s0 += 8) {
+        f32x4_t v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = *(const f32x4_t*)(po + (s0 + u) * sstride + c);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc += wsplit[s0 + u] * v[u];
+      }
+      for (; s0 < S; ++s0) acc += wsplit[s0] * *(const f32x4_t*)(po + s0 * sstride + c);
+      acc *= inv;
+      if (a.out_format == LCA_F32) {
+        *(f32x4_t*)((float*)a.out + ob + c) = acc;
+      } else {
+        uint2 w2;
+        w2.x = (uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
+        w2.y = (uint32_t)f32_to_bf16(acc[2]) | ((uint32_t)f32_to_bf16(acc[3]) << 16);
+        *(uint2*)((uint16_t*)a.out + ob + c) = w2;
+      }
+    }
+    return;
+  }
   for (int x = threadIdx.x; x < D; x += blockDim.x) {
     float acc = 0.0f;
     for (int s = 0; s < S; ++s) acc = fmaf(wsplit[s], a.part_o[((item0 + s) * H + h) * D + x], acc);
@@ -1119,9 +1134,9 @@ hipError_t launch_attn(AttnArgs a, hipStream_t st) {
     }
     const dim3 wgrid((unsigned)(a.B * a.Sq * a.n_splits));
     if (a.comp.format == LCA_BF16)
-      hipLaunchKernelGGL(attn_wide_kernel<LCA_BF16>, wgrid, dim3(256), kWdLds, st, a);
+      hipLaunchKernelGGL(attn_wide_kernel<LCA_BF16>, wgrid, dim3(kWdThreads), kWdLds, st, a);
     else
-      hipLaunchKernelGGL(attn_wide_kernel<LCA_MIXED_FP8>, wgrid, dim3(256), kWdLds, st, a);
+      hipLaunchKernelGGL(attn_wide_kernel<LCA_MIXED_FP8>, wgrid, dim3(kWdThreads), kWdLds, st, a);
   } else if (mfma && a.hg_mode == 1) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) dev = 0;
