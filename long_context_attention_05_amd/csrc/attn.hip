@@ -80,7 +80,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_mfma_kernel(AttnArgs a) {
   float* scale_s = (float*)(vt + 512 * kTStride);    // [kTE]
   int* valid_s = (int*)(scale_s + kTE);              // [kTE]
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int hl = lane & 15, grp = lane >> 4;  // head within the wave's 16, lane group
   const int split = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
   const long long t = a.q_start + r;
@@ -273,16 +273,19 @@ __global__ __launch_bounds__(kAttnThreads) void attn_mfma_kernel(AttnArgs a) {
 // the end; the four head groups of a (row, slice) pair get workgroup ids congruent mod 8 so that they run on one
 // XCD and share its L2 copy of the gathered entries.
 constexpr int kHgRow = 520;                // bf16 per LDS tile row (1040 bytes)
-constexpr int kHgOStride = 516;            // floats per head row in the merge buffer
 constexpr int kWTile = 16;                 // entries per wave tile
 constexpr float kRescaleSlack = 8.0f;
 constexpr int kWBufBytes = kWTile * kHgRow * 2;  // 16640
-// four wave tiles (the merge's 2 x 16 x kHgOStride floats reuse them), the row table, the waves' (max, sum) and
+// four wave tiles, the row table (the merge buffer reuses both), the waves' (max, sum) and
 // the entry scales
 constexpr size_t kHgTableOff = (size_t)4 * kWBufBytes;
-constexpr size_t kHgMlOff = kHgTableOff + (size_t)kHgSplitMax * 4;
+// the merge: every wave leaves its 32 channel tiles, [wave][32][64 lanes] x 16 bytes, over the (then dead) tiles and
+// row table
+constexpr size_t kHgMergeBytes = (size_t)4 * 32 * 64 * 16;
+constexpr size_t kHgMlOff = kHgMergeBytes > kHgTableOff + (size_t)kHgSplitMax * 4
+                                ? kHgMergeBytes
+                                : kHgTableOff + (size_t)kHgSplitMax * 4;
 constexpr size_t kHgwLds = kHgMlOff + 4 * 16 * 2 * 4 + 4 * 16 * 4;
-static_assert((size_t)2 * 16 * kHgOStride * 4 <= (size_t)4 * kWBufBytes, "merge buffer fits the tiles");
 
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
@@ -387,7 +390,7 @@ __global__ __launch_bounds__(256) void attn_hgw_kernel(AttnArgs a, int pairs) {
   sl.p_begin = split * a.split_len;
   sl.npos = max(min(a.split_len, total - sl.p_begin), 0);
   sl.nw = L.nw;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int hl = lane & 15, grp = lane >> 4;
   const int head = 16 * hg + hl;
   uint8_t* wbuf = hgw_lds + wave * kWBufBytes;
@@ -447,7 +450,9 @@ __global__ __launch_bounds__(256) void attn_hgw_kernel(AttnArgs a, int pairs) {
       for (int x = 0; x < 4; ++x) esc[x] = esc_w[4 * grp + x];
     }
     const uint64_t valid = T.valid;
-    hg_load<FMT>(T, a, sl, rows_s, next_i0, lane);  // the tile's registers are free: the next tile is in flight
+    // the tile's registers are free: the wave's next tile goes in flight (none past the slice: a load nobody uses
+    // would still hold up whatever later reuses its registers)
+    if (next_i0 < sl.npos) hg_load<FMT>(T, a, sl, rows_s, next_i0, lane);
     float lg[4];
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
@@ -502,45 +507,36 @@ __global__ __launch_bounds__(256) void attn_hgw_kernel(AttnArgs a, int pairs) {
     for (int tt = wave; tt < ntiles; tt += 4) process(T, kWTile * (tt + 4));
   }
 
-  // merge the four waves (same heads, different entries)
-  __syncthreads();
+  // merge the four waves (same heads, different entries): wave w finalizes channel tiles [8 w, 8 w + 8)
+  __syncthreads();  // every wave is done with its tile: the LDS is reused
   if (grp == 0) {
     ml_s[(wave * 16 + hl) * 2 + 0] = m_run;
     ml_s[(wave * 16 + hl) * 2 + 1] = l_run;
   }
-  __syncthreads();
-  float M = -INFINITY;
+  f32x4_t* mg = (f32x4_t*)hgw_lds;  // [wave][32 channel tiles][64 lanes]
 #pragma unroll
-  for (int w = 0; w < 4; ++w) M = fmaxf(M, ml_s[(w * 16 + hl) * 2 + 0]);
-  float Lsum = 0.0f;
+  for (int dt = 0; dt < 32; ++dt) mg[(wave * 32 + dt) * 64 + lane] = acc_o[dt];
+  __syncthreads();
+  float mw[4], M = -INFINITY;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    const float mw = ml_s[(w * 16 + hl) * 2 + 0];
-    Lsum += (mw == -INFINITY) ? 0.0f : ml_s[(w * 16 + hl) * 2 + 1] * __expf(mw - M);
+    mw[w] = ml_s[(w * 16 + hl) * 2 + 0];
+    M = fmaxf(M, mw[w]);
   }
-  const float own = (m_run == -INFINITY) ? 0.0f : __expf(m_run - M);
+  float Lsum = 0.0f, fw[4];
 #pragma unroll
-  for (int dt = 0; dt < 32; ++dt) acc_o[dt] *= own;
-  float* ob = (float*)hgw_lds;  // [2][16][kHgOStride]
-  if (wave >= 2) {
-#pragma unroll
-    for (int dt = 0; dt < 32; ++dt)
-      *(f32x4_t*)(ob + ((wave - 2) * 16 + hl) * kHgOStride + 16 * dt + 4 * grp) = acc_o[dt];
+  for (int w = 0; w < 4; ++w) {
+    fw[w] = (mw[w] == -INFINITY) ? 0.0f : __expf(mw[w] - M);
+    Lsum += fw[w] * ml_s[(w * 16 + hl) * 2 + 1];
   }
-  __syncthreads();
-  if (wave < 2) {
+  f32x4_t res[8];
 #pragma unroll
-    for (int dt = 0; dt < 32; ++dt) acc_o[dt] += *(const f32x4_t*)(ob + (wave * 16 + hl) * kHgOStride + 16 * dt + 4 * grp);
+  for (int k = 0; k < 8; ++k) {
+    f32x4_t acc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) acc += fw[w] * mg[(w * 32 + 8 * wave + k) * 64 + lane];
+    res[k] = acc;
   }
-  __syncthreads();
-  if (wave == 1) {
-#pragma unroll
-    for (int dt = 0; dt < 32; ++dt) *(f32x4_t*)(ob + hl * kHgOStride + 16 * dt + 4 * grp) = acc_o[dt];
-  }
-  __syncthreads();
-  if (wave != 0) return;
-#pragma unroll
-  for (int dt = 0; dt < 32; ++dt) acc_o[dt] += *(const f32x4_t*)(ob + hl * kHgOStride + 16 * dt + 4 * grp);
 
   if (S == 1) {
     const float z = a.sink[head];
@@ -552,25 +548,25 @@ __global__ __launch_bounds__(256) void attn_hgw_kernel(AttnArgs a, int pairs) {
     }
     const long long obase = ((long long)qrow * 64 + head) * 512;
 #pragma unroll
-    for (int dt = 0; dt < 32; ++dt) {
-      const int c0 = 16 * dt + 4 * grp;
+    for (int k = 0; k < 8; ++k) {
+      const int c0 = 16 * (8 * wave + k) + 4 * grp;
       if (a.out_format == LCA_F32) {
         *(float4*)((float*)a.out + obase + c0) =
-            make_float4(acc_o[dt][0] * f, acc_o[dt][1] * f, acc_o[dt][2] * f, acc_o[dt][3] * f);
+            make_float4(res[k][0] * f, res[k][1] * f, res[k][2] * f, res[k][3] * f);
       } else {
         uint2 w2;
-        w2.x = (uint32_t)f32_to_bf16(acc_o[dt][0] * f) | ((uint32_t)f32_to_bf16(acc_o[dt][1] * f) << 16);
-        w2.y = (uint32_t)f32_to_bf16(acc_o[dt][2] * f) | ((uint32_t)f32_to_bf16(acc_o[dt][3] * f) << 16);
+        w2.x = (uint32_t)f32_to_bf16(res[k][0] * f) | ((uint32_t)f32_to_bf16(res[k][1] * f) << 16);
+        w2.y = (uint32_t)f32_to_bf16(res[k][2] * f) | ((uint32_t)f32_to_bf16(res[k][3] * f) << 16);
         *(uint2*)((uint16_t*)a.out + obase + c0) = w2;
       }
     }
-    if (a.lse && grp == 0) a.lse[(long long)qrow * 64 + head] = (Mz == -INFINITY) ? -INFINITY : Mz + __logf(den);
+    if (a.lse && wave == 0 && grp == 0) a.lse[(long long)qrow * 64 + head] = (Mz == -INFINITY) ? -INFINITY : Mz + __logf(den);
   } else {
     const long long item = (long long)qrow * S + split;
     float* po = a.part_o + (item * 64 + head) * 512;
 #pragma unroll
-    for (int dt = 0; dt < 32; ++dt) *(f32x4_t*)(po + 16 * dt + 4 * grp) = acc_o[dt];
-    if (grp == 0) {
+    for (int k = 0; k < 8; ++k) *(f32x4_t*)(po + 16 * (8 * wave + k) + 4 * grp) = res[k];
+    if (wave == 0 && grp == 0) {
       a.part_ml[(item * 64 + head) * 2 + 0] = M;
       a.part_ml[(item * 64 + head) * 2 + 1] = Lsum;
     }
@@ -695,7 +691,7 @@ __global__ __launch_bounds__(kWdThreads) void attn_wide_kernel(AttnArgs a) {
   sl.p_begin = split * a.split_len;
   sl.npos = max(min(a.split_len, total - sl.p_begin), 0);
   sl.nw = L.nw;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int hl = lane & 15, grp = lane >> 4;
   const int oh = 8 * wave + (lane & 7), oq = lane >> 3;  // softmax owner lane: head oh, entries 4 oq .. 4 oq + 3
   uint8_t* tbuf = wd_lds + wave * kWdTileBytes;
@@ -783,7 +779,7 @@ __global__ __launch_bounds__(kWdThreads) void attn_wide_kernel(AttnArgs a) {
       }
     }
     const uint32_t valid = T.valid;
-    wd_load<FMT>(T, a, sl, rows_s, next_i0, wave, lane);  // the tile's registers are free: the next tile is in flight
+    if (next_i0 < sl.npos) wd_load<FMT>(T, a, sl, rows_s, next_i0, wave, lane);  // the next tile goes in flight
     __syncthreads();
 
     // softmax of head oh over the tile's entries 4 oq + x

@@ -148,15 +148,19 @@ __global__ __launch_bounds__(kRowThreads) void compress_kernel(CompressArgs a, R
   }
   const long long base = (long long)b * a.n;
   // stream a: block i's own tokens; stream b: block i-1's tokens (absent for the first block of the sequence).
-  // Candidates are taken four at a time with all their loads issued before the softmax updates.
+  // Candidates are taken eight at a time with all their loads issued before the softmax updates (a decode append
+  // has at most 2m = 8 of them: one round of loads); loads past the last candidate or channel repeat a valid
+  // address and are masked, so no branch separates them.
   const long long pa0 = (long long)m * i;
   const int na = (int)((a.n - pa0) < m ? (a.n - pa0) : m);
   const int nbk = (a.overlap && gblock >= 1) ? m : 0;
-  for (int r0 = 0; r0 < na + nbk; r0 += 4) {
-    float zl[4][CPT], cv[4][CPT];
+  const int ncand = na + nbk;
+  constexpr int kBatch = 8;
+  for (int r0 = 0; r0 < ncand; r0 += kBatch) {
+    float zl[kBatch][CPT], cv[kBatch][CPT];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int rr = r0 + q;
+    for (int q = 0; q < kBatch; ++q) {
+      const int rr = min(r0 + q, ncand - 1);
       const bool from_a = rr < na;
       const int r = from_a ? rr : rr - na;
       const float *zr, *cr, *br;
@@ -173,18 +177,16 @@ __global__ __launch_bounds__(kRowThreads) void compress_kernel(CompressArgs a, R
         cr = a.tCb + ((long long)b * m + r) * c;
         br = a.Bb + (long long)r * c;
       }
-      const bool ok = rr < na + nbk;
 #pragma unroll
       for (int u = 0; u < CPT; ++u) {
-        const int j = threadIdx.x + blockDim.x * u;
-        const bool v = ok && j < c;
-        zl[q][u] = v ? zr[j] + br[j] : 0.0f;
-        cv[q][u] = v ? cr[j] : 0.0f;
+        const int j = min((int)threadIdx.x + (int)blockDim.x * u, c - 1);
+        zl[q][u] = zr[j] + br[j];
+        cv[q][u] = cr[j];
       }
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (r0 + q < na + nbk) {
+    for (int q = 0; q < kBatch; ++q) {
+      if (r0 + q < ncand) {
 #pragma unroll
         for (int u = 0; u < CPT; ++u) softmax_acc(zl[q][u], cv[q][u], mx[u], den[u], num[u]);
       }

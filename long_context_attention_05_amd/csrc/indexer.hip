@@ -126,7 +126,7 @@ __global__ __launch_bounds__(256) void idx_score_mfma(IdxArgs a, int qpb) {
 #pragma clang fp contract(off)
   __shared__ uint16_t q_s[64 * kQStride];
   __shared__ float w_s[64];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int g = lane >> 5, col = lane & 31;
   const int b = blockIdx.z;
   const int e0 = blockIdx.x * kMfmaEntriesPerBlock + wave * kMfmaEntriesPerWave;
@@ -313,7 +313,7 @@ __global__ __launch_bounds__(256, 2) void idx_score_decode_bf16(IdxArgs a) {
 #pragma clang fp contract(off)
   __shared__ int hist_s[kSelBins];
   constexpr int KPW = 16 * kBfGroups;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int g = lane >> 4, col = lane & 15;
   const int b = blockIdx.y;
   const int nvis = nvis_of(a.q_start, a.m, a.N);
@@ -409,7 +409,7 @@ __global__ __launch_bounds__(256, 2) void idx_score_decode_fp4(IdxArgs a) {
 #pragma clang fp contract(off)
   __shared__ int hist_s[kSelBins];
   constexpr int KPW = 16 * kF4Groups;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int g = lane >> 4, col = lane & 15;
   const int b = blockIdx.y;
   const int nvis = nvis_of(a.q_start, a.m, a.N);
