@@ -196,9 +196,10 @@ def main():
         del src_t, dst_t
 
     ev = HipEvents()
-    has_scores = w.HI > 0
+    has_scores = w.HI > 0   # CSA: the indexer scoring kernel dominates; HCA: the attention kernel
     K = args.steps
-    pairs = [(ev.create(), ev.create()) for _ in range(K)] if has_scores else []
+    pairs = [(ev.create(), ev.create()) for _ in range(K)]
+    set_events = lca.lca_set_score_events if has_scores else lca.lca_set_attn_events
     stream = torch.cuda.current_stream().cuda_stream
 
     for i in range(args.warmup):
@@ -206,11 +207,9 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        if has_scores:
-            lca.lca_set_score_events(pairs[i][0], pairs[i][1])
+        set_events(pairs[i][0], pairs[i][1])
         step.run(i % copies, stream)
-    if has_scores:
-        lca.lca_set_score_events(None, None)
+    set_events(None, None)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = 1e3 * elapsed / K
@@ -234,10 +233,19 @@ def main():
     res["step_algorithmic_flops"] = step.step_flops()
     res["achieved_TFLOPs"] = step.step_flops() / (ms_per_step / 1e3) / 1e12
 
+    durs = [ev.elapsed_ms(a, b) for a, b in pairs]
+    avg_ms = sum(durs) / len(durs)
+    if not has_scores:
+        src = ["long_context_attention_05_amd/csrc/attn.hip", "long_context_attention_05_amd/csrc/lca_device.h"]
+        kname = "attn_wide_kernel"
+        per_launch = step.attn_kernel_bytes()
+        achieved = per_launch / (avg_ms / 1e3) / 1e9
+        res["roofline"] = {"kernel": kname, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                           "frac": achieved / HBM_PEAK_GBPS,
+                           "traffic": traffic_record(kname, w.name, src, per_launch),
+                           "avg_launch_us": avg_ms * 1e3, "algorithmic_bytes_per_launch": per_launch}
     src = ["long_context_attention_05_amd/csrc/indexer.hip", "long_context_attention_05_amd/csrc/lca_device.h"]
     if has_scores:
-        durs = [ev.elapsed_ms(a, b) for a, b in pairs]
-        avg_ms = sum(durs) / len(durs)
         if w.Sq == 1:
             kname = "idx_score_decode_fp4" if w.key_fmt == "fp4" else "idx_score_decode_bf16"
             per_launch = step.score_kernel_bytes()

@@ -134,6 +134,13 @@ size_t indexer_score_topk_workspace_size(int B, int Sq, int N, int k);
  */
 void lca_set_score_events(void* ev_begin, void* ev_end);
 
+/*
+ * lca_set_attn_events -- the same hook for the attention kernel: while both are non-NULL, every sparse_mqa_attn
+ * and hca_attn call made from the calling host thread records ev_begin just before its attention kernel and ev_end
+ * just after it (before the merge of split partials, when there is one).  Pass NULL, NULL to stop.
+ */
+void lca_set_attn_events(void* ev_begin, void* ev_end);
+
 int indexer_score_topk(lca_tensor qI, const float* w, lca_tensor kI, int B, int Sq, int HI, int DI, int N, int m, int k,
                        long long q_start_pos, int32_t* idx_out, float* score_out, void* ws, size_t ws_bytes,
                        void* stream);

@@ -46,8 +46,9 @@ int hip_status(hipError_t e) {
   return e == hipSuccess ? LCA_OK : LCA_ERR_HIP;
 }
 
-// profiling hook (per host thread): events recorded around the indexer scoring kernel
+// profiling hooks (per host thread): events recorded around the indexer scoring kernel and the attention kernel
 thread_local hipEvent_t t_ev_begin = nullptr, t_ev_end = nullptr;
+thread_local hipEvent_t t_attn_ev_begin = nullptr, t_attn_ev_end = nullptr;
 
 // Split plan of the attention: rows = B * Sq query rows, each with up to max_entries list positions.
 // mode 0: one workgroup per (row, split), all heads; 1 (head-group kernel): four workgroups of 16 heads per (row,
@@ -172,7 +173,7 @@ int run_attn(const void* q, int q_format, const lca_tensor& comp, int N, int hca
     a.part_o = (float*)ws;
     a.part_ml = (float*)((char*)ws + align_up(items * H * D * sizeof(float)));
   }
-  return hip_status(launch_attn(a, (hipStream_t)stream));
+  return hip_status(launch_attn(a, (hipStream_t)stream, t_attn_ev_begin, t_attn_ev_end));
 }
 
 }  // namespace
@@ -232,6 +233,11 @@ const char* lca_last_hip_error(void) { return hipGetErrorString(t_last_hip); }
 void lca_set_score_events(void* ev_begin, void* ev_end) {
   t_ev_begin = (hipEvent_t)ev_begin;
   t_ev_end = (hipEvent_t)ev_end;
+}
+
+void lca_set_attn_events(void* ev_begin, void* ev_end) {
+  t_attn_ev_begin = (hipEvent_t)ev_begin;
+  t_attn_ev_end = (hipEvent_t)ev_end;
 }
 
 // Workspace of indexer_score_topk: the score keys [B * Sq][N]; for one query row per sequence (decode) also the

@@ -1112,10 +1112,14 @@ bool attn_uses_mfma(int H, int D, int q_format, int kv_format) {
   return H == 64 && D == 512 && q_format == LCA_BF16 && (kv_format == LCA_BF16 || kv_format == LCA_MIXED_FP8);
 }
 
-hipError_t launch_attn(AttnArgs a, hipStream_t st) {
+hipError_t launch_attn(AttnArgs a, hipStream_t st, hipEvent_t ev_begin, hipEvent_t ev_end) {
   const bool mfma = attn_uses_mfma(a.H, a.D, a.q_format, a.comp.format);
   dim3 grid((unsigned)a.n_splits, (unsigned)a.Sq, (unsigned)a.B);
   clear_stale_error();
+  if (ev_begin && ev_end) {
+    const hipError_t e = hipEventRecord(ev_begin, st);
+    if (e != hipSuccess) return e;
+  }
   if (mfma && a.hg_mode == 2) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) dev = 0;
@@ -1171,6 +1175,7 @@ hipError_t launch_attn(AttnArgs a, hipStream_t st) {
     hipLaunchKernelGGL(attn_simt_kernel, grid, dim3(256), 0, st, a);
   }
   hipError_t e = hipGetLastError();
+  if (e == hipSuccess && ev_begin && ev_end) e = hipEventRecord(ev_end, st);
   if (e != hipSuccess || a.n_splits == 1) return e;
   const size_t lds = sizeof(float) * (size_t)a.n_splits;
   hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)a.H, (unsigned)a.Sq, (unsigned)a.B), dim3(kMergeThreads), lds,

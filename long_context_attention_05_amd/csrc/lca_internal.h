@@ -82,6 +82,7 @@ struct AttnArgs {
 };
 constexpr int kHgSplitMax = 2048;  // list positions per workgroup slice in the head-group kernel
 bool attn_uses_mfma(int H, int D, int q_format, int kv_format);
-hipError_t launch_attn(AttnArgs a, hipStream_t st);
+// ev_begin / ev_end (nullable): recorded around the attention kernel, before the merge of split partials.
+hipError_t launch_attn(AttnArgs a, hipStream_t st, hipEvent_t ev_begin = nullptr, hipEvent_t ev_end = nullptr);
 
 }  // namespace lca

@@ -53,6 +53,8 @@ _lib.indexer_score_topk_workspace_size.restype = _S
 _lib.indexer_score_topk.argtypes = [lca_tensor, _P, lca_tensor] + [_I] * 7 + [_L, _P, _P, _P, _S, _P]
 _lib.lca_set_score_events.argtypes = [_P, _P]
 _lib.lca_set_score_events.restype = None
+_lib.lca_set_attn_events.argtypes = [_P, _P]
+_lib.lca_set_attn_events.restype = None
 _lib.sparse_mqa_attn_workspace_size.argtypes = [_I] * 5
 _lib.sparse_mqa_attn_workspace_size.restype = _S
 _lib.sparse_mqa_attn.argtypes = [_P, _I, lca_tensor, _I, lca_tensor, _L, _I, _P, _I, _P] + [_I] * 5 + [
@@ -155,6 +157,11 @@ def indexer_score_topk_workspace_size(B: int, Sq: int, N: int, k: int) -> int:
 def lca_set_score_events(ev_begin, ev_end):
     """hipEvent_t handles (ints) recorded around the indexer scoring kernel; None, None to stop."""
     _lib.lca_set_score_events(ev_begin, ev_end)
+
+
+def lca_set_attn_events(ev_begin, ev_end):
+    """hipEvent_t handles (ints) recorded around the attention kernel (not the split merge); None, None to stop."""
+    _lib.lca_set_attn_events(ev_begin, ev_end)
 
 
 def indexer_score_topk(qI: lca_tensor, w, kI: lca_tensor, B: int, Sq: int, HI: int, DI: int, N: int, m: int, k: int,

@@ -182,6 +182,12 @@ class HcaDecode:
         eb = _entry_bytes(w.main_fmt, w.D, w.rope)
         return eb * w.B * (w.N + w.window) + 2 * 2 * w.B * w.H * w.D + self.main.nbytes
 
+    def attn_kernel_bytes(self) -> int:
+        """Algorithmic bytes one attention launch must read: every visible entry and the window once, q once."""
+        w = self.w
+        eb = _entry_bytes(w.main_fmt, w.D, w.rope)
+        return eb * w.B * (w.N + w.window) + 2 * w.B * w.H * w.D
+
     def step_flops(self) -> int:
         w = self.w
         return 4 * w.B * w.H * w.D * (w.N + w.window)
