@@ -53,19 +53,21 @@ thread_local hipEvent_t t_attn_ev_begin = nullptr, t_attn_ev_end = nullptr;
 // Split plan of the attention: rows = B * Sq query rows, each with up to max_entries list positions.
 // mode 0: one workgroup per (row, split), all heads; 1 (head-group kernel): four workgroups of 16 heads per (row,
 // split); 2 (wide kernel): one workgroup per (row, split) with the channels split over its waves.
-void attn_plan(int B, int Sq, int H, int max_entries, int mode, int& n_splits, int& split_len) {
+// table: the kernel resolves a slice's rows into an LDS table of kHgSplitMax entries (every MFMA kernel), so no
+// slice may be longer.
+void attn_plan(int B, int Sq, int H, int max_entries, int mode, bool table, int& n_splits, int& split_len) {
   const long long rows = (long long)B * Sq;
-  n_splits = 1;
-  split_len = max_entries > 0 ? max_entries : 1;
-  if (rows >= 256 || max_entries <= 64) return;
   const long long unit = mode == 1 ? 64 : 32;
-  const long long per_row = mode == 1 ? rows * (H / 16) : rows;
-  const long long want = (256 + per_row - 1) / per_row;
-  long long len = (max_entries + want - 1) / want;
-  len = (len + unit - 1) / unit * unit;
-  if (len < 64) len = 64;
-  if (mode != 0 && len > kHgSplitMax) len = kHgSplitMax;  // these kernels resolve a slice's rows into LDS
-  long long ns = (max_entries + len - 1) / len;
+  long long ns = 1, len = max_entries > 0 ? max_entries : 1;
+  if (rows < 256 && max_entries > 64) {
+    const long long per_row = mode == 1 ? rows * (H / 16) : rows;
+    const long long want = (256 + per_row - 1) / per_row;
+    len = (max_entries + want - 1) / want;
+    len = (len + unit - 1) / unit * unit;
+    if (len < 64) len = 64;
+  }
+  if (table && len > kHgSplitMax) len = kHgSplitMax;
+  ns = (max_entries + len - 1) / len;
   const long long max_splits = 4096;  // the merge keeps one weight per split in LDS
   if (ns > max_splits) {
     ns = max_splits;
@@ -73,6 +75,7 @@ void attn_plan(int B, int Sq, int H, int max_entries, int mode, int& n_splits, i
     len = (len + unit - 1) / unit * unit;
     ns = (max_entries + len - 1) / len;
   }
+  if (ns < 1) ns = 1;
   n_splits = (int)ns;
   split_len = (int)len;
 }
@@ -84,9 +87,9 @@ int attn_mode(int B, int Sq, int H, int D, int q_format, int kv_format, int hca_
   return hca_m > 0 ? 2 : 1;
 }
 
-size_t attn_ws_plan_size(int B, int Sq, int H, int D, int max_entries, int mode) {
+size_t attn_ws_plan_size(int B, int Sq, int H, int D, int max_entries, int mode, bool table) {
   int ns, len;
-  attn_plan(B, Sq, H, max_entries, mode, ns, len);
+  attn_plan(B, Sq, H, max_entries, mode, table, ns, len);
   if (ns <= 1) return 0;
   const size_t items = (size_t)B * Sq * ns;
   return align_up(items * H * D * sizeof(float)) + align_up(items * H * 2 * sizeof(float));
@@ -94,10 +97,10 @@ size_t attn_ws_plan_size(int B, int Sq, int H, int D, int max_entries, int mode)
 
 // Enough for whichever kernel the call will take (the size query does not know the formats).
 size_t attn_ws_size(int B, int Sq, int H, int D, int max_entries) {
-  size_t need = attn_ws_plan_size(B, Sq, H, D, max_entries, 0);
+  size_t need = attn_ws_plan_size(B, Sq, H, D, max_entries, 0, false);
   if (H == 64 && D == 512)
-    for (int mode = 1; mode <= 2; ++mode) {
-      const size_t m = attn_ws_plan_size(B, Sq, H, D, max_entries, mode);
+    for (int mode = 0; mode <= 2; ++mode) {
+      const size_t m = attn_ws_plan_size(B, Sq, H, D, max_entries, mode, true);
       if (m > need) need = m;
     }
   return need;
@@ -138,9 +141,9 @@ int run_attn(const void* q, int q_format, const lca_tensor& comp, int N, int hca
   const int max_entries = window + (hca_m > 0 ? N : k);
   const int mode = attn_mode(B, Sq, H, D, q_format, comp.format, hca_m);
   int ns, len;
-  attn_plan(B, Sq, H, max_entries, mode, ns, len);
-  if (mode != 0 && len > kHgSplitMax) return LCA_ERR_UNSUPPORTED;  // more than 4096 x 2048 list positions per row
-  const size_t need = attn_ws_plan_size(B, Sq, H, D, max_entries, mode);
+  attn_plan(B, Sq, H, max_entries, mode, mfma, ns, len);
+  if (mfma && len > kHgSplitMax) return LCA_ERR_UNSUPPORTED;  // more than 4096 x 2048 list positions per row
+  const size_t need = attn_ws_plan_size(B, Sq, H, D, max_entries, mode, mfma);
   if (need > 0 && (!ws || ws_bytes < need)) return LCA_ERR_WORKSPACE;
 
   AttnArgs a{};

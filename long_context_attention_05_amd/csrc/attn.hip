@@ -60,107 +60,160 @@ __device__ __forceinline__ long long list_row(const AttnArgs& a, const RowList& 
   return (long long)b * a.comp.cap + e;
 }
 
-// ------------------------------------------------------------------------------------------------
-// MFMA kernel: H = 64, D = 512, q bf16, KV bf16 or mixed fp8/bf16
-// ------------------------------------------------------------------------------------------------
-constexpr int kTE = 32;            // entries per LDS tile
-constexpr int kRowStride = 520;    // bf16 per entry row in the row-major tile
-constexpr int kTStride = 36;       // bf16 per channel in the channel-major tile (32 entries + pad)
-constexpr int kAttnThreads = 256;
+// The running softmax max only moves when a logit exceeds it by more than kRescaleSlack (e^8 keeps every weight and
+// sum far inside fp32, and bf16 keeps 8 significant bits at any scale), so accumulators are rescaled a few times per
+// row instead of on every tile.
+constexpr float kRescaleSlack = 8.0f;
 
-__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t two) {
-  return (uint32_t)f32_to_bf16(fp8_decode(two & 0xFFu)) | ((uint32_t)f32_to_bf16(fp8_decode((two >> 8) & 0xFFu)) << 16);
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2_t;
+
+// Four OCP e4m3 codes -> four bf16 (exact), via the hardware fp8 -> f32 conversion.
+__device__ __forceinline__ uint2 fp8x4_to_bf16x4(uint32_t w) {
+  const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  uint2 r;
+  r.x = (__float_as_uint(lo[0]) >> 16) | (__float_as_uint(lo[1]) & 0xFFFF0000u);
+  r.y = (__float_as_uint(hi[0]) >> 16) | (__float_as_uint(hi[1]) & 0xFFFF0000u);
+  return r;
 }
+
+// ------------------------------------------------------------------------------------------------
+// MFMA kernel for many query rows (prefill chunks): H = 64, D = 512, q bf16, KV bf16 or mixed fp8/bf16
+// ------------------------------------------------------------------------------------------------
+// One workgroup per (query row, slice of its list) with all 64 heads, wave w holding heads [16 w, 16 w + 16).  The
+// rows of the slice's list positions are resolved into LDS first; then 32-entry tiles are gathered (all 256 threads,
+// 128 contiguous bytes each) into registers one tile ahead, written row-major into a double-buffered LDS tile (fp8
+// widened to bf16) and scored with the same MFMA layouts as the head-group kernel: S^T = K Q^T with A = the tile
+// rows (ds_read_b128) and B = the wave's queries in registers, then O^T += V^T P^T with A = V^T from
+// ds_read_b64_tr_b16 of the row-major tile.  One barrier per tile.
+constexpr int kPfTE = 32;                        // entries per tile
+constexpr int kPfRow = 520;                      // bf16 per LDS tile row (1040 bytes)
+constexpr int kPfTileBytes = kPfTE * kPfRow * 2;  // 33280
+constexpr int kAttnThreads = 256;
+constexpr size_t kPfScaleOff = (size_t)2 * kPfTileBytes;      // [2][32] entry scales
+constexpr size_t kPfValidOff = kPfScaleOff + 2 * kPfTE * 4;    // [2] tile validity masks
+constexpr size_t kPfTableOff = kPfValidOff + 2 * 4 + 8;
+constexpr size_t kMfmaLds = kPfTableOff + (size_t)kHgSplitMax * 4;
 
 template <int FMT>
 __global__ __launch_bounds__(kAttnThreads) void attn_mfma_kernel(AttnArgs a) {
-  extern __shared__ uint16_t lds[];
-  uint16_t* kt = lds;                                // [kTE][kRowStride]
-  uint16_t* vt = lds + kTE * kRowStride;             // [512][kTStride]
-  float* scale_s = (float*)(vt + 512 * kTStride);    // [kTE]
-  int* valid_s = (int*)(scale_s + kTE);              // [kTE]
+  extern __shared__ __attribute__((aligned(16))) uint8_t pf_lds[];
+  float* scale_s = (float*)(pf_lds + kPfScaleOff);
+  uint32_t* valid_s = (uint32_t*)(pf_lds + kPfValidOff);
+  int* rows_s = (int*)(pf_lds + kPfTableOff);
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int hl = lane & 15, grp = lane >> 4;  // head within the wave's 16, lane group
+  const int hl = lane & 15, grp = lane >> 4;
   const int split = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
   const long long t = a.q_start + r;
   const RowList L = row_list(a, t);
   const int total = L.nw + L.nc;
   const int p_begin = split * a.split_len;
-  const int p_end = min(p_begin + a.split_len, total);
+  const int npos = max(min(a.split_len, total - p_begin), 0);
   const int head = 16 * wave + hl;
 
+  for (int i = threadIdx.x; i < npos; i += blockDim.x) {
+    const int p = p_begin + i;
+    int row;
+    if (p < L.nw) {
+      row = (int)(L.w0 + p - a.raw_start);
+    } else if (a.hca_m > 0) {
+      row = p - L.nw;
+    } else {
+      const int e = a.idx[((long long)b * a.Sq + r) * a.k + (p - L.nw)];
+      row = (e >= 0 && e < a.N) ? e : -1;
+    }
+    rows_s[i] = row;
+  }
   // Q^T B operand for 16 K-steps of 32 channels: lane holds q[head][32 s + 8 grp .. + 7]
   bf16x8_t qreg[16];
   {
-    const uint16_t* qp = (const uint16_t*)a.q + (((long long)b * a.Sq + r) * 64 + head) * 512 + 8 * grp;
+    const uint8_t* qp = (const uint8_t*)a.q + ((((long long)b * a.Sq + r) * 64 + head) * 512 + 8 * grp) * 2;
 #pragma unroll
-    for (int s = 0; s < 16; ++s) qreg[s] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(qp + 32 * s));
+    for (int s = 0; s < 16; ++s) qreg[s] = __builtin_bit_cast(bf16x8_t, *(gbl_u32x4_t*)(qp + 64 * s));
   }
+  __syncthreads();
+
+  // gather: thread (ge, gc) moves channels [64 gc, 64 gc + 64) of tile entry ge
+  const int ge = threadIdx.x & 31, gc = threadIdx.x >> 5;
+  u32x4_t gv[8];
+  float gsc = 1.0f;
+  bool gok = false;
+  auto gather = [&](int i0) {
+    const int i = min(i0 + ge, npos - 1);
+    const int row = rows_s[i];
+    gok = i0 + ge < npos && row >= 0;
+    const bool from_raw = p_begin + i < L.nw;
+    const lca_tensor& src = from_raw ? a.raw : a.comp;
+    const long long rr = (long long)b * src.cap + (row >= 0 ? row : 0);
+    if constexpr (FMT == LCA_BF16) {
+      const uint8_t* gp = (const uint8_t*)src.data + rr * 1024 + 128 * gc;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) gv[x] = *(gbl_u32x4_t*)(gp + 16 * x);
+    } else {
+      if (gc < 7) {
+        const uint8_t* gp = (const uint8_t*)src.data + rr * 448 + 64 * gc;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) gv[x] = *(gbl_u32x4_t*)(gp + 16 * x);
+      } else {
+        const uint8_t* gp = (const uint8_t*)src.rope + rr * 128;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) gv[x] = *(gbl_u32x4_t*)(gp + 16 * x);
+      }
+      gsc = ((const float*)src.scale)[rr];
+    }
+  };
+  auto stage = [&](int buf) {
+    uint8_t* kp = pf_lds + buf * kPfTileBytes + ge * (kPfRow * 2) + 128 * gc;
+    if constexpr (FMT == LCA_BF16) {
+#pragma unroll
+      for (int x = 0; x < 8; ++x) *(u32x4_t*)(kp + 16 * x) = gv[x];
+    } else {
+      if (gc < 7) {  // 64 fp8 codes -> 64 bf16 (exact)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const uint2 a0 = fp8x4_to_bf16x4(gv[x].x), a1 = fp8x4_to_bf16x4(gv[x].y);
+          const uint2 a2 = fp8x4_to_bf16x4(gv[x].z), a3 = fp8x4_to_bf16x4(gv[x].w);
+          *(u32x4_t*)(kp + 32 * x) = u32x4_t{a0.x, a0.y, a1.x, a1.y};
+          *(u32x4_t*)(kp + 32 * x + 16) = u32x4_t{a2.x, a2.y, a3.x, a3.y};
+        }
+      } else {
+#pragma unroll
+        for (int x = 0; x < 8; ++x) *(u32x4_t*)(kp + 16 * x) = gv[x];
+      }
+      if (gc == 0) scale_s[buf * kPfTE + ge] = gsc;
+    }
+    const uint64_t vb = __ballot(gok);
+    if (threadIdx.x == 0) valid_s[buf] = (uint32_t)vb;  // lanes 0..31 are the tile's entries (gc = 0)
+  };
+
   f32x4_t acc_o[32];
 #pragma unroll
   for (int dt = 0; dt < 32; ++dt) acc_o[dt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   float m_run = -INFINITY, l_run = 0.0f;
 
-  const int ge = threadIdx.x & 31, gc = threadIdx.x >> 5;  // gather: entry, 64-channel chunk
-  for (int p0 = p_begin; p0 < p_end; p0 += kTE) {
-    __syncthreads();
-    {  // gather 32 entries: thread (ge, gc) moves channels [64 gc, 64 gc + 64) of entry ge
-      const int p = p0 + ge;
-      const long long row = (p < p_end) ? list_row(a, L, b, r, p) : -1;
-      const bool from_raw = p < L.nw;
-      const lca_tensor& src = from_raw ? a.raw : a.comp;
-      uint4 v[8];
-      float sc = 1.0f;
-      if (row >= 0) {
-        if (FMT == LCA_BF16) {
-          const uint4* gp = (const uint4*)((const uint16_t*)src.data + row * 512 + 64 * gc);
-#pragma unroll
-          for (int x = 0; x < 8; ++x) v[x] = gp[x];
-        } else {
-          if (gc < 7) {
-            const uint4* gp = (const uint4*)((const uint8_t*)src.data + row * 448 + 64 * gc);
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-              uint4 c = gp[x];
-              v[2 * x] = make_uint4(fp8x2_to_bf16x2(c.x), fp8x2_to_bf16x2(c.x >> 16), fp8x2_to_bf16x2(c.y),
-                                    fp8x2_to_bf16x2(c.y >> 16));
-              v[2 * x + 1] = make_uint4(fp8x2_to_bf16x2(c.z), fp8x2_to_bf16x2(c.z >> 16), fp8x2_to_bf16x2(c.w),
-                                        fp8x2_to_bf16x2(c.w >> 16));
-            }
-          } else {
-            const uint4* gp = (const uint4*)((const uint16_t*)src.rope + row * 64);
-#pragma unroll
-            for (int x = 0; x < 8; ++x) v[x] = gp[x];
-          }
-          sc = ((const float*)src.scale)[row];
-        }
-      } else {
-#pragma unroll
-        for (int x = 0; x < 8; ++x) v[x] = make_uint4(0, 0, 0, 0);
-      }
-      uint4* kp = (uint4*)(kt + ge * kRowStride + 64 * gc);
-#pragma unroll
-      for (int x = 0; x < 8; ++x) kp[x] = v[x];
-      const uint16_t* hv = (const uint16_t*)v;
-#pragma unroll
-      for (int x = 0; x < 64; ++x) vt[(64 * gc + x) * kTStride + ge] = hv[x];
-      if (gc == 0) {
-        scale_s[ge] = sc;
-        valid_s[ge] = row >= 0;
-      }
-    }
-    __syncthreads();
+  const int ntiles = (npos + kPfTE - 1) / kPfTE;
+  if (ntiles > 0) {
+    gather(0);
+    stage(0);
+  }
+  __syncthreads();
+  for (int tt = 0; tt < ntiles; ++tt) {
+    const int cur = tt & 1;
+    if (tt + 1 < ntiles) gather(kPfTE * (tt + 1));  // block-uniform: the next tile is in flight
+    const uint16_t* kt = (const uint16_t*)(pf_lds + cur * kPfTileBytes);
+    const uint32_t valid = valid_s[cur];
 
-    // S^T = K Q^T for two 16-entry tiles
-    float lg[2][4];
+    // S^T = K Q^T for the two 16-entry halves
+    float lg[2][4], esc[2][4];
 #pragma unroll
     for (int et = 0; et < 2; ++et) {
       f32x4_t am = {0.0f, 0.0f, 0.0f, 0.0f}, ar = {0.0f, 0.0f, 0.0f, 0.0f};
-      const uint16_t* kp = kt + (16 * et + hl) * kRowStride + 8 * grp;
+      const uint16_t* kp = kt + (16 * et + hl) * kPfRow + 8 * grp;
 #pragma unroll
       for (int s = 0; s < 16; ++s) {
-        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, *(const uint4*)(kp + 32 * s));
+        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(kp + 32 * s));
         if (FMT == LCA_MIXED_FP8 && s >= 14)
           ar = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qreg[s], ar, 0, 0, 0);
         else
@@ -169,16 +222,18 @@ __global__ __launch_bounds__(kAttnThreads) void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
         const int e = 16 * et + 4 * grp + x;
-        float l = (FMT == LCA_MIXED_FP8) ? a.scale * (scale_s[e] * am[x] + ar[x]) : a.scale * am[x];
-        lg[et][x] = valid_s[e] ? l : -INFINITY;
+        esc[et][x] = (FMT == LCA_MIXED_FP8) ? scale_s[cur * kPfTE + e] : 1.0f;
+        const float l = (FMT == LCA_MIXED_FP8) ? a.scale * (esc[et][x] * am[x] + ar[x]) : a.scale * am[x];
+        lg[et][x] = ((valid >> e) & 1u) ? l : -INFINITY;
       }
     }
-    // online softmax for head `head` (lanes hl, hl+16, hl+32, hl+48 hold its 32 logits)
+    // online softmax for head `head` (lanes hl, hl + 16, hl + 32, hl + 48 hold its 32 logits); the reference max
+    // only moves by more than kRescaleSlack, as in the decode kernels
     float mt = fmaxf(fmaxf(fmaxf(lg[0][0], lg[0][1]), fmaxf(lg[0][2], lg[0][3])),
                      fmaxf(fmaxf(lg[1][0], lg[1][1]), fmaxf(lg[1][2], lg[1][3])));
     mt = xor32_max(xor16_max(mt));
-    const float m_new = fmaxf(m_run, mt);
-    const float alpha = (m_new == -INFINITY) ? 1.0f : __expf(m_run - m_new);
+    const float m_new = (mt > m_run + kRescaleSlack) ? mt : m_run;
+    const float alpha = (m_new == m_run) ? 1.0f : __expf(m_run - m_new);
     float pv[2][4], psum = 0.0f;
 #pragma unroll
     for (int et = 0; et < 2; ++et)
@@ -190,26 +245,34 @@ __global__ __launch_bounds__(kAttnThreads) void attn_mfma_kernel(AttnArgs a) {
     psum = xor32_sum(xor16_sum(psum));
     l_run = l_run * alpha + psum;
     m_run = m_new;
+    if (__ballot(alpha != 1.0f)) {
 #pragma unroll
-    for (int dt = 0; dt < 32; ++dt) acc_o[dt] *= alpha;
+      for (int dt = 0; dt < 32; ++dt) acc_o[dt] *= alpha;
+    }
 
-    // O^T += V^T P^T
+    // O^T += V^T P^T, 16 entries per product
 #pragma unroll
     for (int et = 0; et < 2; ++et) {
       s16x4_t pb, pbs;
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
         pb[x] = (short)f32_to_bf16(pv[et][x]);
-        pbs[x] = (short)f32_to_bf16(pv[et][x] * scale_s[16 * et + 4 * grp + x]);
+        pbs[x] = (FMT == LCA_MIXED_FP8) ? (short)f32_to_bf16(pv[et][x] * esc[et][x]) : pb[x];
       }
-      const uint16_t* vp = vt + hl * kTStride + 16 * et + 4 * grp;
+      const uint16_t* vp = kt + (16 * et + 4 * grp + (hl >> 2)) * kPfRow + 4 * (hl & 3);
 #pragma unroll
-      for (int dt = 0; dt < 32; ++dt) {
-        const s16x4_t av = __builtin_bit_cast(s16x4_t, *(const uint2*)(vp + 16 * dt * kTStride));
-        const s16x4_t bop = (FMT == LCA_MIXED_FP8 && dt < 28) ? pbs : pb;
-        acc_o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bop, acc_o[dt], 0, 0, 0);
+      for (int d0 = 0; d0 < 32; d0 += 8) {
+        s16x4_t av[8];
+#pragma unroll
+        for (int d = 0; d < 8; ++d) av[d] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vp + 16 * (d0 + d)));
+#pragma unroll
+        for (int d = 0; d < 8; ++d)
+          acc_o[d0 + d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+              av[d], (FMT == LCA_MIXED_FP8 && d0 + d < 28) ? pbs : pb, acc_o[d0 + d], 0, 0, 0);
       }
     }
+    if (tt + 1 < ntiles) stage(cur ^ 1);
+    __syncthreads();
   }
 
   // lane holds o^T[channel 16 dt + 4 grp + x][head]
@@ -274,7 +337,6 @@ __global__ __launch_bounds__(kAttnThreads) void attn_mfma_kernel(AttnArgs a) {
 // XCD and share its L2 copy of the gathered entries.
 constexpr int kHgRow = 520;                // bf16 per LDS tile row (1040 bytes)
 constexpr int kWTile = 16;                 // entries per wave tile
-constexpr float kRescaleSlack = 8.0f;
 constexpr int kWBufBytes = kWTile * kHgRow * 2;  // 16640
 // four wave tiles, the row table (the merge buffer reuses both), the waves' (max, sum) and
 // the entry scales
@@ -286,23 +348,6 @@ constexpr size_t kHgMlOff = kHgMergeBytes > kHgTableOff + (size_t)kHgSplitMax * 
                                 ? kHgMergeBytes
                                 : kHgTableOff + (size_t)kHgSplitMax * 4;
 constexpr size_t kHgwLds = kHgMlOff + 4 * 16 * 2 * 4 + 4 * 16 * 4;
-
-typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(1))) const u32x4_t gbl_u32x4_t;
-typedef __attribute__((address_space(1))) const u32x2_t gbl_u32x2_t;
-typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2_t;
-
-// Four OCP e4m3 codes -> four bf16 (exact), via the hardware fp8 -> f32 conversion.
-__device__ __forceinline__ uint2 fp8x4_to_bf16x4(uint32_t w) {
-  const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
-  const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
-  uint2 r;
-  r.x = (__float_as_uint(lo[0]) >> 16) | (__float_as_uint(lo[1]) & 0xFFFF0000u);
-  r.y = (__float_as_uint(hi[0]) >> 16) | (__float_as_uint(hi[1]) & 0xFFFF0000u);
-  return r;
-}
 
 // A wave's tile in the S^T operand layout.  bf16: v[s] = bytes 64 s + 16 (l / 16) .. + 15 of entry l % 16's row.
 // mixed: f[s] = fp8 bytes 32 s + 8 (l / 16) .. + 7 (s < 14), r[s] = RoPE bf16 bytes 64 s + 16 (l / 16) .. (s < 2).
@@ -1103,7 +1148,6 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
   }
 }
 
-constexpr size_t kMfmaLds = (size_t)kTE * kRowStride * 2 + (size_t)512 * kTStride * 2 + kTE * 4 * 2;
 static bool g_attn_attr[64];
 static bool g_hg_attr[64];
 static bool g_wd_attr[64];

@@ -121,11 +121,30 @@ __device__ __forceinline__ void load_row64(const lca_tensor& t, long long row, i
   }
 }
 
+// One query row's 64 x 128 block (bf16; fp4 widened exactly) as 4 chunks of 8 channels per thread of 256.
+template <int FMT>
+__device__ __forceinline__ void load_qblock(const IdxArgs& a, long long qrow0, u32x4_t (&v)[4]) {
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int chunk = threadIdx.x + 256 * it;  // 1024 chunks of 8 channels
+    const int h = chunk >> 4, c8 = chunk & 15;
+    if constexpr (FMT == LCA_BF16) {
+      v[it] = *(gbl_u32x4_t*)((const uint16_t*)a.q.data + (qrow0 + h) * 128 + 8 * c8);
+    } else {
+      const uint32_t codes = *(const uint32_t*)((const uint8_t*)a.q.data + (qrow0 + h) * 64 + 4 * c8);
+      const int e = (int)((const uint8_t*)a.q.scale)[(qrow0 + h) * 8 + (c8 >> 1)] - 127;
+      const uint4 w = fp4x8_to_bf16x8(codes, e);
+      v[it] = u32x4_t{w.x, w.y, w.z, w.w};
+    }
+  }
+}
+
 template <int FMT>
 __global__ __launch_bounds__(256) void idx_score_mfma(IdxArgs a, int qpb) {
 #pragma clang fp contract(off)
-  __shared__ uint16_t q_s[64 * kQStride];
-  __shared__ float w_s[64];
+  // query blocks double-buffered in LDS: the next row's block is loaded into registers while this row is scored
+  __shared__ uint16_t q_s[2][64 * kQStride];
+  __shared__ float w_s[2][64];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int g = lane >> 5, col = lane & 31;
   const int b = blockIdx.z;
@@ -151,76 +170,74 @@ __global__ __launch_bounds__(256) void idx_score_mfma(IdxArgs a, int qpb) {
     for (int s = 0; s < 8; ++s) kb[u][s] = __builtin_bit_cast(bf16x8_t, raw[s]);
   }
 
-  for (int r = r_begin; r < r_end; ++r) {
-    const long long t = a.q_start + r;
-    const int nvis = nvis_of(t, a.m, a.N);
-    if (blockIdx.x * kMfmaEntriesPerBlock >= nvis) continue;  // block-uniform
-    __syncthreads();
-    {  // stage the 64 x 128 query block (bf16) in LDS: 256 threads x 4 chunks of 8 channels
-      const long long qrow0 = ((long long)b * a.Sq + r) * 64;
+  u32x4_t qn[4];
+  float wn = 0.0f;
+  auto stage = [&](int buf) {
 #pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const int chunk = threadIdx.x + 256 * it;  // 1024 chunks of 8 channels
-        const int h = chunk >> 4, c8 = chunk & 15;
-        uint4 v;
-        if (FMT == LCA_BF16) {
-          v = *(const uint4*)((const uint16_t*)a.q.data + (qrow0 + h) * 128 + 8 * c8);
-        } else {
-          uint32_t codes = *(const uint32_t*)((const uint8_t*)a.q.data + (qrow0 + h) * 64 + 4 * c8);
-          int e = (int)((const uint8_t*)a.q.scale)[(qrow0 + h) * 8 + (c8 >> 1)] - 127;
-          v = fp4x8_to_bf16x8(codes, e);
-        }
-        *(uint4*)&q_s[h * kQStride + 8 * c8] = v;
-      }
-      if (threadIdx.x < 64) w_s[threadIdx.x] = a.w[((long long)b * a.Sq + r) * 64 + threadIdx.x];
+    for (int it = 0; it < 4; ++it) {
+      const int chunk = threadIdx.x + 256 * it;
+      *(u32x4_t*)&q_s[buf][(chunk >> 4) * kQStride + 8 * (chunk & 15)] = qn[it];
     }
-    __syncthreads();
-    if (e0 >= nvis) continue;  // wave-uniform
+    if (threadIdx.x < 64) w_s[buf][threadIdx.x] = wn;
+  };
+  load_qblock<FMT>(a, ((long long)b * a.Sq + r_begin) * 64, qn);
+  if (threadIdx.x < 64) wn = a.w[((long long)b * a.Sq + r_begin) * 64 + threadIdx.x];
+  stage(0);
+  __syncthreads();
 
-    f32x16_t acc[2][2];
+  for (int r = r_begin; r < r_end; ++r) {
+    const int cur = (r - r_begin) & 1;
+    {  // the next row's block is in flight while this row is scored (the last row reloads itself, unused)
+      const int rn = min(r + 1, r_end - 1);
+      load_qblock<FMT>(a, ((long long)b * a.Sq + rn) * 64, qn);
+      if (threadIdx.x < 64) wn = a.w[((long long)b * a.Sq + rn) * 64 + threadIdx.x];
+    }
+    const int nvis = nvis_of(a.q_start + r, a.m, a.N);
+    if (e0 < nvis) {  // wave-uniform
+      f32x16_t acc[2][2];
 #pragma unroll
-    for (int T = 0; T < 2; ++T)
+      for (int T = 0; T < 2; ++T)
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int x = 0; x < 16; ++x) acc[T][u][x] = 0.0f;
+          for (int x = 0; x < 16; ++x) acc[T][u][x] = 0.0f;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
+      for (int s = 0; s < 8; ++s) {
 #pragma unroll
-      for (int T = 0; T < 2; ++T) {
-        const uint4 qv = *(const uint4*)&q_s[(32 * T + col) * kQStride + 64 * g + 8 * s];
-        const bf16x8_t qa = __builtin_bit_cast(bf16x8_t, qv);
+        for (int T = 0; T < 2; ++T) {
+          const uint4 qv = *(const uint4*)&q_s[cur][(32 * T + col) * kQStride + 64 * g + 8 * s];
+          const bf16x8_t qa = __builtin_bit_cast(bf16x8_t, qv);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) acc[T][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kb[u][s], acc[T][u], 0, 0, 0);
+          for (int u = 0; u < 2; ++u)
+            acc[T][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kb[u][s], acc[T][u], 0, 0, 0);
+        }
+      }
+      // epilogue: head h = 32T + 8(x/4) + 4g + (x%4) for register x; fixed halving tree over h
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        float l1[16];
+#pragma unroll
+        for (int x = 0; x < 16; ++x) {  // level 1: h + 32
+          const int h = 8 * (x >> 2) + 4 * g + (x & 3);
+          const float p0 = w_s[cur][h] * fmaxf(acc[0][u][x], 0.0f);
+          const float p1 = w_s[cur][32 + h] * fmaxf(acc[1][u][x], 0.0f);
+          l1[x] = p0 + p1;
+        }
+        float l2[8], l3[4], l4[4];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) l2[x] = l1[x] + l1[x + 8];  // h + 16
+#pragma unroll
+        for (int x = 0; x < 4; ++x) l3[x] = l2[x] + l2[x + 4];  // h + 8
+#pragma unroll
+        for (int x = 0; x < 4; ++x) l4[x] = xor32_sum(l3[x]);  // h + 4: the partner lane holds the other 4g half
+        const float l5_0 = l4[0] + l4[2], l5_1 = l4[1] + l4[3];  // h + 2
+        const float sc = l5_0 + l5_1;                            // h + 1
+        const int e = e0 + 32 * u + col;
+        if (g == 0 && e < nvis) a.keys[((long long)b * a.Sq + r) * a.N + e] = score_key(sc);
       }
     }
-    // epilogue: head h = 32T + 8(x/4) + 4g + (x%4) for register x; fixed halving tree over h
-    float wv[2][16];
-#pragma unroll
-    for (int T = 0; T < 2; ++T)
-#pragma unroll
-      for (int x = 0; x < 16; ++x) wv[T][x] = w_s[32 * T + 8 * (x >> 2) + 4 * g + (x & 3)];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      float l1[16];
-#pragma unroll
-      for (int x = 0; x < 16; ++x) {  // level 1: h + 32
-        float p0 = wv[0][x] * fmaxf(acc[0][u][x], 0.0f);
-        float p1 = wv[1][x] * fmaxf(acc[1][u][x], 0.0f);
-        l1[x] = p0 + p1;
-      }
-      float l2[8], l3[4], l4[4];
-#pragma unroll
-      for (int x = 0; x < 8; ++x) l2[x] = l1[x] + l1[x + 8];  // h + 16
-#pragma unroll
-      for (int x = 0; x < 4; ++x) l3[x] = l2[x] + l2[x + 4];  // h + 8
-#pragma unroll
-      for (int x = 0; x < 4; ++x) l4[x] = xor32_sum(l3[x]);  // h + 4: the partner lane holds the other 4g half
-      float l5_0 = l4[0] + l4[2], l5_1 = l4[1] + l4[3];  // h + 2
-      float s = l5_0 + l5_1;                             // h + 1
-      const int e = e0 + 32 * u + col;
-      if (g == 0 && e < nvis) a.keys[((long long)b * a.Sq + r) * a.N + e] = score_key(s);
-    }
+    stage(cur ^ 1);
+    __syncthreads();
   }
 }
 

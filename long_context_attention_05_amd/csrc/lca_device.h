@@ -15,6 +15,12 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+// Plain 16- and 8-byte vectors: unlike HIP's uint4 struct, copies of these stay in registers (no memcpy through
+// private memory); the address-space-1 pointer types make loads global rather than flat.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(1))) const u32x4_t gbl_u32x4_t;
+typedef __attribute__((address_space(1))) const u32x2_t gbl_u32x2_t;
 
 namespace lca {
 

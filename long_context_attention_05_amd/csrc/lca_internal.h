@@ -80,7 +80,7 @@ struct AttnArgs {
   int hg_mode;     // 1: one workgroup per (16-head group, row, split); 2: one per (row, split) with the channels
                    // split over the waves -- few rows (decode)
 };
-constexpr int kHgSplitMax = 2048;  // list positions per workgroup slice in the head-group kernel
+constexpr int kHgSplitMax = 2048;  // list positions per workgroup slice in the MFMA attention kernels (LDS row table)
 bool attn_uses_mfma(int H, int D, int q_format, int kv_format);
 // ev_begin / ev_end (nullable): recorded around the attention kernel, before the merge of split partials.
 hipError_t launch_attn(AttnArgs a, hipStream_t st, hipEvent_t ev_begin = nullptr, hipEvent_t ev_end = nullptr);
