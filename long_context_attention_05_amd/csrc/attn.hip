@@ -78,6 +78,49 @@ __device__ __forceinline__ uint2 fp8x4_to_bf16x4(uint32_t w) {
   return r;
 }
 
+// Writes a prefill workgroup's result for head `head`: lane (head, grp) holds o^T[channel 16 dt + 4 grp + x][head]
+// in acc_o[dt][x].  A single split normalises with the sink in place; otherwise (max, sum, o) go to the partials.
+__device__ __forceinline__ void pf_finish(const AttnArgs& a, const f32x4_t (&acc_o)[32], float m_run, float l_run,
+                                          int b, int r, int split, int head, int grp) {
+  const long long item = ((long long)b * a.Sq + r) * a.n_splits + split;
+  if (a.n_splits == 1) {
+    const float z = a.sink[head];
+    const float M = fmaxf(m_run, z);
+    float den, f;
+    if (M == -INFINITY) {
+      den = 0.0f;
+      f = 0.0f;
+    } else {
+      den = ((z == -INFINITY) ? 0.0f : __expf(z - M)) + l_run * ((m_run == -INFINITY) ? 0.0f : __expf(m_run - M));
+      f = (m_run == -INFINITY) ? 0.0f : __expf(m_run - M) / den;
+    }
+    const long long ob = (((long long)b * a.Sq + r) * 64 + head) * 512;
+#pragma unroll
+    for (int dt = 0; dt < 32; ++dt) {
+      const int c0 = 16 * dt + 4 * grp;
+      if (a.out_format == LCA_F32) {
+        *(float4*)((float*)a.out + ob + c0) =
+            make_float4(acc_o[dt][0] * f, acc_o[dt][1] * f, acc_o[dt][2] * f, acc_o[dt][3] * f);
+      } else {
+        uint2 w2;
+        w2.x = (uint32_t)f32_to_bf16(acc_o[dt][0] * f) | ((uint32_t)f32_to_bf16(acc_o[dt][1] * f) << 16);
+        w2.y = (uint32_t)f32_to_bf16(acc_o[dt][2] * f) | ((uint32_t)f32_to_bf16(acc_o[dt][3] * f) << 16);
+        *(uint2*)((uint16_t*)a.out + ob + c0) = w2;
+      }
+    }
+    if (a.lse && grp == 0) a.lse[((long long)b * a.Sq + r) * 64 + head] = (M == -INFINITY) ? -INFINITY : M + __logf(den);
+  } else {
+    float* po = a.part_o + (item * 64 + head) * 512;
+#pragma unroll
+    for (int dt = 0; dt < 32; ++dt)
+      *(float4*)(po + 16 * dt + 4 * grp) = make_float4(acc_o[dt][0], acc_o[dt][1], acc_o[dt][2], acc_o[dt][3]);
+    if (grp == 0) {
+      a.part_ml[(item * 64 + head) * 2 + 0] = m_run;
+      a.part_ml[(item * 64 + head) * 2 + 1] = l_run;
+    }
+  }
+}
+
 // ------------------------------------------------------------------------------------------------
 // MFMA kernel for many query rows (prefill chunks): H = 64, D = 512, q bf16, KV bf16 or mixed fp8/bf16
 // ------------------------------------------------------------------------------------------------
@@ -275,42 +318,352 @@ __global__ __launch_bounds__(kAttnThreads) void attn_mfma_kernel(AttnArgs a) {
     __syncthreads();
   }
 
-  // lane holds o^T[channel 16 dt + 4 grp + x][head]
-  const long long item = ((long long)b * a.Sq + r) * a.n_splits + split;
-  if (a.n_splits == 1) {
-    const float z = a.sink[head];
-    const float M = fmaxf(m_run, z);
-    float den, f;
-    if (M == -INFINITY) {
-      den = 0.0f;
-      f = 0.0f;
-    } else {
-      den = ((z == -INFINITY) ? 0.0f : __expf(z - M)) + l_run * ((m_run == -INFINITY) ? 0.0f : __expf(m_run - M));
-      f = (m_run == -INFINITY) ? 0.0f : __expf(m_run - M) / den;
-    }
-    const long long ob = (((long long)b * a.Sq + r) * 64 + head) * 512;
+  pf_finish(a, acc_o, m_run, l_run, b, r, split, head, grp);
+}
+
+// ------------------------------------------------------------------------------------------------
+// bf16 prefill kernel: LDS-direct loads into a four-tile ring, QK by heads, PV by channels
+// ------------------------------------------------------------------------------------------------
+// One workgroup per (query row, slice of its list), four waves, 32-entry tiles.
+//   Loads: the tiles travel from memory straight into LDS (buffer_load ... lds: one instruction moves one 1 KB entry
+//     row, 16 bytes per lane), so no registers hold data in flight; three tiles are in flight while one is scored.
+//     Each ring slot is its own LDS variable and the tile loop is unrolled over the slots, so the compiler can tell
+//     that a slot's reads do not alias loads still landing in other slots; the waits for a slot are explicit counts.
+//   S^T = K Q^T: wave w owns heads 16 w .. 16 w + 15 (v_mfma_f32_16x16x32_bf16, A = K rows from LDS, B = the wave's
+//     queries in registers) and runs their online softmax.
+//   O^T += V^T P^T: wave w owns channels 128 w .. 128 w + 127 for all 64 heads.  Each wave publishes its P^T operand
+//     (lane: head, 8 entries) and the heads' rescale factors in LDS; every V^T operand (two transposing reads,
+//     ds_read_b64_tr_b16) then feeds four MFMAs, one per head group, which quarters the transposing reads against a
+//     split by heads.  The K index 8 g + v of lane group g stands for entry 4 g + v (v < 4) and 16 + 4 g + v - 4
+//     (v >= 4): the pair of 16-entry halves that the S^T accumulators and the two transposing reads already hold.
+//   One barrier per tile: before it a wave has scored its tile, published P and waited for its share of the next
+//   tile's loads; after it the freed ring slot is refilled and the PV product runs.
+constexpr int kPdSlots = 4;
+constexpr int kPdRowB = 1040;                    // LDS bytes per tile row
+constexpr int kPdTileB = kPfTE * kPdRowB;        // 33280
+__shared__ __attribute__((aligned(16))) uint8_t pd_slot0[kPdTileB];
+__shared__ __attribute__((aligned(16))) uint8_t pd_slot1[kPdTileB];
+__shared__ __attribute__((aligned(16))) uint8_t pd_slot2[kPdTileB];
+__shared__ __attribute__((aligned(16))) uint8_t pd_slot3[kPdTileB];
+__shared__ int pd_rows[kHgSplitMax];
+__shared__ __attribute__((aligned(16))) u32x4_t pd_p[2][4][64];   // [tile parity][head group][lane]: P^T operands
+__shared__ __attribute__((aligned(16))) float pd_alpha[2][16][4];  // [tile parity][head % 16][head / 16]
+__shared__ float pd_ml[64][2];
+
+template <int S>
+__device__ __forceinline__ uint8_t* pd_slot() {
+  if constexpr (S == 0) return pd_slot0;
+  else if constexpr (S == 1) return pd_slot1;
+  else if constexpr (S == 2) return pd_slot2;
+  else return pd_slot3;
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+// Buffer descriptor word 3 for raw untyped loads (32-bit data format, no swizzle, no index stride).
+constexpr int kBufRsrcWord3 = 0x00020000;
+// s_waitcnt immediates (vmcnt in bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8])
+constexpr int kWaitVm8 = (0xF << 8) | (7 << 4) | 8;  // vmcnt(8)
+constexpr int kWaitVm0 = (0xF << 8) | (7 << 4);      // vmcnt(0)
+
+// Workgroup barrier for LDS only: the compiler keeps memory accesses on their side of it and no load in flight is
+// waited for (the caller has already waited for what it needs).
+__device__ __forceinline__ void pd_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__global__ __launch_bounds__(kAttnThreads) void attn_pf_kernel(AttnArgs a) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int hl = lane & 15, grp = lane >> 4;
+  const int split = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
+  const long long t = a.q_start + r;
+  const RowList L = row_list(a, t);
+  const int total = L.nw + L.nc;
+  const int p_begin = split * a.split_len;
+  const int npos = max(min(a.split_len, total - p_begin), 0);
+  const int qhead = 16 * wave + hl;  // the head this lane scores
+
+  // the queries load first, so that the barrier after the row table has them in registers before the ring starts
+  bf16x8_t qreg[16];
+  {
+    const uint8_t* qp = (const uint8_t*)a.q + ((((long long)b * a.Sq + r) * 64 + qhead) * 512 + 8 * grp) * 2;
 #pragma unroll
-    for (int dt = 0; dt < 32; ++dt) {
-      const int c0 = 16 * dt + 4 * grp;
-      if (a.out_format == LCA_F32) {
-        *(float4*)((float*)a.out + ob + c0) =
-            make_float4(acc_o[dt][0] * f, acc_o[dt][1] * f, acc_o[dt][2] * f, acc_o[dt][3] * f);
-      } else {
-        uint2 w2;
-        w2.x = (uint32_t)f32_to_bf16(acc_o[dt][0] * f) | ((uint32_t)f32_to_bf16(acc_o[dt][1] * f) << 16);
-        w2.y = (uint32_t)f32_to_bf16(acc_o[dt][2] * f) | ((uint32_t)f32_to_bf16(acc_o[dt][3] * f) << 16);
-        *(uint2*)((uint16_t*)a.out + ob + c0) = w2;
+    for (int s = 0; s < 16; ++s) qreg[s] = __builtin_bit_cast(bf16x8_t, *(gbl_u32x4_t*)(qp + 64 * s));
+  }
+  for (int i = threadIdx.x; i < npos; i += blockDim.x) {
+    const int p = p_begin + i;
+    int row;
+    if (p < L.nw) {
+      row = (int)(L.w0 + p - a.raw_start);
+    } else if (a.hca_m > 0) {
+      row = p - L.nw;
+    } else {
+      const int e = a.idx[((long long)b * a.Sq + r) * a.k + (p - L.nw)];
+      row = (e >= 0 && e < a.N) ? e : -1;
+    }
+    pd_rows[i] = row;
+  }
+  // An empty asm re-defines each query register, so that the tile loop does not see registers defined by memory
+  // loads from before it (the compiler would otherwise wait for every load in flight when entering the loop).
+#pragma unroll
+  for (int s = 0; s < 16; ++s) asm volatile("" : "+v"(qreg[s]));
+  // acc[hg][dt]: lane (hl, grp) holds o^T[channel 128 w + 16 dt + 4 grp + x][head 16 hg + hl]
+  f32x4_t acc[4][8];
+#pragma unroll
+  for (int hg = 0; hg < 4; ++hg)
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) acc[hg][dt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  float m_run = -INFINITY, l_run = 0.0f;  // of head qhead
+  __syncthreads();
+
+  const int ntiles = (npos + kPfTE - 1) / kPfTE;
+  if (ntiles > 0) {  // block-uniform
+    // one buffer descriptor per tensor of batch b (range-checked, 32-bit offsets: the launcher keeps a batch's rows
+    // under 2 GiB); the row offset goes in the scalar offset, 16 bytes per lane in the vector offset
+    const __amdgpu_buffer_rsrc_t raw_rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const uint8_t*)a.raw.data + (long long)b * a.raw.cap * 1024), 0, (int)(a.raw.cap * 1024), kBufRsrcWord3);
+    const __amdgpu_buffer_rsrc_t comp_rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const uint8_t*)a.comp.data + (long long)b * a.comp.cap * 1024), 0, (int)(a.comp.cap * 1024),
+        kBufRsrcWord3);
+    // Wave w moves entries 8 w .. 8 w + 7 of tile tt into ring slot S; positions past the slice repeat its last
+    // entry, so every tile issues the same number of loads and the wait counts stay fixed.
+    auto issue = [&](auto SC, int tt) {
+      constexpr int S = decltype(SC)::value;
+      const int ii = min(kPfTE * tt + 8 * wave + (lane & 7), npos - 1);
+      const int myrow = pd_rows[ii];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int i = __builtin_amdgcn_readfirstlane(min(kPfTE * tt + 8 * wave + q, npos - 1));
+        const int row = __builtin_amdgcn_readlane(myrow, q);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(p_begin + i < L.nw ? raw_rs : comp_rs,
+                                                 (lds_void_t*)(pd_slot<S>() + (8 * wave + q) * kPdRowB), 16, 16 * lane,
+                                                 max(row, 0) * 1024, 0, 0);
+      }
+    };
+    // S^T = K Q^T of tile tt (slot S) for the wave's 16 heads.  LDS reads go in batches of 4 with three batches in
+    // flight (12 reads: the wave's counter of outstanding LDS reads holds at most 15).  K batch j: K-steps 2 j and
+    // 2 j + 1 of both 16-entry halves; four independent accumulator chains.
+    // Also returns the tile's mask of entries with a row.
+    auto qk = [&](auto SC, f32x4_t (&am)[2][2], int tt) -> uint32_t {
+      constexpr int S = decltype(SC)::value;
+      const int iv = kPfTE * tt + (lane & 31);
+      const uint32_t valid = (uint32_t)__ballot(iv < npos && pd_rows[min(iv, npos - 1)] >= 0);
+      const uint8_t* kp = pd_slot<S>() + hl * kPdRowB + 16 * grp;
+      u32x4_t kb[3][4];
+      auto kload = [&](u32x4_t (&dst)[4], int j) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          dst[2 * u] = *(const u32x4_t*)(kp + 64 * (2 * j + u));
+          dst[2 * u + 1] = *(const u32x4_t*)(kp + 16 * kPdRowB + 64 * (2 * j + u));
+        }
+      };
+#pragma unroll
+      for (int et = 0; et < 2; ++et) am[et][0] = am[et][1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      kload(kb[0], 0);
+      kload(kb[1], 1);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (j + 2 < 8) kload(kb[(j + 2) % 3], j + 2);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int et = 0; et < 2; ++et)
+            am[et][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kb[j % 3][2 * u + et]),
+                                                                qreg[2 * j + u], am[et][u], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      return valid;
+    };
+    // Online softmax of tile tt for head qhead (lanes hl, hl + 16, hl + 32, hl + 48 hold its 32 logits; the
+    // reference max only moves by more than kRescaleSlack); publishes P^T and the rescale factor in buffer tt & 1.
+    auto softmax = [&](const f32x4_t (&am)[2][2], uint32_t valid, int tt) {
+      float lg[2][4];
+#pragma unroll
+      for (int et = 0; et < 2; ++et) {
+        const f32x4_t sum = am[et][0] + am[et][1];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) lg[et][x] = ((valid >> (16 * et + 4 * grp + x)) & 1u) ? a.scale * sum[x] : -INFINITY;
+      }
+      float mt = fmaxf(fmaxf(fmaxf(lg[0][0], lg[0][1]), fmaxf(lg[0][2], lg[0][3])),
+                       fmaxf(fmaxf(lg[1][0], lg[1][1]), fmaxf(lg[1][2], lg[1][3])));
+      mt = xor32_max(xor16_max(mt));
+      const float m_new = (mt > m_run + kRescaleSlack) ? mt : m_run;
+      const float alpha = (m_new == m_run) ? 1.0f : __expf(m_run - m_new);
+      float psum = 0.0f;
+      u32x4_t pw;
+#pragma unroll
+      for (int et = 0; et < 2; ++et)
+#pragma unroll
+        for (int x = 0; x < 4; x += 2) {
+          const float p0 = (lg[et][x] == -INFINITY) ? 0.0f : __expf(lg[et][x] - m_new);
+          const float p1 = (lg[et][x + 1] == -INFINITY) ? 0.0f : __expf(lg[et][x + 1] - m_new);
+          psum += p0 + p1;
+          pw[2 * et + x / 2] = (uint32_t)f32_to_bf16(p0) | ((uint32_t)f32_to_bf16(p1) << 16);
+        }
+      psum = xor32_sum(xor16_sum(psum));
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+      pd_p[tt & 1][wave][lane] = pw;
+      pd_alpha[tt & 1][hl][wave] = alpha;  // the four lanes of a head store the same value
+    };
+    // After the barrier that publishes tile tt: bring the accumulators to the reference maxima of tile tt (rare:
+    // only when some head's reference max moved).
+    auto rescale = [&](int tt) {
+      const f32x4_t al = *(const f32x4_t*)&pd_alpha[tt & 1][hl][0];
+      if (__ballot(al[0] != 1.0f || al[1] != 1.0f || al[2] != 1.0f || al[3] != 1.0f)) {
+#pragma unroll
+        for (int hg = 0; hg < 4; ++hg)
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) acc[hg][dt] *= al[hg];
+      }
+    };
+    // O^T += V^T P^T of tile tp (slot S) for the wave's 128 channels and all 64 heads, P from buffer tp & 1.  When
+    // `am` is given, the softmax of the next tile runs between the MFMAs (its VALU work issues while they execute).
+    auto pv = [&](auto SC, auto WITH_SM, int tp, const f32x4_t (&am)[2][2], uint32_t valid, int tt) {
+      constexpr int S = decltype(SC)::value;
+      // lane 4 a + e of group g reads V[4 g + v][128 w + 16 dt + 4 a + e] (first half) and V[16 + 4 g + v][..]
+      const uint8_t* vp = pd_slot<S>() + (4 * grp + (hl >> 2)) * kPdRowB + 8 * (hl & 3) + 256 * wave;
+      bf16x8_t pb[4];
+#pragma unroll
+      for (int hg = 0; hg < 4; ++hg) pb[hg] = __builtin_bit_cast(bf16x8_t, pd_p[tp & 1][hg][lane]);
+      s16x4_t vb[2][8];
+      auto vload = [&](s16x4_t (&dst)[8], int j) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          dst[2 * u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vp + 32 * (4 * j + u)));
+          dst[2 * u + 1] =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vp + 16 * kPdRowB + 32 * (4 * j + u)));
+        }
+      };
+      vload(vb[0], 0);
+      vload(vb[1], 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const bf16x8_t av = __builtin_bit_cast(
+              bf16x8_t, __builtin_shufflevector(vb[j][2 * u], vb[j][2 * u + 1], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+          for (int hg = 0; hg < 4; ++hg)
+            acc[hg][4 * j + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[hg], acc[hg][4 * j + u], 0, 0, 0);
+        }
+      if constexpr (decltype(WITH_SM)::value) {
+        softmax(am, valid, tt);
+        // one MFMA, then up to five other ALU instructions, 32 times
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    using S3 = std::integral_constant<int, 3>;
+    // Tile tt sits in slot tt % 4.  Step tt (tt >= 1): QK of tile tt; PV of tile tt - 1 with the softmax of tile tt
+    // between its MFMAs; wait for this wave's loads of tile tt + 1 (tile tt + 2 may still be landing: 8 loads);
+    // barrier (tile tt + 1 has landed for every wave, P of tile tt is published, every wave is done with tile
+    // tt - 1); start tile tt + 3 in the slot tile tt - 1 used; rescale for tile tt.
+    auto step = [&](auto SQ, auto SP, int tt) {
+      f32x4_t am[2][2];
+      const uint32_t valid = qk(SQ, am, tt);
+      pv(SP, std::true_type{}, tt - 1, am, valid, tt);
+      __builtin_amdgcn_s_waitcnt(kWaitVm8);
+      pd_barrier();
+      issue(SP, tt + 3);
+      rescale(tt);
+    };
+    issue(S0{}, 0);
+    issue(S1{}, 1);
+    issue(S2{}, 2);
+    __builtin_amdgcn_s_waitcnt((1 << 14) | (0xF << 8) | (7 << 4));  // vmcnt(16): tile 0 has landed
+    pd_barrier();
+    {
+      f32x4_t am[2][2];
+      const uint32_t valid = qk(S0{}, am, 0);
+      softmax(am, valid, 0);
+      __builtin_amdgcn_s_waitcnt(kWaitVm8);
+      pd_barrier();
+      issue(S3{}, 3);
+      rescale(0);
+    }
+    // Steps 1 .. ntiles - 1 in whole groups of four, then the last 0..3 nested, so that every step is entered only
+    // from the step before it and the wait counts hold on every path; then PV of the last tile.
+    const int nfull = 1 + ((ntiles - 1) & ~3);
+    for (int tt = 1; tt < nfull; tt += 4) {
+      step(S1{}, S0{}, tt);
+      step(S2{}, S1{}, tt + 1);
+      step(S3{}, S2{}, tt + 2);
+      step(S0{}, S3{}, tt + 3);
+    }
+    if (nfull < ntiles) {
+      step(S1{}, S0{}, nfull);
+      if (nfull + 1 < ntiles) {
+        step(S2{}, S1{}, nfull + 1);
+        if (nfull + 2 < ntiles) step(S3{}, S2{}, nfull + 2);
       }
     }
-    if (a.lse && grp == 0) a.lse[((long long)b * a.Sq + r) * 64 + head] = (M == -INFINITY) ? -INFINITY : M + __logf(den);
-  } else {
-    float* po = a.part_o + (item * 64 + head) * 512;
+    const f32x4_t none[2][2] = {};
+    switch ((ntiles - 1) & 3) {
+      case 0: pv(S0{}, std::false_type{}, ntiles - 1, none, 0u, 0); break;
+      case 1: pv(S1{}, std::false_type{}, ntiles - 1, none, 0u, 0); break;
+      case 2: pv(S2{}, std::false_type{}, ntiles - 1, none, 0u, 0); break;
+      default: pv(S3{}, std::false_type{}, ntiles - 1, none, 0u, 0); break;
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // the trailing ring loads land before the workgroup can end
+  }
+
+  // finish: (max, sum) of every head through LDS, then each lane writes its 4 heads x 8 x 4 channels
+  const long long item = ((long long)b * a.Sq + r) * a.n_splits + split;
+  if (grp == 0) {
+    pd_ml[qhead][0] = m_run;
+    pd_ml[qhead][1] = l_run;
+  }
+  __syncthreads();
 #pragma unroll
-    for (int dt = 0; dt < 32; ++dt)
-      *(float4*)(po + 16 * dt + 4 * grp) = make_float4(acc_o[dt][0], acc_o[dt][1], acc_o[dt][2], acc_o[dt][3]);
-    if (grp == 0) {
-      a.part_ml[(item * 64 + head) * 2 + 0] = m_run;
-      a.part_ml[(item * 64 + head) * 2 + 1] = l_run;
+  for (int hg = 0; hg < 4; ++hg) {
+    const int head = 16 * hg + hl;
+    const float m = pd_ml[head][0], l = pd_ml[head][1];
+    if (a.n_splits == 1) {
+      const float z = a.sink[head];
+      const float M = fmaxf(m, z);
+      float den, f;
+      if (M == -INFINITY) {
+        den = 0.0f;
+        f = 0.0f;
+      } else {
+        den = ((z == -INFINITY) ? 0.0f : __expf(z - M)) + l * ((m == -INFINITY) ? 0.0f : __expf(m - M));
+        f = (m == -INFINITY) ? 0.0f : __expf(m - M) / den;
+      }
+      const long long ob = (((long long)b * a.Sq + r) * 64 + head) * 512 + 128 * wave + 4 * grp;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const f32x4_t o = acc[hg][dt] * f;
+        if (a.out_format == LCA_F32) {
+          *(float4*)((float*)a.out + ob + 16 * dt) = make_float4(o[0], o[1], o[2], o[3]);
+        } else {
+          uint2 w2;
+          w2.x = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
+          w2.y = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
+          *(uint2*)((uint16_t*)a.out + ob + 16 * dt) = w2;
+        }
+      }
+      if (a.lse && wave == 0 && grp == 0)
+        a.lse[((long long)b * a.Sq + r) * 64 + head] = (M == -INFINITY) ? -INFINITY : M + __logf(den);
+    } else {
+      float* po = a.part_o + (item * 64 + head) * 512 + 128 * wave + 4 * grp;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        *(float4*)(po + 16 * dt) = make_float4(acc[hg][dt][0], acc[hg][dt][1], acc[hg][dt][2], acc[hg][dt][3]);
+      if (wave == 0 && grp == 0) {
+        a.part_ml[(item * 64 + head) * 2 + 0] = m;
+        a.part_ml[(item * 64 + head) * 2 + 1] = l;
+      }
     }
   }
 }
@@ -1211,7 +1564,9 @@ hipError_t launch_attn(AttnArgs a, hipStream_t st, hipEvent_t ev_begin, hipEvent
       if (e != hipSuccess) return e;
       g_attn_attr[dev] = true;
     }
-    if (a.comp.format == LCA_BF16)
+    if (a.comp.format == LCA_BF16 && a.raw.cap * 1024 < (1ll << 31) && a.comp.cap * 1024 < (1ll << 31))
+      hipLaunchKernelGGL(attn_pf_kernel, grid, dim3(kAttnThreads), 0, st, a);
+    else if (a.comp.format == LCA_BF16)
       hipLaunchKernelGGL(attn_mfma_kernel<LCA_BF16>, grid, dim3(kAttnThreads), kMfmaLds, st, a);
     else
       hipLaunchKernelGGL(attn_mfma_kernel<LCA_MIXED_FP8>, grid, dim3(kAttnThreads), kMfmaLds, st, a);
