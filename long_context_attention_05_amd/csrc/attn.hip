@@ -338,7 +338,6 @@ __global__ __launch_bounds__(kAttnThreads) void attn_mfma_kernel(AttnArgs a) {
 //     (v >= 4): the pair of 16-entry halves that the S^T accumulators and the two transposing reads already hold.
 //   One barrier per tile: before it a wave has scored its tile, published P and waited for its share of the next
 //   tile's loads; after it the freed ring slot is refilled and the PV product runs.
-constexpr int kPdSlots = 4;
 constexpr int kPdRowB = 1040;                    // LDS bytes per tile row
 constexpr int kPdTileB = kPfTE * kPdRowB;        // 33280
 __shared__ __attribute__((aligned(16))) uint8_t pd_slot0[kPdTileB];

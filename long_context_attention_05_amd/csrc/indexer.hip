@@ -258,23 +258,40 @@ __global__ __launch_bounds__(256) void idx_score_mfma(IdxArgs a, int qpb) {
 // counts into the row's histogram, zeroed before the launch.  The select that follows reads it instead of making
 // its own first pass over the keys.
 
-__device__ __forceinline__ float head_tree(const f32x4_t (&acc)[4], const float (&wv)[4][4]) {
-  float l1[2][4], l2[4], l3[4], l4[4];
+// In-lane part of the tree for one 16-key group: v[r] = ((w relu)(T=0) + (T=2)) + ((T=1) + (T=3)) for the lane's
+// heads 4 (l / 16) + r (+ 16 T).  ReLU is one integer max of the bit pattern with 0: non-negative floats order like
+// their bit patterns and every negative one (-0 included) has the sign bit set, so the result equals max(x, 0)
+// without the float max's NaN canonicalization.
+__device__ __forceinline__ void head_partial(const f32x4_t (&acc)[4], const float (&wv)[4][4], float (&v)[4]) {
 #pragma unroll
-  for (int T = 0; T < 2; ++T)
+  for (int r = 0; r < 4; ++r) {
+    float p[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float p0 = wv[T][r] * fmaxf(acc[T][r], 0.0f);
-      const float p1 = wv[T + 2][r] * fmaxf(acc[T + 2][r], 0.0f);
-      l1[T][r] = p0 + p1;
-    }
+    for (int T = 0; T < 4; ++T) p[T] = wv[T][r] * __int_as_float(max(__float_as_int(acc[T][r]), 0));
+    v[r] = (p[0] + p[2]) + (p[1] + p[3]);
+  }
+}
+
+// Cross-lane part for four groups at once, as a reduce-scatter: h+8 pairs lane rows g and g + 2 (lanes l, l ^ 32),
+// h+4 pairs rows g and g + 1 (l, l ^ 16), then h+2 and h+1 in-lane.  permlane32_swap(A, B) returns (A.lo, B.lo) and
+// (A.hi, B.hi), so one swap and one add leave group 0 (2)'s pair sums in the low (high) half; permlane16_swap does
+// the same for rows 0/1 and 2/3.  Row g of the wave ends with group g's four partial sums, and the lane returns the
+// score of group g, key l % 16.  The pairs are those of the fixed halving tree (fp32 addition is commutative).
+__device__ __forceinline__ float head_cross4(const float (&v)[4][4]) {
+  float s02[4], s13[4], t[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) l2[r] = l1[0][r] + l1[1][r];
+  for (int r = 0; r < 4; ++r) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[0][r]), __float_as_uint(v[2][r]), false, false);
+    s02[r] = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[1][r]), __float_as_uint(v[3][r]), false, false);
+    s13[r] = __uint_as_float(c[0]) + __uint_as_float(c[1]);
+  }
 #pragma unroll
-  for (int r = 0; r < 4; ++r) l3[r] = xor32_sum(l2[r]);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) l4[r] = xor16_sum(l3[r]);
-  return (l4[0] + l4[2]) + (l4[1] + l4[3]);
+  for (int r = 0; r < 4; ++r) {
+    const auto d = __builtin_amdgcn_permlane16_swap(__float_as_uint(s02[r]), __float_as_uint(s13[r]), false, false);
+    t[r] = __uint_as_float(d[0]) + __uint_as_float(d[1]);
+  }
+  return (t[0] + t[2]) + (t[1] + t[3]);
 }
 
 __device__ __forceinline__ void flush_hist(const int* hist_s, int* gh) {
@@ -285,8 +302,8 @@ __device__ __forceinline__ void flush_hist(const int* hist_s, int* gh) {
   }
 }
 
-// Scores of four 16-key groups (every lane of a key holds its score after the head tree): lane (g, col) takes
-// group q0 + g, so that one store writes 64 keys.  The store is unconditional -- a lane past the range holds the
+// Scores of four 16-key groups (lane (g, col) holds group q0 + g's score after the head tree), so that one store
+// writes 64 keys.  The store is unconditional -- a lane past the range holds the
 // score of the clamped key k1 - 1 and writes that same value there -- and is issued after the next stage's loads,
 // so no branch or register reuse separates the loads in flight from their waits.
 struct KeyOut {
@@ -294,8 +311,7 @@ struct KeyOut {
   int e;
 };
 
-__device__ __forceinline__ KeyOut pick_key4(int gbase, int g, const float (&sc)[4]) {
-  const float s = g == 0 ? sc[0] : g == 1 ? sc[1] : g == 2 ? sc[2] : sc[3];
+__device__ __forceinline__ KeyOut lane_key(int gbase, int g, float s) {
   return KeyOut{score_key(s), gbase + 16 * g + (int)(threadIdx.x & 15)};
 }
 
@@ -309,7 +325,7 @@ __device__ __forceinline__ void store_key(const IdxArgs& a, int b, int k1, const
 
 // ---- bf16: v_mfma_f32_16x16x32_bf16, A = queries (lane: head 16T + l % 16, channels 8 (l / 16) + 32 s + v),
 //      B = keys (lane: key l % 16, the same channels), i.e. 16 bytes at 16 (l / 16) + 64 s of the 256-byte row.
-constexpr int kBfGroups = 4;  // 16-key groups per wave per stage (16 KB per wave in flight)
+constexpr int kBfGroups = 4;  // 16-key groups per wave per stage (16 KB per wave in flight); the tree takes 4
 
 struct BfStage {
   uint4 c[kBfGroups][4];
@@ -368,7 +384,7 @@ __global__ __launch_bounds__(256, 2) void idx_score_decode_bf16(IdxArgs a) {
     }
     if (st > 0) store_key(a, b, k1, pend, hist_s, hist);
     const BfStage& C = S[st & 1];
-    float sc[kBfGroups];
+    float v[kBfGroups][4];
 #pragma unroll
     for (int j = 0; j < kBfGroups; ++j) {
       f32x4_t acc[4];
@@ -380,124 +396,257 @@ __global__ __launch_bounds__(256, 2) void idx_score_decode_bf16(IdxArgs a) {
 #pragma unroll
         for (int T = 0; T < 4; ++T) acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[T][s], kv, acc[T], 0, 0, 0);
       }
-      sc[j] = head_tree(acc, wv);
+      head_partial(acc, wv, v[j]);
     }
-    pend = pick_key4(kbase, g, sc);
+    pend = lane_key(kbase, g, head_cross4(v));
   }
   store_key(a, b, k1, pend, hist_s, hist);
   if (hist) flush_hist(hist_s, a.sel_state + (long long)b * kSelStateInts);
 }
 
-// ---- fp4: v_mfma_scale_f32_16x16x128_f8f6f4 with both operands in fp4 e2m1 applies one E8M0 scale per lane to
-// the lane's 32 contraction slots (A: lane l holds row l % 16, slots 32 (l / 16) .. + 31; B: column l % 16, same
-// slots).  The cache scales each 16 elements, so each lane fills the first 16 slots of its block with one
-// 16-element group and the other 16 with zeros; two instructions (h = 0, 1) cover the 8 groups of a 128-dim row:
-// block b of instruction h holds group 2b + h.  A lane's operand bytes are 16 bytes at 16 (l / 16) of the key's
-// 64-byte code row (groups 2g, 2g + 1) and the two scale bytes at 2 (l / 16) of its 8-byte scale row.  Products of
-// fp4 values and their block sums are exact, scaled by powers of two, so the per-head dots equal the exact ones
-// whenever they fit fp32 -- the fixed head-reduction order then makes the scores bit-reproducible.
 typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8_t;
 
-__device__ __forceinline__ i32x8_t fp4_operand(uint32_t lo, uint32_t hi) {
-  i32x8_t v = {(int)lo, (int)hi, 0, 0, 0, 0, 0, 0};
-  return v;
+// ---- fp4 decode scoring with the keys streamed into an LDS ring: one workgroup of eight waves per CU takes NST
+// stages of 512 keys.  A stage's codes (32 KB) and scales (4 KB) travel from memory straight into a ring slot with
+// buffer loads into LDS (no registers hold data in flight), three stages in flight while one is scored; each slot is
+// its own pair of LDS variables and the stage loop is fully unrolled, so every wait is a count fixed at compile
+// time.  Each wave moves and scores its own 64 keys of a stage, so waves never wait for each other.  Code rows are
+// stored with their four 16-byte chunks XOR-swizzled by bits 2..3 of the key's position in its 16-key group, which
+// makes the operand reads bank-conflict free.
+//
+// Scoring runs on v_mfma_scale_f32_32x32x64_f8f6f4, which takes fp4 operands at twice the rate of the 16x16x128
+// form: A = 32 heads (lane l: head l % 32, contraction slots 32 (l / 32) .. + 31), B = 32 keys (lane l: key l % 32,
+// the same slots), one E8M0 scale per lane applied to the lane's 32 slots.  The cache scales each 16 elements, so
+// lane half hh = l / 32 takes code chunk c = 2 i + hh (groups 2c, 2c + 1) in instruction pair i; the key operand is
+// the chunk as loaded and the query operand keeps one of its two groups (h = 0, 1) with that group's scales and
+// zeros the other 16 slots, whose products are exact zeros (e2m1 has no infinities or NaNs).  Eight instructions
+// (2 head tiles x 2 chunk pairs x 2 groups) give the 64 x 32 dots.  Products of fp4 values and their block sums are
+// exact, scaled by powers of two, so the per-head dots equal the exact ones whenever they fit fp32 -- the fixed
+// head-reduction order then makes the scores bit-reproducible.  Lane l, register k of the 32x32 result holds head
+// 32 T + 8 (k / 4) + 4 hh + k % 4 for key l % 32: the tree's h+32, h+16, h+8 steps run in lane, h+4 and h+2 across
+// the lane halves, h+1 in lane -- the same pairs as the 16x16 kernels.
+constexpr int kF4rWaves = 8;
+constexpr int kF4rStage = 64 * kF4rWaves;  // keys per stage
+constexpr int kF4rCodeB = kF4rStage * 64;  // 32 KB
+constexpr int kF4rScaleB = kF4rStage * 8;  // 4 KB
+__shared__ __attribute__((aligned(16))) uint8_t f4r_c0[kF4rCodeB];
+__shared__ __attribute__((aligned(16))) uint8_t f4r_c1[kF4rCodeB];
+__shared__ __attribute__((aligned(16))) uint8_t f4r_c2[kF4rCodeB];
+__shared__ __attribute__((aligned(16))) uint8_t f4r_c3[kF4rCodeB];
+__shared__ __attribute__((aligned(16))) uint8_t f4r_s0[kF4rScaleB];
+__shared__ __attribute__((aligned(16))) uint8_t f4r_s1[kF4rScaleB];
+__shared__ __attribute__((aligned(16))) uint8_t f4r_s2[kF4rScaleB];
+__shared__ __attribute__((aligned(16))) uint8_t f4r_s3[kF4rScaleB];
+__shared__ int f4r_hist[kSelBins];
+
+template <int S>
+__device__ __forceinline__ uint8_t* f4r_codes() {
+  if constexpr (S == 0) return f4r_c0;
+  else if constexpr (S == 1) return f4r_c1;
+  else if constexpr (S == 2) return f4r_c2;
+  else return f4r_c3;
+}
+template <int S>
+__device__ __forceinline__ uint8_t* f4r_scales() {
+  if constexpr (S == 0) return f4r_s0;
+  else if constexpr (S == 1) return f4r_s1;
+  else if constexpr (S == 2) return f4r_s2;
+  else return f4r_s3;
 }
 
-constexpr int kF4Groups = 8;  // 16-key groups per wave per stage (9 KB per wave in flight)
+typedef __attribute__((address_space(3))) void idx_lds_void_t;
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+constexpr int kIdxBufWord3 = 0x00020000;  // buffer descriptor word 3: raw untyped loads
 
-struct F4Stage {
-  uint4 c[kF4Groups];
-  uint32_t s[kF4Groups];
-};
+// s_waitcnt immediate for vmcnt(n) with the other counters untouched
+__host__ __device__ constexpr int vm_wait_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (0xF << 8) | (7 << 4); }
 
-__device__ __forceinline__ void f4_load_stage(F4Stage& S, const uint8_t* codes, const uint8_t* scales, int kbase,
-                                              int klast, int lane) {
-  const int g = lane >> 4, col = lane & 15;
-#pragma unroll
-  for (int j = 0; j < kF4Groups; ++j) {
-    const int e = min(kbase + 16 * j + col, klast);
-    S.c[j] = *(const uint4*)(codes + (long long)e * 64 + 16 * g);
-    S.s[j] = *(const uint16_t*)(scales + (long long)e * 8 + 2 * g);
+// Memory operations a wave has issued after the loads of stage st when step st waits for them: the loads of the
+// (at most two) stages after it and the key stores of the steps since they were issued (6 loads per stage: 4 code
+// rows of 1 KB and 2 scale rows of 256 bytes; 1 store per step).
+__host__ __device__ constexpr int f4r_wait_count(int st, int nst) {
+  const int later = (st + 2 < nst - 1 ? st + 2 : nst - 1) - st;
+  const int stores = st - (st - 3 > 0 ? st - 3 : 0);
+  return 6 * later + stores;
+}
+
+// Calls f(integral_constant<int, ST>) for ST = ST0 .. NST - 1 in order (a loop whose index is a constant).
+template <int ST, int NST, class F>
+__device__ __forceinline__ void unroll_steps(F& f) {
+  if constexpr (ST < NST) {
+    f(std::integral_constant<int, ST>{});
+    unroll_steps<ST + 1, NST>(f);
   }
+}
+
+// Score of key l % 32 from the 32x32 results of the two head tiles (every lane of the key returns it).
+__device__ __forceinline__ float head_tree32(const f32x16_t (&acc)[2], const float (&wv)[2][16]) {
+  float a[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const float p0 = wv[0][k] * __int_as_float(max(__float_as_int(acc[0][k]), 0));
+    const float p1 = wv[1][k] * __int_as_float(max(__float_as_int(acc[1][k]), 0));
+    a[k] = p0 + p1;  // h+32
+  }
+  float c[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) c[r] = (a[r] + a[r + 8]) + (a[r + 4] + a[r + 12]);  // h+16, then h+8
+  // h+4 across the lane halves, scattered: the low half keeps head classes 0 and 1, the high half 2 and 3
+  const auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(c[0]), __float_as_uint(c[2]), false, false);
+  const auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(c[1]), __float_as_uint(c[3]), false, false);
+  const float d02 = __uint_as_float(s02[0]) + __uint_as_float(s02[1]);
+  const float d13 = __uint_as_float(s13[0]) + __uint_as_float(s13[1]);
+  return xor32_sum(d02) + xor32_sum(d13);  // h+2 across the halves, then h+1
 }
 
 template <int NST>
-__global__ __launch_bounds__(256, 2) void idx_score_decode_fp4(IdxArgs a) {
+__global__ __launch_bounds__(kF4rWaves * 64) void idx_score_decode_fp4_ring(IdxArgs a) {
 #pragma clang fp contract(off)
-  __shared__ int hist_s[kSelBins];
-  constexpr int KPW = 16 * kF4Groups;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int g = lane >> 4, col = lane & 15;
+  const int col = lane & 31, hh = lane >> 5;
   const int b = blockIdx.y;
   const int nvis = nvis_of(a.q_start, a.m, a.N);
-  const int k0 = blockIdx.x * (NST * 4 * KPW);
-  const int k1 = min(k0 + NST * 4 * KPW, nvis);
-  if (k0 >= k1) return;
+  const int k0 = blockIdx.x * (NST * kF4rStage);
+  const int k1 = min(k0 + NST * kF4rStage, nvis);
+  if (k0 >= k1) return;  // block-uniform
   const bool hist = a.sel_state != nullptr;
-  if (hist)
-    for (int i = threadIdx.x; i < kSelBins; i += blockDim.x) hist_s[i] = 0;
-  const uint8_t* codes = (const uint8_t*)a.k.data + (long long)b * a.k.cap * 64;
-  const uint8_t* scales = (const uint8_t*)a.k.scale + (long long)b * a.k.cap * 8;
+  for (int i = threadIdx.x; i < kSelBins; i += blockDim.x) f4r_hist[i] = 0;
 
-  F4Stage S[2];
-  f4_load_stage(S[0], codes, scales, k0 + wave * KPW, k1 - 1, lane);
-  // query operands: M-tile T = heads 16T .. 16T + 15; lane holds head 16T + col, groups 2g and 2g + 1
-  uint32_t qc[4][4];  // [T][0..1] = group 2g codes, [2..3] = group 2g + 1 codes
-  int qs[4][2];
-  float wv[4][4];
+  // query: head tile T = heads 32 T .. 32 T + 31, lane head 32 T + col; chunks hh and 2 + hh of its code row and the
+  // matching scale bytes 2 hh, 2 hh + 1, 4 + 2 hh, 5 + 2 hh.  The raw loads go first and the operands are built after
+  // the ring's first loads are issued, so that nothing waits for the queries before the ring starts.
+  uint4 qraw[2][2];
+  uint2 sraw[2];
+  float wv[2][16];
 #pragma unroll
-  for (int T = 0; T < 4; ++T) {
-    const long long row = (long long)b * 64 + 16 * T + col;
-    const uint4 c = *(const uint4*)((const uint8_t*)a.q.data + row * 64 + 16 * g);
-    qc[T][0] = c.x;
-    qc[T][1] = c.y;
-    qc[T][2] = c.z;
-    qc[T][3] = c.w;
-    const uint32_t s2 = *(const uint16_t*)((const uint8_t*)a.q.scale + row * 8 + 2 * g);
-    qs[T][0] = (int)(s2 & 255u);
-    qs[T][1] = (int)(s2 >> 8);
+  for (int T = 0; T < 2; ++T) {
+    const long long row = (long long)b * 64 + 32 * T + col;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) wv[T][r] = a.w[(long long)b * 64 + 16 * T + 4 * g + r];
+    for (int i = 0; i < 2; ++i) qraw[T][i] = *(const uint4*)((const uint8_t*)a.q.data + row * 64 + 16 * (2 * i + hh));
+    sraw[T] = *(const uint2*)((const uint8_t*)a.q.scale + row * 8);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) wv[T][k] = a.w[(long long)b * 64 + 32 * T + 8 * (k >> 2) + 4 * hh + (k & 3)];
   }
-  if (hist) __syncthreads();  // histogram zeroed before any update
+  __builtin_amdgcn_sched_barrier(0);
+  i32x8_t qop[2][2][2];
+  int qs[2][2][2];
 
-  // straight-line stages as in the bf16 kernel; a stage is two batches of four groups, and each batch's keys are
-  // stored once the next batch (or the next stage's loads) is under way
-  KeyOut pend{0u, k1};
+  // buffer descriptors over the workgroup's own keys [k0, k1): offsets stay small whatever the cache size, and the
+  // range check covers exactly the keys the workgroup may read
+  const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const uint8_t*)a.k.data + ((long long)b * a.k.cap + k0) * 64), 0, (k1 - k0) * 64, kIdxBufWord3);
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const uint8_t*)a.k.scale + ((long long)b * a.k.cap + k0) * 8), 0, (k1 - k0) * 8, kIdxBufWord3);
+  // stage st into slot S: code instruction i of wave w moves keys 64 w + 16 i .. + 15 (lane l: key + l / 4, chunk
+  // position l % 4 holding code chunk (l % 4) ^ (l / 16)); scale instruction i moves 32 keys' scale rows.  Keys past
+  // k1 repeat key k1 - 1.
+  auto issue = [&](auto SC, int st) {
+    constexpr int S = decltype(SC)::value;
+    const int kst = st * kF4rStage;  // relative to k0
 #pragma unroll
-  for (int st = 0; st < NST; ++st) {
-    const int kbase = k0 + st * 4 * KPW + wave * KPW;
-    if (st + 1 < NST) {
-      f4_load_stage(S[(st + 1) & 1], codes, scales, kbase + 4 * KPW, k1 - 1, lane);
-      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the scoring
+    for (int i = 0; i < 4; ++i) {
+      const int key = min(kst + 64 * wave + 16 * i + (lane >> 2), k1 - k0 - 1);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(crs, (idx_lds_void_t*)(f4r_codes<S>() + (64 * wave + 16 * i) * 64), 16,
+                                               key * 64 + 16 * ((lane & 3) ^ (lane >> 4)), 0, 0, 0);
     }
-    const F4Stage& C = S[st & 1];
 #pragma unroll
-    for (int q = 0; q < kF4Groups / 4; ++q) {
-      if (st > 0 || q > 0) store_key(a, b, k1, pend, hist_s, hist);
-      float sc[4];
+    for (int i = 0; i < 2; ++i) {
+      const int key = min(kst + 64 * wave + 32 * i + (lane >> 1), k1 - k0 - 1);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, (idx_lds_void_t*)(f4r_scales<S>() + (64 * wave + 32 * i) * 8), 4,
+                                               key * 8 + 4 * (lane & 1), 0, 0, 0);
+    }
+  };
+  // 64 x 32 dots of the wave's key tile u (keys 64 w + 32 u + col of stage slot S)
+  auto dots = [&](auto SC, int u, f32x16_t (&acc)[2]) {
+    constexpr int S = decltype(SC)::value;
+    const int kl = 64 * wave + 32 * u + col;
+    const uint8_t* cb = f4r_codes<S>() + kl * 64;
+    const int sw = (kl >> 2) & 3;
+    const uint2 s8 = *(const uint2*)(f4r_scales<S>() + kl * 8);
+    i32x8_t kop[2];
+    int ks[2][2];
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int j = 4 * q + jj;
-        const uint4 kc = C.c[j];
-        const i32x8_t kop0 = fp4_operand(kc.x, kc.y), kop1 = fp4_operand(kc.z, kc.w);
-        const int ks0 = (int)(C.s[j] & 255u), ks1 = (int)(C.s[j] >> 8);
-        f32x4_t acc[4];
+    for (int i = 0; i < 2; ++i) {
+      const u32x4_t kc = *(const u32x4_t*)(cb + 16 * ((2 * i + hh) ^ sw));
+      kop[i] = i32x8_t{(int)kc[0], (int)kc[1], (int)kc[2], (int)kc[3], 0, 0, 0, 0};
+      const uint32_t sword = i == 0 ? s8.x : s8.y;  // bytes 4i .. 4i + 3
+      ks[i][0] = (int)((sword >> (16 * hh)) & 255u);
+      ks[i][1] = (int)((sword >> (16 * hh + 8)) & 255u);
+    }
 #pragma unroll
-        for (int T = 0; T < 4; ++T) {
-          acc[T] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-          acc[T] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fp4_operand(qc[T][0], qc[T][1]), kop0, acc[T], 4,
-                                                                    4, 0, qs[T][0], 0, ks0);
-          acc[T] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fp4_operand(qc[T][2], qc[T][3]), kop1, acc[T], 4,
-                                                                    4, 0, qs[T][1], 0, ks1);
-        }
-        sc[jj] = head_tree(acc, wv);
-      }
-      pend = pick_key4(kbase + 64 * q, g, sc);
+    for (int T = 0; T < 2; ++T) {
+      acc[T] = f32x16_t{};
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          acc[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qop[T][i][h], kop[i], acc[T], 4, 4, 0,
+                                                                   qs[T][i][h], 0, ks[i][h]);
+    }
+  };
+  // lane (col, hh) returns the key of tile u's key col (both halves hold it)
+  auto score = [&](auto SC, int st) -> uint2 {
+    f32x16_t acc0[2], acc1[2];
+    dots(SC, 0, acc0);
+    __builtin_amdgcn_sched_barrier(0);
+    dots(SC, 1, acc1);
+    const float s0 = head_tree32(acc0, wv);
+    // the second tile's MFMAs run while the first tile's tree issues between them
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const float s1 = head_tree32(acc1, wv);
+    (void)st;
+    return uint2{score_key(s0), score_key(s1)};
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  // the query loads above are older than the ring's, so the first wait covers them
+  issue(S0{}, 0);
+  if constexpr (NST > 1) issue(S1{}, 1);
+  if constexpr (NST > 2) issue(S2{}, 2);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int T = 0; T < 2; ++T)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint4 c = qraw[T][i];
+      qop[T][i][0] = i32x8_t{(int)c.x, (int)c.y, 0, 0, 0, 0, 0, 0};
+      qop[T][i][1] = i32x8_t{0, 0, (int)c.z, (int)c.w, 0, 0, 0, 0};
+      const uint32_t sword = i == 0 ? sraw[T].x : sraw[T].y;
+      qs[T][i][0] = (int)((sword >> (16 * hh)) & 255u);
+      qs[T][i][1] = (int)((sword >> (16 * hh + 8)) & 255u);
+    }
+
+  // Stage st sits in slot st % 4.  A wave loads exactly the keys it scores, so the ring needs no barrier: step st
+  // waits for this wave's own loads of stage st, starts stage st + 3 in the slot this wave finished with in step
+  // st - 1, scores and stores.  The histogram counts wait until the ring is drained: an LDS atomic while ring loads
+  // are in flight would make the compiler wait for all of them.
+  uint2 kept[NST];
+  auto step = [&](auto STC) {
+    constexpr int st = decltype(STC)::value;
+    __builtin_amdgcn_s_waitcnt(vm_wait_imm(f4r_wait_count(st, NST)));
+    asm volatile("" ::: "memory");
+    if constexpr (st + 3 < NST) issue(std::integral_constant<int, (st + 3) % 4>{}, st + 3);
+    kept[st] = score(std::integral_constant<int, st % 4>{}, st);
+    // lane (col, hh) stores tile hh's key col: 64 keys per store
+    const int e = k0 + st * kF4rStage + 64 * wave + 32 * hh + col;
+    a.keys[(long long)b * a.N + min(e, k1 - 1)] = hh ? kept[st].y : kept[st].x;
+  };
+  unroll_steps<0, NST>(step);
+  if (hist) {
+    __syncthreads();  // every wave has zeroed its part of the histogram
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      const int e = k0 + st * kF4rStage + 64 * wave + 32 * hh + col;
+      if (e < k1) atomicAdd(&f4r_hist[(hh ? kept[st].y : kept[st].x) >> 21], 1);
     }
   }
-  store_key(a, b, k1, pend, hist_s, hist);
-  if (hist) flush_hist(hist_s, a.sel_state + (long long)b * kSelStateInts);
+  if (hist) flush_hist(f4r_hist, a.sel_state + (long long)b * kSelStateInts);
 }
 
 bool indexer_uses_decode_kernel(int B, int Sq, int HI, int DI, int q_format, int k_format) {
@@ -512,22 +661,28 @@ hipError_t launch_indexer_scores(const IdxArgs& a, hipStream_t st) {
   const bool mfma = a.HI == 64 && a.DI == 128 && a.q.format == a.k.format &&
                     (a.q.format == LCA_BF16 || a.q.format == LCA_FP4);
   if (indexer_uses_decode_kernel(a.B, a.Sq, a.HI, a.DI, a.q.format, a.k.format)) {
+    const bool fp4 = a.q.format == LCA_FP4;
+    if (fp4) {
+      // one workgroup per CU where the context allows: the most stages per workgroup that still leave 256
+      int nst = 8;
+      while (nst > 1 && (long long)a.B * ((nvis_max + nst * kF4rStage - 1) / (nst * kF4rStage)) < 256) nst >>= 1;
+      const dim3 grid((unsigned)((nvis_max + nst * kF4rStage - 1) / (nst * kF4rStage)), (unsigned)a.B);
+      const dim3 block(kF4rWaves * 64);
+      if (nst == 8) hipLaunchKernelGGL(idx_score_decode_fp4_ring<8>, grid, block, 0, st, a);
+      else if (nst == 4) hipLaunchKernelGGL(idx_score_decode_fp4_ring<4>, grid, block, 0, st, a);
+      else if (nst == 2) hipLaunchKernelGGL(idx_score_decode_fp4_ring<2>, grid, block, 0, st, a);
+      else hipLaunchKernelGGL(idx_score_decode_fp4_ring<1>, grid, block, 0, st, a);
+      return hipGetLastError();
+    }
     // a fixed key range per workgroup (NST stages of 4 waves x KPW keys), the grid grows with the context; fewer
     // stages when that leaves fewer than about two workgroups per CU
-    const bool fp4 = a.q.format == LCA_FP4;
-    const int kpw = fp4 ? 16 * kF4Groups : 16 * kBfGroups;
+    const int kpw = 16 * kBfGroups;
     int nst = 4;
     while (nst > 1 && (long long)a.B * ((nvis_max + nst * 4 * kpw - 1) / (nst * 4 * kpw)) < 512) nst >>= 1;
     const dim3 grid((unsigned)((nvis_max + nst * 4 * kpw - 1) / (nst * 4 * kpw)), (unsigned)a.B);
-    if (fp4) {
-      if (nst == 4) hipLaunchKernelGGL(idx_score_decode_fp4<4>, grid, dim3(256), 0, st, a);
-      else if (nst == 2) hipLaunchKernelGGL(idx_score_decode_fp4<2>, grid, dim3(256), 0, st, a);
-      else hipLaunchKernelGGL(idx_score_decode_fp4<1>, grid, dim3(256), 0, st, a);
-    } else {
-      if (nst == 4) hipLaunchKernelGGL(idx_score_decode_bf16<4>, grid, dim3(256), 0, st, a);
-      else if (nst == 2) hipLaunchKernelGGL(idx_score_decode_bf16<2>, grid, dim3(256), 0, st, a);
-      else hipLaunchKernelGGL(idx_score_decode_bf16<1>, grid, dim3(256), 0, st, a);
-    }
+    if (nst == 4) hipLaunchKernelGGL(idx_score_decode_bf16<4>, grid, dim3(256), 0, st, a);
+    else if (nst == 2) hipLaunchKernelGGL(idx_score_decode_bf16<2>, grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL(idx_score_decode_bf16<1>, grid, dim3(256), 0, st, a);
   } else if (mfma) {
     const int qpb = a.Sq >= 16 ? 16 : a.Sq;
     dim3 grid((unsigned)((nvis_max + kMfmaEntriesPerBlock - 1) / kMfmaEntriesPerBlock),
