@@ -248,7 +248,7 @@ void lca_set_attn_events(void* ev_begin, void* ev_end) {
 struct IdxWs {
   size_t keys, state, counts, cand, total;
 };
-constexpr long long kMaxMultiN = 256LL * kSliceKeys;  // slices per row <= 256
+constexpr long long kMaxMultiN = 1024LL * kSliceKeys;  // slices per row <= 1024, one per finishing thread
 
 IdxWs idx_ws_layout(int B, int Sq, int N) {
   IdxWs l{};

@@ -354,15 +354,21 @@ __device__ __forceinline__ int cand_segment(const int* seg_off, int nseg, int j)
   return lo;
 }
 
-constexpr size_t kFinishLds = (size_t)kCandCap * 8 + (size_t)kCandCap * 2;  // candidates + segment map
+// The finishing workgroup: 1024 threads, so that one round of loads gathers up to kCandCap candidates (6 per thread)
+// and one round of the ordered compaction writes them; the pass-3 histogram is counted while the candidates are in
+// registers.
+constexpr int kFinThreads = 1024;
+constexpr int kFinPer = kCandCap / kFinThreads;  // 6
+constexpr int kFinMaxSlices = kFinThreads;       // one slice count per thread
+constexpr size_t kFinishLds = (size_t)kCandCap * 8;
 
-__global__ __launch_bounds__(kMbThreads) void topk_finish_kernel(SelArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint32_t mb_lds[];  // the row's candidates, then the segment map
-  __shared__ int hist[kSelBins];
-  __shared__ int hist2[kSelBins];
-  __shared__ int seg_off[257];
-  __shared__ int wsum[kMbThreads / 64];
-  __shared__ int sh[4];
+__global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(SelArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t mb_lds[];  // the row's candidates (when they fit)
+  __shared__ int hist[kSelBins];   // pass 1, then pass 3
+  __shared__ int hist2[kSelBins];  // pass 2
+  __shared__ int seg_off[kFinMaxSlices];
+  __shared__ int wsum[kSelWaves];
+  __shared__ int sh[2];
   const int row = blockIdx.x, tid = threadIdx.x;
   const int nvis = sel_row_nvis(a, row);
   const int k = a.k;
@@ -370,106 +376,95 @@ __global__ __launch_bounds__(kMbThreads) void topk_finish_kernel(SelArgs a) {
   float* sout = a.score_out ? a.score_out + (long long)row * k : nullptr;
   if (nvis <= k) {  // every visible entry is selected
     const uint32_t* kg = a.keys + (long long)row * a.N;
-    for (int j = tid; j < k; j += kMbThreads) {
+    for (int j = tid; j < k; j += kFinThreads) {
       out[j] = j < nvis ? j : -1;
       if (sout) sout[j] = j < nvis ? key_score(kg[j]) : -INFINITY;
     }
     return;
   }
-  const int P = (nvis + kSliceKeys - 1) / kSliceKeys;
+  const int P = (nvis + kSliceKeys - 1) / kSliceKeys;  // <= kFinMaxSlices (checked at launch)
   const int slots = (a.N + kSliceKeys - 1) / kSliceKeys;
   const int* gh = a.sel_state + (long long)row * kSelStateInts;
   // segment lengths and both histograms, all loads in flight together
   const int c = tid < P ? a.counts[(long long)row * slots + tid] : 0;
-  int hv[kSelBins / kMbThreads], hv2[kSelBins / kMbThreads];
+  int hv[kSelBins / kFinThreads], hv2[kSelBins / kFinThreads];
 #pragma unroll
-  for (int u = 0; u < kSelBins / kMbThreads; ++u) {
-    hv[u] = gh[tid + kMbThreads * u];
-    hv2[u] = gh[kSelBins + tid + kMbThreads * u];
+  for (int u = 0; u < kSelBins / kFinThreads; ++u) {
+    hv[u] = gh[tid + kFinThreads * u];
+    hv2[u] = gh[kSelBins + tid + kFinThreads * u];
   }
 #pragma unroll
-  for (int u = 0; u < kSelBins / kMbThreads; ++u) {
-    hist[tid + kMbThreads * u] = hv[u];
-    hist2[tid + kMbThreads * u] = hv2[u];
+  for (int u = 0; u < kSelBins / kFinThreads; ++u) {
+    hist[tid + kFinThreads * u] = hv[u];
+    hist2[tid + kFinThreads * u] = hv2[u];
   }
   int total;
-  const int off = block256_excl_scan(c, wsum, total);  // (its barriers also publish both histograms)
+  const int off = block_excl_scan(c, wsum, total);  // (its barriers also publish both histograms)
   if (tid < P) seg_off[tid] = off;
   // passes 1 and 2 from the histograms
-  int above;
-  const int b1 = find_bin256(hist, k, wsum, sh, &above);
-  int need = k - above;
-  const int b2 = find_bin256(hist2, need, wsum, sh, &above);
-  need -= above;
+  const int b1 = find_bin(hist, k, wsum, sh);
+  int need = k - sh[1];
+  const int b2 = find_bin(hist2, need, wsum, sh);
+  need -= sh[1];
   const uint32_t prefix12 = ((uint32_t)b1 << 21) | ((uint32_t)b2 << 10);
+#pragma unroll
+  for (int u = 0; u < kSelBins / kFinThreads; ++u) hist[tid + kFinThreads * u] = 0;  // pass 3 counts
+  __syncthreads();
 
   const uint2* cseg = a.cand + (long long)row * a.N;
   const bool in_lds = total <= kCandCap;
   uint2* cl = (uint2*)mb_lds;
-  uint16_t* seg_of = (uint16_t*)(mb_lds + 2 * kCandCap);  // candidate -> its segment
-  if (in_lds) {
-    if (tid < P)
-      for (int i = 0; i < c; ++i) seg_of[off + i] = (uint16_t)tid;
-    __syncthreads();
-    // straight-line gather, eight candidates per thread at a time: indices clamp to the last candidate (loaded
-    // again, not stored), so the map reads, then the loads, all go out together
-    for (int base = 0; base < total; base += 8 * kMbThreads) {
-      int jc[8], sg[8];
-      uint2 cv[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        jc[i] = min(base + tid + kMbThreads * i, total - 1);
-        sg[i] = seg_of[jc[i]];
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) cv[i] = cseg[(long long)sg[i] * kSliceKeys + (jc[i] - seg_off[sg[i]])];
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (base + tid + kMbThreads * i < total) cl[base + tid + kMbThreads * i] = cv[i];
-    }
-  }
-  __syncthreads();
-  // more candidates than fit in LDS (many keys in the border bin): read them from the segments, locating each by a
-  // search over the segment offsets
-  auto cand = [&](int j) -> uint2 {
-    if (in_lds) return cl[j];
+  auto load_cand = [&](int j) -> uint2 {
     const int sgm = cand_segment(seg_off, P, j);
     return cseg[(long long)sgm * kSliceKeys + (j - seg_off[sgm])];
   };
-
-  // pass 3 (bits [9:0]) over the candidates sharing the 21-bit prefix
-  for (int i = tid; i < kSelBins; i += kMbThreads) hist[i] = 0;
-  __syncthreads();
-  for (int j = tid; j < total; j += kMbThreads) {
-    const uint32_t key = cand(j).x;
-    if ((key & 0xFFFFFC00u) == prefix12) atomicAdd(&hist[key & 0x3FFu], 1);
+  if (in_lds) {
+    // one round: every thread locates and loads its candidates (indices clamp to the last one, loaded again and
+    // not stored), stores them to LDS and counts pass 3 over the keys sharing the 21-bit prefix
+    uint2 cv[kFinPer];
+#pragma unroll
+    for (int i = 0; i < kFinPer; ++i) cv[i] = load_cand(min(tid + kFinThreads * i, total - 1));
+#pragma unroll
+    for (int i = 0; i < kFinPer; ++i) {
+      const int j = tid + kFinThreads * i;
+      if (j < total) {
+        cl[j] = cv[i];
+        if ((cv[i].x & 0xFFFFFC00u) == prefix12) atomicAdd(&hist[cv[i].x & 0x3FFu], 1);
+      }
+    }
+  } else {
+    for (int j = tid; j < total; j += kFinThreads) {
+      const uint32_t key = load_cand(j).x;
+      if ((key & 0xFFFFFC00u) == prefix12) atomicAdd(&hist[key & 0x3FFu], 1);
+    }
   }
   __syncthreads();
-  const int b3 = find_bin256(hist, need, wsum, sh, &above);
-  need -= above;
+  const int b3 = find_bin(hist, need, wsum, sh);
+  need -= sh[1];
   const uint32_t kappa = prefix12 | (uint32_t)b3;  // the k-th largest key; `need` of the keys equal to it are taken
 
-  // ordered output: candidates > kappa, then the first `need` equal to kappa
+  // ordered output: candidates > kappa, then the first `need` equal to kappa; thread t takes kFinPer consecutive
+  // candidates of each round
   int sel_run = 0, eq_run = 0;
-  for (int base = 0; base < total && sel_run < k; base += kMbThreads * 8) {
-    const int j0 = base + 8 * tid;
-    uint2 cv[8];
+  for (int base = 0; base < total && sel_run < k; base += kCandCap) {
+    const int j0 = base + kFinPer * tid;
+    uint2 cv[kFinPer];
     int gt = 0, eq = 0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < kFinPer; ++j) {
       const bool v = j0 + j < total;
-      cv[j] = v ? cand(j0 + j) : make_uint2(0u, 0u);
+      cv[j] = v ? (in_lds ? cl[j0 + j] : load_cand(j0 + j)) : make_uint2(0u, 0u);
       gt += (v && cv[j].x > kappa) ? 1 : 0;
       eq += (v && cv[j].x == kappa) ? 1 : 0;
     }
     int ptot;
-    const int packed = block256_excl_scan(gt | (eq << 16), wsum, ptot);
+    const int packed = block_excl_scan(gt | (eq << 16), wsum, ptot);
     const int gt_before = packed & 0xFFFF, eq_before = packed >> 16;
     const int rem = need - eq_run > 0 ? need - eq_run : 0;
     int o = sel_run + gt_before + (eq_before < rem ? eq_before : rem);
     int eq_seen = eq_run + eq_before;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < kFinPer; ++j) {
       if (j0 + j >= total) break;
       bool sel = cv[j].x > kappa;
       if (cv[j].x == kappa) {
@@ -500,10 +495,11 @@ hipError_t launch_topk(const SelArgs& a, hipStream_t st) {
   clear_stale_error();
   if (a.sel_state) {
     const int P = (nvis_max + kSliceKeys - 1) / kSliceKeys;
+    if (P > kFinMaxSlices) return hipErrorInvalidValue;  // more than 4M entries per row
     if (nvis_max > a.k)
       hipLaunchKernelGGL(topk_collect_kernel, dim3((unsigned)P, (unsigned)a.rows), dim3(kMbThreads),
                          (size_t)kSliceKeys * 4, st, a);
-    hipLaunchKernelGGL(topk_finish_kernel, dim3((unsigned)a.rows), dim3(kMbThreads), kFinishLds, st, a);
+    hipLaunchKernelGGL(topk_finish_kernel, dim3((unsigned)a.rows), dim3(kFinThreads), kFinishLds, st, a);
   } else if (nvis_max <= kLdsKeys) {
     if (!g_lds_attr_set) {
       hipError_t e = hipFuncSetAttribute((const void*)topk_select_kernel<true>,
