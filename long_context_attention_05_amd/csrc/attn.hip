@@ -103,8 +103,8 @@ __device__ __forceinline__ void pf_finish(const AttnArgs& a, const f32x4_t (&acc
             make_float4(acc_o[dt][0] * f, acc_o[dt][1] * f, acc_o[dt][2] * f, acc_o[dt][3] * f);
       } else {
         uint2 w2;
-        w2.x = (uint32_t)f32_to_bf16(acc_o[dt][0] * f) | ((uint32_t)f32_to_bf16(acc_o[dt][1] * f) << 16);
-        w2.y = (uint32_t)f32_to_bf16(acc_o[dt][2] * f) | ((uint32_t)f32_to_bf16(acc_o[dt][3] * f) << 16);
+        w2.x = pack_bf16x2(acc_o[dt][0] * f, acc_o[dt][1] * f);
+        w2.y = pack_bf16x2(acc_o[dt][2] * f, acc_o[dt][3] * f);
         *(uint2*)((uint16_t*)a.out + ob + c0) = w2;
       }
     }
@@ -499,7 +499,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_pf_kernel(AttnArgs a) {
           const float p0 = (lg[et][x] == -INFINITY) ? 0.0f : __expf(lg[et][x] - m_new);
           const float p1 = (lg[et][x + 1] == -INFINITY) ? 0.0f : __expf(lg[et][x + 1] - m_new);
           psum += p0 + p1;
-          pw[2 * et + x / 2] = (uint32_t)f32_to_bf16(p0) | ((uint32_t)f32_to_bf16(p1) << 16);
+          pw[2 * et + x / 2] = pack_bf16x2(p0, p1);
         }
       psum = xor32_sum(xor16_sum(psum));
       l_run = l_run * alpha + psum;
@@ -647,8 +647,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_pf_kernel(AttnArgs a) {
           *(float4*)((float*)a.out + ob + 16 * dt) = make_float4(o[0], o[1], o[2], o[3]);
         } else {
           uint2 w2;
-          w2.x = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
-          w2.y = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
+          w2.x = pack_bf16x2(o[0], o[1]);
+          w2.y = pack_bf16x2(o[2], o[3]);
           *(uint2*)((uint16_t*)a.out + ob + 16 * dt) = w2;
         }
       }
@@ -952,8 +952,8 @@ __global__ __launch_bounds__(256) void attn_hgw_kernel(AttnArgs a, int pairs) {
             make_float4(res[k][0] * f, res[k][1] * f, res[k][2] * f, res[k][3] * f);
       } else {
         uint2 w2;
-        w2.x = (uint32_t)f32_to_bf16(res[k][0] * f) | ((uint32_t)f32_to_bf16(res[k][1] * f) << 16);
-        w2.y = (uint32_t)f32_to_bf16(res[k][2] * f) | ((uint32_t)f32_to_bf16(res[k][3] * f) << 16);
+        w2.x = pack_bf16x2(res[k][0] * f, res[k][1] * f);
+        w2.y = pack_bf16x2(res[k][2] * f, res[k][3] * f);
         *(uint2*)((uint16_t*)a.out + obase + c0) = w2;
       }
     }
@@ -1198,13 +1198,13 @@ __global__ __launch_bounds__(kWdThreads) void attn_wide_kernel(AttnArgs a) {
       psum += p[x];
     }
     uint2 pw;
-    pw.x = (uint32_t)f32_to_bf16(p[0]) | ((uint32_t)f32_to_bf16(p[1]) << 16);
-    pw.y = (uint32_t)f32_to_bf16(p[2]) | ((uint32_t)f32_to_bf16(p[3]) << 16);
+    pw.x = pack_bf16x2(p[0], p[1]);
+    pw.y = pack_bf16x2(p[2], p[3]);
     *(uint2*)(P_s + oh * kWdPStride + 4 * oq) = pw;
     if constexpr (kMixed) {
       uint2 pe;
-      pe.x = (uint32_t)f32_to_bf16(p[0] * esc[0]) | ((uint32_t)f32_to_bf16(p[1] * esc[1]) << 16);
-      pe.y = (uint32_t)f32_to_bf16(p[2] * esc[2]) | ((uint32_t)f32_to_bf16(p[3] * esc[3]) << 16);
+      pe.x = pack_bf16x2(p[0] * esc[0], p[1] * esc[1]);
+      pe.y = pack_bf16x2(p[2] * esc[2], p[3] * esc[3]);
       *(uint2*)(Pe_s + oh * kWdPStride + 4 * oq) = pe;
     }
     psum += xor8_get(psum);
@@ -1280,8 +1280,8 @@ __global__ __launch_bounds__(kWdThreads) void attn_wide_kernel(AttnArgs a) {
           *(float4*)((float*)a.out + obase + 16 * mb) = make_float4(o[0] * f, o[1] * f, o[2] * f, o[3] * f);
         } else {
           uint2 w2;
-          w2.x = (uint32_t)f32_to_bf16(o[0] * f) | ((uint32_t)f32_to_bf16(o[1] * f) << 16);
-          w2.y = (uint32_t)f32_to_bf16(o[2] * f) | ((uint32_t)f32_to_bf16(o[3] * f) << 16);
+          w2.x = pack_bf16x2(o[0] * f, o[1] * f);
+          w2.y = pack_bf16x2(o[2] * f, o[3] * f);
           *(uint2*)((uint16_t*)a.out + obase + 16 * mb) = w2;
         }
       }
@@ -1482,8 +1482,8 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
         *(f32x4_t*)((float*)a.out + ob + c) = acc;
       } else {
         uint2 w2;
-        w2.x = (uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
-        w2.y = (uint32_t)f32_to_bf16(acc[2]) | ((uint32_t)f32_to_bf16(acc[3]) << 16);
+        w2.x = pack_bf16x2(acc[0], acc[1]);
+        w2.y = pack_bf16x2(acc[2], acc[3]);
         *(uint2*)((uint16_t*)a.out + ob + c) = w2;
       }
     }

@@ -89,9 +89,6 @@ constexpr int kMfmaEntriesPerWave = 64;
 constexpr int kMfmaEntriesPerBlock = 4 * kMfmaEntriesPerWave;
 constexpr int kQStride = 136;  // bf16 elements per query head row in LDS (128 + 8 padding: no bank conflicts)
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
-}
 
 // Eight consecutive fp4 codes (one little-endian uint32) with their scale, widened to eight bf16 (exact).
 __device__ __forceinline__ uint4 fp4x8_to_bf16x8(uint32_t codes, int e) {

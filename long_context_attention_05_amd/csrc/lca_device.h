@@ -27,11 +27,12 @@ namespace lca {
 // ------------------------------------------------------------------------------------------------
 // bfloat16
 // ------------------------------------------------------------------------------------------------
-__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
-  uint32_t u = __float_as_uint(x);
-  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return 0x7FC0;  // NaN
-  u += 0x7FFFu + ((u >> 16) & 1u);                                            // round half to even
-  return (uint16_t)(u >> 16);
+// fp32 -> bf16 with round half to even: the hardware conversion (v_cvt_pk_bf16_f32), one instruction per two values.
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
