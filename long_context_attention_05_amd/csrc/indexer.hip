@@ -136,6 +136,26 @@ __device__ __forceinline__ void load_qblock(const IdxArgs& a, long long qrow0, u
   }
 }
 
+// Score of key l % 32 from the 32x32 results of the two head tiles (every lane of the key returns it).
+__device__ __forceinline__ float head_tree32(const f32x16_t (&acc)[2], const float (&wv)[2][16]) {
+  float a[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const float p0 = wv[0][k] * __int_as_float(max(__float_as_int(acc[0][k]), 0));
+    const float p1 = wv[1][k] * __int_as_float(max(__float_as_int(acc[1][k]), 0));
+    a[k] = p0 + p1;  // h+32
+  }
+  float c[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) c[r] = (a[r] + a[r + 8]) + (a[r + 4] + a[r + 12]);  // h+16, then h+8
+  // h+4 across the lane halves, scattered: the low half keeps head classes 0 and 1, the high half 2 and 3
+  const auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(c[0]), __float_as_uint(c[2]), false, false);
+  const auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(c[1]), __float_as_uint(c[3]), false, false);
+  const float d02 = __uint_as_float(s02[0]) + __uint_as_float(s02[1]);
+  const float d13 = __uint_as_float(s13[0]) + __uint_as_float(s13[1]);
+  return xor32_sum(d02) + xor32_sum(d13);  // h+2 across the halves, then h+1
+}
+
 template <int FMT>
 __global__ __launch_bounds__(256) void idx_score_mfma(IdxArgs a, int qpb) {
 #pragma clang fp contract(off)
@@ -210,25 +230,15 @@ __global__ __launch_bounds__(256) void idx_score_mfma(IdxArgs a, int qpb) {
         }
       }
       // epilogue: head h = 32T + 8(x/4) + 4g + (x%4) for register x; fixed halving tree over h
+      float wv[2][16];
+#pragma unroll
+      for (int T = 0; T < 2; ++T)
+#pragma unroll
+        for (int x = 0; x < 16; ++x) wv[T][x] = w_s[cur][32 * T + 8 * (x >> 2) + 4 * g + (x & 3)];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        float l1[16];
-#pragma unroll
-        for (int x = 0; x < 16; ++x) {  // level 1: h + 32
-          const int h = 8 * (x >> 2) + 4 * g + (x & 3);
-          const float p0 = w_s[cur][h] * fmaxf(acc[0][u][x], 0.0f);
-          const float p1 = w_s[cur][32 + h] * fmaxf(acc[1][u][x], 0.0f);
-          l1[x] = p0 + p1;
-        }
-        float l2[8], l3[4], l4[4];
-#pragma unroll
-        for (int x = 0; x < 8; ++x) l2[x] = l1[x] + l1[x + 8];  // h + 16
-#pragma unroll
-        for (int x = 0; x < 4; ++x) l3[x] = l2[x] + l2[x + 4];  // h + 8
-#pragma unroll
-        for (int x = 0; x < 4; ++x) l4[x] = xor32_sum(l3[x]);  // h + 4: the partner lane holds the other 4g half
-        const float l5_0 = l4[0] + l4[2], l5_1 = l4[1] + l4[3];  // h + 2
-        const float sc = l5_0 + l5_1;                            // h + 1
+        const f32x16_t au[2] = {acc[0][u], acc[1][u]};
+        const float sc = head_tree32(au, wv);
         const int e = e0 + 32 * u + col;
         if (g == 0 && e < nvis) a.keys[((long long)b * a.Sq + r) * a.N + e] = score_key(sc);
       }
@@ -452,7 +462,6 @@ __device__ __forceinline__ uint8_t* f4r_scales() {
 }
 
 typedef __attribute__((address_space(3))) void idx_lds_void_t;
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
 constexpr int kIdxBufWord3 = 0x00020000;  // buffer descriptor word 3: raw untyped loads
 
 // s_waitcnt immediate for vmcnt(n) with the other counters untouched
@@ -476,25 +485,6 @@ __device__ __forceinline__ void unroll_steps(F& f) {
   }
 }
 
-// Score of key l % 32 from the 32x32 results of the two head tiles (every lane of the key returns it).
-__device__ __forceinline__ float head_tree32(const f32x16_t (&acc)[2], const float (&wv)[2][16]) {
-  float a[16];
-#pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    const float p0 = wv[0][k] * __int_as_float(max(__float_as_int(acc[0][k]), 0));
-    const float p1 = wv[1][k] * __int_as_float(max(__float_as_int(acc[1][k]), 0));
-    a[k] = p0 + p1;  // h+32
-  }
-  float c[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) c[r] = (a[r] + a[r + 8]) + (a[r + 4] + a[r + 12]);  // h+16, then h+8
-  // h+4 across the lane halves, scattered: the low half keeps head classes 0 and 1, the high half 2 and 3
-  const auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(c[0]), __float_as_uint(c[2]), false, false);
-  const auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(c[1]), __float_as_uint(c[3]), false, false);
-  const float d02 = __uint_as_float(s02[0]) + __uint_as_float(s02[1]);
-  const float d13 = __uint_as_float(s13[0]) + __uint_as_float(s13[1]);
-  return xor32_sum(d02) + xor32_sum(d13);  // h+2 across the halves, then h+1
-}
 
 template <int NST>
 __global__ __launch_bounds__(kF4rWaves * 64) void idx_score_decode_fp4_ring(IdxArgs a) {
