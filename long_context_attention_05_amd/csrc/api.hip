@@ -80,14 +80,23 @@ void attn_plan(int B, int Sq, int H, int max_entries, int mode, bool table, int&
   split_len = (int)len;
 }
 
-// The kernel a call takes: few query rows on the MFMA path go to the head-group kernel (sparse lists) or the
-// wide kernel (dense HCA lists, many entries per row).
-int attn_mode(int B, int Sq, int H, int D, int q_format, int kv_format, int hca_m) {
+// The kernel a call takes: few query rows on the MFMA path go to the two-pass decode kernels (sparse lists of up to
+// kDecMaxEntries positions), the head-group kernel (longer sparse lists) or the wide kernel (dense HCA lists, many
+// entries per row).
+int attn_mode(int B, int Sq, int H, int D, int q_format, int kv_format, int hca_m, int max_entries) {
   if (!attn_uses_mfma(H, D, q_format, kv_format) || (long long)B * Sq >= 256) return 0;
-  return hca_m > 0 ? 2 : 1;
+  if (hca_m > 0) return 2;
+  return max_entries <= kDecMaxEntries ? 3 : 1;
 }
 
+// 32-entry tiles per row of the decode probabilities: whole 64-entry score tiles, at least one
+int dec_tiles(int max_entries) { return 2 * (max_entries > 0 ? (max_entries + 63) / 64 : 1); }
+
 size_t attn_ws_plan_size(int B, int Sq, int H, int D, int max_entries, int mode, bool table) {
+  if (mode == 3) {  // probabilities [rows][H][tiles * 32] bf16 and (m, l) [rows][tiles][H] float2
+    const size_t rows = (size_t)B * Sq, T = (size_t)dec_tiles(max_entries);
+    return align_up(rows * H * T * 32 * sizeof(uint16_t)) + align_up(rows * T * H * 2 * sizeof(float));
+  }
   int ns, len;
   attn_plan(B, Sq, H, max_entries, mode, table, ns, len);
   if (ns <= 1) return 0;
@@ -98,8 +107,9 @@ size_t attn_ws_plan_size(int B, int Sq, int H, int D, int max_entries, int mode,
 // Enough for whichever kernel the call will take (the size query does not know the formats).
 size_t attn_ws_size(int B, int Sq, int H, int D, int max_entries) {
   size_t need = attn_ws_plan_size(B, Sq, H, D, max_entries, 0, false);
-  if (H == 64 && D == 512)
-    for (int mode = 0; mode <= 2; ++mode) {
+  if (H == 64 && D == 512 && (long long)B * Sq < 256)  // the few-row kernels (see attn_mode)
+    for (int mode = 0; mode <= 3; ++mode) {
+      if (mode == 3 && max_entries > kDecMaxEntries) continue;
       const size_t m = attn_ws_plan_size(B, Sq, H, D, max_entries, mode, true);
       if (m > need) need = m;
     }
@@ -139,9 +149,9 @@ int run_attn(const void* q, int q_format, const lca_tensor& comp, int N, int hca
     return LCA_ERR_UNSUPPORTED;
   }
   const int max_entries = window + (hca_m > 0 ? N : k);
-  const int mode = attn_mode(B, Sq, H, D, q_format, comp.format, hca_m);
-  int ns, len;
-  attn_plan(B, Sq, H, max_entries, mode, mfma, ns, len);
+  const int mode = attn_mode(B, Sq, H, D, q_format, comp.format, hca_m, max_entries);
+  int ns = 1, len = max_entries;
+  if (mode != 3) attn_plan(B, Sq, H, max_entries, mode, mfma, ns, len);
   if (mfma && len > kHgSplitMax) return LCA_ERR_UNSUPPORTED;  // more than 4096 x 2048 list positions per row
   const size_t need = attn_ws_plan_size(B, Sq, H, D, max_entries, mode, mfma);
   if (need > 0 && (!ws || ws_bytes < need)) return LCA_ERR_WORKSPACE;
@@ -171,7 +181,11 @@ int run_attn(const void* q, int q_format, const lca_tensor& comp, int N, int hca
   a.n_splits = ns;
   a.split_len = len;
   a.hg_mode = mode;
-  if (ns > 1) {
+  if (mode == 3) {
+    a.dec_tiles = dec_tiles(max_entries);
+    a.dec_p = (uint16_t*)ws;
+    a.dec_ml = (float*)((char*)ws + align_up((size_t)B * Sq * H * a.dec_tiles * 32 * sizeof(uint16_t)));
+  } else if (ns > 1) {
     const size_t items = (size_t)B * Sq * ns;
     a.part_o = (float*)ws;
     a.part_ml = (float*)((char*)ws + align_up(items * H * D * sizeof(float)));

@@ -78,8 +78,14 @@ struct AttnArgs {
   float* part_o;   // [B][Sq][n_splits][H][D]
   float* part_ml;  // [B][Sq][n_splits][H][2]
   int hg_mode;     // 1: one workgroup per (16-head group, row, split); 2: one per (row, split) with the channels
-                   // split over the waves -- few rows (decode)
+                   // split over the waves; 3: scores then values in two passes -- few rows (decode)
+  // mode 3: the score pass's probabilities and per-tile (max, sum)
+  int dec_tiles;     // 32-entry tiles per row (an even number: list capacity / 64, rounded up, times 2)
+  uint16_t* dec_p;   // [B][Sq][H / 16][dec_tiles][64 lanes][8] bf16 probabilities e^(l - m_t), in the order the
+                     // value pass loads its MFMA operand (lane 16 q + h % 16: entries 8 q .. 8 q + 7 of head h)
+  float* dec_ml;     // [B][Sq][dec_tiles][H][2] (m_t, l_t)
 };
+constexpr int kDecMaxEntries = 2048;  // list positions per row in the two-pass decode attention
 constexpr int kHgSplitMax = 2048;  // list positions per workgroup slice in the MFMA attention kernels (LDS row table)
 bool attn_uses_mfma(int H, int D, int q_format, int kv_format);
 // ev_begin / ev_end (nullable): recorded around the attention kernel, before the merge of split partials.
