@@ -247,7 +247,7 @@ def main():
     src = ["long_context_attention_05_amd/csrc/indexer.hip", "long_context_attention_05_amd/csrc/lca_device.h"]
     if has_scores:
         if w.Sq == 1:
-            kname = "idx_score_decode_fp4" if w.key_fmt == "fp4" else "idx_score_decode_bf16"
+            kname = "idx_score_decode_fp4_ring" if w.key_fmt == "fp4" else "idx_score_decode_bf16"
             per_launch = step.score_kernel_bytes()
             achieved = per_launch / (avg_ms / 1e3) / 1e9
             res["roofline"] = {"kernel": kname, "bound": "hbm", "achieved": achieved,
