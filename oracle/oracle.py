@@ -247,6 +247,8 @@ def attn(q: dict, comp: dict, N: int, raw: dict, raw_start: int, S_raw: int, idx
     lse = np.empty((B, nr, H), np.float64)
     sink = np.ascontiguousarray(sink, np.float32)
     idx_a = None if idx is None else np.ascontiguousarray(idx, np.int32)
+    if hca_m == 0 and (idx_a is None or idx_a.size != B * Sq * k):
+        raise ValueError("idx must hold [B, Sq, k] entries (row r of the call reads idx[b, r])")
     q_s, c_s, r_s = _cstruct(q), _cstruct(comp), _cstruct(raw)
     rc = lib().orc_attn(ctypes.byref(q_s), ctypes.byref(c_s), N, ctypes.byref(r_s), raw_start, S_raw, _ptr(idx_a),
                         k, hca_m, _ptr(sink), B, Sq, H, D, window, float(scale), q_start_pos, _ptr(rows), nr,

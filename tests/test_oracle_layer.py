@@ -307,8 +307,10 @@ def test_own_block_invisible_through_compressed_path():
         comp["cap"] = keys["cap"] = N
         s64, _, _, _ = orc.indexer_scores(orc.plain_cache(qI, "f32"), w, keys, B, n, HI, DI, N, m, 0, rows=[t])
         idx, _, _ = orc.topk(s64.reshape(1, N), orc.nvis_rows(B, [t], 0, m, N), k)
+        idx_all = np.full((B, n, k), -1, np.int32)  # the oracle reads row t of a [B, Sq, k] list
+        idx_all[:, t, :] = idx
         o, _ = orc.attn(orc.plain_cache(q, "f32"), comp, N, dict(orc.plain_cache(raw, "f32"), cap=n), 0, n,
-                        idx.reshape(B, 1, k), k, 0, sink, B, n, H, c, W, 0.5, 0, rows=[t])
+                        idx_all, k, 0, sink, B, n, H, c, W, 0.5, 0, rows=[t])
         return o
 
     for t in (21, 22, 23, 40):
