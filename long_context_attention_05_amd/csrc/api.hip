@@ -181,6 +181,7 @@ int run_attn(const void* q, int q_format, const lca_tensor& comp, int N, int hca
   a.n_splits = ns;
   a.split_len = len;
   a.hg_mode = mode;
+  a.part_bf16 = mode == 2 ? 1 : 0;  // the wide kernel's partials (its only split output path)
   if (mode == 3) {
     a.dec_tiles = dec_tiles(max_entries);
     a.dec_p = (uint16_t*)ws;

@@ -1290,9 +1290,17 @@ __global__ __launch_bounds__(kWdThreads) void attn_wide_kernel(AttnArgs a) {
       if (a.lse && wave == 2 * hb + (hl >> 3) && grp == 0)
         a.lse[(long long)qrow * 64 + head] = (Mz == -INFINITY) ? -INFINITY : Mz + __logf(den);
     } else {
-      float* po = a.part_o + ((long long)item * 64 + head) * 512 + 64 * wave + 4 * grp;
+      // unnormalised partial sums in bf16 (the merge rescales them in fp32; the output is bf16 or checked at bf16
+      // precision anyway), half the bytes of the split round trip
+      const long long pi = ((long long)item * 64 + head) * 512 + 64 * wave + 4 * grp;
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) *(f32x4_t*)(po + 16 * mb) = acc_o[mb][hb];
+      for (int mb = 0; mb < 4; ++mb) {
+        const f32x4_t o = acc_o[mb][hb];
+        uint2 w2;
+        w2.x = pack_bf16x2(o[0], o[1]);
+        w2.y = pack_bf16x2(o[2], o[3]);
+        *(uint2*)((uint16_t*)a.part_o + pi + 16 * mb) = w2;
+      }
       if (wave == 2 * hb + (hl >> 3) && grp == 0) {
         a.part_ml[((long long)item * 64 + head) * 2 + 0] = M;
         a.part_ml[((long long)item * 64 + head) * 2 + 1] = Ls;
@@ -1841,6 +1849,54 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
   const int H = a.H, D = a.D, S = a.n_splits;
   const long long item0 = ((long long)b * a.Sq + r) * S;
   const float z = a.sink[h];
+  if (a.part_bf16 && S <= 32 && D == 4 * kMergeThreads) {
+    // bf16 partials, at most 32 splits: thread t's four channels of every split are loaded at once, behind the
+    // splits' (max, sum) (loaded unconditionally, so that the wait for them does not cover the partials), and the
+    // weights are formed while the partials are in flight
+    const int tid = threadIdx.x;
+    const long long sstride = (long long)H * D;
+    const uint16_t* pb = (const uint16_t*)a.part_o + (item0 * H + h) * D + 4 * tid;
+    const float2 ml = ((const float2*)a.part_ml)[(item0 + min(tid, S - 1)) * H + h];
+    uint2 pv[32];
+#pragma unroll
+    for (int s = 0; s < 32; ++s) pv[s] = *(const uint2*)(pb + min(s, S - 1) * sstride);
+    const float ms = tid < S ? ml.x : -INFINITY;
+    float mloc = wave_max(ms);
+    if ((tid & 63) == 0) red[tid >> 6] = mloc;
+    __syncthreads();
+    float M = z;
+    for (int i = 0; i < kMergeThreads / 64; ++i) M = fmaxf(M, red[i]);
+    const float wgt = (M == -INFINITY || ms == -INFINITY) ? 0.0f : __expf(ms - M);
+    if (tid < S) wsplit[tid] = wgt;
+    float dloc = wave_sum(tid < S ? wgt * ml.y : 0.0f);
+    __syncthreads();
+    if ((tid & 63) == 0) red[tid >> 6] = dloc;
+    __syncthreads();
+    float den = (M == -INFINITY || z == -INFINITY) ? 0.0f : __expf(z - M);
+    for (int i = 0; i < kMergeThreads / 64; ++i) den += red[i];
+    if (tid == 0 && a.lse) a.lse[((long long)b * a.Sq + r) * H + h] = (M == -INFINITY) ? -INFINITY : M + __logf(den);
+    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < 32; ++s) {
+      if (s < S) {
+        const uint2 w = pv[s];
+        acc += wsplit[s] * f32x4_t{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
+                                   __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u)};
+      }
+    }
+    acc *= inv;
+    const long long ob = (((long long)b * a.Sq + r) * H + h) * D + 4 * tid;
+    if (a.out_format == LCA_F32) {
+      *(f32x4_t*)((float*)a.out + ob) = acc;
+    } else {
+      uint2 w2;
+      w2.x = pack_bf16x2(acc[0], acc[1]);
+      w2.y = pack_bf16x2(acc[2], acc[3]);
+      *(uint2*)((uint16_t*)a.out + ob) = w2;
+    }
+    return;
+  }
   // M = max(z, m_s)
   float mloc = -INFINITY;
   for (int s = threadIdx.x; s < S; s += blockDim.x) mloc = fmaxf(mloc, a.part_ml[((item0 + s) * H + h) * 2 + 0]);
@@ -1871,30 +1927,50 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
   const float inv = stat[0];
   const long long ob = (((long long)b * a.Sq + r) * H + h) * D;
   if ((D & 3) == 0) {
-    // four channels per thread, eight splits' loads in flight at a time
-    const float* po = a.part_o + (item0 * H + h) * D;
+    // four channels per thread, eight (fp32) or sixteen (bf16) splits' loads in flight at a time
     const long long sstride = (long long)H * D;
-    for (int c = 4 * threadIdx.x; c < D; c += 4 * blockDim.x) {
-      f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-      int s0 = 0;
-      for (; s0 + 8 <= S; s0 += 8) {
-        f32x4_t v[8];
+    const float* po = a.part_o + (item0 * H + h) * D;
+    const uint16_t* pb = (const uint16_t*)a.part_o + (item0 * H + h) * D;
+    // split s's four channels c .. c + 3 (bf16 partials widened exactly); the format is a template flag of the loop
+    // so that its loads carry no branch between them
+    auto merge = [&](auto bfc) {
+      constexpr bool BF = decltype(bfc)::value;
+      auto part = [&](int s, int c) -> f32x4_t {
+        if constexpr (BF) {
+          const uint2 w = *(const uint2*)(pb + s * sstride + c);
+          return f32x4_t{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
+                         __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u)};
+        } else {
+          return *(const f32x4_t*)(po + s * sstride + c);
+        }
+      };
+      constexpr int NB = BF ? 16 : 8;  // splits whose loads are in flight together
+      for (int c = 4 * threadIdx.x; c < D; c += 4 * blockDim.x) {
+        f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        int s0 = 0;
+        for (; s0 + NB <= S; s0 += NB) {
+          f32x4_t v[NB];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = *(const f32x4_t*)(po + (s0 + u) * sstride + c);
+          for (int u = 0; u < NB; ++u) v[u] = part(s0 + u, c);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) acc += wsplit[s0 + u] * v[u];
+          for (int u = 0; u < NB; ++u) acc += wsplit[s0 + u] * v[u];
+        }
+        for (; s0 < S; ++s0) acc += wsplit[s0] * part(s0, c);
+        acc *= inv;
+        if (a.out_format == LCA_F32) {
+          *(f32x4_t*)((float*)a.out + ob + c) = acc;
+        } else {
+          uint2 w2;
+          w2.x = pack_bf16x2(acc[0], acc[1]);
+          w2.y = pack_bf16x2(acc[2], acc[3]);
+          *(uint2*)((uint16_t*)a.out + ob + c) = w2;
+        }
       }
-      for (; s0 < S; ++s0) acc += wsplit[s0] * *(const f32x4_t*)(po + s0 * sstride + c);
-      acc *= inv;
-      if (a.out_format == LCA_F32) {
-        *(f32x4_t*)((float*)a.out + ob + c) = acc;
-      } else {
-        uint2 w2;
-        w2.x = pack_bf16x2(acc[0], acc[1]);
-        w2.y = pack_bf16x2(acc[2], acc[3]);
-        *(uint2*)((uint16_t*)a.out + ob + c) = w2;
-      }
-    }
+    };
+    if (a.part_bf16)
+      merge(std::true_type{});
+    else
+      merge(std::false_type{});
     return;
   }
   for (int x = threadIdx.x; x < D; x += blockDim.x) {
