@@ -106,7 +106,10 @@ size_t attn_ws_plan_size(int B, int Sq, int H, int D, int max_entries, int mode,
 
 // Enough for whichever kernel the call will take (the size query does not know the formats).
 size_t attn_ws_size(int B, int Sq, int H, int D, int max_entries) {
+  // many rows: the plan without a row-table cap (SIMT kernels) or with it (MFMA kernels split longer lists)
   size_t need = attn_ws_plan_size(B, Sq, H, D, max_entries, 0, false);
+  const size_t tabled = attn_ws_plan_size(B, Sq, H, D, max_entries, 0, true);
+  if (tabled > need) need = tabled;
   if (H == 64 && D == 512 && (long long)B * Sq < 256)  // the few-row kernels (see attn_mode)
     for (int mode = 0; mode <= 3; ++mode) {
       if (mode == 3 && max_entries > kDecMaxEntries) continue;

@@ -322,31 +322,19 @@ __global__ __launch_bounds__(kAttnThreads) void attn_mfma_kernel(AttnArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------------
-// bf16 prefill kernel: LDS-direct loads into a four-tile ring, QK by heads, PV by channels
+// LDS tile ring of the bf16 prefill kernel (attn_pfs_kernel below)
 // ------------------------------------------------------------------------------------------------
-// One workgroup per (query row, slice of its list), four waves, 32-entry tiles.
-//   Loads: the tiles travel from memory straight into LDS (buffer_load ... lds: one instruction moves one 1 KB entry
-//     row, 16 bytes per lane), so no registers hold data in flight; three tiles are in flight while one is scored.
-//     Each ring slot is its own LDS variable and the tile loop is unrolled over the slots, so the compiler can tell
-//     that a slot's reads do not alias loads still landing in other slots; the waits for a slot are explicit counts.
-//   S^T = K Q^T: wave w owns heads 16 w .. 16 w + 15 (v_mfma_f32_16x16x32_bf16, A = K rows from LDS, B = the wave's
-//     queries in registers) and runs their online softmax.
-//   O^T += V^T P^T: wave w owns channels 128 w .. 128 w + 127 for all 64 heads.  Each wave publishes its P^T operand
-//     (lane: head, 8 entries) and the heads' rescale factors in LDS; every V^T operand (two transposing reads,
-//     ds_read_b64_tr_b16) then feeds four MFMAs, one per head group, which quarters the transposing reads against a
-//     split by heads.  The K index 8 g + v of lane group g stands for entry 4 g + v (v < 4) and 16 + 4 g + v - 4
-//     (v >= 4): the pair of 16-entry halves that the S^T accumulators and the two transposing reads already hold.
-//   One barrier per tile: before it a wave has scored its tile, published P and waited for its share of the next
-//   tile's loads; after it the freed ring slot is refilled and the PV product runs.
-constexpr int kPdRowB = 1040;                    // LDS bytes per tile row
-constexpr int kPdTileB = kPfTE * kPdRowB;        // 33280
+// The tiles travel from memory straight into LDS (buffer_load ... lds: one instruction moves one 1 KB entry row, 16
+// bytes per lane), so no registers hold data in flight.  Each ring slot is its own LDS variable and the tile loop is
+// unrolled over the slots, so the compiler can tell that a slot's reads do not alias loads still landing in other
+// slots; the waits for a slot are explicit counts.
+constexpr int kPdRowB = 1024;                    // LDS bytes per tile row
+constexpr int kPdTileB = kPfTE * kPdRowB;        // 32768
 __shared__ __attribute__((aligned(16))) uint8_t pd_slot0[kPdTileB];
 __shared__ __attribute__((aligned(16))) uint8_t pd_slot1[kPdTileB];
 __shared__ __attribute__((aligned(16))) uint8_t pd_slot2[kPdTileB];
 __shared__ __attribute__((aligned(16))) uint8_t pd_slot3[kPdTileB];
 __shared__ int pd_rows[kHgSplitMax];
-__shared__ __attribute__((aligned(16))) u32x4_t pd_p[2][4][64];   // [tile parity][head group][lane]: P^T operands
-__shared__ __attribute__((aligned(16))) float pd_alpha[2][16][4];  // [tile parity][head % 16][head / 16]
 __shared__ float pd_ml[64][2];
 
 template <int S>
@@ -374,23 +362,50 @@ __device__ __forceinline__ void pd_barrier() {
   asm volatile("" ::: "memory");
 }
 
-__global__ __launch_bounds__(kAttnThreads) void attn_pf_kernel(AttnArgs a) {
+// ------------------------------------------------------------------------------------------------
+// bf16 attention for many query rows (prefill), score and value waves: H = 64, D = 512
+// ------------------------------------------------------------------------------------------------
+// Eight waves in two roles, one of each per SIMD, a tile apart:
+//   score waves 0-3: wave g scores head group g (heads 16 g .. 16 g + 15) over all 512 channels,
+//                    S^T = K Q^T (A = the tile's K read from LDS, B = the group's queries held in registers),
+//                    runs the online softmax of its 16 heads and publishes P^T and the rescale factors;
+//   value waves 4-7: wave 4 + v accumulates O^T for channels 128 v .. 128 v + 127 and all 64 heads,
+//                    O^T += V^T P^T (A = V^T by transposing LDS reads, B = the published P^T), and moves the
+//                    tiles into the LDS ring.
+// In step tt the score waves work on tile tt and the value waves on tile tt - 1, so each SIMD overlaps one wave's
+// LDS reads and softmax arithmetic with the other's MFMAs; one barrier per step hands P^T(tt) over and
+// retires tile tt - 1.  The ring holds four 32-entry tiles (tile tt in slot tt % 4; tiles tt + 1 and tt + 2 in
+// flight during step tt).  Entry rows sit 1024 bytes apart with 16-byte chunk c of tile row r stored at chunk
+// c ^ (r % 16), which keeps the K reads (16 rows x 4 chunks per instruction) and the transposing V reads free of
+// bank conflicts.  Logits are kept in base 2 (scale * log2(e) folded into the one multiply).
+constexpr int kPsThreads = 512;
+constexpr float kLog2e = 1.4426950408889634f;
+__shared__ __attribute__((aligned(16))) u32x4_t ps_p[2][4][64];    // [tile parity][head group][lane]: P^T operands
+__shared__ __attribute__((aligned(16))) float ps_alpha[2][16][4];  // [tile parity][head % 16][head / 16]
+
+__global__ __launch_bounds__(kPsThreads) void attn_pfs_kernel(AttnArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int hl = lane & 15, grp = lane >> 4;
+  const bool scorer = wave < 4;    // wave-uniform role
+  const int vw = wave & 3;         // head group (score waves) or channel quarter (value waves)
   const int split = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
   const long long t = a.q_start + r;
   const RowList L = row_list(a, t);
   const int total = L.nw + L.nc;
   const int p_begin = split * a.split_len;
   const int npos = max(min(a.split_len, total - p_begin), 0);
-  const int qhead = 16 * wave + hl;  // the head this lane scores
+  const int qhead = 16 * vw + hl;  // the head a score lane works on
 
-  // the queries load first, so that the barrier after the row table has them in registers before the ring starts
+  // score waves: qreg[s] = channels 32 s + 8 grp .. + 7 of head qhead (loaded first, so that they land while the
+  // row table is built)
   bf16x8_t qreg[16];
   {
-    const uint8_t* qp = (const uint8_t*)a.q + ((((long long)b * a.Sq + r) * 64 + qhead) * 512 + 8 * grp) * 2;
+    const uint8_t* qp =
+        (const uint8_t*)a.q + ((((long long)b * a.Sq + r) * 64 + (scorer ? qhead : hl)) * 512 + 8 * grp) * 2;
+    if (scorer) {
 #pragma unroll
-    for (int s = 0; s < 16; ++s) qreg[s] = __builtin_bit_cast(bf16x8_t, *(gbl_u32x4_t*)(qp + 64 * s));
+      for (int s = 0; s < 16; ++s) qreg[s] = __builtin_bit_cast(bf16x8_t, *(gbl_u32x4_t*)(qp + 64 * s));
+    }
   }
   for (int i = threadIdx.x; i < npos; i += blockDim.x) {
     const int p = p_begin + i;
@@ -405,60 +420,69 @@ __global__ __launch_bounds__(kAttnThreads) void attn_pf_kernel(AttnArgs a) {
     }
     pd_rows[i] = row;
   }
-  // An empty asm re-defines each query register, so that the tile loop does not see registers defined by memory
-  // loads from before it (the compiler would otherwise wait for every load in flight when entering the loop).
-#pragma unroll
-  for (int s = 0; s < 16; ++s) asm volatile("" : "+v"(qreg[s]));
-  // acc[hg][dt]: lane (hl, grp) holds o^T[channel 128 w + 16 dt + 4 grp + x][head 16 hg + hl]
+  // value waves: acc[hg][dt] holds o^T[channel 128 v + 16 dt + 4 grp + x][head 16 hg + hl] in lane (hl, grp)
   f32x4_t acc[4][8];
-#pragma unroll
-  for (int hg = 0; hg < 4; ++hg)
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) acc[hg][dt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  float m_run = -INFINITY, l_run = 0.0f;  // of head qhead
+  float m_run = -INFINITY, l_run = 0.0f;  // score waves: of head qhead, base 2
+  const float c2 = a.scale * kLog2e;
   __syncthreads();
+  // The two roles run separate loops with the same barriers (one per step), so that the score waves' queries and
+  // the value waves' accumulators never share registers.
+  if (scorer) {
+    // an empty asm re-defines each query register, so that the tile loop does not see registers defined by memory
+    // loads from before it
+#pragma unroll
+    for (int s = 0; s < 16; ++s) asm volatile("" : "+v"(qreg[s]));
+  } else {
+#pragma unroll
+    for (int hg = 0; hg < 4; ++hg)
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) acc[hg][dt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  }
 
   const int ntiles = (npos + kPfTE - 1) / kPfTE;
   if (ntiles > 0) {  // block-uniform
-    // one buffer descriptor per tensor of batch b (range-checked, 32-bit offsets: the launcher keeps a batch's rows
-    // under 2 GiB); the row offset goes in the scalar offset, 16 bytes per lane in the vector offset
     const __amdgpu_buffer_rsrc_t raw_rs = __builtin_amdgcn_make_buffer_rsrc(
         (void*)((const uint8_t*)a.raw.data + (long long)b * a.raw.cap * 1024), 0, (int)(a.raw.cap * 1024), kBufRsrcWord3);
     const __amdgpu_buffer_rsrc_t comp_rs = __builtin_amdgcn_make_buffer_rsrc(
         (void*)((const uint8_t*)a.comp.data + (long long)b * a.comp.cap * 1024), 0, (int)(a.comp.cap * 1024),
         kBufRsrcWord3);
-    // Wave w moves entries 8 w .. 8 w + 7 of tile tt into ring slot S; positions past the slice repeat its last
-    // entry, so every tile issues the same number of loads and the wait counts stay fixed.
+    // Value wave v moves entries 8 v .. 8 v + 7 of tile tt into ring slot S (lane j takes chunk j ^ (tile row % 16)
+    // of the entry into LDS chunk j); positions past the slice repeat its last entry, so every tile issues the same
+    // number of loads and the wait counts stay fixed.
     auto issue = [&](auto SC, int tt) {
       constexpr int S = decltype(SC)::value;
-      const int ii = min(kPfTE * tt + 8 * wave + (lane & 7), npos - 1);
+      const int ii = min(kPfTE * tt + 8 * vw + (lane & 7), npos - 1);
       const int myrow = pd_rows[ii];
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
-        const int i = __builtin_amdgcn_readfirstlane(min(kPfTE * tt + 8 * wave + q, npos - 1));
+        const int i = __builtin_amdgcn_readfirstlane(min(kPfTE * tt + 8 * vw + q, npos - 1));
         const int row = __builtin_amdgcn_readlane(myrow, q);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(p_begin + i < L.nw ? raw_rs : comp_rs,
-                                                 (lds_void_t*)(pd_slot<S>() + (8 * wave + q) * kPdRowB), 16, 16 * lane,
-                                                 max(row, 0) * 1024, 0, 0);
+                                                 (lds_void_t*)(pd_slot<S>() + (8 * vw + q) * kPdRowB), 16,
+                                                 16 * (lane ^ ((8 * vw + q) & 15)), max(row, 0) * 1024, 0, 0);
       }
     };
-    // S^T = K Q^T of tile tt (slot S) for the wave's 16 heads.  LDS reads go in batches of 4 with three batches in
-    // flight (12 reads: the wave's counter of outstanding LDS reads holds at most 15).  K batch j: K-steps 2 j and
-    // 2 j + 1 of both 16-entry halves; four independent accumulator chains.
-    // Also returns the tile's mask of entries with a row.
-    auto qk = [&](auto SC, f32x4_t (&am)[2][2], int tt) -> uint32_t {
+    // Score waves: S^T of tile tt (slot S) for head group vw over all channels, then the softmax; publishes P^T and
+    // the rescale factor in buffer tt & 1.  K batch j: K-steps 2 j and 2 j + 1 of both 16-entry halves (four reads,
+    // three batches in flight), four independent accumulator chains.
+    auto score = [&](auto SC, int tt) {
       constexpr int S = decltype(SC)::value;
       const int iv = kPfTE * tt + (lane & 31);
       const uint32_t valid = (uint32_t)__ballot(iv < npos && pd_rows[min(iv, npos - 1)] >= 0);
-      const uint8_t* kp = pd_slot<S>() + hl * kPdRowB + 16 * grp;
+      // K-step kk reads chunk 4 kk + grp of rows hl and 16 + hl, stored at chunk (4 kk + grp) ^ hl
+      const uint8_t* kp = pd_slot<S>() + hl * kPdRowB;
+      const int koff = 16 * (grp ^ (hl & 3)) + 64 * (hl >> 2);
       u32x4_t kb[3][4];
       auto kload = [&](u32x4_t (&dst)[4], int j) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          dst[2 * u] = *(const u32x4_t*)(kp + 64 * (2 * j + u));
-          dst[2 * u + 1] = *(const u32x4_t*)(kp + 16 * kPdRowB + 64 * (2 * j + u));
+          const int kk = 2 * j + u;
+          const uint8_t* kq = kp + (koff ^ (64 * (kk & 3))) + 256 * (kk >> 2);
+          dst[2 * u] = *(const u32x4_t*)kq;
+          dst[2 * u + 1] = *(const u32x4_t*)(kq + 16 * kPdRowB);
         }
       };
+      f32x4_t am[2][2];
 #pragma unroll
       for (int et = 0; et < 2; ++et) am[et][0] = am[et][1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
       kload(kb[0], 0);
@@ -475,157 +499,149 @@ __global__ __launch_bounds__(kAttnThreads) void attn_pf_kernel(AttnArgs a) {
                                                                 qreg[2 * j + u], am[et][u], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
-      return valid;
-    };
-    // Online softmax of tile tt for head qhead (lanes hl, hl + 16, hl + 32, hl + 48 hold its 32 logits; the
-    // reference max only moves by more than kRescaleSlack); publishes P^T and the rescale factor in buffer tt & 1.
-    auto softmax = [&](const f32x4_t (&am)[2][2], uint32_t valid, int tt) {
+      // softmax: lanes hl, hl + 16, hl + 32, hl + 48 hold head qhead's 32 logits; the reference max only moves by
+      // more than kRescaleSlack
       float lg[2][4];
 #pragma unroll
       for (int et = 0; et < 2; ++et) {
-        const f32x4_t sum = am[et][0] + am[et][1];
+        const f32x4_t s = am[et][0] + am[et][1];
 #pragma unroll
-        for (int x = 0; x < 4; ++x) lg[et][x] = ((valid >> (16 * et + 4 * grp + x)) & 1u) ? a.scale * sum[x] : -INFINITY;
+        for (int x = 0; x < 4; ++x) lg[et][x] = s[x] * c2;
+      }
+      if (valid != 0xFFFFFFFFu) {  // block-uniform: the slice's last tile, or rows without an entry
+#pragma unroll
+        for (int et = 0; et < 2; ++et)
+#pragma unroll
+          for (int x = 0; x < 4; ++x)
+            if (!((valid >> (16 * et + 4 * grp + x)) & 1u)) lg[et][x] = -INFINITY;
       }
       float mt = fmaxf(fmaxf(fmaxf(lg[0][0], lg[0][1]), fmaxf(lg[0][2], lg[0][3])),
                        fmaxf(fmaxf(lg[1][0], lg[1][1]), fmaxf(lg[1][2], lg[1][3])));
       mt = xor32_max(xor16_max(mt));
-      const float m_new = (mt > m_run + kRescaleSlack) ? mt : m_run;
-      const float alpha = (m_new == m_run) ? 1.0f : __expf(m_run - m_new);
+      const float m_new = (mt > m_run + kRescaleSlack * kLog2e) ? mt : m_run;
+      const float alpha = (m_new == m_run) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+      const float m_sub = (m_new == -INFINITY) ? 0.0f : m_new;  // no entry yet: every weight is exp2(-inf) = 0
       float psum = 0.0f;
       u32x4_t pw;
 #pragma unroll
       for (int et = 0; et < 2; ++et)
 #pragma unroll
         for (int x = 0; x < 4; x += 2) {
-          const float p0 = (lg[et][x] == -INFINITY) ? 0.0f : __expf(lg[et][x] - m_new);
-          const float p1 = (lg[et][x + 1] == -INFINITY) ? 0.0f : __expf(lg[et][x + 1] - m_new);
+          const float p0 = __builtin_amdgcn_exp2f(lg[et][x] - m_sub);
+          const float p1 = __builtin_amdgcn_exp2f(lg[et][x + 1] - m_sub);
           psum += p0 + p1;
           pw[2 * et + x / 2] = pack_bf16x2(p0, p1);
         }
       psum = xor32_sum(xor16_sum(psum));
       l_run = l_run * alpha + psum;
       m_run = m_new;
-      pd_p[tt & 1][wave][lane] = pw;
-      pd_alpha[tt & 1][hl][wave] = alpha;  // the four lanes of a head store the same value
+      ps_p[tt & 1][vw][lane] = pw;
+      ps_alpha[tt & 1][hl][vw] = alpha;  // the four lanes of a head store the same value
     };
-    // After the barrier that publishes tile tt: bring the accumulators to the reference maxima of tile tt (rare:
-    // only when some head's reference max moved).
-    auto rescale = [&](int tt) {
-      const f32x4_t al = *(const f32x4_t*)&pd_alpha[tt & 1][hl][0];
+    // Value waves: bring the accumulators to the reference maxima of tile tp (rare: only when some head's reference
+    // max moved), then O^T += V^T P^T of tile tp (slot S) for the wave's 128 channels and all 64 heads.
+    auto value = [&](auto SC, int tp) {
+      constexpr int S = decltype(SC)::value;
+      const f32x4_t al = *(const f32x4_t*)&ps_alpha[tp & 1][hl][0];
       if (__ballot(al[0] != 1.0f || al[1] != 1.0f || al[2] != 1.0f || al[3] != 1.0f)) {
 #pragma unroll
         for (int hg = 0; hg < 4; ++hg)
 #pragma unroll
           for (int dt = 0; dt < 8; ++dt) acc[hg][dt] *= al[hg];
       }
-    };
-    // O^T += V^T P^T of tile tp (slot S) for the wave's 128 channels and all 64 heads, P from buffer tp & 1.  When
-    // `am` is given, the softmax of the next tile runs between the MFMAs (its VALU work issues while they execute).
-    auto pv = [&](auto SC, auto WITH_SM, int tp, const f32x4_t (&am)[2][2], uint32_t valid, int tt) {
-      constexpr int S = decltype(SC)::value;
-      // lane 4 a + e of group g reads V[4 g + v][128 w + 16 dt + 4 a + e] (first half) and V[16 + 4 g + v][..]
-      const uint8_t* vp = pd_slot<S>() + (4 * grp + (hl >> 2)) * kPdRowB + 8 * (hl & 3) + 256 * wave;
       bf16x8_t pb[4];
 #pragma unroll
-      for (int hg = 0; hg < 4; ++hg) pb[hg] = __builtin_bit_cast(bf16x8_t, pd_p[tp & 1][hg][lane]);
-      s16x4_t vb[2][8];
-      auto vload = [&](s16x4_t (&dst)[8], int j) {
+      for (int hg = 0; hg < 4; ++hg) pb[hg] = __builtin_bit_cast(bf16x8_t, ps_p[tp & 1][hg][lane]);
+      // lane 4 a + e of group g reads V[4 g + v][128 w + 16 dt + 4 a + e] (first half) and V[16 + 4 g + v][..]:
+      // lane (hl, grp) addresses row R = 4 grp + hl / 4 (and 16 + R), bytes 8 (hl % 4) + 32 dt + 256 w, whose
+      // 16-byte chunk C sits at chunk C ^ R
+      const int vrow = 4 * grp + (hl >> 2);
+      const int vchunk = ((((hl & 3) >> 1) + 16 * vw) ^ vrow) * 16;  // of dt = 0; dt flips chunk bits 1-3
+      const uint8_t* vp = pd_slot<S>() + vrow * kPdRowB + 8 * (hl & 1);
+      // V batch j: channel tiles 2 j and 2 j + 1 (four reads), the next batch in flight
+      s16x4_t vb[2][4];
+      auto vload = [&](s16x4_t (&dst)[4], int j) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          dst[2 * u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vp + 32 * (4 * j + u)));
-          dst[2 * u + 1] =
-              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vp + 16 * kPdRowB + 32 * (4 * j + u)));
+        for (int u = 0; u < 2; ++u) {
+          const uint8_t* vq = vp + (vchunk ^ (32 * (2 * j + u)));
+          dst[2 * u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)vq);
+          dst[2 * u + 1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vq + 16 * kPdRowB));
         }
       };
       vload(vb[0], 0);
-      vload(vb[1], 1);
-      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < 4; ++j) {
+        if (j + 1 < 4) vload(vb[(j + 1) & 1], j + 1);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < 2; ++u) {
           const bf16x8_t av = __builtin_bit_cast(
-              bf16x8_t, __builtin_shufflevector(vb[j][2 * u], vb[j][2 * u + 1], 0, 1, 2, 3, 4, 5, 6, 7));
+              bf16x8_t, __builtin_shufflevector(vb[j & 1][2 * u], vb[j & 1][2 * u + 1], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
           for (int hg = 0; hg < 4; ++hg)
-            acc[hg][4 * j + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[hg], acc[hg][4 * j + u], 0, 0, 0);
+            acc[hg][2 * j + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[hg], acc[hg][2 * j + u], 0, 0, 0);
         }
-      if constexpr (decltype(WITH_SM)::value) {
-        softmax(am, valid, tt);
-        // one MFMA, then up to five other ALU instructions, 32 times
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
-        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
     };
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
     using S2 = std::integral_constant<int, 2>;
     using S3 = std::integral_constant<int, 3>;
-    // Tile tt sits in slot tt % 4.  Step tt (tt >= 1): QK of tile tt; PV of tile tt - 1 with the softmax of tile tt
-    // between its MFMAs; wait for this wave's loads of tile tt + 1 (tile tt + 2 may still be landing: 8 loads);
-    // barrier (tile tt + 1 has landed for every wave, P of tile tt is published, every wave is done with tile
-    // tt - 1); start tile tt + 3 in the slot tile tt - 1 used; rescale for tile tt.
-    auto step = [&](auto SQ, auto SP, int tt) {
-      f32x4_t am[2][2];
-      const uint32_t valid = qk(SQ, am, tt);
-      pv(SP, std::true_type{}, tt - 1, am, valid, tt);
-      __builtin_amdgcn_s_waitcnt(kWaitVm8);
+    // Step tt (tt >= 1): score tile tt (slot SQ) | value tile tt - 1 (slot SP) and wait for this wave's loads of
+    // tile tt + 1; barrier (tile tt + 1 has landed, P^T(tt) is published, tile tt - 1 is retired); start tile
+    // tt + 3 in the slot tile tt - 1 used.  The steps run in whole groups of four: up to three tiles past the slice
+    // take part with no valid position (P = 0), so that the loop has one shape, every step is entered only from
+    // the step before it (the wait counts hold on every path), and the last tile sits in slot 0.
+    const int nsteps = 1 + ((ntiles - 1 + 3) & ~3);
+    if (scorer) {
+      auto sstep = [&](auto SQ, int tt) {
+        score(SQ, tt);
+        pd_barrier();
+      };
+      pd_barrier();  // tile 0 has landed
+      sstep(S0{}, 0);
+      for (int tt = 1; tt < nsteps; tt += 4) {
+        sstep(S1{}, tt);
+        sstep(S2{}, tt + 1);
+        sstep(S3{}, tt + 2);
+        sstep(S0{}, tt + 3);
+      }
+    } else {
+      auto vstep = [&](auto SP, int tt) {
+        value(SP, tt - 1);
+        __builtin_amdgcn_s_waitcnt(kWaitVm8);
+        pd_barrier();
+        issue(SP, tt + 3);
+      };
+      issue(S0{}, 0);
+      issue(S1{}, 1);
+      issue(S2{}, 2);
+      __builtin_amdgcn_s_waitcnt((1 << 14) | (0xF << 8) | (7 << 4));  // vmcnt(16): tile 0 has landed
       pd_barrier();
-      issue(SP, tt + 3);
-      rescale(tt);
-    };
-    issue(S0{}, 0);
-    issue(S1{}, 1);
-    issue(S2{}, 2);
-    __builtin_amdgcn_s_waitcnt((1 << 14) | (0xF << 8) | (7 << 4));  // vmcnt(16): tile 0 has landed
-    pd_barrier();
-    {
-      f32x4_t am[2][2];
-      const uint32_t valid = qk(S0{}, am, 0);
-      softmax(am, valid, 0);
-      __builtin_amdgcn_s_waitcnt(kWaitVm8);
+      __builtin_amdgcn_s_waitcnt(kWaitVm8);  // step 0: tile 1 has landed
       pd_barrier();
       issue(S3{}, 3);
-      rescale(0);
-    }
-    // Steps 1 .. ntiles - 1 in whole groups of four, then the last 0..3 nested, so that every step is entered only
-    // from the step before it and the wait counts hold on every path; then PV of the last tile.
-    const int nfull = 1 + ((ntiles - 1) & ~3);
-    for (int tt = 1; tt < nfull; tt += 4) {
-      step(S1{}, S0{}, tt);
-      step(S2{}, S1{}, tt + 1);
-      step(S3{}, S2{}, tt + 2);
-      step(S0{}, S3{}, tt + 3);
-    }
-    if (nfull < ntiles) {
-      step(S1{}, S0{}, nfull);
-      if (nfull + 1 < ntiles) {
-        step(S2{}, S1{}, nfull + 1);
-        if (nfull + 2 < ntiles) step(S3{}, S2{}, nfull + 2);
+      for (int tt = 1; tt < nsteps; tt += 4) {
+        vstep(S0{}, tt);
+        vstep(S1{}, tt + 1);
+        vstep(S2{}, tt + 2);
+        vstep(S3{}, tt + 3);
       }
+      value(S0{}, nsteps - 1);  // the last tile ((nsteps - 1) % 4 == 0)
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);  // the trailing ring loads land before the workgroup can end
     }
-    const f32x4_t none[2][2] = {};
-    switch ((ntiles - 1) & 3) {
-      case 0: pv(S0{}, std::false_type{}, ntiles - 1, none, 0u, 0); break;
-      case 1: pv(S1{}, std::false_type{}, ntiles - 1, none, 0u, 0); break;
-      case 2: pv(S2{}, std::false_type{}, ntiles - 1, none, 0u, 0); break;
-      default: pv(S3{}, std::false_type{}, ntiles - 1, none, 0u, 0); break;
-    }
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // the trailing ring loads land before the workgroup can end
   }
 
-  // finish: (max, sum) of every head through LDS, then each lane writes its 4 heads x 8 x 4 channels
+  // finish: (max, sum) of every head through LDS (back to natural-log units); each value lane writes 4 heads x 8 x
+  // 4 channels
   const long long item = ((long long)b * a.Sq + r) * a.n_splits + split;
-  if (grp == 0) {
-    pd_ml[qhead][0] = m_run;
+  if (scorer && grp == 0) {
+    pd_ml[qhead][0] = m_run * (1.0f / kLog2e);
     pd_ml[qhead][1] = l_run;
   }
   __syncthreads();
+  if (scorer) return;
 #pragma unroll
   for (int hg = 0; hg < 4; ++hg) {
     const int head = 16 * hg + hl;
@@ -641,7 +657,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_pf_kernel(AttnArgs a) {
         den = ((z == -INFINITY) ? 0.0f : __expf(z - M)) + l * ((m == -INFINITY) ? 0.0f : __expf(m - M));
         f = (m == -INFINITY) ? 0.0f : __expf(m - M) / den;
       }
-      const long long ob = (((long long)b * a.Sq + r) * 64 + head) * 512 + 128 * wave + 4 * grp;
+      const long long ob = (((long long)b * a.Sq + r) * 64 + head) * 512 + 128 * vw + 4 * grp;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
         const f32x4_t o = acc[hg][dt] * f;
@@ -654,14 +670,14 @@ __global__ __launch_bounds__(kAttnThreads) void attn_pf_kernel(AttnArgs a) {
           *(uint2*)((uint16_t*)a.out + ob + 16 * dt) = w2;
         }
       }
-      if (a.lse && wave == 0 && grp == 0)
+      if (a.lse && vw == 0 && grp == 0)
         a.lse[((long long)b * a.Sq + r) * 64 + head] = (M == -INFINITY) ? -INFINITY : M + __logf(den);
     } else {
-      float* po = a.part_o + (item * 64 + head) * 512 + 128 * wave + 4 * grp;
+      float* po = a.part_o + (item * 64 + head) * 512 + 128 * vw + 4 * grp;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt)
         *(float4*)(po + 16 * dt) = make_float4(acc[hg][dt][0], acc[hg][dt][1], acc[hg][dt][2], acc[hg][dt][3]);
-      if (wave == 0 && grp == 0) {
+      if (vw == 0 && grp == 0) {
         a.part_ml[(item * 64 + head) * 2 + 0] = m;
         a.part_ml[(item * 64 + head) * 2 + 1] = l;
       }
@@ -2074,7 +2090,7 @@ hipError_t launch_attn(AttnArgs a, hipStream_t st, hipEvent_t ev_begin, hipEvent
       g_attn_attr[dev] = true;
     }
     if (a.comp.format == LCA_BF16 && a.raw.cap * 1024 < (1ll << 31) && a.comp.cap * 1024 < (1ll << 31))
-      hipLaunchKernelGGL(attn_pf_kernel, grid, dim3(kAttnThreads), 0, st, a);
+      hipLaunchKernelGGL(attn_pfs_kernel, grid, dim3(kPsThreads), 0, st, a);
     else if (a.comp.format == LCA_BF16)
       hipLaunchKernelGGL(attn_mfma_kernel<LCA_BF16>, grid, dim3(kAttnThreads), kMfmaLds, st, a);
     else

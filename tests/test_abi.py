@@ -44,6 +44,8 @@ def test_workspace_sizes_are_consistent():
     assert lca.indexer_score_topk_workspace_size(16, 1, 32768, 512) >= 16 * 32768 * 4
     assert lca.sparse_mqa_attn_workspace_size(4096, 1, 64, 512, 1152) == 0  # enough rows: no split partials
     assert lca.sparse_mqa_attn_workspace_size(16, 1, 64, 512, 640) > 0
+    # many rows with a list longer than one 2048-position slice: the MFMA kernels split it and need partials
+    assert lca.sparse_mqa_attn_workspace_size(256, 1, 64, 512, 2116) >= 256 * 2 * 64 * 512 * 4
     assert lca.hca_attn_workspace_size(8, 1, 64, 512, 8320) > 0
 
 

@@ -281,6 +281,17 @@ def test_attn_mfma(B, Sq, N, k, window, fmt):
     np.testing.assert_allclose(l, lr, rtol=1e-3, atol=1e-3)
 
 
+@pytest.mark.parametrize("B,Sq,N,k,window,q_start,seed", [(1, 300, 500, 64, 128, 0, 41),
+                                                          (1, 256, 3000, 2100, 16, 60000, 42),
+                                                          (2, 130, 1000, 40, 128, 77, 43)])
+def test_attn_many_rows(B, Sq, N, k, window, q_start, seed):
+    # the many-row bf16 kernel: windows that grow from one position (q_start 0), a list longer than one slice
+    # (two splits and the merge), and rows of two sequences
+    o, ref, l, lr = _attn_case(B, Sq, 64, 512, N, k, window, q_start, "bf16", seed, scale=1.0)
+    assert row_rel_err(o, ref) <= 1e-2
+    np.testing.assert_allclose(l, lr, rtol=1e-3, atol=1e-3)
+
+
 @pytest.mark.parametrize("fmt", ["bf16", "mixed"])
 def test_hca_short_list_single_split(fmt):
     # window 16 + 40 entries: one slice per row, the output finalized in the attention kernel itself
