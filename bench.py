@@ -75,7 +75,8 @@ def source_hash(files) -> str:
 
 
 def traffic_record(kernel: str, workload: str, src_files, per_launch_units: float):
-    """HBM bytes per launch from a committed rocprofv3 counter summary, if it was taken on the current source."""
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it was taken on the current source and
+    build flags (the hash covers the kernel's source files and the build script)."""
     path = os.path.join(ROOT, "profiles", "traffic_%s_%s.json" % (kernel, workload))
     if not os.path.exists(path):
         return None
@@ -236,7 +237,8 @@ def main():
     durs = [ev.elapsed_ms(a, b) for a, b in pairs]
     avg_ms = sum(durs) / len(durs)
     if not has_scores:
-        src = ["long_context_attention_05_amd/csrc/attn.hip", "long_context_attention_05_amd/csrc/lca_device.h"]
+        src = ["long_context_attention_05_amd/csrc/attn.hip", "long_context_attention_05_amd/csrc/lca_device.h",
+               "long_context_attention_05_amd/build.py"]
         kname = "attn_wide_kernel"
         per_launch = step.attn_kernel_bytes()
         achieved = per_launch / (avg_ms / 1e3) / 1e9
@@ -244,7 +246,8 @@ def main():
                            "frac": achieved / HBM_PEAK_GBPS,
                            "traffic": traffic_record(kname, w.name, src, per_launch),
                            "avg_launch_us": avg_ms * 1e3, "algorithmic_bytes_per_launch": per_launch}
-    src = ["long_context_attention_05_amd/csrc/indexer.hip", "long_context_attention_05_amd/csrc/lca_device.h"]
+    src = ["long_context_attention_05_amd/csrc/indexer.hip", "long_context_attention_05_amd/csrc/lca_device.h",
+           "long_context_attention_05_amd/build.py"]
     if has_scores:
         if w.Sq == 1:
             kname = "idx_score_decode_fp4_ring" if w.key_fmt == "fp4" else "idx_score_decode_bf16"
