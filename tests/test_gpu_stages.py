@@ -196,10 +196,12 @@ def test_indexer_ties_go_to_lower_index():
 # stages 3/4: attention
 # ------------------------------------------------------------------------------------------------------
 def _attn_case(B, Sq, H, D, N, k, window, q_start, fmt, seed, hca_m=0, sink_mode="normal", idx_mode="random",
-               scale=None, rope=64):
+               scale=None, rope=64, gain=0.0):
     g = _rng(seed)
     q = (g.standard_normal((B, Sq, H, D)) / math.sqrt(D)).astype(np.float32)
     comp = g.standard_normal((B, N, D)).astype(np.float32)
+    if gain:  # entry e scaled by 1 + gain * e / N: logits grow along a sorted list, so the running max moves
+        comp *= (1.0 + gain * np.arange(N, dtype=np.float32) / N)[None, :, None]
     raw_start = max(0, q_start - window + 1)
     S_raw = q_start + Sq - raw_start
     raw = g.standard_normal((B, max(S_raw, 1), D)).astype(np.float32)
@@ -290,6 +292,26 @@ def test_attn_many_rows(B, Sq, N, k, window, q_start, seed):
     o, ref, l, lr = _attn_case(B, Sq, 64, 512, N, k, window, q_start, "bf16", seed, scale=1.0)
     assert row_rel_err(o, ref) <= 1e-2
     np.testing.assert_allclose(l, lr, rtol=1e-3, atol=1e-3)
+
+
+@pytest.mark.parametrize("B,Sq,k", [(1, 260, 512), (2, 1, 512), (1, 1, 2100)])
+def test_attn_running_max_moves(B, Sq, k):
+    # entries later in the (sorted) list have logits up to 40x larger, so the reference max of every head moves many
+    # times by more than the rescale slack: the many-row kernel (260 rows), the two-pass decode kernels (512) and the
+    # head-group kernel (2100)
+    o, ref, l, lr = _attn_case(B, Sq, 64, 512, 4000, k, 16, 60000, "bf16", 44, scale=1.0, gain=40.0)
+    assert row_rel_err(o, ref) <= 1e-2
+    np.testing.assert_allclose(l, lr, rtol=1e-3, atol=1e-3)
+
+
+def test_attn_many_rows_empty_lists():
+    # many rows, no window, every list empty: o = 0, lse = -inf; then only the sink: o = 0, lse = z
+    o, ref, l, lr = _attn_case(1, 256, 64, 512, 50, 16, 0, 400, "bf16", 45, sink_mode="none", idx_mode="empty")
+    assert np.all(o == 0) and np.all(ref == 0)
+    assert np.all(np.isneginf(l)) and np.all(np.isneginf(lr))
+    o, ref, l, lr = _attn_case(1, 256, 64, 512, 50, 16, 0, 400, "bf16", 46, idx_mode="empty")
+    assert np.all(o == 0)
+    np.testing.assert_allclose(l, lr, rtol=1e-6)
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "mixed"])
