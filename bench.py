@@ -239,7 +239,8 @@ def main():
     if not has_scores:
         src = ["long_context_attention_05_amd/csrc/attn.hip", "long_context_attention_05_amd/csrc/lca_device.h",
                "long_context_attention_05_amd/build.py"]
-        kname = "attn_wide_kernel"
+        # dense HCA rows: the many-row kernel over a bf16 cache, the wide kernel over the mixed cache
+        kname = "attn_pfs_kernel" if w.main_fmt == "bf16" else "attn_wide_kernel"
         per_launch = step.attn_kernel_bytes()
         achieved = per_launch / (avg_ms / 1e3) / 1e9
         res["roofline"] = {"kernel": kname, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",

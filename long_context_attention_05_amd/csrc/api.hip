@@ -81,11 +81,12 @@ void attn_plan(int B, int Sq, int H, int max_entries, int mode, bool table, int&
 }
 
 // The kernel a call takes: few query rows on the MFMA path go to the two-pass decode kernels (sparse lists of up to
-// kDecMaxEntries positions), the head-group kernel (longer sparse lists) or the wide kernel (dense HCA lists, many
-// entries per row).
+// kDecMaxEntries positions), the head-group kernel (longer sparse lists) or, for dense HCA lists over the mixed
+// cache, the wide kernel.  Dense HCA lists over a bf16 cache take the many-row path (mode 0): its LDS ring keeps two
+// tiles in flight where the wide kernel holds one in registers, and it splits the list the same way.
 int attn_mode(int B, int Sq, int H, int D, int q_format, int kv_format, int hca_m, int max_entries) {
   if (!attn_uses_mfma(H, D, q_format, kv_format) || (long long)B * Sq >= 256) return 0;
-  if (hca_m > 0) return 2;
+  if (hca_m > 0) return kv_format == LCA_BF16 ? 0 : 2;
   return max_entries <= kDecMaxEntries ? 3 : 1;
 }
 

@@ -673,10 +673,21 @@ __global__ __launch_bounds__(kPsThreads) void attn_pfs_kernel(AttnArgs a) {
       if (a.lse && vw == 0 && grp == 0)
         a.lse[((long long)b * a.Sq + r) * 64 + head] = (M == -INFINITY) ? -INFINITY : M + __logf(den);
     } else {
-      float* po = a.part_o + (item * 64 + head) * 512 + 128 * vw + 4 * grp;
+      const long long pi = (item * 64 + head) * 512 + 128 * vw + 4 * grp;
+      if (a.part_bf16) {  // unnormalised partial sums in bf16 (the merge rescales them in fp32): half the bytes
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt)
-        *(float4*)(po + 16 * dt) = make_float4(acc[hg][dt][0], acc[hg][dt][1], acc[hg][dt][2], acc[hg][dt][3]);
+        for (int dt = 0; dt < 8; ++dt) {
+          uint2 w2;
+          w2.x = pack_bf16x2(acc[hg][dt][0], acc[hg][dt][1]);
+          w2.y = pack_bf16x2(acc[hg][dt][2], acc[hg][dt][3]);
+          *(uint2*)((uint16_t*)a.part_o + pi + 16 * dt) = w2;
+        }
+      } else {
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+          *(float4*)(a.part_o + pi + 16 * dt) =
+              make_float4(acc[hg][dt][0], acc[hg][dt][1], acc[hg][dt][2], acc[hg][dt][3]);
+      }
       if (vw == 0 && grp == 0) {
         a.part_ml[(item * 64 + head) * 2 + 0] = m;
         a.part_ml[(item * 64 + head) * 2 + 1] = l;
@@ -2089,8 +2100,10 @@ hipError_t launch_attn(AttnArgs a, hipStream_t st, hipEvent_t ev_begin, hipEvent
       if (e != hipSuccess) return e;
       g_attn_attr[dev] = true;
     }
-    if (a.comp.format == LCA_BF16 && a.raw.cap * 1024 < (1ll << 31) && a.comp.cap * 1024 < (1ll << 31))
+    if (a.comp.format == LCA_BF16 && a.raw.cap * 1024 < (1ll << 31) && a.comp.cap * 1024 < (1ll << 31)) {
+      a.part_bf16 = 1;  // split partials in bf16, for this kernel and the merge after it
       hipLaunchKernelGGL(attn_pfs_kernel, grid, dim3(kPsThreads), 0, st, a);
+    }
     else if (a.comp.format == LCA_BF16)
       hipLaunchKernelGGL(attn_mfma_kernel<LCA_BF16>, grid, dim3(kAttnThreads), kMfmaLds, st, a);
     else
