@@ -77,7 +77,8 @@ struct AttnArgs {
   int n_splits, split_len;
   float* part_o;   // [B][Sq][n_splits][H][D] fp32, or bf16 when part_bf16
   float* part_ml;  // [B][Sq][n_splits][H][2]
-  int part_bf16;   // split partial outputs stored as bf16 (the wide kernel: half the partial traffic)
+  int part_bf16;   // split partial outputs stored as bf16 (the wide and the many-row bf16 kernels: half the
+                   // partial traffic); set by the launcher for the kernel it takes
   int hg_mode;     // 1: one workgroup per (16-head group, row, split); 2: one per (row, split) with the channels
                    // split over the waves; 3: scores then values in two passes -- few rows (decode)
   // mode 3: the score pass's probabilities and per-tile (max, sum)
