@@ -1000,7 +1000,8 @@ __global__ __launch_bounds__(256) void attn_hgw_kernel(AttnArgs a, int pairs) {
 }
 
 // ------------------------------------------------------------------------------------------------
-// wide MFMA kernel (few query rows over many entries: dense HCA decode): H = 64, D = 512, bf16 or mixed entries
+// wide MFMA kernel (few query rows over many entries: dense HCA decode over the mixed cache): H = 64, D = 512
+// (written for bf16 or mixed entries; launched for the mixed cache, since bf16 rows take the many-row kernel)
 // ------------------------------------------------------------------------------------------------
 // One 512-thread workgroup per (query row, slice of its list) with all 64 heads; wave w owns channels
 // [64 w, 64 w + 64) of every entry (for the mixed cache, waves 0..6 hold the 448 fp8 channels and wave 7 the 64 RoPE
@@ -2056,20 +2057,16 @@ hipError_t launch_attn(AttnArgs a, hipStream_t st, hipEvent_t ev_begin, hipEvent
   } else if (mfma && a.hg_mode == 2) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    // mode 2 is chosen for the mixed cache only (dense HCA rows over a bf16 cache take the many-row kernel)
+    if (a.comp.format != LCA_MIXED_FP8) return hipErrorInvalidValue;
     if (dev >= 0 && dev < 64 && !g_wd_attr[dev]) {
-      hipError_t e = hipFuncSetAttribute((const void*)attn_wide_kernel<LCA_BF16>,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)kWdLds);
-      if (e == hipSuccess)
-        e = hipFuncSetAttribute((const void*)attn_wide_kernel<LCA_MIXED_FP8>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kWdLds);
+      const hipError_t e = hipFuncSetAttribute((const void*)attn_wide_kernel<LCA_MIXED_FP8>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)kWdLds);
       if (e != hipSuccess) return e;
       g_wd_attr[dev] = true;
     }
     const dim3 wgrid((unsigned)(a.B * a.Sq * a.n_splits));
-    if (a.comp.format == LCA_BF16)
-      hipLaunchKernelGGL(attn_wide_kernel<LCA_BF16>, wgrid, dim3(kWdThreads), kWdLds, st, a);
-    else
-      hipLaunchKernelGGL(attn_wide_kernel<LCA_MIXED_FP8>, wgrid, dim3(kWdThreads), kWdLds, st, a);
+    hipLaunchKernelGGL(attn_wide_kernel<LCA_MIXED_FP8>, wgrid, dim3(kWdThreads), kWdLds, st, a);
   } else if (mfma && a.hg_mode == 1) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) dev = 0;
