@@ -114,9 +114,13 @@ def test_compress_quantised_outputs(fmt, c, rope):
 # ------------------------------------------------------------------------------------------------------
 # stage 2: indexer scores + exact top-k
 # ------------------------------------------------------------------------------------------------------
-def _indexer_case(B, Sq, HI, DI, N, m, k, q_start, fmt, seed, dyadic=False, dup_rows=False):
+def _indexer_case(B, Sq, HI, DI, N, m, k, q_start, fmt, seed, dyadic=False, dup_rows=False, zero_q=False):
     g = _rng(seed)
-    if dyadic:
+    if zero_q:  # every score is exactly 0: the selection is the first k visible entries
+        q = np.zeros((B, Sq, HI, DI), np.float32)
+        K = g.standard_normal((B, N, DI)).astype(np.float32)
+        w = g.standard_normal((B, Sq, HI)).astype(np.float32)
+    elif dyadic:
         q = (g.integers(-3, 4, (B, Sq, HI, DI)) * 0.5).astype(np.float32)
         K = (g.integers(-3, 4, (B, N, DI)) * 0.25).astype(np.float32)
         w = (g.integers(-4, 5, (B, Sq, HI)) * 0.0625).astype(np.float32)
@@ -151,7 +155,7 @@ def _indexer_case(B, Sq, HI, DI, N, m, k, q_start, fmt, seed, dyadic=False, dup_
     w_s = ws(nbytes)
     lca.indexer_score_topk(qg.desc(), wd, kg.desc(), B, Sq, HI, DI, N, m, k, q_start, idx, sc, w_s, nbytes)
     torch.cuda.synchronize()
-    exact = fmt == "fp4" or dyadic
+    exact = fmt == "fp4" or dyadic or zero_q
     s64, s32, ab, bad = orc.indexer_scores(qr, w, kr, B, Sq, HI, DI, N, m, q_start, canonical=exact, want_abs=True)
     if exact:
         assert bad == 0, "per-head dots not exact in fp32: the exact comparison does not apply"
@@ -184,6 +188,16 @@ def test_indexer_mfma_bf16_prefill_causal():
                                              (2, 2, 500, 64, 16, 64), (8, 1, 65613, 1024, 64, 128)])
 def test_indexer_fp4_bit_exact(B, Sq, N, k, HI, DI):
     _indexer_case(B, Sq, HI, DI, N, 4, k, 4 * N, "fp4", 14)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "f32"])
+def test_indexer_all_scores_equal(fmt):
+    # many rows (the LDS select) and a decode row (the multi-workgroup select): one key value, so the first k
+    # visible entries in index order
+    _indexer_case(1, 6, 64 if fmt == "bf16" else 8, 128 if fmt == "bf16" else 32, 700, 4, 40, 4 * 700, fmt, 18,
+                  zero_q=True)
+    _indexer_case(2, 1, 64 if fmt == "bf16" else 8, 128 if fmt == "bf16" else 32, 3000, 4, 512, 4 * 3000, fmt, 19,
+                  zero_q=True)
 
 
 def test_indexer_ties_go_to_lower_index():
