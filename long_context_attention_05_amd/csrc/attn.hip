@@ -363,7 +363,8 @@ __device__ __forceinline__ void pd_barrier() {
 }
 
 // ------------------------------------------------------------------------------------------------
-// bf16 attention for many query rows (prefill), score and value waves: H = 64, D = 512
+// bf16 attention for many query rows (prefill; also dense HCA rows split into slices), score and value waves:
+// H = 64, D = 512
 // ------------------------------------------------------------------------------------------------
 // Eight waves in two roles, one of each per SIMD, a tile apart:
 //   score waves 0-3: wave g scores head group g (heads 16 g .. 16 g + 15) over all 512 channels,
@@ -376,8 +377,10 @@ __device__ __forceinline__ void pd_barrier() {
 // LDS reads and softmax arithmetic with the other's MFMAs; one barrier per step hands P^T(tt) over and
 // retires tile tt - 1.  The ring holds four 32-entry tiles (tile tt in slot tt % 4; tiles tt + 1 and tt + 2 in
 // flight during step tt).  Entry rows sit 1024 bytes apart with 16-byte chunk c of tile row r stored at chunk
-// c ^ (r % 16), which keeps the K reads (16 rows x 4 chunks per instruction) and the transposing V reads free of
-// bank conflicts.  Logits are kept in base 2 (scale * log2(e) folded into the one multiply).
+// c ^ (r % 16), which keeps the K reads (16 rows x 4 chunks per instruction) free of bank conflicts (a padded
+// 1040-byte pitch halves their rate); the transposing V reads run at the same rate under either layout.  Logits are
+// kept in base 2 (scale * log2(e) folded into the one multiply).  Split partials are written in bf16 when the
+// launcher asks for them (part_bf16).
 constexpr int kPsThreads = 512;
 constexpr float kLog2e = 1.4426950408889634f;
 __shared__ __attribute__((aligned(16))) u32x4_t ps_p[2][4][64];    // [tile parity][head group][lane]: P^T operands
