@@ -37,7 +37,7 @@ extern "C" {
 typedef enum {
   LCA_OK = 0,
   LCA_ERR_INVALID_ARG = -1, /* null pointer, bad size, inconsistent shapes or positions          */
-  LCA_ERR_UNSUPPORTED = -2, /* valid request that no kernel of this build implements             */
+  LCA_ERR_UNSUPPORTED = -2, /* valid request that no kernel of this library implements           */
   LCA_ERR_WORKSPACE = -3,   /* ws NULL or ws_bytes smaller than the matching *_workspace_size    */
   LCA_ERR_ALIGNMENT = -4,   /* a pointer is not 16-byte aligned                                 */
   LCA_ERR_HIP = -5          /* the HIP runtime rejected a launch                                */
