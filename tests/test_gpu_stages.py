@@ -210,7 +210,7 @@ def test_indexer_ties_go_to_lower_index():
 # stages 3/4: attention
 # ------------------------------------------------------------------------------------------------------
 def _attn_case(B, Sq, H, D, N, k, window, q_start, fmt, seed, hca_m=0, sink_mode="normal", idx_mode="random",
-               scale=None, rope=64, gain=0.0):
+               scale=None, rope=64, gain=0.0, out_f32=False, with_lse=True):
     g = _rng(seed)
     q = (g.standard_normal((B, Sq, H, D)) / math.sqrt(D)).astype(np.float32)
     comp = g.standard_normal((B, N, D)).astype(np.float32)
@@ -252,25 +252,28 @@ def _attn_case(B, Sq, H, D, N, k, window, q_start, fmt, seed, hca_m=0, sink_mode
         qb = gen.bf16_bits(q)
         qd, qr = up(qb), orc.plain_cache(qb, "bf16")
     cr["cap"], rr["cap"] = N, max(S_raw, 1)
-    out = torch.empty((B, Sq, H, D), dtype=torch.float32 if fmt == "f32" else torch.int16, device="cuda")
-    lse = torch.empty((B, Sq, H), dtype=torch.float32, device="cuda")
+    f32_out = fmt == "f32" or out_f32
+    out = torch.empty((B, Sq, H, D), dtype=torch.float32 if f32_out else torch.int16, device="cuda")
+    lse = torch.full((B, Sq, H), 12345.0, dtype=torch.float32, device="cuda")
     sd = up(sink)
-    of = lca.LCA_F32 if fmt == "f32" else lca.LCA_BF16
+    of = lca.LCA_F32 if f32_out else lca.LCA_BF16
     qfmt = lca.FORMATS[qf]
     if hca_m:
         nbytes = lca.hca_attn_workspace_size(B, Sq, H, D, window + N)
         w_s = ws(nbytes)
         lca.hca_attn(qd, qfmt, cg.desc(), N, hca_m, rg.desc(), raw_start, S_raw, sd, B, Sq, H, D, window, scale,
-                     q_start, out, of, lse, w_s, nbytes)
+                     q_start, out, of, lse if with_lse else None, w_s, nbytes)
     else:
         nbytes = lca.sparse_mqa_attn_workspace_size(B, Sq, H, D, window + k)
         w_s = ws(nbytes)
         lca.sparse_mqa_attn(qd, qfmt, cg.desc(), N, rg.desc(), raw_start, S_raw, up(idx), k, sd, B, Sq, H, D, window,
-                            scale, q_start, out, of, lse, w_s, nbytes)
+                            scale, q_start, out, of, lse if with_lse else None, w_s, nbytes)
     torch.cuda.synchronize()
     o_ref, l_ref = orc.attn(qr, cr, N, rr, raw_start, S_raw, idx, k, hca_m, sink, B, Sq, H, D, window, scale, q_start)
     o = out.cpu().numpy()
-    o = o.astype(np.float64) if fmt == "f32" else bf16_to_f64(o.view(np.uint16))
+    o = o.astype(np.float64) if f32_out else bf16_to_f64(o.view(np.uint16))
+    if not with_lse:  # no lse pointer: nothing may have been written there
+        assert torch.all(lse == 12345.0)
     return o, o_ref, lse.cpu().numpy(), l_ref
 
 
@@ -316,6 +319,17 @@ def test_attn_running_max_moves(B, Sq, k):
     o, ref, l, lr = _attn_case(B, Sq, 64, 512, 4000, k, 16, 60000, "bf16", 44, scale=1.0, gain=40.0)
     assert row_rel_err(o, ref) <= 1e-2
     np.testing.assert_allclose(l, lr, rtol=1e-3, atol=1e-3)
+
+
+@pytest.mark.parametrize("hca_m,k", [(0, 100), (0, 2100), (128, 0)])
+def test_attn_bf16_cache_f32_output_no_lse(hca_m, k):
+    # fp32 output and no lse pointer on the many-row kernel: one slice, split slices (fp32 partials' bf16 path and
+    # the merge) and dense HCA rows
+    N = 3000 if hca_m == 0 else 300
+    q_start = 60000 if hca_m == 0 else 128 * N + 40
+    o, ref, l, lr = _attn_case(1, 260 if hca_m == 0 else 3, 64, 512, N, k, 128, q_start, "bf16", 47, hca_m=hca_m,
+                               scale=1.0 / math.sqrt(512), out_f32=True, with_lse=False)
+    assert row_rel_err(o, ref) <= 1e-2
 
 
 def test_attn_many_rows_empty_lists():
