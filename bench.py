@@ -98,9 +98,10 @@ def cpu_baseline_csa_decode(w, inp, sample_seqs: int, min_wall_s: float = 1.0):
         _oracle_csa_decode_once(w, inp, S, sl)
         reps += 1
     dt = time.perf_counter() - t0
-    return dict(value=reps * S / dt, unit="tokens/s", cores=orc.num_threads(), kind="oracle",
-                sample="%d repetition(s) of %d of %d sequences of one decode step (compress append, fp64 indexer "
-                       "scores over all %d entries, top-%d, attention); %.2f s wall" % (reps, S, w.B, w.N, w.k, dt))
+    return dict(value=reps * S * w.Sq / dt, unit="tokens/s", cores=orc.num_threads(), kind="oracle",
+                sample="%d repetition(s) of %d of %d sequences of one decode step of %d token(s) (compress append, "
+                       "fp64 indexer scores over all %d entries, top-%d, attention); %.2f s wall"
+                       % (reps, S, w.B, w.Sq, w.N, w.k, dt))
 
 
 def _oracle_csa_decode_once(w, inp, S, sl):
@@ -118,20 +119,22 @@ def _oracle_csa_decode_once(w, inp, S, sl):
         kc = orc.plain_cache(gen.bf16_bits(inp["keys"][sl]), "bf16")
         qc = orc.plain_cache(gen.bf16_bits(inp["qI"][sl]), "bf16")
     kc["cap"] = w.N
-    s64, s32, _, _ = orc.indexer_scores(qc, inp["w"][sl], kc, S, 1, w.HI, w.DI, w.N, 4, w.n_ctx,
+    Sq = w.Sq
+    s64, s32, _, _ = orc.indexer_scores(qc, inp["w"][sl], kc, S, Sq, w.HI, w.DI, w.N, 4, w.n_ctx,
                                         canonical=(w.key_fmt == "fp4"))
     scores = s32.astype(np.float64) if s32 is not None else s64
-    idx, _, _ = orc.topk(scores.reshape(S, w.N), orc.nvis_rows(S, [0], w.n_ctx, 4, w.N), w.k)
+    idx, _, _ = orc.topk(scores.reshape(S * Sq, w.N), orc.nvis_rows(S, list(range(Sq)), w.n_ctx, 4, w.N), w.k)
     if w.main_fmt == "mixed":
         cc = orc.encode(inp["comp"][sl].reshape(-1, w.D), "mixed", w.rope)
         rc = orc.encode(inp["window_kv"][sl].reshape(-1, w.D), "mixed", w.rope)
     else:
         cc = orc.plain_cache(gen.bf16_bits(inp["comp"][sl]), "bf16")
         rc = orc.plain_cache(gen.bf16_bits(inp["window_kv"][sl]), "bf16")
-    cc["cap"], rc["cap"] = w.N, w.window
+    S_raw = w.window + Sq - 1
+    cc["cap"], rc["cap"] = w.N, S_raw
     qa = orc.plain_cache(gen.bf16_bits(inp["q"][sl]), "bf16")
-    orc.attn(qa, cc, w.N, rc, w.n_ctx - w.window + 1, w.window, idx.reshape(S, 1, w.k), w.k, 0, inp["sink"], S, 1, w.H,
-             w.D, w.window, w.scale, w.n_ctx)
+    orc.attn(qa, cc, w.N, rc, w.n_ctx - w.window + 1, S_raw, idx.reshape(S, Sq, w.k), w.k, 0, inp["sink"], S, Sq,
+             w.H, w.D, w.window, w.scale, w.n_ctx)
 
 
 def cpu_baseline_hca_decode(w, inp, sample_seqs: int, min_wall_s: float = 1.0):
@@ -176,7 +179,7 @@ def main():
     w = gen.WORKLOADS[args.workload]
     torch.cuda.init()
     t_gen = time.perf_counter()
-    if w.Sq == 1:
+    if w.is_decode:
         inp = gen.decode_inputs(w)
         step = (steps.HcaDecode if w.HI == 0 else steps.CsaDecode)(w, inp, copies=args.copies)
         copies = args.copies
@@ -250,7 +253,7 @@ def main():
     src = ["long_context_attention_05_amd/csrc/indexer.hip", "long_context_attention_05_amd/csrc/lca_device.h",
            "long_context_attention_05_amd/build.py"]
     if has_scores:
-        if w.Sq == 1:
+        if w.is_decode:
             kname = "idx_score_decode_fp4_ring" if w.key_fmt == "fp4" else "idx_score_decode_bf16"
             per_launch = step.score_kernel_bytes()
             achieved = per_launch / (avg_ms / 1e3) / 1e9
@@ -266,9 +269,9 @@ def main():
                                "traffic": traffic_record("idx_score_mfma", w.name, src, per_launch),
                                "avg_launch_us": avg_ms * 1e3, "algorithmic_flops_per_launch": per_launch}
     if not args.no_cpu_baseline:
-        if w.Sq == 1 and w.HI > 0:
+        if w.is_decode and w.HI > 0:
             res["cpu_baseline"] = cpu_baseline_csa_decode(w, inp, sample_seqs=w.B)
-        elif w.Sq == 1:
+        elif w.is_decode:
             res["cpu_baseline"] = cpu_baseline_hca_decode(w, inp, sample_seqs=w.B)
     print(json.dumps(res), flush=True)
 

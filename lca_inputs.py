@@ -68,6 +68,11 @@ class Workload:
     def N(self) -> int:
         return self.n_ctx // self.m
 
+    @property
+    def is_decode(self) -> bool:
+        """A decode step: one token, or a few draft tokens verified together, against a given cache."""
+        return self.n_ctx > 0 and self.Sq <= 4
+
 
 # The five workloads of the layer (sizes from the pages' 128K-1M contexts, Pro/Flash k = 1024/512).
 WORKLOADS = {
@@ -82,6 +87,11 @@ WORKLOADS = {
                                    "bf16", "bf16", "bf16", "bf16", 1.0, 1.0 / math.sqrt(512)),
     "csa_decode_1m_mixed": Workload("csa_decode_1m_mixed", 105, 4, 1 << 20, 1, 4, 512, 64, 64, 64, 128, 1024, 128,
                                     "mixed", "fp4", "bf16", "fp4", 1.0, 1.0 / math.sqrt(512)),
+    # multi-token prediction: each step verifies two tokens per sequence (the new one and one draft)
+    "csa_decode_128k_bf16_mtp2": Workload("csa_decode_128k_bf16_mtp2", 106, 16, 131072, 2, 4, 512, 64, 64, 64, 128,
+                                          512, 128, "bf16", "bf16", "bf16", "bf16", 1.0 / math.sqrt(512), 1.0),
+    "csa_decode_1m_mixed_mtp2": Workload("csa_decode_1m_mixed_mtp2", 107, 4, 1 << 20, 2, 4, 512, 64, 64, 64, 128,
+                                         1024, 128, "mixed", "fp4", "bf16", "fp4", 1.0, 1.0 / math.sqrt(512)),
 }
 
 
@@ -91,11 +101,12 @@ def scaled(w: Workload, **kw) -> Workload:
 
 
 def decode_inputs(w: Workload) -> dict:
-    """One decode step (Sq = 1 new token at position n_ctx) over a cache that is given directly.
+    """One decode step (Sq <= 4 new tokens at positions n_ctx .. n_ctx + Sq - 1; n_ctx is a multiple of m) over a
+    cache that is given directly.
 
-    Draw order: comp cache [B, N, D]; indexer keys [B, N, DI]; window KV [B, window, D] (raw positions
-    n_ctx - window + 1 .. n_ctx); q [B, 1, H, D] * q_std; qI [B, 1, HI, DI]; w [B, 1, HI] / sqrt(DI * HI);
-    sink [H]; then the new token's compression streams (Ca, Cb, Za, Zb [B, 1, D] and [B, 1, DI]) and the
+    Draw order: comp cache [B, N, D]; indexer keys [B, N, DI]; window KV [B, window + Sq - 1, D] (raw positions
+    n_ctx - window + 1 .. n_ctx + Sq - 1); q [B, Sq, H, D] * q_std; qI [B, Sq, HI, DI]; w [B, Sq, HI] / sqrt(DI * HI);
+    sink [H]; then the new tokens' compression streams (Ca, Cb, Za, Zb [B, Sq, D] and [B, Sq, DI]) and the
     carried previous block's stream-b tail (tail_Cb, tail_Zb [B, m, D] / [B, m, DI]) and the position
     biases Ba, Bb [m, D] / [m, DI] (std 0.1).  For HCA (no indexer) the indexer tensors are skipped and
     the streams have a single C/Z pair of width D.
@@ -106,19 +117,19 @@ def decode_inputs(w: Workload) -> dict:
     out["comp"] = normal(g, (w.B, N, w.D))
     if w.HI:
         out["keys"] = normal(g, (w.B, N, w.DI))
-    out["window_kv"] = normal(g, (w.B, w.window, w.D))
-    out["q"] = normal(g, (w.B, 1, w.H, w.D), w.q_std)
+    out["window_kv"] = normal(g, (w.B, w.window + w.Sq - 1, w.D))
+    out["q"] = normal(g, (w.B, w.Sq, w.H, w.D), w.q_std)
     if w.HI:
-        out["qI"] = normal(g, (w.B, 1, w.HI, w.DI))
-        out["w"] = normal(g, (w.B, 1, w.HI), 1.0 / math.sqrt(w.DI * w.HI))
+        out["qI"] = normal(g, (w.B, w.Sq, w.HI, w.DI))
+        out["w"] = normal(g, (w.B, w.Sq, w.HI), 1.0 / math.sqrt(w.DI * w.HI))
     out["sink"] = normal(g, (w.H,))
     overlap = (w.m == 4)
     for tag, c in (("", w.D),) + ((("_I", w.DI),) if w.HI else ()):
-        out["Ca" + tag] = normal(g, (w.B, 1, c))
-        out["Za" + tag] = normal(g, (w.B, 1, c))
+        out["Ca" + tag] = normal(g, (w.B, w.Sq, c))
+        out["Za" + tag] = normal(g, (w.B, w.Sq, c))
         if overlap:
-            out["Cb" + tag] = normal(g, (w.B, 1, c))
-            out["Zb" + tag] = normal(g, (w.B, 1, c))
+            out["Cb" + tag] = normal(g, (w.B, w.Sq, c))
+            out["Zb" + tag] = normal(g, (w.B, w.Sq, c))
             out["tail_Cb" + tag] = normal(g, (w.B, w.m, c))
             out["tail_Zb" + tag] = normal(g, (w.B, w.m, c))
         out["Ba" + tag] = normal(g, (w.m, c), 0.1)

@@ -262,8 +262,8 @@ void lca_set_attn_events(void* ev_begin, void* ev_end) {
   t_attn_ev_end = (hipEvent_t)ev_end;
 }
 
-// Workspace of indexer_score_topk: the score keys [B * Sq][N]; for one query row per sequence (decode) also the
-// select buffers of the decode path: per-row histograms, per-slice counts and candidate segments.
+// Workspace of indexer_score_topk: the score keys [B * Sq][N]; for up to kDecodeMaxRows query rows per sequence
+// (decode) also the select buffers of the decode path: per-row histograms, per-slice counts and candidate segments.
 struct IdxWs {
   size_t keys, state, counts, cand, total;
 };
@@ -274,7 +274,7 @@ IdxWs idx_ws_layout(int B, int Sq, int N) {
   const size_t rows = (size_t)B * Sq;
   l.keys = 0;
   size_t off = align_up(rows * N * sizeof(uint32_t));
-  if (Sq == 1 && N <= kMaxMultiN) {
+  if (Sq <= kDecodeMaxRows && N <= kMaxMultiN) {
     const size_t slots = ((size_t)N + kSliceKeys - 1) / kSliceKeys;
     l.state = off;
     off += align_up(rows * kSelStateInts * sizeof(int));
@@ -310,8 +310,8 @@ int indexer_score_topk(lca_tensor qI, const float* w, lca_tensor kI, int B, int 
   if (N > 0 && (!ws || ws_bytes < indexer_score_topk_workspace_size(B, Sq, N, k))) return LCA_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   const IdxWs L = idx_ws_layout(B, Sq, N > 0 ? N : 1);
-  const bool multi = N > 0 && Sq == 1 && N <= kMaxMultiN &&
-                     indexer_uses_decode_kernel(B, Sq, HI, DI, qI.format, kI.format);
+  const bool multi = N > 0 && Sq <= kDecodeMaxRows && N <= kMaxMultiN &&
+                     indexer_uses_decode_kernel(B, Sq, HI, DI, N, qI.format, kI.format);
   char* wsb = (char*)ws;
   int* state = multi ? (int*)(wsb + L.state) : nullptr;
   IdxArgs a{qI, kI, w, (uint32_t*)(wsb + L.keys), B, Sq, HI, DI, N, m, q_start_pos, state};

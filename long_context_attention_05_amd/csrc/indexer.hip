@@ -249,8 +249,12 @@ __global__ __launch_bounds__(256) void idx_score_mfma(IdxArgs a, int qpb) {
 }
 
 // ------------------------------------------------------------------------------------------------
-// decode kernels (one query row per sequence): the key stream is the whole cost
+// decode kernels (up to kDecodeMaxRows query rows per sequence): the key stream is the whole cost
 // ------------------------------------------------------------------------------------------------
+// Grid y is the query row b * Sq + r.  With several rows the grid's x extent (key ranges) is rounded up to a multiple
+// of eight, the XCD count: the workgroups of a sequence's rows for one key range are then a multiple of eight apart
+// in dispatch order, so they run on one XCD at about the same time and the later rows read the keys from its L2
+// rather than from memory.  The padding workgroups find no keys and exit.
 // Both formats use 16-key MFMA column blocks whose B operand is a run of whole cache rows, so each lane loads its
 // operand bytes straight from HBM into registers (no LDS staging, no barriers in the loop).  A wave streams its own
 // slab of keys in stages; the next stage's loads are issued, unconditionally, before the current stage is scored,
@@ -355,8 +359,8 @@ __global__ __launch_bounds__(256, 2) void idx_score_decode_bf16(IdxArgs a) {
   constexpr int KPW = 16 * kBfGroups;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int g = lane >> 4, col = lane & 15;
-  const int b = blockIdx.y;
-  const int nvis = nvis_of(a.q_start, a.m, a.N);
+  const int qrow = blockIdx.y, b = qrow / a.Sq;  // query row b * Sq + r
+  const int nvis = nvis_of(a.q_start + (qrow - b * a.Sq), a.m, a.N);
   const int k0 = blockIdx.x * (NST * 4 * KPW);
   const int k1 = min(k0 + NST * 4 * KPW, nvis);
   if (k0 >= k1) return;
@@ -371,11 +375,11 @@ __global__ __launch_bounds__(256, 2) void idx_score_decode_bf16(IdxArgs a) {
   float wv[4][4];
 #pragma unroll
   for (int T = 0; T < 4; ++T) {
-    const uint8_t* qrow = (const uint8_t*)a.q.data + ((long long)b * 64 + 16 * T + col) * 256;
+    const uint8_t* qp = (const uint8_t*)a.q.data + ((long long)qrow * 64 + 16 * T + col) * 256;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) qa[T][s] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(qrow + 16 * g + 64 * s));
+    for (int s = 0; s < 4; ++s) qa[T][s] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(qp + 16 * g + 64 * s));
 #pragma unroll
-    for (int r = 0; r < 4; ++r) wv[T][r] = a.w[(long long)b * 64 + 16 * T + 4 * g + r];
+    for (int r = 0; r < 4; ++r) wv[T][r] = a.w[(long long)qrow * 64 + 16 * T + 4 * g + r];
   }
   if (hist) __syncthreads();  // histogram zeroed before any update
 
@@ -389,7 +393,7 @@ __global__ __launch_bounds__(256, 2) void idx_score_decode_bf16(IdxArgs a) {
       bf_load_stage(S[(st + 1) & 1], kb, kbase + 4 * KPW, k1 - 1, lane);
       __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the scoring
     }
-    if (st > 0) store_key(a, b, k1, pend, hist_s, hist);
+    if (st > 0) store_key(a, qrow, k1, pend, hist_s, hist);
     const BfStage& C = S[st & 1];
     float v[kBfGroups][4];
 #pragma unroll
@@ -407,8 +411,8 @@ __global__ __launch_bounds__(256, 2) void idx_score_decode_bf16(IdxArgs a) {
     }
     pend = lane_key(kbase, g, head_cross4(v));
   }
-  store_key(a, b, k1, pend, hist_s, hist);
-  if (hist) flush_hist(hist_s, a.sel_state + (long long)b * kSelStateInts);
+  store_key(a, qrow, k1, pend, hist_s, hist);
+  if (hist) flush_hist(hist_s, a.sel_state + (long long)qrow * kSelStateInts);
 }
 
 typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8_t;
@@ -491,8 +495,8 @@ __global__ __launch_bounds__(kF4rWaves * 64) void idx_score_decode_fp4_ring(IdxA
 #pragma clang fp contract(off)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int col = lane & 31, hh = lane >> 5;
-  const int b = blockIdx.y;
-  const int nvis = nvis_of(a.q_start, a.m, a.N);
+  const int qrow = blockIdx.y, b = qrow / a.Sq;  // query row b * Sq + r
+  const int nvis = nvis_of(a.q_start + (qrow - b * a.Sq), a.m, a.N);
   const int k0 = blockIdx.x * (NST * kF4rStage);
   const int k1 = min(k0 + NST * kF4rStage, nvis);
   if (k0 >= k1) return;  // block-uniform
@@ -507,12 +511,12 @@ __global__ __launch_bounds__(kF4rWaves * 64) void idx_score_decode_fp4_ring(IdxA
   float wv[2][16];
 #pragma unroll
   for (int T = 0; T < 2; ++T) {
-    const long long row = (long long)b * 64 + 32 * T + col;
+    const long long row = (long long)qrow * 64 + 32 * T + col;
 #pragma unroll
     for (int i = 0; i < 2; ++i) qraw[T][i] = *(const uint4*)((const uint8_t*)a.q.data + row * 64 + 16 * (2 * i + hh));
     sraw[T] = *(const uint2*)((const uint8_t*)a.q.scale + row * 8);
 #pragma unroll
-    for (int k = 0; k < 16; ++k) wv[T][k] = a.w[(long long)b * 64 + 32 * T + 8 * (k >> 2) + 4 * hh + (k & 3)];
+    for (int k = 0; k < 16; ++k) wv[T][k] = a.w[(long long)qrow * 64 + 32 * T + 8 * (k >> 2) + 4 * hh + (k & 3)];
   }
   __builtin_amdgcn_sched_barrier(0);
   i32x8_t qop[2][2][2];
@@ -622,7 +626,7 @@ __global__ __launch_bounds__(kF4rWaves * 64) void idx_score_decode_fp4_ring(IdxA
     kept[st] = score(std::integral_constant<int, st % 4>{}, st);
     // lane (col, hh) stores tile hh's key col: 64 keys per store
     const int e = k0 + st * kF4rStage + 64 * wave + 32 * hh + col;
-    a.keys[(long long)b * a.N + min(e, k1 - 1)] = hh ? kept[st].y : kept[st].x;
+    a.keys[(long long)qrow * a.N + min(e, k1 - 1)] = hh ? kept[st].y : kept[st].x;
   };
   unroll_steps<0, NST>(step);
   if (hist) {
@@ -633,12 +637,20 @@ __global__ __launch_bounds__(kF4rWaves * 64) void idx_score_decode_fp4_ring(IdxA
       if (e < k1) atomicAdd(&f4r_hist[(hh ? kept[st].y : kept[st].x) >> 21], 1);
     }
   }
-  if (hist) flush_hist(f4r_hist, a.sel_state + (long long)b * kSelStateInts);
+  if (hist) flush_hist(f4r_hist, a.sel_state + (long long)qrow * kSelStateInts);
 }
 
-bool indexer_uses_decode_kernel(int B, int Sq, int HI, int DI, int q_format, int k_format) {
+// key ranges of a decode launch: a multiple of the eight XCDs when several rows share them
+static int decode_grid_x(int ranges, int Sq) { return Sq > 1 ? (ranges + 7) & ~7 : ranges; }
+
+// A bf16 row costs the decode kernel a whole pass of MFMAs and head tree per key, while the many-row kernel keeps a
+// key tile in registers across rows; with three or four bf16 rows of up to kTopkLdsKeys entries (whose selection
+// then runs from LDS) the many-row path is the faster one.
+bool indexer_uses_decode_kernel(int B, int Sq, int HI, int DI, int N, int q_format, int k_format) {
   (void)B;
-  return Sq == 1 && HI == 64 && DI == 128 && q_format == k_format && (q_format == LCA_BF16 || q_format == LCA_FP4);
+  if (Sq < 1 || Sq > kDecodeMaxRows || HI != 64 || DI != 128 || q_format != k_format) return false;
+  if (q_format == LCA_FP4) return true;
+  return q_format == LCA_BF16 && (Sq <= 2 || N > kTopkLdsKeys);
 }
 
 hipError_t launch_indexer_scores(const IdxArgs& a, hipStream_t st) {
@@ -647,13 +659,15 @@ hipError_t launch_indexer_scores(const IdxArgs& a, hipStream_t st) {
   clear_stale_error();
   const bool mfma = a.HI == 64 && a.DI == 128 && a.q.format == a.k.format &&
                     (a.q.format == LCA_BF16 || a.q.format == LCA_FP4);
-  if (indexer_uses_decode_kernel(a.B, a.Sq, a.HI, a.DI, a.q.format, a.k.format)) {
+  if (indexer_uses_decode_kernel(a.B, a.Sq, a.HI, a.DI, a.N, a.q.format, a.k.format)) {
     const bool fp4 = a.q.format == LCA_FP4;
     if (fp4) {
       // one workgroup per CU where the context allows: the most stages per workgroup that still leave 256
+      const long long rows = (long long)a.B * a.Sq;
       int nst = 8;
-      while (nst > 1 && (long long)a.B * ((nvis_max + nst * kF4rStage - 1) / (nst * kF4rStage)) < 256) nst >>= 1;
-      const dim3 grid((unsigned)((nvis_max + nst * kF4rStage - 1) / (nst * kF4rStage)), (unsigned)a.B);
+      while (nst > 1 && rows * ((nvis_max + nst * kF4rStage - 1) / (nst * kF4rStage)) < 256) nst >>= 1;
+      const dim3 grid((unsigned)decode_grid_x((nvis_max + nst * kF4rStage - 1) / (nst * kF4rStage), a.Sq),
+                      (unsigned)rows);
       const dim3 block(kF4rWaves * 64);
       if (nst == 8) hipLaunchKernelGGL(idx_score_decode_fp4_ring<8>, grid, block, 0, st, a);
       else if (nst == 4) hipLaunchKernelGGL(idx_score_decode_fp4_ring<4>, grid, block, 0, st, a);
@@ -664,9 +678,10 @@ hipError_t launch_indexer_scores(const IdxArgs& a, hipStream_t st) {
     // a fixed key range per workgroup (NST stages of 4 waves x KPW keys), the grid grows with the context; fewer
     // stages when that leaves fewer than about two workgroups per CU
     const int kpw = 16 * kBfGroups;
+    const long long rows = (long long)a.B * a.Sq;
     int nst = 4;
-    while (nst > 1 && (long long)a.B * ((nvis_max + nst * 4 * kpw - 1) / (nst * 4 * kpw)) < 512) nst >>= 1;
-    const dim3 grid((unsigned)((nvis_max + nst * 4 * kpw - 1) / (nst * 4 * kpw)), (unsigned)a.B);
+    while (nst > 1 && rows * ((nvis_max + nst * 4 * kpw - 1) / (nst * 4 * kpw)) < 512) nst >>= 1;
+    const dim3 grid((unsigned)decode_grid_x((nvis_max + nst * 4 * kpw - 1) / (nst * 4 * kpw), a.Sq), (unsigned)rows);
     if (nst == 4) hipLaunchKernelGGL(idx_score_decode_bf16<4>, grid, dim3(256), 0, st, a);
     else if (nst == 2) hipLaunchKernelGGL(idx_score_decode_bf16<2>, grid, dim3(256), 0, st, a);
     else hipLaunchKernelGGL(idx_score_decode_bf16<1>, grid, dim3(256), 0, st, a);

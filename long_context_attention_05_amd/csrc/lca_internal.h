@@ -31,8 +31,13 @@ struct IdxArgs {
   long long q_start;
   int* sel_state;  // nullable: [B * Sq][kSelStateInts] row histograms the decode kernels add into (zeroed first)
 };
-// Whether launch_indexer_scores takes the one-row-per-sequence decode kernels (which fill sel_state).
-bool indexer_uses_decode_kernel(int B, int Sq, int HI, int DI, int q_format, int k_format);
+// Decode kernels take up to this many query rows per sequence (one token, or a few draft tokens verified together):
+// the rows of a sequence score the same keys side by side, so the key stream is read from memory about once.
+constexpr int kDecodeMaxRows = 4;
+// Rows of at most this many keys are selected from an LDS copy by the many-row top-k.
+constexpr int kTopkLdsKeys = 32768;
+// Whether launch_indexer_scores takes the decode kernels (which fill sel_state) for N entries per sequence.
+bool indexer_uses_decode_kernel(int B, int Sq, int HI, int DI, int N, int q_format, int k_format);
 hipError_t launch_indexer_scores(const IdxArgs& a, hipStream_t st);
 
 // stage 2b, exact top-k (topk.hip)

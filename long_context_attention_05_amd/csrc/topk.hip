@@ -16,7 +16,7 @@ namespace lca {
 
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kLdsKeys = 32768;  // 128 KB of keys in LDS
+constexpr int kLdsKeys = kTopkLdsKeys;  // 128 KB of keys in LDS
 constexpr size_t kSelDynLds = (size_t)kLdsKeys * 4;
 
 
@@ -202,8 +202,8 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(SelArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------------
-// decode rows (one query per sequence): the scoring kernel has already built each row's histogram of key bits
-// [31:21], so pass 1 is a read of 2048 counts instead of a pass over the keys.  Every pass over all the keys runs
+// decode rows (up to kDecodeMaxRows queries per sequence): the scoring kernel has already built each row's
+// histogram of key bits [31:21], so pass 1 is a read of 2048 counts instead of a pass over the keys.  Every pass over all the keys runs
 // spread over many workgroups; one workgroup per row then works on a few thousand candidates only.
 // ------------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void sel_zero_kernel(int* state) {

@@ -87,36 +87,38 @@ class _Streams:
 
 
 class CsaDecode:
-    """CSA decode step of a batch of B sequences holding n_ctx tokens (N = n_ctx / 4 committed entries)."""
+    """CSA decode step of a batch of B sequences holding n_ctx tokens (N = n_ctx / 4 committed entries); Sq <= 4
+    new tokens per sequence (the new token and its drafts) are appended, scored and attended together."""
 
     def __init__(self, w, inp: dict, copies: int = 1):
         self.w = w
-        B, N, D, DI, HI, H, k = w.B, w.N, w.D, w.DI, w.HI, w.H, w.k
+        B, N, D, DI, HI, H, k, Sq = w.B, w.N, w.D, w.DI, w.HI, w.H, w.k, w.Sq
         self.copies = copies
         cap = N + 1  # room for the provisional entry of the block the new token starts
         base_comp = make_cache(w.main_fmt, B, cap, D, w.rope, inp["comp"])
         base_keys = make_cache(w.key_fmt, B, cap, DI, 0, inp["keys"])
-        base_raw = make_cache(w.main_fmt, B, w.window, D, w.rope, inp["window_kv"])
+        self.S_raw = w.window + Sq - 1
+        base_raw = make_cache(w.main_fmt, B, self.S_raw, D, w.rope, inp["window_kv"])
         self.comp = [base_comp] + [clone_cache(base_comp) for _ in range(copies - 1)]
         self.keys = [base_keys] + [clone_cache(base_keys) for _ in range(copies - 1)]
         self.raw = [base_raw] + [clone_cache(base_raw) for _ in range(copies - 1)]
         self.q = _up(_bf16_bits(inp["q"]))
         if w.qi_fmt == "fp4":
-            self.qI = make_cache("fp4", B, HI, DI, 0, inp["qI"].reshape(B, HI, DI))
+            self.qI = make_cache("fp4", B, Sq * HI, DI, 0, inp["qI"].reshape(B, Sq * HI, DI))
             self.qI_desc = self.qI.desc()
         else:
             self.qI = _up(_bf16_bits(inp["qI"]))
-            self.qI_desc = lca.plain_desc(self.qI, "bf16", DI, HI)
+            self.qI_desc = lca.plain_desc(self.qI, "bf16", DI, Sq * HI)
         self.wgt = _up(inp["w"])
         self.sink = _up(inp["sink"])
         self.main = _Streams(inp, "", True, True)
         self.ind = _Streams(inp, "_I", True, True)
-        self.idx = torch.empty((B, 1, k), dtype=torch.int32, device=DEV)
-        self.scores = torch.empty((B, 1, k), dtype=torch.float32, device=DEV)
-        self.out = torch.empty((B, 1, H, D), dtype=torch.int16, device=DEV)
-        self.lse = torch.empty((B, 1, H), dtype=torch.float32, device=DEV)
-        self.ws_i_bytes = lca.indexer_score_topk_workspace_size(B, 1, N, k)
-        self.ws_a_bytes = lca.sparse_mqa_attn_workspace_size(B, 1, H, D, w.window + k)
+        self.idx = torch.empty((B, Sq, k), dtype=torch.int32, device=DEV)
+        self.scores = torch.empty((B, Sq, k), dtype=torch.float32, device=DEV)
+        self.out = torch.empty((B, Sq, H, D), dtype=torch.int16, device=DEV)
+        self.lse = torch.empty((B, Sq, H), dtype=torch.float32, device=DEV)
+        self.ws_i_bytes = lca.indexer_score_topk_workspace_size(B, Sq, N, k)
+        self.ws_a_bytes = lca.sparse_mqa_attn_workspace_size(B, Sq, H, D, w.window + k)
         self.ws_i = torch.empty(max(self.ws_i_bytes, 256), dtype=torch.uint8, device=DEV)
         self.ws_a = torch.empty(max(self.ws_a_bytes, 256), dtype=torch.uint8, device=DEV)
         self.raw_start = w.n_ctx - w.window + 1
@@ -125,30 +127,30 @@ class CsaDecode:
         w = self.w
         self.main.compress(4, True, w.n_ctx, self.comp[c], stream)
         self.ind.compress(4, True, w.n_ctx, self.keys[c], stream)
-        lca.indexer_score_topk(self.qI_desc, self.wgt, self.keys[c].desc(), w.B, 1, w.HI, w.DI, w.N, 4, w.k, w.n_ctx,
-                               self.idx, self.scores, self.ws_i, self.ws_i_bytes, stream)
+        lca.indexer_score_topk(self.qI_desc, self.wgt, self.keys[c].desc(), w.B, w.Sq, w.HI, w.DI, w.N, 4, w.k,
+                               w.n_ctx, self.idx, self.scores, self.ws_i, self.ws_i_bytes, stream)
         lca.sparse_mqa_attn(self.q, lca.LCA_BF16, self.comp[c].desc(), w.N, self.raw[c].desc(), self.raw_start,
-                            w.window, self.idx, w.k, self.sink, w.B, 1, w.H, w.D, w.window, w.scale, w.n_ctx, self.out,
-                            lca.LCA_BF16, self.lse, self.ws_a, self.ws_a_bytes, stream)
+                            self.S_raw, self.idx, w.k, self.sink, w.B, w.Sq, w.H, w.D, w.window, w.scale, w.n_ctx,
+                            self.out, lca.LCA_BF16, self.lse, self.ws_a, self.ws_a_bytes, stream)
 
     # algorithmic traffic and work of one step (what the method must move / compute)
     def score_kernel_bytes(self) -> int:
         w = self.w
-        key_b = _entry_bytes(w.key_fmt, w.DI, 0) * w.B * w.N
-        qi_b = _entry_bytes(w.qi_fmt, w.DI, 0) * w.B * w.HI
-        return key_b + qi_b + 4 * w.B * w.HI
+        key_b = _entry_bytes(w.key_fmt, w.DI, 0) * w.B * w.N  # every visible key once, whatever Sq
+        qi_b = _entry_bytes(w.qi_fmt, w.DI, 0) * w.B * w.Sq * w.HI
+        return key_b + qi_b + 4 * w.B * w.Sq * w.HI
 
     def step_bytes(self) -> int:
         w = self.w
         eb = _entry_bytes(w.main_fmt, w.D, w.rope)
-        gather = eb * w.B * (w.k + w.window)
-        q_out = 2 * 2 * w.B * w.H * w.D
-        idx = 2 * 4 * w.B * w.k
+        gather = eb * w.B * w.Sq * (w.k + w.window)
+        q_out = 2 * 2 * w.B * w.Sq * w.H * w.D
+        idx = 2 * 4 * w.B * w.Sq * w.k
         return self.score_kernel_bytes() + gather + q_out + idx + self.main.nbytes + self.ind.nbytes
 
     def step_flops(self) -> int:
         w = self.w
-        return 2 * w.B * w.HI * w.DI * w.N + 4 * w.B * w.H * w.D * (w.k + w.window)
+        return w.Sq * (2 * w.B * w.HI * w.DI * w.N + 4 * w.B * w.H * w.D * (w.k + w.window))
 
 
 class HcaDecode:

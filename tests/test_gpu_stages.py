@@ -190,6 +190,24 @@ def test_indexer_fp4_bit_exact(B, Sq, N, k, HI, DI):
     _indexer_case(B, Sq, HI, DI, N, 4, k, 4 * N, "fp4", 14)
 
 
+@pytest.mark.parametrize("B,Sq,N,k,q_off,fmt", [(3, 2, 2037, 512, -1, "bf16"), (2, 4, 16411, 512, -2, "bf16"),
+                                                (2, 4, 3001, 1024, -3, "fp4"), (1, 2, 70000, 1024, -1, "fp4"),
+                                                (4, 3, 8200, 512, 0, "bf16")])
+def test_indexer_decode_multi_row(B, Sq, N, k, q_off, fmt):
+    # several query rows per sequence (draft tokens verified together) share the decode kernels; with q_start just
+    # below a multiple of m the rows see N - 1 and N entries
+    st = _indexer_case(B, Sq, 64, 128, N, 4, k, 4 * N + q_off, fmt, 20 + Sq)
+    if fmt == "bf16":
+        assert st["exact_rows"] >= st["rows"] - 1
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp4"])
+def test_indexer_decode_multi_row_short(fmt):
+    # rows on either side of k (511 and 512 visible entries, k = 511) and rows that see no entry at all
+    _indexer_case(1, 4, 64, 128, 600, 4, 511, 4 * 512 - 2, fmt, 30)
+    _indexer_case(2, 4, 64, 128, 600, 4, 64, 2, fmt, 31)
+
+
 @pytest.mark.parametrize("fmt", ["bf16", "f32"])
 def test_indexer_all_scores_equal(fmt):
     # many rows (the LDS select) and a decode row (the multi-workgroup select): one key value, so the first k

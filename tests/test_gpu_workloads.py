@@ -99,7 +99,8 @@ def test_tiny_csa_prefill_f32_full_chain():
 
 # ------------------------------------------------------------------------------------------------------
 def _check_decode(w, inp, step):
-    B, N = w.B, w.N
+    B, N, Sq = w.B, w.N, w.Sq
+    R = B * Sq  # query rows
     torch.cuda.synchronize()
     # appended entries (block N, provisional): latent and indexer key
     for tag, cache, c, fmt in (("", step.comp[0], w.D, w.main_fmt), ("_I", step.keys[0], w.DI, w.key_fmt)):
@@ -123,17 +124,17 @@ def _check_decode(w, inp, step):
         kc = orc.plain_cache(_bf16(inp["keys"]), "bf16")
         qc = orc.plain_cache(_bf16(inp["qI"]), "bf16")
     kc["cap"] = N
-    s64, s32, ab, bad = orc.indexer_scores(qc, inp["w"], kc, B, 1, w.HI, w.DI, N, 4, w.n_ctx, canonical=exact,
+    s64, s32, ab, bad = orc.indexer_scores(qc, inp["w"], kc, B, Sq, w.HI, w.DI, N, 4, w.n_ctx, canonical=exact,
                                            want_abs=True)
     if exact:
         assert bad == 0
-    nv = orc.nvis_rows(B, [0], w.n_ctx, 4, N)
-    gidx = step.idx.cpu().numpy().reshape(B, w.k)
-    st = check_topk(gidx, step.scores.cpu().numpy().reshape(B, w.k), s64.reshape(B, N), ab.reshape(B, N), nv, w.k,
-                    GAMMA(w.DI, w.HI), exact=exact, s32=None if s32 is None else s32.reshape(B, N))
+    nv = orc.nvis_rows(B, list(range(Sq)), w.n_ctx, 4, N)
+    gidx = step.idx.cpu().numpy().reshape(R, w.k)
+    st = check_topk(gidx, step.scores.cpu().numpy().reshape(R, w.k), s64.reshape(R, N), ab.reshape(R, N), nv, w.k,
+                    GAMMA(w.DI, w.HI), exact=exact, s32=None if s32 is None else s32.reshape(R, N))
     # attention with the oracle's own selection, on rows whose selection matches
     ref_scores = s32.astype(np.float64) if exact else s64
-    oidx, _, _ = orc.topk(ref_scores.reshape(B, N), nv, w.k)
+    oidx, _, _ = orc.topk(ref_scores.reshape(R, N), nv, w.k)
     if w.main_fmt == "mixed":
         cc = orc.encode(inp["comp"].reshape(-1, w.D), "mixed", w.rope)
         rc = orc.encode(inp["window_kv"].reshape(-1, w.D), "mixed", w.rope)
@@ -143,15 +144,17 @@ def _check_decode(w, inp, step):
     else:
         cc = orc.plain_cache(_bf16(inp["comp"]), "bf16")
         rc = orc.plain_cache(_bf16(inp["window_kv"]), "bf16")
-    cc["cap"], rc["cap"] = N, w.window
+    S_raw = w.window + Sq - 1
+    cc["cap"], rc["cap"] = N, S_raw
     qa = orc.plain_cache(_bf16(inp["q"]), "bf16")
     rows = _attn_rows_match(gidx, oidx)
-    assert len(rows) >= B - 1
-    o_ref, l_ref = orc.attn(qa, cc, N, rc, w.n_ctx - w.window + 1, w.window, oidx.reshape(B, 1, w.k), w.k, 0,
-                            inp["sink"], B, 1, w.H, w.D, w.window, w.scale, w.n_ctx)
-    o = bf16_to_f64(step.out.cpu().numpy().view(np.uint16)).reshape(B, w.H, w.D)
-    assert row_rel_err(o[rows], o_ref[rows, 0]) <= 1e-2
-    np.testing.assert_allclose(step.lse.cpu().numpy().reshape(B, w.H)[rows], l_ref[rows, 0], rtol=1e-3, atol=1e-3)
+    assert len(rows) >= R - 1
+    o_ref, l_ref = orc.attn(qa, cc, N, rc, w.n_ctx - w.window + 1, S_raw, oidx.reshape(B, Sq, w.k), w.k, 0,
+                            inp["sink"], B, Sq, w.H, w.D, w.window, w.scale, w.n_ctx)
+    o = bf16_to_f64(step.out.cpu().numpy().view(np.uint16)).reshape(R, w.H, w.D)
+    assert row_rel_err(o[rows], o_ref.reshape(R, w.H, w.D)[rows]) <= 1e-2
+    np.testing.assert_allclose(step.lse.cpu().numpy().reshape(R, w.H)[rows], l_ref.reshape(R, w.H)[rows], rtol=1e-3,
+                               atol=1e-3)
     return st
 
 
@@ -172,6 +175,25 @@ def test_csa_decode_1m_mixed_full():
     step.run()
     st = _check_decode(w, inp, step)
     assert st["exact_rows"] == w.B
+
+
+def test_csa_decode_128k_bf16_mtp2_full():
+    """Two query rows per sequence (a new token and one draft) through the decode kernels."""
+    w = gen.WORKLOADS["csa_decode_128k_bf16_mtp2"]
+    inp = gen.decode_inputs(w)
+    step = steps.CsaDecode(w, inp, copies=1)
+    step.run()
+    st = _check_decode(w, inp, step)
+    assert st["exact_rows"] >= w.B * w.Sq - 1
+
+
+def test_csa_decode_1m_mixed_mtp2_full():
+    w = gen.WORKLOADS["csa_decode_1m_mixed_mtp2"]
+    inp = gen.decode_inputs(w)
+    step = steps.CsaDecode(w, inp, copies=1)
+    step.run()
+    st = _check_decode(w, inp, step)
+    assert st["exact_rows"] == w.B * w.Sq
 
 
 # ------------------------------------------------------------------------------------------------------
