@@ -311,7 +311,8 @@ def test_attn_simt_f32_multisplit_and_mixed():
 @pytest.mark.parametrize("B,Sq,N,k,window,fmt", [(2, 1, 3000, 512, 128, "bf16"), (1, 300, 2000, 64, 128, "bf16"),
                                                   (2, 1, 5000, 1024, 128, "mixed"), (1, 3, 500, 100, 7, "bf16"),
                                                   (3, 1, 900, 300, 40, "mixed"), (1, 1, 5000, 2100, 128, "bf16"),
-                                                  (1, 2, 6000, 2100, 128, "mixed")])
+                                                  (1, 2, 6000, 2100, 128, "mixed"), (4, 4, 20000, 1024, 128, "mixed"),
+                                                  (8, 2, 32768, 512, 128, "bf16")])
 def test_attn_mfma(B, Sq, N, k, window, fmt):
     o, ref, l, lr = _attn_case(B, Sq, 64, 512, N, k, window, 60000, fmt, 23, scale=1.0)
     assert row_rel_err(o, ref) <= 1e-2
