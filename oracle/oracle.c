@@ -253,6 +253,24 @@ void orc_decode_rows(const orc_cache* c, long long row0, long long rows, double*
 /* Stage 1: KV compression ([P2] sec. 2.3 Eq. 11-12 text and Compressor excerpt; [P2] sec. 2.4        */
 /* Eq. 22-23 text; [P1] mechanism 2; [P5] sec. 2 "half-window overlap").                             */
 /* ------------------------------------------------------------------------------------------------ */
+/* Hadamard rotation of indexer rows ([P2] section 2.3, the Indexer excerpt: the indexer's queries, and the keys
+ * its own compressor writes, are rotated by a Hadamard transform before their FP4 quantisation).  The plain
+ * definition of the orthonormal Sylvester-Hadamard matrix of order n (a power of two), evaluated as written,
+ * O(n^2) per row, in double:
+ *   y[i] = sum_j (-1)^popcount(i & j) x[j] / sqrt(n). */
+void orc_hadamard_rows(const double* x, long long rows, int n, double* y) {
+  const double s = sqrt((double)n);
+#pragma omp parallel for schedule(static)
+  for (long long r = 0; r < rows; ++r) {
+    const double* xr = x + r * n;
+    for (int i = 0; i < n; ++i) {
+      double acc = 0.0;
+      for (int j = 0; j < n; ++j) acc += (__builtin_popcount((unsigned)(i & j)) & 1) ? -xr[j] : xr[j];
+      y[r * n + i] = acc / s;
+    }
+  }
+}
+
 /*
  * Entry i (block i of m consecutive tokens), channel j, is a softmax-weighted sum of candidates:
  *   - the tokens of block i from stream a: logit Za[p][j] + Ba[r][j], value Ca[p][j], p = m*i + r;

@@ -70,6 +70,7 @@ def _setup(L):
     L.orc_fp4_decode1.restype = ctypes.c_double
     L.orc_encode_rows.argtypes = [_P, ctypes.c_longlong, ctypes.c_int, ctypes.c_int, ctypes.c_int, _P, _P, _P]
     L.orc_decode_rows.argtypes = [ctypes.POINTER(_Cache), ctypes.c_longlong, ctypes.c_longlong, _P]
+    L.orc_hadamard_rows.argtypes = [_P, ctypes.c_longlong, ctypes.c_int, _P]
     L.orc_kv_compress.argtypes = [_P] * 8 + [ctypes.c_int, ctypes.c_longlong, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                              ctypes.c_longlong, _P]
     L.orc_indexer_scores.argtypes = [ctypes.POINTER(_Cache), _P, ctypes.POINTER(_Cache)] + [ctypes.c_int] * 6 + [
@@ -141,6 +142,21 @@ def encode(x: np.ndarray, fmt: str, rope: int = 0, cap: int | None = None) -> di
     c = empty_cache(fmt, rows, dim, rope, cap)
     lib().orc_encode_rows(_ptr(x), rows, FMT[fmt], dim, rope, _ptr(c["data"]), _ptr(c["rope_data"]), _ptr(c["scale"]))
     return c
+
+
+def hadamard_rotate(x: np.ndarray) -> np.ndarray:
+    """Rows x[..., n] (n a power of two) times the orthonormal Sylvester-Hadamard matrix, in fp64 (oracle.c)."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    n = x.shape[-1]
+    assert n > 0 and n & (n - 1) == 0, "the Hadamard rotation needs a power-of-two row length"
+    y = np.empty_like(x)
+    lib().orc_hadamard_rows(_ptr(x), x.size // n, n, _ptr(y))
+    return y
+
+
+def encode_rotated(x: np.ndarray, fmt: str, cap: int | None = None) -> dict:
+    """A writer with the rotation flag: rotate each row (fp64), round to fp32, encode."""
+    return encode(hadamard_rotate(x).astype(np.float32), fmt, 0, cap)
 
 
 def _cstruct(c: dict) -> _Cache:
