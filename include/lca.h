@@ -56,6 +56,16 @@ typedef enum {
                      /* e = smallest integer with amax(16 elements) <= 6 * 2^e (e = -127 if amax = 0)   */
 } lca_format;
 
+/* Tensor flag LCA_ROTATE_HADAMARD (paper notes, the Indexer excerpt: the indexer's queries, and the keys of its own
+ * compressor, are rotated by a Hadamard transform that spreads outliers before they are quantised to FP4).  The
+ * rows hold rotated values: writers (lca_encode, kv_compress) multiply each fp32 row x by the orthonormal
+ * Sylvester-Hadamard matrix of order dim, y[i] = sum_j (-1)^popcount(i & j) x[j] / sqrt(dim), before encoding.
+ * dim must be a power of two and the format not LCA_MIXED_FP8.  Readers use the stored values as they are: the
+ * rotation is orthogonal, so dot products of rotated queries and rotated keys equal the unrotated ones up to the
+ * encoding.  The writers compute the transform in fp32 (log2(dim) butterfly stages, then one multiply by
+ * 1/sqrt(dim) rounded to fp32). */
+#define LCA_ROTATE_HADAMARD 1
+
 /* One cache (or query) tensor: `cap` rows per sequence, each row one entry of `dim` channels. */
 typedef struct {
   int format;    /* lca_format                                                                       */
@@ -65,6 +75,7 @@ typedef struct {
   void* data;    /* see lca_format                                                                   */
   void* rope;    /* LCA_MIXED_FP8 only, else NULL                                                    */
   void* scale;   /* LCA_MIXED_FP8 / LCA_FP4 only, else NULL                                          */
+  int flags;     /* 0 or LCA_ROTATE_HADAMARD; other bits are INVALID_ARG                             */
 } lca_tensor;
 
 /* Human-readable name of a status code (static string). */
@@ -78,8 +89,9 @@ const char* lca_last_hip_error(void);
  * mixed-precision cache).  src: float [B][rows][dst.dim].  Writes rows [row0, row0 + rows) of every
  * sequence of dst (row0 + rows <= dst.cap).  Formats as described at lca_format; rounding is to nearest,
  * ties to even, for bf16, fp8 and fp4.
- * Errors: INVALID_ARG (null, rows < 0, row0 < 0, row range beyond cap, fp4 dim % 16 != 0, bad rope_dims),
- *         UNSUPPORTED (dim > 1024).
+ * With LCA_ROTATE_HADAMARD in dst.flags each row is rotated first (see the flag).
+ * Errors: INVALID_ARG (null, rows < 0, row0 < 0, row range beyond cap, fp4 dim % 16 != 0, bad rope_dims,
+ *         a rotation with dim not a power of two or the mixed format), UNSUPPORTED (dim > 1024).
  */
 int lca_encode(const float* src, int B, long long rows, long long row0, lca_tensor dst, void* stream);
 
@@ -90,7 +102,7 @@ int lca_encode(const float* src, int B, long long rows, long long row0, lca_tens
  * logits Z + B weights their values C.  Candidates are block i's tokens from stream a (logit Za[p][j] +
  * Ba[r][j], value Ca[p][j]) and, when overlap != 0 (CSA, m = 4), block i-1's tokens from stream b (logit
  * Zb[p][j] + Bb[r][j], value Cb[p][j]); block -1 contributes nothing.  Entries are computed in fp32 and
- * encoded into out's format.
+ * encoded into out's format (rotated first when out.flags has LCA_ROTATE_HADAMARD).
  *   Ca, Za (and Cb, Zb when overlap): float [B][n][c], tokens start_pos .. start_pos + n - 1.
  *   Ba (and Bb when overlap): float [m][c] position biases.
  *   tail_Cb, tail_Zb: float [B][m][c], stream-b values/logits of block start_pos/m - 1; required when

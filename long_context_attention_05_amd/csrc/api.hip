@@ -16,8 +16,15 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Validates one tensor descriptor: format, dim, pointers and their alignment.
+// A writer's rotation: the Sylvester-Hadamard matrix exists for powers of two; the mixed format keeps its RoPE
+// channels apart, so a rotation across them is refused.
+static bool rotation_ok(const lca_tensor& t) {
+  if (!(t.flags & LCA_ROTATE_HADAMARD)) return true;
+  return t.format != LCA_MIXED_FP8 && (t.dim & (t.dim - 1)) == 0;
+}
+
 int check_tensor(const lca_tensor& t, bool allow_fp4, bool allow_mixed) {
-  if (t.dim <= 0 || t.cap <= 0 || !t.data) return LCA_ERR_INVALID_ARG;
+  if (t.dim <= 0 || t.cap <= 0 || !t.data || (t.flags & ~LCA_ROTATE_HADAMARD)) return LCA_ERR_INVALID_ARG;
   switch (t.format) {
     case LCA_F32:
     case LCA_BF16:
@@ -227,6 +234,7 @@ int lca_encode(const float* src, int B, long long rows, long long row0, lca_tens
   if (rc) return rc;
   if (row0 + rows > dst.cap) return LCA_ERR_INVALID_ARG;
   if (dst.dim > 1024) return LCA_ERR_UNSUPPORTED;
+  if (!rotation_ok(dst)) return LCA_ERR_INVALID_ARG;
   if (rows == 0) return LCA_OK;
   return hip_status(launch_encode(src, B, rows, row0, dst, (hipStream_t)stream));
 }
@@ -242,6 +250,7 @@ int kv_compress(const float* Ca, const float* Cb, const float* Za, const float* 
   if (rc) return rc;
   if (out.dim != c) return LCA_ERR_INVALID_ARG;
   if (c > 1024) return LCA_ERR_UNSUPPORTED;
+  if (!rotation_ok(out)) return LCA_ERR_INVALID_ARG;
   const long long nb = (n + m - 1) / m;
   if (start_pos / m + nb > out.cap) return LCA_ERR_INVALID_ARG;
   return hip_status(launch_compress(Ca, overlap ? Cb : nullptr, Za, overlap ? Zb : nullptr, Ba, overlap ? Bb : nullptr,

@@ -19,7 +19,7 @@ namespace lca {
 constexpr int kRowThreads = 256;
 
 struct RowOut {
-  int format, dim, rope;
+  int format, dim, rope, rotate;
   long long cap;
   void* data;
   void* rope_data;
@@ -37,12 +37,70 @@ __device__ __forceinline__ float block_max_256(float v, float* red) {
   return r;
 }
 
-// Encode one row held as v[u] = channel (threadIdx.x + blockDim.x * u), u < CPT, and store it at `row`.
-// All threads of the block must call this (block-wide reduction for the fp8 scale).
+constexpr int kRotMaxDim = 1024;
+
+// Orthonormal Sylvester-Hadamard rotation of a row held as v[u] = channel (threadIdx.x + blockDim.x * u)
+// (paper notes, the Indexer excerpt: indexer queries and keys are rotated before their FP4 quantisation).
+// dim is a power of two <= kRotMaxDim.  Stage h (h = 1, 2, 4, ...) maps the pair (j, j + h), j & h == 0, to
+// (x_j + x_{j+h}, x_j - x_{j+h}), the stages with h >= 64 through an LDS ping-pong buffer; after log2(dim) stages every output is the sum of
+// all inputs with the signs (-1)^popcount(i & j), and one multiply by 1/sqrt(dim) (exact for even powers of two,
+// fl32(sqrt(2)) * 2^-(p+1)/2 for odd p) makes the matrix orthonormal.  All threads of the block take part.
+// Stages with h < 64 pair lanes of one wave (channel j ^ h sits in lane ^ h, same u, since blockDim is a multiple of
+// 64) and run on shuffles with the same operands as the LDS stages.
 template <int CPT>
-__device__ void store_row(const RowOut& o, long long row, const float (&v)[CPT], float* red) {
+__device__ void hadamard_row(float (&v)[CPT], int dim, float* buf) {
+  const int nt = blockDim.x;
+  const int hw = dim < 64 ? dim : 64;
+  for (int h = 1; h < hw; h <<= 1) {
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int j = threadIdx.x + nt * u;
+      const float o = __shfl_xor(v[u], h, 64);
+      v[u] = (j & h) ? o - v[u] : v[u] + o;
+    }
+  }
+  float* x = buf;
+  float* y = buf + kRotMaxDim;
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) {
+    const int j = threadIdx.x + nt * u;
+    if (j < dim) x[j] = v[u];
+  }
+  __syncthreads();
+  for (int h = hw; h < dim; h <<= 1) {
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int j = threadIdx.x + nt * u;
+      if (j < dim) {
+        const float a = x[j & ~h], b = x[j | h];
+        y[j] = (j & h) ? a - b : a + b;
+      }
+    }
+    __syncthreads();
+    float* t = x;
+    x = y;
+    y = t;
+  }
+  const int p = 31 - __clz(dim);
+  const float s = (p & 1) ? ldexpf(1.41421354f, -(p + 1) / 2) : ldexpf(1.0f, -p / 2);
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) {
+    const int j = threadIdx.x + nt * u;
+    v[u] = j < dim ? x[j] * s : 0.0f;
+  }
+  __syncthreads();  // the buffer may be reused by the caller's next row
+}
+
+// Encode one row held as v[u] = channel (threadIdx.x + blockDim.x * u), u < CPT, and store it at `row`.
+// All threads of the block must call this (block-wide reduction for the fp8 scale; the rotation's exchange).
+template <int CPT>
+__device__ void store_row(const RowOut& o, long long row, const float (&vin)[CPT], float* red, float* rot) {
   const int c = o.dim;
   const int nt = blockDim.x;
+  float v[CPT];
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) v[u] = vin[u];
+  if (o.rotate) hadamard_row<CPT>(v, c, rot);
   if (o.format == LCA_F32) {
     float* d = (float*)o.data + row * c;
 #pragma unroll
@@ -105,6 +163,7 @@ template <int CPT>
 __global__ __launch_bounds__(kRowThreads) void encode_rows_kernel(const float* __restrict__ src, long long rows,
                                                                    long long row0, RowOut o) {
   __shared__ float red[kRowThreads / 64];
+  __shared__ float rot[2 * kRotMaxDim];
   const long long r = blockIdx.x;
   const int b = blockIdx.y;
   const float* s = src + ((long long)b * rows + r) * o.dim;
@@ -114,7 +173,7 @@ __global__ __launch_bounds__(kRowThreads) void encode_rows_kernel(const float* _
     int j = threadIdx.x + blockDim.x * u;
     v[u] = (j < o.dim) ? s[j] : 0.0f;
   }
-  store_row<CPT>(o, (long long)b * o.cap + row0 + r, v, red);
+  store_row<CPT>(o, (long long)b * o.cap + row0 + r, v, red, rot);
 }
 
 struct CompressArgs {
@@ -135,6 +194,7 @@ __device__ __forceinline__ void softmax_acc(float l, float x, float& mx, float& 
 template <int CPT>
 __global__ __launch_bounds__(kRowThreads) void compress_kernel(CompressArgs a, RowOut o) {
   __shared__ float red[kRowThreads / 64];
+  __shared__ float rot[2 * kRotMaxDim];
   const long long i = blockIdx.x;  // local entry index
   const int b = blockIdx.y;
   const int c = a.c, m = a.m;
@@ -195,11 +255,12 @@ __global__ __launch_bounds__(kRowThreads) void compress_kernel(CompressArgs a, R
   float v[CPT];
 #pragma unroll
   for (int u = 0; u < CPT; ++u) v[u] = num[u] / den[u];
-  store_row<CPT>(o, (long long)b * o.cap + gblock, v, red);
+  store_row<CPT>(o, (long long)b * o.cap + gblock, v, red, rot);
 }
 
 static RowOut row_out(const lca_tensor& t) {
-  return RowOut{t.format, t.dim, t.rope_dims, t.cap, t.data, t.rope, t.scale};
+  return RowOut{t.format, t.dim, t.rope_dims, (t.flags & LCA_ROTATE_HADAMARD) ? 1 : 0, t.cap, t.data, t.rope,
+                t.scale};
 }
 
 static int threads_for(int c) {

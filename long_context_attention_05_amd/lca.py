@@ -12,6 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liblca.so")
 
 LCA_F32, LCA_BF16, LCA_MIXED_FP8, LCA_FP4 = 0, 1, 2, 3
+LCA_ROTATE_HADAMARD = 1  # lca_tensor.flags: rows are stored Hadamard-rotated (writers rotate before encoding)
 FORMATS = {"f32": LCA_F32, "bf16": LCA_BF16, "mixed": LCA_MIXED_FP8, "fp4": LCA_FP4}
 STATUS = {0: "LCA_OK", -1: "LCA_ERR_INVALID_ARG", -2: "LCA_ERR_UNSUPPORTED", -3: "LCA_ERR_WORKSPACE",
           -4: "LCA_ERR_ALIGNMENT", -5: "LCA_ERR_HIP"}
@@ -29,7 +30,7 @@ class LcaError(RuntimeError):
 class lca_tensor(ctypes.Structure):
     _fields_ = [("format", ctypes.c_int), ("dim", ctypes.c_int), ("rope_dims", ctypes.c_int),
                 ("cap", ctypes.c_longlong), ("data", ctypes.c_void_p), ("rope", ctypes.c_void_p),
-                ("scale", ctypes.c_void_p)]
+                ("scale", ctypes.c_void_p), ("flags", ctypes.c_int)]
 
 
 if not os.path.exists(LIB_PATH):
@@ -96,9 +97,9 @@ def _check(fn: str, rc: int):
 class CacheTensor:
     """Device storage of one lca_tensor (owns its torch tensors): `cap` rows per sequence for B sequences."""
 
-    def __init__(self, fmt: str, B: int, cap: int, dim: int, rope: int = 0, device="cuda"):
+    def __init__(self, fmt: str, B: int, cap: int, dim: int, rope: int = 0, device="cuda", flags: int = 0):
         import torch
-        self.fmt, self.B, self.cap, self.dim, self.rope = fmt, B, cap, dim, rope
+        self.fmt, self.B, self.cap, self.dim, self.rope, self.flags = fmt, B, cap, dim, rope, flags
         rows = B * cap
         self.rope_t = self.scale_t = None
         if fmt == "f32":
@@ -117,7 +118,7 @@ class CacheTensor:
 
     def desc(self) -> lca_tensor:
         return lca_tensor(FORMATS[self.fmt], self.dim, self.rope, self.cap, _ptr(self.data), _ptr(self.rope_t),
-                          _ptr(self.scale_t))
+                          _ptr(self.scale_t), self.flags)
 
     def host(self) -> dict:
         """Copy to host numpy arrays (for comparisons), as a dict of raw storage arrays."""
