@@ -104,3 +104,24 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     mod = importlib.util.module_from_spec(spec)
     with pytest.raises(ImportError):
         spec.loader.exec_module(mod)
+
+
+def test_descriptor_layout_matches_header(tmp_path):
+    """The binding's lca_tensor has the header's size and field offsets (compiled against include/lca.h)."""
+    import subprocess
+    from long_context_attention_05_amd import lca
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "lca.h"\nint main(void) {\n'
+                   '  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(lca_tensor), offsetof(lca_tensor, format),\n'
+                   '         offsetof(lca_tensor, dim), offsetof(lca_tensor, rope_dims), offsetof(lca_tensor, cap),\n'
+                   '         offsetof(lca_tensor, data), offsetof(lca_tensor, rope), offsetof(lca_tensor, scale),\n'
+                   '         offsetof(lca_tensor, flags));\n  return 0;\n}\n')
+    exe = tmp_path / "layout"
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    subprocess.check_call(["gcc", "-std=c11", "-I", inc, "-x", "c", str(src), "-o", str(exe)])
+    got = [int(v) for v in subprocess.check_output([str(exe)]).split()]
+    T = lca.lca_tensor
+    want = [ctypes.sizeof(T)] + [getattr(T, f).offset for f in
+                                 ("format", "dim", "rope_dims", "cap", "data", "rope", "scale", "flags")]
+    assert got == want
+    assert lca.LCA_ROTATE_HADAMARD == 1
