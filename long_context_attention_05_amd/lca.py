@@ -35,6 +35,11 @@ class lca_tensor(ctypes.Structure):
 
 if not os.path.exists(LIB_PATH):
     raise ImportError("liblca.so is not built (run long_context_attention_05_amd/build.py); no fallback exists")
+# torch first: liblca.so then binds to the HIP runtime torch has already loaded, so the library's launches run in
+# the runtime that owns torch's device memory and streams (loading the library first brings in a second runtime,
+# whose calls then find no device)
+import torch  # noqa: E402,F401
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 _P = ctypes.c_void_p
