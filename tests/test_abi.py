@@ -132,3 +132,15 @@ def test_descriptor_layout_matches_header(tmp_path):
                                  ("format", "dim", "rope_dims", "cap", "data", "rope", "scale", "flags")]
     assert got == want
     assert lca.LCA_ROTATE_HADAMARD == 1
+
+
+def test_binding_loads_torch_before_the_library():
+    """Importing the package first must not bring in a second HIP runtime: torch is loaded before liblca.so."""
+    import subprocess
+    import sys
+    code = ("import sys\n"
+            "import long_context_attention_05_amd as p\n"
+            "mods = list(sys.modules)\n"
+            "assert 'torch' in sys.modules\n"
+            "assert mods.index('torch') < mods.index('long_context_attention_05_amd.lca')\n")
+    subprocess.check_call([sys.executable, "-c", code], cwd=ROOT)
