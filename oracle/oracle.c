@@ -350,18 +350,46 @@ void orc_kv_compress(const float* Ca, const float* Cb, const float* Za, const fl
  * in ([P1] mechanism 1, [P5] sec. 4).  Entries that are not visible get s = -inf.
  *
  * s64 receives the double score.  If s32 is non-NULL it receives the canonical fp32 score, defined
- * whenever every d[h] is exactly representable in fp32 (true for fp4 x fp4 inputs with bounded scale
- * spread): p[h] = fl32(w[h] * max(0, fl32(d[h]))), then a halving tree over the heads padded with
- * zeros to a power of two P: level by level a[j] <- a[j] + a[j + L/2] for j < L/2, in fp32; a -0
- * result is written as +0.  *inexact counts rows/entries where some d[h] was not exact in fp32.
+ * whenever every d[h] is computed exactly by fp32 arithmetic in any summation order (see
+ * orc_dot_is_fp32_exact): p[h] = fl32(w[h] * max(0, fl32(d[h]))), then a halving tree over the heads padded
+ * with zeros to a power of two P: level by level a[j] <- a[j] + a[j + L/2] for j < L/2, in fp32; a -0
+ * result is written as +0.  *inexact counts the (row, entry) pairs with at least one head whose dot is
+ * not certified exact; exact_out (optional, [B][nrows][N]) holds 1 for a certified pair, else 0.
  * abs_out (optional) receives sum_h |w[t,h]| * sum_d |q[t,h,d] * K[i,d]|, the scale of the fp32
  * rounding error of any summation order (used to certify near-ties).
  * Rows evaluated: rows[0..nrows) (offsets into [0, Sq)); outputs are [B][nrows][N].
- * pinned by: dyadic tiny inputs reproduce hand-derivable scores; brute force over tiny inputs.
+ * pinned by: dyadic tiny inputs reproduce hand-derivable scores; brute force over tiny inputs; the
+ * certificate accepts small-spread fp4 rows and rejects a constructed wide-spread row whose fp32 sum
+ * rounds.
  */
+/* Certificate that fp32 arithmetic reproduces the dot sum_d q[d] * k[d] exactly in every summation order
+ * (and in any grouping, such as a matrix unit's blocks with their own scale factors).  The products are
+ * exact in double (fp32 inputs carry at most 24 significant bits).  Let 2^L be the largest power of two
+ * dividing every nonzero product and A = sum_d |q[d] k[d]|.  Every partial sum of any subset of products is
+ * an integer multiple of 2^L no larger than A in magnitude, so if A < 2^(L + 24) each one has at most 24
+ * significant bits and is an fp32 value; L >= -126 keeps them out of the subnormal range.  For fp4 x fp4
+ * rows (per-16 scales) this is the bound on the spread of the groups' scale exponents: a group's products
+ * are multiples of 2^(eq + ek - 2) summing to less than 2^(eq + ek + 10). */
+int orc_dot_is_fp32_exact(const double* q, const double* k, int n) {
+  int L = INT32_MAX;
+  double A = 0.0;
+  for (int d = 0; d < n; ++d) {
+    double p = q[d] * k[d];
+    if (p == 0.0) continue;
+    int e;
+    double f = frexp(fabs(p), &e);            /* |p| = f * 2^e, f in [0.5, 1) */
+    uint64_t mant = (uint64_t)ldexp(f, 53);   /* exact: f has at most 53 significant bits */
+    int low = e - 53 + __builtin_ctzll(mant); /* exponent of the lowest set bit of p */
+    if (low < L) L = low;
+    A += fabs(p);
+  }
+  if (L == INT32_MAX) return 1; /* every product is zero */
+  return L >= -126 && A < ldexp(1.0, L + 24);
+}
+
 void orc_indexer_scores(const orc_cache* q, const float* w, const orc_cache* K, int B, int Sq, int HI, int DI, int N,
                         int m, long long q_start_pos, const int* rows, int nrows, double* s64, float* s32,
-                        double* abs_out, long long* inexact) {
+                        double* abs_out, long long* inexact, unsigned char* exact_out) {
   int P = 1;
   while (P < HI) P <<= 1;
   long long bad = 0;
@@ -383,10 +411,12 @@ void orc_indexer_scores(const orc_cache* q, const float* w, const orc_cache* K, 
           s64[ob + i] = -INFINITY;
           if (s32) s32[ob + i] = -INFINITY;
           if (abs_out) abs_out[ob + i] = 0.0;
+          if (exact_out) exact_out[ob + i] = 1;
           continue;
         }
         decode_row(K, (long long)b * K->cap + i, kd);
         double acc = 0.0, aacc = 0.0;
+        int certified = 1;
         for (int h = 0; h < P; ++h) a[h] = 0.0f;
         for (int h = 0; h < HI; ++h) {
           double d = 0.0, ad = 0.0;
@@ -396,14 +426,18 @@ void orc_indexer_scores(const orc_cache* q, const float* w, const orc_cache* K, 
           }
           acc += (double)wr[h] * (d > 0.0 ? d : 0.0);
           aacc += fabs((double)wr[h]) * ad;
+          if (s32 || exact_out || inexact) {
+            if (!orc_dot_is_fp32_exact(qd + (size_t)h * DI, kd, DI)) certified = 0;
+          }
           if (s32) {
             float d32 = (float)d;
-            if ((double)d32 != d) ++bad;
             float rl = d32 > 0.0f ? d32 : 0.0f;
             volatile float p = wr[h] * rl; /* fp32 multiply, rounded once */
             a[h] = p;
           }
         }
+        if (!certified) ++bad;
+        if (exact_out) exact_out[ob + i] = (unsigned char)certified;
         s64[ob + i] = acc;
         if (abs_out) abs_out[ob + i] = aacc;
         if (s32) {

@@ -74,7 +74,9 @@ def _setup(L):
     L.orc_kv_compress.argtypes = [_P] * 8 + [ctypes.c_int, ctypes.c_longlong, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                              ctypes.c_longlong, _P]
     L.orc_indexer_scores.argtypes = [ctypes.POINTER(_Cache), _P, ctypes.POINTER(_Cache)] + [ctypes.c_int] * 6 + [
-        ctypes.c_longlong, _P, ctypes.c_int, _P, _P, _P, _P]
+        ctypes.c_longlong, _P, ctypes.c_int, _P, _P, _P, _P, _P]
+    L.orc_dot_is_fp32_exact.argtypes = [_P, _P, ctypes.c_int]
+    L.orc_dot_is_fp32_exact.restype = ctypes.c_int
     L.orc_topk_rows.argtypes = [_P, ctypes.c_longlong, ctypes.c_int, _P, ctypes.c_int, _P, _P, _P]
     L.orc_attn.argtypes = [ctypes.POINTER(_Cache), ctypes.POINTER(_Cache), ctypes.c_int, ctypes.POINTER(_Cache),
                            ctypes.c_longlong, ctypes.c_int, _P, ctypes.c_int, ctypes.c_int, _P] + [ctypes.c_int] * 5 + [
@@ -218,19 +220,33 @@ def compress_to_cache(entries64: np.ndarray, fmt: str, rope: int = 0) -> dict:
 # stage 2: indexer scores + top-k
 # ----------------------------------------------------------------------------------------------------
 def indexer_scores(qI: dict, w: np.ndarray, kI: dict, B: int, Sq: int, HI: int, DI: int, N: int, m: int,
-                   q_start_pos: int, rows=None, canonical: bool = False, want_abs: bool = False):
-    """Returns (s64 [B, nrows, N], s32 or None, abs or None, inexact_count)."""
+                   q_start_pos: int, rows=None, canonical: bool = False, want_abs: bool = False,
+                   want_exact: bool = False):
+    """Returns (s64 [B, nrows, N], s32 or None, abs or None, inexact_count), plus the per-pair exactness
+    certificate [B, nrows, N] (uint8, 1 = every head dot is exact in fp32) as a fifth item when want_exact.
+    inexact_count is the number of visible (row, entry) pairs without the certificate."""
     rows = np.arange(Sq, dtype=np.int32) if rows is None else np.ascontiguousarray(rows, np.int32)
     nr = len(rows)
     w = np.ascontiguousarray(w, np.float32)
     s64 = np.empty((B, nr, N), np.float64)
     s32 = np.empty((B, nr, N), np.float32) if canonical else None
     ab = np.empty((B, nr, N), np.float64) if want_abs else None
+    ex = np.empty((B, nr, N), np.uint8) if want_exact else None
     bad = ctypes.c_longlong(0)
     q_s, k_s = _cstruct(qI), _cstruct(kI)
     lib().orc_indexer_scores(ctypes.byref(q_s), _ptr(w), ctypes.byref(k_s), B, Sq, HI, DI, N, m, q_start_pos,
-                             _ptr(rows), nr, _ptr(s64), _ptr(s32), _ptr(ab), ctypes.byref(bad))
+                             _ptr(rows), nr, _ptr(s64), _ptr(s32), _ptr(ab), ctypes.byref(bad), _ptr(ex))
+    if want_exact:
+        return s64, s32, ab, int(bad.value), ex
     return s64, s32, ab, int(bad.value)
+
+
+def dot_is_fp32_exact(q: np.ndarray, k: np.ndarray) -> bool:
+    """The oracle's certificate that fp32 arithmetic gives sum(q * k) exactly in every summation order."""
+    q = np.ascontiguousarray(q, np.float64)
+    k = np.ascontiguousarray(k, np.float64)
+    assert q.shape == k.shape and q.ndim == 1
+    return bool(lib().orc_dot_is_fp32_exact(_ptr(q), _ptr(k), len(q)))
 
 
 def topk(scores: np.ndarray, nvis: np.ndarray, k: int):
