@@ -133,8 +133,8 @@ int kv_compress(const float* Ca, const float* Cb, const float* Za, const float* 
  * (a[j] += a[j + L/2], L = next power of two of HI, zero padded), so inputs whose per-head dots are exact in
  * fp32 (e.g. fp4 x fp4 with a bounded scale spread) give bit-reproducible selections.
  * ws: device scratch of at least indexer_score_topk_workspace_size(B, Sq, N, k) bytes (contents ignored).
- * Errors: INVALID_ARG (null, sizes <= 0, dims mismatch, DI % 16 for FP4), UNSUPPORTED (HI > 64,
- *         DI > 256, q/k formats not both float-like or both FP4), WORKSPACE, ALIGNMENT.
+ * Errors: INVALID_ARG (null, sizes <= 0, dims mismatch, qI.cap != Sq * HI, DI % 16 for FP4),
+ *         UNSUPPORTED (HI > 64, DI > 128, q/k formats not both float-like or both FP4), WORKSPACE, ALIGNMENT.
  */
 size_t indexer_score_topk_workspace_size(int B, int Sq, int N, int k);
 
@@ -174,8 +174,8 @@ int indexer_score_topk(lca_tensor qI, const float* w, lca_tensor kI, int B, int 
  *   out: [B][Sq][H][D] in out_format (LCA_F32 or LCA_BF16).  lse_out (nullable): float [B][Sq][H], the log
  *   of the softmax denominator M + log(den).
  * ws: device scratch of at least sparse_mqa_attn_workspace_size(B, Sq, H, D, window + k) bytes.
- * Errors: INVALID_ARG, UNSUPPORTED (shape without a kernel: H > 64 or D > 512 on the float path),
- *         WORKSPACE, ALIGNMENT.
+ * Errors: INVALID_ARG, UNSUPPORTED (shape without a kernel: on the float path -- q or the caches not bf16 over
+ *         bf16/mixed, or H != 64, or D != 512 -- H > 64, D > 512 or H * D > 8192), WORKSPACE, ALIGNMENT.
  */
 size_t sparse_mqa_attn_workspace_size(int B, int Sq, int H, int D, int max_entries);
 int sparse_mqa_attn(const void* q, int q_format, lca_tensor kv_comp, int N, lca_tensor kv_raw, long long raw_start_pos,

@@ -3,8 +3,33 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+#include <vector>
+
 #include "lca_internal.h"
 
+
+namespace lca {
+
+hipError_t ensure_dyn_lds(const void* kernel, int bytes) {
+  struct Done {
+    const void* kernel;
+    int device, bytes;
+  };
+  static std::mutex mu;
+  static std::vector<Done> done;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const Done& d : done)
+    if (d.kernel == kernel && d.device == dev && d.bytes >= bytes) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) done.push_back(Done{kernel, dev, bytes});
+  return e;
+}
+
+}  // namespace lca
 
 using namespace lca;
 
@@ -311,7 +336,8 @@ int indexer_score_topk(lca_tensor qI, const float* w, lca_tensor kI, int B, int 
   if (rc) return rc;
   rc = check_tensor(kI, true, false);
   if (rc) return rc;
-  if (qI.dim != DI || kI.dim != DI || qI.cap < (long long)Sq * HI || kI.cap < N) return LCA_ERR_INVALID_ARG;
+  // the kernels address query row r of sequence b at rows (b * Sq + r) * HI + h: the tensor must be exactly that
+  if (qI.dim != DI || kI.dim != DI || qI.cap != (long long)Sq * HI || kI.cap < N) return LCA_ERR_INVALID_ARG;
   if ((qI.format == LCA_FP4) != (kI.format == LCA_FP4)) return LCA_ERR_UNSUPPORTED;
   if (HI > 64 || DI > 128) return LCA_ERR_UNSUPPORTED;
   if (((uintptr_t)w & 3u) || ((uintptr_t)idx_out & 3u) || (score_out && ((uintptr_t)score_out & 3u)))

@@ -2030,10 +2030,6 @@ void launch_dec_value(int nti, dim3 grid, hipStream_t st, const AttnArgs& a) {
   }
 }
 
-static bool g_attn_attr[64];
-static bool g_hg_attr[64];
-static bool g_wd_attr[64];
-
 bool attn_uses_mfma(int H, int D, int q_format, int kv_format) {
   return H == 64 && D == 512 && q_format == LCA_BF16 && (kv_format == LCA_BF16 || kv_format == LCA_MIXED_FP8);
 }
@@ -2058,30 +2054,16 @@ hipError_t launch_attn(AttnArgs a, hipStream_t st, hipEvent_t ev_begin, hipEvent
       launch_dec_value<LCA_MIXED_FP8>(nti, vgrid, st, a);
     }
   } else if (mfma && a.hg_mode == 2) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
     // mode 2 is chosen for the mixed cache only (dense HCA rows over a bf16 cache take the many-row kernel)
     if (a.comp.format != LCA_MIXED_FP8) return hipErrorInvalidValue;
-    if (dev >= 0 && dev < 64 && !g_wd_attr[dev]) {
-      const hipError_t e = hipFuncSetAttribute((const void*)attn_wide_kernel<LCA_MIXED_FP8>,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)kWdLds);
-      if (e != hipSuccess) return e;
-      g_wd_attr[dev] = true;
-    }
+    const hipError_t e = ensure_dyn_lds((const void*)attn_wide_kernel<LCA_MIXED_FP8>, (int)kWdLds);
+    if (e != hipSuccess) return e;
     const dim3 wgrid((unsigned)(a.B * a.Sq * a.n_splits));
     hipLaunchKernelGGL(attn_wide_kernel<LCA_MIXED_FP8>, wgrid, dim3(kWdThreads), kWdLds, st, a);
   } else if (mfma && a.hg_mode == 1) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-    if (dev >= 0 && dev < 64 && !g_hg_attr[dev]) {
-      hipError_t e = hipFuncSetAttribute((const void*)attn_hgw_kernel<LCA_BF16>,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)kHgwLds);
-      if (e == hipSuccess)
-        e = hipFuncSetAttribute((const void*)attn_hgw_kernel<LCA_MIXED_FP8>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kHgwLds);
-      if (e != hipSuccess) return e;
-      g_hg_attr[dev] = true;
-    }
+    hipError_t e = ensure_dyn_lds((const void*)attn_hgw_kernel<LCA_BF16>, (int)kHgwLds);
+    if (e == hipSuccess) e = ensure_dyn_lds((const void*)attn_hgw_kernel<LCA_MIXED_FP8>, (int)kHgwLds);
+    if (e != hipSuccess) return e;
     const int pairs = a.B * a.Sq * a.n_splits;
     const dim3 hgrid((unsigned)(((pairs + 7) / 8) * 32));
     if (a.comp.format == LCA_BF16)
@@ -2089,17 +2071,9 @@ hipError_t launch_attn(AttnArgs a, hipStream_t st, hipEvent_t ev_begin, hipEvent
     else
       hipLaunchKernelGGL(attn_hgw_kernel<LCA_MIXED_FP8>, hgrid, dim3(256), kHgwLds, st, a, pairs);
   } else if (mfma) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-    if (dev >= 0 && dev < 64 && !g_attn_attr[dev]) {
-      hipError_t e = hipFuncSetAttribute((const void*)attn_mfma_kernel<LCA_BF16>,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMfmaLds);
-      if (e == hipSuccess)
-        e = hipFuncSetAttribute((const void*)attn_mfma_kernel<LCA_MIXED_FP8>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMfmaLds);
-      if (e != hipSuccess) return e;
-      g_attn_attr[dev] = true;
-    }
+    hipError_t e = ensure_dyn_lds((const void*)attn_mfma_kernel<LCA_BF16>, (int)kMfmaLds);
+    if (e == hipSuccess) e = ensure_dyn_lds((const void*)attn_mfma_kernel<LCA_MIXED_FP8>, (int)kMfmaLds);
+    if (e != hipSuccess) return e;
     if (a.comp.format == LCA_BF16 && a.raw.cap * 1024 < (1ll << 31) && a.comp.cap * 1024 < (1ll << 31)) {
       a.part_bf16 = 1;  // split partials in bf16, for this kernel and the merge after it
       hipLaunchKernelGGL(attn_pfs_kernel, grid, dim3(kPsThreads), 0, st, a);

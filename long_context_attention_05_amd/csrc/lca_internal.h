@@ -15,6 +15,10 @@ inline void clear_stale_error() {
   (void)e;
 }
 
+// Raises a kernel's dynamic LDS limit to `bytes` on the current device, once per (kernel, device); safe to call from
+// several host threads at once (api.hip).
+hipError_t ensure_dyn_lds(const void* kernel, int bytes);
+
 // stage 1 + codec (compress.hip)
 hipError_t launch_encode(const float* src, int B, long long rows, long long row0, const lca_tensor& dst,
                          hipStream_t st);

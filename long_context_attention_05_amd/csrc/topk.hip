@@ -485,8 +485,6 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(SelArgs a) {
   }
 }
 
-static bool g_lds_attr_set = false;
-
 hipError_t launch_topk(const SelArgs& a, hipStream_t st) {
   if (a.rows <= 0) return hipSuccess;
   // the longest visible row decides the variant (rows of one call differ only by their causal limit)
@@ -501,12 +499,8 @@ hipError_t launch_topk(const SelArgs& a, hipStream_t st) {
                          (size_t)kSliceKeys * 4, st, a);
     hipLaunchKernelGGL(topk_finish_kernel, dim3((unsigned)a.rows), dim3(kFinThreads), kFinishLds, st, a);
   } else if (nvis_max <= kLdsKeys) {
-    if (!g_lds_attr_set) {
-      hipError_t e = hipFuncSetAttribute((const void*)topk_select_kernel<true>,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSelDynLds);
-      if (e != hipSuccess) return e;
-      g_lds_attr_set = true;
-    }
+    const hipError_t e = ensure_dyn_lds((const void*)topk_select_kernel<true>, (int)kSelDynLds);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(topk_select_kernel<true>, dim3((unsigned)a.rows), dim3(kSelThreads), kSelDynLds, st, a);
   } else {
     hipLaunchKernelGGL(topk_select_kernel<false>, dim3((unsigned)a.rows), dim3(kSelThreads), 0, st, a);

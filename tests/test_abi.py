@@ -85,6 +85,14 @@ def test_host_validation_errors():
     assert L.indexer_score_topk(q, P, _t(fmt=3, dim=128, cap=1000, scale=P), 1, 1, 64, 128, 1000, 4, 64, 4000, P, None,
                                 P, 1 << 30, None) == UNS
     assert L.indexer_score_topk(q, None, k, 1, 1, 64, 128, 1000, 4, 64, 4000, P, None, P, 1 << 30, None) == INV
+    # the query tensor must hold exactly Sq * HI rows per sequence (the kernels address rows (b * Sq + r) * HI + h)
+    assert L.indexer_score_topk(_t(dim=128, cap=65), P, k, 2, 1, 64, 128, 1000, 4, 64, 4000, P, None, P, 1 << 30,
+                                None) == INV
+    assert L.indexer_score_topk(_t(dim=128, cap=128), P, k, 2, 2, 64, 128, 1000, 4, 64, 4000, P, None, P, 16,
+                                None) == WS  # cap = Sq * HI passes (the next check, the workspace, fails)
+    # DI beyond 128 has no kernel (fp4 rows of 144 dims are otherwise valid)
+    assert L.indexer_score_topk(_t(fmt=3, dim=144, cap=64, scale=P), P, _t(fmt=3, dim=144, cap=1000, scale=P), 1, 1,
+                                64, 144, 1000, 4, 64, 4000, P, None, P, 1 << 30, None) == UNS
     assert L.indexer_score_topk(q, P, _t(dim=128, cap=1000, flags=8), 1, 1, 64, 128, 1000, 4, 64, 4000, P, None, P,
                                 1 << 30, None) == INV
     # attention: window outside the raw span, workspace missing for a split plan, bad formats
@@ -99,6 +107,11 @@ def test_host_validation_errors():
                              1 << 30, None) == INV
     assert L.hca_attn(P, 1, comp, 5000, 0, raw, 373, 128, P, 2, 1, 64, 512, 128, f, 500, P, 1, None, P, 1 << 30,
                       None) == INV
+    # the float path (fp32 queries or caches) covers H * D <= 8192 only: 64 heads x 512 channels in fp32 has no kernel
+    assert L.sparse_mqa_attn(P, 0, comp, 5000, raw, 373, 128, P, 512, P, 2, 1, 64, 512, 128, f, 500, P, 1, None, P,
+                             1 << 30, None) == UNS
+    assert L.sparse_mqa_attn(P, 0, _t(fmt=0, dim=144, cap=5000), 5000, _t(fmt=0, dim=144, cap=128), 373, 128, P, 512,
+                             P, 2, 1, 64, 144, 128, f, 500, P, 1, None, P, 1 << 30, None) == UNS
 
 
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):

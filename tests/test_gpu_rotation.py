@@ -11,7 +11,7 @@ import torch
 
 from long_context_attention_05_amd import lca
 from oracle import oracle as orc
-from gpu_util import up
+from tests.gpu_util import up
 
 pytestmark = pytest.mark.gpu
 ROT = lca.LCA_ROTATE_HADAMARD

@@ -88,12 +88,6 @@ def test_compress_f32_matches_oracle(B, n, c, m, overlap, start):
     assert row_rel_err(got, ref) <= 1e-4
 
 
-def _code_steps(got_codes, ref_codes, decode):
-    """Quantised outputs of slightly different fp32 entries: most codes equal, the rest one grid step apart."""
-    same = np.mean(got_codes == ref_codes)
-    return same
-
-
 @pytest.mark.parametrize("fmt,c,rope", [("bf16", 512, 0), ("mixed", 512, 64), ("fp4", 128, 0)])
 def test_compress_quantised_outputs(fmt, c, rope):
     B, n, m = 2, 4100, 4
