@@ -158,6 +158,22 @@ int indexer_score_topk(lca_tensor qI, const float* w, lca_tensor kI, int B, int 
                        void* stream);
 
 /*
+ * indexer_score_topk_noalloc -- for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): indexer_score_topk with the same arguments, kernels and
+ * results, minus ws / ws_bytes.  Its scratch is a fixed device array inside the library of
+ * LCA_NOALLOC_SCRATCH_BYTES per device, held by each device that runs it until the process ends; the call itself
+ * allocates nothing.  Every call on one device shares that device's array and leaves its contents behind (what
+ * must start at zero is cleared inside each call): calls that overlap in time on one device (several streams or
+ * host threads) race and give undefined results.
+ * Errors: those of indexer_score_topk, and WORKSPACE when indexer_score_topk_workspace_size(B, Sq, N, k) exceeds
+ *         LCA_NOALLOC_SCRATCH_BYTES (e.g. the decode workloads fit: 4 x 262144 or 16 x 32768 entries, one or two
+ *         query rows; long prefill chunks do not).
+ */
+#define LCA_NOALLOC_SCRATCH_BYTES (32u << 20)
+int indexer_score_topk_noalloc(lca_tensor qI, const float* w, lca_tensor kI, int B, int Sq, int HI, int DI, int N, int m,
+                               int k, long long q_start_pos, int32_t* idx_out, float* score_out, void* stream);
+
+/*
  * sparse_mqa_attn -- stage 3, shared-KV multi-query attention over the sliding window, the selected
  * compressed entries and a per-head sink (paper notes section 2.3 item 3 and the Attention.forward excerpt;
  * itsolotime mechanisms 1 and 3; 67808.cn section 4).

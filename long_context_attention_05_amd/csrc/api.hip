@@ -4,32 +4,40 @@
 #include <stdint.h>
 
 #include <mutex>
-#include <vector>
 
 #include "lca_internal.h"
 
 
 namespace lca {
 
+// (kernel, device) pairs whose LDS limit is raised: a fixed table, so that no call allocates host memory either.
+// A pair that does not fit is set again on every launch (the attribute call is idempotent).
 hipError_t ensure_dyn_lds(const void* kernel, int bytes) {
   struct Done {
     const void* kernel;
     int device, bytes;
   };
+  constexpr int kMaxDone = 1024;
   static std::mutex mu;
-  static std::vector<Done> done;
+  static Done done[kMaxDone];
+  static int n_done = 0;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   std::lock_guard<std::mutex> lock(mu);
-  for (const Done& d : done)
-    if (d.kernel == kernel && d.device == dev && d.bytes >= bytes) return hipSuccess;
+  for (int i = 0; i < n_done; ++i)
+    if (done[i].kernel == kernel && done[i].device == dev && done[i].bytes >= bytes) return hipSuccess;
   e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-  if (e == hipSuccess) done.push_back(Done{kernel, dev, bytes});
+  if (e == hipSuccess && n_done < kMaxDone) done[n_done++] = Done{kernel, dev, bytes};
   return e;
 }
 
 }  // namespace lca
+
+// Scratch memory of indexer_score_topk_noalloc: one array per device (each device that runs the library holds its
+// own copy until the process ends).  Host code never passes this name to a kernel: on the host it stands for no
+// device address.  The device address comes from hipGetSymbolAddress, once per device (scratch_ptr below).
+static __device__ __align__(256) unsigned char scratch[LCA_NOALLOC_SCRATCH_BYTES];
 
 using namespace lca;
 
@@ -327,6 +335,31 @@ size_t indexer_score_topk_workspace_size(int B, int Sq, int N, int k) {
   return idx_ws_layout(B, Sq, N).total;
 }
 
+namespace {
+
+// Device address of this device's `scratch` array, looked up with the device current on its first use and kept.
+hipError_t scratch_ptr(void** out) {
+  constexpr int kMaxDevices = 256;
+  static std::mutex mu;
+  static void* ptrs[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
 int indexer_score_topk(lca_tensor qI, const float* w, lca_tensor kI, int B, int Sq, int HI, int DI, int N, int m, int k,
                        long long q_start_pos, int32_t* idx_out, float* score_out, void* ws, size_t ws_bytes,
                        void* stream) {
@@ -364,6 +397,19 @@ int indexer_score_topk(lca_tensor qI, const float* w, lca_tensor kI, int B, int 
   SelArgs s{(const uint32_t*)(wsb + L.keys), idx_out, score_out, B * Sq, Sq, N, m, k, q_start_pos, state,
             multi ? (int*)(wsb + L.counts) : nullptr, multi ? (uint2*)(wsb + L.cand) : nullptr};
   return hip_status(launch_topk(s, st));
+}
+
+int indexer_score_topk_noalloc(lca_tensor qI, const float* w, lca_tensor kI, int B, int Sq, int HI, int DI, int N, int m,
+                               int k, long long q_start_pos, int32_t* idx_out, float* score_out, void* stream) {
+  if (B > 0 && Sq > 0 && N > 0 && indexer_score_topk_workspace_size(B, Sq, N, k) > (size_t)LCA_NOALLOC_SCRATCH_BYTES)
+    return LCA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const int rc = hip_status(scratch_ptr(&ws));
+  if (rc) return rc;
+  // the same kernels as indexer_score_topk over the device's scratch array: every buffer that must start at zero
+  // (the row histograms) is cleared by a fill kernel inside the call, the rest is written before it is read
+  return indexer_score_topk(qI, w, kI, B, Sq, HI, DI, N, m, k, q_start_pos, idx_out, score_out, ws,
+                            (size_t)LCA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 size_t sparse_mqa_attn_workspace_size(int B, int Sq, int H, int D, int max_entries) {

@@ -57,6 +57,7 @@ _lib.kv_compress.argtypes = [_P] * 8 + [_I, _L, _I, _I, _I, _L, lca_tensor, _P]
 _lib.indexer_score_topk_workspace_size.argtypes = [_I, _I, _I, _I]
 _lib.indexer_score_topk_workspace_size.restype = _S
 _lib.indexer_score_topk.argtypes = [lca_tensor, _P, lca_tensor] + [_I] * 7 + [_L, _P, _P, _P, _S, _P]
+_lib.indexer_score_topk_noalloc.argtypes = [lca_tensor, _P, lca_tensor] + [_I] * 7 + [_L, _P, _P, _P]
 _lib.lca_set_score_events.argtypes = [_P, _P]
 _lib.lca_set_score_events.restype = None
 _lib.lca_set_attn_events.argtypes = [_P, _P]
@@ -175,6 +176,16 @@ def indexer_score_topk(qI: lca_tensor, w, kI: lca_tensor, B: int, Sq: int, HI: i
     _check("indexer_score_topk", _lib.indexer_score_topk(qI, _ptr(w), kI, B, Sq, HI, DI, N, m, k, q_start_pos,
                                                          _ptr(idx_out), _ptr(score_out), _ptr(ws), ws_bytes,
                                                          _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # LCA_NOALLOC_SCRATCH_BYTES
+
+
+def indexer_score_topk_noalloc(qI: lca_tensor, w, kI: lca_tensor, B: int, Sq: int, HI: int, DI: int, N: int, m: int,
+                               k: int, q_start_pos: int, idx_out, score_out, stream=None):
+    _check("indexer_score_topk_noalloc",
+           _lib.indexer_score_topk_noalloc(qI, _ptr(w), kI, B, Sq, HI, DI, N, m, k, q_start_pos, _ptr(idx_out),
+                                           _ptr(score_out), _stream(stream)))
 
 
 def sparse_mqa_attn_workspace_size(B: int, Sq: int, H: int, D: int, max_entries: int) -> int:
