@@ -19,8 +19,8 @@
  *   - Every argument is validated on the host before anything is launched; on error nothing is enqueued
  *     and a negative lca_status is returned.  A failed launch returns LCA_ERR_HIP.  Faults inside a kernel
  *     surface at the caller's next synchronisation.
- *   - Positions are absolute token positions; query row r of a call is at q_start_pos + r for every sequence
- *     (all sequences of a call share their length and positions).
+ *   - Positions are absolute token positions; query row r of a call is at q_start_pos + r for every sequence,
+ *     unless the call takes a ragged batch (lca_ragged: each sequence at its own position).
  *   - Calls are deterministic: the same inputs give bit-identical outputs.  Calls that share a workspace must
  *     not overlap in time.
  */
@@ -66,7 +66,17 @@ typedef enum {
  * 1/sqrt(dim) rounded to fp32). */
 #define LCA_ROTATE_HADAMARD 1
 
-/* One cache (or query) tensor: `cap` rows per sequence, each row one entry of `dim` channels. */
+/* One cache (or query) tensor: `cap` rows per sequence, each row one entry of `dim` channels.
+ *
+ * Dense tensor (block_table NULL): sequence b owns rows [b * cap, (b + 1) * cap) of the data / rope / scale arrays.
+ * Paged tensor (block_table set; itsolotime page, question 5: the compressed cache is managed in fixed blocks of
+ * lcm(4, 128) = 128 tokens, i.e. 32 CSA entries or one HCA entry per block): the arrays hold a pool of pool_rows rows
+ * in blocks of block_rows rows, and row i of sequence b is pool row
+ *     block_table[b * (cap / block_rows) + i / block_rows] * block_rows + i % block_rows.
+ * block_table is a DEVICE int32 array [B][cap / block_rows] owned by the caller; its entries must name blocks inside
+ * the pool (not checked: they are device data).  Compressed caches and indexer keys may be paged (kv_compress and
+ * lca_encode write through the table; the indexer and the attention read through it); query tensors and the raw
+ * window may not. */
 typedef struct {
   int format;    /* lca_format                                                                       */
   int dim;       /* channels per row                                                                 */
@@ -76,13 +86,38 @@ typedef struct {
   void* rope;    /* LCA_MIXED_FP8 only, else NULL                                                    */
   void* scale;   /* LCA_MIXED_FP8 / LCA_FP4 only, else NULL                                          */
   int flags;     /* 0 or LCA_ROTATE_HADAMARD; other bits are INVALID_ARG                             */
+  const int32_t* block_table; /* NULL: dense; else paged (see above)                                 */
+  int block_rows;             /* paged: rows per block, a power of two dividing cap                  */
+  long long pool_rows;        /* paged: rows in the pool arrays (a multiple of block_rows, < 2^31)  */
 } lca_tensor;
+
+/* A ragged batch: each sequence of a call at its own position.  All pointers are DEVICE arrays of B elements owned
+ * by the caller; the struct itself is passed by a host pointer (NULL: every sequence at the call's uniform position).
+ *   pos[b] replaces the call's position for sequence b: start_pos of kv_compress (a multiple of m), q_start_pos of
+ *     indexer_score_topk, sparse_mqa_attn and hca_attn.  The call's uniform position must then be the largest pos[b]
+ *     (it sizes the launch and the host-side checks).  In the attention, sequence b's raw window rows start at
+ *     position raw_start_pos + pos[b] - q_start_pos (the same offset from its queries as the call's).
+ *   len[b] (kv_compress only, nullable): tokens of sequence b among the n given, 1 <= len[b] <= n; entries
+ *     [pos[b] / m, pos[b] / m + ceil(len[b] / m)) of sequence b are written. */
+typedef struct {
+  const long long* pos;
+  const int* len;
+} lca_ragged;
 
 /* Human-readable name of a status code (static string). */
 const char* lca_status_string(int status);
 
 /* The HIP runtime's message for the last LCA_ERR_HIP returned on the calling host thread (static string). */
 const char* lca_last_hip_error(void);
+
+/*
+ * lca_stream_read -- measurement helper, not part of the layer: reads `bytes` (a multiple of 16) of device memory at
+ * `src` once with 16-byte loads spread over `workgroups` workgroups of 256 threads, and XORs what it read into
+ * *out (uint32, device).  Timing it gives the read-stream rate that HBM-bound kernels are compared with, next to
+ * the 8 TB/s peak.  Errors: INVALID_ARG (null, bytes 0 or not a multiple of 16, workgroups out of [1, 2^20]),
+ * ALIGNMENT (src not 16-byte aligned, out not 4-byte aligned).
+ */
+int lca_stream_read(const void* src, size_t bytes, uint32_t* out, int workgroups, void* stream);
 
 /*
  * lca_encode -- quantise-on-write: encode fp32 rows into a cache tensor's format (the codec of the
@@ -94,6 +129,22 @@ const char* lca_last_hip_error(void);
  *         a rotation with dim not a power of two or the mixed format), UNSUPPORTED (dim > 1024).
  */
 int lca_encode(const float* src, int B, long long rows, long long row0, lca_tensor dst, void* stream);
+
+/* Epilogues kv_compress applies to each fp32 entry, in this order, before the output flag's Hadamard rotation and the
+ * encoding (paper notes, section 2.3: the Compressor normalises its entries with an RMSNorm over the head dim, and
+ * the Indexer excerpt applies rotary position embedding to the trailing channels):
+ *   norm_weight != NULL (device, float [c]): y[j] = x[j] / sqrt(mean_j(x[j]^2) + norm_eps) * norm_weight[j];
+ *   rope_dims > 0 (even, <= c): channel pair (c - rope_dims + 2i, c - rope_dims + 2i + 1) of entry e (the absolute
+ *     entry index) turns by the angle p * rope_base^(-2i / rope_dims) with p = m * e, the position of the first
+ *     token of the entry's block: (a, b) -> (a cos - b sin, a sin + b cos).  The angle and its sine and cosine are
+ *     computed in double precision, the rotation itself in fp32.
+ * The RMS is reduced in fp32. */
+typedef struct {
+  const float* norm_weight; /* NULL: no normalisation                                                            */
+  float norm_eps;           /* >= 0                                                                              */
+  int rope_dims;            /* 0: no rotary embedding                                                            */
+  float rope_base;          /* > 0 when rope_dims > 0                                                            */
+} lca_epilogue;
 
 /*
  * kv_compress -- stage 1, KV compression (paper notes section 2.3 Eq. 11-12 and the Compressor excerpt;
@@ -110,12 +161,16 @@ int lca_encode(const float* src, int B, long long rows, long long row0, lca_tens
  *   start_pos must be a multiple of m.  A decode append passes the tokens of the current partial block
  *   again plus the new token.  Writes entries [start_pos/m, start_pos/m + ceil(n/m)) of each sequence of
  *   out (out.dim == c); the last one is provisional when n is not a multiple of m.
+ *   epi (HOST pointer, nullable): the entry epilogues (see lca_epilogue); NULL applies none.
+ *   ragged (HOST pointer, nullable): per-sequence start positions and token counts (see lca_ragged); with
+ *   ragged->pos, a tail is passed whenever overlap (it is read for the sequences whose pos[b] > 0).
  * Errors: INVALID_ARG (null, n <= 0, c != out.dim, m <= 0, start_pos % m, rows beyond out.cap,
- *         missing tail), UNSUPPORTED (c > 1024), ALIGNMENT.
+ *         missing tail, an epilogue with rope_dims odd, negative or > c, rope_base <= 0, norm_eps < 0 or not
+ *         finite), UNSUPPORTED (c > 1024), ALIGNMENT.
  */
 int kv_compress(const float* Ca, const float* Cb, const float* Za, const float* Zb, const float* Ba, const float* Bb,
                 const float* tail_Cb, const float* tail_Zb, int B, long long n, int c, int m, int overlap,
-                long long start_pos, lca_tensor out, void* stream);
+                long long start_pos, const lca_epilogue* epi, const lca_ragged* ragged, lca_tensor out, void* stream);
 
 /*
  * indexer_score_topk -- stage 2, Lightning Indexer score and exact top-k (paper notes section 2.3 Eq. 16 and
@@ -133,8 +188,11 @@ int kv_compress(const float* Ca, const float* Cb, const float* Za, const float* 
  * (a[j] += a[j + L/2], L = next power of two of HI, zero padded), so inputs whose per-head dots are exact in
  * fp32 (e.g. fp4 x fp4 with a bounded scale spread) give bit-reproducible selections.
  * ws: device scratch of at least indexer_score_topk_workspace_size(B, Sq, N, k) bytes (contents ignored).
+ * ragged (HOST pointer, nullable): per-sequence query positions (see lca_ragged).
  * Errors: INVALID_ARG (null, sizes <= 0, dims mismatch, qI.cap != Sq * HI, DI % 16 for FP4),
- *         UNSUPPORTED (HI > 64, DI > 128, q/k formats not both float-like or both FP4), WORKSPACE, ALIGNMENT.
+ *         UNSUPPORTED (HI > 64, DI > 128, q/k formats not both float-like or both FP4; a paged kI with blocks of
+ *         fewer than 32 rows, or an fp4 pool of 2 GiB of codes or more, on the decode kernels -- 64 heads of 128
+ *         dims and up to 4 query rows per sequence), WORKSPACE, ALIGNMENT.
  */
 size_t indexer_score_topk_workspace_size(int B, int Sq, int N, int k);
 
@@ -142,7 +200,8 @@ size_t indexer_score_topk_workspace_size(int B, int Sq, int N, int k);
  * lca_set_score_events -- profiling hook for the dominant kernel.  While both are non-NULL, every
  * indexer_score_topk call made from the calling host thread records ev_begin (a hipEvent_t) on its stream just
  * before its scoring kernel and ev_end just after it, so the caller can time that kernel with
- * hipEventElapsedTime.  Pass NULL, NULL to stop.  The events are owned by the caller.
+ * hipEventElapsedTime.  Pass NULL, NULL to stop.  The events are owned by the caller.  Nothing is recorded while the
+ * stream is being captured into a graph.
  */
 void lca_set_score_events(void* ev_begin, void* ev_end);
 
@@ -155,7 +214,7 @@ void lca_set_attn_events(void* ev_begin, void* ev_end);
 
 int indexer_score_topk(lca_tensor qI, const float* w, lca_tensor kI, int B, int Sq, int HI, int DI, int N, int m, int k,
                        long long q_start_pos, int32_t* idx_out, float* score_out, void* ws, size_t ws_bytes,
-                       void* stream);
+                       const lca_ragged* ragged, void* stream);
 
 /*
  * indexer_score_topk_noalloc -- for callers that cannot allocate device memory (code under HIP graph capture,
@@ -171,7 +230,8 @@ int indexer_score_topk(lca_tensor qI, const float* w, lca_tensor kI, int B, int 
  */
 #define LCA_NOALLOC_SCRATCH_BYTES (32u << 20)
 int indexer_score_topk_noalloc(lca_tensor qI, const float* w, lca_tensor kI, int B, int Sq, int HI, int DI, int N, int m,
-                               int k, long long q_start_pos, int32_t* idx_out, float* score_out, void* stream);
+                               int k, long long q_start_pos, int32_t* idx_out, float* score_out,
+                               const lca_ragged* ragged, void* stream);
 
 /*
  * sparse_mqa_attn -- stage 3, shared-KV multi-query attention over the sliding window, the selected
@@ -184,12 +244,15 @@ int indexer_score_topk_noalloc(lca_tensor qI, const float* w, lca_tensor kI, int
  *   o[t][h] = sum_j e^(l_j - M) kv_j / (e^(sink[h] - M) + sum_j e^(l_j - M)).
  * sink[h] = -INFINITY disables the sink.  An empty set without a sink gives o = 0 and lse = -inf.
  *   q: [B][Sq][H][D] in q_format (LCA_F32 or LCA_BF16).
- *   kv_comp, kv_raw: dim = D, formats F32, BF16 or MIXED_FP8 (both the same format).
+ *   kv_comp, kv_raw: dim = D, formats F32, BF16 or MIXED_FP8 (both the same format).  A window-only call (k = 0,
+ *   idx NULL: the ratio-0 pure sliding-window layer of the paper notes' section 2.4 config excerpt) may pass a
+ *   kv_comp with data NULL (N is then taken as 0).
  *   The window positions of every query must lie in [raw_start_pos, raw_start_pos + S_raw), and
  *   S_raw <= kv_raw.cap.
  *   out: [B][Sq][H][D] in out_format (LCA_F32 or LCA_BF16).  lse_out (nullable): float [B][Sq][H], the log
  *   of the softmax denominator M + log(den).
  * ws: device scratch of at least sparse_mqa_attn_workspace_size(B, Sq, H, D, window + k) bytes.
+ * ragged (HOST pointer, nullable): per-sequence query positions (see lca_ragged).
  * Errors: INVALID_ARG, UNSUPPORTED (shape without a kernel: on the float path -- q or the caches not bf16 over
  *         bf16/mixed, or H != 64, or D != 512 -- H > 64, D > 512 or H * D > 8192), WORKSPACE, ALIGNMENT.
  */
@@ -197,7 +260,7 @@ size_t sparse_mqa_attn_workspace_size(int B, int Sq, int H, int D, int max_entri
 int sparse_mqa_attn(const void* q, int q_format, lca_tensor kv_comp, int N, lca_tensor kv_raw, long long raw_start_pos,
                     int S_raw, const int32_t* idx, int k, const float* sink, int B, int Sq, int H, int D, int window,
                     float scale, long long q_start_pos, void* out, int out_format, float* lse_out, void* ws,
-                    size_t ws_bytes, void* stream);
+                    size_t ws_bytes, const lca_ragged* ragged, void* stream);
 
 /*
  * hca_attn -- stage 4, the HCA variant: dense MQA over every visible m:1 entry (i < min(floor(t/m), N)),
@@ -209,7 +272,7 @@ size_t hca_attn_workspace_size(int B, int Sq, int H, int D, int max_entries);
 int hca_attn(const void* q, int q_format, lca_tensor kv_comp, int N, int m, lca_tensor kv_raw, long long raw_start_pos,
              int S_raw, const float* sink, int B, int Sq, int H, int D, int window, float scale,
              long long q_start_pos, void* out, int out_format, float* lse_out, void* ws, size_t ws_bytes,
-             void* stream);
+             const lca_ragged* ragged, void* stream);
 
 #ifdef __cplusplus
 }

@@ -63,6 +63,8 @@ class Workload:
     qi_fmt: str         # indexer query format
     q_std: float        # std of the attention queries
     scale: float        # softmax scale sigma
+    layer: str = ""     # "" (CSA if HI else HCA), "swa" (ratio-0 window-only layer) or "shared2" (two CSA layers
+                        # whose attention shares one indexer selection)
 
     @property
     def N(self) -> int:
@@ -92,7 +94,23 @@ WORKLOADS = {
                                           512, 128, "bf16", "bf16", "bf16", "bf16", 1.0 / math.sqrt(512), 1.0),
     "csa_decode_1m_mixed_mtp2": Workload("csa_decode_1m_mixed_mtp2", 107, 4, 1 << 20, 2, 4, 512, 64, 64, 64, 128,
                                          1024, 128, "mixed", "fp4", "bf16", "fp4", 1.0, 1.0 / math.sqrt(512)),
+    # the ratio-0 layer: window + sink only, at the decode shape of the 128K workload (the cache and indexer draws are
+    # made but unused)
+    "swa_decode_128k_bf16": Workload("swa_decode_128k_bf16", 108, 16, 131072, 1, 4, 512, 64, 64, 64, 128, 512, 128,
+                                     "bf16", "bf16", "bf16", "bf16", 1.0 / math.sqrt(512), 1.0, "swa"),
+    # two CSA layers, one indexer selection feeding both layers' attention (the second layer's own cache, window,
+    # queries and sink come from layer_inputs)
+    "csa_decode_128k_bf16_shared2": Workload("csa_decode_128k_bf16_shared2", 109, 16, 131072, 1, 4, 512, 64, 64, 64,
+                                             128, 512, 128, "bf16", "bf16", "bf16", "bf16", 1.0 / math.sqrt(512), 1.0,
+                                             "shared2"),
 }
+
+
+def layer_inputs(w: Workload, layer: int) -> dict:
+    """A further attention layer's own inputs for a step that shares one indexer selection across layers: the
+    decode draws of the same shape under seed + 1000 * layer (only the latent cache, window, queries, sink and the
+    latent compression streams are used)."""
+    return decode_inputs(dataclasses.replace(w, seed=w.seed + 1000 * layer))
 
 
 def scaled(w: Workload, **kw) -> Workload:

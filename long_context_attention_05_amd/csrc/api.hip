@@ -56,8 +56,15 @@ static bool rotation_ok(const lca_tensor& t) {
   return t.format != LCA_MIXED_FP8 && (t.dim & (t.dim - 1)) == 0;
 }
 
-int check_tensor(const lca_tensor& t, bool allow_fp4, bool allow_mixed) {
+int check_tensor(const lca_tensor& t, bool allow_fp4, bool allow_mixed, bool allow_paged = false) {
   if (t.dim <= 0 || t.cap <= 0 || !t.data || (t.flags & ~LCA_ROTATE_HADAMARD)) return LCA_ERR_INVALID_ARG;
+  if (t.block_table) {
+    if (!allow_paged) return LCA_ERR_INVALID_ARG;
+    const long long br = t.block_rows;
+    if (br <= 0 || (br & (br - 1)) || t.cap % br || t.pool_rows <= 0 || t.pool_rows % br || t.pool_rows >= (1ll << 31))
+      return LCA_ERR_INVALID_ARG;
+    if ((uintptr_t)t.block_table & 3u) return LCA_ERR_ALIGNMENT;
+  }
   switch (t.format) {
     case LCA_F32:
     case LCA_BF16:
@@ -160,16 +167,27 @@ size_t attn_ws_size(int B, int Sq, int H, int D, int max_entries) {
   return need;
 }
 
-int run_attn(const void* q, int q_format, const lca_tensor& comp, int N, int hca_m, const lca_tensor& raw,
+int run_attn(const void* q, int q_format, const lca_tensor& comp_in, int N, int hca_m, const lca_tensor& raw,
              long long raw_start, int S_raw, const int32_t* idx, int k, const float* sink, int B, int Sq, int H, int D,
              int window, float scale, long long q_start, void* out, int out_format, float* lse, void* ws,
-             size_t ws_bytes, void* stream) {
+             size_t ws_bytes, const lca_ragged* ragged, void* stream) {
   if (!q || !sink || !out) return LCA_ERR_INVALID_ARG;
+  const long long* seq_pos = ragged ? ragged->pos : nullptr;
+  if (seq_pos && ((uintptr_t)seq_pos & 7u)) return LCA_ERR_ALIGNMENT;
   if (B <= 0 || Sq <= 0 || H <= 0 || D <= 0 || window < 0 || N < 0 || q_start < 0) return LCA_ERR_INVALID_ARG;
   if (hca_m == 0 && (k < 0 || (k > 0 && !idx))) return LCA_ERR_INVALID_ARG;
   if (q_format != LCA_F32 && q_format != LCA_BF16) return LCA_ERR_INVALID_ARG;
   if (out_format != LCA_F32 && out_format != LCA_BF16) return LCA_ERR_INVALID_ARG;
-  int rc = check_tensor(comp, false, true);
+  // a window-only call (the ratio-0 layer: no compressed entry can be attended) may leave kv_comp empty; the
+  // kernels then take the window's tensor for both roles and never read a compressed row
+  lca_tensor comp = comp_in;
+  const bool no_comp = (hca_m == 0 && k == 0) || N == 0;
+  if (no_comp && !comp.data) {
+    if (window <= 0) return LCA_ERR_INVALID_ARG;
+    comp = raw;
+    N = 0;
+  }
+  int rc = check_tensor(comp, false, true, comp.data != raw.data);
   if (rc) return rc;
   if (window > 0) {
     rc = check_tensor(raw, false, true);
@@ -222,6 +240,7 @@ int run_attn(const void* q, int q_format, const lca_tensor& comp, int N, int hca
   a.out = out;
   a.out_format = out_format;
   a.lse = lse;
+  a.seq_pos = seq_pos;
   a.n_splits = ns;
   a.split_len = len;
   a.hg_mode = mode;
@@ -263,7 +282,7 @@ const char* lca_status_string(int status) {
 
 int lca_encode(const float* src, int B, long long rows, long long row0, lca_tensor dst, void* stream) {
   if (!src || B <= 0 || rows < 0 || row0 < 0) return LCA_ERR_INVALID_ARG;
-  int rc = check_tensor(dst, true, true);
+  int rc = check_tensor(dst, true, true, true);
   if (rc) return rc;
   if (row0 + rows > dst.cap) return LCA_ERR_INVALID_ARG;
   if (dst.dim > 1024) return LCA_ERR_UNSUPPORTED;
@@ -274,25 +293,45 @@ int lca_encode(const float* src, int B, long long rows, long long row0, lca_tens
 
 int kv_compress(const float* Ca, const float* Cb, const float* Za, const float* Zb, const float* Ba, const float* Bb,
                 const float* tail_Cb, const float* tail_Zb, int B, long long n, int c, int m, int overlap,
-                long long start_pos, lca_tensor out, void* stream) {
+                long long start_pos, const lca_epilogue* epi, const lca_ragged* ragged, lca_tensor out,
+                void* stream) {
   if (!Ca || !Za || !Ba || B <= 0 || n <= 0 || c <= 0 || m <= 0 || start_pos < 0) return LCA_ERR_INVALID_ARG;
   if (overlap && (!Cb || !Zb || !Bb)) return LCA_ERR_INVALID_ARG;
   if (start_pos % m != 0) return LCA_ERR_INVALID_ARG;
+  const long long* seq_pos = ragged ? ragged->pos : nullptr;
+  const int* seq_len = ragged ? ragged->len : nullptr;
+  if ((seq_pos && ((uintptr_t)seq_pos & 7u)) || (seq_len && ((uintptr_t)seq_len & 3u))) return LCA_ERR_ALIGNMENT;
+  // a ragged call's sequences may start anywhere up to start_pos: the tail is needed whenever any of them may be > 0
+  const bool tail = overlap && (start_pos > 0 || seq_pos);
   if (overlap && start_pos > 0 && (!tail_Cb || !tail_Zb)) return LCA_ERR_INVALID_ARG;
-  int rc = check_tensor(out, true, true);
+  int rc = check_tensor(out, true, true, true);
   if (rc) return rc;
   if (out.dim != c) return LCA_ERR_INVALID_ARG;
   if (c > 1024) return LCA_ERR_UNSUPPORTED;
   if (!rotation_ok(out)) return LCA_ERR_INVALID_ARG;
   const long long nb = (n + m - 1) / m;
   if (start_pos / m + nb > out.cap) return LCA_ERR_INVALID_ARG;
+  lca_epilogue e{nullptr, 0.0f, 0, 0.0f};
+  if (epi) {
+    e = *epi;
+    if (e.rope_dims < 0 || (e.rope_dims & 1) || e.rope_dims > c) return LCA_ERR_INVALID_ARG;
+    if (e.rope_dims > 0 && !(e.rope_base > 0.0f && e.rope_base < INFINITY)) return LCA_ERR_INVALID_ARG;
+    if (e.norm_weight && !(e.norm_eps >= 0.0f && e.norm_eps < INFINITY)) return LCA_ERR_INVALID_ARG;
+    if ((uintptr_t)e.norm_weight & 3u) return LCA_ERR_ALIGNMENT;
+  }
   return hip_status(launch_compress(Ca, overlap ? Cb : nullptr, Za, overlap ? Zb : nullptr, Ba, overlap ? Bb : nullptr,
-                                    (overlap && start_pos > 0) ? tail_Cb : nullptr,
-                                    (overlap && start_pos > 0) ? tail_Zb : nullptr, B, n, c, m, overlap ? 1 : 0,
-                                    start_pos, out, (hipStream_t)stream));
+                                    tail ? tail_Cb : nullptr, tail ? tail_Zb : nullptr, B, n, c, m, overlap ? 1 : 0,
+                                    start_pos, seq_pos, seq_len, e, out, (hipStream_t)stream));
 }
 
 const char* lca_last_hip_error(void) { return hipGetErrorString(t_last_hip); }
+
+int lca_stream_read(const void* src, size_t bytes, uint32_t* out, int workgroups, void* stream) {
+  if (!src || !out || bytes == 0 || bytes % 16 != 0 || workgroups <= 0 || workgroups > (1 << 20))
+    return LCA_ERR_INVALID_ARG;
+  if (!aligned16(src) || ((uintptr_t)out & 3u)) return LCA_ERR_ALIGNMENT;
+  return hip_status(launch_stream_read(src, bytes, out, workgroups, (hipStream_t)stream));
+}
 
 void lca_set_score_events(void* ev_begin, void* ev_end) {
   t_ev_begin = (hipEvent_t)ev_begin;
@@ -362,12 +401,14 @@ hipError_t scratch_ptr(void** out) {
 
 int indexer_score_topk(lca_tensor qI, const float* w, lca_tensor kI, int B, int Sq, int HI, int DI, int N, int m, int k,
                        long long q_start_pos, int32_t* idx_out, float* score_out, void* ws, size_t ws_bytes,
-                       void* stream) {
+                       const lca_ragged* ragged, void* stream) {
   if (!w || !idx_out || B <= 0 || Sq <= 0 || HI <= 0 || DI <= 0 || N < 0 || m <= 0 || k <= 0 || q_start_pos < 0)
     return LCA_ERR_INVALID_ARG;
+  const long long* seq_pos = ragged ? ragged->pos : nullptr;
+  if (seq_pos && ((uintptr_t)seq_pos & 7u)) return LCA_ERR_ALIGNMENT;
   int rc = check_tensor(qI, true, false);
   if (rc) return rc;
-  rc = check_tensor(kI, true, false);
+  rc = check_tensor(kI, true, false, true);
   if (rc) return rc;
   // the kernels address query row r of sequence b at rows (b * Sq + r) * HI + h: the tensor must be exactly that
   if (qI.dim != DI || kI.dim != DI || qI.cap != (long long)Sq * HI || kI.cap < N) return LCA_ERR_INVALID_ARG;
@@ -380,27 +421,40 @@ int indexer_score_topk(lca_tensor qI, const float* w, lca_tensor kI, int B, int 
   const IdxWs L = idx_ws_layout(B, Sq, N > 0 ? N : 1);
   const bool multi = N > 0 && Sq <= kDecodeMaxRows && N <= kMaxMultiN &&
                      indexer_uses_decode_kernel(B, Sq, HI, DI, N, qI.format, kI.format);
+  // the decode scorers read a paged key cache a wave's 64 keys at a time from at most two blocks, and the fp4 one
+  // addresses the pool with 32-bit buffer offsets
+  if (kI.block_table && N > 0 && indexer_uses_decode_kernel(B, Sq, HI, DI, N, qI.format, kI.format)) {
+    if (kI.block_rows < 32) return LCA_ERR_UNSUPPORTED;
+    if (kI.format == LCA_FP4 && kI.pool_rows * (DI / 2) >= (1ll << 31)) return LCA_ERR_UNSUPPORTED;
+  }
   char* wsb = (char*)ws;
   int* state = multi ? (int*)(wsb + L.state) : nullptr;
-  IdxArgs a{qI, kI, w, (uint32_t*)(wsb + L.keys), B, Sq, HI, DI, N, m, q_start_pos, state};
+  IdxArgs a{qI, kI, w, (uint32_t*)(wsb + L.keys), B, Sq, HI, DI, N, m, q_start_pos, seq_pos, state};
   if (N > 0) {
     if (state) {  // the decode scoring kernels add into the row histograms
       rc = hip_status(launch_sel_zero(state, B * Sq, st));
       if (rc) return rc;
     }
     const bool timed = t_ev_begin && t_ev_end;
-    if (timed && hipEventRecord(t_ev_begin, st) != hipSuccess) return LCA_ERR_HIP;
+    if (timed) {
+      rc = hip_status(record_hook_event(t_ev_begin, st));
+      if (rc) return rc;
+    }
     rc = hip_status(launch_indexer_scores(a, st));
     if (rc) return rc;
-    if (timed && hipEventRecord(t_ev_end, st) != hipSuccess) return LCA_ERR_HIP;
+    if (timed) {
+      rc = hip_status(record_hook_event(t_ev_end, st));
+      if (rc) return rc;
+    }
   }
-  SelArgs s{(const uint32_t*)(wsb + L.keys), idx_out, score_out, B * Sq, Sq, N, m, k, q_start_pos, state,
+  SelArgs s{(const uint32_t*)(wsb + L.keys), idx_out, score_out, B * Sq, Sq, N, m, k, q_start_pos, seq_pos, state,
             multi ? (int*)(wsb + L.counts) : nullptr, multi ? (uint2*)(wsb + L.cand) : nullptr};
   return hip_status(launch_topk(s, st));
 }
 
 int indexer_score_topk_noalloc(lca_tensor qI, const float* w, lca_tensor kI, int B, int Sq, int HI, int DI, int N, int m,
-                               int k, long long q_start_pos, int32_t* idx_out, float* score_out, void* stream) {
+                               int k, long long q_start_pos, int32_t* idx_out, float* score_out,
+                               const lca_ragged* ragged, void* stream) {
   if (B > 0 && Sq > 0 && N > 0 && indexer_score_topk_workspace_size(B, Sq, N, k) > (size_t)LCA_NOALLOC_SCRATCH_BYTES)
     return LCA_ERR_WORKSPACE;
   void* ws = nullptr;
@@ -409,7 +463,7 @@ int indexer_score_topk_noalloc(lca_tensor qI, const float* w, lca_tensor kI, int
   // the same kernels as indexer_score_topk over the device's scratch array: every buffer that must start at zero
   // (the row histograms) is cleared by a fill kernel inside the call, the rest is written before it is read
   return indexer_score_topk(qI, w, kI, B, Sq, HI, DI, N, m, k, q_start_pos, idx_out, score_out, ws,
-                            (size_t)LCA_NOALLOC_SCRATCH_BYTES, stream);
+                            (size_t)LCA_NOALLOC_SCRATCH_BYTES, ragged, stream);
 }
 
 size_t sparse_mqa_attn_workspace_size(int B, int Sq, int H, int D, int max_entries) {
@@ -419,9 +473,9 @@ size_t sparse_mqa_attn_workspace_size(int B, int Sq, int H, int D, int max_entri
 int sparse_mqa_attn(const void* q, int q_format, lca_tensor kv_comp, int N, lca_tensor kv_raw, long long raw_start_pos,
                     int S_raw, const int32_t* idx, int k, const float* sink, int B, int Sq, int H, int D, int window,
                     float scale, long long q_start_pos, void* out, int out_format, float* lse_out, void* ws,
-                    size_t ws_bytes, void* stream) {
+                    size_t ws_bytes, const lca_ragged* ragged, void* stream) {
   return run_attn(q, q_format, kv_comp, N, 0, kv_raw, raw_start_pos, S_raw, idx, k, sink, B, Sq, H, D, window, scale,
-                  q_start_pos, out, out_format, lse_out, ws, ws_bytes, stream);
+                  q_start_pos, out, out_format, lse_out, ws, ws_bytes, ragged, stream);
 }
 
 size_t hca_attn_workspace_size(int B, int Sq, int H, int D, int max_entries) {
@@ -431,10 +485,10 @@ size_t hca_attn_workspace_size(int B, int Sq, int H, int D, int max_entries) {
 int hca_attn(const void* q, int q_format, lca_tensor kv_comp, int N, int m, lca_tensor kv_raw, long long raw_start_pos,
              int S_raw, const float* sink, int B, int Sq, int H, int D, int window, float scale,
              long long q_start_pos, void* out, int out_format, float* lse_out, void* ws, size_t ws_bytes,
-             void* stream) {
+             const lca_ragged* ragged, void* stream) {
   if (m <= 0) return LCA_ERR_INVALID_ARG;
   return run_attn(q, q_format, kv_comp, N, m, kv_raw, raw_start_pos, S_raw, nullptr, 0, sink, B, Sq, H, D, window,
-                  scale, q_start_pos, out, out_format, lse_out, ws, ws_bytes, stream);
+                  scale, q_start_pos, out, out_format, lse_out, ws, ws_bytes, ragged, stream);
 }
 
 }  // extern "C"

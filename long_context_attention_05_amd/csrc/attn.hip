@@ -25,13 +25,18 @@ namespace lca {
 
 
 struct RowList {
-  long long w0;  // first window position
-  int nw;        // window entries
-  int nc;        // compressed list length
+  long long w0;    // first window position
+  long long raw0;  // position of the sequence's raw row 0
+  int nw;          // window entries
+  int nc;          // compressed list length
 };
 
-__device__ __forceinline__ RowList row_list(const AttnArgs& a, long long t) {
+// The list of query row r of sequence b: its position is the sequence's (ragged batch) or the call's, plus r.
+__device__ __forceinline__ RowList row_list(const AttnArgs& a, int b, int r) {
+  const long long pos = seq_position(a.seq_pos, a.q_start, b);
+  const long long t = pos + r;
   RowList L;
+  L.raw0 = a.raw_start + (pos - a.q_start);
   long long w0 = t - a.window + 1;
   if (w0 < 0) w0 = 0;
   L.w0 = w0;
@@ -45,9 +50,11 @@ __device__ __forceinline__ RowList row_list(const AttnArgs& a, long long t) {
   return L;
 }
 
-// Row (within the tensor) of list position p, or -1 if the position is padding.
-__device__ __forceinline__ long long list_row(const AttnArgs& a, const RowList& L, int b, int r, int p) {
-  if (p < L.nw) return (long long)b * a.raw.cap + (L.w0 + p - a.raw_start);
+// Storage row of list position p of query row r of sequence b -- window positions in the raw tensor, the rest in the
+// compressed one (through its block table when it is paged) -- or -1 where the position is padding.  Storage rows of
+// both tensors are below 2^31.
+__device__ __forceinline__ int list_row(const AttnArgs& a, const RowList& L, int b, int r, int p) {
+  if (p < L.nw) return (int)((long long)b * a.raw.cap + (L.w0 + p - L.raw0));
   int j = p - L.nw;
   if (j >= L.nc) return -1;
   int e;
@@ -57,7 +64,12 @@ __device__ __forceinline__ long long list_row(const AttnArgs& a, const RowList& 
     e = a.idx[((long long)b * a.Sq + r) * a.k + j];
     if (e < 0 || e >= a.N) return -1;
   }
-  return (long long)b * a.comp.cap + e;
+  return (int)tensor_row(a.comp, b, e);
+}
+
+// Rows held by a tensor's arrays: the pool of a paged tensor, B * cap of a dense one.
+__host__ __device__ __forceinline__ long long tensor_storage_rows(const lca_tensor& t, int B) {
+  return t.block_table ? t.pool_rows : (long long)B * t.cap;
 }
 
 // The running softmax max only moves when a logit exceeds it by more than kRescaleSlack (e^8 keeps every weight and
@@ -149,8 +161,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_mfma_kernel(AttnArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int hl = lane & 15, grp = lane >> 4;
   const int split = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
-  const long long t = a.q_start + r;
-  const RowList L = row_list(a, t);
+  const RowList L = row_list(a, b, r);
   const int total = L.nw + L.nc;
   const int p_begin = split * a.split_len;
   const int npos = max(min(a.split_len, total - p_begin), 0);
@@ -158,15 +169,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_mfma_kernel(AttnArgs a) {
 
   for (int i = threadIdx.x; i < npos; i += blockDim.x) {
     const int p = p_begin + i;
-    int row;
-    if (p < L.nw) {
-      row = (int)(L.w0 + p - a.raw_start);
-    } else if (a.hca_m > 0) {
-      row = p - L.nw;
-    } else {
-      const int e = a.idx[((long long)b * a.Sq + r) * a.k + (p - L.nw)];
-      row = (e >= 0 && e < a.N) ? e : -1;
-    }
+    const int row = list_row(a, L, b, r, p);
     rows_s[i] = row;
   }
   // Q^T B operand for 16 K-steps of 32 channels: lane holds q[head][32 s + 8 grp .. + 7]
@@ -189,7 +192,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_mfma_kernel(AttnArgs a) {
     gok = i0 + ge < npos && row >= 0;
     const bool from_raw = p_begin + i < L.nw;
     const lca_tensor& src = from_raw ? a.raw : a.comp;
-    const long long rr = (long long)b * src.cap + (row >= 0 ? row : 0);
+    const long long rr = row >= 0 ? row : 0;
     if constexpr (FMT == LCA_BF16) {
       const uint8_t* gp = (const uint8_t*)src.data + rr * 1024 + 128 * gc;
 #pragma unroll
@@ -392,8 +395,7 @@ __global__ __launch_bounds__(kPsThreads) void attn_pfs_kernel(AttnArgs a) {
   const bool scorer = wave < 4;    // wave-uniform role
   const int vw = wave & 3;         // head group (score waves) or channel quarter (value waves)
   const int split = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
-  const long long t = a.q_start + r;
-  const RowList L = row_list(a, t);
+  const RowList L = row_list(a, b, r);
   const int total = L.nw + L.nc;
   const int p_begin = split * a.split_len;
   const int npos = max(min(a.split_len, total - p_begin), 0);
@@ -412,15 +414,7 @@ __global__ __launch_bounds__(kPsThreads) void attn_pfs_kernel(AttnArgs a) {
   }
   for (int i = threadIdx.x; i < npos; i += blockDim.x) {
     const int p = p_begin + i;
-    int row;
-    if (p < L.nw) {
-      row = (int)(L.w0 + p - a.raw_start);
-    } else if (a.hca_m > 0) {
-      row = p - L.nw;
-    } else {
-      const int e = a.idx[((long long)b * a.Sq + r) * a.k + (p - L.nw)];
-      row = (e >= 0 && e < a.N) ? e : -1;
-    }
+    const int row = list_row(a, L, b, r, p);
     pd_rows[i] = row;
   }
   // value waves: acc[hg][dt] holds o^T[channel 128 v + 16 dt + 4 grp + x][head 16 hg + hl] in lane (hl, grp)
@@ -444,11 +438,11 @@ __global__ __launch_bounds__(kPsThreads) void attn_pfs_kernel(AttnArgs a) {
 
   const int ntiles = (npos + kPfTE - 1) / kPfTE;
   if (ntiles > 0) {  // block-uniform
+    // descriptors over the whole tensors (the table holds storage rows; the launcher checks both stay under 2 GiB)
     const __amdgpu_buffer_rsrc_t raw_rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)((const uint8_t*)a.raw.data + (long long)b * a.raw.cap * 1024), 0, (int)(a.raw.cap * 1024), kBufRsrcWord3);
+        (void*)a.raw.data, 0, (int)(tensor_storage_rows(a.raw, a.B) * 1024), kBufRsrcWord3);
     const __amdgpu_buffer_rsrc_t comp_rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)((const uint8_t*)a.comp.data + (long long)b * a.comp.cap * 1024), 0, (int)(a.comp.cap * 1024),
-        kBufRsrcWord3);
+        (void*)a.comp.data, 0, (int)(tensor_storage_rows(a.comp, a.B) * 1024), kBufRsrcWord3);
     // Value wave v moves entries 8 v .. 8 v + 7 of tile tt into ring slot S (lane j takes chunk j ^ (tile row % 16)
     // of the entry into LDS chunk j); positions past the slice repeat its last entry, so every tile issues the same
     // number of loads and the wait counts stay fixed.
@@ -762,7 +756,7 @@ __device__ __forceinline__ void hg_load(HgTile<FMT>& T, const AttnArgs& a, const
   const int row = rows_s[i];
   const bool raw = sl.p_begin + i < sl.nw;
   const lca_tensor& src = raw ? a.raw : a.comp;
-  const long long rr = (long long)sl.b * src.cap + (row >= 0 ? row : 0);
+  const long long rr = row >= 0 ? row : 0;
   T.valid = __ballot(lane < 16 && i0 + hl < sl.npos && row >= 0) & 0xFFFFull;
   if constexpr (FMT == LCA_BF16) {
     const unsigned long long base = (unsigned long long)((const uint8_t*)src.data + rr * 1024) + 16 * grp;
@@ -811,8 +805,7 @@ __global__ __launch_bounds__(256) void attn_hgw_kernel(AttnArgs a, int pairs) {
   const int S = a.n_splits;
   const int qrow = pair / S, split = pair % S;
   const int b = qrow / a.Sq, r = qrow % a.Sq;
-  const long long t = a.q_start + r;
-  const RowList L = row_list(a, t);
+  const RowList L = row_list(a, b, r);
   const int total = L.nw + L.nc;
   HgSlice sl;
   sl.b = b;
@@ -831,15 +824,7 @@ __global__ __launch_bounds__(256) void attn_hgw_kernel(AttnArgs a, int pairs) {
   // padding)
   for (int i = threadIdx.x; i < sl.npos; i += blockDim.x) {
     const int p = sl.p_begin + i;
-    int row;
-    if (p < L.nw) {
-      row = (int)(L.w0 + p - a.raw_start);
-    } else if (a.hca_m > 0) {
-      row = p - L.nw;
-    } else {
-      const int e = a.idx[((long long)b * a.Sq + r) * a.k + (p - L.nw)];
-      row = (e >= 0 && e < a.N) ? e : -1;
-    }
+    const int row = list_row(a, L, b, r, p);
     rows_s[i] = row;
   }
   // the 16 heads' queries as the B operand: lane holds head 16 hg + hl, channels 32 s + 8 grp .. + 7
@@ -1059,7 +1044,7 @@ __device__ __forceinline__ void wd_load(WdTile<FMT>& T, const AttnArgs& a, const
     const int row = rows_s[i];
     const bool raw = sl.p_begin + i < sl.nw;
     const lca_tensor& src = raw ? a.raw : a.comp;
-    const long long rr = (long long)sl.b * src.cap + (row >= 0 ? row : 0);
+    const long long rr = row >= 0 ? row : 0;
     valid |= (uint32_t)(__ballot(lane < 16 && i0 + 16 * eb + hl < sl.npos && row >= 0) & 0xFFFFull) << (16 * eb);
     if constexpr (FMT == LCA_BF16) {
       const unsigned long long base = (unsigned long long)((const uint8_t*)src.data + rr * 1024) + 128 * wave + 16 * grp;
@@ -1113,8 +1098,7 @@ __global__ __launch_bounds__(kWdThreads) void attn_wide_kernel(AttnArgs a) {
   const int S = a.n_splits;
   const int qrow = item / S, split = item % S;
   const int b = qrow / a.Sq, r = qrow % a.Sq;
-  const long long t = a.q_start + r;
-  const RowList L = row_list(a, t);
+  const RowList L = row_list(a, b, r);
   const int total = L.nw + L.nc;
   HgSlice sl;
   sl.b = b;
@@ -1136,15 +1120,7 @@ __global__ __launch_bounds__(kWdThreads) void attn_wide_kernel(AttnArgs a) {
 
   for (int i = threadIdx.x; i < sl.npos; i += blockDim.x) {
     const int p = sl.p_begin + i;
-    int row;
-    if (p < L.nw) {
-      row = (int)(L.w0 + p - a.raw_start);
-    } else if (a.hca_m > 0) {
-      row = p - L.nw;
-    } else {
-      const int e = a.idx[((long long)b * a.Sq + r) * a.k + (p - L.nw)];
-      row = (e >= 0 && e < a.N) ? e : -1;
-    }
+    const int row = list_row(a, L, b, r, p);
     rows_s[i] = row;
   }
   // queries (B operand of the partial S^T): lane holds head 16 hb + hl, channels 64 wave + 32 s + 8 grp .. + 7
@@ -1361,8 +1337,7 @@ __global__ __launch_bounds__(256) void attn_simt_kernel(AttnArgs a) {
   __shared__ float m_s[64], l_s[64];
   const int H = a.H, D = a.D;
   const int split = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
-  const long long t = a.q_start + r;
-  const RowList L = row_list(a, t);
+  const RowList L = row_list(a, b, r);
   const int total = L.nw + L.nc;
   const int p_begin = split * a.split_len;
   const int p_end = min(p_begin + a.split_len, total);
@@ -1498,7 +1473,7 @@ __global__ __launch_bounds__(64 * kDsWaves) void attn_dec_score_kernel(AttnArgs 
   uint8_t* const kt = ds_lds + 65536;
   const int qrow = blockIdx.x, tile = blockIdx.y;
   const int b = qrow / a.Sq, r = qrow - b * a.Sq;
-  const RowList L = row_list(a, a.q_start + r);
+  const RowList L = row_list(a, b, r);
   const int total = L.nw + L.nc;
   const int p0 = tile * kDsTile;
   if (p0 >= total) return;  // past this row's list: the value pass does not read these tiles
@@ -1526,9 +1501,10 @@ __global__ __launch_bounds__(64 * kDsWaves) void attn_dec_score_kernel(AttnArgs 
   }
   __builtin_amdgcn_s_waitcnt(kWaitVm8);  // the index load has landed; the eight query copies may still be in flight
   __builtin_amdgcn_sched_barrier(0);
-  const int rowl = rwl ? (int)(L.w0 + pl - a.raw_start) : ((sel & (xl >= 0) & (xl < a.N)) ? xl : -1);
+  const int rowl = rwl ? (int)(L.w0 + pl - L.raw0) : ((sel & (xl >= 0) & (xl < a.N)) ? xl : -1);
   const bool okl = rowl >= 0;
-  const long long rabsl = (long long)b * (rwl ? a.raw.cap : a.comp.cap) + (okl ? rowl : 0);
+  // storage row: the raw tensor is dense; the compressed one may be paged (a dependent table read)
+  const long long rabsl = rwl ? (long long)b * a.raw.cap + rowl : tensor_row(a.comp, b, okl ? rowl : 0);
   const int rlo = (int)rabsl, rhi = (int)(rabsl >> 32), rwi = rwl ? 1 : 0;
   // entries
   if constexpr (!MX) {
@@ -1674,7 +1650,7 @@ void attn_dec_value_kernel(AttnArgs a) {
   __shared__ float dred[kGroups][16];
   const int qrow = blockIdx.x, cb = blockIdx.y, hg = blockIdx.z;
   const int b = qrow / a.Sq, r = qrow - b * a.Sq;
-  const RowList L = row_list(a, a.q_start + r);
+  const RowList L = row_list(a, b, r);
   const int total = L.nw + L.nc;
   const int nt = (total + kDecTile - 1) / kDecTile;
   const int T = a.dec_tiles;
@@ -1684,14 +1660,7 @@ void attn_dec_value_kernel(AttnArgs a) {
 
   // rows of all T * 32 list positions (-1: padding or past the list)
   for (int p = tid; p < T * kDecTile; p += 64 * kDvWaves) {
-    int row = -1;
-    if (p < L.nw) {
-      row = (int)(L.w0 + p - a.raw_start);
-    } else if (p < total) {
-      const int e = a.idx[(long long)qrow * a.k + (p - L.nw)];
-      row = (e >= 0 && e < a.N) ? e : -1;
-    }
-    drows[p] = row;
+    drows[p] = p < total ? list_row(a, L, b, r, p) : -1;
   }
   // this thread's tiles' (m_t, l_t) for head 16 hg + (tid % 16) and that head's sink; both read before the value
   // loads (a load issued after them could only be waited for together with all of them), tiles past the list
@@ -1739,7 +1708,7 @@ void attn_dec_value_kernel(AttnArgs a) {
           const bool rw = p < L.nw;
           // (fields selected one by one: a lane-dependent choice of the whole tensor struct would be read through
           // per-lane pointers)
-          const long long rabs = (long long)b * (rw ? a.raw.cap : a.comp.cap) + (row >= 0 ? row : 0);
+          const long long rabs = row >= 0 ? row : 0;
           const uint8_t* vp = FMT == LCA_MIXED_FP8
                                   ? (const uint8_t*)(rw ? a.raw.rope : a.comp.rope) + rabs * 128
                                   : (const uint8_t*)(rw ? a.raw.data : a.comp.data) + rabs * 1024 + 128 * cb;
@@ -1753,7 +1722,7 @@ void attn_dec_value_kernel(AttnArgs a) {
           const int row = drows[p];
           ok[i][k] = row >= 0;
           const bool rw = p < L.nw;
-          const long long rabs = (long long)b * (rw ? a.raw.cap : a.comp.cap) + (row >= 0 ? row : 0);
+          const long long rabs = row >= 0 ? row : 0;
           vr[i][k] = *(gbl_u32x4_t*)((const uint8_t*)(rw ? a.raw.data : a.comp.data) + rabs * 448 + 64 * cb +
                                      16 * (lane & 3));
           es[i][k] = ((const float*)(rw ? a.raw.scale : a.comp.scale))[rabs];
@@ -2039,7 +2008,7 @@ hipError_t launch_attn(AttnArgs a, hipStream_t st, hipEvent_t ev_begin, hipEvent
   dim3 grid((unsigned)a.n_splits, (unsigned)a.Sq, (unsigned)a.B);
   clear_stale_error();
   if (ev_begin && ev_end) {
-    const hipError_t e = hipEventRecord(ev_begin, st);
+    const hipError_t e = record_hook_event(ev_begin, st);
     if (e != hipSuccess) return e;
   }
   if (mfma && a.hg_mode == 3) {
@@ -2074,7 +2043,8 @@ hipError_t launch_attn(AttnArgs a, hipStream_t st, hipEvent_t ev_begin, hipEvent
     hipError_t e = ensure_dyn_lds((const void*)attn_mfma_kernel<LCA_BF16>, (int)kMfmaLds);
     if (e == hipSuccess) e = ensure_dyn_lds((const void*)attn_mfma_kernel<LCA_MIXED_FP8>, (int)kMfmaLds);
     if (e != hipSuccess) return e;
-    if (a.comp.format == LCA_BF16 && a.raw.cap * 1024 < (1ll << 31) && a.comp.cap * 1024 < (1ll << 31)) {
+    if (a.comp.format == LCA_BF16 && tensor_storage_rows(a.raw, a.B) * 1024 < (1ll << 31) &&
+        tensor_storage_rows(a.comp, a.B) * 1024 < (1ll << 31)) {
       a.part_bf16 = 1;  // split partials in bf16, for this kernel and the merge after it
       hipLaunchKernelGGL(attn_pfs_kernel, grid, dim3(kPsThreads), 0, st, a);
     }
@@ -2086,7 +2056,7 @@ hipError_t launch_attn(AttnArgs a, hipStream_t st, hipEvent_t ev_begin, hipEvent
     hipLaunchKernelGGL(attn_simt_kernel, grid, dim3(256), 0, st, a);
   }
   hipError_t e = hipGetLastError();
-  if (e == hipSuccess && ev_begin && ev_end) e = hipEventRecord(ev_end, st);
+  if (e == hipSuccess && ev_begin && ev_end) e = record_hook_event(ev_end, st);
   if (e != hipSuccess || a.n_splits == 1) return e;
   const size_t lds = sizeof(float) * (size_t)a.n_splits;
   hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)a.H, (unsigned)a.Sq, (unsigned)a.B), dim3(kMergeThreads), lds,

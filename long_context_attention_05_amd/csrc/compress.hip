@@ -24,7 +24,16 @@ struct RowOut {
   void* data;
   void* rope_data;
   void* scale;
+  const int32_t* table;  // paged output: block table [B][cap / block_rows] (else NULL)
+  int block_rows;
 };
+
+// Storage row of row i of sequence b of the output (see tensor_row).
+__device__ __forceinline__ long long out_row(const RowOut& o, int b, long long i) {
+  if (!o.table) return (long long)b * o.cap + i;
+  const int sh = __builtin_ctz((unsigned)o.block_rows);
+  return (long long)o.table[(long long)b * (o.cap >> sh) + (i >> sh)] * o.block_rows + (i & (o.block_rows - 1));
+}
 
 __device__ __forceinline__ float block_max_256(float v, float* red) {
   v = wave_max(v);
@@ -34,6 +43,17 @@ __device__ __forceinline__ float block_max_256(float v, float* red) {
   __syncthreads();
   float r = red[0];
   for (int i = 1; i < (int)(blockDim.x >> 6); ++i) r = fmaxf(r, red[i]);
+  return r;
+}
+
+__device__ __forceinline__ float block_sum_256(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __syncthreads();
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  float r = red[0];
+  for (int i = 1; i < (int)(blockDim.x >> 6); ++i) r += red[i];
   return r;
 }
 
@@ -173,14 +193,59 @@ __global__ __launch_bounds__(kRowThreads) void encode_rows_kernel(const float* _
     int j = threadIdx.x + blockDim.x * u;
     v[u] = (j < o.dim) ? s[j] : 0.0f;
   }
-  store_row<CPT>(o, (long long)b * o.cap + row0 + r, v, red, rot);
+  store_row<CPT>(o, out_row(o, b, row0 + r), v, red, rot);
 }
 
 struct CompressArgs {
   const float *Ca, *Cb, *Za, *Zb, *Ba, *Bb, *tCb, *tZb;
   long long n, start_pos;
+  const long long* seq_pos;  // nullable [B]: sequence b's start (a ragged batch)
+  const int* seq_len;        // nullable [B]: sequence b's tokens among the n given
   int c, m, overlap;
+  lca_epilogue epi;
 };
+
+// The entry epilogues (RMSNorm, then rotary embedding of the trailing channels at the block's first token) on a row
+// held as v[u] = channel (threadIdx.x + blockDim.x * u).  All threads of the block must call this.  A channel pair
+// (2i, 2i + 1) lies in lanes l and l ^ 1 of one wave (blockDim.x is a multiple of 64), so each lane takes its
+// partner's value with one shuffle.
+template <int CPT>
+__device__ void entry_epilogue(const lca_epilogue& e, int c, long long entry, int m, float (&v)[CPT], float* red) {
+  const int nt = blockDim.x;
+  if (e.norm_weight) {
+    float ss = 0.0f;
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int j = threadIdx.x + nt * u;
+      if (j < c) ss += v[u] * v[u];
+    }
+    ss = block_sum_256(ss, red);
+    const float inv = 1.0f / sqrtf(ss / (float)c + e.norm_eps);
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int j = threadIdx.x + nt * u;
+      if (j < c) v[u] = v[u] * inv * e.norm_weight[j];
+    }
+  }
+  if (e.rope_dims > 0) {
+    const int r0 = c - e.rope_dims;
+    const double p = (double)m * (double)entry;
+    const double lb = log2((double)e.rope_base);
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int j = threadIdx.x + nt * u;
+      const float other = __shfl_xor(v[u], 1, 64);
+      if (j >= r0 && j < c) {
+        const int i = (j - r0) >> 1;
+        const double ang = p * exp2(-2.0 * (double)i / (double)e.rope_dims * lb);
+        double sd, cd;
+        sincos(ang, &sd, &cd);
+        const float sn = (float)sd, cs = (float)cd;
+        v[u] = ((j - r0) & 1) ? other * sn + v[u] * cs : v[u] * cs - other * sn;
+      }
+    }
+  }
+}
 
 __device__ __forceinline__ void softmax_acc(float l, float x, float& mx, float& den, float& num) {
   float nm = fmaxf(mx, l);
@@ -198,7 +263,9 @@ __global__ __launch_bounds__(kRowThreads) void compress_kernel(CompressArgs a, R
   const long long i = blockIdx.x;  // local entry index
   const int b = blockIdx.y;
   const int c = a.c, m = a.m;
-  const long long gblock = a.start_pos / m + i;
+  const long long n_b = a.seq_len ? a.seq_len[b] : a.n;  // this sequence's tokens (rows [0, n_b) of its slice)
+  if ((long long)m * i >= n_b) return;                      // block-uniform: no token of this sequence's entry i
+  const long long gblock = seq_position(a.seq_pos, a.start_pos, b) / m + i;
   float mx[CPT], den[CPT], num[CPT];
 #pragma unroll
   for (int u = 0; u < CPT; ++u) {
@@ -212,7 +279,7 @@ __global__ __launch_bounds__(kRowThreads) void compress_kernel(CompressArgs a, R
   // has at most 2m = 8 of them: one round of loads); loads past the last candidate or channel repeat a valid
   // address and are masked, so no branch separates them.
   const long long pa0 = (long long)m * i;
-  const int na = (int)((a.n - pa0) < m ? (a.n - pa0) : m);
+  const int na = (int)((n_b - pa0) < m ? (n_b - pa0) : m);
   const int nbk = (a.overlap && gblock >= 1) ? m : 0;
   const int ncand = na + nbk;
   constexpr int kBatch = 8;
@@ -255,12 +322,13 @@ __global__ __launch_bounds__(kRowThreads) void compress_kernel(CompressArgs a, R
   float v[CPT];
 #pragma unroll
   for (int u = 0; u < CPT; ++u) v[u] = num[u] / den[u];
-  store_row<CPT>(o, (long long)b * o.cap + gblock, v, red, rot);
+  if (a.epi.norm_weight || a.epi.rope_dims > 0) entry_epilogue<CPT>(a.epi, c, gblock, m, v, red);
+  store_row<CPT>(o, out_row(o, b, gblock), v, red, rot);
 }
 
 static RowOut row_out(const lca_tensor& t) {
   return RowOut{t.format, t.dim, t.rope_dims, (t.flags & LCA_ROTATE_HADAMARD) ? 1 : 0, t.cap, t.data, t.rope,
-                t.scale};
+                t.scale, t.block_table, t.block_rows};
 }
 
 static int threads_for(int c) {
@@ -286,8 +354,9 @@ hipError_t launch_encode(const float* src, int B, long long rows, long long row0
 
 hipError_t launch_compress(const float* Ca, const float* Cb, const float* Za, const float* Zb, const float* Ba,
                            const float* Bb, const float* tCb, const float* tZb, int B, long long n, int c, int m,
-                           int overlap, long long start_pos, const lca_tensor& out, hipStream_t st) {
-  CompressArgs a{Ca, Cb, Za, Zb, Ba, Bb, tCb, tZb, n, start_pos, c, m, overlap};
+                           int overlap, long long start_pos, const long long* seq_pos, const int* seq_len,
+                           const lca_epilogue& epi, const lca_tensor& out, hipStream_t st) {
+  CompressArgs a{Ca, Cb, Za, Zb, Ba, Bb, tCb, tZb, n, start_pos, seq_pos, seq_len, c, m, overlap, epi};
   RowOut o = row_out(out);
   int nt = threads_for(c);
   int cpt = (c + nt - 1) / nt;

@@ -45,7 +45,7 @@ __global__ __launch_bounds__(256) void idx_score_simt(IdxArgs a) {
   __shared__ float k_s[kSimtTile * 129];
   __shared__ float p_s[kSimtTile * 65];
   const int b = blockIdx.z, r = blockIdx.y;
-  const long long t = a.q_start + r;
+  const long long t = seq_position(a.seq_pos, a.q_start, b) + r;
   const int nvis = nvis_of(t, a.m, a.N);
   const int e0 = blockIdx.x * kSimtTile;
   if (e0 >= nvis) return;
@@ -54,7 +54,7 @@ __global__ __launch_bounds__(256) void idx_score_simt(IdxArgs a) {
   for (int x = threadIdx.x; x < HI * DI; x += blockDim.x) q_s[x] = load_elem(a.q, qrow0 + x / DI, x % DI);
   for (int x = threadIdx.x; x < kSimtTile * DI; x += blockDim.x) {
     int e = x / DI, j = x % DI;
-    k_s[e * 129 + j] = (e0 + e < nvis) ? load_elem(a.k, (long long)b * a.k.cap + e0 + e, j) : 0.0f;
+    k_s[e * 129 + j] = (e0 + e < nvis) ? load_elem(a.k, tensor_row(a.k, b, e0 + e), j) : 0.0f;
   }
   __syncthreads();
   const float* wr = a.w + ((long long)b * a.Sq + r) * HI;
@@ -168,7 +168,8 @@ __global__ __launch_bounds__(256) void idx_score_mfma(IdxArgs a, int qpb) {
   const int e0 = blockIdx.x * kMfmaEntriesPerBlock + wave * kMfmaEntriesPerWave;
   const int r_begin = blockIdx.y * qpb;
   const int r_end = min(r_begin + qpb, a.Sq);
-  const int nvis_last = nvis_of(a.q_start + r_end - 1, a.m, a.N);
+  const long long qpos = seq_position(a.seq_pos, a.q_start, b);
+  const int nvis_last = nvis_of(qpos + r_end - 1, a.m, a.N);
   if (blockIdx.x * kMfmaEntriesPerBlock >= nvis_last) return;  // whole block invisible to every query
 
   // keys of this wave: two 32-entry column tiles, B operand for 8 K-steps each
@@ -178,7 +179,7 @@ __global__ __launch_bounds__(256) void idx_score_mfma(IdxArgs a, int qpb) {
     const int e = e0 + 32 * u + col;
     uint4 raw[8];
     if (e < nvis_last) {
-      load_row64<FMT>(a.k, (long long)b * a.k.cap + e, g, raw);
+      load_row64<FMT>(a.k, tensor_row(a.k, b, e), g, raw);
     } else {
 #pragma unroll
       for (int s = 0; s < 8; ++s) raw[s] = make_uint4(0, 0, 0, 0);
@@ -209,7 +210,7 @@ __global__ __launch_bounds__(256) void idx_score_mfma(IdxArgs a, int qpb) {
       load_qblock<FMT>(a, ((long long)b * a.Sq + rn) * 64, qn);
       if (threadIdx.x < 64) wn = a.w[((long long)b * a.Sq + rn) * 64 + threadIdx.x];
     }
-    const int nvis = nvis_of(a.q_start + r, a.m, a.N);
+    const int nvis = nvis_of(qpos + r, a.m, a.N);
     if (e0 < nvis) {  // wave-uniform
       f32x16_t acc[2][2];
 #pragma unroll
@@ -342,13 +343,17 @@ struct BfStage {
   uint4 c[kBfGroups][4];
 };
 
-__device__ __forceinline__ void bf_load_stage(BfStage& S, const uint8_t* kb, int kbase, int klast, int lane) {
+// Key e of the wave's keys kbase .. kbase + 63 (kbase a multiple of 64) is row b * cap + e of a dense cache; in a
+// paged one (blocks of at least 32 rows) it sits in block blk[0] (keys kbase .. + 31) or blk[1] (the rest).
+__device__ __forceinline__ void bf_load_stage(BfStage& S, const uint8_t* kd, long long dense0, const int (&blk)[2],
+                                              int br, int kbase, int klast, int lane) {
   const int g = lane >> 4, col = lane & 15;
 #pragma unroll
   for (int j = 0; j < kBfGroups; ++j) {
     const int e = min(kbase + 16 * j + col, klast);
+    const long long row = br ? (long long)blk[j >= 2] * br + (e & (br - 1)) : dense0 + e;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) S.c[j][s] = *(const uint4*)(kb + (long long)e * 256 + 16 * g + 64 * s);
+    for (int s = 0; s < 4; ++s) S.c[j][s] = *(const uint4*)(kd + row * 256 + 16 * g + 64 * s);
   }
 }
 
@@ -360,17 +365,33 @@ __global__ __launch_bounds__(256, 2) void idx_score_decode_bf16(IdxArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int g = lane >> 4, col = lane & 15;
   const int qrow = blockIdx.y, b = qrow / a.Sq;  // query row b * Sq + r
-  const int nvis = nvis_of(a.q_start + (qrow - b * a.Sq), a.m, a.N);
+  const int nvis = nvis_of(seq_position(a.seq_pos, a.q_start, b) + (qrow - b * a.Sq), a.m, a.N);
   const int k0 = blockIdx.x * (NST * 4 * KPW);
   const int k1 = min(k0 + NST * 4 * KPW, nvis);
   if (k0 >= k1) return;
   const bool hist = a.sel_state != nullptr;
   if (hist)
     for (int i = threadIdx.x; i < kSelBins; i += blockDim.x) hist_s[i] = 0;
-  const uint8_t* kb = (const uint8_t*)a.k.data + (long long)b * a.k.cap * 256;
+  const uint8_t* kd = (const uint8_t*)a.k.data;
+  // paged: every stage's blocks, resolved before the stream starts (wave-uniform table reads)
+  const int br = a.k.block_table ? a.k.block_rows : 0;
+  const long long dense0 = (long long)b * a.k.cap;
+  int blk[NST][2];
+#pragma unroll
+  for (int st = 0; st < NST; ++st) {
+    blk[st][0] = blk[st][1] = 0;
+    if (br) {
+      const int kbase = k0 + st * 4 * KPW + wave * KPW;
+      const int sh = __builtin_ctz((unsigned)br);
+      const long long tb = (long long)b * (a.k.cap >> sh);
+      const int kl = min(kbase, k1 - 1), kh = min(kbase + 32, k1 - 1);
+      blk[st][0] = a.k.block_table[tb + (kl >> sh)];
+      blk[st][1] = a.k.block_table[tb + (kh >> sh)];
+    }
+  }
 
   BfStage S[2];
-  bf_load_stage(S[0], kb, k0 + wave * KPW, k1 - 1, lane);
+  bf_load_stage(S[0], kd, dense0, blk[0], br, k0 + wave * KPW, k1 - 1, lane);
   bf16x8_t qa[4][4];
   float wv[4][4];
 #pragma unroll
@@ -390,7 +411,7 @@ __global__ __launch_bounds__(256, 2) void idx_score_decode_bf16(IdxArgs a) {
   for (int st = 0; st < NST; ++st) {
     const int kbase = k0 + st * 4 * KPW + wave * KPW;
     if (st + 1 < NST) {
-      bf_load_stage(S[(st + 1) & 1], kb, kbase + 4 * KPW, k1 - 1, lane);
+      bf_load_stage(S[(st + 1) & 1], kd, dense0, blk[st + 1], br, kbase + 4 * KPW, k1 - 1, lane);
       __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the scoring
     }
     if (st > 0) store_key(a, qrow, k1, pend, hist_s, hist);
@@ -496,7 +517,7 @@ __global__ __launch_bounds__(kF4rWaves * 64) void idx_score_decode_fp4_ring(IdxA
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int col = lane & 31, hh = lane >> 5;
   const int qrow = blockIdx.y, b = qrow / a.Sq;  // query row b * Sq + r
-  const int nvis = nvis_of(a.q_start + (qrow - b * a.Sq), a.m, a.N);
+  const int nvis = nvis_of(seq_position(a.seq_pos, a.q_start, b) + (qrow - b * a.Sq), a.m, a.N);
   const int k0 = blockIdx.x * (NST * kF4rStage);
   const int k1 = min(k0 + NST * kF4rStage, nvis);
   if (k0 >= k1) return;  // block-uniform
@@ -522,12 +543,34 @@ __global__ __launch_bounds__(kF4rWaves * 64) void idx_score_decode_fp4_ring(IdxA
   i32x8_t qop[2][2][2];
   int qs[2][2][2];
 
-  // buffer descriptors over the workgroup's own keys [k0, k1): offsets stay small whatever the cache size, and the
-  // range check covers exactly the keys the workgroup may read
+  // buffer descriptors over the workgroup's own keys [k0, k1) of a dense cache (offsets stay small whatever the cache
+  // size, and the range check covers exactly the keys the workgroup may read), or over the whole pool of a paged one
+  // (blocks of at least 32 rows, pool under 2 GiB of codes: checked on the host)
+  const int br = a.k.block_table ? a.k.block_rows : 0;
+  const long long rb0 = br ? 0 : (long long)b * a.k.cap + k0;
+  const long long nrows = br ? a.k.pool_rows : (long long)(k1 - k0);
   const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((const uint8_t*)a.k.data + ((long long)b * a.k.cap + k0) * 64), 0, (k1 - k0) * 64, kIdxBufWord3);
+      (void*)((const uint8_t*)a.k.data + rb0 * 64), 0, (int)(nrows * 64), kIdxBufWord3);
   const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((const uint8_t*)a.k.scale + ((long long)b * a.k.cap + k0) * 8), 0, (k1 - k0) * 8, kIdxBufWord3);
+      (void*)((const uint8_t*)a.k.scale + rb0 * 8), 0, (int)(nrows * 8), kIdxBufWord3);
+  // paged: the blocks of each stage's 64 wave keys (keys 0..31 and 32..63 of the slice), read before the ring starts
+  int blk[NST][2];
+#pragma unroll
+  for (int st = 0; st < NST; ++st) {
+    blk[st][0] = blk[st][1] = 0;
+    if (br) {
+      const int sh = __builtin_ctz((unsigned)br);
+      const long long tb = (long long)b * (a.k.cap >> sh);
+      const int kl = min(k0 + st * kF4rStage + 64 * wave, k1 - 1), kh = min(kl + 32, k1 - 1);
+      blk[st][0] = a.k.block_table[tb + (kl >> sh)];
+      blk[st][1] = a.k.block_table[tb + (kh >> sh)];
+    }
+  }
+  // row (relative to the descriptor) of key kst + 64 w + o, o < 64
+  auto key_row = [&](int st, int kst, int o) -> int {
+    const int key = min(kst + 64 * wave + o, k1 - k0 - 1);
+    return br ? blk[st][o >= 32] * br + ((k0 + key) & (br - 1)) : key;
+  };
   // stage st into slot S: code instruction i of wave w moves keys 64 w + 16 i .. + 15 (lane l: key + l / 4, chunk
   // position l % 4 holding code chunk (l % 4) ^ (l / 16)); scale instruction i moves 32 keys' scale rows.  Keys past
   // k1 repeat key k1 - 1.
@@ -536,15 +579,15 @@ __global__ __launch_bounds__(kF4rWaves * 64) void idx_score_decode_fp4_ring(IdxA
     const int kst = st * kF4rStage;  // relative to k0
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int key = min(kst + 64 * wave + 16 * i + (lane >> 2), k1 - k0 - 1);
+      const int row = key_row(st, kst, 16 * i + (lane >> 2));
       __builtin_amdgcn_raw_ptr_buffer_load_lds(crs, (idx_lds_void_t*)(f4r_codes<S>() + (64 * wave + 16 * i) * 64), 16,
-                                               key * 64 + 16 * ((lane & 3) ^ (lane >> 4)), 0, 0, 0);
+                                               row * 64 + 16 * ((lane & 3) ^ (lane >> 4)), 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int key = min(kst + 64 * wave + 32 * i + (lane >> 1), k1 - k0 - 1);
+      const int row = key_row(st, kst, 32 * i + (lane >> 1));
       __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, (idx_lds_void_t*)(f4r_scales<S>() + (64 * wave + 32 * i) * 8), 4,
-                                               key * 8 + 4 * (lane & 1), 0, 0, 0);
+                                               row * 8 + 4 * (lane & 1), 0, 0, 0);
     }
   };
   // 64 x 32 dots of the wave's key tile u (keys 64 w + 32 u + col of stage slot S)
@@ -654,7 +697,7 @@ bool indexer_uses_decode_kernel(int B, int Sq, int HI, int DI, int N, int q_form
 }
 
 hipError_t launch_indexer_scores(const IdxArgs& a, hipStream_t st) {
-  const int nvis_max = nvis_of(a.q_start + a.Sq - 1, a.m, a.N);
+  const int nvis_max = nvis_of(a.q_start + a.Sq - 1, a.m, a.N);  // q_start is the largest position of the call
   if (nvis_max <= 0) return hipSuccess;
   clear_stale_error();
   const bool mfma = a.HI == 64 && a.DI == 128 && a.q.format == a.k.format &&

@@ -93,6 +93,21 @@ __device__ __forceinline__ float fp4_value(uint32_t code) {
 }
 
 // ------------------------------------------------------------------------------------------------
+// Rows and positions
+// ------------------------------------------------------------------------------------------------
+// Storage row of row i of sequence b: b * cap + i in a dense tensor; through the block table in a paged one.
+__device__ __forceinline__ long long tensor_row(const lca_tensor& t, int b, long long i) {
+  if (!t.block_table) return (long long)b * t.cap + i;
+  const int sh = __builtin_ctz((unsigned)t.block_rows);
+  const int blk = t.block_table[(long long)b * (t.cap >> sh) + (i >> sh)];
+  return (long long)blk * t.block_rows + (i & (t.block_rows - 1));
+}
+// Position of sequence b: its own in a ragged batch, else the call's.
+__device__ __forceinline__ long long seq_position(const long long* pos, long long uniform, int b) {
+  return pos ? pos[b] : uniform;
+}
+
+// ------------------------------------------------------------------------------------------------
 // Order-preserving key of an fp32 score (larger float -> larger key); -0 is folded onto +0.
 // ------------------------------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t score_key(float s) {

@@ -15,6 +15,15 @@ inline void clear_stale_error() {
   (void)e;
 }
 
+// Records a profiling-hook event on st; nothing while st is being captured into a graph (the hooks time eager
+// launches only).
+inline hipError_t record_hook_event(hipEvent_t e, hipStream_t st) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  hipError_t r = hipStreamIsCapturing(st, &cs);
+  if (r != hipSuccess) return r;
+  return cs == hipStreamCaptureStatusNone ? hipEventRecord(e, st) : hipSuccess;
+}
+
 // Raises a kernel's dynamic LDS limit to `bytes` on the current device, once per (kernel, device); safe to call from
 // several host threads at once (api.hip).
 hipError_t ensure_dyn_lds(const void* kernel, int bytes);
@@ -24,7 +33,8 @@ hipError_t launch_encode(const float* src, int B, long long rows, long long row0
                          hipStream_t st);
 hipError_t launch_compress(const float* Ca, const float* Cb, const float* Za, const float* Zb, const float* Ba,
                            const float* Bb, const float* tCb, const float* tZb, int B, long long n, int c, int m,
-                           int overlap, long long start_pos, const lca_tensor& out, hipStream_t st);
+                           int overlap, long long start_pos, const long long* seq_pos, const int* seq_len,
+                           const lca_epilogue& epi, const lca_tensor& out, hipStream_t st);
 
 // stage 2a, indexer scores (indexer.hip)
 struct IdxArgs {
@@ -32,7 +42,8 @@ struct IdxArgs {
   const float* w;
   uint32_t* keys;  // [B][Sq][N] order-preserving score keys (workspace)
   int B, Sq, HI, DI, N, m;
-  long long q_start;
+  long long q_start;       // the largest query position of the call (row r of sequence b: seq_position + r)
+  const long long* seq_pos;  // nullable [B]: each sequence's position (a ragged batch)
   int* sel_state;  // nullable: [B * Sq][kSelStateInts] row histograms the decode kernels add into (zeroed first)
 };
 // Decode kernels take up to this many query rows per sequence (one token, or a few draft tokens verified together):
@@ -51,6 +62,7 @@ struct SelArgs {
   float* score_out;      // nullable [rows][k]
   int rows, Sq, N, m, k;
   long long q_start;
+  const long long* seq_pos;  // nullable [rows / Sq]: each sequence's position (a ragged batch)
   // decode rows: the row histograms written by the scoring kernel, and the multi-workgroup select buffers; all null
   // for the select that makes its own histogram passes
   int* sel_state;  // [rows][kSelStateInts]: histograms of key bits [31:21] (all keys, from the scoring kernel) and
@@ -80,6 +92,8 @@ struct AttnArgs {
   int B, Sq, H, D, window;
   float scale;
   long long q_start;
+  const long long* seq_pos;  // nullable [B]: each sequence's position; its raw rows start at raw_start + seq_pos[b] -
+                             // q_start
   void* out;
   int out_format;
   float* lse;
@@ -101,5 +115,8 @@ constexpr int kHgSplitMax = 2048;  // list positions per workgroup slice in the 
 bool attn_uses_mfma(int H, int D, int q_format, int kv_format);
 // ev_begin / ev_end (nullable): recorded around the attention kernel, before the merge of split partials.
 hipError_t launch_attn(AttnArgs a, hipStream_t st, hipEvent_t ev_begin = nullptr, hipEvent_t ev_end = nullptr);
+
+// measurement helper (measure.hip)
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* out, int workgroups, hipStream_t st);
 
 }  // namespace lca

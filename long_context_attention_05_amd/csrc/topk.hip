@@ -71,7 +71,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(SelArgs a) {
 
   const int row = blockIdx.x;
   const int r = row % a.Sq;
-  const long long t = a.q_start + r;
+  const long long t = seq_position(a.seq_pos, a.q_start, row / a.Sq) + r;
   const long long nv = t / a.m;
   const int nvis = (int)(nv < a.N ? nv : a.N);
   const int k = a.k;
@@ -219,7 +219,7 @@ hipError_t launch_sel_zero(int* state, int rows, hipStream_t st) {
 }
 
 __device__ __forceinline__ int sel_row_nvis(const SelArgs& a, int row) {
-  const long long t = a.q_start + row % a.Sq;
+  const long long t = seq_position(a.seq_pos, a.q_start, row / a.Sq) + row % a.Sq;
   const long long nv = t / a.m;
   return (int)(nv < a.N ? nv : a.N);
 }
@@ -487,7 +487,7 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(SelArgs a) {
 
 hipError_t launch_topk(const SelArgs& a, hipStream_t st) {
   if (a.rows <= 0) return hipSuccess;
-  // the longest visible row decides the variant (rows of one call differ only by their causal limit)
+  // the longest visible row decides the variant (q_start is the largest position of the call)
   long long nv = (a.q_start + a.Sq - 1) / a.m;
   const int nvis_max = (int)(nv < a.N ? nv : a.N);
   clear_stale_error();

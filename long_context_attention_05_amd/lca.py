@@ -30,7 +30,17 @@ class LcaError(RuntimeError):
 class lca_tensor(ctypes.Structure):
     _fields_ = [("format", ctypes.c_int), ("dim", ctypes.c_int), ("rope_dims", ctypes.c_int),
                 ("cap", ctypes.c_longlong), ("data", ctypes.c_void_p), ("rope", ctypes.c_void_p),
-                ("scale", ctypes.c_void_p), ("flags", ctypes.c_int)]
+                ("scale", ctypes.c_void_p), ("flags", ctypes.c_int), ("block_table", ctypes.c_void_p),
+                ("block_rows", ctypes.c_int), ("pool_rows", ctypes.c_longlong)]
+
+
+class lca_ragged(ctypes.Structure):
+    _fields_ = [("pos", ctypes.c_void_p), ("len", ctypes.c_void_p)]
+
+
+class lca_epilogue(ctypes.Structure):
+    _fields_ = [("norm_weight", ctypes.c_void_p), ("norm_eps", ctypes.c_float), ("rope_dims", ctypes.c_int),
+                ("rope_base", ctypes.c_float)]
 
 
 if not os.path.exists(LIB_PATH):
@@ -53,11 +63,13 @@ _lib.lca_status_string.restype = ctypes.c_char_p
 _lib.lca_last_hip_error.argtypes = []
 _lib.lca_last_hip_error.restype = ctypes.c_char_p
 _lib.lca_encode.argtypes = [_P, _I, _L, _L, lca_tensor, _P]
-_lib.kv_compress.argtypes = [_P] * 8 + [_I, _L, _I, _I, _I, _L, lca_tensor, _P]
+_lib.lca_stream_read.argtypes = [_P, _S, _P, _I, _P]
+_RG = ctypes.POINTER(lca_ragged)
+_lib.kv_compress.argtypes = [_P] * 8 + [_I, _L, _I, _I, _I, _L, ctypes.POINTER(lca_epilogue), _RG, lca_tensor, _P]
 _lib.indexer_score_topk_workspace_size.argtypes = [_I, _I, _I, _I]
 _lib.indexer_score_topk_workspace_size.restype = _S
-_lib.indexer_score_topk.argtypes = [lca_tensor, _P, lca_tensor] + [_I] * 7 + [_L, _P, _P, _P, _S, _P]
-_lib.indexer_score_topk_noalloc.argtypes = [lca_tensor, _P, lca_tensor] + [_I] * 7 + [_L, _P, _P, _P]
+_lib.indexer_score_topk.argtypes = [lca_tensor, _P, lca_tensor] + [_I] * 7 + [_L, _P, _P, _P, _S, _RG, _P]
+_lib.indexer_score_topk_noalloc.argtypes = [lca_tensor, _P, lca_tensor] + [_I] * 7 + [_L, _P, _P, _RG, _P]
 _lib.lca_set_score_events.argtypes = [_P, _P]
 _lib.lca_set_score_events.restype = None
 _lib.lca_set_attn_events.argtypes = [_P, _P]
@@ -65,11 +77,11 @@ _lib.lca_set_attn_events.restype = None
 _lib.sparse_mqa_attn_workspace_size.argtypes = [_I] * 5
 _lib.sparse_mqa_attn_workspace_size.restype = _S
 _lib.sparse_mqa_attn.argtypes = [_P, _I, lca_tensor, _I, lca_tensor, _L, _I, _P, _I, _P] + [_I] * 5 + [
-    _F, _L, _P, _I, _P, _P, _S, _P]
+    _F, _L, _P, _I, _P, _P, _S, _RG, _P]
 _lib.hca_attn_workspace_size.argtypes = [_I] * 5
 _lib.hca_attn_workspace_size.restype = _S
 _lib.hca_attn.argtypes = [_P, _I, lca_tensor, _I, _I, lca_tensor, _L, _I, _P] + [_I] * 5 + [
-    _F, _L, _P, _I, _P, _P, _S, _P]
+    _F, _L, _P, _I, _P, _P, _S, _RG, _P]
 
 
 def library():
@@ -126,6 +138,7 @@ class CacheTensor:
         return lca_tensor(FORMATS[self.fmt], self.dim, self.rope, self.cap, _ptr(self.data), _ptr(self.rope_t),
                           _ptr(self.scale_t), self.flags)
 
+
     def host(self) -> dict:
         """Copy to host numpy arrays (for comparisons), as a dict of raw storage arrays."""
         import numpy as np
@@ -138,6 +151,27 @@ class CacheTensor:
         return d
 
 
+class PagedCache(CacheTensor):
+    """A paged tensor: a pool of `pool_blocks` blocks of `block_rows` rows and a device block table [B][cap /
+    block_rows] (int32) mapping each sequence's logical blocks to pool blocks."""
+
+    def __init__(self, fmt: str, B: int, cap: int, dim: int, rope: int, block_rows: int, table, pool_blocks: int,
+                 device="cuda", flags: int = 0):
+        assert cap % block_rows == 0
+        super().__init__(fmt, 1, pool_blocks * block_rows, dim, rope, device, flags)
+        self.B, self.cap, self.block_rows, self.pool_rows = B, cap, block_rows, pool_blocks * block_rows
+        self.table = table  # device int32 tensor [B, cap / block_rows]
+        assert tuple(table.shape) == (B, cap // block_rows)
+
+    def desc(self) -> lca_tensor:
+        d = super().desc()
+        d.cap = self.cap
+        d.block_table = _ptr(self.table)
+        d.block_rows = self.block_rows
+        d.pool_rows = self.pool_rows
+        return d
+
+
 def plain_desc(t, fmt: str, dim: int, cap: int) -> lca_tensor:
     """Descriptor over an existing dense f32/bf16 tensor (rows = B * cap)."""
     return lca_tensor(FORMATS[fmt], dim, 0, cap, _ptr(t), None, None)
@@ -146,14 +180,41 @@ def plain_desc(t, fmt: str, dim: int, cap: int) -> lca_tensor:
 # ----------------------------------------------------------------------------------------------------
 # entry points (names as in include/lca.h)
 # ----------------------------------------------------------------------------------------------------
+def lca_stream_read(src, nbytes: int, out, workgroups: int, stream=None):
+    """Measurement helper: one streaming read of `nbytes` at src (see include/lca.h)."""
+    _check("lca_stream_read", _lib.lca_stream_read(_ptr(src), nbytes, _ptr(out), workgroups, _stream(stream)))
+
+
 def lca_encode(src, B: int, rows: int, row0: int, dst: lca_tensor, stream=None):
     _check("lca_encode", _lib.lca_encode(_ptr(src), B, rows, row0, dst, _stream(stream)))
 
 
+def epilogue(norm_weight=None, norm_eps: float = 0.0, rope_dims: int = 0, rope_base: float = 0.0) -> lca_epilogue:
+    """kv_compress's entry epilogues (norm_weight: a device float tensor [c] or None, referenced by the descriptor
+    so that it outlives the asynchronous calls)."""
+    e = lca_epilogue(_ptr(norm_weight), norm_eps, rope_dims, rope_base)
+    e._tensors = (norm_weight,)
+    return e
+
+
+def ragged(pos, lens=None) -> lca_ragged:
+    """Per-sequence positions (device int64 tensor [B]) and, for kv_compress, token counts (device int32 [B]).  The
+    descriptor holds references to both tensors, so that they outlive the calls that read them asynchronously."""
+    r = lca_ragged(_ptr(pos), _ptr(lens))
+    r._tensors = (pos, lens)
+    return r
+
+
+def _rg(r):
+    return None if r is None else ctypes.byref(r)
+
+
 def kv_compress(Ca, Cb, Za, Zb, Ba, Bb, tail_Cb, tail_Zb, B: int, n: int, c: int, m: int, overlap: bool,
-                start_pos: int, out: lca_tensor, stream=None):
+                start_pos: int, out: lca_tensor, stream=None, epi: lca_epilogue | None = None,
+                ragged: lca_ragged | None = None):
     _check("kv_compress", _lib.kv_compress(_ptr(Ca), _ptr(Cb), _ptr(Za), _ptr(Zb), _ptr(Ba), _ptr(Bb), _ptr(tail_Cb),
-                                           _ptr(tail_Zb), B, n, c, m, int(bool(overlap)), start_pos, out,
+                                           _ptr(tail_Zb), B, n, c, m, int(bool(overlap)), start_pos,
+                                           None if epi is None else ctypes.byref(epi), _rg(ragged), out,
                                            _stream(stream)))
 
 
@@ -172,20 +233,22 @@ def lca_set_attn_events(ev_begin, ev_end):
 
 
 def indexer_score_topk(qI: lca_tensor, w, kI: lca_tensor, B: int, Sq: int, HI: int, DI: int, N: int, m: int, k: int,
-                       q_start_pos: int, idx_out, score_out, ws, ws_bytes: int, stream=None):
+                       q_start_pos: int, idx_out, score_out, ws, ws_bytes: int, stream=None,
+                       ragged: lca_ragged | None = None):
     _check("indexer_score_topk", _lib.indexer_score_topk(qI, _ptr(w), kI, B, Sq, HI, DI, N, m, k, q_start_pos,
                                                          _ptr(idx_out), _ptr(score_out), _ptr(ws), ws_bytes,
-                                                         _stream(stream)))
+                                                         _rg(ragged), _stream(stream)))
 
 
 NOALLOC_SCRATCH_BYTES = 32 << 20  # LCA_NOALLOC_SCRATCH_BYTES
 
 
 def indexer_score_topk_noalloc(qI: lca_tensor, w, kI: lca_tensor, B: int, Sq: int, HI: int, DI: int, N: int, m: int,
-                               k: int, q_start_pos: int, idx_out, score_out, stream=None):
+                               k: int, q_start_pos: int, idx_out, score_out, stream=None,
+                               ragged: lca_ragged | None = None):
     _check("indexer_score_topk_noalloc",
            _lib.indexer_score_topk_noalloc(qI, _ptr(w), kI, B, Sq, HI, DI, N, m, k, q_start_pos, _ptr(idx_out),
-                                           _ptr(score_out), _stream(stream)))
+                                           _ptr(score_out), _rg(ragged), _stream(stream)))
 
 
 def sparse_mqa_attn_workspace_size(B: int, Sq: int, H: int, D: int, max_entries: int) -> int:
@@ -194,11 +257,12 @@ def sparse_mqa_attn_workspace_size(B: int, Sq: int, H: int, D: int, max_entries:
 
 def sparse_mqa_attn(q, q_format: int, kv_comp: lca_tensor, N: int, kv_raw: lca_tensor, raw_start_pos: int, S_raw: int,
                     idx, k: int, sink, B: int, Sq: int, H: int, D: int, window: int, scale: float, q_start_pos: int,
-                    out, out_format: int, lse_out, ws, ws_bytes: int, stream=None):
+                    out, out_format: int, lse_out, ws, ws_bytes: int, stream=None,
+                    ragged: lca_ragged | None = None):
     _check("sparse_mqa_attn", _lib.sparse_mqa_attn(_ptr(q), q_format, kv_comp, N, kv_raw, raw_start_pos, S_raw,
                                                    _ptr(idx), k, _ptr(sink), B, Sq, H, D, window, scale, q_start_pos,
                                                    _ptr(out), out_format, _ptr(lse_out), _ptr(ws), ws_bytes,
-                                                   _stream(stream)))
+                                                   _rg(ragged), _stream(stream)))
 
 
 def hca_attn_workspace_size(B: int, Sq: int, H: int, D: int, max_entries: int) -> int:
@@ -207,7 +271,7 @@ def hca_attn_workspace_size(B: int, Sq: int, H: int, D: int, max_entries: int) -
 
 def hca_attn(q, q_format: int, kv_comp: lca_tensor, N: int, m: int, kv_raw: lca_tensor, raw_start_pos: int, S_raw: int,
              sink, B: int, Sq: int, H: int, D: int, window: int, scale: float, q_start_pos: int, out, out_format: int,
-             lse_out, ws, ws_bytes: int, stream=None):
+             lse_out, ws, ws_bytes: int, stream=None, ragged: lca_ragged | None = None):
     _check("hca_attn", _lib.hca_attn(_ptr(q), q_format, kv_comp, N, m, kv_raw, raw_start_pos, S_raw, _ptr(sink), B, Sq,
                                      H, D, window, scale, q_start_pos, _ptr(out), out_format, _ptr(lse_out), _ptr(ws),
-                                     ws_bytes, _stream(stream)))
+                                     ws_bytes, _rg(ragged), _stream(stream)))

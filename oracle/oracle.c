@@ -164,7 +164,21 @@ typedef struct {
   const void* data;
   const void* rope_data;
   const void* scale;
+  /* A paged cache ([P1] question 5: the compressed cache is managed in fixed-size blocks): when table != NULL, entry
+   * i of sequence b is row table[b * (cap / block_rows) + i / block_rows] * block_rows + i % block_rows of the
+   * arrays above (a pool of blocks); otherwise it is row b * cap + i. */
+  const int* table;
+  int block_rows;
 } orc_cache;
+
+/* Storage row of entry i of sequence b (see orc_cache).
+ * pinned by: a cache whose blocks are permuted through its table gives the same scores and outputs as the dense
+ * cache. */
+static long long cache_row(const orc_cache* c, int b, long long i) {
+  if (!c->table) return (long long)b * c->cap + i;
+  const long long nblk = c->cap / c->block_rows;
+  return (long long)c->table[(long long)b * nblk + i / c->block_rows] * c->block_rows + i % c->block_rows;
+}
 
 /* Encode fp32 rows into a cache format (the quantise-on-write of the mixed-precision cache).
  * The fp8 per-row scale is s = fl32(amax / 448) over the row's non-RoPE dims (s = 1 if amax = 0);
@@ -338,6 +352,44 @@ void orc_kv_compress(const float* Ca, const float* Cb, const float* Za, const fl
   }
 }
 
+/* Epilogues on compressed entries ([P2] section 2.3: the Compressor holds an RMSNorm over the entry's head_dim; the
+ * Indexer excerpt applies rotary position embedding to the trailing rd channels).  Plain definitions, in double.
+ *
+ * RMS normalisation of each row: y[j] = x[j] / sqrt(mean_j(x[j]^2) + eps) * g[j].
+ * pinned by: a hand-computed row; invariance to scaling x (eps = 0); mean(y^2) = 1 for g = 1, eps = 0. */
+void orc_rmsnorm_rows(const double* x, long long rows, int c, const float* g, double eps, double* y) {
+#pragma omp parallel for schedule(static)
+  for (long long r = 0; r < rows; ++r) {
+    const double* xr = x + r * c;
+    double ss = 0.0;
+    for (int j = 0; j < c; ++j) ss += xr[j] * xr[j];
+    const double inv = 1.0 / sqrt(ss / c + eps);
+    for (int j = 0; j < c; ++j) y[r * c + j] = xr[j] * inv * (double)g[j];
+  }
+}
+
+/* Rotary position embedding of the trailing rd channels of each row (rd even): channel pair (2j, 2j+1) of that
+ * segment is rotated by the angle pos[r] * base^(-2j/rd):
+ *   (a, b) -> (a cos - b sin, a sin + b cos).
+ * The leading c - rd channels are copied.
+ * pinned by: position 0 is the identity; pair norms are preserved; hand-computed angles; composition of positions;
+ * dot products of two rotated rows depend only on the difference of their positions. */
+void orc_rope_rows(const double* x, long long rows, int c, int rd, const double* pos, double base, double* y) {
+#pragma omp parallel for schedule(static)
+  for (long long r = 0; r < rows; ++r) {
+    const double* xr = x + r * c;
+    double* yr = y + r * c;
+    for (int j = 0; j < c - rd; ++j) yr[j] = xr[j];
+    for (int j = 0; j < rd / 2; ++j) {
+      const double ang = pos[r] * pow(base, -2.0 * j / rd);
+      const double cs = cos(ang), sn = sin(ang);
+      const double a = xr[c - rd + 2 * j], b = xr[c - rd + 2 * j + 1];
+      yr[c - rd + 2 * j] = a * cs - b * sn;
+      yr[c - rd + 2 * j + 1] = a * sn + b * cs;
+    }
+  }
+}
+
 /* ------------------------------------------------------------------------------------------------ */
 /* Stage 2: Lightning Indexer score ([P2] sec. 2.3 Eq. 16 and Indexer excerpt; [P4] sec. 3; [P5]      */
 /* sec. 2) and exact top-k.                                                                          */
@@ -357,7 +409,8 @@ void orc_kv_compress(const float* Ca, const float* Cb, const float* Za, const fl
  * not certified exact; exact_out (optional, [B][nrows][N]) holds 1 for a certified pair, else 0.
  * abs_out (optional) receives sum_h |w[t,h]| * sum_d |q[t,h,d] * K[i,d]|, the scale of the fp32
  * rounding error of any summation order (used to certify near-ties).
- * Rows evaluated: rows[0..nrows) (offsets into [0, Sq)); outputs are [B][nrows][N].
+ * Rows evaluated: rows[0..nrows) (offsets into [0, Sq)); outputs are [B][nrows][N].  seq_pos (nullable, [B]) puts
+ * the rows of sequence b at seq_pos[b] + row instead (a ragged batch).
  * pinned by: dyadic tiny inputs reproduce hand-derivable scores; brute force over tiny inputs; the
  * certificate accepts small-spread fp4 rows and rejects a constructed wide-spread row whose fp32 sum
  * rounds.
@@ -388,8 +441,8 @@ int orc_dot_is_fp32_exact(const double* q, const double* k, int n) {
 }
 
 void orc_indexer_scores(const orc_cache* q, const float* w, const orc_cache* K, int B, int Sq, int HI, int DI, int N,
-                        int m, long long q_start_pos, const int* rows, int nrows, double* s64, float* s32,
-                        double* abs_out, long long* inexact, unsigned char* exact_out) {
+                        int m, long long q_start_pos, const long long* seq_pos, const int* rows, int nrows,
+                        double* s64, float* s32, double* abs_out, long long* inexact, unsigned char* exact_out) {
   int P = 1;
   while (P < HI) P <<= 1;
   long long bad = 0;
@@ -397,7 +450,7 @@ void orc_indexer_scores(const orc_cache* q, const float* w, const orc_cache* K, 
   for (int b = 0; b < B; ++b) {
     for (int rr = 0; rr < nrows; ++rr) {
       int row = rows[rr];
-      long long t = q_start_pos + row;
+      long long t = (seq_pos ? seq_pos[b] : q_start_pos) + row;
       long long nvis = t / m;
       if (nvis > N) nvis = N;
       double* qd = (double*)malloc(sizeof(double) * (size_t)HI * DI);
@@ -414,7 +467,7 @@ void orc_indexer_scores(const orc_cache* q, const float* w, const orc_cache* K, 
           if (exact_out) exact_out[ob + i] = 1;
           continue;
         }
-        decode_row(K, (long long)b * K->cap + i, kd);
+        decode_row(K, cache_row(K, b, i), kd);
         double acc = 0.0, aacc = 0.0;
         int certified = 1;
         for (int h = 0; h < P; ++h) a[h] = 0.0f;
@@ -517,23 +570,28 @@ void orc_topk_rows(const double* s, long long nrows, int N, const int* nvis, int
  * Each entry is both key and value.  l_j = scale * q . kv_j.  The sink logit z_h joins the softmax
  * denominator only: M = max(z_h, max l), den = e^(z_h - M) + sum e^(l_j - M), o = sum e^(l_j - M) kv_j / den,
  * lse = M + log(den).  z_h = -inf disables the sink.  An empty set with no sink gives o = 0, lse = -inf.
+ * seq_pos (nullable, [B]) places the rows of sequence b at seq_pos[b] + row (a ragged batch); its raw rows then
+ * start at position raw_start + seq_pos[b] - q_start_pos.
  * Returns 0, or -1 if a window position falls outside the raw span given.
  * pinned by: m = 1 collapse to causal attention (library routine), the sink closed form
  * o(z) = o(-inf) * S / (S + e^z), invariance to permuting idx, own block invisible.
  */
 int orc_attn(const orc_cache* q, const orc_cache* comp, int N, const orc_cache* raw, long long raw_start, int S_raw,
              const int* idx, int k, int hca_m, const float* sink, int B, int Sq, int H, int D, int window,
-             double scale, long long q_start_pos, const int* rows, int nrows, double* out, double* lse) {
+             double scale, long long q_start_pos, const long long* seq_pos, const int* rows, int nrows, double* out,
+             double* lse) {
   int err = 0;
 #pragma omp parallel for collapse(2) schedule(dynamic, 1) reduction(| : err)
   for (int b = 0; b < B; ++b) {
     for (int rr = 0; rr < nrows; ++rr) {
       int row = rows[rr];
-      long long t = q_start_pos + row;
+      const long long pos_b = seq_pos ? seq_pos[b] : q_start_pos;
+      const long long rs = raw_start + (pos_b - q_start_pos); /* sequence b's raw rows keep the same offset */
+      long long t = pos_b + row;
       long long w0 = t - window + 1;
       if (w0 < 0) w0 = 0;
       long long nw = (window > 0) ? (t - w0 + 1) : 0;
-      if (nw > 0 && (w0 < raw_start || t >= raw_start + S_raw)) {
+      if (nw > 0 && (w0 < rs || t >= rs + S_raw)) {
         err |= 1;
         continue;
       }
@@ -549,7 +607,7 @@ int orc_attn(const orc_cache* q, const orc_cache* comp, int N, const orc_cache* 
       char* use = (char*)malloc((size_t)(tot > 0 ? tot : 1));
       long long cnt = 0;
       for (long long p = w0; p < w0 + nw; ++p) {
-        decode_row(raw, (long long)b * raw->cap + (p - raw_start), kv + (size_t)cnt * D);
+        decode_row(raw, cache_row(raw, b, p - rs), kv + (size_t)cnt * D);
         use[cnt++] = 1;
       }
       for (long long j = 0; j < nc; ++j) {
@@ -558,7 +616,7 @@ int orc_attn(const orc_cache* q, const orc_cache* comp, int N, const orc_cache* 
           use[cnt++] = 0;
           continue;
         }
-        decode_row(comp, (long long)b * comp->cap + e, kv + (size_t)cnt * D);
+        decode_row(comp, cache_row(comp, b, e), kv + (size_t)cnt * D);
         use[cnt++] = 1;
       }
       double* qd = (double*)malloc(sizeof(double) * (size_t)D);

@@ -48,7 +48,8 @@ def lib():
 
 class _Cache(ctypes.Structure):
     _fields_ = [("fmt", ctypes.c_int), ("dim", ctypes.c_int), ("rope", ctypes.c_int), ("cap", ctypes.c_longlong),
-                ("data", ctypes.c_void_p), ("rope_data", ctypes.c_void_p), ("scale", ctypes.c_void_p)]
+                ("data", ctypes.c_void_p), ("rope_data", ctypes.c_void_p), ("scale", ctypes.c_void_p),
+                ("table", ctypes.c_void_p), ("block_rows", ctypes.c_int)]
 
 
 _P = ctypes.c_void_p
@@ -74,13 +75,15 @@ def _setup(L):
     L.orc_kv_compress.argtypes = [_P] * 8 + [ctypes.c_int, ctypes.c_longlong, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                              ctypes.c_longlong, _P]
     L.orc_indexer_scores.argtypes = [ctypes.POINTER(_Cache), _P, ctypes.POINTER(_Cache)] + [ctypes.c_int] * 6 + [
-        ctypes.c_longlong, _P, ctypes.c_int, _P, _P, _P, _P, _P]
+        ctypes.c_longlong, _P, _P, ctypes.c_int, _P, _P, _P, _P, _P]
+    L.orc_rmsnorm_rows.argtypes = [_P, ctypes.c_longlong, ctypes.c_int, _P, ctypes.c_double, _P]
+    L.orc_rope_rows.argtypes = [_P, ctypes.c_longlong, ctypes.c_int, ctypes.c_int, _P, ctypes.c_double, _P]
     L.orc_dot_is_fp32_exact.argtypes = [_P, _P, ctypes.c_int]
     L.orc_dot_is_fp32_exact.restype = ctypes.c_int
     L.orc_topk_rows.argtypes = [_P, ctypes.c_longlong, ctypes.c_int, _P, ctypes.c_int, _P, _P, _P]
     L.orc_attn.argtypes = [ctypes.POINTER(_Cache), ctypes.POINTER(_Cache), ctypes.c_int, ctypes.POINTER(_Cache),
                            ctypes.c_longlong, ctypes.c_int, _P, ctypes.c_int, ctypes.c_int, _P] + [ctypes.c_int] * 5 + [
-                               ctypes.c_double, ctypes.c_longlong, _P, ctypes.c_int, _P, _P]
+                               ctypes.c_double, ctypes.c_longlong, _P, _P, ctypes.c_int, _P, _P]
     L.orc_attn.restype = ctypes.c_int
 
 
@@ -162,8 +165,29 @@ def encode_rotated(x: np.ndarray, fmt: str, cap: int | None = None) -> dict:
 
 
 def _cstruct(c: dict) -> _Cache:
+    table = c.get("table")
+    if table is not None:
+        assert table.dtype == np.int32 and c["cap"] % c["block_rows"] == 0
     return _Cache(FMT[c["fmt"]], int(c["dim"]), int(c["rope"]), int(c["cap"]), _ptr(c["data"]), _ptr(c["rope_data"]),
-                  _ptr(c["scale"]))
+                  _ptr(c["scale"]), _ptr(table), int(c.get("block_rows", 0)))
+
+
+def paged(c: dict, B: int, block_rows: int, perm: np.ndarray) -> dict:
+    """The same cache stored as a pool of blocks: dense block j (of sequence b, j = b * nblk + jj) moves to pool block
+    perm[j]; the table maps (b, jj) to perm[b * nblk + jj].  Only moves bytes."""
+    cap = int(c["cap"])
+    assert cap % block_rows == 0
+    nblk = cap // block_rows
+    assert len(perm) == B * nblk
+    out = dict(c, table=np.ascontiguousarray(perm.astype(np.int32)), block_rows=block_rows)
+    inv = np.argsort(perm)
+    for key in ("data", "rope_data", "scale"):
+        a = c[key]
+        if a is None:
+            continue
+        blocks = a.reshape(B * nblk, block_rows, *a.shape[1:])
+        out[key] = np.ascontiguousarray(blocks[inv].reshape(a.shape))
+    return out
 
 
 def decode(c: dict, row0: int = 0, rows: int | None = None) -> np.ndarray:
@@ -211,6 +235,41 @@ def kv_compress(Ca, Cb, Za, Zb, Ba, Bb, tail_Cb=None, tail_Zb=None, m=4, overlap
     return out
 
 
+def rmsnorm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
+    """Rows x[..., c] RMS-normalised with gains g[c] (oracle.c, double)."""
+    x = np.ascontiguousarray(x, np.float64)
+    c = x.shape[-1]
+    g = np.ascontiguousarray(g, np.float32)
+    assert g.shape == (c,)
+    y = np.empty_like(x)
+    lib().orc_rmsnorm_rows(_ptr(x), x.size // c, c, _ptr(g), float(eps), _ptr(y))
+    return y
+
+
+def rope(x: np.ndarray, pos: np.ndarray, rd: int, base: float) -> np.ndarray:
+    """Rotary embedding of the trailing rd channels of rows x[..., c] at positions pos[...] (oracle.c, double)."""
+    x = np.ascontiguousarray(x, np.float64)
+    c = x.shape[-1]
+    p = np.ascontiguousarray(np.broadcast_to(pos, x.shape[:-1]), np.float64)
+    y = np.empty_like(x)
+    lib().orc_rope_rows(_ptr(x), x.size // c, c, int(rd), _ptr(p), float(base), _ptr(y))
+    return y
+
+
+def compress_epilogue(E: np.ndarray, m: int, start_pos: int, norm_g=None, eps: float = 0.0, rope_dims: int = 0,
+                      rope_base: float = 10000.0) -> np.ndarray:
+    """The epilogues of the compressed entries E [B, n_entries, c] written from token start_pos on: RMSNorm (gains
+    norm_g), then RoPE of the trailing rope_dims channels at each entry's position, the first token of its block
+    (m * (start_pos / m + i))."""
+    y = np.asarray(E, np.float64)
+    if norm_g is not None:
+        y = rmsnorm(y, norm_g, eps)
+    if rope_dims:
+        pos = (m * (start_pos // m + np.arange(y.shape[1], dtype=np.float64)))[None, :]
+        y = rope(y, np.broadcast_to(pos, y.shape[:-1]), rope_dims, rope_base)
+    return y
+
+
 def compress_to_cache(entries64: np.ndarray, fmt: str, rope: int = 0) -> dict:
     """Entries are computed in fp32 by the layer: round the double entries to fp32, then encode."""
     return encode(entries64.astype(np.float32), fmt, rope)
@@ -221,7 +280,7 @@ def compress_to_cache(entries64: np.ndarray, fmt: str, rope: int = 0) -> dict:
 # ----------------------------------------------------------------------------------------------------
 def indexer_scores(qI: dict, w: np.ndarray, kI: dict, B: int, Sq: int, HI: int, DI: int, N: int, m: int,
                    q_start_pos: int, rows=None, canonical: bool = False, want_abs: bool = False,
-                   want_exact: bool = False):
+                   want_exact: bool = False, seq_pos=None):
     """Returns (s64 [B, nrows, N], s32 or None, abs or None, inexact_count), plus the per-pair exactness
     certificate [B, nrows, N] (uint8, 1 = every head dot is exact in fp32) as a fifth item when want_exact.
     inexact_count is the number of visible (row, entry) pairs without the certificate."""
@@ -234,7 +293,9 @@ def indexer_scores(qI: dict, w: np.ndarray, kI: dict, B: int, Sq: int, HI: int, 
     ex = np.empty((B, nr, N), np.uint8) if want_exact else None
     bad = ctypes.c_longlong(0)
     q_s, k_s = _cstruct(qI), _cstruct(kI)
-    lib().orc_indexer_scores(ctypes.byref(q_s), _ptr(w), ctypes.byref(k_s), B, Sq, HI, DI, N, m, q_start_pos,
+    sp = None if seq_pos is None else np.ascontiguousarray(seq_pos, np.int64)
+    assert sp is None or sp.shape == (B,)
+    lib().orc_indexer_scores(ctypes.byref(q_s), _ptr(w), ctypes.byref(k_s), B, Sq, HI, DI, N, m, q_start_pos, _ptr(sp),
                              _ptr(rows), nr, _ptr(s64), _ptr(s32), _ptr(ab), ctypes.byref(bad), _ptr(ex))
     if want_exact:
         return s64, s32, ab, int(bad.value), ex
@@ -271,7 +332,7 @@ def nvis_rows(B: int, rows, q_start_pos: int, m: int, N: int) -> np.ndarray:
 # stages 3/4: attention
 # ----------------------------------------------------------------------------------------------------
 def attn(q: dict, comp: dict, N: int, raw: dict, raw_start: int, S_raw: int, idx, k: int, hca_m: int, sink,
-         B: int, Sq: int, H: int, D: int, window: int, scale: float, q_start_pos: int, rows=None):
+         B: int, Sq: int, H: int, D: int, window: int, scale: float, q_start_pos: int, rows=None, seq_pos=None):
     """Returns (o [B, nrows, H, D] float64, lse [B, nrows, H] float64)."""
     rows = np.arange(Sq, dtype=np.int32) if rows is None else np.ascontiguousarray(rows, np.int32)
     nr = len(rows)
@@ -279,11 +340,13 @@ def attn(q: dict, comp: dict, N: int, raw: dict, raw_start: int, S_raw: int, idx
     lse = np.empty((B, nr, H), np.float64)
     sink = np.ascontiguousarray(sink, np.float32)
     idx_a = None if idx is None else np.ascontiguousarray(idx, np.int32)
-    if hca_m == 0 and (idx_a is None or idx_a.size != B * Sq * k):
+    if hca_m == 0 and k > 0 and (idx_a is None or idx_a.size != B * Sq * k):
         raise ValueError("idx must hold [B, Sq, k] entries (row r of the call reads idx[b, r])")
     q_s, c_s, r_s = _cstruct(q), _cstruct(comp), _cstruct(raw)
+    sp = None if seq_pos is None else np.ascontiguousarray(seq_pos, np.int64)
+    assert sp is None or sp.shape == (B,)
     rc = lib().orc_attn(ctypes.byref(q_s), ctypes.byref(c_s), N, ctypes.byref(r_s), raw_start, S_raw, _ptr(idx_a),
-                        k, hca_m, _ptr(sink), B, Sq, H, D, window, float(scale), q_start_pos, _ptr(rows), nr,
+                        k, hca_m, _ptr(sink), B, Sq, H, D, window, float(scale), q_start_pos, _ptr(sp), _ptr(rows), nr,
                         _ptr(out), _ptr(lse))
     if rc != 0:
         raise ValueError("window positions fall outside the raw KV span")

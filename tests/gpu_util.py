@@ -108,3 +108,133 @@ def check_topk(gpu_idx: np.ndarray, gpu_sc: np.ndarray, s64: np.ndarray, absb: n
             assert np.all(np.abs(gpu_sc[r, :ke] - s64[r, sel]) <= gamma * absb[r, sel] + 1e-30), "score off"
         assert np.all(np.isneginf(gpu_sc[r, ke:]))
     return stats
+
+
+# ----------------------------------------------------------------------------------------------------------------
+# quantised outputs: the GPU encodes fp32 values computed in a different order than the oracle's double values, so a
+# code may differ from the oracle's where the value is next to a rounding boundary.  A GPU code is accepted iff it is
+# the round-to-nearest result of some value within `tol` of the oracle's value x: |decode(code) - x| <= tol + half
+# the grid spacing at the code.  For a value of ordinary size that is the oracle's code, or the neighbouring one when
+# x lies within tol of the midpoint between them; tol = tol_rel * max|row| is the fp32 error of the GPU's entry
+# (softmax sums, normalisation and rotation in fp32, a few hundred ulps at most).
+# ----------------------------------------------------------------------------------------------------------------
+def _half_step(v: np.ndarray, mant_bits: int, min_normal_exp: int) -> np.ndarray:
+    """Half the spacing of a binary float grid with mant_bits stored mantissa bits at value v (the larger of the two
+    spacings around a power of two)."""
+    a = np.abs(v)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, min_normal_exp)
+    return np.ldexp(1.0, (e - mant_bits - 1).astype(int))
+
+
+def check_bf16_codes(got: np.ndarray, x64: np.ndarray, tol_rel: float = 2.0 ** -16) -> int:
+    """got: bf16 bits [rows, c]; x64: oracle values [rows, c].  Returns the number of codes that differ from the
+    oracle's own encoding (all of them checked by the rule above)."""
+    from oracle import oracle as orc
+    got = got.reshape(x64.shape).astype(np.uint16)
+    ref = orc.encode(x64.astype(np.float32), "bf16")["data"].reshape(x64.shape)
+    bad = got != ref
+    n = int(bad.sum())
+    if n:
+        rows, _ = np.nonzero(bad)
+        gv = bf16_to_f64(got[bad])
+        tol = tol_rel * np.abs(x64).max(axis=1)[rows]
+        err = np.abs(gv - x64[bad])
+        ok = err <= tol + _half_step(gv, 7, -126)
+        assert np.all(ok), "bf16 code not a rounding of a value within tol: err %g at |x| %g" % (
+            err[~ok][0], np.abs(x64[bad])[~ok][0])
+    return n
+
+
+def _fp8_value(codes: np.ndarray) -> np.ndarray:
+    from oracle import oracle as orc
+    table = np.array([orc.fp8_decode1(c) for c in range(256)])
+    return table[codes.astype(np.int64)]
+
+
+def check_mixed_codes(got: dict, x64: np.ndarray, rope: int, tol_rel: float = 2.0 ** -16) -> int:
+    """got: host dict of a mixed cache restricted to the compared rows (data [rows, c - rope] fp8 codes, rope_data
+    [rows, rope] bf16, scale [rows]); x64: oracle values [rows, c].  The scale must be fl32(amax / 448) of an amax
+    within tol of the oracle's; the RoPE channels follow the bf16 rule; every fp8 code must be a rounding of a value
+    within tol / s of x / s, s the GPU's own scale.  Returns the number of codes that differ from the oracle's
+    encoding with that scale."""
+    rows, c = x64.shape
+    dm = c - rope
+    data = got["data"].reshape(rows, dm)
+    s_g = got["scale"].reshape(rows).astype(np.float64)
+    tol = tol_rel * np.abs(x64).max(axis=1)
+    amax = np.abs(x64[:, :dm]).max(axis=1)
+    assert np.all(np.abs(s_g * 448.0 - amax) <= tol + 2.0 ** -22 * amax), "fp8 scale away from the oracle's amax/448"
+    n = check_bf16_codes(got["rope_data"].reshape(rows, rope), x64[:, dm:], tol_rel) if rope else 0
+    y = x64[:, :dm] / s_g[:, None]  # the GPU's own scale
+    ref = _fp8_ref(y)
+    bad = data != ref
+    nb = int(bad.sum())
+    if nb:
+        r_i, _ = np.nonzero(bad)
+        gv = _fp8_value(data[bad])
+        yc = np.clip(y[bad], -448.0, 448.0)
+        err = np.abs(gv - yc)
+        ok = err <= tol[r_i] / s_g[r_i] + _half_step(gv, 3, -6)
+        assert np.all(ok), "fp8 code not a rounding of a value within tol"
+    return n + nb
+
+
+def _fp8_ref(y: np.ndarray) -> np.ndarray:
+    """The oracle's e4m3 codes of y (already divided by the scale), through its row encoder with scale 1: each row
+    is padded with one 448 channel, so that its amax is 448 and s = 448 / 448 = 1 exactly."""
+    from oracle import oracle as orc
+    rows, dm = y.shape
+    yc = np.clip(y, -448.0, 448.0).astype(np.float32)
+    pad = np.concatenate([yc, np.full((rows, 1), 448.0, np.float32)], axis=1)
+    enc = orc.encode(np.concatenate([pad, np.zeros((rows, 1), np.float32)], axis=1), "mixed", 1)
+    assert np.all(enc["scale"] == 1.0)
+    return enc["data"].reshape(rows, dm + 1)[:, :dm]
+
+
+_E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+_E2M1_HALF = np.array([0.25, 0.25, 0.25, 0.25, 0.5, 0.5, 1.0, 1.0])  # half the larger neighbouring spacing
+
+
+def check_fp4_codes(got: dict, x64: np.ndarray, tol_rel: float = 2.0 ** -16) -> int:
+    """got: host dict of an fp4 cache restricted to the compared rows (data [rows, c/2], scale [rows, c/16]); x64:
+    oracle values [rows, c].  A group scale must equal the oracle's unless the group's amax lies within tol of the
+    boundary 6 * 2^e between them; every code must be a rounding (saturating at 6) of a value within tol * 2^-e of
+    x * 2^-e, e the GPU's own group exponent.  Returns the number of codes that differ from the oracle's encoding
+    with that exponent."""
+    from oracle import oracle as orc
+    rows, c = x64.shape
+    tol = tol_rel * np.abs(x64).max(axis=1)
+    e_g = got["scale"].reshape(rows, c // 16).astype(np.int64) - 127
+    ref = orc.encode(x64.astype(np.float32), "fp4")
+    e_o = ref["scale"].reshape(rows, c // 16).astype(np.int64) - 127
+    if np.any(e_g != e_o):
+        r_i, g_i = np.nonzero(e_g != e_o)
+        amax = np.abs(x64.reshape(rows, c // 16, 16)).max(axis=2)[r_i, g_i]
+        assert np.all(np.abs(e_g - e_o)[r_i, g_i] == 1), "fp4 group scales more than one exponent apart"
+        bound = 6.0 * 2.0 ** np.minimum(e_g, e_o)[r_i, g_i]
+        assert np.all(np.abs(amax - bound) <= tol[r_i]), "an fp4 group scale away from a scale boundary"
+    packed = got["data"].reshape(rows, c // 2)
+    codes = np.stack([packed & 0xF, packed >> 4], axis=-1).reshape(rows, c).astype(np.int64)
+    y = x64 * 2.0 ** -np.repeat(e_g, 16, axis=1)
+    want = _fp4_ref(y)
+    bad = codes != want
+    n = int(bad.sum())
+    if n:
+        r_i, c_i = np.nonzero(bad)
+        mag = codes[bad] & 7
+        gv = np.where(codes[bad] & 8, -1.0, 1.0) * _E2M1[mag]
+        yc = np.clip(y[bad], -6.0, 6.0)
+        scl = 2.0 ** -e_g[r_i, c_i // 16]
+        ok = np.abs(gv - yc) <= tol[r_i] * scl + _E2M1_HALF[mag]
+        assert np.all(ok), "fp4 code not a rounding of a value within tol"
+    return n
+
+
+def _fp4_ref(y: np.ndarray) -> np.ndarray:
+    """The oracle's e2m1 codes of y (already scaled), by its nearest-even encoder on each distinct value."""
+    from oracle import oracle as orc
+    flat = np.clip(y.reshape(-1), -6.0, 6.0)
+    uniq, inv = np.unique(flat, return_inverse=True)
+    codes = np.array([orc.fp4_encode1(v) for v in uniq], np.int64)
+    return codes[inv].reshape(y.shape)

@@ -9,7 +9,8 @@ import torch
 
 import lca_inputs as gen
 from oracle import oracle as orc
-from tests.gpu_util import bf16_to_f64, check_topk, row_rel_err
+from tests.gpu_util import (bf16_to_f64, check_bf16_codes, check_fp4_codes, check_mixed_codes, check_topk,
+                            row_rel_err)
 
 pytestmark = pytest.mark.gpu
 
@@ -34,10 +35,6 @@ def _decoded_entries(cache: lca.CacheTensor, B, rows: slice):
     h = cache.host()
     d = h["data"].reshape(B, cache.cap, -1)[:, rows]
     return bf16_to_f64(d)
-
-
-def _attn_rows_match(gidx, oidx):
-    return [r for r in range(gidx.shape[0]) if np.array_equal(gidx[r], oidx[r])]
 
 
 # ------------------------------------------------------------------------------------------------------
@@ -74,27 +71,24 @@ def test_tiny_csa_prefill_f32_full_chain():
     # stage 1: both caches within 1e-4
     assert row_rel_err(comp.data.cpu().numpy().reshape(1, N, w.D), main_e) <= 1e-4
     assert row_rel_err(keys.data.cpu().numpy().reshape(1, N, w.DI), key_e) <= 1e-4
-    # stage 2: the oracle scores its own keys; keys differ from the GPU's by fp32 rounding of the compression, which
-    # the certified bound covers (a few ulps per key element)
-    kc = orc.plain_cache(main_e.astype(np.float32), "f32")
-    kk = orc.plain_cache(key_e.astype(np.float32), "f32")
-    kc["cap"] = kk["cap"] = N
+    # stage 2, stage-isolated: the oracle scores the key bytes the GPU wrote, with the plain fp32 rounding bound
+    kk = dict(orc.plain_cache(keys.data.cpu().numpy().reshape(1, N, w.DI), "f32"), cap=N)
     s64, _, ab, _ = orc.indexer_scores(orc.plain_cache(inp["qI"], "f32"), inp["w"], kk, 1, w.Sq, w.HI, w.DI, N, 4, 0,
                                        want_abs=True)
     nv = orc.nvis_rows(1, np.arange(w.Sq), 0, 4, N)
     gidx = idx.cpu().numpy().reshape(w.Sq, w.k)
     st = check_topk(gidx, sc.cpu().numpy().reshape(w.Sq, w.k), s64.reshape(w.Sq, N), ab.reshape(w.Sq, N), nv, w.k,
-                    4 * GAMMA(w.DI, w.HI))
-    assert st["exact_rows"] >= 0.97 * w.Sq
-    # stage 3: oracle attention with the oracle's selection, compared on rows whose selection matches
-    oidx, _, _ = orc.topk(s64.reshape(w.Sq, N), nv, w.k)
+                    GAMMA(w.DI, w.HI))
+    print("tiny chain: %d of %d rows exact, %d certified near-ties" % (st["exact_rows"], w.Sq, st["near_tie_rows"]))
+    assert st["near_tie_rows"] <= 3
+    # stage 3, stage-isolated: the oracle attends the GPU's selection over the latent entries the GPU wrote: every row
+    kc = dict(orc.plain_cache(comp.data.cpu().numpy().reshape(1, N, w.D), "f32"), cap=N)
     o_ref, l_ref = orc.attn(orc.plain_cache(inp["q"], "f32"), kc, N, dict(orc.plain_cache(inp["raw_kv"], "f32"),
-                                                                         cap=w.Sq), 0, w.Sq, oidx.reshape(1, w.Sq, w.k),
+                                                                         cap=w.Sq), 0, w.Sq, gidx.reshape(1, w.Sq, w.k),
                             w.k, 0, inp["sink"], 1, w.Sq, w.H, w.D, w.window, w.scale, 0)
-    rows = _attn_rows_match(gidx, oidx)
     o = out.cpu().numpy()[0]
-    assert row_rel_err(o[rows], o_ref[0, rows]) <= 1e-4
-    np.testing.assert_allclose(lse.cpu().numpy()[0, rows], l_ref[0, rows], rtol=1e-5, atol=1e-5)
+    assert row_rel_err(o, o_ref[0]) <= 1e-4
+    np.testing.assert_allclose(lse.cpu().numpy()[0], l_ref[0], rtol=1e-5, atol=1e-5)
 
 
 # ------------------------------------------------------------------------------------------------------
@@ -102,16 +96,18 @@ def _check_decode(w, inp, step):
     B, N, Sq = w.B, w.N, w.Sq
     R = B * Sq  # query rows
     torch.cuda.synchronize()
-    # appended entries (block N, provisional): latent and indexer key
+    # appended entries (block N, provisional): latent and indexer key, code by code
     for tag, cache, c, fmt in (("", step.comp[0], w.D, w.main_fmt), ("_I", step.keys[0], w.DI, w.key_fmt)):
-        E = _compress_ref(inp, tag, 4, True, w.n_ctx)[:, :1]
+        E = _compress_ref(inp, tag, 4, True, w.n_ctx)[:, 0]  # [B, c]
+        h = cache.host()
+        row = lambda a: a.reshape(B, cache.cap, *a.shape[1:])[:, N]  # noqa: E731
         if fmt == "bf16":
-            assert row_rel_err(_decoded_entries(cache, B, slice(N, N + 1)), E) <= 1e-2
+            check_bf16_codes(row(h["data"]), E)
+        elif fmt == "mixed":
+            check_mixed_codes(dict(data=row(h["data"]), rope_data=row(h["rope_data"]), scale=row(h["scale"])), E,
+                              w.rope)
         else:
-            got = cache.host()
-            ref = orc.compress_to_cache(E, fmt, w.rope if tag == "" else 0)
-            gd = got["data"].reshape(B, cache.cap, -1)[:, N].view(np.uint8)
-            assert np.mean(gd.reshape(-1) == ref["data"].view(np.uint8).reshape(-1)) > 0.98
+            check_fp4_codes(dict(data=row(h["data"]), scale=row(h["scale"])), E)
     # indexer: oracle scores over the same key bytes
     exact = w.key_fmt == "fp4"
     if exact:
@@ -132,9 +128,7 @@ def _check_decode(w, inp, step):
     gidx = step.idx.cpu().numpy().reshape(R, w.k)
     st = check_topk(gidx, step.scores.cpu().numpy().reshape(R, w.k), s64.reshape(R, N), ab.reshape(R, N), nv, w.k,
                     GAMMA(w.DI, w.HI), exact=exact, s32=None if s32 is None else s32.reshape(R, N))
-    # attention with the oracle's own selection, on rows whose selection matches
-    ref_scores = s32.astype(np.float64) if exact else s64
-    oidx, _, _ = orc.topk(ref_scores.reshape(R, N), nv, w.k)
+    # attention, stage-isolated: the oracle attends the GPU's own selection, every row
     if w.main_fmt == "mixed":
         cc = orc.encode(inp["comp"].reshape(-1, w.D), "mixed", w.rope)
         rc = orc.encode(inp["window_kv"].reshape(-1, w.D), "mixed", w.rope)
@@ -147,14 +141,12 @@ def _check_decode(w, inp, step):
     S_raw = w.window + Sq - 1
     cc["cap"], rc["cap"] = N, S_raw
     qa = orc.plain_cache(_bf16(inp["q"]), "bf16")
-    rows = _attn_rows_match(gidx, oidx)
-    assert len(rows) >= R - 1
-    o_ref, l_ref = orc.attn(qa, cc, N, rc, w.n_ctx - w.window + 1, S_raw, oidx.reshape(B, Sq, w.k), w.k, 0,
+    o_ref, l_ref = orc.attn(qa, cc, N, rc, w.n_ctx - w.window + 1, S_raw, gidx.reshape(B, Sq, w.k), w.k, 0,
                             inp["sink"], B, Sq, w.H, w.D, w.window, w.scale, w.n_ctx)
     o = bf16_to_f64(step.out.cpu().numpy().view(np.uint16)).reshape(R, w.H, w.D)
-    assert row_rel_err(o[rows], o_ref.reshape(R, w.H, w.D)[rows]) <= 1e-2
-    np.testing.assert_allclose(step.lse.cpu().numpy().reshape(R, w.H)[rows], l_ref.reshape(R, w.H)[rows], rtol=1e-3,
-                               atol=1e-3)
+    assert row_rel_err(o, o_ref.reshape(R, w.H, w.D)) <= 1e-2
+    np.testing.assert_allclose(step.lse.cpu().numpy().reshape(R, w.H), l_ref.reshape(R, w.H), rtol=1e-4, atol=1e-4)
+    print("%s: %d of %d rows exact, %d certified near-ties" % (w.name, st["exact_rows"], R, st["near_tie_rows"]))
     return st
 
 
@@ -164,7 +156,7 @@ def test_csa_decode_128k_bf16_full():
     step = steps.CsaDecode(w, inp, copies=1)
     step.run()
     st = _check_decode(w, inp, step)
-    assert st["exact_rows"] >= w.B - 1
+    assert st["near_tie_rows"] <= 1
 
 
 def test_csa_decode_1m_mixed_full():
@@ -184,7 +176,7 @@ def test_csa_decode_128k_bf16_mtp2_full():
     step = steps.CsaDecode(w, inp, copies=1)
     step.run()
     st = _check_decode(w, inp, step)
-    assert st["exact_rows"] >= w.B * w.Sq - 1
+    assert st["near_tie_rows"] <= 1
 
 
 def test_csa_decode_1m_mixed_mtp2_full():
@@ -205,7 +197,7 @@ def test_hca_decode_1m_bf16_full():
     torch.cuda.synchronize()
     B, N = w.B, w.N
     E = orc.kv_compress(inp["Ca"], None, inp["Za"], None, inp["Ba"], None, m=w.m, overlap=False, start_pos=w.n_ctx)
-    assert row_rel_err(_decoded_entries(step.comp[0], B, slice(N, N + 1)), E) <= 1e-2
+    check_bf16_codes(step.comp[0].host()["data"].reshape(B, N + 1, w.D)[:, N], E[:, 0])
     cc = orc.plain_cache(_bf16(inp["comp"]), "bf16")
     rc = orc.plain_cache(_bf16(inp["window_kv"]), "bf16")
     cc["cap"], rc["cap"] = N, w.window
@@ -225,14 +217,15 @@ def test_hca_cache_build_1m_sampled():
     lca.kv_compress(C, None, Z, None, Bad, None, None, None, w.B, w.n_ctx, w.D, w.m, False, 0, out.desc())
     torch.cuda.synchronize()
     rng = np.random.default_rng(7)
-    picks = [(b, int(i)) for b in range(w.B) for i in rng.choice(w.N, 3, replace=False)] + [(0, 0), (w.B - 1, w.N - 1)]
+    picks = [(b, int(i)) for b in range(w.B) for i in rng.choice(w.N, 32, replace=False)] + [(0, 0), (w.B - 1, w.N - 1)]
     got = out.data.view(w.B, w.N, w.D)
-    for b, i in picks:
+    Es, gs = [], []
+    for b, i in picks:  # every sampled entry's 128 tokens copied back, compressed by the oracle, codes compared
         cs = C[b:b + 1, i * w.m:(i + 1) * w.m].cpu().numpy()
         zs = Z[b:b + 1, i * w.m:(i + 1) * w.m].cpu().numpy()
-        E = orc.kv_compress(cs, None, zs, None, Ba, None, m=w.m, overlap=False)
-        g = bf16_to_f64(got[b, i].cpu().numpy().view(np.uint16))
-        assert row_rel_err(g[None, None], E) <= 1e-2
+        Es.append(orc.kv_compress(cs, None, zs, None, Ba, None, m=w.m, overlap=False)[0, 0])
+        gs.append(got[b, i].cpu().numpy().view(np.uint16))
+    check_bf16_codes(np.stack(gs), np.stack(Es))
     # entry count: ceil(n / m)
     assert w.N == math.ceil(w.n_ctx / w.m) == 8192
     del C, Z
@@ -248,34 +241,33 @@ def test_csa_prefill_64k_chunk4k_bf16_sampled():
     step.run()
     torch.cuda.synchronize()
     N0, N = step.N0, step.N
-    # new entries of both caches (bf16): the codes are decisions on fp32 entries -> nearly all equal the oracle's
+    # new entries of both caches (bf16), code by code against the oracle's compression
     Em = _compress_ref(inp, "", 4, True, w.n_ctx)
     Ek = _compress_ref(inp, "_I", 4, True, w.n_ctx)
-    gm = _decoded_entries(step.comp, 1, slice(N0, N))
-    gk = _decoded_entries(step.keys, 1, slice(N0, N))
-    assert row_rel_err(gm, Em) <= 1e-2 and row_rel_err(gk, Ek) <= 1e-2
-    # the oracle's caches: given part + its own compressed chunk (bf16 of the fp32 entries)
-    main_bits = np.concatenate([_bf16(inp["comp"]), _bf16(Em.astype(np.float32))], axis=1)
-    key_bits = np.concatenate([_bf16(inp["keys"]), _bf16(Ek.astype(np.float32))], axis=1)
-    ck, cm = orc.plain_cache(key_bits, "bf16"), orc.plain_cache(main_bits, "bf16")
-    ck["cap"] = cm["cap"] = N
-    rows = np.array([0, 1, 3, 100, 1023, 2047, 2048, 3000, 4094, 4095], np.int32)
+    hm, hk = step.comp.host(), step.keys.host()
+    check_bf16_codes(hm["data"].reshape(N, w.D)[N0:N], Em[0])
+    check_bf16_codes(hk["data"].reshape(N, w.DI)[N0:N], Ek[0])
+    # stage-isolated: the oracle scores the GPU-written key cache (given part + the chunk the GPU compressed) with the
+    # plain fp32 rounding bound, on 64 rows spread over the chunk plus its first and last rows
+    ck = dict(orc.plain_cache(hk["data"].reshape(1, N, w.DI), "bf16"), cap=N)
+    cm = dict(orc.plain_cache(hm["data"].reshape(1, N, w.D), "bf16"), cap=N)
+    rows = np.unique(np.concatenate([np.linspace(0, w.Sq - 1, 64).astype(np.int32), [1, 3, 2047, 2048]])).astype(
+        np.int32)
     s64, _, ab, _ = orc.indexer_scores(orc.plain_cache(_bf16(inp["qI"]), "bf16"), inp["w"], ck, 1, w.Sq, w.HI, w.DI, N,
                                        4, w.n_ctx, rows=rows, want_abs=True)
     nv = orc.nvis_rows(1, rows, w.n_ctx, 4, N)
     gidx = step.idx.cpu().numpy()[0, rows]
-    # keys of the new chunk may differ from the oracle's by one bf16 rounding of an entry element: the bound adds
-    # 2^-8 relative per key element to the fp32 bound
     st = check_topk(gidx, step.scores.cpu().numpy()[0, rows], s64.reshape(len(rows), N), ab.reshape(len(rows), N), nv,
-                    w.k, GAMMA(w.DI, w.HI) + 2.0 ** -8)
-    oidx, _, _ = orc.topk(s64.reshape(len(rows), N), nv, w.k)
+                    w.k, GAMMA(w.DI, w.HI))
+    print("prefill: %d of %d rows exact, %d certified near-ties" % (st["exact_rows"], len(rows), st["near_tie_rows"]))
+    assert st["near_tie_rows"] <= 2
+    # attention over the GPU's own selection and latent cache, every sampled row
     raw = orc.plain_cache(_bf16(inp["raw_kv"]), "bf16")
     raw["cap"] = inp["raw_kv"].shape[1]
     full_idx = np.full((1, w.Sq, w.k), -1, np.int32)
-    full_idx[0, rows] = oidx
-    o_ref, _ = orc.attn(orc.plain_cache(_bf16(inp["q"]), "bf16"), cm, N, raw, inp["raw_start"], raw["cap"], full_idx,
-                        w.k, 0, inp["sink"], 1, w.Sq, w.H, w.D, w.window, w.scale, w.n_ctx, rows=rows)
-    match = _attn_rows_match(gidx, oidx)
-    assert len(match) >= len(rows) - 2
+    full_idx[0, rows] = gidx
+    o_ref, l_ref = orc.attn(orc.plain_cache(_bf16(inp["q"]), "bf16"), cm, N, raw, inp["raw_start"], raw["cap"],
+                            full_idx, w.k, 0, inp["sink"], 1, w.Sq, w.H, w.D, w.window, w.scale, w.n_ctx, rows=rows)
     o = bf16_to_f64(step.out.cpu().numpy()[0, rows].view(np.uint16))
-    assert row_rel_err(o[match], o_ref[0, match]) <= 1e-2
+    assert row_rel_err(o, o_ref[0]) <= 1e-2
+    np.testing.assert_allclose(step.lse.cpu().numpy()[0, rows], l_ref[0], rtol=1e-4, atol=1e-4)

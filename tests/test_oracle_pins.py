@@ -275,3 +275,181 @@ def test_certificate_on_fp4_rows():
     kc2["cap"] = N
     s64, _, _, bad, ex = orc.indexer_scores(qc2, w, kc2, B, Sq, HI, DI, N, m, 4 * N, canonical=True, want_exact=True)
     assert bad == 1 and not ex[0, 0, 5] and ex[0, 0, np.arange(N) != 5].all()
+
+
+# ---------------------------------------------------------------------------------------------------
+# ratio-0 layer: pure sliding-window attention with the sink (paper notes, section 2.4, the compress_ratios list
+# of the config excerpt ends in a ratio-0 layer)
+# ---------------------------------------------------------------------------------------------------
+def test_window_only_layer_is_banded_causal_attention():
+    """k = 0 and no compressed entries: the layer is causal attention over the last `window` raw tokens, checked
+    against torch's scaled_dot_product_attention with a banded causal mask in fp64; a sink adds e^z to the
+    denominator (closed form)."""
+    import torch
+    g = np.random.default_rng(47)
+    B, n, H, D, W = 2, 50, 3, 16, 7
+    kv = g.standard_normal((B, n, D)).astype(np.float32)
+    q = g.standard_normal((B, n, H, D)).astype(np.float32)
+    scale = 1.0 / math.sqrt(D)
+    empty = dict(orc.plain_cache(kv[:, :1], "f32"), cap=1)
+    rs = dict(orc.plain_cache(kv, "f32"), cap=n)
+
+    def run(sink):
+        return orc.attn(orc.plain_cache(q, "f32"), empty, 0, rs, 0, n, None, 0, 0, sink, B, n, H, D, W, scale, 0)
+
+    o, lse = run(np.full(H, -np.inf, np.float32))
+    t = np.arange(n)
+    band = (t[None, :] <= t[:, None]) & (t[None, :] > t[:, None] - W)
+    qt = torch.from_numpy(q.astype(np.float64)).permute(0, 2, 1, 3)
+    kt = torch.from_numpy(kv.astype(np.float64))[:, None].expand(B, H, n, D)
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, kt, attn_mask=torch.from_numpy(band),
+                                                           scale=scale).permute(0, 2, 1, 3).numpy()
+    np.testing.assert_allclose(o, ref, rtol=1e-10, atol=1e-12)
+    z = g.standard_normal(H).astype(np.float32)
+    o1, _ = run(z)
+    S = np.exp(lse)
+    np.testing.assert_allclose(o1, o * (S / (S + np.exp(z.astype(np.float64))))[..., None], rtol=1e-12)
+
+
+# ---------------------------------------------------------------------------------------------------
+# epilogues on compressed entries: RMSNorm and rotary position embedding (paper notes, section 2.3: the
+# Compressor's RMSNorm over the entry's head_dim; the Indexer excerpt's rotary embedding of the trailing rd dims)
+# ---------------------------------------------------------------------------------------------------
+def test_rmsnorm_closed_forms():
+    # hand case: x = (3, 4), mean square 12.5, gains (1, 2): y = (3, 8) / sqrt(12.5)
+    y = orc.rmsnorm(np.array([[3.0, 4.0]]), np.array([1.0, 2.0], np.float32), 0.0)
+    np.testing.assert_allclose(y, [[3 / math.sqrt(12.5), 8 / math.sqrt(12.5)]], rtol=1e-15)
+    # with eps: x = (1, 1, 1, 1), eps = 3: y = 1 / sqrt(1 + 3) = 0.5
+    np.testing.assert_allclose(orc.rmsnorm(np.ones((1, 4)), np.ones(4, np.float32), 3.0), 0.5, rtol=1e-15)
+    g = np.random.default_rng(48)
+    x = g.standard_normal((5, 64))
+    ones = np.ones(64, np.float32)
+    y = orc.rmsnorm(x, ones, 0.0)
+    np.testing.assert_allclose((y ** 2).mean(axis=1), 1.0, rtol=1e-13)
+    np.testing.assert_allclose(orc.rmsnorm(7.5 * x, ones, 0.0), y, rtol=1e-13)
+    gains = g.standard_normal(64).astype(np.float32)
+    np.testing.assert_allclose(orc.rmsnorm(x, gains, 0.0), y * gains, rtol=1e-13)
+
+
+def test_rope_closed_forms():
+    g = np.random.default_rng(49)
+    c, rd = 12, 8
+    x = g.standard_normal((6, c))
+    # position 0 is the identity; the leading c - rd channels are never touched
+    np.testing.assert_array_equal(orc.rope(x, np.zeros(6), rd, 10000.0), x)
+    y = orc.rope(x, np.arange(6) * 37.0, rd, 10000.0)
+    np.testing.assert_array_equal(y[:, :c - rd], x[:, :c - rd])
+    # pair norms preserved
+    pn = lambda v: np.hypot(v[:, c - rd::2], v[:, c - rd + 1::2])  # noqa: E731
+    np.testing.assert_allclose(pn(y), pn(x), rtol=1e-13)
+    # hand angles: pair 0 turns by p radians; with rd = 4, base 10000, pair 1 turns by p / 100
+    e = np.array([[1.0, 0.0, 1.0, 0.0]])
+    for p in (1.0, 2.5, 100.0):
+        r = orc.rope(e, np.array([p]), 4, 10000.0)
+        np.testing.assert_allclose(r, [[math.cos(p), math.sin(p), math.cos(p / 100), math.sin(p / 100)]], rtol=1e-13,
+                                   atol=1e-15)
+    # composition: rotating by p then by q equals rotating by p + q
+    p, q = 123.0, 4567.0
+    np.testing.assert_allclose(orc.rope(orc.rope(x, p, rd, 500.0), q, rd, 500.0), orc.rope(x, p + q, rd, 500.0),
+                               rtol=1e-9, atol=1e-12)
+    # relative positions: <R(p) a, R(q) b> depends only on p - q (over the rotated channels)
+    a, b = x[0], x[1]
+    d1 = orc.rope(a[None], 1000.0, rd, 10000.0)[0, c - rd:] @ orc.rope(b[None], 900.0, rd, 10000.0)[0, c - rd:]
+    d2 = orc.rope(a[None], 5100.0, rd, 10000.0)[0, c - rd:] @ orc.rope(b[None], 5000.0, rd, 10000.0)[0, c - rd:]
+    assert abs(d1 - d2) < 1e-9
+
+
+def test_compress_epilogue_positions():
+    """The epilogue composition: entry i written from start_pos takes the rotary position m * (start_pos / m + i),
+    the first token of its block; a constant entry normalises to the gains."""
+    g = np.random.default_rng(50)
+    B, n, c, m, rd = 2, 16, 8, 4, 4
+    E = g.standard_normal((B, n // m, c))
+    y = orc.compress_epilogue(E, m, 64, rope_dims=rd, rope_base=10.0)
+    for i in range(n // m):
+        np.testing.assert_allclose(y[:, i], orc.rope(E[:, i], float(m * (16 + i)), rd, 10.0), rtol=1e-15)
+    gains = g.standard_normal(c).astype(np.float32)
+    y = orc.compress_epilogue(np.full((1, 3, c), -2.5), m, 0, norm_g=gains, eps=0.0)
+    np.testing.assert_allclose(y, np.broadcast_to(-gains.astype(np.float64), (1, 3, c)), rtol=1e-15)
+
+
+# ---------------------------------------------------------------------------------------------------
+# block-managed (paged) caches and ragged batches (itsolotime page, question 5: the compressed cache is
+# managed in blocks of lcm(4, 128) = 128 tokens, i.e. 32 CSA entries or one HCA entry per block)
+# ---------------------------------------------------------------------------------------------------
+def test_paged_cache_equals_dense():
+    """Moving every block of a cache to a shuffled pool slot, with the table pointing at it, changes nothing: scores,
+    selections and attention outputs are bit-identical to the dense cache's (indexer keys and latent cache alike;
+    block sizes 32 and 1)."""
+    g = np.random.default_rng(51)
+    B, Sq, HI, DI, H, D, N, k, W, m = 3, 2, 4, 16, 3, 32, 128, 9, 6, 4
+    cap = 160
+    keys = g.standard_normal((B, cap, DI)).astype(np.float32)
+    comp = g.standard_normal((B, cap, D)).astype(np.float32)
+    raw = g.standard_normal((B, W + Sq, D)).astype(np.float32)
+    qI = g.standard_normal((B, Sq, HI, DI)).astype(np.float32)
+    w = g.standard_normal((B, Sq, HI)).astype(np.float32)
+    q = g.standard_normal((B, Sq, H, D)).astype(np.float32)
+    sink = g.standard_normal(H).astype(np.float32)
+    q0 = 4 * N
+    kd, cd = orc.encode(keys, "fp4", cap=cap), orc.encode(comp, "mixed", 8, cap=cap)
+    rc = dict(orc.encode(raw, "mixed", 8), cap=W + Sq)
+    qc = orc.encode(qI, "fp4")
+    for br in (32, 1):
+        perm_k = g.permutation(B * cap // br)
+        perm_c = g.permutation(B * cap // br)
+        kp, cp = orc.paged(kd, B, br, perm_k), orc.paged(cd, B, br, perm_c)
+        assert not np.array_equal(kp["data"], kd["data"])
+        s_d, s32_d, _, _ = orc.indexer_scores(qc, w, kd, B, Sq, HI, DI, N, m, q0, canonical=True)
+        s_p, s32_p, _, _ = orc.indexer_scores(qc, w, kp, B, Sq, HI, DI, N, m, q0, canonical=True)
+        np.testing.assert_array_equal(s_p, s_d)
+        np.testing.assert_array_equal(s32_p, s32_d)
+        idx, _, _ = orc.topk(s32_d.reshape(B * Sq, N).astype(np.float64),
+                             orc.nvis_rows(B, np.arange(Sq), q0, m, N), k)
+        args = (rc, q0 - W + 1, W + Sq, idx.reshape(B, Sq, k), k, 0, sink, B, Sq, H, D, W, 0.2, q0)
+        o_d, l_d = orc.attn(orc.plain_cache(q, "f32"), cd, N, *args)
+        o_p, l_p = orc.attn(orc.plain_cache(q, "f32"), cp, N, *args)
+        np.testing.assert_array_equal(o_p, o_d)
+        np.testing.assert_array_equal(l_p, l_d)
+        # dense HCA rows through a one-entry-per-block table
+        h_d, _ = orc.attn(orc.plain_cache(q, "f32"), cd, N, rc, q0 - W + 1, W + Sq, None, 0, m, sink, B, Sq, H, D, W,
+                          0.2, q0)
+        h_p, _ = orc.attn(orc.plain_cache(q, "f32"), cp, N, rc, q0 - W + 1, W + Sq, None, 0, m, sink, B, Sq, H, D, W,
+                          0.2, q0)
+        np.testing.assert_array_equal(h_p, h_d)
+
+
+def test_ragged_batch_equals_separate_calls():
+    """Sequences at their own positions (seq_pos) give, for each sequence, exactly the result of a call on that
+    sequence alone at its position; its raw rows keep the call's offset from the query position."""
+    g = np.random.default_rng(52)
+    B, Sq, HI, DI, H, D, N, k, W, m = 3, 2, 4, 16, 3, 32, 100, 7, 5, 4
+    pos = np.array([4 * 100, 4 * 37 + 2, 4 * 63 + 1], np.int64)
+    q0 = int(pos.max())
+    keys = g.standard_normal((B, N, DI)).astype(np.float32)
+    comp = g.standard_normal((B, N, D)).astype(np.float32)
+    S_raw = W + Sq - 1
+    raw = g.standard_normal((B, S_raw, D)).astype(np.float32)
+    qI = g.standard_normal((B, Sq, HI, DI)).astype(np.float32)
+    w = g.standard_normal((B, Sq, HI)).astype(np.float32)
+    q = g.standard_normal((B, Sq, H, D)).astype(np.float32)
+    sink = g.standard_normal(H).astype(np.float32)
+    kc, cc, rc = (dict(orc.plain_cache(x, "f32"), cap=x.shape[1]) for x in (keys, comp, raw))
+    s_r, _, _, _ = orc.indexer_scores(orc.plain_cache(qI, "f32"), w, kc, B, Sq, HI, DI, N, m, q0, seq_pos=pos)
+    nv = np.concatenate([orc.nvis_rows(1, np.arange(Sq), int(p), m, N) for p in pos])
+    idx, _, _ = orc.topk(s_r.reshape(B * Sq, N), nv, k)
+    idx = idx.reshape(B, Sq, k)
+    o_r, l_r = orc.attn(orc.plain_cache(q, "f32"), cc, N, rc, q0 - W + 1, S_raw, idx, k, 0, sink, B, Sq, H, D, W, 0.3,
+                        q0, seq_pos=pos)
+    for b in range(B):
+        one = lambda x: dict(orc.plain_cache(np.ascontiguousarray(x[b:b + 1]), "f32"), cap=x.shape[1])  # noqa: E731
+        s1, _, _, _ = orc.indexer_scores(orc.plain_cache(np.ascontiguousarray(qI[b:b + 1]), "f32"), w[b:b + 1],
+                                         one(keys), 1, Sq, HI, DI, N, m, int(pos[b]))
+        np.testing.assert_array_equal(s1[0], s_r[b])
+        o1, l1 = orc.attn(orc.plain_cache(np.ascontiguousarray(q[b:b + 1]), "f32"), one(comp), N, one(raw),
+                          int(pos[b]) - W + 1, S_raw, np.ascontiguousarray(idx[b:b + 1]), k, 0, sink, 1, Sq, H, D, W,
+                          0.3, int(pos[b]))
+        np.testing.assert_array_equal(o1[0], o_r[b])
+        np.testing.assert_array_equal(l1[0], l_r[b])
+    # the visible counts differ per sequence: floor((pos + r) / m)
+    assert len(set(nv.tolist())) == B * Sq - 1 or len(set(nv.tolist())) >= B
