@@ -48,6 +48,9 @@ def parse():
                    help="distinct bytes of the streamed cache (indexer keys; HCA: the latent cache) the steps rotate "
                         "through")
     p.add_argument("--no-warm", action="store_true", help="skip the warm (single copy) measurement")
+    p.add_argument("--paged", action="store_true",
+                   help="CSA decode: hold the latent cache and the indexer keys as block-managed (paged) tensors, "
+                        "32 entries (128 tokens) per block in a shuffled pool behind a block table")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="before the steps, run one device copy of this many MiB (a known-size reference for HBM "
@@ -325,7 +328,8 @@ def main():
         else:
             per_copy = steps._entry_bytes(w.key_fmt, w.DI, 0) * w.B * w.N
             key_copies = max(args.copies, -(-stream_bytes // per_copy))
-            step = steps.CsaDecode(w, inp, copies=args.copies, key_copies=key_copies)
+            step = steps.CsaDecode(w, inp, copies=args.copies, key_copies=key_copies,
+                                   block_rows=32 if args.paged else 0)
             n_distinct = step.copies
             streamed = key_copies * per_copy
     else:
@@ -368,6 +372,8 @@ def main():
                       "compress_ratio": w.m, "latent_dim": w.D, "heads": w.H, "indexer": [w.HI, w.DI], "topk": w.k,
                       "window": w.window, "cache_format": w.main_fmt, "key_format": w.key_fmt,
                       "distinct_steps": n_distinct, "streamed_cache_bytes": streamed,
+                      "cache_layout": ("paged: 32-entry (128-token) blocks in a shuffled pool" if
+                                       getattr(step, "block_rows", 0) else "dense"),
                       "timing": "HIP graph of %d steps replayed, median of 20 event windows" % n_distinct}}
     if hasattr(step, "step_bytes"):
         sb = step.step_bytes()
