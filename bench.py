@@ -51,6 +51,9 @@ def parse():
     p.add_argument("--paged", action="store_true",
                    help="CSA decode: hold the latent cache and the indexer keys as block-managed (paged) tensors, "
                         "32 entries (128 tokens) per block in a shuffled pool behind a block table")
+    p.add_argument("--no-cache-build", action="store_true",
+                   help="HCA decode: skip timing the one-off build of the whole compressed cache from the context's "
+                        "token streams")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="before the steps, run one device copy of this many MiB (a known-size reference for HBM "
@@ -247,6 +250,37 @@ def measured_read_peak(lca, torch, nbytes: int = 2 << 30):
     return {"GBps": best[0], "bytes": nbytes, "workgroups": best[1], "kernel": "stream_read_kernel"}
 
 
+def time_cache_build(w, torch, lca, gen, runs: int = 5):
+    """The one-off HCA cache build: kv_compress over every token of the context (B x n_ctx rows of the C and Z
+    streams, fp32) into the bf16 compressed cache, timed with HIP events around each of `runs` builds (median).
+    Algorithmic bytes: both streams read once plus the cache written once."""
+    from long_context_attention_05_amd import steps as steps_mod
+    rope = w.rope if w.main_fmt == "mixed" else 0
+    C, Z, Ba = gen.hca_build_streams_device(w, "cuda")
+    out = lca.CacheTensor(w.main_fmt, w.B, w.N, w.D, rope)
+    Bad = torch.from_numpy(Ba).cuda()
+
+    def build():
+        lca.kv_compress(C, None, Z, None, Bad, None, None, None, w.B, w.n_ctx, w.D, w.m, False, 0, out.desc())
+
+    build()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(runs)]
+    for a, b in evs:
+        a.record()
+        build()
+        b.record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in evs)[runs // 2]
+    nbytes = 2 * w.B * w.n_ctx * w.D * 4 + w.B * w.N * steps_mod._entry_bytes(w.main_fmt, w.D, rope)
+    del C, Z, out
+    torch.cuda.empty_cache()
+    return {"kernel": "compress_kernel", "tokens": w.B * w.n_ctx, "entries": w.B * w.N, "ms": ms,
+            "algorithmic_bytes": nbytes, "achieved_GBps": nbytes / (ms / 1e3) / 1e9,
+            "frac": nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS,
+            "timed_with": "HIP events around each of %d whole builds (median)" % runs}
+
+
 def time_steps(step, torch, steps_mod, n_distinct: int, steps: int, warmup: int, ev, set_events, windows: int = 20,
                same_copy: bool = False):
     """Capture n_distinct consecutive steps (one per cache copy; all on copy 0 when same_copy) in a HIP graph and
@@ -388,8 +422,8 @@ def main():
     if not has_scores:
         src = ["long_context_attention_05_amd/csrc/attn.hip", "long_context_attention_05_amd/csrc/lca_device.h",
                "long_context_attention_05_amd/build.py"]
-        if w.layer == "swa":  # few rows, a 128-entry window list: the two-pass decode attention (score pass timed)
-            kname = "attn_dec_score_kernel"
+        if w.layer == "swa":  # few rows, a 128-entry window list: the two-pass decode attention (both passes timed)
+            kname = "attn_dec_score_kernel+attn_dec_value_kernel"
             per_launch = step.step_bytes()
         else:  # dense HCA rows: the many-row kernel over a bf16 cache, the wide kernel over the mixed cache
             kname = "attn_pfs_kernel" if w.main_fmt == "bf16" else "attn_wide_kernel"
@@ -420,14 +454,20 @@ def main():
                                "traffic": traffic_record("idx_score_mfma", w.name, src, per_launch),
                                "avg_launch_us": avg_ms * 1e3, "algorithmic_flops_per_launch": per_launch,
                                "timed_with": how}
+    del step
+    torch.cuda.empty_cache()
+    if w.is_decode and w.HI == 0 and w.layer != "swa" and not args.no_cache_build:
+        res["cache_build"] = time_cache_build(w, torch, lca, gen)
+        print("cache build: %.3f ms (%.0f GB/s)" % (res["cache_build"]["ms"], res["cache_build"]["achieved_GBps"]),
+              file=sys.stderr, flush=True)
     if res["roofline"]["bound"] == "hbm":
         rp = measured_read_peak(lca, torch)
         res["roofline"]["measured_read_peak"] = rp
         res["roofline"]["frac_of_measured_read_peak"] = res["roofline"]["achieved"] / rp["GBps"]
         if "achieved_hbm_GBps" in res:
             res["step_frac_of_measured_read_peak"] = res["achieved_hbm_GBps"] / rp["GBps"]
-    del step
-    torch.cuda.empty_cache()
+        if "cache_build" in res:
+            res["cache_build"]["frac_of_measured_read_peak"] = res["cache_build"]["achieved_GBps"] / rp["GBps"]
     if not args.no_cpu_baseline:
         if w.layer in ("swa", "shared2"):
             pass  # extra lines beside the five workloads: no CPU baseline

@@ -198,17 +198,18 @@ size_t indexer_score_topk_workspace_size(int B, int Sq, int N, int k);
 
 /*
  * lca_set_score_events -- profiling hook for the dominant kernel.  While both are non-NULL, every
- * indexer_score_topk call made from the calling host thread records ev_begin (a hipEvent_t) on its stream just
- * before its scoring kernel and ev_end just after it, so the caller can time that kernel with
- * hipEventElapsedTime.  Pass NULL, NULL to stop.  The events are owned by the caller.  Nothing is recorded while the
- * stream is being captured into a graph.
+ * indexer_score_topk call made from the calling host thread launches its scoring kernel with hipExtLaunchKernel
+ * and these two events (hipEvent_t, created by the caller with timing enabled), which the runtime stamps with that
+ * dispatch's own start and end, so hipEventElapsedTime(ev_begin, ev_end) is the kernel's duration.  Pass NULL, NULL
+ * to stop.  The events are owned by the caller.  Nothing is stamped while the stream is being captured into a graph.
  */
 void lca_set_score_events(void* ev_begin, void* ev_end);
 
 /*
- * lca_set_attn_events -- the same hook for the attention kernel: while both are non-NULL, every sparse_mqa_attn
- * and hca_attn call made from the calling host thread records ev_begin just before its attention kernel and ev_end
- * just after it (before the merge of split partials, when there is one).  Pass NULL, NULL to stop.
+ * lca_set_attn_events -- the same hook for the attention: while both are non-NULL, every sparse_mqa_attn and
+ * hca_attn call made from the calling host thread has ev_begin stamped with the start of its first attention kernel
+ * and ev_end with the end of its last one before the merge of split partials (the decode path's score and value
+ * passes are timed together).  Pass NULL, NULL to stop.
  */
 void lca_set_attn_events(void* ev_begin, void* ev_end);
 

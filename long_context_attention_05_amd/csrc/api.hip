@@ -254,7 +254,10 @@ int run_attn(const void* q, int q_format, const lca_tensor& comp_in, int N, int 
     a.part_o = (float*)ws;
     a.part_ml = (float*)((char*)ws + align_up(items * H * D * sizeof(float)));
   }
-  return hip_status(launch_attn(a, (hipStream_t)stream, t_attn_ev_begin, t_attn_ev_end));
+  hipEvent_t eb = t_attn_ev_begin, ee = t_attn_ev_end;
+  const int rh = hip_status(hook_pair(eb, ee, (hipStream_t)stream));
+  if (rh) return rh;
+  return hip_status(launch_attn(a, (hipStream_t)stream, eb, ee));
 }
 
 }  // namespace
@@ -435,17 +438,11 @@ int indexer_score_topk(lca_tensor qI, const float* w, lca_tensor kI, int B, int 
       rc = hip_status(launch_sel_zero(state, B * Sq, st));
       if (rc) return rc;
     }
-    const bool timed = t_ev_begin && t_ev_end;
-    if (timed) {
-      rc = hip_status(record_hook_event(t_ev_begin, st));
-      if (rc) return rc;
-    }
-    rc = hip_status(launch_indexer_scores(a, st));
+    hipEvent_t eb = t_ev_begin, ee = t_ev_end;
+    rc = hip_status(hook_pair(eb, ee, st));
     if (rc) return rc;
-    if (timed) {
-      rc = hip_status(record_hook_event(t_ev_end, st));
-      if (rc) return rc;
-    }
+    rc = hip_status(launch_indexer_scores(a, st, eb, ee));
+    if (rc) return rc;
   }
   SelArgs s{(const uint32_t*)(wsb + L.keys), idx_out, score_out, B * Sq, Sq, N, m, k, q_start_pos, seq_pos, state,
             multi ? (int*)(wsb + L.counts) : nullptr, multi ? (uint2*)(wsb + L.cand) : nullptr};

@@ -1986,16 +1986,16 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
 
 // The value pass with the smallest per-wave load round that holds a wave's nti tiles (at most 8 per round).
 template <int FMT>
-void launch_dec_value(int nti, dim3 grid, hipStream_t st, const AttnArgs& a) {
+void launch_dec_value(int nti, dim3 grid, hipStream_t st, hipEvent_t ee, const AttnArgs& a) {
   const dim3 blk(64 * kDvWaves);
   switch (nti <= 1 ? 1 : nti >= 7 ? 8 : nti) {
-    case 1: hipLaunchKernelGGL((attn_dec_value_kernel<FMT, 1>), grid, blk, 0, st, a); break;
-    case 2: hipLaunchKernelGGL((attn_dec_value_kernel<FMT, 2>), grid, blk, 0, st, a); break;
-    case 3: hipLaunchKernelGGL((attn_dec_value_kernel<FMT, 3>), grid, blk, 0, st, a); break;
-    case 4: hipLaunchKernelGGL((attn_dec_value_kernel<FMT, 4>), grid, blk, 0, st, a); break;
-    case 5: hipLaunchKernelGGL((attn_dec_value_kernel<FMT, 5>), grid, blk, 0, st, a); break;
-    case 6: hipLaunchKernelGGL((attn_dec_value_kernel<FMT, 6>), grid, blk, 0, st, a); break;
-    default: hipLaunchKernelGGL((attn_dec_value_kernel<FMT, 8>), grid, blk, 0, st, a); break;
+    case 1: hipExtLaunchKernelGGL((attn_dec_value_kernel<FMT, 1>), grid, blk, 0, st, nullptr, ee, 0, a); break;
+    case 2: hipExtLaunchKernelGGL((attn_dec_value_kernel<FMT, 2>), grid, blk, 0, st, nullptr, ee, 0, a); break;
+    case 3: hipExtLaunchKernelGGL((attn_dec_value_kernel<FMT, 3>), grid, blk, 0, st, nullptr, ee, 0, a); break;
+    case 4: hipExtLaunchKernelGGL((attn_dec_value_kernel<FMT, 4>), grid, blk, 0, st, nullptr, ee, 0, a); break;
+    case 5: hipExtLaunchKernelGGL((attn_dec_value_kernel<FMT, 5>), grid, blk, 0, st, nullptr, ee, 0, a); break;
+    case 6: hipExtLaunchKernelGGL((attn_dec_value_kernel<FMT, 6>), grid, blk, 0, st, nullptr, ee, 0, a); break;
+    default: hipExtLaunchKernelGGL((attn_dec_value_kernel<FMT, 8>), grid, blk, 0, st, nullptr, ee, 0, a); break;
   }
 }
 
@@ -2003,24 +2003,21 @@ bool attn_uses_mfma(int H, int D, int q_format, int kv_format) {
   return H == 64 && D == 512 && q_format == LCA_BF16 && (kv_format == LCA_BF16 || kv_format == LCA_MIXED_FP8);
 }
 
-hipError_t launch_attn(AttnArgs a, hipStream_t st, hipEvent_t ev_begin, hipEvent_t ev_end) {
+hipError_t launch_attn(AttnArgs a, hipStream_t st, hipEvent_t eb, hipEvent_t ee) {
   const bool mfma = attn_uses_mfma(a.H, a.D, a.q_format, a.comp.format);
   dim3 grid((unsigned)a.n_splits, (unsigned)a.Sq, (unsigned)a.B);
   clear_stale_error();
-  if (ev_begin && ev_end) {
-    const hipError_t e = record_hook_event(ev_begin, st);
-    if (e != hipSuccess) return e;
-  }
   if (mfma && a.hg_mode == 3) {
     const dim3 sgrid((unsigned)(a.B * a.Sq), (unsigned)(a.dec_tiles / 2));
     const dim3 vgrid((unsigned)(a.B * a.Sq), 8u, 4u);
     const int nti = (a.dec_tiles + kDvWaves - 1) / kDvWaves;  // most tiles a value-pass wave takes
     if (a.comp.format == LCA_BF16) {
-      hipLaunchKernelGGL(attn_dec_score_kernel<LCA_BF16>, sgrid, dim3(64 * kDsWaves), 0, st, a);
-      launch_dec_value<LCA_BF16>(nti, vgrid, st, a);
+      hipExtLaunchKernelGGL(attn_dec_score_kernel<LCA_BF16>, sgrid, dim3(64 * kDsWaves), 0, st, eb, nullptr, 0, a);
+      launch_dec_value<LCA_BF16>(nti, vgrid, st, ee, a);
     } else {
-      hipLaunchKernelGGL(attn_dec_score_kernel<LCA_MIXED_FP8>, sgrid, dim3(64 * kDsWaves), 0, st, a);
-      launch_dec_value<LCA_MIXED_FP8>(nti, vgrid, st, a);
+      hipExtLaunchKernelGGL(attn_dec_score_kernel<LCA_MIXED_FP8>, sgrid, dim3(64 * kDsWaves), 0, st, eb, nullptr, 0,
+                            a);
+      launch_dec_value<LCA_MIXED_FP8>(nti, vgrid, st, ee, a);
     }
   } else if (mfma && a.hg_mode == 2) {
     // mode 2 is chosen for the mixed cache only (dense HCA rows over a bf16 cache take the many-row kernel)
@@ -2028,7 +2025,7 @@ hipError_t launch_attn(AttnArgs a, hipStream_t st, hipEvent_t ev_begin, hipEvent
     const hipError_t e = ensure_dyn_lds((const void*)attn_wide_kernel<LCA_MIXED_FP8>, (int)kWdLds);
     if (e != hipSuccess) return e;
     const dim3 wgrid((unsigned)(a.B * a.Sq * a.n_splits));
-    hipLaunchKernelGGL(attn_wide_kernel<LCA_MIXED_FP8>, wgrid, dim3(kWdThreads), kWdLds, st, a);
+    hipExtLaunchKernelGGL(attn_wide_kernel<LCA_MIXED_FP8>, wgrid, dim3(kWdThreads), kWdLds, st, eb, ee, 0, a);
   } else if (mfma && a.hg_mode == 1) {
     hipError_t e = ensure_dyn_lds((const void*)attn_hgw_kernel<LCA_BF16>, (int)kHgwLds);
     if (e == hipSuccess) e = ensure_dyn_lds((const void*)attn_hgw_kernel<LCA_MIXED_FP8>, (int)kHgwLds);
@@ -2036,9 +2033,9 @@ hipError_t launch_attn(AttnArgs a, hipStream_t st, hipEvent_t ev_begin, hipEvent
     const int pairs = a.B * a.Sq * a.n_splits;
     const dim3 hgrid((unsigned)(((pairs + 7) / 8) * 32));
     if (a.comp.format == LCA_BF16)
-      hipLaunchKernelGGL(attn_hgw_kernel<LCA_BF16>, hgrid, dim3(256), kHgwLds, st, a, pairs);
+      hipExtLaunchKernelGGL(attn_hgw_kernel<LCA_BF16>, hgrid, dim3(256), kHgwLds, st, eb, ee, 0, a, pairs);
     else
-      hipLaunchKernelGGL(attn_hgw_kernel<LCA_MIXED_FP8>, hgrid, dim3(256), kHgwLds, st, a, pairs);
+      hipExtLaunchKernelGGL(attn_hgw_kernel<LCA_MIXED_FP8>, hgrid, dim3(256), kHgwLds, st, eb, ee, 0, a, pairs);
   } else if (mfma) {
     hipError_t e = ensure_dyn_lds((const void*)attn_mfma_kernel<LCA_BF16>, (int)kMfmaLds);
     if (e == hipSuccess) e = ensure_dyn_lds((const void*)attn_mfma_kernel<LCA_MIXED_FP8>, (int)kMfmaLds);
@@ -2046,17 +2043,16 @@ hipError_t launch_attn(AttnArgs a, hipStream_t st, hipEvent_t ev_begin, hipEvent
     if (a.comp.format == LCA_BF16 && tensor_storage_rows(a.raw, a.B) * 1024 < (1ll << 31) &&
         tensor_storage_rows(a.comp, a.B) * 1024 < (1ll << 31)) {
       a.part_bf16 = 1;  // split partials in bf16, for this kernel and the merge after it
-      hipLaunchKernelGGL(attn_pfs_kernel, grid, dim3(kPsThreads), 0, st, a);
+      hipExtLaunchKernelGGL(attn_pfs_kernel, grid, dim3(kPsThreads), 0, st, eb, ee, 0, a);
     }
     else if (a.comp.format == LCA_BF16)
-      hipLaunchKernelGGL(attn_mfma_kernel<LCA_BF16>, grid, dim3(kAttnThreads), kMfmaLds, st, a);
+      hipExtLaunchKernelGGL(attn_mfma_kernel<LCA_BF16>, grid, dim3(kAttnThreads), kMfmaLds, st, eb, ee, 0, a);
     else
-      hipLaunchKernelGGL(attn_mfma_kernel<LCA_MIXED_FP8>, grid, dim3(kAttnThreads), kMfmaLds, st, a);
+      hipExtLaunchKernelGGL(attn_mfma_kernel<LCA_MIXED_FP8>, grid, dim3(kAttnThreads), kMfmaLds, st, eb, ee, 0, a);
   } else {
-    hipLaunchKernelGGL(attn_simt_kernel, grid, dim3(256), 0, st, a);
+    hipExtLaunchKernelGGL(attn_simt_kernel, grid, dim3(256), 0, st, eb, ee, 0, a);
   }
   hipError_t e = hipGetLastError();
-  if (e == hipSuccess && ev_begin && ev_end) e = record_hook_event(ev_end, st);
   if (e != hipSuccess || a.n_splits == 1) return e;
   const size_t lds = sizeof(float) * (size_t)a.n_splits;
   hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)a.H, (unsigned)a.Sq, (unsigned)a.B), dim3(kMergeThreads), lds,

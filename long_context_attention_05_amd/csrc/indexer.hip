@@ -696,7 +696,7 @@ bool indexer_uses_decode_kernel(int B, int Sq, int HI, int DI, int N, int q_form
   return q_format == LCA_BF16 && (Sq <= 2 || N > kTopkLdsKeys);
 }
 
-hipError_t launch_indexer_scores(const IdxArgs& a, hipStream_t st) {
+hipError_t launch_indexer_scores(const IdxArgs& a, hipStream_t st, hipEvent_t eb, hipEvent_t ee) {
   const int nvis_max = nvis_of(a.q_start + a.Sq - 1, a.m, a.N);  // q_start is the largest position of the call
   if (nvis_max <= 0) return hipSuccess;
   clear_stale_error();
@@ -712,10 +712,10 @@ hipError_t launch_indexer_scores(const IdxArgs& a, hipStream_t st) {
       const dim3 grid((unsigned)decode_grid_x((nvis_max + nst * kF4rStage - 1) / (nst * kF4rStage), a.Sq),
                       (unsigned)rows);
       const dim3 block(kF4rWaves * 64);
-      if (nst == 8) hipLaunchKernelGGL(idx_score_decode_fp4_ring<8>, grid, block, 0, st, a);
-      else if (nst == 4) hipLaunchKernelGGL(idx_score_decode_fp4_ring<4>, grid, block, 0, st, a);
-      else if (nst == 2) hipLaunchKernelGGL(idx_score_decode_fp4_ring<2>, grid, block, 0, st, a);
-      else hipLaunchKernelGGL(idx_score_decode_fp4_ring<1>, grid, block, 0, st, a);
+      if (nst == 8) hipExtLaunchKernelGGL(idx_score_decode_fp4_ring<8>, grid, block, 0, st, eb, ee, 0, a);
+      else if (nst == 4) hipExtLaunchKernelGGL(idx_score_decode_fp4_ring<4>, grid, block, 0, st, eb, ee, 0, a);
+      else if (nst == 2) hipExtLaunchKernelGGL(idx_score_decode_fp4_ring<2>, grid, block, 0, st, eb, ee, 0, a);
+      else hipExtLaunchKernelGGL(idx_score_decode_fp4_ring<1>, grid, block, 0, st, eb, ee, 0, a);
       return hipGetLastError();
     }
     // a fixed key range per workgroup (NST stages of 4 waves x KPW keys), the grid grows with the context; fewer
@@ -725,20 +725,20 @@ hipError_t launch_indexer_scores(const IdxArgs& a, hipStream_t st) {
     int nst = 4;
     while (nst > 1 && rows * ((nvis_max + nst * 4 * kpw - 1) / (nst * 4 * kpw)) < 512) nst >>= 1;
     const dim3 grid((unsigned)decode_grid_x((nvis_max + nst * 4 * kpw - 1) / (nst * 4 * kpw), a.Sq), (unsigned)rows);
-    if (nst == 4) hipLaunchKernelGGL(idx_score_decode_bf16<4>, grid, dim3(256), 0, st, a);
-    else if (nst == 2) hipLaunchKernelGGL(idx_score_decode_bf16<2>, grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL(idx_score_decode_bf16<1>, grid, dim3(256), 0, st, a);
+    if (nst == 4) hipExtLaunchKernelGGL(idx_score_decode_bf16<4>, grid, dim3(256), 0, st, eb, ee, 0, a);
+    else if (nst == 2) hipExtLaunchKernelGGL(idx_score_decode_bf16<2>, grid, dim3(256), 0, st, eb, ee, 0, a);
+    else hipExtLaunchKernelGGL(idx_score_decode_bf16<1>, grid, dim3(256), 0, st, eb, ee, 0, a);
   } else if (mfma) {
     const int qpb = a.Sq >= 16 ? 16 : a.Sq;
     dim3 grid((unsigned)((nvis_max + kMfmaEntriesPerBlock - 1) / kMfmaEntriesPerBlock),
               (unsigned)((a.Sq + qpb - 1) / qpb), (unsigned)a.B);
     if (a.q.format == LCA_BF16)
-      hipLaunchKernelGGL(idx_score_mfma<LCA_BF16>, grid, dim3(256), 0, st, a, qpb);
+      hipExtLaunchKernelGGL(idx_score_mfma<LCA_BF16>, grid, dim3(256), 0, st, eb, ee, 0, a, qpb);
     else
-      hipLaunchKernelGGL(idx_score_mfma<LCA_FP4>, grid, dim3(256), 0, st, a, qpb);
+      hipExtLaunchKernelGGL(idx_score_mfma<LCA_FP4>, grid, dim3(256), 0, st, eb, ee, 0, a, qpb);
   } else {
     dim3 grid((unsigned)((nvis_max + kSimtTile - 1) / kSimtTile), (unsigned)a.Sq, (unsigned)a.B);
-    hipLaunchKernelGGL(idx_score_simt, grid, dim3(256), 0, st, a);
+    hipExtLaunchKernelGGL(idx_score_simt, grid, dim3(256), 0, st, eb, ee, 0, a);
   }
   return hipGetLastError();
 }

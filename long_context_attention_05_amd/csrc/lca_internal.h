@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "../../include/lca.h"
+#include <hip/hip_ext.h>
 
 namespace lca {
 
@@ -15,13 +16,19 @@ inline void clear_stale_error() {
   (void)e;
 }
 
-// Records a profiling-hook event on st; nothing while st is being captured into a graph (the hooks time eager
-// launches only).
-inline hipError_t record_hook_event(hipEvent_t e, hipStream_t st) {
+// The profiling hook's event pair for one timed kernel: kept when both are set and st is not being captured into a
+// graph (the hooks time eager launches only), else both null.  The timed kernel is launched with
+// hipExtLaunchKernelGGL, which stamps the events with that dispatch's own start and end times.
+inline hipError_t hook_pair(hipEvent_t& b, hipEvent_t& e, hipStream_t st) {
+  if (!b || !e) {
+    b = e = nullptr;
+    return hipSuccess;
+  }
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-  hipError_t r = hipStreamIsCapturing(st, &cs);
+  const hipError_t r = hipStreamIsCapturing(st, &cs);
   if (r != hipSuccess) return r;
-  return cs == hipStreamCaptureStatusNone ? hipEventRecord(e, st) : hipSuccess;
+  if (cs != hipStreamCaptureStatusNone) b = e = nullptr;
+  return hipSuccess;
 }
 
 // Raises a kernel's dynamic LDS limit to `bytes` on the current device, once per (kernel, device); safe to call from
@@ -53,7 +60,9 @@ constexpr int kDecodeMaxRows = 4;
 constexpr int kTopkLdsKeys = 32768;
 // Whether launch_indexer_scores takes the decode kernels (which fill sel_state) for N entries per sequence.
 bool indexer_uses_decode_kernel(int B, int Sq, int HI, int DI, int N, int q_format, int k_format);
-hipError_t launch_indexer_scores(const IdxArgs& a, hipStream_t st);
+// ev_begin / ev_end (nullable, from hook_pair): stamped with the scoring kernel's start and end.
+hipError_t launch_indexer_scores(const IdxArgs& a, hipStream_t st, hipEvent_t ev_begin = nullptr,
+                                 hipEvent_t ev_end = nullptr);
 
 // stage 2b, exact top-k (topk.hip)
 struct SelArgs {
@@ -113,7 +122,8 @@ struct AttnArgs {
 constexpr int kDecMaxEntries = 2048;  // list positions per row in the two-pass decode attention
 constexpr int kHgSplitMax = 2048;  // list positions per workgroup slice in the MFMA attention kernels (LDS row table)
 bool attn_uses_mfma(int H, int D, int q_format, int kv_format);
-// ev_begin / ev_end (nullable): recorded around the attention kernel, before the merge of split partials.
+// ev_begin / ev_end (nullable, from hook_pair): stamped with the start of the attention's first kernel and the end of
+// its last one before the merge of split partials.
 hipError_t launch_attn(AttnArgs a, hipStream_t st, hipEvent_t ev_begin = nullptr, hipEvent_t ev_end = nullptr);
 
 // measurement helper (measure.hip)
