@@ -639,11 +639,11 @@ __global__ __launch_bounds__(kPsThreads) void attn_pfs_kernel(AttnArgs a) {
   }
   __syncthreads();
   if (scorer) return;
+  if (a.n_splits == 1) {
 #pragma unroll
-  for (int hg = 0; hg < 4; ++hg) {
-    const int head = 16 * hg + hl;
-    const float m = pd_ml[head][0], l = pd_ml[head][1];
-    if (a.n_splits == 1) {
+    for (int hg = 0; hg < 4; ++hg) {
+      const int head = 16 * hg + hl;
+      const float m = pd_ml[head][0], l = pd_ml[head][1];
       const float z = a.sink[head];
       const float M = fmaxf(m, z);
       float den, f;
@@ -669,27 +669,47 @@ __global__ __launch_bounds__(kPsThreads) void attn_pfs_kernel(AttnArgs a) {
       }
       if (a.lse && vw == 0 && grp == 0)
         a.lse[((long long)b * a.Sq + r) * 64 + head] = (M == -INFINITY) ? -INFINITY : M + __logf(den);
-    } else {
-      const long long pi = (item * 64 + head) * 512 + 128 * vw + 4 * grp;
-      if (a.part_bf16) {  // unnormalised partial sums in bf16 (the merge rescales them in fp32): half the bytes
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-          uint2 w2;
-          w2.x = pack_bf16x2(acc[hg][dt][0], acc[hg][dt][1]);
-          w2.y = pack_bf16x2(acc[hg][dt][2], acc[hg][dt][3]);
-          *(uint2*)((uint16_t*)a.part_o + pi + 16 * dt) = w2;
-        }
-      } else {
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
-          *(float4*)(a.part_o + pi + 16 * dt) =
-              make_float4(acc[hg][dt][0], acc[hg][dt][1], acc[hg][dt][2], acc[hg][dt][3]);
-      }
-      if (vw == 0 && grp == 0) {
-        a.part_ml[(item * 64 + head) * 2 + 0] = m;
-        a.part_ml[(item * 64 + head) * 2 + 1] = l;
-      }
     }
+    return;
+  }
+  if (vw == 0 && grp == 0) {
+#pragma unroll
+    for (int hg = 0; hg < 4; ++hg) {
+      const int head = 16 * hg + hl;
+      a.part_ml[(item * 64 + head) * 2 + 0] = pd_ml[head][0];
+      a.part_ml[(item * 64 + head) * 2 + 1] = pd_ml[head][1];
+    }
+  }
+  if (!a.part_bf16) {
+#pragma unroll
+    for (int hg = 0; hg < 4; ++hg) {
+      const long long pi = (item * 64 + 16 * hg + hl) * 512 + 128 * vw + 4 * grp;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        *(float4*)(a.part_o + pi + 16 * dt) =
+            make_float4(acc[hg][dt][0], acc[hg][dt][1], acc[hg][dt][2], acc[hg][dt][3]);
+    }
+    return;
+  }
+  // unnormalised partial sums in bf16 (the merge rescales them in fp32): half the bytes.  The wave's 64 heads x 128
+  // channels go through its own slot of the idle ring (every load has landed and every wave is past its last tile),
+  // so that each store writes whole 256-byte head rows, 1 KB per instruction, instead of 32-byte pieces.
+  constexpr int kPr = 272;  // LDS bytes per head row: 256 + 16, which spreads the lanes' 8-byte writes over banks
+  uint8_t* stage = vw == 0 ? pd_slot0 : vw == 1 ? pd_slot1 : vw == 2 ? pd_slot2 : pd_slot3;
+#pragma unroll
+  for (int hg = 0; hg < 4; ++hg)
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      uint2 w2;
+      w2.x = pack_bf16x2(acc[hg][dt][0], acc[hg][dt][1]);
+      w2.y = pack_bf16x2(acc[hg][dt][2], acc[hg][dt][3]);
+      *(uint2*)(stage + (16 * hg + hl) * kPr + 2 * (16 * dt + 4 * grp)) = w2;
+    }
+  uint8_t* po = (uint8_t*)a.part_o + (item * 64 * 512 + 128 * vw) * 2;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int head = 4 * i + (lane >> 4);
+    *(uint4*)(po + (long long)head * 1024 + 16 * (lane & 15)) = *(const uint4*)(stage + head * kPr + 16 * (lane & 15));
   }
 }
 
