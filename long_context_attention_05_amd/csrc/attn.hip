@@ -639,6 +639,19 @@ __global__ __launch_bounds__(kPsThreads) void attn_pfs_kernel(AttnArgs a) {
   }
   __syncthreads();
   if (scorer) return;
+  // bf16 rows (the output of a whole row, or a split's unnormalised partial sums, which the merge rescales in
+  // fp32) go through the wave's own slot of the idle ring (every load has landed and every wave is past its last
+  // tile), so that each store writes whole 256-byte head rows, 1 KB per instruction, instead of 32-byte pieces
+  constexpr int kPr = 272;  // LDS bytes per head row: 256 + 16, which spreads the lanes' 8-byte writes over banks
+  uint8_t* stage = vw == 0 ? pd_slot0 : vw == 1 ? pd_slot1 : vw == 2 ? pd_slot2 : pd_slot3;
+  auto store_rows = [&](uint8_t* dst) {  // dst: head 0 of the wave's 128 channels; head rows 1 KB apart
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int head = 4 * i + (lane >> 4);
+      *(uint4*)(dst + (long long)head * 1024 + 16 * (lane & 15)) =
+          *(const uint4*)(stage + head * kPr + 16 * (lane & 15));
+    }
+  };
   if (a.n_splits == 1) {
 #pragma unroll
     for (int hg = 0; hg < 4; ++hg) {
@@ -664,12 +677,14 @@ __global__ __launch_bounds__(kPsThreads) void attn_pfs_kernel(AttnArgs a) {
           uint2 w2;
           w2.x = pack_bf16x2(o[0], o[1]);
           w2.y = pack_bf16x2(o[2], o[3]);
-          *(uint2*)((uint16_t*)a.out + ob + 16 * dt) = w2;
+          *(uint2*)(stage + head * kPr + 2 * (16 * dt + 4 * grp)) = w2;
         }
       }
       if (a.lse && vw == 0 && grp == 0)
         a.lse[((long long)b * a.Sq + r) * 64 + head] = (M == -INFINITY) ? -INFINITY : M + __logf(den);
     }
+    if (a.out_format != LCA_F32)
+      store_rows((uint8_t*)a.out + ((((long long)b * a.Sq + r) * 64) * 512 + 128 * vw) * 2);
     return;
   }
   if (vw == 0 && grp == 0) {
@@ -691,11 +706,6 @@ __global__ __launch_bounds__(kPsThreads) void attn_pfs_kernel(AttnArgs a) {
     }
     return;
   }
-  // unnormalised partial sums in bf16 (the merge rescales them in fp32): half the bytes.  The wave's 64 heads x 128
-  // channels go through its own slot of the idle ring (every load has landed and every wave is past its last tile),
-  // so that each store writes whole 256-byte head rows, 1 KB per instruction, instead of 32-byte pieces.
-  constexpr int kPr = 272;  // LDS bytes per head row: 256 + 16, which spreads the lanes' 8-byte writes over banks
-  uint8_t* stage = vw == 0 ? pd_slot0 : vw == 1 ? pd_slot1 : vw == 2 ? pd_slot2 : pd_slot3;
 #pragma unroll
   for (int hg = 0; hg < 4; ++hg)
 #pragma unroll
@@ -705,12 +715,7 @@ __global__ __launch_bounds__(kPsThreads) void attn_pfs_kernel(AttnArgs a) {
       w2.y = pack_bf16x2(acc[hg][dt][2], acc[hg][dt][3]);
       *(uint2*)(stage + (16 * hg + hl) * kPr + 2 * (16 * dt + 4 * grp)) = w2;
     }
-  uint8_t* po = (uint8_t*)a.part_o + (item * 64 * 512 + 128 * vw) * 2;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int head = 4 * i + (lane >> 4);
-    *(uint4*)(po + (long long)head * 1024 + 16 * (lane & 15)) = *(const uint4*)(stage + head * kPr + 16 * (lane & 15));
-  }
+  store_rows((uint8_t*)a.part_o + (item * 64 * 512 + 128 * vw) * 2);
 }
 
 // ------------------------------------------------------------------------------------------------
