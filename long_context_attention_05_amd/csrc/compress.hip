@@ -179,21 +179,109 @@ __device__ void store_row(const RowOut& o, long long row, const float (&vin)[CPT
   }
 }
 
-template <int CPT>
-__global__ __launch_bounds__(kRowThreads) void encode_rows_kernel(const float* __restrict__ src, long long rows,
-                                                                   long long row0, RowOut o) {
-  __shared__ float red[kRowThreads / 64];
-  __shared__ float rot[2 * kRotMaxDim];
-  const long long r = blockIdx.x;
-  const int b = blockIdx.y;
-  const float* s = src + ((long long)b * rows + r) * o.dim;
-  float v[CPT];
+// The codec for rows that arrive already in memory (lca_encode): one wave per row, four rows per workgroup, a row
+// held as v[u] = channel (lane + 64 u), u < CPW.  Every reduction stays inside the wave, and so does the rotation:
+// its stages with h < 64 pair lanes (shuffles) and those with h >= 64 pair registers u and u ^ (h / 64) of one lane,
+// with the same operands in the same order as hadamard_row (x_j + x_{j+h}, x_j - x_{j+h}).  The codes are those of
+// store_row.
+constexpr int kEncWaves = 4;
+
+template <int CPW>
+__device__ void store_row_wave(const RowOut& o, long long row, float (&v)[CPW]) {
+  const int c = o.dim, lane = threadIdx.x & 63;
+  if (o.rotate) {
+    const int hw = c < 64 ? c : 64;
+    for (int h = 1; h < hw; h <<= 1) {
 #pragma unroll
-  for (int u = 0; u < CPT; ++u) {
-    int j = threadIdx.x + blockDim.x * u;
-    v[u] = (j < o.dim) ? s[j] : 0.0f;
+      for (int u = 0; u < CPW; ++u) {
+        const float x = __shfl_xor(v[u], h, 64);
+        v[u] = (lane & h) ? x - v[u] : v[u] + x;
+      }
+    }
+#pragma unroll
+    for (int s = 1; s < CPW; s <<= 1) {
+      if (64 * s >= c) break;
+#pragma unroll
+      for (int u = 0; u < CPW; ++u) {
+        if (u & s) continue;
+        const float x = v[u], y = v[u | s];
+        v[u] = x + y;
+        v[u | s] = x - y;
+      }
+    }
+    const int p = 31 - __clz(c);
+    const float sc = (p & 1) ? ldexpf(1.41421354f, -(p + 1) / 2) : ldexpf(1.0f, -p / 2);
+#pragma unroll
+    for (int u = 0; u < CPW; ++u) v[u] = (lane + 64 * u < c) ? v[u] * sc : 0.0f;
   }
-  store_row<CPT>(o, out_row(o, b, row0 + r), v, red, rot);
+  if (o.format == LCA_F32) {
+    float* d = (float*)o.data + row * c;
+#pragma unroll
+    for (int u = 0; u < CPW; ++u)
+      if (lane + 64 * u < c) d[lane + 64 * u] = v[u];
+  } else if (o.format == LCA_BF16) {
+    uint16_t* d = (uint16_t*)o.data + row * c;
+#pragma unroll
+    for (int u = 0; u < CPW; ++u)
+      if (lane + 64 * u < c) d[lane + 64 * u] = f32_to_bf16(v[u]);
+  } else if (o.format == LCA_MIXED_FP8) {
+    const int dm = c - o.rope;
+    float am = 0.0f;
+#pragma unroll
+    for (int u = 0; u < CPW; ++u)
+      if (lane + 64 * u < dm) am = fmaxf(am, fabsf(v[u]));
+    am = wave_max(am);
+    const float s = (am == 0.0f) ? 1.0f : am / 448.0f;  // IEEE fp32 divide
+    uint8_t* d = (uint8_t*)o.data + row * dm;
+    uint16_t* rd = (uint16_t*)o.rope_data + row * o.rope;
+#pragma unroll
+    for (int u = 0; u < CPW; ++u) {
+      const int j = lane + 64 * u;
+      if (j < dm) {
+        const float y = fminf(fmaxf(v[u] / s, -448.0f), 448.0f);
+        d[j] = fp8_encode(y);
+      } else if (j < c) {
+        rd[j - dm] = f32_to_bf16(v[u]);
+      }
+    }
+    if (lane == 0) ((float*)o.scale)[row] = s;
+  } else {  // LCA_FP4: groups of 16 consecutive channels live in 16 consecutive lanes
+    uint8_t* d = (uint8_t*)o.data + row * (c / 2);
+    uint8_t* sc = (uint8_t*)o.scale + row * (c / 16);
+#pragma unroll
+    for (int u = 0; u < CPW; ++u) {
+      const int j = lane + 64 * u;
+      float a = (j < c) ? fabsf(v[u]) : 0.0f;
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
+      const int e = fp4_group_exp(a);
+      const uint32_t code = fp4_encode(ldexpf(v[u], -e));
+      const uint32_t other = __shfl_xor(code, 1, 64);
+      if (j < c) {
+        if ((j & 1) == 0) d[j >> 1] = (uint8_t)(code | (other << 4));
+        if ((j & 15) == 0) sc[j >> 4] = (uint8_t)(e + 127);
+      }
+    }
+  }
+}
+
+// RPW rows per wave (short rows), every row's loads issued before the first is encoded.
+template <int CPW, int RPW>
+__global__ __launch_bounds__(64 * kEncWaves) void encode_rows_kernel(const float* __restrict__ src, long long rows,
+                                                                      long long row0, RowOut o) {
+  const long long r0 = ((long long)blockIdx.x * kEncWaves + (threadIdx.x >> 6)) * RPW;
+  if (r0 >= rows) return;  // wave-uniform
+  const int b = blockIdx.y, lane = threadIdx.x & 63;
+  float v[RPW][CPW];
+#pragma unroll
+  for (int q = 0; q < RPW; ++q) {
+    const float* s = src + ((long long)b * rows + min(r0 + q, rows - 1)) * o.dim;
+#pragma unroll
+    for (int u = 0; u < CPW; ++u) v[q][u] = (lane + 64 * u < o.dim) ? s[lane + 64 * u] : 0.0f;
+  }
+#pragma unroll
+  for (int q = 0; q < RPW; ++q)
+    if (r0 + q < rows) store_row_wave<CPW>(o, out_row(o, b, row0 + r0 + q), v[q]);
 }
 
 struct CompressArgs {
@@ -338,17 +426,22 @@ static int threads_for(int c) {
 
 hipError_t launch_encode(const float* src, int B, long long rows, long long row0, const lca_tensor& dst,
                          hipStream_t st) {
-  RowOut o = row_out(dst);
-  int nt = threads_for(dst.dim);
-  int cpt = (dst.dim + nt - 1) / nt;
-  dim3 grid((unsigned)rows, (unsigned)B);
+  const RowOut o = row_out(dst);
+  const int cpw = (dst.dim + 63) / 64;  // dim <= 1024 (checked by the caller)
+  const int rpw = cpw <= 2 ? 4 : cpw <= 4 ? 2 : 1;  // rows per wave: about 2 KB of each wave's loads in flight
+  const long long per_wg = (long long)kEncWaves * rpw;
+  const dim3 grid((unsigned)((rows + per_wg - 1) / per_wg), (unsigned)B), block(64 * kEncWaves);
   clear_stale_error();
-  if (cpt <= 1)
-    hipLaunchKernelGGL(encode_rows_kernel<1>, grid, dim3(nt), 0, st, src, rows, row0, o);
-  else if (cpt <= 2)
-    hipLaunchKernelGGL(encode_rows_kernel<2>, grid, dim3(nt), 0, st, src, rows, row0, o);
+  if (cpw <= 1)
+    hipLaunchKernelGGL((encode_rows_kernel<1, 4>), grid, block, 0, st, src, rows, row0, o);
+  else if (cpw <= 2)
+    hipLaunchKernelGGL((encode_rows_kernel<2, 4>), grid, block, 0, st, src, rows, row0, o);
+  else if (cpw <= 4)
+    hipLaunchKernelGGL((encode_rows_kernel<4, 2>), grid, block, 0, st, src, rows, row0, o);
+  else if (cpw <= 8)
+    hipLaunchKernelGGL((encode_rows_kernel<8, 1>), grid, block, 0, st, src, rows, row0, o);
   else
-    hipLaunchKernelGGL(encode_rows_kernel<4>, grid, dim3(nt), 0, st, src, rows, row0, o);
+    hipLaunchKernelGGL((encode_rows_kernel<16, 1>), grid, block, 0, st, src, rows, row0, o);
   return hipGetLastError();
 }
 
