@@ -62,19 +62,23 @@ def parse():
 
 
 class HipEvents:
-    """hipEvent_t pairs through the HIP runtime that torch already loaded."""
+    """hipEvent_t pairs through the HIP runtime that torch already loaded, created for timing only
+    (hipEventDisableSystemFence: no cache writeback and invalidation when they complete, which would otherwise add
+    to the interval they measure)."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000  # hipEventDisableSystemFence
 
     def __init__(self):
         self.hip = ctypes.CDLL("libamdhip64.so")
-        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
 
     def create(self):
         e = ctypes.c_void_p()
-        rc = self.hip.hipEventCreate(ctypes.byref(e))
+        rc = self.hip.hipEventCreateWithFlags(ctypes.byref(e), self.DISABLE_SYSTEM_FENCE)
         if rc != 0:
-            raise RuntimeError("hipEventCreate failed: %d" % rc)
+            raise RuntimeError("hipEventCreateWithFlags failed: %d" % rc)
         return e.value
 
     def elapsed_ms(self, a, b) -> float:
@@ -322,7 +326,8 @@ def time_steps(step, torch, steps_mod, n_distinct: int, steps: int, warmup: int,
     set_events(None, None)
     torch.cuda.synchronize()
     kms = [ev.elapsed_ms(a, b) for a, b in pairs]
-    how = "HIP events around each of %d launches in eager steps queued back to back" % n_k
+    how = ("dispatch-stamped HIP events (hipExtLaunchKernel, no system fence) on each of %d launches in eager steps "
+           "queued back to back" % n_k)
     return med, windows * reps * n_distinct, sum(kms) / len(kms), how
 
 
