@@ -469,7 +469,10 @@ __shared__ __attribute__((aligned(16))) uint8_t f4r_s0[kF4rScaleB];
 __shared__ __attribute__((aligned(16))) uint8_t f4r_s1[kF4rScaleB];
 __shared__ __attribute__((aligned(16))) uint8_t f4r_s2[kF4rScaleB];
 __shared__ __attribute__((aligned(16))) uint8_t f4r_s3[kF4rScaleB];
-__shared__ int f4r_hist[kSelBins];
+// Row histograms of pass 1 in LDS, one per query row the workgroup scores (with 4 slots of codes and scales, two rows
+// fill the 160 KB of a CU's LDS exactly).
+constexpr int kF4rMaxRows = 2;
+__shared__ int f4r_hist[kF4rMaxRows * kSelBins];
 
 template <int S>
 __device__ __forceinline__ uint8_t* f4r_codes() {
@@ -494,11 +497,11 @@ __host__ __device__ constexpr int vm_wait_imm(int n) { return (n & 15) | ((n >> 
 
 // Memory operations a wave has issued after the loads of stage st when step st waits for them: the loads of the
 // (at most two) stages after it and the key stores of the steps since they were issued (6 loads per stage: 4 code
-// rows of 1 KB and 2 scale rows of 256 bytes; 1 store per step).
-__host__ __device__ constexpr int f4r_wait_count(int st, int nst) {
+// rows of 1 KB and 2 scale rows of 256 bytes; nr stores per step, one per query row).
+__host__ __device__ constexpr int f4r_wait_count(int st, int nst, int nr) {
   const int later = (st + 2 < nst - 1 ? st + 2 : nst - 1) - st;
   const int stores = st - (st - 3 > 0 ? st - 3 : 0);
-  return 6 * later + stores;
+  return 6 * later + nr * stores;
 }
 
 // Calls f(integral_constant<int, ST>) for ST = ST0 .. NST - 1 in order (a loop whose index is a constant).
@@ -510,38 +513,47 @@ __device__ __forceinline__ void unroll_steps(F& f) {
   }
 }
 
-
-template <int NST>
+// NR query rows (consecutive rows of one sequence) per workgroup: every key stage is loaded once and scored for each
+// row, its key operands read from LDS once for all of them.
+template <int NST, int NR>
 __global__ __launch_bounds__(kF4rWaves * 64) void idx_score_decode_fp4_ring(IdxArgs a) {
 #pragma clang fp contract(off)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int col = lane & 31, hh = lane >> 5;
-  const int qrow = blockIdx.y, b = qrow / a.Sq;  // query row b * Sq + r
-  const int nvis = nvis_of(seq_position(a.seq_pos, a.q_start, b) + (qrow - b * a.Sq), a.m, a.N);
+  const int qrow0 = blockIdx.y * NR, b = qrow0 / a.Sq;  // query rows qrow0 .. qrow0 + NR - 1, all of sequence b
+  const long long pos0 = seq_position(a.seq_pos, a.q_start, b) + (qrow0 - b * a.Sq);
+  int nv[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) nv[r] = nvis_of(pos0 + r, a.m, a.N);
+  const int nvis = nv[NR - 1];  // the group's last row sees the most entries
   const int k0 = blockIdx.x * (NST * kF4rStage);
   const int k1 = min(k0 + NST * kF4rStage, nvis);
   if (k0 >= k1) return;  // block-uniform
   const bool hist = a.sel_state != nullptr;
-  for (int i = threadIdx.x; i < kSelBins; i += blockDim.x) f4r_hist[i] = 0;
+  for (int i = threadIdx.x; i < NR * kSelBins; i += blockDim.x) f4r_hist[i] = 0;
 
-  // query: head tile T = heads 32 T .. 32 T + 31, lane head 32 T + col; chunks hh and 2 + hh of its code row and the
+  // queries: head tile T = heads 32 T .. 32 T + 31, lane head 32 T + col; chunks hh and 2 + hh of its code row and the
   // matching scale bytes 2 hh, 2 hh + 1, 4 + 2 hh, 5 + 2 hh.  The raw loads go first and the operands are built after
   // the ring's first loads are issued, so that nothing waits for the queries before the ring starts.
-  uint4 qraw[2][2];
-  uint2 sraw[2];
-  float wv[2][16];
+  uint4 qraw[NR][2][2];
+  uint2 sraw[NR][2];
+  float wv[NR][2][16];
 #pragma unroll
-  for (int T = 0; T < 2; ++T) {
-    const long long row = (long long)qrow * 64 + 32 * T + col;
+  for (int r = 0; r < NR; ++r)
 #pragma unroll
-    for (int i = 0; i < 2; ++i) qraw[T][i] = *(const uint4*)((const uint8_t*)a.q.data + row * 64 + 16 * (2 * i + hh));
-    sraw[T] = *(const uint2*)((const uint8_t*)a.q.scale + row * 8);
+    for (int T = 0; T < 2; ++T) {
+      const long long row = (long long)(qrow0 + r) * 64 + 32 * T + col;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) wv[T][k] = a.w[(long long)qrow * 64 + 32 * T + 8 * (k >> 2) + 4 * hh + (k & 3)];
-  }
+      for (int i = 0; i < 2; ++i)
+        qraw[r][T][i] = *(const uint4*)((const uint8_t*)a.q.data + row * 64 + 16 * (2 * i + hh));
+      sraw[r][T] = *(const uint2*)((const uint8_t*)a.q.scale + row * 8);
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        wv[r][T][k] = a.w[(long long)(qrow0 + r) * 64 + 32 * T + 8 * (k >> 2) + 4 * hh + (k & 3)];
+    }
   __builtin_amdgcn_sched_barrier(0);
-  i32x8_t qop[2][2][2];
-  int qs[2][2][2];
+  i32x8_t qop[NR][2][2][2];
+  int qs[NR][2][2][2];
 
   // buffer descriptors over the workgroup's own keys [k0, k1) of a dense cache (offsets stay small whatever the cache
   // size, and the range check covers exactly the keys the workgroup may read), or over the whole pool of a paged one
@@ -590,15 +602,13 @@ __global__ __launch_bounds__(kF4rWaves * 64) void idx_score_decode_fp4_ring(IdxA
                                                row * 8 + 4 * (lane & 1), 0, 0, 0);
     }
   };
-  // 64 x 32 dots of the wave's key tile u (keys 64 w + 32 u + col of stage slot S)
-  auto dots = [&](auto SC, int u, f32x16_t (&acc)[2]) {
+  // key operands of the wave's key tile u (keys 64 w + 32 u + col of stage slot S)
+  auto kops = [&](auto SC, int u, i32x8_t (&kop)[2], int (&ks)[2][2]) {
     constexpr int S = decltype(SC)::value;
     const int kl = 64 * wave + 32 * u + col;
     const uint8_t* cb = f4r_codes<S>() + kl * 64;
     const int sw = (kl >> 2) & 3;
     const uint2 s8 = *(const uint2*)(f4r_scales<S>() + kl * 8);
-    i32x8_t kop[2];
-    int ks[2][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const u32x4_t kc = *(const u32x4_t*)(cb + 16 * ((2 * i + hh) ^ sw));
@@ -607,6 +617,9 @@ __global__ __launch_bounds__(kF4rWaves * 64) void idx_score_decode_fp4_ring(IdxA
       ks[i][0] = (int)((sword >> (16 * hh)) & 255u);
       ks[i][1] = (int)((sword >> (16 * hh + 8)) & 255u);
     }
+  };
+  // 64 x 32 dots of query row r against one key tile
+  auto dots = [&](const i32x8_t (&kop)[2], const int (&ks)[2][2], int r, f32x16_t (&acc)[2]) {
 #pragma unroll
     for (int T = 0; T < 2; ++T) {
       acc[T] = f32x16_t{};
@@ -614,27 +627,9 @@ __global__ __launch_bounds__(kF4rWaves * 64) void idx_score_decode_fp4_ring(IdxA
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-          acc[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qop[T][i][h], kop[i], acc[T], 4, 4, 0,
-                                                                   qs[T][i][h], 0, ks[i][h]);
+          acc[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qop[r][T][i][h], kop[i], acc[T], 4, 4, 0,
+                                                                   qs[r][T][i][h], 0, ks[i][h]);
     }
-  };
-  // lane (col, hh) returns the key of tile u's key col (both halves hold it)
-  auto score = [&](auto SC, int st) -> uint2 {
-    f32x16_t acc0[2], acc1[2];
-    dots(SC, 0, acc0);
-    __builtin_amdgcn_sched_barrier(0);
-    dots(SC, 1, acc1);
-    const float s0 = head_tree32(acc0, wv);
-    // the second tile's MFMAs run while the first tile's tree issues between them
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    const float s1 = head_tree32(acc1, wv);
-    (void)st;
-    return uint2{score_key(s0), score_key(s1)};
   };
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
@@ -645,42 +640,71 @@ __global__ __launch_bounds__(kF4rWaves * 64) void idx_score_decode_fp4_ring(IdxA
   if constexpr (NST > 2) issue(S2{}, 2);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int T = 0; T < 2; ++T)
+  for (int r = 0; r < NR; ++r)
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const uint4 c = qraw[T][i];
-      qop[T][i][0] = i32x8_t{(int)c.x, (int)c.y, 0, 0, 0, 0, 0, 0};
-      qop[T][i][1] = i32x8_t{0, 0, (int)c.z, (int)c.w, 0, 0, 0, 0};
-      const uint32_t sword = i == 0 ? sraw[T].x : sraw[T].y;
-      qs[T][i][0] = (int)((sword >> (16 * hh)) & 255u);
-      qs[T][i][1] = (int)((sword >> (16 * hh + 8)) & 255u);
-    }
+    for (int T = 0; T < 2; ++T)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const uint4 c = qraw[r][T][i];
+        qop[r][T][i][0] = i32x8_t{(int)c.x, (int)c.y, 0, 0, 0, 0, 0, 0};
+        qop[r][T][i][1] = i32x8_t{0, 0, (int)c.z, (int)c.w, 0, 0, 0, 0};
+        const uint32_t sword = i == 0 ? sraw[r][T].x : sraw[r][T].y;
+        qs[r][T][i][0] = (int)((sword >> (16 * hh)) & 255u);
+        qs[r][T][i][1] = (int)((sword >> (16 * hh + 8)) & 255u);
+      }
 
   // Stage st sits in slot st % 4.  A wave loads exactly the keys it scores, so the ring needs no barrier: step st
   // waits for this wave's own loads of stage st, starts stage st + 3 in the slot this wave finished with in step
-  // st - 1, scores and stores.  The histogram counts wait until the ring is drained: an LDS atomic while ring loads
-  // are in flight would make the compiler wait for all of them.
-  uint2 kept[NST];
+  // st - 1, scores it for every row and stores.  The histogram counts wait until the ring is drained: an LDS atomic
+  // while ring loads are in flight would make the compiler wait for all of them.
+  uint2 kept[NR][NST];  // lane (col, hh): the keys of tile 0 and tile 1's key col, per row and stage
   auto step = [&](auto STC) {
     constexpr int st = decltype(STC)::value;
-    __builtin_amdgcn_s_waitcnt(vm_wait_imm(f4r_wait_count(st, NST)));
+    using SC = std::integral_constant<int, st % 4>;
+    __builtin_amdgcn_s_waitcnt(vm_wait_imm(f4r_wait_count(st, NST, NR)));
     asm volatile("" ::: "memory");
     if constexpr (st + 3 < NST) issue(std::integral_constant<int, (st + 3) % 4>{}, st + 3);
-    kept[st] = score(std::integral_constant<int, st % 4>{}, st);
-    // lane (col, hh) stores tile hh's key col: 64 keys per store
+    i32x8_t kop0[2], kop1[2];
+    int ks0[2][2], ks1[2][2];
+    kops(SC{}, 0, kop0, ks0);
+    kops(SC{}, 1, kop1, ks1);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      f32x16_t acc0[2], acc1[2];
+      dots(kop0, ks0, r, acc0);
+      __builtin_amdgcn_sched_barrier(0);
+      dots(kop1, ks1, r, acc1);
+      const float s0 = head_tree32(acc0, wv[r]);
+      // the second tile's MFMAs run while the first tile's tree issues between them
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      const float s1 = head_tree32(acc1, wv[r]);
+      kept[r][st] = uint2{score_key(s0), score_key(s1)};
+    }
+    // lane (col, hh) stores tile hh's key col: 64 keys per store and row
     const int e = k0 + st * kF4rStage + 64 * wave + 32 * hh + col;
-    a.keys[(long long)qrow * a.N + min(e, k1 - 1)] = hh ? kept[st].y : kept[st].x;
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+      a.keys[(long long)(qrow0 + r) * a.N + min(e, k1 - 1)] = hh ? kept[r][st].y : kept[r][st].x;
   };
   unroll_steps<0, NST>(step);
   if (hist) {
-    __syncthreads();  // every wave has zeroed its part of the histogram
+    __syncthreads();  // every wave has zeroed its part of the histograms
 #pragma unroll
-    for (int st = 0; st < NST; ++st) {
-      const int e = k0 + st * kF4rStage + 64 * wave + 32 * hh + col;
-      if (e < k1) atomicAdd(&f4r_hist[(hh ? kept[st].y : kept[st].x) >> 21], 1);
-    }
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+      for (int st = 0; st < NST; ++st) {
+        const int e = k0 + st * kF4rStage + 64 * wave + 32 * hh + col;
+        if (e < nv[r]) atomicAdd(&f4r_hist[r * kSelBins + ((hh ? kept[r][st].y : kept[r][st].x) >> 21)], 1);
+      }
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+      flush_hist(f4r_hist + r * kSelBins, a.sel_state + (long long)(qrow0 + r) * kSelStateInts);
   }
-  if (hist) flush_hist(f4r_hist, a.sel_state + (long long)qrow * kSelStateInts);
 }
 
 // key ranges of a decode launch: a multiple of the eight XCDs when several rows share them
@@ -705,17 +729,26 @@ hipError_t launch_indexer_scores(const IdxArgs& a, hipStream_t st, hipEvent_t eb
   if (indexer_uses_decode_kernel(a.B, a.Sq, a.HI, a.DI, a.N, a.q.format, a.k.format)) {
     const bool fp4 = a.q.format == LCA_FP4;
     if (fp4) {
-      // one workgroup per CU where the context allows: the most stages per workgroup that still leave 256
-      const long long rows = (long long)a.B * a.Sq;
+      // one workgroup per CU where the context allows: the most stages per workgroup that still leave 256; two query
+      // rows of a sequence per workgroup when the rows per sequence are even (each key stage loaded once for both)
+      const int nr = a.Sq % 2 == 0 ? 2 : 1;
+      const long long groups = (long long)a.B * a.Sq / nr;
       int nst = 8;
-      while (nst > 1 && rows * ((nvis_max + nst * kF4rStage - 1) / (nst * kF4rStage)) < 256) nst >>= 1;
-      const dim3 grid((unsigned)decode_grid_x((nvis_max + nst * kF4rStage - 1) / (nst * kF4rStage), a.Sq),
-                      (unsigned)rows);
+      while (nst > 1 && groups * ((nvis_max + nst * kF4rStage - 1) / (nst * kF4rStage)) < 256) nst >>= 1;
+      const dim3 grid((unsigned)decode_grid_x((nvis_max + nst * kF4rStage - 1) / (nst * kF4rStage), a.Sq / nr),
+                      (unsigned)groups);
       const dim3 block(kF4rWaves * 64);
-      if (nst == 8) hipExtLaunchKernelGGL(idx_score_decode_fp4_ring<8>, grid, block, 0, st, eb, ee, 0, a);
-      else if (nst == 4) hipExtLaunchKernelGGL(idx_score_decode_fp4_ring<4>, grid, block, 0, st, eb, ee, 0, a);
-      else if (nst == 2) hipExtLaunchKernelGGL(idx_score_decode_fp4_ring<2>, grid, block, 0, st, eb, ee, 0, a);
-      else hipExtLaunchKernelGGL(idx_score_decode_fp4_ring<1>, grid, block, 0, st, eb, ee, 0, a);
+      if (nr == 2) {
+        if (nst == 8) hipExtLaunchKernelGGL((idx_score_decode_fp4_ring<8, 2>), grid, block, 0, st, eb, ee, 0, a);
+        else if (nst == 4) hipExtLaunchKernelGGL((idx_score_decode_fp4_ring<4, 2>), grid, block, 0, st, eb, ee, 0, a);
+        else if (nst == 2) hipExtLaunchKernelGGL((idx_score_decode_fp4_ring<2, 2>), grid, block, 0, st, eb, ee, 0, a);
+        else hipExtLaunchKernelGGL((idx_score_decode_fp4_ring<1, 2>), grid, block, 0, st, eb, ee, 0, a);
+      } else {
+        if (nst == 8) hipExtLaunchKernelGGL((idx_score_decode_fp4_ring<8, 1>), grid, block, 0, st, eb, ee, 0, a);
+        else if (nst == 4) hipExtLaunchKernelGGL((idx_score_decode_fp4_ring<4, 1>), grid, block, 0, st, eb, ee, 0, a);
+        else if (nst == 2) hipExtLaunchKernelGGL((idx_score_decode_fp4_ring<2, 1>), grid, block, 0, st, eb, ee, 0, a);
+        else hipExtLaunchKernelGGL((idx_score_decode_fp4_ring<1, 1>), grid, block, 0, st, eb, ee, 0, a);
+      }
       return hipGetLastError();
     }
     // a fixed key range per workgroup (NST stages of 4 waves x KPW keys), the grid grows with the context; fewer
