@@ -231,6 +231,63 @@ def test_hca_cache_build_1m_sampled():
     del C, Z
 
 
+def test_hca_cache_build_1m_constant_values():
+    """Compression weights sum to one, so a context whose values are constant per channel compresses into entries
+    equal to those constants, over the whole 1M-token build: every entry of every sequence, the first block
+    included, with the drawn logits and position bias.  The constants are powers of two (every product and sum then
+    scales exactly) or 3, 6 and 1.5 (rounding leaves them far from a bf16 boundary), so each of the 8 x 8192 x 512
+    codes is checked bit for bit -- an invariant that needs no oracle."""
+    w = gen.WORKLOADS["hca_decode_1m_bf16"]
+    C, Z, Ba = gen.hca_build_streams_device(w, "cuda")
+    del C
+    vals = torch.tensor([1.0, -2.0, 0.5, 3.0, -0.25, 6.0, 1.5, -1.0], dtype=torch.float32, device="cuda")
+    chan = vals.repeat(w.D // vals.numel())
+    Cc = chan.expand(w.B, w.n_ctx, w.D).contiguous()
+    out = lca.CacheTensor("bf16", w.B, w.N, w.D)
+    lca.kv_compress(Cc, None, Z, None, torch.from_numpy(Ba).cuda(), None, None, None, w.B, w.n_ctx, w.D, w.m, False, 0,
+                    out.desc())
+    torch.cuda.synchronize()
+    del Cc, Z
+    exp_bits = torch.from_numpy(gen.bf16_bits(chan.cpu().numpy()).astype(np.int16)).cuda()
+    got = out.data.view(w.B, w.N, w.D)
+    bad = int((got != exp_bits).sum().item())
+    assert bad == 0, "%d of %d codes differ from the constants" % (bad, got.numel())
+
+
+def test_hca_build_then_decode_1m_chained():
+    """The HCA path end to end at full size, stage-isolated: the 1M-token cache built on the GPU (kv_compress over
+    8 x 2^20 tokens), then hca_attn over it for every sequence, against the oracle attending the GPU-written cache
+    (read back) with the same window, queries and sink."""
+    w = gen.WORKLOADS["hca_decode_1m_bf16"]
+    inp = gen.decode_inputs(w)
+    B, N, H, D = w.B, w.N, w.H, w.D
+    C, Z, Ba = gen.hca_build_streams_device(w, "cuda")
+    comp = lca.CacheTensor("bf16", B, N, D)
+    lca.kv_compress(C, None, Z, None, torch.from_numpy(Ba).cuda(), None, None, None, B, w.n_ctx, D, w.m, False, 0,
+                    comp.desc())
+    torch.cuda.synchronize()
+    del C, Z
+    raw = steps.make_cache("bf16", B, w.window, D, 0, inp["window_kv"])
+    q = torch.from_numpy(_bf16(inp["q"]).view(np.int16)).cuda()
+    sink = torch.from_numpy(inp["sink"].astype(np.float32)).cuda()
+    out = torch.empty((B, 1, H, D), dtype=torch.int16, device="cuda")
+    lse = torch.empty((B, 1, H), dtype=torch.float32, device="cuda")
+    ws_bytes = lca.hca_attn_workspace_size(B, 1, H, D, w.window + N)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+    raw_start = w.n_ctx - w.window + 1
+    lca.hca_attn(q, lca.LCA_BF16, comp.desc(), N, w.m, raw.desc(), raw_start, w.window, sink, B, 1, H, D, w.window,
+                 w.scale, w.n_ctx, out, lca.LCA_BF16, lse, ws, ws_bytes)
+    torch.cuda.synchronize()
+    cc = orc.plain_cache(comp.data.view(B, N, D).cpu().numpy().view(np.uint16), "bf16")
+    rc = orc.plain_cache(_bf16(inp["window_kv"]), "bf16")
+    cc["cap"], rc["cap"] = N, w.window
+    o_ref, l_ref = orc.attn(orc.plain_cache(_bf16(inp["q"]), "bf16"), cc, N, rc, raw_start, w.window, None, 0, w.m,
+                            inp["sink"], B, 1, H, D, w.window, w.scale, w.n_ctx)
+    o = bf16_to_f64(out.cpu().numpy().view(np.uint16)).reshape(B, 1, H, D)
+    assert row_rel_err(o, o_ref) <= 1e-2
+    np.testing.assert_allclose(lse.cpu().numpy(), l_ref, rtol=1e-3, atol=1e-3)
+
+
 # ------------------------------------------------------------------------------------------------------
 def test_csa_prefill_64k_chunk4k_bf16_sampled():
     """Prefill chunk: 4096 new tokens after 65536 cached ones; the GPU runs the whole chunk, the oracle checks the new
