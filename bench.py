@@ -12,8 +12,8 @@ the median over 20 windows of replays, each bracketed by HIP events.  The append
 second stream, forked once before the first step and joined once after the last.  The streamed cache (indexer keys; the latent
 cache for HCA) is kept in enough independent copies that the replays stream at least --stream-gb GB of distinct
 addresses, so no step is served from the 256 MB last-level cache; a warm line (one copy, every step on the same
-addresses) is reported beside it.  The dominant kernel is timed with HIP events around each of its launches in
-eager steps queued back to back right after the replays.
+addresses) is reported beside it.  The dominant kernel is timed by HIP events that each of its launches stamps with
+its own start and end, in eager steps queued back to back right after the replays.
 
 Prints one JSON line: whole-step throughput (tokens/s = sequences decoded per second), the step's algorithmic HBM
 rate, the roofline of the dominant kernel, a measured read-stream rate, and the CPU oracle timed on a bounded sample
@@ -292,8 +292,8 @@ def time_steps(step, torch, steps_mod, n_distinct: int, steps: int, warmup: int,
     (steps_mod.run_many).
 
     Returns (median ms per step over the windows, steps timed, per-launch ms of the dominant kernel, how it was
-    timed).  The dominant kernel is timed by HIP events around each of its launches (the library's hook, recorded
-    on the stream the kernel runs on) in eager steps right after the replays, one per cache copy."""
+    timed).  The dominant kernel is timed by HIP events that each of its launches stamps with its own start and end
+    (the library's hook) in eager steps right after the replays, one per cache copy."""
     side = torch.cuda.Stream()  # default priority, like every stream here
     order = [0 if same_copy else c for c in range(n_distinct)]
     # eager warm-up outside the graph (first-use setup such as kernel attributes happens here)

@@ -93,7 +93,8 @@ int hip_status(hipError_t e) {
   return e == hipSuccess ? LCA_OK : LCA_ERR_HIP;
 }
 
-// profiling hooks (per host thread): events recorded around the indexer scoring kernel and the attention kernel
+// profiling hooks (per host thread): events stamped with the start and end of the indexer scoring kernel and of the
+// attention kernels
 thread_local hipEvent_t t_ev_begin = nullptr, t_ev_end = nullptr;
 thread_local hipEvent_t t_attn_ev_begin = nullptr, t_attn_ev_end = nullptr;
 

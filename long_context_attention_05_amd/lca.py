@@ -223,12 +223,13 @@ def indexer_score_topk_workspace_size(B: int, Sq: int, N: int, k: int) -> int:
 
 
 def lca_set_score_events(ev_begin, ev_end):
-    """hipEvent_t handles (ints) recorded around the indexer scoring kernel; None, None to stop."""
+    """hipEvent_t handles (ints) stamped with the indexer scoring kernel's start and end; None, None to stop."""
     _lib.lca_set_score_events(ev_begin, ev_end)
 
 
 def lca_set_attn_events(ev_begin, ev_end):
-    """hipEvent_t handles (ints) recorded around the attention kernel (not the split merge); None, None to stop."""
+    """hipEvent_t handles (ints) stamped with the attention kernels' start and end (not the split merge); None, None
+    to stop."""
     _lib.lca_set_attn_events(ev_begin, ev_end)
 
 
