@@ -10,9 +10,12 @@
 // stream is read once (decode).  fp4 keys/queries are widened to bf16 in registers, which is exact (a 2-bit
 // significand times a power of two).  Other shapes and fp32 inputs use a vector-ALU kernel.
 //
-// Both kernels reduce the heads the same way so that exact dots give bit-identical scores:
-//   p[h] = fl32(w[h] * max(0, d[h])), then a halving tree a[j] += a[j + L/2] over L = 64, 32, ..., 2
-// (zero padded to a power of two).  Scores are written to the workspace as order-preserving uint32 keys.
+// Every kernel reduces the heads in the same (canonical) order so that exact dots give bit-identical scores: with
+// r[h] = max(0, d[h]) and the heads zero padded to a power of two P >= 16, sixteen chains c_j = fl32(w_j r_j)
+// followed by fused multiply-adds of heads j + 16, j + 32, ..., then a halving tree c_j += c_(j + L/2) over
+// L = 16, 8, 4, 2 (fewer than 16 heads: the products, then the halving tree).  Most of the work is then fused
+// multiply-adds within one lane of an MFMA result.  Scores are written to the workspace as order-preserving uint32
+// keys.
 #include "lca_device.h"
 #include "lca_internal.h"
 
@@ -62,15 +65,28 @@ __global__ __launch_bounds__(256) void idx_score_simt(IdxArgs a) {
   for (int h = threadIdx.x / kSimtTile; h < HI; h += blockDim.x / kSimtTile) {
     float d = 0.0f;
     for (int j = 0; j < DI; ++j) d = fmaf(q_s[h * DI + j], k_s[e * 129 + j], d);
-    p_s[e * 65 + h] = wr[h] * fmaxf(d, 0.0f);
+    p_s[e * 65 + h] = fmaxf(d, 0.0f);
   }
   __syncthreads();
+  // the canonical head sum: with the heads padded to a power of two P, sixteen chains c_j = w_j r_j, then fused
+  // multiply-adds of heads j + 16, j + 32, ... (P >= 16), or the P products (P < 16); then a halving tree
   if (threadIdx.x < kSimtTile && e0 + threadIdx.x < nvis) {
     int P = 1;
     while (P < HI) P <<= 1;
+    const float* rr = p_s + threadIdx.x * 65;
     float v[64];
-    for (int h = 0; h < P; ++h) v[h] = (h < HI) ? p_s[threadIdx.x * 65 + h] : 0.0f;
-    for (int L = P; L > 1; L >>= 1)
+    int L = P;
+    if (P >= 16) {
+      for (int j = 0; j < 16; ++j) {
+        float c = (j < HI) ? wr[j] * rr[j] : 0.0f;
+        for (int h = j + 16; h < HI; h += 16) c = __builtin_fmaf(wr[h], rr[h], c);
+        v[j] = c;
+      }
+      L = 16;
+    } else {
+      for (int h = 0; h < P; ++h) v[h] = (h < HI) ? wr[h] * rr[h] : 0.0f;
+    }
+    for (; L > 1; L >>= 1)
       for (int j = 0; j < L / 2; ++j) v[j] = v[j] + v[j + L / 2];
     a.keys[((long long)b * a.Sq + r) * a.N + e0 + threadIdx.x] = score_key(v[0]);
   }
@@ -136,24 +152,33 @@ __device__ __forceinline__ void load_qblock(const IdxArgs& a, long long qrow0, u
   }
 }
 
-// Score of key l % 32 from the 32x32 results of the two head tiles (every lane of the key returns it).
+// Score of key l % 32 from the 32x32 results of the two head tiles (every lane of the key returns it), in the
+// canonical order: chain j (heads j, j + 16, j + 32, j + 48) is c_j = w r, then three fused multiply-adds; then
+// the halving tree c_j + c_(j+8), + c_(j+4), + c_(j+2), + c_(j+1).  Register k of tile T holds head
+// 32 T + 8 (k / 4) + 4 hh + k % 4, so lane half hh holds the whole chains j = 4 hh + r (registers r, 8 + r of both
+// tiles) and j = 8 + 4 hh + r (registers 4 + r, 12 + r): the chains and the +8 step run in lane, +4 across the lane
+// halves, +2 across them again after the scattered swap, +1 in lane.
 __device__ __forceinline__ float head_tree32(const f32x16_t (&acc)[2], const float (&wv)[2][16]) {
-  float a[16];
+  auto relu = [&](int T, int k) { return __int_as_float(max(__float_as_int(acc[T][k]), 0)); };
+  float t[4];
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    const float p0 = wv[0][k] * __int_as_float(max(__float_as_int(acc[0][k]), 0));
-    const float p1 = wv[1][k] * __int_as_float(max(__float_as_int(acc[1][k]), 0));
-    a[k] = p0 + p1;  // h+32
+  for (int r = 0; r < 4; ++r) {
+    float ca = wv[0][r] * relu(0, r);
+    ca = __builtin_fmaf(wv[0][8 + r], relu(0, 8 + r), ca);
+    ca = __builtin_fmaf(wv[1][r], relu(1, r), ca);
+    ca = __builtin_fmaf(wv[1][8 + r], relu(1, 8 + r), ca);
+    float cb = wv[0][4 + r] * relu(0, 4 + r);
+    cb = __builtin_fmaf(wv[0][12 + r], relu(0, 12 + r), cb);
+    cb = __builtin_fmaf(wv[1][4 + r], relu(1, 4 + r), cb);
+    cb = __builtin_fmaf(wv[1][12 + r], relu(1, 12 + r), cb);
+    t[r] = ca + cb;  // +8
   }
-  float c[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) c[r] = (a[r] + a[r + 8]) + (a[r + 4] + a[r + 12]);  // h+16, then h+8
-  // h+4 across the lane halves, scattered: the low half keeps head classes 0 and 1, the high half 2 and 3
-  const auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(c[0]), __float_as_uint(c[2]), false, false);
-  const auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(c[1]), __float_as_uint(c[3]), false, false);
-  const float d02 = __uint_as_float(s02[0]) + __uint_as_float(s02[1]);
-  const float d13 = __uint_as_float(s13[0]) + __uint_as_float(s13[1]);
-  return xor32_sum(d02) + xor32_sum(d13);  // h+2 across the halves, then h+1
+  // +4 across the lane halves, scattered: the low half keeps classes 0 and 1, the high half 2 and 3
+  const auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(t[0]), __float_as_uint(t[2]), false, false);
+  const auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(t[1]), __float_as_uint(t[3]), false, false);
+  const float u02 = __uint_as_float(s02[0]) + __uint_as_float(s02[1]);
+  const float u13 = __uint_as_float(s13[0]) + __uint_as_float(s13[1]);
+  return xor32_sum(u02) + xor32_sum(u13);  // +2 across the halves, then +1
 }
 
 template <int FMT>
@@ -230,7 +255,7 @@ __global__ __launch_bounds__(256) void idx_score_mfma(IdxArgs a, int qpb) {
             acc[T][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kb[u][s], acc[T][u], 0, 0, 0);
         }
       }
-      // epilogue: head h = 32T + 8(x/4) + 4g + (x%4) for register x; fixed halving tree over h
+      // epilogue: head h = 32T + 8(x/4) + 4g + (x%4) for register x; the canonical reduction over h
       float wv[2][16];
 #pragma unroll
       for (int T = 0; T < 2; ++T)
@@ -263,32 +288,33 @@ __global__ __launch_bounds__(256) void idx_score_mfma(IdxArgs a, int qpb) {
 // addresses clamp to its last key (loaded, scored, never written).
 //
 // Accumulator layout of both 16x16 MFMAs: lane l, register r holds head 16 T + 4 (l / 16) + r (M-tile T) for key
-// l % 16.  The fixed halving tree over the 64 heads is then: h+32 (T, T+2) and h+16 (T, T+1) in-lane, h+8 (lanes
-// l, l ^ 32) and h+4 (l, l ^ 16) across lanes, h+2 and h+1 in-lane.
+// l % 16.  The canonical reduction over the 64 heads is then: the chain of head j = 4 (l / 16) + r over T in-lane,
+// +8 (lanes l, l ^ 32) and +4 (l, l ^ 16) across lanes, +2 and +1 in-lane.
 //
 // With a row histogram to fill (decode select), each workgroup counts its keys' bits [31:21] in LDS and adds the
 // counts into the row's histogram, zeroed before the launch.  The select that follows reads it instead of making
 // its own first pass over the keys.
 
-// In-lane part of the tree for one 16-key group: v[r] = ((w relu)(T=0) + (T=2)) + ((T=1) + (T=3)) for the lane's
-// heads 4 (l / 16) + r (+ 16 T).  ReLU is one integer max of the bit pattern with 0: non-negative floats order like
-// their bit patterns and every negative one (-0 included) has the sign bit set, so the result equals max(x, 0)
-// without the float max's NaN canonicalization.
+// In-lane part of the tree for one 16-key group: the canonical chain of head j = 4 (l / 16) + r over heads j + 16 T,
+// v[r] = fma(w r (T=3), fma(w r (T=2), fma(w r (T=1), w r (T=0)))).  ReLU is one integer max of the bit pattern
+// with 0: non-negative floats order like their bit patterns and every negative one (-0 included) has the sign bit
+// set, so the result equals max(x, 0) without the float max's NaN canonicalization.
 __device__ __forceinline__ void head_partial(const f32x4_t (&acc)[4], const float (&wv)[4][4], float (&v)[4]) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    float p[4];
+    float c = wv[0][r] * __int_as_float(max(__float_as_int(acc[0][r]), 0));
 #pragma unroll
-    for (int T = 0; T < 4; ++T) p[T] = wv[T][r] * __int_as_float(max(__float_as_int(acc[T][r]), 0));
-    v[r] = (p[0] + p[2]) + (p[1] + p[3]);
+    for (int T = 1; T < 4; ++T) c = __builtin_fmaf(wv[T][r], __int_as_float(max(__float_as_int(acc[T][r]), 0)), c);
+    v[r] = c;
   }
 }
 
-// Cross-lane part for four groups at once, as a reduce-scatter: h+8 pairs lane rows g and g + 2 (lanes l, l ^ 32),
-// h+4 pairs rows g and g + 1 (l, l ^ 16), then h+2 and h+1 in-lane.  permlane32_swap(A, B) returns (A.lo, B.lo) and
+// Cross-lane part for four groups at once, as a reduce-scatter over the chains: +8 pairs lane rows g and g + 2
+// (lanes l, l ^ 32), +4 pairs rows g and g + 1 (l, l ^ 16), then +2 and +1 in-lane.  permlane32_swap(A, B) returns (A.lo, B.lo) and
 // (A.hi, B.hi), so one swap and one add leave group 0 (2)'s pair sums in the low (high) half; permlane16_swap does
 // the same for rows 0/1 and 2/3.  Row g of the wave ends with group g's four partial sums, and the lane returns the
-// score of group g, key l % 16.  The pairs are those of the fixed halving tree (fp32 addition is commutative).
+// score of group g, key l % 16.  The pairs are those of the canonical halving tree over the chains (fp32
+// addition is commutative).
 __device__ __forceinline__ float head_cross4(const float (&v)[4][4]) {
   float s02[4], s13[4], t[4];
 #pragma unroll
@@ -455,8 +481,8 @@ typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8_t;
 // (2 head tiles x 2 chunk pairs x 2 groups) give the 64 x 32 dots.  Products of fp4 values and their block sums are
 // exact, scaled by powers of two, so the per-head dots equal the exact ones whenever they fit fp32 -- the fixed
 // head-reduction order then makes the scores bit-reproducible.  Lane l, register k of the 32x32 result holds head
-// 32 T + 8 (k / 4) + 4 hh + k % 4 for key l % 32: the tree's h+32, h+16, h+8 steps run in lane, h+4 and h+2 across
-// the lane halves, h+1 in lane -- the same pairs as the 16x16 kernels.
+// 32 T + 8 (k / 4) + 4 hh + k % 4 for key l % 32: the chains and the +8 step run in lane, +4 and +2 across the lane
+// halves, +1 in lane -- the same pairs as the 16x16 kernels.
 constexpr int kF4rWaves = 8;
 constexpr int kF4rStage = 64 * kF4rWaves;  // keys per stage
 constexpr int kF4rCodeB = kF4rStage * 64;  // 32 KB
@@ -553,7 +579,7 @@ __global__ __launch_bounds__(kF4rWaves * 64) void idx_score_decode_fp4_ring(IdxA
     }
   __builtin_amdgcn_sched_barrier(0);
   i32x8_t qop[NR][2][2][2];
-  int qs[NR][2][2][2];
+  int qs[NR][2][2];  // bytes 0 and 1: the scales of the query groups kept in qop[..][0] and qop[..][1]
 
   // buffer descriptors over the workgroup's own keys [k0, k1) of a dense cache (offsets stay small whatever the cache
   // size, and the range check covers exactly the keys the workgroup may read), or over the whole pool of a paged one
@@ -602,8 +628,9 @@ __global__ __launch_bounds__(kF4rWaves * 64) void idx_score_decode_fp4_ring(IdxA
                                                row * 8 + 4 * (lane & 1), 0, 0, 0);
     }
   };
-  // key operands of the wave's key tile u (keys 64 w + 32 u + col of stage slot S)
-  auto kops = [&](auto SC, int u, i32x8_t (&kop)[2], int (&ks)[2][2]) {
+  // key operands of the wave's key tile u (keys 64 w + 32 u + col of stage slot S); ks[i] holds the scales of
+  // groups 2c, 2c + 1 (c = 2 i + hh) in its bytes 0 and 1, which the instruction's byte select picks
+  auto kops = [&](auto SC, int u, i32x8_t (&kop)[2], int (&ks)[2]) {
     constexpr int S = decltype(SC)::value;
     const int kl = 64 * wave + 32 * u + col;
     const uint8_t* cb = f4r_codes<S>() + kl * 64;
@@ -613,22 +640,21 @@ __global__ __launch_bounds__(kF4rWaves * 64) void idx_score_decode_fp4_ring(IdxA
     for (int i = 0; i < 2; ++i) {
       const u32x4_t kc = *(const u32x4_t*)(cb + 16 * ((2 * i + hh) ^ sw));
       kop[i] = i32x8_t{(int)kc[0], (int)kc[1], (int)kc[2], (int)kc[3], 0, 0, 0, 0};
-      const uint32_t sword = i == 0 ? s8.x : s8.y;  // bytes 4i .. 4i + 3
-      ks[i][0] = (int)((sword >> (16 * hh)) & 255u);
-      ks[i][1] = (int)((sword >> (16 * hh + 8)) & 255u);
+      ks[i] = (int)((i == 0 ? s8.x : s8.y) >> (16 * hh));  // bytes 4i .. 4i + 3 of the row
     }
   };
   // 64 x 32 dots of query row r against one key tile
-  auto dots = [&](const i32x8_t (&kop)[2], const int (&ks)[2][2], int r, f32x16_t (&acc)[2]) {
+  auto dots = [&](const i32x8_t (&kop)[2], const int (&ks)[2], int r, f32x16_t (&acc)[2]) {
 #pragma unroll
     for (int T = 0; T < 2; ++T) {
       acc[T] = f32x16_t{};
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          acc[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qop[r][T][i][h], kop[i], acc[T], 4, 4, 0,
-                                                                   qs[r][T][i][h], 0, ks[i][h]);
+      for (int i = 0; i < 2; ++i) {
+        acc[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qop[r][T][i][0], kop[i], acc[T], 4, 4, 0,
+                                                                 qs[r][T][i], 0, ks[i]);
+        acc[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qop[r][T][i][1], kop[i], acc[T], 4, 4, 1,
+                                                                 qs[r][T][i], 1, ks[i]);
+      }
     }
   };
   using S0 = std::integral_constant<int, 0>;
@@ -648,16 +674,14 @@ __global__ __launch_bounds__(kF4rWaves * 64) void idx_score_decode_fp4_ring(IdxA
         const uint4 c = qraw[r][T][i];
         qop[r][T][i][0] = i32x8_t{(int)c.x, (int)c.y, 0, 0, 0, 0, 0, 0};
         qop[r][T][i][1] = i32x8_t{0, 0, (int)c.z, (int)c.w, 0, 0, 0, 0};
-        const uint32_t sword = i == 0 ? sraw[r][T].x : sraw[r][T].y;
-        qs[r][T][i][0] = (int)((sword >> (16 * hh)) & 255u);
-        qs[r][T][i][1] = (int)((sword >> (16 * hh + 8)) & 255u);
+        qs[r][T][i] = (int)((i == 0 ? sraw[r][T].x : sraw[r][T].y) >> (16 * hh));
       }
 
   // Stage st sits in slot st % 4.  A wave loads exactly the keys it scores, so the ring needs no barrier: step st
   // waits for this wave's own loads of stage st, starts stage st + 3 in the slot this wave finished with in step
   // st - 1, scores it for every row and stores.  The histogram counts wait until the ring is drained: an LDS atomic
   // while ring loads are in flight would make the compiler wait for all of them.
-  uint2 kept[NR][NST];  // lane (col, hh): the keys of tile 0 and tile 1's key col, per row and stage
+  uint32_t kbin[NR][NST];  // lane (col, hh): the histogram bins of tile 0 (low half) and tile 1's key col
   auto step = [&](auto STC) {
     constexpr int st = decltype(STC)::value;
     using SC = std::integral_constant<int, st % 4>;
@@ -665,7 +689,7 @@ __global__ __launch_bounds__(kF4rWaves * 64) void idx_score_decode_fp4_ring(IdxA
     asm volatile("" ::: "memory");
     if constexpr (st + 3 < NST) issue(std::integral_constant<int, (st + 3) % 4>{}, st + 3);
     i32x8_t kop0[2], kop1[2];
-    int ks0[2][2], ks1[2][2];
+    int ks0[2], ks1[2];
     kops(SC{}, 0, kop0, ks0);
     kops(SC{}, 1, kop1, ks1);
 #pragma unroll
@@ -683,13 +707,12 @@ __global__ __launch_bounds__(kF4rWaves * 64) void idx_score_decode_fp4_ring(IdxA
       }
       __builtin_amdgcn_sched_barrier(0);
       const float s1 = head_tree32(acc1, wv[r]);
-      kept[r][st] = uint2{score_key(s0), score_key(s1)};
+      const uint32_t key0 = score_key(s0), key1 = score_key(s1);
+      kbin[r][st] = (key0 >> 21) | ((key1 >> 21) << 16);
+      // lane (col, hh) stores tile hh's key col: 64 keys per store and row
+      const int e = k0 + st * kF4rStage + 64 * wave + 32 * hh + col;
+      a.keys[(long long)(qrow0 + r) * a.N + min(e, k1 - 1)] = hh ? key1 : key0;
     }
-    // lane (col, hh) stores tile hh's key col: 64 keys per store and row
-    const int e = k0 + st * kF4rStage + 64 * wave + 32 * hh + col;
-#pragma unroll
-    for (int r = 0; r < NR; ++r)
-      a.keys[(long long)(qrow0 + r) * a.N + min(e, k1 - 1)] = hh ? kept[r][st].y : kept[r][st].x;
   };
   unroll_steps<0, NST>(step);
   if (hist) {
@@ -699,7 +722,7 @@ __global__ __launch_bounds__(kF4rWaves * 64) void idx_score_decode_fp4_ring(IdxA
 #pragma unroll
       for (int st = 0; st < NST; ++st) {
         const int e = k0 + st * kF4rStage + 64 * wave + 32 * hh + col;
-        if (e < nv[r]) atomicAdd(&f4r_hist[r * kSelBins + ((hh ? kept[r][st].y : kept[r][st].x) >> 21)], 1);
+        if (e < nv[r]) atomicAdd(&f4r_hist[r * kSelBins + (hh ? kbin[r][st] >> 16 : kbin[r][st] & 0xFFFFu)], 1);
       }
 #pragma unroll
     for (int r = 0; r < NR; ++r)

@@ -403,9 +403,14 @@ void orc_rope_rows(const double* x, long long rows, int c, int rd, const double*
  *
  * s64 receives the double score.  If s32 is non-NULL it receives the canonical fp32 score, defined
  * whenever every d[h] is computed exactly by fp32 arithmetic in any summation order (see
- * orc_dot_is_fp32_exact): p[h] = fl32(w[h] * max(0, fl32(d[h]))), then a halving tree over the heads padded
- * with zeros to a power of two P: level by level a[j] <- a[j] + a[j + L/2] for j < L/2, in fp32; a -0
- * result is written as +0.  *inexact counts the (row, entry) pairs with at least one head whose dot is
+ * orc_dot_is_fp32_exact).  With r[h] = max(0, fl32(d[h])) and the heads padded with zeros (w = r = 0) to a power
+ * of two P (the paper notes fix no summation order; this one is the library's, chosen so that most of the
+ * reduction is fused multiply-adds that stay within one lane of a matrix unit's result):
+ *   P >= 16: sixteen chains, c[j] = fl32(w[j] r[j]), then c[j] <- fma32(w[j + 16 m], r[j + 16 m], c[j]) for
+ *            m = 1 .. P/16 - 1 (one rounding per step), then a halving tree over c[0..15];
+ *   P < 16:  p[h] = fl32(w[h] r[h]), then a halving tree over p[0..P-1];
+ * a halving tree adds level by level a[j] <- a[j] + a[j + L/2] for j < L/2, in fp32.  A -0 result is written
+ * as +0.  *inexact counts the (row, entry) pairs with at least one head whose dot is
  * not certified exact; exact_out (optional, [B][nrows][N]) holds 1 for a certified pair, else 0.
  * abs_out (optional) receives sum_h |w[t,h]| * sum_d |q[t,h,d] * K[i,d]|, the scale of the fp32
  * rounding error of any summation order (used to certify near-ties).
@@ -484,9 +489,7 @@ void orc_indexer_scores(const orc_cache* q, const float* w, const orc_cache* K, 
           }
           if (s32) {
             float d32 = (float)d;
-            float rl = d32 > 0.0f ? d32 : 0.0f;
-            volatile float p = wr[h] * rl; /* fp32 multiply, rounded once */
-            a[h] = p;
+            a[h] = d32 > 0.0f ? d32 : 0.0f; /* r[h]; padded heads stay 0 */
           }
         }
         if (!certified) ++bad;
@@ -494,7 +497,24 @@ void orc_indexer_scores(const orc_cache* q, const float* w, const orc_cache* K, 
         s64[ob + i] = acc;
         if (abs_out) abs_out[ob + i] = aacc;
         if (s32) {
-          for (int L = P; L > 1; L >>= 1) {
+          int L = P;
+          if (P >= 16) {
+            for (int j = 0; j < 16; ++j) {
+              volatile float c = (j < HI ? wr[j] : 0.0f) * a[j]; /* fp32 multiply, rounded once */
+              for (int h = j + 16; h < P; h += 16) {
+                volatile float f = fmaf(h < HI ? wr[h] : 0.0f, a[h], c); /* fused: one rounding */
+                c = f;
+              }
+              a[j] = c;
+            }
+            L = 16;
+          } else {
+            for (int h = 0; h < P; ++h) {
+              volatile float pr = (h < HI ? wr[h] : 0.0f) * a[h];
+              a[h] = pr;
+            }
+          }
+          for (; L > 1; L >>= 1) {
             for (int j = 0; j < L / 2; ++j) {
               volatile float sum = a[j] + a[j + L / 2];
               a[j] = sum;

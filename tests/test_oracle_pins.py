@@ -1,8 +1,9 @@
 """Pins of the oracle's compression weights (position bias, softmax temperature, stream/block assignment), the
-sink's independence from the softmax scale, the fp32 exactness certificate of the indexer dots, and two
-metamorphic properties (power-of-two scaling, batch isolation).  Every expected value is a hand-derived closed
+sink's independence from the softmax scale, the fp32 exactness certificate of the indexer dots, the canonical fp32
+order of the indexer's head sum, and two metamorphic properties (power-of-two scaling, batch isolation).  Every expected value is a hand-derived closed
 form, brute force, or a property the definition fixes.  CPU only."""
 import math
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -453,3 +454,82 @@ def test_ragged_batch_equals_separate_calls():
         np.testing.assert_array_equal(l1[0], l_r[b])
     # the visible counts differ per sequence: floor((pos + r) / m)
     assert len(set(nv.tolist())) == B * Sq - 1 or len(set(nv.tolist())) >= B
+
+
+# ---------------------------------------------------------------------------------------------------
+# the canonical fp32 indexer score: the paper notes fix no summation order for Eq. 16's head sum; the library's
+# order is sixteen fused multiply-add chains over the heads j, j + 16, j + 32, ... then a halving tree over the
+# chains (a plain halving tree below 16 heads).  Emulated here with exact rationals and one fp32 rounding per step.
+# ---------------------------------------------------------------------------------------------------
+def _round_f32(x: Fraction) -> Fraction:
+    """x rounded to the nearest fp32 value, ties to even (subnormals included; no overflow in these tests)."""
+    if x == 0:
+        return Fraction(0)
+    sign, a = (-1 if x < 0 else 1), abs(x)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    quantum = Fraction(2) ** (max(e, -126) - 23)
+    n = a / quantum
+    fl = n.numerator // n.denominator
+    rem = n - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return sign * fl * quantum
+
+
+def _chained_sum(w, r):
+    P = len(r)
+    if P >= 16:
+        c = []
+        for j in range(16):
+            v = _round_f32(w[j] * r[j])
+            for h in range(j + 16, P, 16):
+                v = _round_f32(w[h] * r[h] + v)  # fused multiply-add: one rounding
+            c.append(v)
+    else:
+        c = [_round_f32(w[h] * r[h]) for h in range(P)]
+    while len(c) > 1:
+        half = len(c) // 2
+        c = [_round_f32(c[j] + c[j + half]) for j in range(half)]
+    return c[0]
+
+
+def _plain_halving_sum(w, r):
+    c = [_round_f32(w[h] * r[h]) for h in range(len(r))]
+    while len(c) > 1:
+        half = len(c) // 2
+        c = [_round_f32(c[j] + c[j + half]) for j in range(half)]
+    return c[0]
+
+
+@pytest.mark.parametrize("HI", [64, 20, 4])
+def test_canonical_score_order(HI):
+    """fp4 queries and keys (every dot certified exact) with arbitrary fp32 weights, so that the head sum rounds:
+    the oracle's canonical fp32 score equals the exact-rational emulation of the chained order bit for bit, and (for
+    16 heads or more) differs from a plain halving tree of rounded products on some entries."""
+    g = np.random.default_rng(60 + HI)
+    B, Sq, DI, N, m = 1, 1, 32, 24, 4
+    qx = g.standard_normal((HI, DI)).astype(np.float32)
+    kx = g.standard_normal((N, DI)).astype(np.float32)
+    w = (g.standard_normal((B, Sq, HI)) * 0.37).astype(np.float32)
+    qc, kc = orc.encode(qx, "fp4"), orc.encode(kx, "fp4")
+    kc["cap"] = N
+    _, s32, _, bad, _ = orc.indexer_scores(qc, w, kc, B, Sq, HI, DI, N, m, 4 * N, canonical=True, want_exact=True)
+    assert bad == 0
+    qd, kd = orc.decode(qc), orc.decode(kc)
+    P = 1
+    while P < HI:
+        P *= 2
+    wf = [Fraction(float(x)) for x in w[0, 0]] + [Fraction(0)] * (P - HI)
+    differ = 0
+    for i in range(N):
+        r = [max(sum((Fraction(float(a)) * Fraction(float(b)) for a, b in zip(qd[h], kd[i])), Fraction(0)),
+                 Fraction(0)) for h in range(HI)] + [Fraction(0)] * (P - HI)
+        want = _chained_sum(wf, r)
+        assert np.float32(s32[0, 0, i]) == np.float32(float(want)), (HI, i)
+        differ += _plain_halving_sum(wf, r) != want
+    if HI >= 16:
+        assert differ > 0
