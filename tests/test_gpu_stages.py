@@ -184,8 +184,11 @@ def test_indexer_mfma_bf16_prefill_causal():
 
 
 @pytest.mark.parametrize("B,Sq,N,k,HI,DI", [(2, 1, 3000, 1024, 64, 128), (1, 3, 40000, 1024, 64, 128),
-                                             (2, 2, 500, 64, 16, 64), (8, 1, 65613, 1024, 64, 128)])
+                                             (2, 2, 500, 64, 16, 64), (8, 1, 65613, 1024, 64, 128),
+                                             (2, 2, 500, 64, 40, 64), (1, 1, 700, 128, 32, 64)])
 def test_indexer_fp4_bit_exact(B, Sq, N, k, HI, DI):
+    # (other than 64 x 128 the vector-ALU kernel scores: 40 heads pad to 64, so its fused chains run over four heads
+    # with padding; 32 heads give chains of two)
     _indexer_case(B, Sq, HI, DI, N, 4, k, 4 * N, "fp4", 14)
 
 
