@@ -52,8 +52,9 @@ typedef enum {
                      /* scale: float [rows] s = fl32(amax / 448) over those dims (1 if amax = 0),       */
                      /* rope: uint16 [rows][rope_dims] bfloat16 bits of the LAST rope_dims channels     */
   LCA_FP4 = 3        /* data: uint8   [rows][dim / 2] OCP fp4 e2m1 codes of x * 2^-e, element 2j in    */
-                     /* the low nibble of byte j; scale: uint8 [rows][dim / 16] E8M0 byte e + 127,     */
-                     /* e = smallest integer with amax(16 elements) <= 6 * 2^e (e = -127 if amax = 0)   */
+                     /* the low nibble of byte j; scale: uint8 [rows][dim / 32] E8M0 byte e + 127, one  */
+                     /* per block of 32 consecutive elements (dim a multiple of 32), e = smallest       */
+                     /* integer with amax(block) <= 6 * 2^e (e = -127 if amax = 0)                      */
 } lca_format;
 
 /* Tensor flag LCA_ROTATE_HADAMARD (paper notes, the Indexer excerpt: the indexer's queries, and the keys of its own

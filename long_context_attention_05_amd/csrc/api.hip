@@ -76,7 +76,7 @@ int check_tensor(const lca_tensor& t, bool allow_fp4, bool allow_mixed, bool all
       break;
     case LCA_FP4:
       if (!allow_fp4) return LCA_ERR_UNSUPPORTED;
-      if (t.dim % 16 != 0 || !t.scale) return LCA_ERR_INVALID_ARG;
+      if (t.dim % kFp4Block != 0 || !t.scale) return LCA_ERR_INVALID_ARG;
       if ((uintptr_t)t.scale & 3u) return LCA_ERR_ALIGNMENT;
       break;
     default:

@@ -10,7 +10,7 @@
 //
 // The codec (mixed-precision cache: cosmocat page section 3; Mind Observatory page) is applied in the same
 // pass: fp32 entries are encoded to bf16 / fp8 e4m3 with a per-entry scale plus bf16 RoPE dims / fp4 e2m1 with
-// per-16 power-of-two scales while the row is still in registers.
+// one power-of-two scale per 32-element block while the row is still in registers.
 #include "lca_device.h"
 #include "lca_internal.h"
 
@@ -158,22 +158,22 @@ __device__ void store_row(const RowOut& o, long long row, const float (&vin)[CPT
       }
     }
     if (threadIdx.x == 0) ((float*)o.scale)[row] = s;
-  } else {  // LCA_FP4: groups of 16 consecutive channels live in 16 consecutive lanes
+  } else {  // LCA_FP4: blocks of 32 consecutive channels live in 32 consecutive lanes
     uint8_t* d = (uint8_t*)o.data + row * (c / 2);
-    uint8_t* sc = (uint8_t*)o.scale + row * (c / 16);
+    uint8_t* sc = (uint8_t*)o.scale + row * (c / kFp4Block);
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
       int j = threadIdx.x + nt * u;
       float a = (j < c) ? fabsf(v[u]) : 0.0f;
 #pragma unroll
-      for (int off = 1; off < 16; off <<= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
+      for (int off = 1; off < kFp4Block; off <<= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
       int e = fp4_group_exp(a);
       float y = ldexpf(v[u], -e);
       uint32_t code = fp4_encode(y);
       uint32_t other = __shfl_xor(code, 1, 64);
       if (j < c) {
         if ((j & 1) == 0) d[j >> 1] = (uint8_t)(code | (other << 4));
-        if ((j & 15) == 0) sc[j >> 4] = (uint8_t)(e + 127);
+        if ((j & (kFp4Block - 1)) == 0) sc[j / kFp4Block] = (uint8_t)(e + 127);
       }
     }
   }
@@ -245,21 +245,21 @@ __device__ void store_row_wave(const RowOut& o, long long row, float (&v)[CPW]) 
       }
     }
     if (lane == 0) ((float*)o.scale)[row] = s;
-  } else {  // LCA_FP4: groups of 16 consecutive channels live in 16 consecutive lanes
+  } else {  // LCA_FP4: blocks of 32 consecutive channels live in 32 consecutive lanes
     uint8_t* d = (uint8_t*)o.data + row * (c / 2);
-    uint8_t* sc = (uint8_t*)o.scale + row * (c / 16);
+    uint8_t* sc = (uint8_t*)o.scale + row * (c / kFp4Block);
 #pragma unroll
     for (int u = 0; u < CPW; ++u) {
       const int j = lane + 64 * u;
       float a = (j < c) ? fabsf(v[u]) : 0.0f;
 #pragma unroll
-      for (int off = 1; off < 16; off <<= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
+      for (int off = 1; off < kFp4Block; off <<= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
       const int e = fp4_group_exp(a);
       const uint32_t code = fp4_encode(ldexpf(v[u], -e));
       const uint32_t other = __shfl_xor(code, 1, 64);
       if (j < c) {
         if ((j & 1) == 0) d[j >> 1] = (uint8_t)(code | (other << 4));
-        if ((j & 15) == 0) sc[j >> 4] = (uint8_t)(e + 127);
+        if ((j & (kFp4Block - 1)) == 0) sc[j / kFp4Block] = (uint8_t)(e + 127);
       }
     }
   }

@@ -38,7 +38,7 @@ __device__ __forceinline__ float load_elem(const lca_tensor& t, long long row, i
   // FP4
   uint32_t byte = ((const uint8_t*)t.data)[row * (t.dim / 2) + (j >> 1)];
   uint32_t code = (j & 1) ? (byte >> 4) : (byte & 15u);
-  int e = (int)((const uint8_t*)t.scale)[row * (t.dim / 16) + (j >> 4)] - 127;
+  int e = (int)((const uint8_t*)t.scale)[row * (t.dim / kFp4Block) + j / kFp4Block] - 127;
   return fp4_value(code) * exp2i(e);
 }
 
@@ -125,12 +125,13 @@ __device__ __forceinline__ void load_row64(const lca_tensor& t, long long row, i
 #pragma unroll
     for (int s = 0; s < 8; ++s) out[s] = p[s];
   } else {
+    // channels 64 g .. 64 g + 63 are blocks 2 g and 2 g + 1: chunk s (8 channels) is in block 2 g + s / 4
     const uint4* p = (const uint4*)((const uint8_t*)t.data + row * 64 + 32 * g);
     uint4 c0 = p[0], c1 = p[1];
-    uint32_t sc = *(const uint32_t*)((const uint8_t*)t.scale + row * 8 + 4 * g);
+    const uint32_t sc = *(const uint16_t*)((const uint8_t*)t.scale + row * 4 + 2 * g);
     uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
 #pragma unroll
-    for (int s = 0; s < 8; ++s) out[s] = fp4x8_to_bf16x8(cw[s], (int)((sc >> (8 * (s >> 1))) & 255u) - 127);
+    for (int s = 0; s < 8; ++s) out[s] = fp4x8_to_bf16x8(cw[s], (int)((sc >> (8 * (s >> 2))) & 255u) - 127);
   }
 }
 
@@ -145,7 +146,7 @@ __device__ __forceinline__ void load_qblock(const IdxArgs& a, long long qrow0, u
       v[it] = *(gbl_u32x4_t*)((const uint16_t*)a.q.data + (qrow0 + h) * 128 + 8 * c8);
     } else {
       const uint32_t codes = *(const uint32_t*)((const uint8_t*)a.q.data + (qrow0 + h) * 64 + 4 * c8);
-      const int e = (int)((const uint8_t*)a.q.scale)[(qrow0 + h) * 8 + (c8 >> 1)] - 127;
+      const int e = (int)((const uint8_t*)a.q.scale)[(qrow0 + h) * 4 + (c8 >> 2)] - 127;
       const uint4 w = fp4x8_to_bf16x8(codes, e);
       v[it] = u32x4_t{w.x, w.y, w.z, w.w};
     }
@@ -465,7 +466,7 @@ __global__ __launch_bounds__(256, 2) void idx_score_decode_bf16(IdxArgs a) {
 typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8_t;
 
 // ---- fp4 decode scoring with the keys streamed into an LDS ring: one workgroup of eight waves per CU takes NST
-// stages of 512 keys.  A stage's codes (32 KB) and scales (4 KB) travel from memory straight into a ring slot with
+// stages of 512 keys.  A stage's codes (32 KB) and scales (2 KB) travel from memory straight into a ring slot with
 // buffer loads into LDS (no registers hold data in flight), three stages in flight while one is scored; each slot is
 // its own pair of LDS variables and the stage loop is fully unrolled, so every wait is a count fixed at compile
 // time.  Each wave moves and scores its own 64 keys of a stage, so waves never wait for each other.  Code rows are
@@ -474,19 +475,18 @@ typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8_t;
 //
 // Scoring runs on v_mfma_scale_f32_32x32x64_f8f6f4, which takes fp4 operands at twice the rate of the 16x16x128
 // form: A = 32 heads (lane l: head l % 32, contraction slots 32 (l / 32) .. + 31), B = 32 keys (lane l: key l % 32,
-// the same slots), one E8M0 scale per lane applied to the lane's 32 slots.  The cache scales each 16 elements, so
-// lane half hh = l / 32 takes code chunk c = 2 i + hh (groups 2c, 2c + 1) in instruction pair i; the key operand is
-// the chunk as loaded and the query operand keeps one of its two groups (h = 0, 1) with that group's scales and
-// zeros the other 16 slots, whose products are exact zeros (e2m1 has no infinities or NaNs).  Eight instructions
-// (2 head tiles x 2 chunk pairs x 2 groups) give the 64 x 32 dots.  Products of fp4 values and their block sums are
-// exact, scaled by powers of two, so the per-head dots equal the exact ones whenever they fit fp32 -- the fixed
-// head-reduction order then makes the scores bit-reproducible.  Lane l, register k of the 32x32 result holds head
-// 32 T + 8 (k / 4) + 4 hh + k % 4 for key l % 32: the chains and the +8 step run in lane, +4 and +2 across the lane
-// halves, +1 in lane -- the same pairs as the 16x16 kernels.
+// the same slots), one E8M0 scale per lane applied to the lane's 32 slots -- exactly the cache's 32-element scale
+// block.  Lane half hh takes code chunk (block) c = 2 i + hh in instruction i, both operands with that block's scale
+// (the instruction's byte select picks it from the row's scale word), so four instructions (2 head tiles x 2 chunk
+// pairs) give the 64 x 32 dots.  Products of fp4 values and their block sums are exact, scaled by powers of two, so
+// the per-head dots equal the exact ones whenever they fit fp32 -- the fixed head-reduction order then makes the
+// scores bit-reproducible.  Lane l, register k of the 32x32 result holds head 32 T + 8 (k / 4) + 4 hh + k % 4 for
+// key l % 32: the chains and the +8 step run in lane, +4 and +2 across the lane halves, +1 in lane -- the same pairs
+// as the 16x16 kernels.
 constexpr int kF4rWaves = 8;
 constexpr int kF4rStage = 64 * kF4rWaves;  // keys per stage
 constexpr int kF4rCodeB = kF4rStage * 64;  // 32 KB
-constexpr int kF4rScaleB = kF4rStage * 8;  // 4 KB
+constexpr int kF4rScaleB = kF4rStage * 4;  // 2 KB: four scale bytes per key
 __shared__ __attribute__((aligned(16))) uint8_t f4r_c0[kF4rCodeB];
 __shared__ __attribute__((aligned(16))) uint8_t f4r_c1[kF4rCodeB];
 __shared__ __attribute__((aligned(16))) uint8_t f4r_c2[kF4rCodeB];
@@ -496,7 +496,7 @@ __shared__ __attribute__((aligned(16))) uint8_t f4r_s1[kF4rScaleB];
 __shared__ __attribute__((aligned(16))) uint8_t f4r_s2[kF4rScaleB];
 __shared__ __attribute__((aligned(16))) uint8_t f4r_s3[kF4rScaleB];
 // Row histograms of pass 1 in LDS, one per query row the workgroup scores (with 4 slots of codes and scales, two rows
-// fill the 160 KB of a CU's LDS exactly).
+// take 152 of the 160 KB of a CU's LDS).
 constexpr int kF4rMaxRows = 2;
 __shared__ int f4r_hist[kF4rMaxRows * kSelBins];
 
@@ -522,12 +522,12 @@ constexpr int kIdxBufWord3 = 0x00020000;  // buffer descriptor word 3: raw untyp
 __host__ __device__ constexpr int vm_wait_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (0xF << 8) | (7 << 4); }
 
 // Memory operations a wave has issued after the loads of stage st when step st waits for them: the loads of the
-// (at most two) stages after it and the key stores of the steps since they were issued (6 loads per stage: 4 code
-// rows of 1 KB and 2 scale rows of 256 bytes; nr stores per step, one per query row).
+// (at most two) stages after it and the key stores of the steps since they were issued (5 loads per stage: 4 code
+// rows of 1 KB and one row of 256 scale bytes; nr stores per step, one per query row).
 __host__ __device__ constexpr int f4r_wait_count(int st, int nst, int nr) {
   const int later = (st + 2 < nst - 1 ? st + 2 : nst - 1) - st;
   const int stores = st - (st - 3 > 0 ? st - 3 : 0);
-  return 6 * later + nr * stores;
+  return 5 * later + nr * stores;
 }
 
 // Calls f(integral_constant<int, ST>) for ST = ST0 .. NST - 1 in order (a loop whose index is a constant).
@@ -558,11 +558,11 @@ __global__ __launch_bounds__(kF4rWaves * 64) void idx_score_decode_fp4_ring(IdxA
   const bool hist = a.sel_state != nullptr;
   for (int i = threadIdx.x; i < NR * kSelBins; i += blockDim.x) f4r_hist[i] = 0;
 
-  // queries: head tile T = heads 32 T .. 32 T + 31, lane head 32 T + col; chunks hh and 2 + hh of its code row and the
-  // matching scale bytes 2 hh, 2 hh + 1, 4 + 2 hh, 5 + 2 hh.  The raw loads go first and the operands are built after
-  // the ring's first loads are issued, so that nothing waits for the queries before the ring starts.
+  // queries: head tile T = heads 32 T .. 32 T + 31, lane head 32 T + col; chunks (blocks) hh and 2 + hh of its code
+  // row and its scale word.  The raw loads go first and the operands are built after the ring's first loads are
+  // issued, so that nothing waits for the queries before the ring starts.
   uint4 qraw[NR][2][2];
-  uint2 sraw[NR][2];
+  uint32_t sraw[NR][2];
   float wv[NR][2][16];
 #pragma unroll
   for (int r = 0; r < NR; ++r)
@@ -572,14 +572,14 @@ __global__ __launch_bounds__(kF4rWaves * 64) void idx_score_decode_fp4_ring(IdxA
 #pragma unroll
       for (int i = 0; i < 2; ++i)
         qraw[r][T][i] = *(const uint4*)((const uint8_t*)a.q.data + row * 64 + 16 * (2 * i + hh));
-      sraw[r][T] = *(const uint2*)((const uint8_t*)a.q.scale + row * 8);
+      sraw[r][T] = *(const uint32_t*)((const uint8_t*)a.q.scale + row * 4);
 #pragma unroll
       for (int k = 0; k < 16; ++k)
         wv[r][T][k] = a.w[(long long)(qrow0 + r) * 64 + 32 * T + 8 * (k >> 2) + 4 * hh + (k & 3)];
     }
   __builtin_amdgcn_sched_barrier(0);
-  i32x8_t qop[NR][2][2][2];
-  int qs[NR][2][2];  // bytes 0 and 1: the scales of the query groups kept in qop[..][0] and qop[..][1]
+  i32x8_t qop[NR][2][2];
+  int qs[NR][2];  // bytes 0 and 2: the scales of blocks hh and 2 + hh (the operands qop[..][0] and qop[..][1])
 
   // buffer descriptors over the workgroup's own keys [k0, k1) of a dense cache (offsets stay small whatever the cache
   // size, and the range check covers exactly the keys the workgroup may read), or over the whole pool of a paged one
@@ -590,7 +590,7 @@ __global__ __launch_bounds__(kF4rWaves * 64) void idx_score_decode_fp4_ring(IdxA
   const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)((const uint8_t*)a.k.data + rb0 * 64), 0, (int)(nrows * 64), kIdxBufWord3);
   const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((const uint8_t*)a.k.scale + rb0 * 8), 0, (int)(nrows * 8), kIdxBufWord3);
+      (void*)((const uint8_t*)a.k.scale + rb0 * 4), 0, (int)(nrows * 4), kIdxBufWord3);
   // paged: the blocks of each stage's 64 wave keys (keys 0..31 and 32..63 of the slice), read before the ring starts
   int blk[NST][2];
 #pragma unroll
@@ -610,8 +610,8 @@ __global__ __launch_bounds__(kF4rWaves * 64) void idx_score_decode_fp4_ring(IdxA
     return br ? blk[st][o >= 32] * br + ((k0 + key) & (br - 1)) : key;
   };
   // stage st into slot S: code instruction i of wave w moves keys 64 w + 16 i .. + 15 (lane l: key + l / 4, chunk
-  // position l % 4 holding code chunk (l % 4) ^ (l / 16)); scale instruction i moves 32 keys' scale rows.  Keys past
-  // k1 repeat key k1 - 1.
+  // position l % 4 holding code chunk (l % 4) ^ (l / 16)); the scale instruction moves the wave's 64 scale words
+  // (lane l: key 64 w + l).  Keys past k1 repeat key k1 - 1.
   auto issue = [&](auto SC, int st) {
     constexpr int S = decltype(SC)::value;
     const int kst = st * kF4rStage;  // relative to k0
@@ -621,40 +621,31 @@ __global__ __launch_bounds__(kF4rWaves * 64) void idx_score_decode_fp4_ring(IdxA
       __builtin_amdgcn_raw_ptr_buffer_load_lds(crs, (idx_lds_void_t*)(f4r_codes<S>() + (64 * wave + 16 * i) * 64), 16,
                                                row * 64 + 16 * ((lane & 3) ^ (lane >> 4)), 0, 0, 0);
     }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = key_row(st, kst, 32 * i + (lane >> 1));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, (idx_lds_void_t*)(f4r_scales<S>() + (64 * wave + 32 * i) * 8), 4,
-                                               row * 8 + 4 * (lane & 1), 0, 0, 0);
-    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, (idx_lds_void_t*)(f4r_scales<S>() + 64 * wave * 4), 4,
+                                             key_row(st, kst, lane) * 4, 0, 0, 0);
   };
-  // key operands of the wave's key tile u (keys 64 w + 32 u + col of stage slot S); ks[i] holds the scales of
-  // groups 2c, 2c + 1 (c = 2 i + hh) in its bytes 0 and 1, which the instruction's byte select picks
-  auto kops = [&](auto SC, int u, i32x8_t (&kop)[2], int (&ks)[2]) {
+  // key operands of the wave's key tile u (keys 64 w + 32 u + col of stage slot S); ks holds the scales of blocks
+  // hh and 2 + hh in its bytes 0 and 2, which the instruction's byte select picks
+  auto kops = [&](auto SC, int u, i32x8_t (&kop)[2], int& ks) {
     constexpr int S = decltype(SC)::value;
     const int kl = 64 * wave + 32 * u + col;
     const uint8_t* cb = f4r_codes<S>() + kl * 64;
     const int sw = (kl >> 2) & 3;
-    const uint2 s8 = *(const uint2*)(f4r_scales<S>() + kl * 8);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const u32x4_t kc = *(const u32x4_t*)(cb + 16 * ((2 * i + hh) ^ sw));
       kop[i] = i32x8_t{(int)kc[0], (int)kc[1], (int)kc[2], (int)kc[3], 0, 0, 0, 0};
-      ks[i] = (int)((i == 0 ? s8.x : s8.y) >> (16 * hh));  // bytes 4i .. 4i + 3 of the row
     }
+    ks = (int)(*(const uint32_t*)(f4r_scales<S>() + kl * 4) >> (8 * hh));
   };
-  // 64 x 32 dots of query row r against one key tile
-  auto dots = [&](const i32x8_t (&kop)[2], const int (&ks)[2], int r, f32x16_t (&acc)[2]) {
+  // 64 x 32 dots of query row r against one key tile: block hh (byte 0 of both scale words), then block 2 + hh
+  // (byte 2)
+  auto dots = [&](const i32x8_t (&kop)[2], int ks, int r, f32x16_t (&acc)[2]) {
 #pragma unroll
     for (int T = 0; T < 2; ++T) {
-      acc[T] = f32x16_t{};
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        acc[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qop[r][T][i][0], kop[i], acc[T], 4, 4, 0,
-                                                                 qs[r][T][i], 0, ks[i]);
-        acc[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qop[r][T][i][1], kop[i], acc[T], 4, 4, 1,
-                                                                 qs[r][T][i], 1, ks[i]);
-      }
+      acc[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qop[r][T][0], kop[0], f32x16_t{}, 4, 4, 0, qs[r][T], 0,
+                                                               ks);
+      acc[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qop[r][T][1], kop[1], acc[T], 4, 4, 2, qs[r][T], 2, ks);
     }
   };
   using S0 = std::integral_constant<int, 0>;
@@ -668,14 +659,14 @@ __global__ __launch_bounds__(kF4rWaves * 64) void idx_score_decode_fp4_ring(IdxA
 #pragma unroll
   for (int r = 0; r < NR; ++r)
 #pragma unroll
-    for (int T = 0; T < 2; ++T)
+    for (int T = 0; T < 2; ++T) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const uint4 c = qraw[r][T][i];
-        qop[r][T][i][0] = i32x8_t{(int)c.x, (int)c.y, 0, 0, 0, 0, 0, 0};
-        qop[r][T][i][1] = i32x8_t{0, 0, (int)c.z, (int)c.w, 0, 0, 0, 0};
-        qs[r][T][i] = (int)((i == 0 ? sraw[r][T].x : sraw[r][T].y) >> (16 * hh));
+        qop[r][T][i] = i32x8_t{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
       }
+      qs[r][T] = (int)(sraw[r][T] >> (8 * hh));
+    }
 
   // Stage st sits in slot st % 4.  A wave loads exactly the keys it scores, so the ring needs no barrier: step st
   // waits for this wave's own loads of stage st, starts stage st + 3 in the slot this wave finished with in step
@@ -689,7 +680,7 @@ __global__ __launch_bounds__(kF4rWaves * 64) void idx_score_decode_fp4_ring(IdxA
     asm volatile("" ::: "memory");
     if constexpr (st + 3 < NST) issue(std::integral_constant<int, (st + 3) % 4>{}, st + 3);
     i32x8_t kop0[2], kop1[2];
-    int ks0[2], ks1[2];
+    int ks0, ks1;
     kops(SC{}, 0, kop0, ks0);
     kops(SC{}, 1, kop1, ks1);
 #pragma unroll

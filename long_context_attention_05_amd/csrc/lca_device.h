@@ -63,7 +63,7 @@ __device__ __forceinline__ float fp8_decode(uint32_t c) {
 }
 
 // ------------------------------------------------------------------------------------------------
-// OCP FP4 E2M1 with a power-of-two scale per 16 elements.
+// OCP FP4 E2M1 with a power-of-two (E8M0) scale per block of kFp4Block consecutive elements.
 // ------------------------------------------------------------------------------------------------
 // Smallest integer e with amax <= 6 * 2^e, clamped to [-127, 127]; -127 when amax == 0.
 __device__ __forceinline__ int fp4_group_exp(float amax) {

@@ -55,6 +55,11 @@ struct IdxArgs {
 };
 // Decode kernels take up to this many query rows per sequence (one token, or a few draft tokens verified together):
 // the rows of a sequence score the same keys side by side, so the key stream is read from memory about once.
+// fp4 caches: one power-of-two (E8M0) scale per block of 32 consecutive elements -- the 1x32 FP4 sub-blocks with
+// their own scale factors of the page "百万token成本暴降90%！DeepSeek-V4揭秘" (question 4), and the block one lane of
+// a scaled MFMA applies its scale to.
+constexpr int kFp4Block = 32;
+
 constexpr int kDecodeMaxRows = 4;
 // Rows of at most this many keys are selected from an LDS copy by the many-row top-k.
 constexpr int kTopkLdsKeys = 32768;

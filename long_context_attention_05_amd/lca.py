@@ -130,7 +130,7 @@ class CacheTensor:
             self.scale_t = torch.empty((rows,), dtype=torch.float32, device=device)
         elif fmt == "fp4":
             self.data = torch.empty((rows, dim // 2), dtype=torch.uint8, device=device)
-            self.scale_t = torch.empty((rows, dim // 16), dtype=torch.uint8, device=device)
+            self.scale_t = torch.empty((rows, dim // 32), dtype=torch.uint8, device=device)
         else:
             raise ValueError(fmt)
 

@@ -35,7 +35,7 @@ def _bf16_bits(x: np.ndarray) -> np.ndarray:
 
 
 def _entry_bytes(fmt: str, dim: int, rope: int) -> int:
-    return {"f32": 4 * dim, "bf16": 2 * dim, "mixed": (dim - rope) + 2 * rope + 4, "fp4": dim // 2 + dim // 16}[fmt]
+    return {"f32": 4 * dim, "bf16": 2 * dim, "mixed": (dim - rope) + 2 * rope + 4, "fp4": dim // 2 + dim // 32}[fmt]
 
 
 def make_cache(fmt: str, B: int, cap: int, dim: int, rope: int, x: np.ndarray | None) -> lca.CacheTensor:

@@ -138,8 +138,10 @@ uint8_t orc_fp4_encode1(double y) {
 
 double orc_fp4_decode1(uint8_t c) { return ((c & 8) ? -1.0 : 1.0) * kE2M1[c & 7]; }
 
-/* Per-16 power-of-two scale: the smallest integer e with amax <= 6 * 2^e (exact comparison), kept
- * in [-127, 127]; amax == 0 gives e = -127.  Stored as the E8M0 byte e + 127. */
+/* fp4 blocks of ORC_FP4_BLOCK consecutive elements share one power-of-two scale ([P1] question 4: each 1x32 FP4
+ * sub-block has its own scale factor): the smallest integer e with amax <= 6 * 2^e over the block (exact
+ * comparison), kept in [-127, 127]; amax == 0 gives e = -127.  Stored as the E8M0 byte e + 127. */
+#define ORC_FP4_BLOCK 32
 static int fp4_group_exponent(double amax) {
   if (amax == 0.0) return -127;
   int e = floor_log2(amax) - 3; /* 6 * 2^e < amax here unless amax is tiny; walk up exactly */
@@ -156,7 +158,7 @@ static int fp4_group_exponent(double amax) {
  *   MIXED: data = uint8 fp8 codes [rows][dim - rope], scale = float[rows], rope = uint16 bf16 [rows][rope]
  *          (the RoPE dims are the last `rope` channels of the row, [P2] Indexer excerpt applies RoPE to
  *          q[..., -rd:]; [P3]/[P4] sec.3: RoPE dims bf16, the rest fp8)
- *   FP4  : data = uint8 packed [rows][dim/2] (element 2j in the low nibble), scale = uint8 E8M0 [rows][dim/16]
+ *   FP4  : data = uint8 packed [rows][dim/2] (element 2j in the low nibble), scale = uint8 E8M0 [rows][dim/32]
  */
 typedef struct {
   int fmt, dim, rope;
@@ -182,7 +184,7 @@ static long long cache_row(const orc_cache* c, int b, long long i) {
 
 /* Encode fp32 rows into a cache format (the quantise-on-write of the mixed-precision cache).
  * The fp8 per-row scale is s = fl32(amax / 448) over the row's non-RoPE dims (s = 1 if amax = 0);
- * code = fp8(clamp(fl32(x / s), +-448)).  fp4 per 16 elements: see fp4_group_exponent.
+ * code = fp8(clamp(fl32(x / s), +-448)).  fp4 per block of ORC_FP4_BLOCK elements: see fp4_group_exponent.
  * pinned by: codec round-trip and torch-cast tests. */
 void orc_encode_rows(const float* x, long long rows, int fmt, int dim, int rope, void* data, void* rope_data,
                      void* scale) {
@@ -213,19 +215,20 @@ void orc_encode_rows(const float* x, long long rows, int fmt, int dim, int rope,
       for (int j = 0; j < rope; ++j) ro[j] = orc_bf16_encode1(xr[dm + j]);
     } else { /* FP4 */
       uint8_t* o = (uint8_t*)data + r * (dim / 2);
-      uint8_t* sc = (uint8_t*)scale + r * (dim / 16);
-      for (int g = 0; g < dim / 16; ++g) {
+      uint8_t* sc = (uint8_t*)scale + r * (dim / ORC_FP4_BLOCK);
+      for (int g = 0; g < dim / ORC_FP4_BLOCK; ++g) {
+        const float* xb = xr + (size_t)ORC_FP4_BLOCK * g;
         double amax = 0.0;
-        for (int j = 0; j < 16; ++j) {
-          double a = fabs((double)xr[16 * g + j]);
+        for (int j = 0; j < ORC_FP4_BLOCK; ++j) {
+          double a = fabs((double)xb[j]);
           if (a > amax) amax = a;
         }
         int e = fp4_group_exponent(amax);
         sc[g] = (uint8_t)(e + 127);
-        for (int j = 0; j < 16; j += 2) {
-          uint8_t lo = orc_fp4_encode1(ldexp((double)xr[16 * g + j], -e));
-          uint8_t hi = orc_fp4_encode1(ldexp((double)xr[16 * g + j + 1], -e));
-          o[8 * g + j / 2] = (uint8_t)(lo | (hi << 4));
+        for (int j = 0; j < ORC_FP4_BLOCK; j += 2) {
+          uint8_t lo = orc_fp4_encode1(ldexp((double)xb[j], -e));
+          uint8_t hi = orc_fp4_encode1(ldexp((double)xb[j + 1], -e));
+          o[(ORC_FP4_BLOCK / 2) * g + j / 2] = (uint8_t)(lo | (hi << 4));
         }
       }
     }
@@ -249,11 +252,11 @@ static void decode_row(const orc_cache* c, long long row, double* out) {
     for (int j = 0; j < c->rope; ++j) out[dm + j] = orc_bf16_decode1(rp[j]);
   } else {
     const uint8_t* p = (const uint8_t*)c->data + row * (dim / 2);
-    const uint8_t* sc = (const uint8_t*)c->scale + row * (dim / 16);
+    const uint8_t* sc = (const uint8_t*)c->scale + row * (dim / ORC_FP4_BLOCK);
     for (int j = 0; j < dim; ++j) {
       uint8_t byte = p[j / 2];
       uint8_t code = (j & 1) ? (byte >> 4) : (byte & 0xF);
-      out[j] = ldexp(orc_fp4_decode1(code), (int)sc[j / 16] - 127);
+      out[j] = ldexp(orc_fp4_decode1(code), (int)sc[j / ORC_FP4_BLOCK] - 127);
     }
   }
 }
@@ -426,8 +429,8 @@ void orc_rope_rows(const double* x, long long rows, int c, int rd, const double*
  * dividing every nonzero product and A = sum_d |q[d] k[d]|.  Every partial sum of any subset of products is
  * an integer multiple of 2^L no larger than A in magnitude, so if A < 2^(L + 24) each one has at most 24
  * significant bits and is an fp32 value; L >= -126 keeps them out of the subnormal range.  For fp4 x fp4
- * rows (per-16 scales) this is the bound on the spread of the groups' scale exponents: a group's products
- * are multiples of 2^(eq + ek - 2) summing to less than 2^(eq + ek + 10). */
+ * rows (one scale per 32-element block) this is the bound on the spread of the blocks' scale exponents: a block's
+ * products are multiples of 2^(eq + ek - 2) summing to less than 2^(eq + ek + 11). */
 int orc_dot_is_fp32_exact(const double* q, const double* k, int n) {
   int L = INT32_MAX;
   double A = 0.0;

@@ -132,7 +132,7 @@ def empty_cache(fmt: str, rows: int, dim: int, rope: int = 0, cap: int | None = 
                  scale=np.zeros((rows,), np.float32))
     elif fmt == "fp4":
         assert dim % 16 == 0
-        d = dict(data=np.zeros((rows, dim // 2), np.uint8), rope_data=None, scale=np.zeros((rows, dim // 16), np.uint8))
+        d = dict(data=np.zeros((rows, dim // 2), np.uint8), rope_data=None, scale=np.zeros((rows, dim // 32), np.uint8))
     else:
         raise ValueError(fmt)
     d.update(fmt=fmt, dim=dim, rope=rope, cap=cap if cap is not None else rows)
@@ -143,6 +143,8 @@ def encode(x: np.ndarray, fmt: str, rope: int = 0, cap: int | None = None) -> di
     """Encode fp32 rows x[..., dim] into a cache dict (rows flattened)."""
     x = np.ascontiguousarray(x, dtype=np.float32)
     dim = x.shape[-1]
+    if fmt == "fp4" and dim % 32:
+        raise ValueError("fp4 rows are whole 32-element scale blocks")
     rows = x.size // dim
     c = empty_cache(fmt, rows, dim, rope, cap)
     lib().orc_encode_rows(_ptr(x), rows, FMT[fmt], dim, rope, _ptr(c["data"]), _ptr(c["rope_data"]), _ptr(c["scale"]))

@@ -197,26 +197,27 @@ _E2M1_HALF = np.array([0.25, 0.25, 0.25, 0.25, 0.5, 0.5, 1.0, 1.0])  # half the 
 
 
 def check_fp4_codes(got: dict, x64: np.ndarray, tol_rel: float = 2.0 ** -16) -> int:
-    """got: host dict of an fp4 cache restricted to the compared rows (data [rows, c/2], scale [rows, c/16]); x64:
-    oracle values [rows, c].  A group scale must equal the oracle's unless the group's amax lies within tol of the
+    """got: host dict of an fp4 cache restricted to the compared rows (data [rows, c/2], scale [rows, c/32]); x64:
+    oracle values [rows, c].  A block scale must equal the oracle's unless the block's amax lies within tol of the
     boundary 6 * 2^e between them; every code must be a rounding (saturating at 6) of a value within tol * 2^-e of
-    x * 2^-e, e the GPU's own group exponent.  Returns the number of codes that differ from the oracle's encoding
+    x * 2^-e, e the GPU's own block exponent.  Returns the number of codes that differ from the oracle's encoding
     with that exponent."""
     from oracle import oracle as orc
     rows, c = x64.shape
     tol = tol_rel * np.abs(x64).max(axis=1)
-    e_g = got["scale"].reshape(rows, c // 16).astype(np.int64) - 127
+    blk = 32  # elements per fp4 scale block
+    e_g = got["scale"].reshape(rows, c // blk).astype(np.int64) - 127
     ref = orc.encode(x64.astype(np.float32), "fp4")
-    e_o = ref["scale"].reshape(rows, c // 16).astype(np.int64) - 127
+    e_o = ref["scale"].reshape(rows, c // blk).astype(np.int64) - 127
     if np.any(e_g != e_o):
         r_i, g_i = np.nonzero(e_g != e_o)
-        amax = np.abs(x64.reshape(rows, c // 16, 16)).max(axis=2)[r_i, g_i]
+        amax = np.abs(x64.reshape(rows, c // blk, blk)).max(axis=2)[r_i, g_i]
         assert np.all(np.abs(e_g - e_o)[r_i, g_i] == 1), "fp4 group scales more than one exponent apart"
         bound = 6.0 * 2.0 ** np.minimum(e_g, e_o)[r_i, g_i]
         assert np.all(np.abs(amax - bound) <= tol[r_i]), "an fp4 group scale away from a scale boundary"
     packed = got["data"].reshape(rows, c // 2)
     codes = np.stack([packed & 0xF, packed >> 4], axis=-1).reshape(rows, c).astype(np.int64)
-    y = x64 * 2.0 ** -np.repeat(e_g, 16, axis=1)
+    y = x64 * 2.0 ** -np.repeat(e_g, blk, axis=1)
     want = _fp4_ref(y)
     bad = codes != want
     n = int(bad.sum())
@@ -225,7 +226,7 @@ def check_fp4_codes(got: dict, x64: np.ndarray, tol_rel: float = 2.0 ** -16) -> 
         mag = codes[bad] & 7
         gv = np.where(codes[bad] & 8, -1.0, 1.0) * _E2M1[mag]
         yc = np.clip(y[bad], -6.0, 6.0)
-        scl = 2.0 ** -e_g[r_i, c_i // 16]
+        scl = 2.0 ** -e_g[r_i, c_i // blk]
         ok = np.abs(gv - yc) <= tol[r_i] * scl + _E2M1_HALF[mag]
         assert np.all(ok), "fp4 code not a rounding of a value within tol"
     return n

@@ -74,5 +74,5 @@ def test_epilogue_rotated_fp4_keys():
     out, Y, e0, nb = _run(s, B, n, c, m, 64, "fp4", flags=lca.LCA_ROTATE_HADAMARD)
     h = out.host()
     got = dict(data=h["data"].reshape(B, -1, c // 2)[:, e0:e0 + nb].reshape(-1, c // 2),
-               scale=h["scale"].reshape(B, -1, c // 16)[:, e0:e0 + nb].reshape(-1, c // 16))
+               scale=h["scale"].reshape(B, -1, c // 32)[:, e0:e0 + nb].reshape(-1, c // 32))
     check_fp4_codes(got, Y.reshape(-1, c))

@@ -68,7 +68,7 @@ def test_compress_into_rotated_fp4_keys():
     E = orc.kv_compress(Ca, Cb, Za, Zb, Ba, Bb, m=m, overlap=True, start_pos=0)
     y = orc.hadamard_rotate(E.reshape(-1, c))
     got = out.host()
-    check_fp4_codes(dict(data=got["data"].reshape(-1, c // 2), scale=got["scale"].reshape(-1, c // 16)), y)
+    check_fp4_codes(dict(data=got["data"].reshape(-1, c // 2), scale=got["scale"].reshape(-1, c // 32)), y)
 
 
 def test_rotation_flag_errors():

@@ -115,7 +115,7 @@ def _check_decode(w, inp, step):
         qc = orc.encode(inp["qI"].reshape(-1, w.DI), "fp4")
         got_k = step.keys[0].host()
         np.testing.assert_array_equal(got_k["data"].reshape(B, N + 1, -1)[:, :N].reshape(-1, w.DI // 2), kc["data"])
-        np.testing.assert_array_equal(got_k["scale"].reshape(B, N + 1, -1)[:, :N].reshape(-1, w.DI // 16), kc["scale"])
+        np.testing.assert_array_equal(got_k["scale"].reshape(B, N + 1, -1)[:, :N].reshape(-1, w.DI // 32), kc["scale"])
     else:
         kc = orc.plain_cache(_bf16(inp["keys"]), "bf16")
         qc = orc.plain_cache(_bf16(inp["qI"]), "bf16")

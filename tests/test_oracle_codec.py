@@ -124,22 +124,30 @@ def test_fp4_encode_is_nearest_value():
 
 
 def test_fp4_group_scale_rule():
-    """Per 16 elements: the smallest e with amax <= 6 * 2^e; stored as E8M0 byte e + 127."""
+    """One scale per block of 32 consecutive elements (the 1x32 FP4 sub-blocks with their own scale factors of the
+    page "百万token成本暴降90%！DeepSeek-V4揭秘", question 4): the smallest e with amax <= 6 * 2^e over the block;
+    stored as E8M0 byte e + 127."""
     g = np.random.default_rng(4)
     x = g.standard_normal((200, 128)).astype(np.float32) * np.float32(2.0) ** g.integers(-20, 20, (200, 1)).astype(np.float32)
-    x[0, :16] = 0.0
-    x[1, :16] = 6.0
-    x[2, :16] = 6.0001
+    x[0, :32] = 0.0
+    x[1, :32] = 6.0
+    x[2, :32] = 6.0001
+    # a large first half and a tiny second half of one block share the large half's scale (a 16-element block
+    # would give the tiny half its own)
+    x[4, :16] = 96.0
+    x[4, 16:32] = 0.01
     c = orc.encode(x, "fp4")
+    assert c["scale"].shape == (200, 4)
     e = c["scale"].astype(np.int64) - 127
-    amax = np.abs(x.reshape(200, 8, 16)).max(axis=2).astype(np.float64)
+    amax = np.abs(x.reshape(200, 4, 32)).max(axis=2).astype(np.float64)
     nz = amax > 0
     assert np.all(amax[nz] <= 6.0 * 2.0 ** e[nz])
     assert np.all(amax[nz] > 6.0 * 2.0 ** (e[nz] - 1))
-    assert e[0, 0] == -127 and e[1, 0] == 0 and e[2, 0] == 1
-    dec = orc.decode(c).reshape(200, 8, 16)
+    assert e[0, 0] == -127 and e[1, 0] == 0 and e[2, 0] == 1 and e[4, 0] == 4
+    dec = orc.decode(c).reshape(200, 4, 32)
+    assert np.all(dec[4, 0, :16] == 96.0) and np.all(dec[4, 0, 16:] == 0.0)
     # error of round-to-nearest on the e2m1 grid: at most half the grid step at that magnitude (step <= 2 * 2^e)
-    err = np.abs(dec - x.reshape(200, 8, 16))
+    err = np.abs(dec - x.reshape(200, 4, 32))
     assert np.all(err <= 2.0 ** e[:, :, None] * 1.0 + 1e-30)
     # packing: element 2j in the low nibble
     b = c["data"][3, 0]

@@ -255,10 +255,10 @@ def test_certificate_against_brute_force_orders():
 
 
 def test_certificate_on_fp4_rows():
-    """N(0,1) rows encoded to fp4 (per-16 scales): every pair is certified.  A row built with one group scaled by
-    2^20 against cancelling groups is not, and the inexact count names exactly those pairs."""
+    """N(0,1) rows encoded to fp4 (one scale per 32-element block): every pair is certified.  A row built with one
+    block 2^30 below cancelling blocks is not, and the inexact count names exactly those pairs."""
     g = np.random.default_rng(46)
-    B, Sq, HI, DI, N, m = 1, 1, 4, 64, 12, 4
+    B, Sq, HI, DI, N, m = 1, 1, 4, 128, 12, 4
     qx = g.standard_normal((B * Sq * HI, DI)).astype(np.float32)
     kx = g.standard_normal((B * N, DI)).astype(np.float32)
     w = np.abs(g.standard_normal((B, Sq, HI))).astype(np.float32)
@@ -266,10 +266,10 @@ def test_certificate_on_fp4_rows():
     kc["cap"] = N
     _, s32, _, bad, ex = orc.indexer_scores(qc, w, kc, B, Sq, HI, DI, N, m, 4 * N, canonical=True, want_exact=True)
     assert bad == 0 and ex.all()
-    # entry 5: groups +X, tiny, -X, 0 against a query head of all ones
+    # entry 5: blocks +X, tiny, -X, 0 against a query head of all ones
     kx2 = kx.copy()
-    kx2[5] = np.concatenate([np.full(16, 6.0 * 2 ** 10), np.full(16, 0.5 * 2.0 ** -20), np.full(16, -6.0 * 2 ** 10),
-                             np.zeros(16)]).astype(np.float32)
+    kx2[5] = np.concatenate([np.full(32, 6.0 * 2 ** 10), np.full(32, 0.5 * 2.0 ** -20), np.full(32, -6.0 * 2 ** 10),
+                             np.zeros(32)]).astype(np.float32)
     qx2 = qx.copy()
     qx2[0] = 1.0
     qc2, kc2 = orc.encode(qx2, "fp4"), orc.encode(kx2, "fp4")
@@ -383,7 +383,7 @@ def test_paged_cache_equals_dense():
     selections and attention outputs are bit-identical to the dense cache's (indexer keys and latent cache alike;
     block sizes 32 and 1)."""
     g = np.random.default_rng(51)
-    B, Sq, HI, DI, H, D, N, k, W, m = 3, 2, 4, 16, 3, 32, 128, 9, 6, 4
+    B, Sq, HI, DI, H, D, N, k, W, m = 3, 2, 4, 32, 3, 32, 128, 9, 6, 4
     cap = 160
     keys = g.standard_normal((B, cap, DI)).astype(np.float32)
     comp = g.standard_normal((B, cap, D)).astype(np.float32)
