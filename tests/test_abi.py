@@ -95,9 +95,12 @@ def test_host_validation_errors():
                                 None) == INV
     assert L.indexer_score_topk(_t(dim=128, cap=128), P, k, 2, 2, 64, 128, 1000, 4, 64, 4000, P, None, P, 16, None,
                                 None) == WS  # cap = Sq * HI passes (the next check, the workspace, fails)
-    # DI beyond 128 has no kernel (fp4 rows of 144 dims are otherwise valid)
-    assert L.indexer_score_topk(_t(fmt=3, dim=144, cap=64, scale=P), P, _t(fmt=3, dim=144, cap=1000, scale=P), 1, 1,
-                                64, 144, 1000, 4, 64, 4000, P, None, P, 1 << 30, None, None) == UNS
+    # DI beyond 128 has no kernel (fp4 rows of 160 dims are otherwise valid)
+    assert L.indexer_score_topk(_t(fmt=3, dim=160, cap=64, scale=P), P, _t(fmt=3, dim=160, cap=1000, scale=P), 1, 1,
+                                64, 160, 1000, 4, 64, 4000, P, None, P, 1 << 30, None, None) == UNS
+    # fp4 rows are whole 32-element scale blocks
+    assert L.indexer_score_topk(_t(fmt=3, dim=112, cap=64, scale=P), P, _t(fmt=3, dim=112, cap=1000, scale=P), 1, 1,
+                                64, 112, 1000, 4, 64, 4000, P, None, P, 1 << 30, None, None) == INV
     assert L.indexer_score_topk(q, P, _t(dim=128, cap=1000, flags=8), 1, 1, 64, 128, 1000, 4, 64, 4000, P, None, P,
                                 1 << 30, None, None) == INV
     # attention: window outside the raw span, workspace missing for a split plan, bad formats
