@@ -541,7 +541,7 @@ __device__ __forceinline__ void unroll_steps(F& f) {
 
 // NR query rows (consecutive rows of one sequence) per workgroup: every key stage is loaded once and scored for each
 // row, its key operands read from LDS once for all of them.
-template <int NST, int NR>
+template <int NST, int NR, bool PAGED>
 __global__ __launch_bounds__(kF4rWaves * 64) void idx_score_decode_fp4_ring(IdxArgs a) {
 #pragma clang fp contract(off)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -558,6 +558,12 @@ __global__ __launch_bounds__(kF4rWaves * 64) void idx_score_decode_fp4_ring(IdxA
   const bool hist = a.sel_state != nullptr;
   for (int i = threadIdx.x; i < NR * kSelBins; i += blockDim.x) f4r_hist[i] = 0;
 
+  // The body in two forms: FAST for a dense cache and a workgroup whose NST stages are all below k1 (every workgroup
+  // of a row but its last), which addresses a stage through a descriptor of its own and a constant lane offset (no
+  // vector instructions per load); otherwise every key index is clamped to k1 - 1.  One branch per workgroup picks
+  // the form, so neither has a branch inside its stage loop.
+  auto body = [&](auto FASTC) {
+  constexpr bool FAST = decltype(FASTC)::value;
   // queries: head tile T = heads 32 T .. 32 T + 31, lane head 32 T + col; chunks (blocks) hh and 2 + hh of its code
   // row and its scale word.  The raw loads go first and the operands are built after the ring's first loads are
   // issued, so that nothing waits for the queries before the ring starts.
@@ -584,9 +590,9 @@ __global__ __launch_bounds__(kF4rWaves * 64) void idx_score_decode_fp4_ring(IdxA
   // buffer descriptors over the workgroup's own keys [k0, k1) of a dense cache (offsets stay small whatever the cache
   // size, and the range check covers exactly the keys the workgroup may read), or over the whole pool of a paged one
   // (blocks of at least 32 rows, pool under 2 GiB of codes: checked on the host)
-  const int br = a.k.block_table ? a.k.block_rows : 0;
-  const long long rb0 = br ? 0 : (long long)b * a.k.cap + k0;
-  const long long nrows = br ? a.k.pool_rows : (long long)(k1 - k0);
+  const int br = PAGED ? a.k.block_rows : 0;
+  const long long rb0 = PAGED ? 0 : (long long)b * a.k.cap + k0;
+  const long long nrows = PAGED ? a.k.pool_rows : (long long)(k1 - k0);
   const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)((const uint8_t*)a.k.data + rb0 * 64), 0, (int)(nrows * 64), kIdxBufWord3);
   const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
@@ -596,7 +602,7 @@ __global__ __launch_bounds__(kF4rWaves * 64) void idx_score_decode_fp4_ring(IdxA
 #pragma unroll
   for (int st = 0; st < NST; ++st) {
     blk[st][0] = blk[st][1] = 0;
-    if (br) {
+    if constexpr (PAGED) {
       const int sh = __builtin_ctz((unsigned)br);
       const long long tb = (long long)b * (a.k.cap >> sh);
       const int kl = min(k0 + st * kF4rStage + 64 * wave, k1 - 1), kh = min(kl + 32, k1 - 1);
@@ -607,22 +613,42 @@ __global__ __launch_bounds__(kF4rWaves * 64) void idx_score_decode_fp4_ring(IdxA
   // row (relative to the descriptor) of key kst + 64 w + o, o < 64
   auto key_row = [&](int st, int kst, int o) -> int {
     const int key = min(kst + 64 * wave + o, k1 - k0 - 1);
-    return br ? blk[st][o >= 32] * br + ((k0 + key) & (br - 1)) : key;
+    if constexpr (PAGED) return blk[st][o >= 32] * br + ((k0 + key) & (br - 1));
+    else return key;
   };
+  // FAST: the lane's offsets within a stage, one per code instruction (kept in registers: an instruction's immediate
+  // offset would move its LDS destination as well)
+  const int vcode0 = (64 * wave + (lane >> 2)) * 64 + 16 * ((lane & 3) ^ (lane >> 4));
+  const int vcode1 = vcode0 + 1024, vcode2 = vcode0 + 2048, vcode3 = vcode0 + 3072;
+  const int vscale = (64 * wave + lane) * 4;
   // stage st into slot S: code instruction i of wave w moves keys 64 w + 16 i .. + 15 (lane l: key + l / 4, chunk
   // position l % 4 holding code chunk (l % 4) ^ (l / 16)); the scale instruction moves the wave's 64 scale words
   // (lane l: key 64 w + l).  Keys past k1 repeat key k1 - 1.
   auto issue = [&](auto SC, int st) {
     constexpr int S = decltype(SC)::value;
     const int kst = st * kF4rStage;  // relative to k0
+    uint8_t* const lc = f4r_codes<S>() + 64 * wave * 64;
+    uint8_t* const ls = f4r_scales<S>() + 64 * wave * 4;
+    if constexpr (FAST) {
+      // a descriptor over the stage's own 512 keys (scalar arithmetic), all of them below k1
+      const __amdgpu_buffer_rsrc_t cst = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)((const uint8_t*)a.k.data + (rb0 + kst) * 64), 0, kF4rStage * 64, kIdxBufWord3);
+      const __amdgpu_buffer_rsrc_t sst = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)((const uint8_t*)a.k.scale + (rb0 + kst) * 4), 0, kF4rStage * 4, kIdxBufWord3);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(cst, (idx_lds_void_t*)lc, 16, vcode0, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(cst, (idx_lds_void_t*)(lc + 1024), 16, vcode1, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(cst, (idx_lds_void_t*)(lc + 2048), 16, vcode2, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(cst, (idx_lds_void_t*)(lc + 3072), 16, vcode3, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(sst, (idx_lds_void_t*)ls, 4, vscale, 0, 0, 0);
+    } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = key_row(st, kst, 16 * i + (lane >> 2));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(crs, (idx_lds_void_t*)(f4r_codes<S>() + (64 * wave + 16 * i) * 64), 16,
-                                               row * 64 + 16 * ((lane & 3) ^ (lane >> 4)), 0, 0, 0);
+      for (int i = 0; i < 4; ++i) {
+        const int row = key_row(st, kst, 16 * i + (lane >> 2));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(crs, (idx_lds_void_t*)(lc + 16 * i * 64), 16,
+                                                 row * 64 + 16 * ((lane & 3) ^ (lane >> 4)), 0, 0, 0);
+      }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, (idx_lds_void_t*)ls, 4, key_row(st, kst, lane) * 4, 0, 0, 0);
     }
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, (idx_lds_void_t*)(f4r_scales<S>() + 64 * wave * 4), 4,
-                                             key_row(st, kst, lane) * 4, 0, 0, 0);
   };
   // key operands of the wave's key tile u (keys 64 w + 32 u + col of stage slot S); ks holds the scales of blocks
   // hh and 2 + hh in its bytes 0 and 2, which the instruction's byte select picks
@@ -700,9 +726,10 @@ __global__ __launch_bounds__(kF4rWaves * 64) void idx_score_decode_fp4_ring(IdxA
       const float s1 = head_tree32(acc1, wv[r]);
       const uint32_t key0 = score_key(s0), key1 = score_key(s1);
       kbin[r][st] = (key0 >> 21) | ((key1 >> 21) << 16);
-      // lane (col, hh) stores tile hh's key col: 64 keys per store and row
+      // lane (col, hh) stores tile hh's key col: 64 keys per store and row (a lane past k1 held key k1 - 1 and
+      // writes its score again)
       const int e = k0 + st * kF4rStage + 64 * wave + 32 * hh + col;
-      a.keys[(long long)(qrow0 + r) * a.N + min(e, k1 - 1)] = hh ? key1 : key0;
+      a.keys[(long long)(qrow0 + r) * a.N + (FAST ? e : min(e, k1 - 1))] = hh ? key1 : key0;
     }
   };
   unroll_steps<0, NST>(step);
@@ -719,6 +746,9 @@ __global__ __launch_bounds__(kF4rWaves * 64) void idx_score_decode_fp4_ring(IdxA
     for (int r = 0; r < NR; ++r)
       flush_hist(f4r_hist + r * kSelBins, a.sel_state + (long long)(qrow0 + r) * kSelStateInts);
   }
+  };
+  if (!PAGED && k1 - k0 == NST * kF4rStage) body(std::true_type{});
+  else body(std::false_type{});
 }
 
 // key ranges of a decode launch: a multiple of the eight XCDs when several rows share them
@@ -752,17 +782,24 @@ hipError_t launch_indexer_scores(const IdxArgs& a, hipStream_t st, hipEvent_t eb
       const dim3 grid((unsigned)decode_grid_x((nvis_max + nst * kF4rStage - 1) / (nst * kF4rStage), a.Sq / nr),
                       (unsigned)groups);
       const dim3 block(kF4rWaves * 64);
+      const bool paged = a.k.block_table != nullptr;
+#define LCA_F4R(NS, R, PG) hipExtLaunchKernelGGL((idx_score_decode_fp4_ring<NS, R, PG>), grid, block, 0, st, eb, ee, 0, a)
+#define LCA_F4R_NST(R, PG)                \
+  do {                                    \
+    if (nst == 8) LCA_F4R(8, R, PG);      \
+    else if (nst == 4) LCA_F4R(4, R, PG); \
+    else if (nst == 2) LCA_F4R(2, R, PG); \
+    else LCA_F4R(1, R, PG);               \
+  } while (0)
       if (nr == 2) {
-        if (nst == 8) hipExtLaunchKernelGGL((idx_score_decode_fp4_ring<8, 2>), grid, block, 0, st, eb, ee, 0, a);
-        else if (nst == 4) hipExtLaunchKernelGGL((idx_score_decode_fp4_ring<4, 2>), grid, block, 0, st, eb, ee, 0, a);
-        else if (nst == 2) hipExtLaunchKernelGGL((idx_score_decode_fp4_ring<2, 2>), grid, block, 0, st, eb, ee, 0, a);
-        else hipExtLaunchKernelGGL((idx_score_decode_fp4_ring<1, 2>), grid, block, 0, st, eb, ee, 0, a);
+        if (paged) LCA_F4R_NST(2, true);
+        else LCA_F4R_NST(2, false);
       } else {
-        if (nst == 8) hipExtLaunchKernelGGL((idx_score_decode_fp4_ring<8, 1>), grid, block, 0, st, eb, ee, 0, a);
-        else if (nst == 4) hipExtLaunchKernelGGL((idx_score_decode_fp4_ring<4, 1>), grid, block, 0, st, eb, ee, 0, a);
-        else if (nst == 2) hipExtLaunchKernelGGL((idx_score_decode_fp4_ring<2, 1>), grid, block, 0, st, eb, ee, 0, a);
-        else hipExtLaunchKernelGGL((idx_score_decode_fp4_ring<1, 1>), grid, block, 0, st, eb, ee, 0, a);
+        if (paged) LCA_F4R_NST(1, true);
+        else LCA_F4R_NST(1, false);
       }
+#undef LCA_F4R_NST
+#undef LCA_F4R
       return hipGetLastError();
     }
     // a fixed key range per workgroup (NST stages of 4 waves x KPW keys), the grid grows with the context; fewer
