@@ -516,6 +516,15 @@ __device__ __forceinline__ uint8_t* f4r_scales() {
 }
 
 typedef __attribute__((address_space(3))) void idx_lds_void_t;
+typedef __attribute__((address_space(3))) int idx_lds_int_t;
+
+// Adds one to an LDS counter without a result.  Written as an instruction of its own, so that the compiler does not
+// wait for the LDS-direct loads in flight before it (it cannot tell that they write other LDS addresses); LDS
+// operations complete in order, so the compiler's own counts of outstanding LDS operations stay safe.
+__device__ __forceinline__ void lds_count_one(int* p) {
+  const uint32_t addr = (uint32_t)(uintptr_t)(idx_lds_int_t*)p;
+  asm volatile("ds_add_u32 %0, %1" : : "v"(addr), "v"(1));
+}
 constexpr int kIdxBufWord3 = 0x00020000;  // buffer descriptor word 3: raw untyped loads
 
 // s_waitcnt immediate for vmcnt(n) with the other counters untouched
@@ -557,6 +566,7 @@ __global__ __launch_bounds__(kF4rWaves * 64) void idx_score_decode_fp4_ring(IdxA
   if (k0 >= k1) return;  // block-uniform
   const bool hist = a.sel_state != nullptr;
   for (int i = threadIdx.x; i < NR * kSelBins; i += blockDim.x) f4r_hist[i] = 0;
+  if (hist) __syncthreads();  // the histograms are zeroed before any count (nothing is in flight yet)
 
   // The body in two forms: FAST for a dense cache and a workgroup whose NST stages are all below k1 (every workgroup
   // of a row but its last), which addresses a stage through a descriptor of its own and a constant lane offset (no
@@ -696,9 +706,7 @@ __global__ __launch_bounds__(kF4rWaves * 64) void idx_score_decode_fp4_ring(IdxA
 
   // Stage st sits in slot st % 4.  A wave loads exactly the keys it scores, so the ring needs no barrier: step st
   // waits for this wave's own loads of stage st, starts stage st + 3 in the slot this wave finished with in step
-  // st - 1, scores it for every row and stores.  The histogram counts wait until the ring is drained: an LDS atomic
-  // while ring loads are in flight would make the compiler wait for all of them.
-  uint32_t kbin[NR][NST];  // lane (col, hh): the histogram bins of tile 0 (low half) and tile 1's key col
+  // st - 1, scores it for every row, stores the keys and counts them in the row histograms.
   auto step = [&](auto STC) {
     constexpr int st = decltype(STC)::value;
     using SC = std::integral_constant<int, st % 4>;
@@ -725,23 +733,16 @@ __global__ __launch_bounds__(kF4rWaves * 64) void idx_score_decode_fp4_ring(IdxA
       __builtin_amdgcn_sched_barrier(0);
       const float s1 = head_tree32(acc1, wv[r]);
       const uint32_t key0 = score_key(s0), key1 = score_key(s1);
-      kbin[r][st] = (key0 >> 21) | ((key1 >> 21) << 16);
-      // lane (col, hh) stores tile hh's key col: 64 keys per store and row (a lane past k1 held key k1 - 1 and
-      // writes its score again)
+      // lane (col, hh) stores and counts tile hh's key col: 64 keys per store and row (a lane past k1 held key
+      // k1 - 1 and writes its score again, uncounted)
       const int e = k0 + st * kF4rStage + 64 * wave + 32 * hh + col;
-      a.keys[(long long)(qrow0 + r) * a.N + (FAST ? e : min(e, k1 - 1))] = hh ? key1 : key0;
+      const uint32_t key = hh ? key1 : key0;
+      a.keys[(long long)(qrow0 + r) * a.N + (FAST ? e : min(e, k1 - 1))] = key;
+      if (hist && ((FAST && NR == 1) || e < nv[r])) lds_count_one(&f4r_hist[r * kSelBins + (key >> 21)]);
     }
   };
   unroll_steps<0, NST>(step);
   if (hist) {
-    __syncthreads();  // every wave has zeroed its part of the histograms
-#pragma unroll
-    for (int r = 0; r < NR; ++r)
-#pragma unroll
-      for (int st = 0; st < NST; ++st) {
-        const int e = k0 + st * kF4rStage + 64 * wave + 32 * hh + col;
-        if (e < nv[r]) atomicAdd(&f4r_hist[r * kSelBins + (hh ? kbin[r][st] >> 16 : kbin[r][st] & 0xFFFFu)], 1);
-      }
 #pragma unroll
     for (int r = 0; r < NR; ++r)
       flush_hist(f4r_hist + r * kSelBins, a.sel_state + (long long)(qrow0 + r) * kSelStateInts);
