@@ -23,12 +23,29 @@ constexpr size_t kSelDynLds = (size_t)kLdsKeys * 4;
 constexpr int kBorderCap = 2048;  // keys of the border bin kept in LDS for passes 2 and 3
 constexpr int kPerThread = 8;     // entries per thread in the ordered compaction
 
+// Workgroup barrier for LDS only: this wave's LDS operations complete before it, and no global load in flight is
+// waited for (the caller waits for what it needs).
+__device__ __forceinline__ void sel_lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((3 << 14) | (7 << 4) | 0xF);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Workgroup barrier: LDS-only (LDSB) or a full __syncthreads.
+template <bool LDSB>
+__device__ __forceinline__ void sel_barrier() {
+  if constexpr (LDSB) sel_lds_barrier();
+  else __syncthreads();
+}
+
 // Exclusive scan over the block (1024 threads, one value each); `tot` receives the block total.
+template <bool LDSB = false>
 __device__ __forceinline__ int block_excl_scan(int v, int* wsum, int& tot) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int incl = wave_incl_scan(v);
   if (lane == 63) wsum[w] = incl;
-  __syncthreads();
+  sel_barrier<LDSB>();
   int before = 0;
   tot = 0;
 #pragma unroll
@@ -37,18 +54,19 @@ __device__ __forceinline__ int block_excl_scan(int v, int* wsum, int& tot) {
     if (i < w) before += x;
     tot += x;
   }
-  __syncthreads();
+  sel_barrier<LDSB>();
   return before + incl - v;
 }
 
 // Finds, among 2048 histogram bins read in descending order, the bin holding the need-th largest key.
 // Returns the bin; *above receives the number of keys in higher bins.
+template <bool LDSB = false>
 __device__ __forceinline__ int find_bin(const int* hist, int need, int* wsum, int* shared_pair) {
   const int tid = threadIdx.x;
   const int bhi = 2047 - 2 * tid, blo = bhi - 1;
   const int hh = hist[bhi], hl = hist[blo];
   int tot;
-  const int before = block_excl_scan(hh + hl, wsum, tot);
+  const int before = block_excl_scan<LDSB>(hh + hl, wsum, tot);
   if (before < need && before + hh >= need) {
     shared_pair[0] = bhi;
     shared_pair[1] = before;
@@ -56,7 +74,7 @@ __device__ __forceinline__ int find_bin(const int* hist, int need, int* wsum, in
     shared_pair[0] = blo;
     shared_pair[1] = before + hh;
   }
-  __syncthreads();
+  sel_barrier<LDSB>();
   return shared_pair[0];
 }
 
@@ -280,7 +298,6 @@ __device__ __forceinline__ int find_bin256(const int* hist, int need, int* wsum,
 }
 
 __global__ __launch_bounds__(kMbThreads) void topk_collect_kernel(SelArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint32_t mb_lds[];  // the slice's keys
   __shared__ int hist[kSelBins];
   __shared__ int wsum[kMbThreads / 64];
   __shared__ int sh[4];
@@ -294,19 +311,27 @@ __global__ __launch_bounds__(kMbThreads) void topk_collect_kernel(SelArgs a) {
   const int slots = (a.N + kSliceKeys - 1) / kSliceKeys;
   const int s0 = p * kSliceKeys, s1 = min(s0 + kSliceKeys, nvis);
 
-  // the slice's keys and the row histogram, all loads in flight together
+  // thread t takes the slice's keys 16 t .. 16 t + 15 straight into registers (four 16-byte loads when all of them
+  // are visible and the row starts 16-byte aligned), with the row histogram's loads in flight beside them
+  const int j0 = s0 + kMbPerThread * tid;
   uint32_t kv[kMbPerThread];
+  if ((a.N & 3) == 0 && j0 + kMbPerThread <= s1) {
 #pragma unroll
-  for (int u = 0; u < kMbPerThread; ++u) {
-    const int i = s0 + tid + kMbThreads * u;
-    kv[u] = i < s1 ? kg[i] : 0u;
+    for (int u = 0; u < kMbPerThread / 4; ++u) {
+      const uint4 x = *(const uint4*)(kg + j0 + 4 * u);
+      kv[4 * u] = x.x;
+      kv[4 * u + 1] = x.y;
+      kv[4 * u + 2] = x.z;
+      kv[4 * u + 3] = x.w;
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < kMbPerThread; ++u) kv[u] = j0 + u < s1 ? kg[j0 + u] : 0u;
   }
   const int* gh = a.sel_state + (long long)row * kSelStateInts;
   int hv[kSelBins / kMbThreads];
 #pragma unroll
   for (int u = 0; u < kSelBins / kMbThreads; ++u) hv[u] = gh[tid + kMbThreads * u];
-#pragma unroll
-  for (int u = 0; u < kMbPerThread; ++u) mb_lds[tid + kMbThreads * u] = kv[u];
 #pragma unroll
   for (int u = 0; u < kSelBins / kMbThreads; ++u) hist[tid + kMbThreads * u] = hv[u];
   __syncthreads();
@@ -316,10 +341,7 @@ __global__ __launch_bounds__(kMbThreads) void topk_collect_kernel(SelArgs a) {
   // this slice's keys with bin >= b1, in entry order
   int cnt = 0;
 #pragma unroll
-  for (int j = 0; j < kMbPerThread; ++j) {
-    const int jj = kMbPerThread * tid + j;
-    cnt += (s0 + jj < s1 && (int)(mb_lds[jj] >> 21) >= b1) ? 1 : 0;
-  }
+  for (int j = 0; j < kMbPerThread; ++j) cnt += (j0 + j < s1 && (int)(kv[j] >> 21) >= b1) ? 1 : 0;
 #pragma unroll
   for (int u = 0; u < kSelBins / kMbThreads; ++u) hist[tid + kMbThreads * u] = 0;  // reused for pass 2
   int tot;
@@ -327,10 +349,9 @@ __global__ __launch_bounds__(kMbThreads) void topk_collect_kernel(SelArgs a) {
   uint2* seg = a.cand + (long long)row * a.N + s0;
 #pragma unroll
   for (int j = 0; j < kMbPerThread; ++j) {
-    const int jj = kMbPerThread * tid + j;
-    const uint32_t key = mb_lds[jj];
-    if (s0 + jj < s1 && (int)(key >> 21) >= b1) {
-      seg[pos++] = make_uint2(key, (uint32_t)(s0 + jj));
+    const uint32_t key = kv[j];
+    if (j0 + j < s1 && (int)(key >> 21) >= b1) {
+      seg[pos++] = make_uint2(key, (uint32_t)(j0 + j));
       if ((int)(key >> 21) == b1) atomicAdd(&hist[(key >> 10) & 0x7FFu], 1);
     }
   }
@@ -401,15 +422,7 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(SelArgs a) {
   int total;
   const int off = block_excl_scan(c, wsum, total);  // (its barriers also publish both histograms)
   if (tid < P) seg_off[tid] = off;
-  // passes 1 and 2 from the histograms
-  const int b1 = find_bin(hist, k, wsum, sh);
-  int need = k - sh[1];
-  const int b2 = find_bin(hist2, need, wsum, sh);
-  need -= sh[1];
-  const uint32_t prefix12 = ((uint32_t)b1 << 21) | ((uint32_t)b2 << 10);
-#pragma unroll
-  for (int u = 0; u < kSelBins / kFinThreads; ++u) hist[tid + kFinThreads * u] = 0;  // pass 3 counts
-  __syncthreads();
+  sel_lds_barrier();  // the segment offsets
 
   const uint2* cseg = a.cand + (long long)row * a.N;
   const bool in_lds = total <= kCandCap;
@@ -418,12 +431,24 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(SelArgs a) {
     const int sgm = cand_segment(seg_off, P, j);
     return cseg[(long long)sgm * kSliceKeys + (j - seg_off[sgm])];
   };
+  // one round of candidate loads (indices clamp to the last candidate, loaded again and not stored), in flight
+  // while passes 1 and 2 resolve from the histograms behind LDS-only barriers
+  uint2 cv[kFinPer];
   if (in_lds) {
-    // one round: every thread locates and loads its candidates (indices clamp to the last one, loaded again and
-    // not stored), stores them to LDS and counts pass 3 over the keys sharing the 21-bit prefix
-    uint2 cv[kFinPer];
 #pragma unroll
     for (int i = 0; i < kFinPer; ++i) cv[i] = load_cand(min(tid + kFinThreads * i, total - 1));
+  }
+  const int b1 = find_bin<true>(hist, k, wsum, sh);
+  int need = k - sh[1];
+  const int b2 = find_bin<true>(hist2, need, wsum, sh);
+  need -= sh[1];
+  const uint32_t prefix12 = ((uint32_t)b1 << 21) | ((uint32_t)b2 << 10);
+#pragma unroll
+  for (int u = 0; u < kSelBins / kFinThreads; ++u) hist[tid + kFinThreads * u] = 0;  // pass 3 counts
+  sel_lds_barrier();
+
+  if (in_lds) {
+    // the candidates to LDS, and pass 3 counted over the keys sharing the 21-bit prefix
 #pragma unroll
     for (int i = 0; i < kFinPer; ++i) {
       const int j = tid + kFinThreads * i;
@@ -495,8 +520,7 @@ hipError_t launch_topk(const SelArgs& a, hipStream_t st) {
     const int P = (nvis_max + kSliceKeys - 1) / kSliceKeys;
     if (P > kFinMaxSlices) return hipErrorInvalidValue;  // more than 4M entries per row
     if (nvis_max > a.k)
-      hipLaunchKernelGGL(topk_collect_kernel, dim3((unsigned)P, (unsigned)a.rows), dim3(kMbThreads),
-                         (size_t)kSliceKeys * 4, st, a);
+      hipLaunchKernelGGL(topk_collect_kernel, dim3((unsigned)P, (unsigned)a.rows), dim3(kMbThreads), 0, st, a);
     hipLaunchKernelGGL(topk_finish_kernel, dim3((unsigned)a.rows), dim3(kFinThreads), kFinishLds, st, a);
   } else if (nvis_max <= kLdsKeys) {
     const hipError_t e = ensure_dyn_lds((const void*)topk_select_kernel<true>, (int)kSelDynLds);
