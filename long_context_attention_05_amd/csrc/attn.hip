@@ -1462,59 +1462,63 @@ __global__ __launch_bounds__(256) void attn_simt_kernel(AttnArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------------
-// sparse decode attention in two passes (few query rows, H = 64, D = 512, bf16 or mixed entries)
+// sparse decode attention in one pass per 64-entry tile, then the merge (few query rows, H = 64, D = 512)
 // ------------------------------------------------------------------------------------------------
-// With one query row per sequence, splitting a row's entry list over workgroups leaves one 64 x 512 partial output
-// per split -- more bytes than the split's own entries -- and a merge pass over them.  The decode path instead
-// stores the probabilities, which are 64 values per entry:
-//   scores (one workgroup per (query row, 32-entry tile), all 64 heads): S^T = scale * K Q^T for the tile with
-//     v_mfma_f32_16x16x32_bf16, wave w contracting channels [128 w, 128 w + 128) (fp8 entries widened exactly, the
-//     entry scale applied to their part) and the four partial products added in LDS; then per head the tile max
-//     m_t, P_t = e^(S - m_t) (bf16, 0 for padding) and l_t = sum P_t.
-//   values (one workgroup per (query row, 64 channels, 16 heads)): M = max(z, m_t), den = e^(z - M) +
-//     sum_t l_t e^(m_t - M) and the tile weights f_t = e^(m_t - M) / den, then O^T = sum_t f_t V_t^T P_t^T on
-//     v_mfma_f32_16x16x32_bf16: wave w of 8 takes tiles w, w + 8, ..., issues every load of its tiles at once, turns
-//     each tile's channels into a row-major bf16 tile in its own LDS area (fp8 widened and multiplied by the entry
-//     scale) and reads V^T with ds_read_b64_tr_b16; the eight waves' sums are added in LDS at the end.
-// The exact normaliser is known before any value is weighted, so no partial output goes through memory.
-constexpr int kDecTile = 32;                              // list positions per tile
-constexpr int kDecMaxTiles = kDecMaxEntries / kDecTile;   // 64
-constexpr int kDsTile = 64;                               // list positions per score workgroup (two value tiles)
-constexpr int kDsWaves = 8;                               // waves of a score workgroup
-constexpr int kDvRowB = 144;                              // LDS bytes per entry of a value tile (64 bf16 + pad)
-constexpr int kDvWaves = 8;                               // waves of a value workgroup
+// One workgroup per (query row, 64 list positions), all 64 heads.  Since K = V = the entry, the tile that the
+// scores were computed from is still in LDS when its probabilities are known, so the same workgroup forms the
+// tile's partial output:
+//   S^T = scale * K Q^T on v_mfma_f32_16x16x32_bf16: queries (64 KB) and entries are copied into LDS with
+//   row-contiguous global_load_lds (1 KB per instruction, 16-byte chunks XOR-swizzled by row so that operand reads
+//   are conflict-free), wave w contracts channels [128 (w % 4), + 128) of entries [32 (w / 4), + 32) for all heads
+//   (fp8 entries widened exactly, the entry scale applied to their part), and the four channel quarters are added
+//   in LDS in a fixed order;
+//   m = the tile's max per head, P = e^(S - m) (0 for padding), l = sum P;
+//   O^T = V^T P^T on v_mfma_f32_16x16x32_bf16, wave w taking channels [64 w, 64 w + 64) of all heads; V^T is read
+//   with ds_read_b64_tr_b16 from the tile's bf16 rows (the mixed format's fp8 part widened and multiplied by the
+//   entry scale into bf16 rows first), P^T from LDS in the operand layout;
+//   O (bf16) and (m, l) go to the split partials, and attn_merge_kernel folds the tiles and the sink with LSE
+//   weights.
+// Against two passes (scores for the whole list, then values weighted by the exact normaliser) this saves a launch
+// and the second gather of every entry, for a merge over 64 KB of bf16 partials per tile.
+constexpr int kDsTile = 64;    // list positions per workgroup
+constexpr int kDsWaves = 8;    // waves per workgroup
+constexpr int kDfRowB = 1040;  // LDS bytes per head row of the output staging (1024 + 16)
 
 template <int FMT>
-__global__ __launch_bounds__(64 * kDsWaves) void attn_dec_score_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * kDsWaves) void attn_dec_fused_kernel(AttnArgs a) {
   constexpr bool MX = FMT == LCA_MIXED_FP8;
-  // LDS: the 64 x 512 queries (1 KB rows), then the tile's entries (bf16: 1 KB rows; mixed: 448 fp8 bytes, 128
-  // RoPE bytes and 16 bytes of padding).  bf16 rows keep 16-byte chunk c of row r at chunk c ^ (r % 16), so that
-  // the 16 rows an operand read touches fall on distinct banks; the padded mixed rows do the same by their stride.
+  // LDS: [0, 64 KB) the queries, then the channel partials 0-3, then (mixed) the widened value rows, then the output
+  // staging (64 head rows of kDfRowB bytes, reaching into the entry area once that is dead); the entries (bf16: 1 KB
+  // rows, 16-byte chunk c of row r at chunk c ^ (r % 16); mixed: 448 fp8 bytes, 128 RoPE bytes, 16 bytes of padding);
+  // (mixed) the RoPE partials; P^T as [entry block][head block][64 lanes] x 16 bytes.
   constexpr int KROW = MX ? 592 : 1024;
-  __shared__ __attribute__((aligned(16))) uint8_t ds_lds[65536 + kDsTile * KROW];
-  __shared__ uint8_t ds_ok[kDsTile];
-  __shared__ __attribute__((aligned(16))) float ds_esc[kDsTile];
-  uint8_t* const qs = ds_lds;
-  uint8_t* const kt = ds_lds + 65536;
+  constexpr int kEnt = 65536;
+  constexpr int kRope = kEnt + kDsTile * KROW;
+  constexpr int kP = kRope + (MX ? 16384 : 0);
+  __shared__ __attribute__((aligned(16))) uint8_t df_lds[kP + 8192];
+  __shared__ uint8_t df_ok[kDsTile];
+  __shared__ __attribute__((aligned(16))) float df_esc[kDsTile];
+  static_assert(64 * kDfRowB <= kEnt + kDsTile * KROW, "output staging");
+  uint8_t* const qs = df_lds;
+  uint8_t* const kt = df_lds + kEnt;
   const int qrow = blockIdx.x, tile = blockIdx.y;
   const int b = qrow / a.Sq, r = qrow - b * a.Sq;
   const RowList L = row_list(a, b, r);
   const int total = L.nw + L.nc;
-  const int p0 = tile * kDsTile;
-  if (p0 >= total) return;  // past this row's list: the value pass does not read these tiles
+  const int p0 = tile * kDsTile;  // a tile past the row's list runs with every position masked: O = 0, m = -inf
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int hl = lane & 15, grp = lane >> 4;
+  const long long item = (long long)qrow * a.n_splits + tile;
 
   // lane e of every wave resolves tile entry e: its tensor row (row 0 of the compressed tensor for padding), whether
-  // it is a window entry and whether it is real; the copies below take these by readlane / ds_bpermute
-  // (the index load is unconditional -- a read of the sink array where there is no index -- and its value is used
-  // only after the query copies are issued, so that they are not held up by it)
+  // it is a window entry and whether it is real; the copies below take these by readlane / ds_bpermute (the index
+  // load is unconditional -- a read of the sink array where there is no index -- and its value is used only after
+  // the query copies are issued, so that they are not held up by it)
   const int pl = p0 + lane;
   const bool rwl = pl < L.nw;
   const bool sel = !rwl && pl < total;
   const int xl = *(sel ? a.idx + ((long long)qrow * a.k + (pl - L.nw)) : (const int*)a.sink);
-  // queries: wave w copies head rows 8 w .. 8 w + 7, 1 KB per instruction
   {
     const uint8_t* qg = (const uint8_t*)a.q + (long long)qrow * 65536;
 #pragma unroll
@@ -1528,12 +1532,9 @@ __global__ __launch_bounds__(64 * kDsWaves) void attn_dec_score_kernel(AttnArgs 
   __builtin_amdgcn_sched_barrier(0);
   const int rowl = rwl ? (int)(L.w0 + pl - L.raw0) : ((sel & (xl >= 0) & (xl < a.N)) ? xl : -1);
   const bool okl = rowl >= 0;
-  // storage row: the raw tensor is dense; the compressed one may be paged (a dependent table read)
   const long long rabsl = rwl ? (long long)b * a.raw.cap + rowl : tensor_row(a.comp, b, okl ? rowl : 0);
   const int rlo = (int)rabsl, rhi = (int)(rabsl >> 32), rwi = rwl ? 1 : 0;
-  // entries
   if constexpr (!MX) {
-    // wave w copies entries 8 w .. 8 w + 7, one 1 KB row per instruction
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int e = 8 * wave + i;
@@ -1544,8 +1545,6 @@ __global__ __launch_bounds__(64 * kDsWaves) void attn_dec_score_kernel(AttnArgs 
       __builtin_amdgcn_global_load_lds((const void*)src, (void*)(kt + e * 1024), 16, 0, 0);
     }
   } else {
-    // 37 instructions of 64 16-byte slots: slot s is chunk s % 37 of entry s / 37 (28 fp8 chunks, 8 RoPE chunks,
-    // then the padding slot, which copies fp8 chunk 0); wave w issues instructions w, w + 8, ...
 #pragma unroll
     for (int i = 0; i < 5; ++i) {
       const int j = wave + 8 * i;
@@ -1553,8 +1552,6 @@ __global__ __launch_bounds__(64 * kDsWaves) void attn_dec_score_kernel(AttnArgs 
       const long long rabs = ((long long)__builtin_amdgcn_ds_bpermute(4 * e, rhi) << 32) |
                              (uint32_t)__builtin_amdgcn_ds_bpermute(4 * e, rlo);
       const bool rw = __builtin_amdgcn_ds_bpermute(4 * e, rwi) != 0;
-      // (fields selected one by one: a lane-dependent choice of the whole tensor struct would be read through
-      // per-lane pointers)
       const uint8_t* fb = (const uint8_t*)(rw ? a.raw.data : a.comp.data) + rabs * 448;
       const uint8_t* rb = (const uint8_t*)(rw ? a.raw.rope : a.comp.rope) + rabs * 128;
       const uint8_t* g = c < 28 ? fb + 16 * c : c < 36 ? rb + 16 * (c - 28) : fb;
@@ -1562,15 +1559,15 @@ __global__ __launch_bounds__(64 * kDsWaves) void attn_dec_score_kernel(AttnArgs 
     }
   }
   if (wave == 0) {
-    ds_ok[lane] = okl ? 1 : 0;
+    df_ok[lane] = okl ? 1 : 0;
     if constexpr (MX) {
       const long long rabs = ((long long)rhi << 32) | (uint32_t)rlo;
-      ds_esc[lane] = (rwi ? (const float*)a.raw.scale : (const float*)a.comp.scale)[rabs];
+      df_esc[lane] = (rwi ? (const float*)a.raw.scale : (const float*)a.comp.scale)[rabs];
     }
   }
   __syncthreads();  // every copy has landed
 
-  // wave (cs, eh): channels [128 cs, 128 cs + 128) of entries [32 eh, 32 eh + 32) for all 64 heads
+  // S^T: wave (cs, eh) takes channels [128 cs, 128 cs + 128) of entries [32 eh, 32 eh + 32) for all 64 heads
   const int cs = wave & 3, eh = wave >> 2;
   f32x4_t acc[2][4], accr[2][4];
 #pragma unroll
@@ -1582,7 +1579,7 @@ __global__ __launch_bounds__(64 * kDsWaves) void attn_dec_score_kernel(AttnArgs 
     }
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    const int c = 16 * cs + 4 * ks + grp;  // the lane's 16-byte chunk: channels 8 c .. 8 c + 7
+    const int c = 16 * cs + 4 * ks + grp;
     bf16x8_t qb[4];
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb)
@@ -1610,21 +1607,30 @@ __global__ __launch_bounds__(64 * kDsWaves) void attn_dec_score_kernel(AttnArgs 
       }
     }
   }
-  __syncthreads();  // the staged rows are dead: the partial products go over them
-  // partials [slot][entry block 2 eh + eb][head block][lane]: slot = channel quarter (mixed: slot 4 = RoPE part)
-  f32x4_t* part = (f32x4_t*)ds_lds;
+  __syncthreads();  // the queries are dead: the channel partials go over them
+  // partials [slot][entry block 2 eh + eb][head block][lane]: slot = channel quarter; mixed: the RoPE part apart
+  f32x4_t* part = (f32x4_t*)qs;
+  f32x4_t* partr = (f32x4_t*)(df_lds + kRope);
 #pragma unroll
   for (int eb = 0; eb < 2; ++eb)
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb) {
       part[((cs * 4 + 2 * eh + eb) * 4 + hb) * 64 + lane] = acc[eb][hb];
       if constexpr (MX)
-        if (cs == 3) part[((4 * 4 + 2 * eh + eb) * 4 + hb) * 64 + lane] = accr[eb][hb];
+        if (cs == 3) partr[((2 * eh + eb) * 4 + hb) * 64 + lane] = accr[eb][hb];
     }
+  if constexpr (!MX) {
+    // padding rows of the value tile become zero (their probabilities are zero, and zero times an unloaded row must
+    // not make a NaN): wave w clears its own rows 8 w .. 8 w + 7
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int e = 8 * wave + i;
+      if (!df_ok[e]) *(u32x4_t*)(kt + e * 1024 + 16 * lane) = u32x4_t{0u, 0u, 0u, 0u};
+    }
+  }
   __syncthreads();
 
-  // thread (head h, group g) finishes entries 8 g .. 8 g + 7 of head h: entry 16 B + er of head block h / 16 sits in
-  // lane 16 (er / 4) + h % 16, element er % 4, of entry block B
+  // thread (head h, group g) finishes entries 8 g .. 8 g + 7 of head h
   const int h = tid >> 3, g = tid & 7;
   const int blk = g >> 1, l0 = 32 * (g & 1) + (h & 15), hb = h >> 4;
   float sv[8];
@@ -1633,231 +1639,116 @@ __global__ __launch_bounds__(64 * kDsWaves) void attn_dec_score_kernel(AttnArgs 
     const int l = l0 + 16 * half;
     f32x4_t sm = (part[((0 * 4 + blk) * 4 + hb) * 64 + l] + part[((1 * 4 + blk) * 4 + hb) * 64 + l]) +
                  (part[((2 * 4 + blk) * 4 + hb) * 64 + l] + part[((3 * 4 + blk) * 4 + hb) * 64 + l]);
-    if constexpr (MX) sm = sm * *(const f32x4_t*)&ds_esc[8 * g + 4 * half] + part[((4 * 4 + blk) * 4 + hb) * 64 + l];
+    if constexpr (MX) sm = sm * *(const f32x4_t*)&df_esc[8 * g + 4 * half] + partr[(blk * 4 + hb) * 64 + l];
 #pragma unroll
     for (int x = 0; x < 4; ++x) sv[4 * half + x] = a.scale * sm[x];
   }
-  // per 32-entry value tile (groups g / 4): max, probabilities, sum
+  // the tile's max per head (the 8 groups of a head are 8 neighbouring lanes), probabilities and sum
   float mt = -INFINITY;
 #pragma unroll
   for (int j = 0; j < 8; ++j)
-    if (ds_ok[8 * g + j]) mt = fmaxf(mt, sv[j]);
+    if (df_ok[8 * g + j]) mt = fmaxf(mt, sv[j]);
   mt = fmaxf(mt, __shfl_xor(mt, 1));
   mt = fmaxf(mt, __shfl_xor(mt, 2));
+  mt = fmaxf(mt, __shfl_xor(mt, 4));
   float pv[8], ls = 0.0f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    pv[j] = ds_ok[8 * g + j] ? __expf(sv[j] - mt) : 0.0f;
+    pv[j] = df_ok[8 * g + j] ? __expf(sv[j] - mt) : 0.0f;
     ls += pv[j];
   }
   ls += __shfl_xor(ls, 1);
   ls += __shfl_xor(ls, 2);
-  // P in the value pass's operand order: per (row, head group, tile) 64 lanes x 16 bytes, lane 16 q + (h % 16)
-  // holding entries 8 q .. 8 q + 7 of the tile for head h
-  const int t = 2 * tile + (g >> 2), q = g & 3;
-  const u32x4_t pk = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]), pack_bf16x2(pv[4], pv[5]),
-                      pack_bf16x2(pv[6], pv[7])};
-  *(u32x4_t*)(a.dec_p + ((((long long)qrow * 4 + hb) * a.dec_tiles + t) * 64 + 16 * q + (h & 15)) * 8) = pk;
-  if (q == 0) ((float2*)a.dec_ml)[((long long)qrow * a.dec_tiles + t) * 64 + h] = make_float2(mt, ls);
-}
+  ls += __shfl_xor(ls, 4);
+  // P^T operand of entry block g / 4, head block h / 16: lane 16 (g % 4) + h % 16 holds entries 8 g .. 8 g + 7
+  u32x4_t* const pt = (u32x4_t*)(df_lds + kP);
+  pt[((g >> 2) * 4 + hb) * 64 + 16 * (g & 3) + (h & 15)] =
+      u32x4_t{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]), pack_bf16x2(pv[4], pv[5]),
+              pack_bf16x2(pv[6], pv[7])};
+  if (g == 0) ((float2*)a.part_ml)[item * 64 + h] = make_float2(mt, ls);
+  __syncthreads();  // the channel partials are read and P^T is written
 
-// NTI: the most tiles a wave takes (every wave loads all of its tiles at once).  The occupancy is stated so that the
-// compiler keeps the loads in distinct registers rather than reusing them at the price of waits: 4 waves per SIMD
-// (two workgroups per CU) for short lists, 2 for long ones.
-template <int FMT, int NTI>
-__global__ __launch_bounds__(64 * kDvWaves) __attribute__((amdgpu_waves_per_eu(NTI <= 4 ? 4 : 2, NTI <= 4 ? 4 : 2)))
-void attn_dec_value_kernel(AttnArgs a) {
-  constexpr int kGroups = 4 * kDvWaves;  // tile groups of the weight computation (16 heads x kGroups threads)
-  constexpr int kPer = kDecMaxTiles / kGroups;
-  __shared__ __attribute__((aligned(16))) uint8_t dvt[kDvWaves][kDecTile * kDvRowB];  // each wave's value tile
-  __shared__ int drows[kDecMaxEntries];
-  __shared__ float dfac[kDecMaxTiles][16];
-  __shared__ float dred[kGroups][16];
-  const int qrow = blockIdx.x, cb = blockIdx.y, hg = blockIdx.z;
-  const int b = qrow / a.Sq, r = qrow - b * a.Sq;
-  const RowList L = row_list(a, b, r);
-  const int total = L.nw + L.nc;
-  const int nt = (total + kDecTile - 1) / kDecTile;
-  const int T = a.dec_tiles;
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int hl = lane & 15, grp = lane >> 4;
-
-  // rows of all T * 32 list positions (-1: padding or past the list)
-  for (int p = tid; p < T * kDecTile; p += 64 * kDvWaves) {
-    drows[p] = p < total ? list_row(a, L, b, r, p) : -1;
-  }
-  // this thread's tiles' (m_t, l_t) for head 16 hg + (tid % 16) and that head's sink; both read before the value
-  // loads (a load issued after them could only be waited for together with all of them), tiles past the list
-  // reading the last tile and dropped below
-  const int hh = tid & 15, tg = tid >> 4;
-  const int head = 16 * hg + hh;
-  float2 mlv[kPer];
+  uint8_t* vbase = kt;
+  if constexpr (MX) {
+    // the value rows in bf16 over the dead partials: thread t widens chunks (t % 8) + 8 i of entry t / 8 (fp8 times
+    // the entry scale; padding rows zero), stored at chunk c ^ (e % 16) of a 1 KB row
+    const int e = tid >> 3;
+    const float sc = df_ok[e] ? df_esc[e] : 0.0f;
+    const uint8_t* src = kt + e * KROW;
 #pragma unroll
-  for (int i = 0; i < kPer; ++i)
-    mlv[i] = ((const float2*)a.dec_ml)[((long long)qrow * T + min(tg + kGroups * i, T - 1)) * 64 + head];
-  const float z = a.sink[head];
-  __syncthreads();
-
-  // wave w: tiles w, w + kDvWaves, ... (nti of them); acc[d] = O^T for channels 64 cb + 16 d + 4 grp + x, head
-  // 16 hg + hl
-  const int nti = nt > wave ? (nt - wave + kDvWaves - 1) / kDvWaves : 0;
-  f32x4_t acc[4];
-#pragma unroll
-  for (int d = 0; d < 4; ++d) acc[d] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  uint8_t* vt = dvt[wave];
-  const uint16_t* pbase = a.dec_p + (((long long)qrow * 4 + hg) * T * 64 + lane) * 8;
-  // the V^T reads: rows 8 grp + 4 half + hl / 4, channels 16 d + 4 (hl % 4)
-  const uint8_t* vtr = vt + (8 * grp + (hl >> 2)) * kDvRowB + 8 * (hl & 3);
-
-  // The body twice, for bf16 channels and for fp8 channels (the mixed cache's blocks 0..6), so that neither has a
-  // branch between its loads.
-  auto run = [&](auto f8c) {
-    constexpr bool F8 = decltype(f8c)::value;
-    u32x4_t vr[NTI][4];
-    float es[NTI][2];
-    bool ok[NTI][4];
-    u32x4_t pr[NTI];
-    // every load of the wave's tiles (slots past its last tile repeat a valid tile, so that the count is fixed)
-#pragma unroll
-    for (int i = 0; i < NTI; ++i) {
-      const int t = min(wave + kDvWaves * min(i, max(nti, 1) - 1), T - 1);
-      pr[i] = *(gbl_u32x4_t*)(pbase + 512 * t);
-      if constexpr (!F8) {
-        // entries (lane / 8) + 8 k, 16 bytes (8 channels) at chunk lane % 8
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int p = 32 * t + (lane >> 3) + 8 * k;
-          const int row = drows[p];
-          ok[i][k] = row >= 0;
-          const bool rw = p < L.nw;
-          // (fields selected one by one: a lane-dependent choice of the whole tensor struct would be read through
-          // per-lane pointers)
-          const long long rabs = row >= 0 ? row : 0;
-          const uint8_t* vp = FMT == LCA_MIXED_FP8
-                                  ? (const uint8_t*)(rw ? a.raw.rope : a.comp.rope) + rabs * 128
-                                  : (const uint8_t*)(rw ? a.raw.data : a.comp.data) + rabs * 1024 + 128 * cb;
-          vr[i][k] = *(gbl_u32x4_t*)(vp + 16 * (lane & 7));
-        }
+    for (int i = 0; i < 8; ++i) {
+      const int c = (tid & 7) + 8 * i;
+      u32x4_t w;
+      if (c < 56) {
+        const uint2 f = *(const uint2*)(src + 8 * c);
+        const f32x2_t a0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)f.x, false);
+        const f32x2_t a1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)f.x, true);
+        const f32x2_t a2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)f.y, false);
+        const f32x2_t a3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)f.y, true);
+        w = u32x4_t{pack_bf16x2(a0[0] * sc, a0[1] * sc), pack_bf16x2(a1[0] * sc, a1[1] * sc),
+                    pack_bf16x2(a2[0] * sc, a2[1] * sc), pack_bf16x2(a3[0] * sc, a3[1] * sc)};
       } else {
-        // entries (lane / 4) + 16 k, 16 fp8 channels at chunk lane % 4, and the entry scales
+        const u32x4_t v = *(const u32x4_t*)(src + 448 + 16 * (c - 56));
+        const u32x4_t zero = {0u, 0u, 0u, 0u};
+        w = df_ok[e] ? v : zero;
+      }
+      *(u32x4_t*)(qs + e * 1024 + 16 * (c ^ (e & 15))) = w;
+    }
+    __syncthreads();
+    vbase = qs;
+  }
+
+  // O^T += V^T P^T: wave w, channels 64 w + 16 dt + 4 grp + x (dt < 4) of head 16 hb + hl in oacc[hb][dt].  The A
+  // operand's K slots 8 grp .. 8 grp + 7 are entries 8 grp .. 8 grp + 7 of the entry block, as in P^T: lane (hl, grp)
+  // addresses rows R1 = 8 grp + hl / 4 and R2 = R1 + 4 at bytes 8 (hl % 4) + 32 dt + 128 w, so ds_read_b64_tr_b16
+  // hands lane 4 a + e of the group channel 4 a + e of four consecutive entries.  Logical chunk C of row R sits at
+  // chunk C ^ (R % 16); dt flips chunk bits 1-2, which the lane's chunk at dt = 0 leaves clear.
+  f32x4_t oacc[4][4];
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          const int p = 32 * t + (lane >> 2) + 16 * k;
-          const int row = drows[p];
-          ok[i][k] = row >= 0;
-          const bool rw = p < L.nw;
-          const long long rabs = row >= 0 ? row : 0;
-          vr[i][k] = *(gbl_u32x4_t*)((const uint8_t*)(rw ? a.raw.data : a.comp.data) + rabs * 448 + 64 * cb +
-                                     16 * (lane & 3));
-          es[i][k] = ((const float*)(rw ? a.raw.scale : a.comp.scale))[rabs];
-        }
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) oacc[i][dt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  {
+    const int r1 = 8 * grp + (hl >> 2), r2 = r1 + 4;
+    const int cb = ((hl & 3) >> 1) + 8 * wave;
+    const uint8_t* vp1 = vbase + r1 * 1024 + 8 * (hl & 1);
+    const uint8_t* vp2 = vbase + r2 * 1024 + 8 * (hl & 1);
+    const int vc1 = 16 * (cb ^ (r1 & 15)), vc2 = 16 * (cb ^ (r2 & 15));
+#pragma unroll
+    for (int eb = 0; eb < 2; ++eb) {
+      bf16x8_t pb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pb[i] = __builtin_bit_cast(bf16x8_t, pt[(eb * 4 + i) * 64 + lane]);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const s16x4_t v0 =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vp1 + eb * 32 * 1024 + (vc1 ^ (32 * dt))));
+        const s16x4_t v1 =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vp2 + eb * 32 * 1024 + (vc2 ^ (32 * dt))));
+        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          oacc[i][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[i], oacc[i][dt], 0, 0, 0);
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
-
-    // while the loads are in flight: M = max(z, m_t), den = e^(z - M) + sum_t l_t e^(m_t - M) and
-    // f_t = e^(m_t - M) / den per head of the group (LDS-only barriers: the loads are not waited for)
-    {
-      float mx = -INFINITY;
+  }
+  __syncthreads();  // every value and P^T read is done: the staging goes over the value rows
+  // the tile's partial output in bf16 through LDS, so that each store writes a whole 1 KB head row
 #pragma unroll
-      for (int i = 0; i < kPer; ++i)
-        if (tg + kGroups * i < nt) mx = fmaxf(mx, mlv[i].x);
-      dred[tg][hh] = mx;
-      pd_barrier();
-      float M = z;
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int gi = 0; gi < kGroups; ++gi) M = fmaxf(M, dred[gi][hh]);
-      float d = 0.0f;
-#pragma unroll
-      for (int i = 0; i < kPer; ++i)
-        if (tg + kGroups * i < nt && mlv[i].x != -INFINITY) d += mlv[i].y * __expf(mlv[i].x - M);
-      pd_barrier();
-      dred[tg][hh] = d;
-      pd_barrier();
-      float den = (z == -INFINITY) ? 0.0f : __expf(z - M);
-#pragma unroll
-      for (int gi = 0; gi < kGroups; ++gi) den += dred[gi][hh];
-      const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-#pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        const int t = tg + kGroups * i;
-        if (t < nt) dfac[t][hh] = (mlv[i].x == -INFINITY) ? 0.0f : __expf(mlv[i].x - M) * inv;
-      }
-      if (cb == 0 && tg == 0 && a.lse)
-        a.lse[(long long)qrow * 64 + head] = (M == -INFINITY) ? -INFINITY : M + __logf(den);
-      pd_barrier();
+    for (int dt = 0; dt < 4; ++dt) {
+      uint2 w2;
+      w2.x = pack_bf16x2(oacc[i][dt][0], oacc[i][dt][1]);
+      w2.y = pack_bf16x2(oacc[i][dt][2], oacc[i][dt][3]);
+      *(uint2*)(qs + (16 * i + hl) * kDfRowB + 2 * (64 * wave + 16 * dt + 4 * grp)) = w2;
     }
-
-#pragma unroll
-    for (int i = 0; i < NTI; ++i) {
-      if (i < nti) {
-        const int t = wave + kDvWaves * i;
-        // the tile's channels, row-major bf16 (padding rows zero: their probabilities are zero, and zero times an
-        // unwritten row must not make a NaN); the empty asm keeps each use of the loaded data below the barriers
-        if constexpr (!F8) {
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            u32x4_t v = vr[i][k];
-            asm volatile("" : "+v"(v));
-            const u32x4_t zero = {0u, 0u, 0u, 0u};
-            *(u32x4_t*)(vt + ((lane >> 3) + 8 * k) * kDvRowB + 16 * (lane & 7)) = ok[i][k] ? v : zero;
-          }
-        } else {
-#pragma unroll
-          for (int k = 0; k < 2; ++k) {
-            u32x4_t v = vr[i][k];
-            asm volatile("" : "+v"(v));
-            const float sc = ok[i][k] ? es[i][k] : 0.0f;
-            uint32_t w[8];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[q], false);
-              const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[q], true);
-              w[2 * q] = pack_bf16x2(lo[0] * sc, lo[1] * sc);
-              w[2 * q + 1] = pack_bf16x2(hi[0] * sc, hi[1] * sc);
-            }
-            uint8_t* dst = vt + ((lane >> 2) + 16 * k) * kDvRowB + 32 * (lane & 3);
-            *(u32x4_t*)dst = u32x4_t{w[0], w[1], w[2], w[3]};
-            *(u32x4_t*)(dst + 16) = u32x4_t{w[4], w[5], w[6], w[7]};
-          }
-        }
-        const float f = dfac[t][hl];
-        const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pr[i]);
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vtr + 32 * d));
-          const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vtr + 4 * kDvRowB + 32 * d));
-          const bf16x8_t av = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-          const f32x4_t pvt =
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-          acc[d] += f * pvt;
-        }
-      }
-    }
-  };
-  if (FMT == LCA_MIXED_FP8 && cb < 7)
-    run(std::true_type{});
-  else
-    run(std::false_type{});
-
-  // the eight waves' sums: wave w < 4 finishes channel block 16 w of the 64
-  f32x4_t* mg = (f32x4_t*)dvt[wave];
-#pragma unroll
-  for (int d = 0; d < 4; ++d) mg[d * 64 + lane] = acc[d];
   __syncthreads();
-  if (wave >= 4) return;
-  f32x4_t o = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  uint8_t* const po = (uint8_t*)a.part_o + item * (64 * 512 * 2);
 #pragma unroll
-  for (int w = 0; w < kDvWaves; ++w) o += ((const f32x4_t*)dvt[w])[wave * 64 + lane];
-  const long long oi = ((long long)qrow * 64 + 16 * hg + hl) * 512 + 64 * cb + 16 * wave + 4 * grp;
-  if (a.out_format == LCA_F32) {
-    *(f32x4_t*)((float*)a.out + oi) = o;
-  } else {
-    uint2 w2;
-    w2.x = pack_bf16x2(o[0], o[1]);
-    w2.y = pack_bf16x2(o[2], o[3]);
-    *(uint2*)((uint16_t*)a.out + oi) = w2;
+  for (int i = 0; i < 8; ++i) {
+    const int head = 8 * wave + i;
+    *(u32x4_t*)(po + head * 1024 + 16 * lane) = *(const u32x4_t*)(qs + head * kDfRowB + 16 * lane);
   }
 }
 
@@ -2009,21 +1900,6 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
   }
 }
 
-// The value pass with the smallest per-wave load round that holds a wave's nti tiles (at most 8 per round).
-template <int FMT>
-void launch_dec_value(int nti, dim3 grid, hipStream_t st, hipEvent_t ee, const AttnArgs& a) {
-  const dim3 blk(64 * kDvWaves);
-  switch (nti <= 1 ? 1 : nti >= 7 ? 8 : nti) {
-    case 1: hipExtLaunchKernelGGL((attn_dec_value_kernel<FMT, 1>), grid, blk, 0, st, nullptr, ee, 0, a); break;
-    case 2: hipExtLaunchKernelGGL((attn_dec_value_kernel<FMT, 2>), grid, blk, 0, st, nullptr, ee, 0, a); break;
-    case 3: hipExtLaunchKernelGGL((attn_dec_value_kernel<FMT, 3>), grid, blk, 0, st, nullptr, ee, 0, a); break;
-    case 4: hipExtLaunchKernelGGL((attn_dec_value_kernel<FMT, 4>), grid, blk, 0, st, nullptr, ee, 0, a); break;
-    case 5: hipExtLaunchKernelGGL((attn_dec_value_kernel<FMT, 5>), grid, blk, 0, st, nullptr, ee, 0, a); break;
-    case 6: hipExtLaunchKernelGGL((attn_dec_value_kernel<FMT, 6>), grid, blk, 0, st, nullptr, ee, 0, a); break;
-    default: hipExtLaunchKernelGGL((attn_dec_value_kernel<FMT, 8>), grid, blk, 0, st, nullptr, ee, 0, a); break;
-  }
-}
-
 bool attn_uses_mfma(int H, int D, int q_format, int kv_format) {
   return H == 64 && D == 512 && q_format == LCA_BF16 && (kv_format == LCA_BF16 || kv_format == LCA_MIXED_FP8);
 }
@@ -2033,17 +1909,13 @@ hipError_t launch_attn(AttnArgs a, hipStream_t st, hipEvent_t eb, hipEvent_t ee)
   dim3 grid((unsigned)a.n_splits, (unsigned)a.Sq, (unsigned)a.B);
   clear_stale_error();
   if (mfma && a.hg_mode == 3) {
-    const dim3 sgrid((unsigned)(a.B * a.Sq), (unsigned)(a.dec_tiles / 2));
-    const dim3 vgrid((unsigned)(a.B * a.Sq), 8u, 4u);
-    const int nti = (a.dec_tiles + kDvWaves - 1) / kDvWaves;  // most tiles a value-pass wave takes
-    if (a.comp.format == LCA_BF16) {
-      hipExtLaunchKernelGGL(attn_dec_score_kernel<LCA_BF16>, sgrid, dim3(64 * kDsWaves), 0, st, eb, nullptr, 0, a);
-      launch_dec_value<LCA_BF16>(nti, vgrid, st, ee, a);
-    } else {
-      hipExtLaunchKernelGGL(attn_dec_score_kernel<LCA_MIXED_FP8>, sgrid, dim3(64 * kDsWaves), 0, st, eb, nullptr, 0,
-                            a);
-      launch_dec_value<LCA_MIXED_FP8>(nti, vgrid, st, ee, a);
-    }
+    // one workgroup per (row, 64 list positions), bf16 partials, then the merge
+    if (a.part_bf16 != 1 || a.n_splits > 32) return hipErrorInvalidValue;
+    const dim3 fgrid((unsigned)(a.B * a.Sq), (unsigned)a.n_splits);
+    if (a.comp.format == LCA_BF16)
+      hipExtLaunchKernelGGL(attn_dec_fused_kernel<LCA_BF16>, fgrid, dim3(64 * kDsWaves), 0, st, eb, ee, 0, a);
+    else
+      hipExtLaunchKernelGGL(attn_dec_fused_kernel<LCA_MIXED_FP8>, fgrid, dim3(64 * kDsWaves), 0, st, eb, ee, 0, a);
   } else if (mfma && a.hg_mode == 2) {
     // mode 2 is chosen for the mixed cache only (dense HCA rows over a bf16 cache take the many-row kernel)
     if (a.comp.format != LCA_MIXED_FP8) return hipErrorInvalidValue;
@@ -2078,7 +1950,7 @@ hipError_t launch_attn(AttnArgs a, hipStream_t st, hipEvent_t eb, hipEvent_t ee)
     hipExtLaunchKernelGGL(attn_simt_kernel, grid, dim3(256), 0, st, eb, ee, 0, a);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.n_splits == 1) return e;
+  if (e != hipSuccess || (a.n_splits == 1 && a.hg_mode != 3)) return e;  // (mode 3 always leaves partials)
   const size_t lds = sizeof(float) * (size_t)a.n_splits;
   hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)a.H, (unsigned)a.Sq, (unsigned)a.B), dim3(kMergeThreads), lds,
                      st, a);

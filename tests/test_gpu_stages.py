@@ -335,7 +335,7 @@ def test_attn_many_rows(B, Sq, N, k, window, q_start, seed):
 @pytest.mark.parametrize("B,Sq,k", [(1, 260, 512), (2, 1, 512), (1, 1, 2100)])
 def test_attn_running_max_moves(B, Sq, k):
     # entries later in the (sorted) list have logits up to 40x larger, so the reference max of every head moves many
-    # times by more than the rescale slack: the many-row kernel (260 rows), the two-pass decode kernels (512) and the
+    # times by more than the rescale slack: the many-row kernel (260 rows), the fused decode kernel (512) and the
     # head-group kernel (2100)
     o, ref, l, lr = _attn_case(B, Sq, 64, 512, 4000, k, 16, 60000, "bf16", 44, scale=1.0, gain=40.0)
     assert row_rel_err(o, ref) <= 1e-2
