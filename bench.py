@@ -440,8 +440,8 @@ def main():
     if not has_scores:
         src = ["long_context_attention_05_amd/csrc/attn.hip", "long_context_attention_05_amd/csrc/lca_device.h",
                "long_context_attention_05_amd/build.py"]
-        if w.layer == "swa":  # few rows, a 128-entry window list: the one-pass decode attention (the merge untimed)
-            kname = "attn_dec_fused_kernel"
+        if w.layer == "swa":  # few rows, a 128-entry window list: the two-pass decode attention (both passes timed)
+            kname = "attn_dec_score_kernel+attn_dec_value_kernel"
             per_launch = step.step_bytes()
         else:  # dense HCA rows: the many-row kernel over a bf16 cache, the wide kernel over the mixed cache
             kname = "attn_pfs_kernel" if w.main_fmt == "bf16" else "attn_wide_kernel"

@@ -128,21 +128,27 @@ void attn_plan(int B, int Sq, int H, int max_entries, int mode, bool table, int&
   split_len = (int)len;
 }
 
-// The kernel a call takes: few query rows on the MFMA path go to the one-pass decode kernel and the merge (sparse
-// lists of up to kDecMaxEntries positions), the head-group kernel (longer sparse lists) or, for dense HCA lists over
-// the mixed cache, the wide kernel.  Dense HCA lists over a bf16 cache take the many-row path (mode 0): its LDS ring keeps two
+// The kernel a call takes: few query rows on the MFMA path go to the two-pass decode kernels (sparse lists of up to
+// kDecTwoPassMax positions), the one-pass decode kernel and the merge (up to kDecMaxEntries), the head-group kernel
+// (longer sparse lists) or, for dense HCA lists over the mixed cache, the wide kernel.  Dense HCA lists over a bf16 cache take the many-row path (mode 0): its LDS ring keeps two
 // tiles in flight where the wide kernel holds one in registers, and it splits the list the same way.
 int attn_mode(int B, int Sq, int H, int D, int q_format, int kv_format, int hca_m, int max_entries) {
   if (!attn_uses_mfma(H, D, q_format, kv_format) || (long long)B * Sq >= 256) return 0;
   if (hca_m > 0) return kv_format == LCA_BF16 ? 0 : 2;
-  return max_entries <= kDecMaxEntries ? 3 : 1;
+  return max_entries <= kDecTwoPassMax ? 3 : max_entries <= kDecMaxEntries ? 4 : 1;
 }
 
-// 64-entry tiles per row of the decode attention (each leaves one partial output), at least one
+// 64-entry tiles per row of the decode attention (in mode 4 each leaves one partial output), at least one
 int dec_splits(int max_entries) { return max_entries > 0 ? (max_entries + 63) / 64 : 1; }
+// 32-entry tiles per row of the two-pass probabilities: whole 64-entry score tiles
+int dec_tiles(int max_entries) { return 2 * dec_splits(max_entries); }
 
 size_t attn_ws_plan_size(int B, int Sq, int H, int D, int max_entries, int mode, bool table) {
-  if (mode == 3) {  // per 64-entry tile: a bf16 partial output [H][D] and (m, l) [H] float2
+  if (mode == 3) {  // probabilities [rows][H][tiles * 32] bf16 and (m, l) [rows][tiles][H] float2
+    const size_t rows = (size_t)B * Sq, T = (size_t)dec_tiles(max_entries);
+    return align_up(rows * H * T * 32 * sizeof(uint16_t)) + align_up(rows * T * H * 2 * sizeof(float));
+  }
+  if (mode == 4) {  // per 64-entry tile: a bf16 partial output [H][D] and (m, l) [H] float2
     const size_t items = (size_t)B * Sq * dec_splits(max_entries);
     return align_up(items * H * D * sizeof(uint16_t)) + align_up(items * H * 2 * sizeof(float));
   }
@@ -160,8 +166,8 @@ size_t attn_ws_size(int B, int Sq, int H, int D, int max_entries) {
   const size_t tabled = attn_ws_plan_size(B, Sq, H, D, max_entries, 0, true);
   if (tabled > need) need = tabled;
   if (H == 64 && D == 512 && (long long)B * Sq < 256)  // the few-row kernels (see attn_mode)
-    for (int mode = 0; mode <= 3; ++mode) {
-      if (mode == 3 && max_entries > kDecMaxEntries) continue;
+    for (int mode = 0; mode <= 4; ++mode) {
+      if ((mode == 3 && max_entries > kDecTwoPassMax) || (mode == 4 && max_entries > kDecMaxEntries)) continue;
       const size_t m = attn_ws_plan_size(B, Sq, H, D, max_entries, mode, true);
       if (m > need) need = m;
     }
@@ -214,10 +220,10 @@ int run_attn(const void* q, int q_format, const lca_tensor& comp_in, int N, int 
   const int max_entries = window + (hca_m > 0 ? N : k);
   const int mode = attn_mode(B, Sq, H, D, q_format, comp.format, hca_m, max_entries);
   int ns = 1, len = max_entries;
-  if (mode != 3)
-    attn_plan(B, Sq, H, max_entries, mode, mfma, ns, len);
-  else
+  if (mode == 4)
     ns = dec_splits(max_entries), len = 64;
+  else if (mode != 3)
+    attn_plan(B, Sq, H, max_entries, mode, mfma, ns, len);
   if (mfma && len > kHgSplitMax) return LCA_ERR_UNSUPPORTED;  // more than 4096 x 2048 list positions per row
   const size_t need = attn_ws_plan_size(B, Sq, H, D, max_entries, mode, mfma);
   if (need > 0 && (!ws || ws_bytes < need)) return LCA_ERR_WORKSPACE;
@@ -248,8 +254,12 @@ int run_attn(const void* q, int q_format, const lca_tensor& comp_in, int N, int 
   a.n_splits = ns;
   a.split_len = len;
   a.hg_mode = mode;
-  a.part_bf16 = (mode == 2 || mode == 3) ? 1 : 0;  // the wide and the decode kernels' partials are bf16 only
+  a.part_bf16 = (mode == 2 || mode == 4) ? 1 : 0;  // the wide and the one-pass decode kernels' partials are bf16
   if (mode == 3) {
+    a.dec_tiles = dec_tiles(max_entries);
+    a.dec_p = (uint16_t*)ws;
+    a.dec_ml = (float*)((char*)ws + align_up((size_t)B * Sq * H * a.dec_tiles * 32 * sizeof(uint16_t)));
+  } else if (mode == 4) {
     const size_t items = (size_t)B * Sq * ns;
     a.part_o = (float*)ws;
     a.part_ml = (float*)((char*)ws + align_up(items * H * D * sizeof(uint16_t)));

@@ -1462,6 +1462,406 @@ __global__ __launch_bounds__(256) void attn_simt_kernel(AttnArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------------
+// sparse decode attention in two passes (few query rows, H = 64, D = 512, bf16 or mixed entries)
+// ------------------------------------------------------------------------------------------------
+// With one query row per sequence, splitting a row's entry list over workgroups leaves one 64 x 512 partial output
+// per split -- more bytes than the split's own entries -- and a merge pass over them.  The decode path instead
+// stores the probabilities, which are 64 values per entry:
+//   scores (one workgroup per (query row, 32-entry tile), all 64 heads): S^T = scale * K Q^T for the tile with
+//     v_mfma_f32_16x16x32_bf16, wave w contracting channels [128 w, 128 w + 128) (fp8 entries widened exactly, the
+//     entry scale applied to their part) and the four partial products added in LDS; then per head the tile max
+//     m_t, P_t = e^(S - m_t) (bf16, 0 for padding) and l_t = sum P_t.
+//   values (one workgroup per (query row, 64 channels, 16 heads)): M = max(z, m_t), den = e^(z - M) +
+//     sum_t l_t e^(m_t - M) and the tile weights f_t = e^(m_t - M) / den, then O^T = sum_t f_t V_t^T P_t^T on
+//     v_mfma_f32_16x16x32_bf16: wave w of 8 takes tiles w, w + 8, ..., issues every load of its tiles at once, turns
+//     each tile's channels into a row-major bf16 tile in its own LDS area (fp8 widened and multiplied by the entry
+//     scale) and reads V^T with ds_read_b64_tr_b16; the eight waves' sums are added in LDS at the end.
+// The exact normaliser is known before any value is weighted, so no partial output goes through memory.
+constexpr int kDecTile = 32;                              // list positions per tile
+constexpr int kDecMaxTiles = kDecMaxEntries / kDecTile;   // 64
+constexpr int kDsTile = 64;                               // list positions per score workgroup (two value tiles)
+constexpr int kDsWaves = 8;                               // waves of a score workgroup
+constexpr int kDvRowB = 144;                              // LDS bytes per entry of a value tile (64 bf16 + pad)
+constexpr int kDvWaves = 8;                               // waves of a value workgroup
+
+template <int FMT>
+__global__ __launch_bounds__(64 * kDsWaves) void attn_dec_score_kernel(AttnArgs a) {
+  constexpr bool MX = FMT == LCA_MIXED_FP8;
+  // LDS: the 64 x 512 queries (1 KB rows), then the tile's entries (bf16: 1 KB rows; mixed: 448 fp8 bytes, 128
+  // RoPE bytes and 16 bytes of padding).  bf16 rows keep 16-byte chunk c of row r at chunk c ^ (r % 16), so that
+  // the 16 rows an operand read touches fall on distinct banks; the padded mixed rows do the same by their stride.
+  constexpr int KROW = MX ? 592 : 1024;
+  __shared__ __attribute__((aligned(16))) uint8_t ds_lds[65536 + kDsTile * KROW];
+  __shared__ uint8_t ds_ok[kDsTile];
+  __shared__ __attribute__((aligned(16))) float ds_esc[kDsTile];
+  uint8_t* const qs = ds_lds;
+  uint8_t* const kt = ds_lds + 65536;
+  const int qrow = blockIdx.x, tile = blockIdx.y;
+  const int b = qrow / a.Sq, r = qrow - b * a.Sq;
+  const RowList L = row_list(a, b, r);
+  const int total = L.nw + L.nc;
+  const int p0 = tile * kDsTile;
+  if (p0 >= total) return;  // past this row's list: the value pass does not read these tiles
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int hl = lane & 15, grp = lane >> 4;
+
+  // lane e of every wave resolves tile entry e: its tensor row (row 0 of the compressed tensor for padding), whether
+  // it is a window entry and whether it is real; the copies below take these by readlane / ds_bpermute
+  // (the index load is unconditional -- a read of the sink array where there is no index -- and its value is used
+  // only after the query copies are issued, so that they are not held up by it)
+  const int pl = p0 + lane;
+  const bool rwl = pl < L.nw;
+  const bool sel = !rwl && pl < total;
+  const int xl = *(sel ? a.idx + ((long long)qrow * a.k + (pl - L.nw)) : (const int*)a.sink);
+  // queries: wave w copies head rows 8 w .. 8 w + 7, 1 KB per instruction
+  {
+    const uint8_t* qg = (const uint8_t*)a.q + (long long)qrow * 65536;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int h = 8 * wave + i;
+      __builtin_amdgcn_global_load_lds((const void*)(qg + h * 1024 + 16 * (lane ^ (h & 15))), (void*)(qs + h * 1024),
+                                       16, 0, 0);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVm8);  // the index load has landed; the eight query copies may still be in flight
+  __builtin_amdgcn_sched_barrier(0);
+  const int rowl = rwl ? (int)(L.w0 + pl - L.raw0) : ((sel & (xl >= 0) & (xl < a.N)) ? xl : -1);
+  const bool okl = rowl >= 0;
+  // storage row: the raw tensor is dense; the compressed one may be paged (a dependent table read)
+  const long long rabsl = rwl ? (long long)b * a.raw.cap + rowl : tensor_row(a.comp, b, okl ? rowl : 0);
+  const int rlo = (int)rabsl, rhi = (int)(rabsl >> 32), rwi = rwl ? 1 : 0;
+  // entries
+  if constexpr (!MX) {
+    // wave w copies entries 8 w .. 8 w + 7, one 1 KB row per instruction
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int e = 8 * wave + i;
+      const long long rabs = ((long long)__builtin_amdgcn_readlane(rhi, e) << 32) |
+                             (uint32_t)__builtin_amdgcn_readlane(rlo, e);
+      const uint8_t* src = (const uint8_t*)(__builtin_amdgcn_readlane(rwi, e) ? a.raw.data : a.comp.data) +
+                           rabs * 1024 + 16 * (lane ^ (e & 15));
+      __builtin_amdgcn_global_load_lds((const void*)src, (void*)(kt + e * 1024), 16, 0, 0);
+    }
+  } else {
+    // 37 instructions of 64 16-byte slots: slot s is chunk s % 37 of entry s / 37 (28 fp8 chunks, 8 RoPE chunks,
+    // then the padding slot, which copies fp8 chunk 0); wave w issues instructions w, w + 8, ...
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      const int j = wave + 8 * i;
+      const int sl = 64 * min(j, 36) + lane, e = sl / 37, c = sl - 37 * e;
+      const long long rabs = ((long long)__builtin_amdgcn_ds_bpermute(4 * e, rhi) << 32) |
+                             (uint32_t)__builtin_amdgcn_ds_bpermute(4 * e, rlo);
+      const bool rw = __builtin_amdgcn_ds_bpermute(4 * e, rwi) != 0;
+      // (fields selected one by one: a lane-dependent choice of the whole tensor struct would be read through
+      // per-lane pointers)
+      const uint8_t* fb = (const uint8_t*)(rw ? a.raw.data : a.comp.data) + rabs * 448;
+      const uint8_t* rb = (const uint8_t*)(rw ? a.raw.rope : a.comp.rope) + rabs * 128;
+      const uint8_t* g = c < 28 ? fb + 16 * c : c < 36 ? rb + 16 * (c - 28) : fb;
+      if (j < 37) __builtin_amdgcn_global_load_lds((const void*)g, (void*)(kt + 1024 * j), 16, 0, 0);
+    }
+  }
+  if (wave == 0) {
+    ds_ok[lane] = okl ? 1 : 0;
+    if constexpr (MX) {
+      const long long rabs = ((long long)rhi << 32) | (uint32_t)rlo;
+      ds_esc[lane] = (rwi ? (const float*)a.raw.scale : (const float*)a.comp.scale)[rabs];
+    }
+  }
+  __syncthreads();  // every copy has landed
+
+  // wave (cs, eh): channels [128 cs, 128 cs + 128) of entries [32 eh, 32 eh + 32) for all 64 heads
+  const int cs = wave & 3, eh = wave >> 2;
+  f32x4_t acc[2][4], accr[2][4];
+#pragma unroll
+  for (int eb = 0; eb < 2; ++eb)
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) {
+      acc[eb][hb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      accr[eb][hb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const int c = 16 * cs + 4 * ks + grp;  // the lane's 16-byte chunk: channels 8 c .. 8 c + 7
+    bf16x8_t qb[4];
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb)
+      qb[hb] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(qs + (16 * hb + hl) * 1024 + 16 * (c ^ hl)));
+#pragma unroll
+    for (int eb = 0; eb < 2; ++eb) {
+      const int e = 32 * eh + 16 * eb + hl;
+      if constexpr (!MX) {
+        const bf16x8_t kv = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(kt + e * 1024 + 16 * (c ^ hl)));
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb)
+          acc[eb][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qb[hb], acc[eb][hb], 0, 0, 0);
+      } else if (128 * cs + 32 * ks < 448) {
+        const uint2 f = *(const uint2*)(kt + e * KROW + 8 * c);
+        const uint2 lo = fp8x4_to_bf16x4(f.x), hi = fp8x4_to_bf16x4(f.y);
+        const bf16x8_t kv = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb)
+          acc[eb][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qb[hb], acc[eb][hb], 0, 0, 0);
+      } else {
+        const bf16x8_t kv = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(kt + e * KROW + 448 + 16 * (c - 56)));
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb)
+          accr[eb][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qb[hb], accr[eb][hb], 0, 0, 0);
+      }
+    }
+  }
+  __syncthreads();  // the staged rows are dead: the partial products go over them
+  // partials [slot][entry block 2 eh + eb][head block][lane]: slot = channel quarter (mixed: slot 4 = RoPE part)
+  f32x4_t* part = (f32x4_t*)ds_lds;
+#pragma unroll
+  for (int eb = 0; eb < 2; ++eb)
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) {
+      part[((cs * 4 + 2 * eh + eb) * 4 + hb) * 64 + lane] = acc[eb][hb];
+      if constexpr (MX)
+        if (cs == 3) part[((4 * 4 + 2 * eh + eb) * 4 + hb) * 64 + lane] = accr[eb][hb];
+    }
+  __syncthreads();
+
+  // thread (head h, group g) finishes entries 8 g .. 8 g + 7 of head h: entry 16 B + er of head block h / 16 sits in
+  // lane 16 (er / 4) + h % 16, element er % 4, of entry block B
+  const int h = tid >> 3, g = tid & 7;
+  const int blk = g >> 1, l0 = 32 * (g & 1) + (h & 15), hb = h >> 4;
+  float sv[8];
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int l = l0 + 16 * half;
+    f32x4_t sm = (part[((0 * 4 + blk) * 4 + hb) * 64 + l] + part[((1 * 4 + blk) * 4 + hb) * 64 + l]) +
+                 (part[((2 * 4 + blk) * 4 + hb) * 64 + l] + part[((3 * 4 + blk) * 4 + hb) * 64 + l]);
+    if constexpr (MX) sm = sm * *(const f32x4_t*)&ds_esc[8 * g + 4 * half] + part[((4 * 4 + blk) * 4 + hb) * 64 + l];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) sv[4 * half + x] = a.scale * sm[x];
+  }
+  // per 32-entry value tile (groups g / 4): max, probabilities, sum
+  float mt = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (ds_ok[8 * g + j]) mt = fmaxf(mt, sv[j]);
+  mt = fmaxf(mt, __shfl_xor(mt, 1));
+  mt = fmaxf(mt, __shfl_xor(mt, 2));
+  float pv[8], ls = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    pv[j] = ds_ok[8 * g + j] ? __expf(sv[j] - mt) : 0.0f;
+    ls += pv[j];
+  }
+  ls += __shfl_xor(ls, 1);
+  ls += __shfl_xor(ls, 2);
+  // P in the value pass's operand order: per (row, head group, tile) 64 lanes x 16 bytes, lane 16 q + (h % 16)
+  // holding entries 8 q .. 8 q + 7 of the tile for head h
+  const int t = 2 * tile + (g >> 2), q = g & 3;
+  const u32x4_t pk = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]), pack_bf16x2(pv[4], pv[5]),
+                      pack_bf16x2(pv[6], pv[7])};
+  *(u32x4_t*)(a.dec_p + ((((long long)qrow * 4 + hb) * a.dec_tiles + t) * 64 + 16 * q + (h & 15)) * 8) = pk;
+  if (q == 0) ((float2*)a.dec_ml)[((long long)qrow * a.dec_tiles + t) * 64 + h] = make_float2(mt, ls);
+}
+
+// NTI: the most tiles a wave takes (every wave loads all of its tiles at once).  The occupancy is stated so that the
+// compiler keeps the loads in distinct registers rather than reusing them at the price of waits: 4 waves per SIMD
+// (two workgroups per CU) for short lists, 2 for long ones.
+template <int FMT, int NTI>
+__global__ __launch_bounds__(64 * kDvWaves) __attribute__((amdgpu_waves_per_eu(NTI <= 4 ? 4 : 2, NTI <= 4 ? 4 : 2)))
+void attn_dec_value_kernel(AttnArgs a) {
+  constexpr int kGroups = 4 * kDvWaves;  // tile groups of the weight computation (16 heads x kGroups threads)
+  constexpr int kPer = kDecMaxTiles / kGroups;
+  __shared__ __attribute__((aligned(16))) uint8_t dvt[kDvWaves][kDecTile * kDvRowB];  // each wave's value tile
+  __shared__ int drows[kDecMaxEntries];
+  __shared__ float dfac[kDecMaxTiles][16];
+  __shared__ float dred[kGroups][16];
+  const int qrow = blockIdx.x, cb = blockIdx.y, hg = blockIdx.z;
+  const int b = qrow / a.Sq, r = qrow - b * a.Sq;
+  const RowList L = row_list(a, b, r);
+  const int total = L.nw + L.nc;
+  const int nt = (total + kDecTile - 1) / kDecTile;
+  const int T = a.dec_tiles;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int hl = lane & 15, grp = lane >> 4;
+
+  // rows of all T * 32 list positions (-1: padding or past the list)
+  for (int p = tid; p < T * kDecTile; p += 64 * kDvWaves) {
+    drows[p] = p < total ? list_row(a, L, b, r, p) : -1;
+  }
+  // this thread's tiles' (m_t, l_t) for head 16 hg + (tid % 16) and that head's sink; both read before the value
+  // loads (a load issued after them could only be waited for together with all of them), tiles past the list
+  // reading the last tile and dropped below
+  const int hh = tid & 15, tg = tid >> 4;
+  const int head = 16 * hg + hh;
+  float2 mlv[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i)
+    mlv[i] = ((const float2*)a.dec_ml)[((long long)qrow * T + min(tg + kGroups * i, T - 1)) * 64 + head];
+  const float z = a.sink[head];
+  __syncthreads();
+
+  // wave w: tiles w, w + kDvWaves, ... (nti of them); acc[d] = O^T for channels 64 cb + 16 d + 4 grp + x, head
+  // 16 hg + hl
+  const int nti = nt > wave ? (nt - wave + kDvWaves - 1) / kDvWaves : 0;
+  f32x4_t acc[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) acc[d] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  uint8_t* vt = dvt[wave];
+  const uint16_t* pbase = a.dec_p + (((long long)qrow * 4 + hg) * T * 64 + lane) * 8;
+  // the V^T reads: rows 8 grp + 4 half + hl / 4, channels 16 d + 4 (hl % 4)
+  const uint8_t* vtr = vt + (8 * grp + (hl >> 2)) * kDvRowB + 8 * (hl & 3);
+
+  // The body twice, for bf16 channels and for fp8 channels (the mixed cache's blocks 0..6), so that neither has a
+  // branch between its loads.
+  auto run = [&](auto f8c) {
+    constexpr bool F8 = decltype(f8c)::value;
+    u32x4_t vr[NTI][4];
+    float es[NTI][2];
+    bool ok[NTI][4];
+    u32x4_t pr[NTI];
+    // every load of the wave's tiles (slots past its last tile repeat a valid tile, so that the count is fixed)
+#pragma unroll
+    for (int i = 0; i < NTI; ++i) {
+      const int t = min(wave + kDvWaves * min(i, max(nti, 1) - 1), T - 1);
+      pr[i] = *(gbl_u32x4_t*)(pbase + 512 * t);
+      if constexpr (!F8) {
+        // entries (lane / 8) + 8 k, 16 bytes (8 channels) at chunk lane % 8
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int p = 32 * t + (lane >> 3) + 8 * k;
+          const int row = drows[p];
+          ok[i][k] = row >= 0;
+          const bool rw = p < L.nw;
+          // (fields selected one by one: a lane-dependent choice of the whole tensor struct would be read through
+          // per-lane pointers)
+          const long long rabs = row >= 0 ? row : 0;
+          const uint8_t* vp = FMT == LCA_MIXED_FP8
+                                  ? (const uint8_t*)(rw ? a.raw.rope : a.comp.rope) + rabs * 128
+                                  : (const uint8_t*)(rw ? a.raw.data : a.comp.data) + rabs * 1024 + 128 * cb;
+          vr[i][k] = *(gbl_u32x4_t*)(vp + 16 * (lane & 7));
+        }
+      } else {
+        // entries (lane / 4) + 16 k, 16 fp8 channels at chunk lane % 4, and the entry scales
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int p = 32 * t + (lane >> 2) + 16 * k;
+          const int row = drows[p];
+          ok[i][k] = row >= 0;
+          const bool rw = p < L.nw;
+          const long long rabs = row >= 0 ? row : 0;
+          vr[i][k] = *(gbl_u32x4_t*)((const uint8_t*)(rw ? a.raw.data : a.comp.data) + rabs * 448 + 64 * cb +
+                                     16 * (lane & 3));
+          es[i][k] = ((const float*)(rw ? a.raw.scale : a.comp.scale))[rabs];
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // while the loads are in flight: M = max(z, m_t), den = e^(z - M) + sum_t l_t e^(m_t - M) and
+    // f_t = e^(m_t - M) / den per head of the group (LDS-only barriers: the loads are not waited for)
+    {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < kPer; ++i)
+        if (tg + kGroups * i < nt) mx = fmaxf(mx, mlv[i].x);
+      dred[tg][hh] = mx;
+      pd_barrier();
+      float M = z;
+#pragma unroll
+      for (int gi = 0; gi < kGroups; ++gi) M = fmaxf(M, dred[gi][hh]);
+      float d = 0.0f;
+#pragma unroll
+      for (int i = 0; i < kPer; ++i)
+        if (tg + kGroups * i < nt && mlv[i].x != -INFINITY) d += mlv[i].y * __expf(mlv[i].x - M);
+      pd_barrier();
+      dred[tg][hh] = d;
+      pd_barrier();
+      float den = (z == -INFINITY) ? 0.0f : __expf(z - M);
+#pragma unroll
+      for (int gi = 0; gi < kGroups; ++gi) den += dred[gi][hh];
+      const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int t = tg + kGroups * i;
+        if (t < nt) dfac[t][hh] = (mlv[i].x == -INFINITY) ? 0.0f : __expf(mlv[i].x - M) * inv;
+      }
+      if (cb == 0 && tg == 0 && a.lse)
+        a.lse[(long long)qrow * 64 + head] = (M == -INFINITY) ? -INFINITY : M + __logf(den);
+      pd_barrier();
+    }
+
+#pragma unroll
+    for (int i = 0; i < NTI; ++i) {
+      if (i < nti) {
+        const int t = wave + kDvWaves * i;
+        // the tile's channels, row-major bf16 (padding rows zero: their probabilities are zero, and zero times an
+        // unwritten row must not make a NaN); the empty asm keeps each use of the loaded data below the barriers
+        if constexpr (!F8) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            u32x4_t v = vr[i][k];
+            asm volatile("" : "+v"(v));
+            const u32x4_t zero = {0u, 0u, 0u, 0u};
+            *(u32x4_t*)(vt + ((lane >> 3) + 8 * k) * kDvRowB + 16 * (lane & 7)) = ok[i][k] ? v : zero;
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            u32x4_t v = vr[i][k];
+            asm volatile("" : "+v"(v));
+            const float sc = ok[i][k] ? es[i][k] : 0.0f;
+            uint32_t w[8];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[q], false);
+              const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[q], true);
+              w[2 * q] = pack_bf16x2(lo[0] * sc, lo[1] * sc);
+              w[2 * q + 1] = pack_bf16x2(hi[0] * sc, hi[1] * sc);
+            }
+            uint8_t* dst = vt + ((lane >> 2) + 16 * k) * kDvRowB + 32 * (lane & 3);
+            *(u32x4_t*)dst = u32x4_t{w[0], w[1], w[2], w[3]};
+            *(u32x4_t*)(dst + 16) = u32x4_t{w[4], w[5], w[6], w[7]};
+          }
+        }
+        const float f = dfac[t][hl];
+        const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pr[i]);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vtr + 32 * d));
+          const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vtr + 4 * kDvRowB + 32 * d));
+          const bf16x8_t av = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+          const f32x4_t pvt =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+          acc[d] += f * pvt;
+        }
+      }
+    }
+  };
+  if (FMT == LCA_MIXED_FP8 && cb < 7)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
+
+  // the eight waves' sums: wave w < 4 finishes channel block 16 w of the 64
+  f32x4_t* mg = (f32x4_t*)dvt[wave];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) mg[d * 64 + lane] = acc[d];
+  __syncthreads();
+  if (wave >= 4) return;
+  f32x4_t o = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int w = 0; w < kDvWaves; ++w) o += ((const f32x4_t*)dvt[w])[wave * 64 + lane];
+  const long long oi = ((long long)qrow * 64 + 16 * hg + hl) * 512 + 64 * cb + 16 * wave + 4 * grp;
+  if (a.out_format == LCA_F32) {
+    *(f32x4_t*)((float*)a.out + oi) = o;
+  } else {
+    uint2 w2;
+    w2.x = pack_bf16x2(o[0], o[1]);
+    w2.y = pack_bf16x2(o[2], o[3]);
+    *(uint2*)((uint16_t*)a.out + oi) = w2;
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
 // sparse decode attention in one pass per 64-entry tile, then the merge (few query rows, H = 64, D = 512)
 // ------------------------------------------------------------------------------------------------
 // One workgroup per (query row, 64 list positions), all 64 heads.  Since K = V = the entry, the tile that the
@@ -1480,8 +1880,6 @@ __global__ __launch_bounds__(256) void attn_simt_kernel(AttnArgs a) {
 //   weights.
 // Against two passes (scores for the whole list, then values weighted by the exact normaliser) this saves a launch
 // and the second gather of every entry, for a merge over 64 KB of bf16 partials per tile.
-constexpr int kDsTile = 64;    // list positions per workgroup
-constexpr int kDsWaves = 8;    // waves per workgroup
 constexpr int kDfRowB = 1040;  // LDS bytes per head row of the output staging (1024 + 16)
 
 template <int FMT>
@@ -1900,6 +2298,21 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
   }
 }
 
+// The value pass with the smallest per-wave load round that holds a wave's nti tiles (at most 8 per round).
+template <int FMT>
+void launch_dec_value(int nti, dim3 grid, hipStream_t st, hipEvent_t ee, const AttnArgs& a) {
+  const dim3 blk(64 * kDvWaves);
+  switch (nti <= 1 ? 1 : nti >= 7 ? 8 : nti) {
+    case 1: hipExtLaunchKernelGGL((attn_dec_value_kernel<FMT, 1>), grid, blk, 0, st, nullptr, ee, 0, a); break;
+    case 2: hipExtLaunchKernelGGL((attn_dec_value_kernel<FMT, 2>), grid, blk, 0, st, nullptr, ee, 0, a); break;
+    case 3: hipExtLaunchKernelGGL((attn_dec_value_kernel<FMT, 3>), grid, blk, 0, st, nullptr, ee, 0, a); break;
+    case 4: hipExtLaunchKernelGGL((attn_dec_value_kernel<FMT, 4>), grid, blk, 0, st, nullptr, ee, 0, a); break;
+    case 5: hipExtLaunchKernelGGL((attn_dec_value_kernel<FMT, 5>), grid, blk, 0, st, nullptr, ee, 0, a); break;
+    case 6: hipExtLaunchKernelGGL((attn_dec_value_kernel<FMT, 6>), grid, blk, 0, st, nullptr, ee, 0, a); break;
+    default: hipExtLaunchKernelGGL((attn_dec_value_kernel<FMT, 8>), grid, blk, 0, st, nullptr, ee, 0, a); break;
+  }
+}
+
 bool attn_uses_mfma(int H, int D, int q_format, int kv_format) {
   return H == 64 && D == 512 && q_format == LCA_BF16 && (kv_format == LCA_BF16 || kv_format == LCA_MIXED_FP8);
 }
@@ -1909,6 +2322,18 @@ hipError_t launch_attn(AttnArgs a, hipStream_t st, hipEvent_t eb, hipEvent_t ee)
   dim3 grid((unsigned)a.n_splits, (unsigned)a.Sq, (unsigned)a.B);
   clear_stale_error();
   if (mfma && a.hg_mode == 3) {
+    const dim3 sgrid((unsigned)(a.B * a.Sq), (unsigned)(a.dec_tiles / 2));
+    const dim3 vgrid((unsigned)(a.B * a.Sq), 8u, 4u);
+    const int nti = (a.dec_tiles + kDvWaves - 1) / kDvWaves;  // most tiles a value-pass wave takes
+    if (a.comp.format == LCA_BF16) {
+      hipExtLaunchKernelGGL(attn_dec_score_kernel<LCA_BF16>, sgrid, dim3(64 * kDsWaves), 0, st, eb, nullptr, 0, a);
+      launch_dec_value<LCA_BF16>(nti, vgrid, st, ee, a);
+    } else {
+      hipExtLaunchKernelGGL(attn_dec_score_kernel<LCA_MIXED_FP8>, sgrid, dim3(64 * kDsWaves), 0, st, eb, nullptr, 0,
+                            a);
+      launch_dec_value<LCA_MIXED_FP8>(nti, vgrid, st, ee, a);
+    }
+  } else if (mfma && a.hg_mode == 4) {
     // one workgroup per (row, 64 list positions), bf16 partials, then the merge
     if (a.part_bf16 != 1 || a.n_splits > 32) return hipErrorInvalidValue;
     const dim3 fgrid((unsigned)(a.B * a.Sq), (unsigned)a.n_splits);
@@ -1950,7 +2375,8 @@ hipError_t launch_attn(AttnArgs a, hipStream_t st, hipEvent_t eb, hipEvent_t ee)
     hipExtLaunchKernelGGL(attn_simt_kernel, grid, dim3(256), 0, st, eb, ee, 0, a);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || (a.n_splits == 1 && a.hg_mode != 3)) return e;  // (mode 3 always leaves partials)
+  // mode 3 writes the output itself; mode 4 always leaves partials
+  if (e != hipSuccess || a.hg_mode == 3 || (a.n_splits == 1 && a.hg_mode != 4)) return e;
   const size_t lds = sizeof(float) * (size_t)a.n_splits;
   hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)a.H, (unsigned)a.Sq, (unsigned)a.B), dim3(kMergeThreads), lds,
                      st, a);

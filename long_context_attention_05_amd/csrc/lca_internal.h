@@ -117,10 +117,17 @@ struct AttnArgs {
   int part_bf16;   // split partial outputs stored as bf16 (the wide and the many-row bf16 kernels: half the
                    // partial traffic); set by the launcher for the kernel it takes
   int hg_mode;     // 1: one workgroup per (16-head group, row, split); 2: one per (row, split) with the channels
-                   // split over the waves; 3: one per (row, 64 list positions), partials always merged -- few rows
-                   // (decode)
+                   // split over the waves; 3: scores then values in two passes; 4: one pass per (row, 64 list
+                   // positions), partials always merged -- 3 and 4 for few rows (decode)
+  // mode 3: the score pass's probabilities and per-tile (max, sum)
+  int dec_tiles;     // 32-entry tiles per row (an even number: list capacity / 64, rounded up, times 2)
+  uint16_t* dec_p;   // [B][Sq][H / 16][dec_tiles][64 lanes][8] bf16 probabilities e^(l - m_t), in the order the
+                     // value pass loads its MFMA operand (lane 16 q + h % 16: entries 8 q .. 8 q + 7 of head h)
+  float* dec_ml;     // [B][Sq][dec_tiles][H][2] (m_t, l_t)
 };
-constexpr int kDecMaxEntries = 2048;  // list positions per row in the one-pass decode attention (32 partials)
+constexpr int kDecMaxEntries = 2048;  // list positions per row in the decode attention (mode 4: 32 partials)
+constexpr int kDecTwoPassMax = 512;   // lists up to this long take the two passes (mode 3), whose value pass grows
+                                      // with the list where the one pass pays a fixed merge
 constexpr int kHgSplitMax = 2048;  // list positions per workgroup slice in the MFMA attention kernels (LDS row table)
 bool attn_uses_mfma(int H, int D, int q_format, int kv_format);
 // ev_begin / ev_end (nullable, from hook_pair): stamped with the start of the attention's first kernel and the end of
