@@ -321,6 +321,16 @@ def test_attn_mfma(B, Sq, N, k, window, fmt):
     np.testing.assert_allclose(l, lr, rtol=1e-3, atol=1e-3)
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "mixed"])
+@pytest.mark.parametrize("k", [384, 385])
+def test_attn_decode_forms_at_the_split(k, fmt):
+    # few rows: 384 + 128 = 512 list positions take the two passes, 513 the one-pass kernel and the merge (a last tile
+    # holding one position, with sink); both against the oracle
+    o, ref, l, lr = _attn_case(2, 1, 64, 512, 3000, k, 128, 60000, fmt, 29, scale=1.0)
+    assert row_rel_err(o, ref) <= 1e-2
+    np.testing.assert_allclose(l, lr, rtol=1e-3, atol=1e-3)
+
+
 @pytest.mark.parametrize("B,Sq,N,k,window,q_start,seed", [(1, 300, 500, 64, 128, 0, 41),
                                                           (1, 256, 3000, 2100, 16, 60000, 42),
                                                           (2, 130, 1000, 40, 128, 77, 43)])
