@@ -375,16 +375,13 @@ __device__ __forceinline__ int cand_segment(const int* seg_off, int nseg, int j)
   return lo;
 }
 
-// The finishing workgroup: 1024 threads, so that one round of loads gathers up to kCandCap candidates (6 per thread)
-// and one round of the ordered compaction writes them; the pass-3 histogram is counted while the candidates are in
-// registers.
+// The finishing workgroup: 1024 threads, so that one round of loads gathers up to kCandCap candidates (6 consecutive
+// ones per thread), which stay in registers for the pass-3 count and the one round of the ordered compaction.
 constexpr int kFinThreads = 1024;
 constexpr int kFinPer = kCandCap / kFinThreads;  // 6
 constexpr int kFinMaxSlices = kFinThreads;       // one slice count per thread
-constexpr size_t kFinishLds = (size_t)kCandCap * 8;
 
 __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(SelArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint32_t mb_lds[];  // the row's candidates (when they fit)
   __shared__ int hist[kSelBins];   // pass 1, then pass 3
   __shared__ int hist2[kSelBins];  // pass 2
   __shared__ int seg_off[kFinMaxSlices];
@@ -425,18 +422,30 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(SelArgs a) {
   sel_lds_barrier();  // the segment offsets
 
   const uint2* cseg = a.cand + (long long)row * a.N;
-  const bool in_lds = total <= kCandCap;
-  uint2* cl = (uint2*)mb_lds;
+  const bool in_regs = total <= kCandCap;
   auto load_cand = [&](int j) -> uint2 {
     const int sgm = cand_segment(seg_off, P, j);
     return cseg[(long long)sgm * kSliceKeys + (j - seg_off[sgm])];
   };
-  // one round of candidate loads (indices clamp to the last candidate, loaded again and not stored), in flight
-  // while passes 1 and 2 resolve from the histograms behind LDS-only barriers
+  // one round of candidate loads: thread t takes candidates 6 t .. 6 t + 5 (indices clamp to the last candidate and
+  // are masked below), finding the segment of the first by a search and the others by walking forward, so that the
+  // loads issue after one search; they stay in flight while passes 1 and 2 resolve from the histograms behind
+  // LDS-only barriers, and in registers until the ordered output
+  const int j0 = kFinPer * tid;
   uint2 cv[kFinPer];
-  if (in_lds) {
+  if (in_regs) {
+    int sgm = cand_segment(seg_off, P, min(j0, total - 1));
+    int s_lo = seg_off[sgm], s_hi = sgm + 1 < P ? seg_off[sgm + 1] : total;
 #pragma unroll
-    for (int i = 0; i < kFinPer; ++i) cv[i] = load_cand(min(tid + kFinThreads * i, total - 1));
+    for (int i = 0; i < kFinPer; ++i) {
+      const int j = min(j0 + i, total - 1);
+      while (j >= s_hi) {  // the next non-empty segment
+        ++sgm;
+        s_lo = s_hi;
+        s_hi = sgm + 1 < P ? seg_off[sgm + 1] : total;
+      }
+      cv[i] = cseg[(long long)sgm * kSliceKeys + (j - s_lo)];
+    }
   }
   const int b1 = find_bin<true>(hist, k, wsum, sh);
   int need = k - sh[1];
@@ -447,16 +456,11 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(SelArgs a) {
   for (int u = 0; u < kSelBins / kFinThreads; ++u) hist[tid + kFinThreads * u] = 0;  // pass 3 counts
   sel_lds_barrier();
 
-  if (in_lds) {
-    // the candidates to LDS, and pass 3 counted over the keys sharing the 21-bit prefix
+  // pass 3 over the keys sharing the 21-bit prefix
+  if (in_regs) {
 #pragma unroll
-    for (int i = 0; i < kFinPer; ++i) {
-      const int j = tid + kFinThreads * i;
-      if (j < total) {
-        cl[j] = cv[i];
-        if ((cv[i].x & 0xFFFFFC00u) == prefix12) atomicAdd(&hist[cv[i].x & 0x3FFu], 1);
-      }
-    }
+    for (int i = 0; i < kFinPer; ++i)
+      if (j0 + i < total && (cv[i].x & 0xFFFFFC00u) == prefix12) atomicAdd(&hist[cv[i].x & 0x3FFu], 1);
   } else {
     for (int j = tid; j < total; j += kFinThreads) {
       const uint32_t key = load_cand(j).x;
@@ -469,18 +473,18 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(SelArgs a) {
   const uint32_t kappa = prefix12 | (uint32_t)b3;  // the k-th largest key; `need` of the keys equal to it are taken
 
   // ordered output: candidates > kappa, then the first `need` equal to kappa; thread t takes kFinPer consecutive
-  // candidates of each round
+  // candidates of each round (one round, from registers, when the row has at most kCandCap candidates)
   int sel_run = 0, eq_run = 0;
   for (int base = 0; base < total && sel_run < k; base += kCandCap) {
-    const int j0 = base + kFinPer * tid;
-    uint2 cv[kFinPer];
+    const int jb = base + j0;
+    uint2 cw[kFinPer];
     int gt = 0, eq = 0;
 #pragma unroll
     for (int j = 0; j < kFinPer; ++j) {
-      const bool v = j0 + j < total;
-      cv[j] = v ? (in_lds ? cl[j0 + j] : load_cand(j0 + j)) : make_uint2(0u, 0u);
-      gt += (v && cv[j].x > kappa) ? 1 : 0;
-      eq += (v && cv[j].x == kappa) ? 1 : 0;
+      const bool v = jb + j < total;
+      cw[j] = v ? (in_regs ? cv[j] : load_cand(jb + j)) : make_uint2(0u, 0u);
+      gt += (v && cw[j].x > kappa) ? 1 : 0;
+      eq += (v && cw[j].x == kappa) ? 1 : 0;
     }
     int ptot;
     const int packed = block_excl_scan(gt | (eq << 16), wsum, ptot);
@@ -490,16 +494,16 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(SelArgs a) {
     int eq_seen = eq_run + eq_before;
 #pragma unroll
     for (int j = 0; j < kFinPer; ++j) {
-      if (j0 + j >= total) break;
-      bool sel = cv[j].x > kappa;
-      if (cv[j].x == kappa) {
+      if (jb + j >= total) break;
+      bool sel = cw[j].x > kappa;
+      if (cw[j].x == kappa) {
         sel = eq_seen < need;
         ++eq_seen;
       }
       if (sel) {
         if (o < k) {  // always true for histograms consistent with the keys
-          out[o] = (int32_t)cv[j].y;
-          if (sout) sout[o] = key_score(cv[j].x);
+          out[o] = (int32_t)cw[j].y;
+          if (sout) sout[o] = key_score(cw[j].x);
         }
         ++o;
       }
@@ -521,7 +525,7 @@ hipError_t launch_topk(const SelArgs& a, hipStream_t st) {
     if (P > kFinMaxSlices) return hipErrorInvalidValue;  // more than 4M entries per row
     if (nvis_max > a.k)
       hipLaunchKernelGGL(topk_collect_kernel, dim3((unsigned)P, (unsigned)a.rows), dim3(kMbThreads), 0, st, a);
-    hipLaunchKernelGGL(topk_finish_kernel, dim3((unsigned)a.rows), dim3(kFinThreads), kFinishLds, st, a);
+    hipLaunchKernelGGL(topk_finish_kernel, dim3((unsigned)a.rows), dim3(kFinThreads), 0, st, a);
   } else if (nvis_max <= kLdsKeys) {
     const hipError_t e = ensure_dyn_lds((const void*)topk_select_kernel<true>, (int)kSelDynLds);
     if (e != hipSuccess) return e;
