@@ -79,13 +79,12 @@ struct SelArgs {
   const long long* seq_pos;  // nullable [rows / Sq]: each sequence's position (a ragged batch)
   // decode rows: the row histograms written by the scoring kernel, and the multi-workgroup select buffers; all null
   // for the select that makes its own histogram passes
-  int* sel_state;  // [rows][kSelStateInts]: histograms of key bits [31:21] (all keys, from the scoring kernel) and
-                   // of bits [20:10] (keys of the border bin, from the candidate collection)
+  int* sel_state;  // [rows][kSelStateInts]: histograms of key bits [31:21] (all keys, from the scoring kernel)
   int* counts;     // [rows][slices]
   uint2* cand;     // [rows][N] (key, entry) candidates, slice s at [s * kSliceKeys]
 };
 constexpr int kSelBins = 2048;
-constexpr int kSelStateInts = 2 * kSelBins;
+constexpr int kSelStateInts = kSelBins;
 constexpr int kSliceKeys = 4096;  // keys per workgroup in the multi-workgroup select
 // Zeroes the row histograms [rows][kSelStateInts] (a fill kernel, so that it may be captured in a graph).
 hipError_t launch_sel_zero(int* state, int rows, hipStream_t st);

@@ -243,13 +243,12 @@ __device__ __forceinline__ int sel_row_nvis(const SelArgs& a, int row) {
 }
 
 // Each row is cut into slices of kSliceKeys entries, one 256-thread workgroup per slice.
-//   topk_collect_kernel: every slice finds the border bin b1 from the row histogram, writes its keys with bin >= b1
-//                        (a superset of the selection: about k + |border| keys per row) in entry order to its
-//                        candidate segment with the segment's length, and adds bits [20:10] of its border-bin keys
-//                        into the row's second histogram (pass 2).
+//   topk_collect_kernel: every slice finds the border bin b1 from the row histogram and writes its keys with
+//                        bin >= b1 (a superset of the selection: about k + |border| keys per row) in entry order to
+//                        its candidate segment with the segment's length.
 //   topk_finish_kernel:  one workgroup per row (a separate launch, so that every slice's writes are visible without
-//                        cross-workgroup fences) reads both histograms, gathers the segments, resolves bits [9:0]
-//                        over the candidates (pass 3) and writes the output.
+//                        cross-workgroup fences) reads the row histogram, gathers the segments, resolves bits
+//                        [20:10] (pass 2) and [9:0] (pass 3) over the candidates and writes the output.
 constexpr int kMbThreads = 256;
 constexpr int kMbPerThread = kSliceKeys / kMbThreads;  // 16
 constexpr int kCandCap = 6144;                         // candidates staged in LDS by the finishing workgroup
@@ -342,27 +341,15 @@ __global__ __launch_bounds__(kMbThreads) void topk_collect_kernel(SelArgs a) {
   int cnt = 0;
 #pragma unroll
   for (int j = 0; j < kMbPerThread; ++j) cnt += (j0 + j < s1 && (int)(kv[j] >> 21) >= b1) ? 1 : 0;
-#pragma unroll
-  for (int u = 0; u < kSelBins / kMbThreads; ++u) hist[tid + kMbThreads * u] = 0;  // reused for pass 2
   int tot;
-  int pos = block256_excl_scan(cnt, wsum, tot);  // (its barriers also publish the zeroed histogram)
+  int pos = block256_excl_scan(cnt, wsum, tot);
   uint2* seg = a.cand + (long long)row * a.N + s0;
 #pragma unroll
   for (int j = 0; j < kMbPerThread; ++j) {
     const uint32_t key = kv[j];
-    if (j0 + j < s1 && (int)(key >> 21) >= b1) {
-      seg[pos++] = make_uint2(key, (uint32_t)(j0 + j));
-      if ((int)(key >> 21) == b1) atomicAdd(&hist[(key >> 10) & 0x7FFu], 1);
-    }
+    if (j0 + j < s1 && (int)(key >> 21) >= b1) seg[pos++] = make_uint2(key, (uint32_t)(j0 + j));
   }
   if (tid == 0) a.counts[(long long)row * slots + p] = tot;
-  __syncthreads();
-  int* gh2 = a.sel_state + (long long)row * kSelStateInts + kSelBins;
-#pragma unroll
-  for (int u = 0; u < kSelBins / kMbThreads; ++u) {
-    const int c = hist[tid + kMbThreads * u];
-    if (c) atomicAdd(&gh2[tid + kMbThreads * u], c);
-  }
 }
 
 // Segment of candidate j (row order): the last segment whose start offset is <= j.
@@ -403,21 +390,18 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(SelArgs a) {
   const int P = (nvis + kSliceKeys - 1) / kSliceKeys;  // <= kFinMaxSlices (checked at launch)
   const int slots = (a.N + kSliceKeys - 1) / kSliceKeys;
   const int* gh = a.sel_state + (long long)row * kSelStateInts;
-  // segment lengths and both histograms, all loads in flight together
+  // segment lengths and the pass-1 histogram, all loads in flight together
   const int c = tid < P ? a.counts[(long long)row * slots + tid] : 0;
-  int hv[kSelBins / kFinThreads], hv2[kSelBins / kFinThreads];
+  int hv[kSelBins / kFinThreads];
 #pragma unroll
-  for (int u = 0; u < kSelBins / kFinThreads; ++u) {
-    hv[u] = gh[tid + kFinThreads * u];
-    hv2[u] = gh[kSelBins + tid + kFinThreads * u];
-  }
+  for (int u = 0; u < kSelBins / kFinThreads; ++u) hv[u] = gh[tid + kFinThreads * u];
 #pragma unroll
   for (int u = 0; u < kSelBins / kFinThreads; ++u) {
     hist[tid + kFinThreads * u] = hv[u];
-    hist2[tid + kFinThreads * u] = hv2[u];
+    hist2[tid + kFinThreads * u] = 0;
   }
   int total;
-  const int off = block_excl_scan(c, wsum, total);  // (its barriers also publish both histograms)
+  const int off = block_excl_scan(c, wsum, total);  // (its barriers also publish the histogram and the zeroed one)
   if (tid < P) seg_off[tid] = off;
   sel_lds_barrier();  // the segment offsets
 
@@ -429,8 +413,8 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(SelArgs a) {
   };
   // one round of candidate loads: thread t takes candidates 6 t .. 6 t + 5 (indices clamp to the last candidate and
   // are masked below), finding the segment of the first by a search and the others by walking forward, so that the
-  // loads issue after one search; they stay in flight while passes 1 and 2 resolve from the histograms behind
-  // LDS-only barriers, and in registers until the ordered output
+  // loads issue after one search; they stay in flight while pass 1 resolves from the row histogram behind LDS-only
+  // barriers, and in registers for passes 2 and 3 and the ordered output
   const int j0 = kFinPer * tid;
   uint2 cv[kFinPer];
   if (in_regs) {
@@ -449,12 +433,23 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(SelArgs a) {
   }
   const int b1 = find_bin<true>(hist, k, wsum, sh);
   int need = k - sh[1];
-  const int b2 = find_bin<true>(hist2, need, wsum, sh);
-  need -= sh[1];
-  const uint32_t prefix12 = ((uint32_t)b1 << 21) | ((uint32_t)b2 << 10);
+  // pass 2 over the candidates of the border bin b1
+  if (in_regs) {
+#pragma unroll
+    for (int i = 0; i < kFinPer; ++i)
+      if (j0 + i < total && (int)(cv[i].x >> 21) == b1) atomicAdd(&hist2[(cv[i].x >> 10) & 0x7FFu], 1);
+  } else {
+    for (int j = tid; j < total; j += kFinThreads) {
+      const uint32_t key = load_cand(j).x;
+      if ((int)(key >> 21) == b1) atomicAdd(&hist2[(key >> 10) & 0x7FFu], 1);
+    }
+  }
 #pragma unroll
   for (int u = 0; u < kSelBins / kFinThreads; ++u) hist[tid + kFinThreads * u] = 0;  // pass 3 counts
-  sel_lds_barrier();
+  __syncthreads();
+  const int b2 = find_bin(hist2, need, wsum, sh);
+  need -= sh[1];
+  const uint32_t prefix12 = ((uint32_t)b1 << 21) | ((uint32_t)b2 << 10);
 
   // pass 3 over the keys sharing the 21-bit prefix
   if (in_regs) {
