@@ -21,7 +21,7 @@ constexpr size_t kSelDynLds = (size_t)kLdsKeys * 4;
 
 
 constexpr int kBorderCap = 2048;  // keys of the border bin kept in LDS for passes 2 and 3
-constexpr int kPerThread = 8;     // entries per thread in the ordered compaction
+constexpr int kPerThread = 8;     // entries per thread in the ordered compaction (two 16-byte LDS reads)
 
 // Workgroup barrier for LDS only: this wave's LDS operations complete before it, and no global load in flight is
 // waited for (the caller waits for what it needs).
@@ -80,7 +80,7 @@ __device__ __forceinline__ int find_bin(const int* hist, int need, int* wsum, in
 
 template <bool kLds>
 __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(SelArgs a) {
-  extern __shared__ uint32_t keys_s[];
+  extern __shared__ __attribute__((aligned(16))) uint32_t keys_s[];
   __shared__ int hist[2048];
   __shared__ uint32_t border[kBorderCap];
   __shared__ int wsum[kSelWaves];
@@ -184,10 +184,19 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(SelArgs a) {
   for (int base = 0; base < nvis && sel_run < k; base += kSelThreads * kPerThread) {
     const int i0 = base + tid * kPerThread;
     uint32_t kk[kPerThread];
+    if (kLds && i0 + kPerThread <= nvis) {
+      // the thread's eight keys in two 16-byte LDS reads (eight 4-byte reads 32 bytes apart across the lanes would
+      // each take eight times as long, their lanes meeting in the same banks)
+      const uint4 x0 = *(const uint4*)(K + i0), x1 = *(const uint4*)(K + i0 + 4);
+      kk[0] = x0.x, kk[1] = x0.y, kk[2] = x0.z, kk[3] = x0.w;
+      kk[4] = x1.x, kk[5] = x1.y, kk[6] = x1.z, kk[7] = x1.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < kPerThread; ++j) kk[j] = (i0 + j < nvis) ? K[i0 + j] : 0u;
+    }
     int gt = 0, eq = 0;
 #pragma unroll
     for (int j = 0; j < kPerThread; ++j) {
-      kk[j] = (i0 + j < nvis) ? K[i0 + j] : 0u;
       const bool valid = i0 + j < nvis;
       gt += (valid && kk[j] > kappa) ? 1 : 0;
       eq += (valid && kk[j] == kappa) ? 1 : 0;
