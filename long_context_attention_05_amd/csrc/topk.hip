@@ -260,7 +260,7 @@ __device__ __forceinline__ int sel_row_nvis(const SelArgs& a, int row) {
 //                        [20:10] (pass 2) and [9:0] (pass 3) over the candidates and writes the output.
 constexpr int kMbThreads = 256;
 constexpr int kMbPerThread = kSliceKeys / kMbThreads;  // 16
-constexpr int kCandCap = 6144;                         // candidates staged in LDS by the finishing workgroup
+constexpr int kCandCap = 6144;                         // candidates the finishing workgroup holds in registers
 
 // Exclusive scan over a 256-thread block.
 __device__ __forceinline__ int block256_excl_scan(int v, int* wsum, int& tot) {
