@@ -648,8 +648,8 @@ __global__ __launch_bounds__(kPsThreads) void attn_pfs_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int head = 4 * i + (lane >> 4);
-      *(uint4*)(dst + (long long)head * 1024 + 16 * (lane & 15)) =
-          *(const uint4*)(stage + head * kPr + 16 * (lane & 15));
+      __builtin_nontemporal_store(*(const u32x4_t*)(stage + head * kPr + 16 * (lane & 15)),
+                                  (u32x4_t*)(dst + (long long)head * 1024 + 16 * (lane & 15)));
     }
   };
   if (a.n_splits == 1) {
@@ -2146,7 +2146,7 @@ __global__ __launch_bounds__(64 * kDsWaves) void attn_dec_fused_kernel(AttnArgs 
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int head = 8 * wave + i;
-    *(u32x4_t*)(po + head * 1024 + 16 * lane) = *(const u32x4_t*)(qs + head * kDfRowB + 16 * lane);
+    __builtin_nontemporal_store(*(const u32x4_t*)(qs + head * kDfRowB + 16 * lane), (u32x4_t*)(po + head * 1024 + 16 * lane));
   }
 }
 
