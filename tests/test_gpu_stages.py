@@ -113,7 +113,8 @@ def test_compress_quantised_outputs(fmt, c, rope):
 # ------------------------------------------------------------------------------------------------------
 # stage 2: indexer scores + exact top-k
 # ------------------------------------------------------------------------------------------------------
-def _indexer_case(B, Sq, HI, DI, N, m, k, q_start, fmt, seed, dyadic=False, dup_rows=False, zero_q=False):
+def _indexer_case(B, Sq, HI, DI, N, m, k, q_start, fmt, seed, dyadic=False, dup_rows=False, zero_q=False,
+                  cluster=0.0):
     g = _rng(seed)
     if zero_q:  # every score is exactly 0: the selection is the first k visible entries
         q = np.zeros((B, Sq, HI, DI), np.float32)
@@ -129,6 +130,8 @@ def _indexer_case(B, Sq, HI, DI, N, m, k, q_start, fmt, seed, dyadic=False, dup_
         w = (g.standard_normal((B, Sq, HI)) / math.sqrt(HI * DI)).astype(np.float32)
     if dup_rows:
         K[:, 1::3] = K[:, 0:-1:3][:, :K[:, 1::3].shape[1]]
+    if cluster:  # the first 4096 keys scaled by a power of two: the high scores crowd into the first slice
+        K[:, :4096] *= cluster
     capk = N + 7
     if fmt == "fp4":
         kg = gpu_encode(K, "fp4", cap=capk)
@@ -160,9 +163,11 @@ def _indexer_case(B, Sq, HI, DI, N, m, k, q_start, fmt, seed, dyadic=False, dup_
         assert bad == 0, "per-head dots not exact in fp32: the exact comparison does not apply"
     nv = orc.nvis_rows(B, np.arange(Sq), q_start, m, N)
     gamma = 2.0 * (DI + HI) * 2.0 ** -24
-    return check_topk(idx.cpu().numpy().reshape(B * Sq, k), sc.cpu().numpy().reshape(B * Sq, k),
-                      s64.reshape(B * Sq, N), ab.reshape(B * Sq, N), nv, k, gamma, exact=exact,
-                      s32=None if s32 is None else s32.reshape(B * Sq, N))
+    st = check_topk(idx.cpu().numpy().reshape(B * Sq, k), sc.cpu().numpy().reshape(B * Sq, k),
+                    s64.reshape(B * Sq, N), ab.reshape(B * Sq, N), nv, k, gamma, exact=exact,
+                    s32=None if s32 is None else s32.reshape(B * Sq, N))
+    st["s64"], st["nvis"] = s64.reshape(B * Sq, N), nv
+    return st
 
 
 def test_indexer_simt_f32_prefill():
@@ -218,6 +223,32 @@ def test_indexer_all_scores_equal(fmt):
                   zero_q=True)
     _indexer_case(2, 1, 64 if fmt == "bf16" else 8, 128 if fmt == "bf16" else 32, 3000, 4, 512, 4 * 3000, fmt, 19,
                   zero_q=True)
+
+
+@pytest.mark.parametrize("fmt,B,N,k,cluster,zero_q", [("fp4", 2, 262144, 1024, 0.0, False),
+                                                     ("fp4", 1, 65636, 1024, 4.0, False),
+                                                     ("bf16", 1, 40000, 512, 0.0, True)])
+def test_indexer_decode_candidate_forms(fmt, B, N, k, cluster, zero_q):
+    # the decode select's finishing workgroup holds a row's candidates in registers (up to 6144, six consecutive ones
+    # per thread found by one segment search and a walk over the segments), or re-reads them on every pass: rows of
+    # 64 slices of plain N(0,1) keys; a row whose top scores crowd into its first slice (the walk crosses one long
+    # segment and many short ones); a row of equal scores (every slice is all candidates)
+    st = _indexer_case(B, 1, 64, 128, N, 4, k, 4 * N, fmt, 40, zero_q=zero_q, cluster=cluster)
+    # the form follows from the scores: the candidates of a 4096-entry slice are its keys in or above the bin (key
+    # bits [31:21]) of the k-th largest key
+    forms = []
+    for row, nv in zip(st["s64"], st["nvis"]):
+        bits = (row[:nv].astype(np.float32) + np.float32(0.0)).view(np.uint32)  # -0 counts as +0
+        keys = np.where(bits >> 31, ~bits, bits | np.uint32(0x80000000)).astype(np.uint32)
+        b1 = np.sort(keys >> 21)[::-1][k - 1]
+        per_slice = [int((keys[s:s + 4096] >> 21 >= b1).sum()) for s in range(0, nv, 4096)]
+        forms.append((max(per_slice), sum(per_slice)))
+    if cluster:
+        assert all(m > t // 2 and t <= 6144 for m, t in forms), forms  # one slice holds most of them
+    elif zero_q:
+        assert all(t > 6144 for _, t in forms), forms
+    else:
+        assert all(t <= 6144 for _, t in forms), forms
 
 
 def test_indexer_ties_go_to_lower_index():
