@@ -2164,51 +2164,59 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
   const long long item0 = ((long long)b * a.Sq + r) * S;
   const float z = a.sink[h];
   if (a.part_bf16 && S <= 32 && D == 4 * kMergeThreads) {
-    // bf16 partials, at most 32 splits: thread t's four channels of every split are loaded at once, behind the
-    // splits' (max, sum) (loaded unconditionally, so that the wait for them does not cover the partials), and the
-    // weights are formed while the partials are in flight
-    const int tid = threadIdx.x;
-    const long long sstride = (long long)H * D;
-    const uint16_t* pb = (const uint16_t*)a.part_o + (item0 * H + h) * D + 4 * tid;
-    const float2 ml = ((const float2*)a.part_ml)[(item0 + min(tid, S - 1)) * H + h];
-    uint2 pv[32];
+    // bf16 partials, at most 32 splits: thread t's four channels of every split are loaded at once (in a batch of
+    // NS >= S loads, the last split's repeated), behind the splits' (max, sum) (loaded unconditionally, so that the
+    // wait for them does not cover the partials), and the weights are formed while the partials are in flight
+    auto merge_bf16 = [&](auto NSC) {
+      constexpr int NS = decltype(NSC)::value;
+      const int tid = threadIdx.x;
+      const long long sstride = (long long)H * D;
+      const uint16_t* pb = (const uint16_t*)a.part_o + (item0 * H + h) * D + 4 * tid;
+      const float2 ml = ((const float2*)a.part_ml)[(item0 + min(tid, S - 1)) * H + h];
+      uint2 pv[NS];
 #pragma unroll
-    for (int s = 0; s < 32; ++s) pv[s] = *(const uint2*)(pb + min(s, S - 1) * sstride);
-    const float ms = tid < S ? ml.x : -INFINITY;
-    float mloc = wave_max(ms);
-    if ((tid & 63) == 0) red[tid >> 6] = mloc;
-    __syncthreads();
-    float M = z;
-    for (int i = 0; i < kMergeThreads / 64; ++i) M = fmaxf(M, red[i]);
-    const float wgt = (M == -INFINITY || ms == -INFINITY) ? 0.0f : __expf(ms - M);
-    if (tid < S) wsplit[tid] = wgt;
-    float dloc = wave_sum(tid < S ? wgt * ml.y : 0.0f);
-    __syncthreads();
-    if ((tid & 63) == 0) red[tid >> 6] = dloc;
-    __syncthreads();
-    float den = (M == -INFINITY || z == -INFINITY) ? 0.0f : __expf(z - M);
-    for (int i = 0; i < kMergeThreads / 64; ++i) den += red[i];
-    if (tid == 0 && a.lse) a.lse[((long long)b * a.Sq + r) * H + h] = (M == -INFINITY) ? -INFINITY : M + __logf(den);
-    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int s = 0; s < NS; ++s) pv[s] = *(const uint2*)(pb + min(s, S - 1) * sstride);
+      const float ms = tid < S ? ml.x : -INFINITY;
+      float mloc = wave_max(ms);
+      if ((tid & 63) == 0) red[tid >> 6] = mloc;
+      __syncthreads();
+      float M = z;
+      for (int i = 0; i < kMergeThreads / 64; ++i) M = fmaxf(M, red[i]);
+      const float wgt = (M == -INFINITY || ms == -INFINITY) ? 0.0f : __expf(ms - M);
+      if (tid < S) wsplit[tid] = wgt;
+      float dloc = wave_sum(tid < S ? wgt * ml.y : 0.0f);
+      __syncthreads();
+      if ((tid & 63) == 0) red[tid >> 6] = dloc;
+      __syncthreads();
+      float den = (M == -INFINITY || z == -INFINITY) ? 0.0f : __expf(z - M);
+      for (int i = 0; i < kMergeThreads / 64; ++i) den += red[i];
+      if (tid == 0 && a.lse)
+        a.lse[((long long)b * a.Sq + r) * H + h] = (M == -INFINITY) ? -INFINITY : M + __logf(den);
+      const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+      f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int s = 0; s < 32; ++s) {
-      if (s < S) {
-        const uint2 w = pv[s];
-        acc += wsplit[s] * f32x4_t{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
-                                   __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u)};
+      for (int s = 0; s < NS; ++s) {
+        if (s < S) {
+          const uint2 w = pv[s];
+          acc += wsplit[s] * f32x4_t{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
+                                     __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u)};
+        }
       }
-    }
-    acc *= inv;
-    const long long ob = (((long long)b * a.Sq + r) * H + h) * D + 4 * tid;
-    if (a.out_format == LCA_F32) {
-      *(f32x4_t*)((float*)a.out + ob) = acc;
-    } else {
-      uint2 w2;
-      w2.x = pack_bf16x2(acc[0], acc[1]);
-      w2.y = pack_bf16x2(acc[2], acc[3]);
-      *(uint2*)((uint16_t*)a.out + ob) = w2;
-    }
+      acc *= inv;
+      const long long ob = (((long long)b * a.Sq + r) * H + h) * D + 4 * tid;
+      if (a.out_format == LCA_F32) {
+        *(f32x4_t*)((float*)a.out + ob) = acc;
+      } else {
+        uint2 w2;
+        w2.x = pack_bf16x2(acc[0], acc[1]);
+        w2.y = pack_bf16x2(acc[2], acc[3]);
+        *(uint2*)((uint16_t*)a.out + ob) = w2;
+      }
+    };
+    if (S <= 8) merge_bf16(std::integral_constant<int, 8>{});
+    else if (S <= 16) merge_bf16(std::integral_constant<int, 16>{});
+    else if (S <= 24) merge_bf16(std::integral_constant<int, 24>{});
+    else merge_bf16(std::integral_constant<int, 32>{});
     return;
   }
   // M = max(z, m_s)
