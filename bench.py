@@ -187,8 +187,9 @@ def _oracle_csa_prefill_once(w, inp, rows_n):
         ents[tag] = gen.bf16_bits(E.astype(np.float32))
     N0 = w.N
     N = (w.n_ctx + w.Sq) // w.m
-    keys = np.concatenate([gen.bf16_bits(inp["keys"]), ents["_I"]], axis=1)
-    comp = np.concatenate([gen.bf16_bits(inp["comp"]), ents[""]], axis=1)
+    # the given cached part (none without context) followed by the chunk's own entries
+    keys = np.concatenate([gen.bf16_bits(inp["keys"]), ents["_I"]], axis=1) if N0 else ents["_I"]
+    comp = np.concatenate([gen.bf16_bits(inp["comp"]), ents[""]], axis=1) if N0 else ents[""]
     assert keys.shape[1] == N and comp.shape[1] == N and N0 < N
     rows = np.linspace(0, w.Sq - 1, rows_n).astype(np.int32)
     kc = dict(orc.plain_cache(keys, "bf16"), cap=N)
@@ -461,7 +462,9 @@ def main():
             achieved = per_launch / (avg_ms / 1e3) / 1e9
             res["roofline"] = {"kernel": kname, "bound": "hbm", "achieved": achieved,
                                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                               "traffic": traffic_record(kname, w.name, src, per_launch),
+                               # counters taken on the dense layout say nothing of a paged one
+                               "traffic": traffic_record(kname, w.name + ("_paged" if args.paged else ""), src,
+                                                         per_launch),
                                "avg_launch_us": avg_ms * 1e3, "algorithmic_bytes_per_launch": per_launch,
                                "timed_with": how}
         else:
