@@ -335,6 +335,15 @@ __device__ __forceinline__ float head_cross4(const float (&v)[4][4]) {
 
 __device__ __forceinline__ void flush_hist(const int* hist_s, int* gh) {
   __syncthreads();
+  if (blockDim.x == 512) {  // every bin's count read at once, then the adds
+    int c[kSelBins / 512];
+#pragma unroll
+    for (int u = 0; u < kSelBins / 512; ++u) c[u] = hist_s[threadIdx.x + 512 * u];
+#pragma unroll
+    for (int u = 0; u < kSelBins / 512; ++u)
+      if (c[u]) atomicAdd(&gh[threadIdx.x + 512 * u], c[u]);
+    return;
+  }
   for (int i = threadIdx.x; i < kSelBins; i += blockDim.x) {
     const int c = hist_s[i];
     if (c) atomicAdd(&gh[i], c);
@@ -589,9 +598,22 @@ __global__ __launch_bounds__(kF4rWaves * 64) void idx_score_decode_fp4_ring(IdxA
       for (int i = 0; i < 2; ++i)
         qraw[r][T][i] = *(const uint4*)((const uint8_t*)a.q.data + row * 64 + 16 * (2 * i + hh));
       sraw[r][T] = *(const uint32_t*)((const uint8_t*)a.q.scale + row * 4);
+      // weights of heads 32 T + 8 a + 4 hh + c, c = 0..3: four consecutive floats per a, one 16-byte load each when
+      // the weights start 16-byte aligned
+      const float* wrow = a.w + (long long)(qrow0 + r) * 64 + 32 * T + 4 * hh;
+      if (((uintptr_t)a.w & 15u) == 0) {
 #pragma unroll
-      for (int k = 0; k < 16; ++k)
-        wv[r][T][k] = a.w[(long long)(qrow0 + r) * 64 + 32 * T + 8 * (k >> 2) + 4 * hh + (k & 3)];
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float4 wq = *(const float4*)(wrow + 8 * q4);
+          wv[r][T][4 * q4] = wq.x;
+          wv[r][T][4 * q4 + 1] = wq.y;
+          wv[r][T][4 * q4 + 2] = wq.z;
+          wv[r][T][4 * q4 + 3] = wq.w;
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) wv[r][T][k] = wrow[8 * (k >> 2) + (k & 3)];
+      }
     }
   __builtin_amdgcn_sched_barrier(0);
   i32x8_t qop[NR][2][2];
