@@ -35,6 +35,7 @@ sys.path.insert(0, ROOT)
 METRIC = "CSA/HCA layer decode tokens/s at 128K–1M ctx; achieved HBM TB/s vs peak"
 HBM_PEAK_GBPS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # 256 CUs x 4 SIMDs x 64 lanes x 2 flops per fused multiply-add x 2.4 GHz
 
 
 def parse():
@@ -470,9 +471,13 @@ def main():
         else:
             per_launch = step.score_kernel_flops()
             achieved = per_launch / (avg_ms / 1e3) / 1e12
-            res["roofline"] = {"kernel": "idx_score_mfma", "bound": "mfma", "achieved": achieved,
-                               "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS,
-                               "traffic": traffic_record("idx_score_mfma", w.name, src, per_launch),
+            # 64 heads x 128 dims of bf16 take the MFMA kernel; other shapes and fp32 the vector-ALU one
+            mfma = w.HI == 64 and w.DI == 128 and w.key_fmt == "bf16"
+            kname, bound, peak = (("idx_score_mfma", "mfma", BF16_PEAK_TFLOPS) if mfma else
+                                  ("idx_score_simt", "alu", FP32_VECTOR_PEAK_TFLOPS))
+            res["roofline"] = {"kernel": kname, "bound": bound, "achieved": achieved,
+                               "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
+                               "traffic": traffic_record(kname, w.name, src, per_launch),
                                "avg_launch_us": avg_ms * 1e3, "algorithmic_flops_per_launch": per_launch,
                                "timed_with": how}
     del step, hs_buf
