@@ -2155,6 +2155,8 @@ __global__ __launch_bounds__(64 * kDsWaves) void attn_dec_fused_kernel(AttnArgs 
 // ------------------------------------------------------------------------------------------------
 // One workgroup per (head, query row, sequence): combine the splits' (max, sum, o) with the sink.
 constexpr int kMergeThreads = 128;
+// bf16 partials of at most 16 splits over 512 channels: one wave per (head, row), eight channels per lane
+__host__ __device__ inline bool merge_one_wave(const AttnArgs& a) { return a.part_bf16 && a.n_splits <= 16 && a.D == 512; }
 __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
   extern __shared__ float wsplit[];  // [n_splits] weights e^(m_s - M)
   __shared__ float red[kMergeThreads / 64];
@@ -2163,6 +2165,54 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
   const int H = a.H, D = a.D, S = a.n_splits;
   const long long item0 = ((long long)b * a.Sq + r) * S;
   const float z = a.sink[h];
+  if (merge_one_wave(a)) {
+    // bf16 partials, at most 16 splits, one wave: lane t's eight channels of every split are loaded at once (a batch
+    // of NS >= S loads, the last split's repeated), behind the splits' (max, sum); lane s < S forms split s's weight,
+    // which the channel sums read from it by lane broadcast
+    auto merge_wave = [&](auto NSC) {
+      constexpr int NS = decltype(NSC)::value;
+      const int tid = threadIdx.x;
+      const long long sstride = (long long)H * D;
+      const uint16_t* pb = (const uint16_t*)a.part_o + (item0 * H + h) * D + 8 * tid;
+      const float2 ml = ((const float2*)a.part_ml)[(item0 + min(tid, S - 1)) * H + h];
+      uint4 pv[NS];
+#pragma unroll
+      for (int s = 0; s < NS; ++s) pv[s] = *(const uint4*)(pb + min(s, S - 1) * sstride);
+      const float ms = tid < S ? ml.x : -INFINITY;
+      const float M = fmaxf(z, wave_max(ms));
+      const float wgt = (M == -INFINITY || ms == -INFINITY) ? 0.0f : __expf(ms - M);
+      const float den = wave_sum(tid < S ? wgt * ml.y : 0.0f) +
+                        ((M == -INFINITY || z == -INFINITY) ? 0.0f : __expf(z - M));
+      if (tid == 0 && a.lse)
+        a.lse[((long long)b * a.Sq + r) * H + h] = (M == -INFINITY) ? -INFINITY : M + __logf(den);
+      const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+      f32x4_t lo = {0.0f, 0.0f, 0.0f, 0.0f}, hi = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        if (s < S) {
+          const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), s));
+          const uint4 w = pv[s];
+          lo += ws * f32x4_t{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
+                             __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u)};
+          hi += ws * f32x4_t{__uint_as_float(w.z << 16), __uint_as_float(w.z & 0xFFFF0000u),
+                             __uint_as_float(w.w << 16), __uint_as_float(w.w & 0xFFFF0000u)};
+        }
+      }
+      lo *= inv;
+      hi *= inv;
+      const long long ob = (((long long)b * a.Sq + r) * H + h) * D + 8 * tid;
+      if (a.out_format == LCA_F32) {
+        *(f32x4_t*)((float*)a.out + ob) = lo;
+        *(f32x4_t*)((float*)a.out + ob + 4) = hi;
+      } else {
+        *(uint4*)((uint16_t*)a.out + ob) = make_uint4(pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]),
+                                                      pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3]));
+      }
+    };
+    if (S <= 8) merge_wave(std::integral_constant<int, 8>{});
+    else merge_wave(std::integral_constant<int, 16>{});
+    return;
+  }
   if (a.part_bf16 && S <= 32 && D == 4 * kMergeThreads) {
     // bf16 partials, at most 32 splits: thread t's four channels of every split are loaded at once (in a batch of
     // NS >= S loads, the last split's repeated), behind the splits' (max, sum) (loaded unconditionally, so that the
@@ -2386,8 +2436,8 @@ hipError_t launch_attn(AttnArgs a, hipStream_t st, hipEvent_t eb, hipEvent_t ee)
   // mode 3 writes the output itself; mode 4 always leaves partials
   if (e != hipSuccess || a.hg_mode == 3 || (a.n_splits == 1 && a.hg_mode != 4)) return e;
   const size_t lds = sizeof(float) * (size_t)a.n_splits;
-  hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)a.H, (unsigned)a.Sq, (unsigned)a.B), dim3(kMergeThreads), lds,
-                     st, a);
+  hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)a.H, (unsigned)a.Sq, (unsigned)a.B),
+                     dim3(merge_one_wave(a) ? 64 : kMergeThreads), lds, st, a);
   return hipGetLastError();
 }
 

@@ -306,7 +306,7 @@ __device__ __forceinline__ int find_bin256(const int* hist, int need, int* wsum,
 }
 
 __global__ __launch_bounds__(kMbThreads) void topk_collect_kernel(SelArgs a) {
-  __shared__ int hist[kSelBins];
+  __shared__ __attribute__((aligned(16))) int hist[kSelBins];
   __shared__ int wsum[kMbThreads / 64];
   __shared__ int sh[4];
   const int p = blockIdx.x, row = blockIdx.y, tid = threadIdx.x;
@@ -337,11 +337,10 @@ __global__ __launch_bounds__(kMbThreads) void topk_collect_kernel(SelArgs a) {
     for (int u = 0; u < kMbPerThread; ++u) kv[u] = j0 + u < s1 ? kg[j0 + u] : 0u;
   }
   const int* gh = a.sel_state + (long long)row * kSelStateInts;
-  int hv[kSelBins / kMbThreads];
-#pragma unroll
-  for (int u = 0; u < kSelBins / kMbThreads; ++u) hv[u] = gh[tid + kMbThreads * u];
-#pragma unroll
-  for (int u = 0; u < kSelBins / kMbThreads; ++u) hist[tid + kMbThreads * u] = hv[u];
+  static_assert(kSelBins == 8 * kMbThreads, "eight consecutive bins per thread");
+  const int4 h0 = *(const int4*)(gh + 8 * tid), h1 = *(const int4*)(gh + 8 * tid + 4);
+  *(int4*)(hist + 8 * tid) = h0;
+  *(int4*)(hist + 8 * tid + 4) = h1;
   __syncthreads();
   int above1;
   const int b1 = find_bin256(hist, k, wsum, sh, &above1);
