@@ -2156,7 +2156,9 @@ __global__ __launch_bounds__(64 * kDsWaves) void attn_dec_fused_kernel(AttnArgs 
 // One workgroup per (head, query row, sequence): combine the splits' (max, sum, o) with the sink.
 constexpr int kMergeThreads = 128;
 // bf16 partials of at most 16 splits over 512 channels: one wave per (head, row), eight channels per lane
-__host__ __device__ inline bool merge_one_wave(const AttnArgs& a) { return a.part_bf16 && a.n_splits <= 16 && a.D == 512; }
+__host__ __device__ inline bool merge_one_wave(const AttnArgs& a) {
+  return a.part_bf16 && a.n_splits <= 16 && a.D == 512;
+}
 __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
   extern __shared__ float wsplit[];  // [n_splits] weights e^(m_s - M)
   __shared__ float red[kMergeThreads / 64];
