@@ -393,21 +393,28 @@ __device__ __forceinline__ void bf_load_stage(BfStage& S, const uint8_t* kd, lon
   }
 }
 
-template <int NST>
-__global__ __launch_bounds__(256, 2) void idx_score_decode_bf16(IdxArgs a) {
+// NR query rows (consecutive rows of one sequence) per workgroup: each key stage is loaded once and scored for every
+// row.  One row keeps two workgroups per CU (at most 256 registers a wave); two rows hold both rows' query blocks
+// and take one workgroup per CU, whose waves may use the whole register file.
+template <int NST, int NR>
+__global__ __launch_bounds__(256, NR == 1 ? 2 : 1) void idx_score_decode_bf16(IdxArgs a) {
 #pragma clang fp contract(off)
-  __shared__ int hist_s[kSelBins];
+  __shared__ int hist_s[NR][kSelBins];
   constexpr int KPW = 16 * kBfGroups;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int g = lane >> 4, col = lane & 15;
-  const int qrow = blockIdx.y, b = qrow / a.Sq;  // query row b * Sq + r
-  const int nvis = nvis_of(seq_position(a.seq_pos, a.q_start, b) + (qrow - b * a.Sq), a.m, a.N);
+  const int qrow0 = blockIdx.y * NR, b = qrow0 / a.Sq;  // query rows qrow0 .. qrow0 + NR - 1, all of sequence b
+  const long long pos0 = seq_position(a.seq_pos, a.q_start, b) + (qrow0 - b * a.Sq);
+  int nv[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) nv[r] = nvis_of(pos0 + r, a.m, a.N);
+  const int nvis = nv[NR - 1];  // the group's last row sees the most entries
   const int k0 = blockIdx.x * (NST * 4 * KPW);
   const int k1 = min(k0 + NST * 4 * KPW, nvis);
   if (k0 >= k1) return;
   const bool hist = a.sel_state != nullptr;
   if (hist)
-    for (int i = threadIdx.x; i < kSelBins; i += blockDim.x) hist_s[i] = 0;
+    for (int i = threadIdx.x; i < NR * kSelBins; i += blockDim.x) (&hist_s[0][0])[i] = 0;
   const uint8_t* kd = (const uint8_t*)a.k.data;
   // paged: every stage's blocks, resolved before the stream starts (wave-uniform table reads)
   const int br = a.k.block_table ? a.k.block_rows : 0;
@@ -428,21 +435,25 @@ __global__ __launch_bounds__(256, 2) void idx_score_decode_bf16(IdxArgs a) {
 
   BfStage S[2];
   bf_load_stage(S[0], kd, dense0, blk[0], br, k0 + wave * KPW, k1 - 1, lane);
-  bf16x8_t qa[4][4];
-  float wv[4][4];
+  bf16x8_t qa[NR][4][4];
+  float wv[NR][4][4];
 #pragma unroll
-  for (int T = 0; T < 4; ++T) {
-    const uint8_t* qp = (const uint8_t*)a.q.data + ((long long)qrow * 64 + 16 * T + col) * 256;
+  for (int r = 0; r < NR; ++r)
 #pragma unroll
-    for (int s = 0; s < 4; ++s) qa[T][s] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(qp + 16 * g + 64 * s));
+    for (int T = 0; T < 4; ++T) {
+      const uint8_t* qp = (const uint8_t*)a.q.data + ((long long)(qrow0 + r) * 64 + 16 * T + col) * 256;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) wv[T][r] = a.w[(long long)qrow * 64 + 16 * T + 4 * g + r];
-  }
+      for (int s = 0; s < 4; ++s) qa[r][T][s] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(qp + 16 * g + 64 * s));
+#pragma unroll
+      for (int x = 0; x < 4; ++x) wv[r][T][x] = a.w[(long long)(qrow0 + r) * 64 + 16 * T + 4 * g + x];
+    }
   if (hist) __syncthreads();  // histogram zeroed before any update
 
   // straight-line stages (fully unrolled): the next stage's loads are in flight while this one is scored, and each
   // stage's keys are stored after the following stage's loads are issued
-  KeyOut pend{0u, k1};
+  KeyOut pend[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) pend[r] = KeyOut{0u, k1};
 #pragma unroll
   for (int st = 0; st < NST; ++st) {
     const int kbase = k0 + st * 4 * KPW + wave * KPW;
@@ -450,26 +461,36 @@ __global__ __launch_bounds__(256, 2) void idx_score_decode_bf16(IdxArgs a) {
       bf_load_stage(S[(st + 1) & 1], kd, dense0, blk[st + 1], br, kbase + 4 * KPW, k1 - 1, lane);
       __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the scoring
     }
-    if (st > 0) store_key(a, qrow, k1, pend, hist_s, hist);
+    if (st > 0)
+#pragma unroll
+      for (int r = 0; r < NR; ++r)
+        store_key(a, qrow0 + r, k1, pend[r], hist_s[r], hist && pend[r].e < nv[r]);
     const BfStage& C = S[st & 1];
-    float v[kBfGroups][4];
 #pragma unroll
-    for (int j = 0; j < kBfGroups; ++j) {
-      f32x4_t acc[4];
+    for (int r = 0; r < NR; ++r) {
+      float v[kBfGroups][4];
 #pragma unroll
-      for (int T = 0; T < 4; ++T) acc[T] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int j = 0; j < kBfGroups; ++j) {
+        f32x4_t acc[4];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const bf16x8_t kv = __builtin_bit_cast(bf16x8_t, C.c[j][s]);
+        for (int T = 0; T < 4; ++T) acc[T] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int T = 0; T < 4; ++T) acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[T][s], kv, acc[T], 0, 0, 0);
+        for (int s = 0; s < 4; ++s) {
+          const bf16x8_t kv = __builtin_bit_cast(bf16x8_t, C.c[j][s]);
+#pragma unroll
+          for (int T = 0; T < 4; ++T)
+            acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[r][T][s], kv, acc[T], 0, 0, 0);
+        }
+        head_partial(acc, wv[r], v[j]);
       }
-      head_partial(acc, wv, v[j]);
+      pend[r] = lane_key(kbase, g, head_cross4(v));
     }
-    pend = lane_key(kbase, g, head_cross4(v));
   }
-  store_key(a, qrow, k1, pend, hist_s, hist);
-  if (hist) flush_hist(hist_s, a.sel_state + (long long)qrow * kSelStateInts);
+#pragma unroll
+  for (int r = 0; r < NR; ++r) store_key(a, qrow0 + r, k1, pend[r], hist_s[r], hist && pend[r].e < nv[r]);
+  if (hist)
+#pragma unroll
+    for (int r = 0; r < NR; ++r) flush_hist(hist_s[r], a.sel_state + (long long)(qrow0 + r) * kSelStateInts);
 }
 
 typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8_t;
@@ -826,15 +847,28 @@ hipError_t launch_indexer_scores(const IdxArgs& a, hipStream_t st, hipEvent_t eb
       return hipGetLastError();
     }
     // a fixed key range per workgroup (NST stages of 4 waves x KPW keys), the grid grows with the context; fewer
-    // stages when that leaves fewer than about two workgroups per CU
+    // stages when that leaves fewer than about two workgroups per CU (one per CU for two rows per workgroup, which
+    // also allows eight stages)
     const int kpw = 16 * kBfGroups;
-    const long long rows = (long long)a.B * a.Sq;
-    int nst = 4;
-    while (nst > 1 && rows * ((nvis_max + nst * 4 * kpw - 1) / (nst * 4 * kpw)) < 512) nst >>= 1;
-    const dim3 grid((unsigned)decode_grid_x((nvis_max + nst * 4 * kpw - 1) / (nst * 4 * kpw), a.Sq), (unsigned)rows);
-    if (nst == 4) hipExtLaunchKernelGGL(idx_score_decode_bf16<4>, grid, dim3(256), 0, st, eb, ee, 0, a);
-    else if (nst == 2) hipExtLaunchKernelGGL(idx_score_decode_bf16<2>, grid, dim3(256), 0, st, eb, ee, 0, a);
-    else hipExtLaunchKernelGGL(idx_score_decode_bf16<1>, grid, dim3(256), 0, st, eb, ee, 0, a);
+    const int nr = a.Sq % 2 == 0 ? 2 : 1;
+    const long long groups = (long long)a.B * a.Sq / nr;
+    const long long target = nr == 1 ? 512 : 256;
+    int nst = nr == 1 ? 4 : 8;
+    while (nst > 1 && groups * ((nvis_max + nst * 4 * kpw - 1) / (nst * 4 * kpw)) < target) nst >>= 1;
+    const dim3 grid((unsigned)decode_grid_x((nvis_max + nst * 4 * kpw - 1) / (nst * 4 * kpw), a.Sq / nr),
+                    (unsigned)groups);
+#define LCA_BFD(NS, R) hipExtLaunchKernelGGL((idx_score_decode_bf16<NS, R>), grid, dim3(256), 0, st, eb, ee, 0, a)
+    if (nr == 2) {
+      if (nst == 8) LCA_BFD(8, 2);
+      else if (nst == 4) LCA_BFD(4, 2);
+      else if (nst == 2) LCA_BFD(2, 2);
+      else LCA_BFD(1, 2);
+    } else {
+      if (nst == 4) LCA_BFD(4, 1);
+      else if (nst == 2) LCA_BFD(2, 1);
+      else LCA_BFD(1, 1);
+    }
+#undef LCA_BFD
   } else if (mfma) {
     const int qpb = a.Sq >= 16 ? 16 : a.Sq;
     dim3 grid((unsigned)((nvis_max + kMfmaEntriesPerBlock - 1) / kMfmaEntriesPerBlock),

@@ -199,10 +199,11 @@ def test_indexer_fp4_bit_exact(B, Sq, N, k, HI, DI):
 
 @pytest.mark.parametrize("B,Sq,N,k,q_off,fmt", [(3, 2, 2037, 512, -1, "bf16"), (2, 4, 16411, 512, -2, "bf16"),
                                                 (2, 4, 3001, 1024, -3, "fp4"), (1, 2, 70000, 1024, -1, "fp4"),
-                                                (4, 3, 8200, 512, 0, "bf16")])
+                                                (4, 3, 8200, 512, 0, "bf16"), (1, 4, 40000, 512, -3, "bf16")])
 def test_indexer_decode_multi_row(B, Sq, N, k, q_off, fmt):
-    # several query rows per sequence (draft tokens verified together) share the decode kernels; with q_start just
-    # below a multiple of m the rows see N - 1 and N entries
+    # several query rows per sequence (draft tokens verified together) share the decode kernels, which score an even
+    # number of rows two to a workgroup; with q_start just below a multiple of m the rows see N - 1 and N entries
+    # (four bf16 rows over 40000 entries: two row pairs, the second one's rows seeing different entry counts)
     st = _indexer_case(B, Sq, 64, 128, N, 4, k, 4 * N + q_off, fmt, 20 + Sq)
     if fmt == "bf16":
         assert st["exact_rows"] >= st["rows"] - 1
