@@ -1,7 +1,8 @@
 """Block-managed (paged) caches and ragged batches (itsolotime page, question 5: the compressed cache is managed in
 blocks of lcm(4, 128) = 128 tokens -- 32 CSA entries, one HCA entry -- and a serving batch holds sequences of
 different lengths), through the C-ABI:
-  - decode at the 128K bf16 and 1M mixed shapes with shuffled block tables and every sequence at its own position:
+  - decode at the 128K bf16 and 1M mixed shapes (one and two query rows per sequence) with shuffled block tables and
+    every sequence at its own position:
     the GPU's paged results equal its dense results bit for bit, the selection matches the oracle's (bit-exact for
     fp4) and every attention row matches the oracle attending the GPU's selection;
   - kv_compress appends into a paged cache with ragged starts and token counts;
@@ -46,8 +47,10 @@ def _decode(w, inp, block_rows, pos):
     return step
 
 
-@pytest.mark.parametrize("name", ["csa_decode_128k_bf16", "csa_decode_1m_mixed"])
+@pytest.mark.parametrize("name", ["csa_decode_128k_bf16", "csa_decode_1m_mixed", "csa_decode_128k_bf16_mtp2",
+                                  "csa_decode_1m_mixed_mtp2"])
 def test_paged_ragged_decode_full(name):
+    # (the two-row workloads score both rows of a sequence in one workgroup from the same paged key stages)
     w = gen.WORKLOADS[name]
     inp = gen.decode_inputs(w)
     pos = _ragged_positions(w, 401)
@@ -78,7 +81,7 @@ def test_paged_ragged_decode_full(name):
     gidx = paged.idx.cpu().numpy().reshape(R, w.k)
     st = check_topk(gidx, paged.scores.cpu().numpy().reshape(R, w.k), s64.reshape(R, N), ab.reshape(R, N), nv, w.k,
                     GAMMA(w.DI, w.HI), exact=exact, s32=None if s32 is None else s32.reshape(R, N))
-    assert st["near_tie_rows"] <= 1
+    assert st["near_tie_rows"] <= max(1, R // 16)
     if w.main_fmt == "mixed":
         cc = orc.encode(inp["comp"].reshape(-1, w.D), "mixed", w.rope)
         rc = orc.encode(inp["window_kv"].reshape(-1, w.D), "mixed", w.rope)
