@@ -188,7 +188,8 @@ int kv_compress(const float* Ca, const float* Cb, const float* Za, const float* 
  * Scores are fp32.  The per-head sum is fixed: p[h] = fl32(w[h] * max(0, d[h])) added in a halving tree
  * (a[j] += a[j + L/2], L = next power of two of HI, zero padded), so inputs whose per-head dots are exact in
  * fp32 (e.g. fp4 x fp4 with a bounded scale spread) give bit-reproducible selections.
- * ws: device scratch of at least indexer_score_topk_workspace_size(B, Sq, N, k) bytes (contents ignored).
+ * ws: device scratch of at least indexer_score_topk_workspace_size(B, Sq, N, k) bytes, 16-byte aligned (contents
+ * ignored).
  * ragged (HOST pointer, nullable): per-sequence query positions (see lca_ragged).
  * Errors: INVALID_ARG (null, sizes <= 0, dims mismatch, qI.cap != Sq * HI, DI % 16 for FP4),
  *         UNSUPPORTED (HI > 64, DI > 128, q/k formats not both float-like or both FP4; a paged kI with blocks of
@@ -253,7 +254,8 @@ int indexer_score_topk_noalloc(lca_tensor qI, const float* w, lca_tensor kI, int
  *   S_raw <= kv_raw.cap.
  *   out: [B][Sq][H][D] in out_format (LCA_F32 or LCA_BF16).  lse_out (nullable): float [B][Sq][H], the log
  *   of the softmax denominator M + log(den).
- * ws: device scratch of at least sparse_mqa_attn_workspace_size(B, Sq, H, D, window + k) bytes.
+ * ws: device scratch of at least sparse_mqa_attn_workspace_size(B, Sq, H, D, window + k) bytes, 16-byte aligned when
+ * that size is non-zero.
  * ragged (HOST pointer, nullable): per-sequence query positions (see lca_ragged).
  * Errors: INVALID_ARG, UNSUPPORTED (shape without a kernel: on the float path -- q or the caches not bf16 over
  *         bf16/mixed, or H != 64, or D != 512 -- H > 64, D > 512 or H * D > 8192), WORKSPACE, ALIGNMENT.
@@ -268,7 +270,7 @@ int sparse_mqa_attn(const void* q, int q_format, lca_tensor kv_comp, int N, lca_
  * hca_attn -- stage 4, the HCA variant: dense MQA over every visible m:1 entry (i < min(floor(t/m), N)),
  * the sliding window and the sink (paper notes section 2.4; cosmocat section 4; 67808.cn section 3).
  * Same arithmetic, arguments and errors as sparse_mqa_attn with the index list replaced by all visible
- * entries.  ws: at least hca_attn_workspace_size(B, Sq, H, D, window + N) bytes.
+ * entries.  ws: at least hca_attn_workspace_size(B, Sq, H, D, window + N) bytes, 16-byte aligned.
  */
 size_t hca_attn_workspace_size(int B, int Sq, int H, int D, int max_entries);
 int hca_attn(const void* q, int q_format, lca_tensor kv_comp, int N, int m, lca_tensor kv_raw, long long raw_start_pos,

@@ -227,6 +227,7 @@ int run_attn(const void* q, int q_format, const lca_tensor& comp_in, int N, int 
   if (mfma && len > kHgSplitMax) return LCA_ERR_UNSUPPORTED;  // more than 4096 x 2048 list positions per row
   const size_t need = attn_ws_plan_size(B, Sq, H, D, max_entries, mode, mfma);
   if (need > 0 && (!ws || ws_bytes < need)) return LCA_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(ws)) return LCA_ERR_ALIGNMENT;  // split partials go out in 16-byte stores
 
   AttnArgs a{};
   a.q = q;
@@ -434,6 +435,7 @@ int indexer_score_topk(lca_tensor qI, const float* w, lca_tensor kI, int B, int 
   if (((uintptr_t)w & 3u) || ((uintptr_t)idx_out & 3u) || (score_out && ((uintptr_t)score_out & 3u)))
     return LCA_ERR_ALIGNMENT;
   if (N > 0 && (!ws || ws_bytes < indexer_score_topk_workspace_size(B, Sq, N, k))) return LCA_ERR_WORKSPACE;
+  if (N > 0 && !aligned16(ws)) return LCA_ERR_ALIGNMENT;  // keys, histograms and candidates are read 16 bytes at a time
   hipStream_t st = (hipStream_t)stream;
   const IdxWs L = idx_ws_layout(B, Sq, N > 0 ? N : 1);
   const bool multi = N > 0 && Sq <= kDecodeMaxRows && N <= kMaxMultiN &&

@@ -90,6 +90,8 @@ def test_host_validation_errors():
     assert L.indexer_score_topk(q, P, _t(fmt=3, dim=128, cap=1000, scale=P), 1, 1, 64, 128, 1000, 4, 64, 4000, P, None,
                                 P, 1 << 30, None, None) == UNS
     assert L.indexer_score_topk(q, None, k, 1, 1, 64, 128, 1000, 4, 64, 4000, P, None, P, 1 << 30, None, None) == INV
+    # the workspace is read and written 16 bytes at a time
+    assert L.indexer_score_topk(q, P, k, 1, 1, 64, 128, 1000, 4, 64, 4000, P, None, P + 4, 1 << 30, None, None) == ALN
     # the query tensor must hold exactly Sq * HI rows per sequence (the kernels address rows (b * Sq + r) * HI + h)
     assert L.indexer_score_topk(_t(dim=128, cap=65), P, k, 2, 1, 64, 128, 1000, 4, 64, 4000, P, None, P, 1 << 30, None,
                                 None) == INV
@@ -113,6 +115,9 @@ def test_host_validation_errors():
                              0, None, None) == WS
     assert L.sparse_mqa_attn(P, 7, comp, 5000, raw, 373, 128, P, 512, P, 2, 1, 64, 512, 128, f, 500, P, 1, None, P,
                              1 << 30, None, None) == INV
+    # a split plan's workspace takes 16-byte partial stores
+    assert L.sparse_mqa_attn(P, 1, comp, 5000, raw, 373, 128, P, 512, P, 2, 1, 64, 512, 128, f, 500, P, 1, None, P + 8,
+                             1 << 30, None, None) == ALN
     assert L.hca_attn(P, 1, comp, 5000, 0, raw, 373, 128, P, 2, 1, 64, 512, 128, f, 500, P, 1, None, P, 1 << 30, None,
                       None) == INV
     # the float path (fp32 queries or caches) covers H * D <= 8192 only: 64 heads x 512 channels in fp32 has no kernel

@@ -114,7 +114,7 @@ def test_compress_quantised_outputs(fmt, c, rope):
 # stage 2: indexer scores + exact top-k
 # ------------------------------------------------------------------------------------------------------
 def _indexer_case(B, Sq, HI, DI, N, m, k, q_start, fmt, seed, dyadic=False, dup_rows=False, zero_q=False,
-                  cluster=0.0):
+                  cluster=0.0, w_off=0):
     g = _rng(seed)
     if zero_q:  # every score is exactly 0: the selection is the first k visible entries
         q = np.zeros((B, Sq, HI, DI), np.float32)
@@ -151,6 +151,11 @@ def _indexer_case(B, Sq, HI, DI, N, m, k, q_start, fmt, seed, dyadic=False, dup_
         kr, qr = orc.plain_cache(K, "f32"), orc.plain_cache(q, "f32")
         kr["cap"] = N
     wd = up(w)
+    if w_off:  # the weights w_off floats past a 16-byte boundary (the API asks only for 4-byte alignment)
+        buf = torch.zeros(wd.numel() + w_off, dtype=torch.float32, device="cuda")
+        buf[w_off:] = wd.reshape(-1)
+        wd = buf[w_off:]
+        assert wd.data_ptr() % 16 == 4 * w_off
     idx = torch.empty((B, Sq, k), dtype=torch.int32, device="cuda")
     sc = torch.empty((B, Sq, k), dtype=torch.float32, device="cuda")
     nbytes = lca.indexer_score_topk_workspace_size(B, Sq, N, k)
@@ -250,6 +255,13 @@ def test_indexer_decode_candidate_forms(fmt, B, N, k, cluster, zero_q):
         assert all(t > 6144 for _, t in forms), forms
     else:
         assert all(t <= 6144 for _, t in forms), forms
+
+
+@pytest.mark.parametrize("Sq", [1, 2])
+def test_indexer_fp4_weights_not_16_byte_aligned(Sq):
+    # the fp4 decode scorer reads each lane's head weights in 16-byte loads only when the weights are 16-byte
+    # aligned; 4 bytes past a boundary it takes them one by one, with the same results
+    _indexer_case(2, Sq, 64, 128, 9000, 4, 512, 4 * 9000, "fp4", 41, w_off=1)
 
 
 def test_indexer_ties_go_to_lower_index():
